@@ -1,0 +1,77 @@
+"""Oracle for one rank's column->row MLP share (test infrastructure only).
+
+Sources:
+* ColossalAI 1D tensor parallelism, section 2: with A cut by columns into
+  [A_1 ... A_P], rank i computes Y_i = X A_i and the Y_i side by side form XA.
+* Same page, section 2.1: the second linear layer cuts B by rows into
+  [B_1; ...; B_P]; rank i computes Y_i B_i and the sum over ranks (one
+  all-reduce) is Z = Y B.
+* DeepSpeed-Domino article, "forward" under implementation: each micro-batch
+  runs GeMM, GeLU, GeMM; the row chunks of X are independent.
+* ONNX multi-device proposal, operator-group rules: unary elementwise ops
+  (Erf among them) accept any input sharding, so GeLU commutes with the column
+  split; MatMul with a sharded K axis yields a partial sum.
+
+GeLU is never written out on the pages; the reading taken is the exact form
+x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).  Everything is evaluated in float64
+on the exact values of the (bf16 or fp32) inputs; Y is not rounded.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+from .layout import _as_numpy
+
+GELU_NONE = 0
+GELU_ERF = 1
+
+
+def gelu(x):
+    """x * Phi(x) with Phi the standard normal CDF, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def _f64(t):
+    return _as_numpy(t).astype(np.float64)
+
+
+def mlp_rank(X, A_i, B_i, act=GELU_ERF):
+    """Z_i = act(X A_i) B_i: one rank's fp64 partial output [M, H]."""
+    x, a, b = _f64(X), _f64(A_i), _f64(B_i)
+    if x.shape[1] != a.shape[0] or a.shape[1] != b.shape[0]:
+        raise ValueError("shape mismatch")
+    y = x @ a
+    if act == GELU_ERF:
+        y = gelu(y)
+    return y @ b
+
+
+def mlp_all_ranks(X, A_shards, B_shards, act=GELU_ERF):
+    """Z = sum over ranks i of act(X A_i) B_i (the all-reduced output)."""
+    if len(A_shards) != len(B_shards):
+        raise ValueError("need one B_i per A_i")
+    acc = None
+    for a, b in zip(A_shards, B_shards):
+        z = mlp_rank(X, a, b, act)
+        acc = z if acc is None else acc + z
+    return acc
+
+
+def mlp_unsharded(X, A, B, act=GELU_ERF):
+    """act(X A) B with the full weights: what the sharded sum must equal."""
+    return mlp_rank(X, A, B, act)
+
+
+def mlp_rank_rows(X, A_i, B_i, rows, act=GELU_ERF):
+    """Rows ``rows`` of mlp_rank, computed from those rows of X only.
+
+    Each output row depends on its own row of X alone (the row-chunk
+    independence the Domino article relies on), so a row sample of a large
+    problem is exact, not an approximation.
+    """
+    x = _f64(X)[np.asarray(rows, dtype=np.int64)]
+    return mlp_rank(x, A_i, B_i, act)

@@ -1,0 +1,116 @@
+"""Plant plausible mistakes in the oracle (on the CPU only) and check that the
+pins catch each one.  This shows the pins constrain the oracle rather than
+restate it."""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import erf
+
+import test_oracle_layout as TL
+import test_oracle_mlp as TM
+import test_oracle_reduce as TR
+from oracle import layout as L
+from oracle import mlp as O
+from oracle import reduce as R
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def test_gelu_dropped_term(monkeypatch):
+    monkeypatch.setattr(O, "gelu", lambda x: 0.5 * np.asarray(x, float) * erf(np.asarray(x, float) / math.sqrt(2)))
+    assert _fails(TM.test_gelu_closed_forms)
+
+
+def test_gelu_wrong_sign(monkeypatch):
+    monkeypatch.setattr(O, "gelu", lambda x: 0.5 * np.asarray(x, float) * (1 - erf(np.asarray(x, float) / math.sqrt(2))))
+    assert _fails(TM.test_brute_force_tiny_shapes, O.GELU_ERF)
+
+
+def test_gelu_wrong_scale(monkeypatch):
+    monkeypatch.setattr(O, "gelu", lambda x: 0.5 * np.asarray(x, float) * (1 + erf(np.asarray(x, float))))
+    assert _fails(TM.test_gelu_closed_forms)
+
+
+def test_mlp_transposed_second_operand(monkeypatch):
+    real = O.mlp_rank
+
+    def bad(X, A_i, B_i, act=O.GELU_ERF):
+        x, a, b = O._f64(X), O._f64(A_i), O._f64(B_i)
+        y = x @ a
+        y = O.gelu(y) if act == O.GELU_ERF else y
+        return y @ b.T if b.shape[0] == b.shape[1] else y @ b
+    monkeypatch.setattr(O, "mlp_rank", bad)
+    assert _fails(TM.test_brute_force_tiny_shapes, O.GELU_NONE)
+    monkeypatch.setattr(O, "mlp_rank", real)
+
+
+def test_mlp_activation_after_second_gemm(monkeypatch):
+    def bad(X, A_i, B_i, act=O.GELU_ERF):
+        z = O._f64(X) @ O._f64(A_i) @ O._f64(B_i)
+        return O.gelu(z) if act == O.GELU_ERF else z
+    monkeypatch.setattr(O, "mlp_rank", bad)
+    assert _fails(TM.test_brute_force_tiny_shapes, O.GELU_ERF)
+
+
+def test_split_inner_axis_outermost(monkeypatch):
+    real = L.shard_boxes
+
+    def bad(shape, spec):
+        boxes, groups = real(shape, spec)
+        m = len(spec.get("sharded_dim", []))
+        if m == 2:  # enumerate b-outer / a-inner instead
+            n0 = spec["sharded_dim"][0].get("num_shards") or spec["sharded_dim"][0]["simple_sharding"][0]["num_shards"]
+            n1 = len(boxes) // n0
+            boxes = [boxes[s0 * n1 + s1] for s1 in range(n1) for s0 in range(n0)]
+        return boxes, groups
+    monkeypatch.setattr(L, "shard_boxes", bad)
+    case = [c for c in TL._load()["cases"] if c["name"] == "E3_both_axes"][0]
+    assert _fails(TL.test_page_examples, case)
+
+
+def test_split_device_keys_swapped(monkeypatch):
+    real = L.expand_devices
+    monkeypatch.setattr(L, "expand_devices", lambda spec: list(reversed(real(spec))))
+    case = [c for c in TL._load()["cases"] if c["name"] == "E5_mixed_split_broadcast"][0]
+    assert _fails(TL.test_page_examples, case)
+
+
+def test_split_off_by_one_width(monkeypatch):
+    real = L.shard_boxes
+
+    def bad(shape, spec):
+        boxes, groups = real(shape, spec)
+        return [tuple((a, b) if b - a == s else (a, min(b + 1, s)) for (a, b), s in zip(box, shape))
+                for box in boxes], groups
+    monkeypatch.setattr(L, "shard_boxes", bad)
+    assert _fails(TL.test_brute_force_against_inverse_formula, False)
+
+
+def test_mesh_wrong_dim_used(monkeypatch):
+    real = L.split_dims_mapping
+
+    def bad(tensor, mesh_dims, process_ids, dims_mapping):
+        q = len(mesh_dims)
+        return real(tensor, mesh_dims, process_ids, [(q - 1 - j) if j >= 0 else j for j in dims_mapping])
+    monkeypatch.setattr(L, "split_dims_mapping", bad)
+    case = TL._load()["mesh_cases"][0]
+    assert _fails(TL.test_page_2d_sbp_example, case)
+
+
+def test_reduce_drops_last_partial(monkeypatch):
+    real = R.reduce_full
+    monkeypatch.setattr(R, "reduce_full", lambda parts: real(list(parts)[:-1]) if len(parts) > 1 else real(parts))
+    assert _fails(TR.test_integer_partials_exact)
+
+
+def test_reduce_split_wrong_block(monkeypatch):
+    real = R.reduce_split
+    monkeypatch.setattr(R, "reduce_split", lambda parts, s: list(reversed(real(parts, s))))
+    assert _fails(TR.test_split_blocks_concatenate_to_full)

@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's tensor-parallel MLP share and its layout kernels
+on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input.
+Default workload (GPT-2-small MLP at TP=4, 4096 tokens): cut this rank's
+A_i/B_i out of the full weights (split along columns / rows into 4 shards
+each), run GEMM1 + GeLU and GEMM2 on the compute stream, and sum the 4 fp32
+partials (this rank's and 3 peers' computed beforehand by the same path) on a
+second stream.  The value is per-rank MLP TFLOP/s (2 GEMMs, 2*M*H*F flops
+each) over the whole step.  Per-kernel durations come from HIP events that
+the library records around each of its launches inside the timed region.
+
+Prints one JSON line (last line of stdout).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sharded_gemm_amd as tp  # noqa: E402
+from sharded_gemm_amd import _abi, inputs  # noqa: E402
+from sharded_gemm_amd.workloads import GPT2_SMALL, GPT3_175B, GPT3_6P7B, RESHARD, TINY  # noqa: E402
+
+METRIC = "per-rank TP-MLP TFLOP/s (% bf16 MFMA peak) + shard/reduce GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+# --------------------------------------------------------------------------- workloads
+
+class MlpStep:
+    """Per-rank MLP step, optionally preceded by cutting the weights."""
+
+    def __init__(self, w, split_weights: bool):
+        self.w = w
+        dev = "cuda"
+        dt = "bf16" if w.dtype == "bf16" else "f32"
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        gen_dev = "cuda" if w.cfg in (3, 5) else "cpu"
+        self.X = inputs.normal((w.M, w.H), inputs.seed_for(w.cfg, inputs.SLOT_X), w.std_x, dt, gen_dev).to(dev)
+        self.split = split_weights
+        if split_weights:
+            self.A = inputs.normal((w.H, w.P * w.F), inputs.seed_for(w.cfg, inputs.SLOT_A), w.std_a, dt).to(dev)
+            self.B = inputs.normal((w.P * w.F, w.H), inputs.seed_for(w.cfg, inputs.SLOT_B), w.std_b, dt).to(dev)
+            self.sa = {"device": list(range(w.P)), "sharded_dim": [{"axis": 1, "num_shards": w.P}]}
+            self.sb = {"device": list(range(w.P)), "sharded_dim": [{"axis": 0, "num_shards": w.P}]}
+            self.As = {d: torch.empty((w.H, w.F), dtype=tdt, device=dev) for d in range(w.P)}
+            self.Bs = {d: torch.empty((w.F, w.H), dtype=tdt, device=dev) for d in range(w.P)}
+            tp.tp_shard_materialize(self.A, self.sa, self.As)
+            tp.tp_shard_materialize(self.B, self.sb, self.Bs)
+        else:
+            self.As = {i: inputs.normal((w.H, w.F), inputs.seed_for(w.cfg, inputs.SLOT_A_SHARD + i), w.std_a, dt,
+                                        gen_dev).to(dev) for i in range(w.P)}
+            self.Bs = {i: inputs.normal((w.F, w.H), inputs.seed_for(w.cfg, inputs.SLOT_B_SHARD + i), w.std_b, dt,
+                                        gen_dev).to(dev) for i in range(w.P)}
+        self.Y = torch.empty((w.M, w.F), dtype=tdt, device=dev)
+        self.Z = torch.empty((w.M, w.H), device=dev)
+        self.Zo = torch.empty((w.M, w.H), device=dev)
+        # peers' partials: computed once, untimed, by the same path
+        self.peers = []
+        for i in range(1, w.P):
+            z = torch.empty((w.M, w.H), device=dev)
+            tp.tp_colrow_mlp(self.X, self.As[i], self.Bs[i], self.Y, z, row_chunks=w.R, col_chunks=w.C)
+            self.peers.append(z)
+        torch.cuda.synchronize()
+        self.s0 = torch.cuda.current_stream()
+        self.s1 = torch.cuda.Stream()
+
+    def step(self):
+        if self.split:
+            tp.tp_shard_materialize(self.A, self.sa, self.As, stream=self.s0)
+            tp.tp_shard_materialize(self.B, self.sb, self.Bs, stream=self.s0)
+        tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
+                         col_chunks=self.w.C, peer_partials=self.peers, Z_out=self.Zo,
+                         s_compute=self.s0, s_reduce=self.s1)
+
+    @property
+    def work(self):
+        return float(self.w.flops_per_rank)
+
+    unit = "TFLOP/s"
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name, "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F, "tp": w.P,
+                "row_chunks": w.R, "col_chunks": w.C, "weights_cut_each_step": self.split,
+                "peers": "virtual ranks 1..P-1, partials precomputed by the same path"}
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on this step (sampled rows for the large shapes), fp64."""
+        from threadpoolctl import threadpool_info
+        from oracle import layout as L
+        from oracle import mlp as O
+        from oracle import reduce as R
+        w = self.w
+        Xc = self.X.cpu()
+        A0, B0 = self.As[0].cpu(), self.Bs[0].cpu()
+        rows = w.M if w.M * w.H * w.F <= 4096 * 768 * 768 else 256
+        sample_rows = np.linspace(0, w.M - 1, rows).astype(np.int64)
+        peers = [inputs.normal((rows, w.H), 99000 + p) for p in range(w.P - 1)]
+        Ac = self.A.cpu() if self.split else None
+        Bc = self.B.cpu() if self.split else None
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            if self.split:
+                L.split(Ac, self.sa)
+                L.split(Bc, self.sb)
+            z = O.mlp_rank_rows(Xc, A0, B0, sample_rows)
+            R.reduce_full([z] + peers)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        flops = 4.0 * rows * w.H * w.F
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": (f"{rows} of {w.M} token rows of the per-rank MLP (fp64, numpy BLAS), "
+                           f"{'plus cutting the full weights into shards, ' if self.split else ''}"
+                           f"plus the {w.P}-way partial sum of those rows; {reps} repetitions, "
+                           f"{dt * 1e3:.1f} ms each; host {platform.processor() or platform.machine()}, "
+                           f"os.cpu_count()={os.cpu_count()}")}
+
+
+class ReshardStep:
+    """The 2x4-mesh layout workload: fused split+replicate, then split reduce."""
+
+    def __init__(self, w):
+        self.w = w
+        self.src = inputs.normal(w.src_shape, inputs.seed_for(4, inputs.SLOT_LAYOUT), device="cuda")
+        self.spec = {"device": [-(k + 1) for k in range(8)],
+                     "device_map": {-(k + 1): [2 * k, 2 * k + 1] for k in range(8)},
+                     "sharded_dim": [{"axis": 0, "num_shards": 2}, {"axis": 2, "num_shards": 4}]}
+        self.dst = {d: torch.empty((4, 2048, 2048), device="cuda") for d in range(16)}
+        self.parts = [inputs.normal(w.partial_shape, inputs.seed_for(4, inputs.SLOT_PARTIAL + p), device="cuda")
+                      for p in range(w.num_partials)]
+        rows = w.partial_shape[0] // w.num_splits
+        self.outs = [torch.empty((rows, w.partial_shape[1]), device="cuda") for _ in range(w.num_splits)]
+        self.s0 = torch.cuda.current_stream()
+
+    def step(self):
+        tp.tp_shard_materialize(self.src, self.spec, self.dst, stream=self.s0)
+        tp.tp_partial_reduce(self.parts, self.outs, tp.TP_REDUCE_SPLIT, stream=self.s0)
+
+    @property
+    def work(self):
+        src = self.src.numel() * 4
+        parts = sum(p.numel() for p in self.parts) * 4
+        return float(src + 2 * src + parts + parts / self.w.num_partials)
+
+    unit = "GB/s"
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name, "src_shape": list(w.src_shape), "mesh": list(w.mesh_shape),
+                "dims_mapping": list(w.dims_mapping), "replicas": w.group_size,
+                "partials": w.num_partials, "partial_shape": list(w.partial_shape), "splits": w.num_splits}
+
+    def cpu_baseline(self, budget_s):
+        from oracle import layout as L
+        from oracle import reduce as R
+        w = self.w
+        rows = 256   # a row sample of every tensor (the full 2.5 GiB would take minutes)
+        src = self.src[:, :rows // 8].cpu()
+        parts = [p[:rows].cpu() for p in self.parts]
+        spec = {"device": self.spec["device"], "device_map": self.spec["device_map"],
+                "sharded_dim": self.spec["sharded_dim"]}
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            L.split(src, spec)
+            R.reduce_split(parts, w.num_splits)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        nbytes = src.numel() * 4 * 3 + sum(p.numel() for p in parts) * 4 * (1 + 1 / w.num_partials)
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{rows // 8} of 2048 S-rows of the source and {rows} of 8192 rows of each partial; "
+                          f"{reps} repetitions"}
+
+
+WORKLOADS = {
+    GPT2_SMALL.name: lambda: MlpStep(GPT2_SMALL, split_weights=True),
+    GPT3_6P7B.name: lambda: MlpStep(GPT3_6P7B, split_weights=False),
+    GPT3_175B.name: lambda: MlpStep(GPT3_175B, split_weights=False),
+    TINY.name: lambda: MlpStep(TINY, split_weights=True),
+    RESHARD.name: lambda: ReshardStep(RESHARD),
+}
+
+
+# --------------------------------------------------------------------------- roofline
+
+def kernel_table(stats, steps):
+    out = {}
+    for name, st in stats.items():
+        if st["launches"] == 0:
+            continue
+        is_gemm = name.startswith("gemm")
+        avg_ms = st["total_ms"] / st["launches"]
+        rate = st["work"] / (st["total_ms"] * 1e-3)
+        out[name] = {"launches_per_step": st["launches"] / steps, "avg_ms": avg_ms,
+                     "ms_per_step": st["total_ms"] / steps,
+                     "achieved": rate / (1e12 if is_gemm else 1e9),
+                     "unit": "TFLOP/s" if is_gemm else "GB/s"}
+    return out
+
+
+def roofline(kernels, dtype):
+    if not kernels:
+        return None
+    name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    k = kernels[name]
+    if k["unit"] == "TFLOP/s":
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+        return {"kernel": name, "bound": "mfma" if dtype == "bf16" else "alu", "achieved": k["achieved"],
+                "peak": peak, "unit": "TFLOP/s", "frac": k["achieved"] / peak, "traffic": None}
+    return {"kernel": name, "bound": "hbm", "achieved": k["achieved"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": k["achieved"] / PEAK_HBM_GBS, "traffic": None}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=GPT2_SMALL.name, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the partial sum over ranks runs over virtual shards on one device).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if not os.path.exists(_abi.LIB_PATH):
+        from sharded_gemm_amd import build
+        build.build()
+    tp.load()
+
+    log(f"[bench] workload {args.workload}: setting up")
+    wl = WORKLOADS[args.workload]()
+    dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    tp.tp_timing_enable(True)
+    tp.tp_timing_read()          # drop warmup records (none expected)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(wl.s0)
+    for _ in range(args.steps):
+        wl.step()
+    stop.record(wl.s0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tp.tp_timing_enable(False)
+    stats = tp.tp_timing_read()
+    gpu_ms = start.elapsed_time(stop)
+    ms_per_step = gpu_ms / args.steps
+
+    # the same steps once more without per-kernel events: their overhead, for the record
+    torch.cuda.synchronize()
+    start.record(wl.s0)
+    for _ in range(args.steps):
+        wl.step()
+    stop.record(wl.s0)
+    torch.cuda.synchronize()
+    ms_no_events = start.elapsed_time(stop) / args.steps
+
+    value = wl.work / (ms_per_step * 1e-3) / (1e12 if wl.unit == "TFLOP/s" else 1e9)
+    kernels = kernel_table(stats, args.steps)
+    for name, k in kernels.items():
+        log(f"[bench] {name:12s} {k['launches_per_step']:.0f}/step  avg {k['avg_ms'] * 1e3:9.1f} us  "
+            f"{k['achieved']:9.1f} {k['unit']}")
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us (without per-kernel events {ms_no_events * 1e3:.1f} us), "
+        f"wall {wall / args.steps * 1e3:.3f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu = wl.cpu_baseline(args.cpu_budget)
+
+    rec = {"metric": METRIC, "value": value, "unit": wl.unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded N(0,1)/N(0,0.02) tensors)",
+           "config": wl.config(), "roofline": roofline(kernels, dtype), "cpu_baseline": cpu,
+           "kernels": kernels, "ms_per_step_without_kernel_events": ms_no_events,
+           "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,238 @@
+/*
+ * tpshard: one rank's share of a column->row tensor-parallel MLP block and the
+ * shard-layout kernels around it, for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI.  Every pointer argument is either a host pointer (specs, shapes,
+ * pointer tables: read during the call only) or a device pointer (tensor data:
+ * caller-owned, e.g. allocated by PyTorch).  The library never allocates device
+ * memory.  Every call validates all of its arguments before it enqueues any
+ * work, so a call that returns an error has left every output untouched.
+ * Work is enqueued asynchronously on the caller's HIP stream(s); results are
+ * valid once those streams have completed.
+ *
+ * Pages cited (by title and section):
+ *   [ONNX]  "ONNX multi-device proposal: tensor- and pipeline-parallel
+ *           annotations based on ShardingSpec" (ONNX 多设备执行提案解析)
+ *   [SBP]   OneFlow global tensor article (placement, SBP, 2D SBP)
+ *   [CAI]   "ColossalAI 1D Tensor Parallelism: principles and Shardformer"
+ *   [SPMD]  Paddle "SPMD derivation rules and pipeline scheduling"
+ *   [DOM]   "DeepSpeed-Domino in depth"
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+/* Every entry point returns TP_OK (0) or one of the negative codes below.   */
+enum {
+  TP_OK = 0,
+  TP_ERR_ARG = -1,         /* null pointer, bad size, bad dtype/mode, aliasing */
+  TP_ERR_SPEC = -2,        /* ill-formed layout (axis range, device counts, map keys) */
+  TP_ERR_INDIVISIBLE = -3, /* a dim is not a multiple of its shard / chunk count */
+  TP_ERR_UNSUPPORTED = -4, /* well-formed but outside what this library does */
+  TP_ERR_HIP = -5          /* a HIP runtime call failed (message has hipGetErrorString) */
+};
+
+/* Message describing the last failing call on the calling thread ("" if none).
+ * The string stays valid until the next call on the same thread. */
+const char *tp_last_error(void);
+
+/* Library version, e.g. "tpshard 0.1 gfx950". */
+const char *tp_version(void);
+
+/* A hipStream_t passed as an opaque pointer; NULL means the null stream. */
+typedef void *tp_stream_t;
+
+/* Element types. */
+enum { TP_F32 = 0, TP_BF16 = 1 };
+
+/* ---- layout description ------------------------------------------------ */
+/* Mirror of ShardingSpecProto / ShardedDimProto / SimpleShardedDimProto
+ * ([ONNX] "Proto definitions").  tensor_name is not needed here.            */
+typedef struct {
+  int64_t dim_value;  /* size of the sharded dim if known; 0 = absent (not checked) */
+  int64_t num_shards; /* >= 1, must divide the dim ([ONNX] "note on divisibility":
+                         the backend decides; this one rejects, TP_ERR_INDIVISIBLE) */
+} tp_simple_sharding;
+
+typedef struct {
+  int64_t axis;                              /* in [-r, r-1]; negative counts from the back */
+  const tp_simple_sharding *simple_sharding; /* exactly 1 entry (else TP_ERR_UNSUPPORTED) */
+  int64_t num_simple_sharding;
+} tp_sharded_dim;
+
+typedef struct {
+  int64_t key;            /* negative: the value that stands for this group in `device` */
+  const int64_t *devices; /* physical device ids (>= 0), in replication order */
+  int64_t num_devices;    /* >= 1 */
+} tp_device_group;
+
+typedef struct {
+  /* device[k] receives shard k: a physical id (>= 0) or a negative key into
+   * device_map whose whole group receives a copy ([ONNX] "Sharding as a
+   * Broadcast", "mixing split and broadcast").  num_device must equal the
+   * product of num_shards over sharded_dim. */
+  const int64_t *device;
+  int64_t num_device;
+  const tp_device_group *device_map; /* = index_to_device_group_map; may be NULL if unused */
+  int64_t num_groups;
+  /* Shards are enumerated with the FIRST listed sharded_dim outermost ([ONNX]
+   * "index rule for multi-axis sharding": axis0 outer, axis1 inner). */
+  const tp_sharded_dim *sharded_dim;
+  int64_t num_sharded_dim; /* 0 = pure replication */
+} tp_sharding_spec;
+
+/* [SPMD] "ProcessMesh": mesh shape and process ids laid out row-major. */
+typedef struct {
+  const int64_t *shape;       /* mesh dims, each >= 1 */
+  int64_t ndim;
+  const int64_t *process_ids; /* prod(shape) distinct ids >= 0 */
+} tp_process_mesh;
+
+enum { TP_LAYOUT_SPEC = 0, TP_LAYOUT_DIMS_MAPPING = 1 };
+
+typedef struct {
+  int32_t kind;          /* TP_LAYOUT_SPEC or TP_LAYOUT_DIMS_MAPPING */
+  tp_sharding_spec spec; /* used when kind == TP_LAYOUT_SPEC */
+  tp_process_mesh mesh;  /* used when kind == TP_LAYOUT_DIMS_MAPPING */
+  /* [SPMD] "dims_mapping": length = tensor rank; dims_mapping[i] = j >= 0 cuts
+   * tensor axis i into mesh.shape[j] blocks, the process at mesh coordinate c
+   * holding block c[j]; -1 keeps axis i whole.  A mesh dim may be used once. */
+  const int64_t *dims_mapping;
+} tp_layout;
+
+/* ---- host-only planning ------------------------------------------------ */
+/*
+ * Normalise a layout of a tensor of shape[ndim] into its list of distinct
+ * shards.  Host only: launches nothing, needs no GPU.
+ *   *num_shards_out     number of distinct shards S
+ *   boxes[s*2*ndim ...] for s < min(S, max_shards): per axis (start, stop)
+ *   shard_of_device[d]  for d < num_dst: the shard device d receives, or -1
+ * boxes and shard_of_device may be NULL.  Under TP_LAYOUT_DIMS_MAPPING the
+ * processes holding the same block form one shard (replicated mesh dims).
+ * Errors: TP_ERR_ARG (null shape/layout, ndim < 0 or > 8, negative dims),
+ *         TP_ERR_SPEC, TP_ERR_INDIVISIBLE, TP_ERR_UNSUPPORTED as above.
+ */
+int tp_layout_plan(const int64_t *shape, int64_t ndim, const tp_layout *layout,
+                   int64_t *num_shards_out, int64_t *boxes, int64_t max_shards,
+                   int64_t *shard_of_device, int64_t num_dst);
+
+/* ---- shard materialisation ------------------------------------------- */
+/*
+ * Split and replicate a row-major tensor src[shape] (dtype TP_F32 or TP_BF16;
+ * bits are copied, never converted) into per-device row-major buffers:
+ * dst[d] receives device d's shard, for every device d named by the layout
+ * ([ONNX] "Sharding as a Split"; [SBP] "SBP": split pieces concatenate back to
+ * the tensor, broadcast pieces equal it; [SPMD] "dims_mapping").  Each shard
+ * is read once and written to every device of its group.
+ *   dst: host array of num_dst device pointers, indexed by physical device
+ *        id; num_dst must exceed every id the layout names; entries of ids the
+ *        layout does not name are ignored (may be NULL); named ones must be
+ *        non-NULL and must not overlap src or each other.
+ * Errors: as tp_layout_plan, plus TP_ERR_ARG for a null src, a bad dtype, a
+ *         too-small num_dst or a NULL dst of a named device; TP_ERR_HIP.
+ */
+int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, int64_t ndim,
+                         const tp_layout *layout, void *const *dst, int64_t num_dst,
+                         tp_stream_t stream);
+
+/* ---- partial-sum reduction ------------------------------------------- */
+enum { TP_REDUCE_FULL = 0, TP_REDUCE_SPLIT = 1 };
+/*
+ * Sum P fp32 partial buffers elementwise ([SBP] "SBP": partial-sum pieces add
+ * up to the tensor; [CAI] section 2.1: the row-parallel output is summed by
+ * one all-reduce; sections 3 and 5.3: reduce-scatter leaves rank j block j).
+ * The sum is taken in fp32 in ascending p: ((p0 + p1) + p2) + ...
+ *   partials: host array of P device pointers, each a [rows, cols] matrix with
+ *             row stride ld_in (elements, >= cols).
+ *   TP_REDUCE_FULL : num_splits must be 1; out[0] is [rows, cols], stride ld_out.
+ *                    out[0] may equal partials[0] (in place); no other overlap.
+ *   TP_REDUCE_SPLIT: num_splits = S must divide rows; out[j] (j < S) receives
+ *                    rows [j*rows/S, (j+1)*rows/S) of the sum, stride ld_out;
+ *                    outputs must not overlap inputs.
+ *   1 <= P <= 64, 1 <= S <= 64; rows, cols >= 0 (0 = nothing to do).
+ * Errors: TP_ERR_ARG, TP_ERR_INDIVISIBLE, TP_ERR_UNSUPPORTED (P or S > 64), TP_ERR_HIP.
+ */
+int tp_partial_reduce(const float *const *partials, int64_t P, int64_t rows, int64_t cols,
+                      int64_t ld_in, int32_t mode, int64_t num_splits, float *const *out,
+                      int64_t ld_out, tp_stream_t stream);
+
+/* ---- one rank's column->row MLP ------------------------------------ */
+enum { TP_ACT_NONE = 0, TP_ACT_GELU_ERF = 1 };
+
+typedef struct {
+  int32_t dtype;     /* TP_BF16: X, A_i, B_i, Y_ws bf16 (fp32 accumulate);
+                        TP_F32 : all fp32 */
+  int32_t act;       /* TP_ACT_GELU_ERF: GeLU(x) = x/2 (1 + erf(x/sqrt 2)) applied to
+                        the fp32 accumulator of X A_i (the pages never define GeLU;
+                        the exact erf form is the reading taken); TP_ACT_NONE */
+  int64_t M, H, F;   /* X[M,H], A_i[H,F], B_i[F,H]; all >= 1 */
+  const void *X;     /* [M, H] row-major, replicated input of every rank */
+  const void *A_i;   /* [H, F] row-major: this rank's column slice of A ([CAI] section 2) */
+  const void *B_i;   /* [F, H] row-major: this rank's row slice of B ([CAI] section 2.1) */
+  void *Y_ws;        /* [M, F] caller-owned workspace; on completion holds
+                        act(X A_i) rounded to dtype (RNE) */
+  float *Z_i;        /* [M, H] fp32: this rank's partial Y B_i (no communication,
+                        [DOM] RowParallelLinearNoComm) */
+  int64_t row_chunks;/* R >= 1, divides M: independent row chunks of X ([DOM] "row-wise
+                        split of inputs X") */
+  int64_t col_chunks;/* C >= 1, divides H: column blocks of B_i ([DOM] "column-wise split
+                        of weights B") */
+  int64_t P;         /* tensor-parallel degree, 1..64; 1 = no reduction */
+  const float *const *peer_partials; /* host array of P-1 device pointers, each [M,H]
+                        fp32: the partials of virtual ranks 1..P-1 */
+  float *Z_out;      /* [M,H] fp32, required when P > 1: Z_i + sum of peers, written
+                        block (r,c) by block on s_reduce; may equal Z_i */
+} tp_mlp_args;
+
+/*
+ * Enqueue one rank's MLP share: for each row chunk r, Y[r] = act(X[r] A_i) on
+ * s_compute; for each column block c, Z_i[r,c] = Y[r] B_i[:,c] on s_compute;
+ * when P > 1, s_reduce waits for block (r,c) and reduces it into Z_out while
+ * s_compute moves on to the next block ([DOM] "forward": the all-reduce of one
+ * micro-batch hides behind the next one's GeMM-GeLU-GeMM).  Before returning,
+ * s_compute is made to wait for s_reduce, so completion of s_compute means the
+ * whole call is done.  s_reduce may equal s_compute (serial schedule).
+ * Chunking never changes a result bit: each output element is accumulated in
+ * the same order whatever R and C are.
+ * Errors: TP_ERR_ARG (null or overlapping buffers, bad dtype/act, sizes < 1,
+ *         P out of range), TP_ERR_INDIVISIBLE (R does not divide M, C does not
+ *         divide H), TP_ERR_HIP.
+ */
+int tp_colrow_mlp(const tp_mlp_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
+
+/* ---- per-kernel timing (measurement support) ---------------------------- */
+/* Kernel families timed by the optional instrumentation below. */
+enum { TP_KERNEL_MATERIALIZE = 0, TP_KERNEL_GEMM1 = 1, TP_KERNEL_GEMM2 = 2, TP_KERNEL_REDUCE = 3,
+       TP_KERNEL_KINDS = 4 };
+
+typedef struct {
+  int64_t launches;  /* kernel launches timed since the last read */
+  double total_ms;   /* sum of their durations (HIP events on the launching stream) */
+  double min_ms, max_ms;
+  double work;       /* algorithmic work of those launches: flops for GEMMs
+                        (2 M N K), bytes for copies and reductions (each input
+                        element read once plus each output element written once) */
+} tp_kernel_stat;
+
+/* Turn per-kernel timing on (1) or off (0) for calls made on the calling
+ * thread.  While on, every kernel the library launches is bracketed by two
+ * timing events recorded on its own stream.  Returns TP_OK. */
+int tp_timing_enable(int32_t on);
+
+/* Wait for every timed launch of the calling thread to finish, fold the
+ * durations into stats[kind] for kind < TP_KERNEL_KINDS (stats must hold
+ * TP_KERNEL_KINDS entries) and reset the counters.
+ * Errors: TP_ERR_ARG (stats NULL), TP_ERR_HIP. */
+int tp_timing_read(tp_kernel_stat *stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

@@ -39,14 +39,21 @@ def _f64(t):
     return _as_numpy(t).astype(np.float64)
 
 
-def mlp_rank(X, A_i, B_i, act=GELU_ERF):
-    """Z_i = act(X A_i) B_i: one rank's fp64 partial output [M, H]."""
-    x, a, b = _f64(X), _f64(A_i), _f64(B_i)
-    if x.shape[1] != a.shape[0] or a.shape[1] != b.shape[0]:
+def hidden(X, A_i, act=GELU_ERF):
+    """Y_i = act(X A_i): the column-parallel output of one rank, fp64 [M, F]."""
+    x, a = _f64(X), _f64(A_i)
+    if x.shape[1] != a.shape[0]:
         raise ValueError("shape mismatch")
     y = x @ a
-    if act == GELU_ERF:
-        y = gelu(y)
+    return gelu(y) if act == GELU_ERF else y
+
+
+def mlp_rank(X, A_i, B_i, act=GELU_ERF):
+    """Z_i = act(X A_i) B_i: one rank's fp64 partial output [M, H]."""
+    b = _f64(B_i)
+    y = hidden(X, A_i, act)
+    if y.shape[1] != b.shape[0]:
+        raise ValueError("shape mismatch")
     return y @ b
 
 

@@ -1,0 +1,305 @@
+"""ctypes binding of libtpshard.so: argument marshalling only.
+
+The functions here carry the C ABI's names (``tp_shard_materialize``,
+``tp_colrow_mlp``, ``tp_partial_reduce``, ``tp_layout_plan``) and do nothing
+but turn Python/torch arguments into the C structures and pointers the
+library takes.  Every step of the path runs in the library's HIP kernels; if
+the library is missing this module raises rather than falling back to
+anything.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtpshard.so")
+
+TP_OK = 0
+TP_ERR_ARG = -1
+TP_ERR_SPEC = -2
+TP_ERR_INDIVISIBLE = -3
+TP_ERR_UNSUPPORTED = -4
+TP_ERR_HIP = -5
+ERROR_NAMES = {TP_ERR_ARG: "arg", TP_ERR_SPEC: "spec", TP_ERR_INDIVISIBLE: "indivisible",
+               TP_ERR_UNSUPPORTED: "unsupported", TP_ERR_HIP: "hip"}
+
+TP_F32 = 0
+TP_BF16 = 1
+TP_LAYOUT_SPEC = 0
+TP_LAYOUT_DIMS_MAPPING = 1
+TP_REDUCE_FULL = 0
+TP_REDUCE_SPLIT = 1
+TP_ACT_NONE = 0
+TP_ACT_GELU_ERF = 1
+
+# Every symbol include/tpshard.h declares.
+EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_shard_materialize",
+           "tp_partial_reduce", "tp_colrow_mlp", "tp_timing_enable", "tp_timing_read")
+
+TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce")
+
+
+class TpError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"tpshard error {code} ({ERROR_NAMES.get(code, '?')}): {msg}")
+        self.code = code
+        self.kind = ERROR_NAMES.get(code, "?")
+
+
+class tp_simple_sharding(C.Structure):
+    _fields_ = [("dim_value", C.c_int64), ("num_shards", C.c_int64)]
+
+
+class tp_sharded_dim(C.Structure):
+    _fields_ = [("axis", C.c_int64), ("simple_sharding", C.POINTER(tp_simple_sharding)),
+                ("num_simple_sharding", C.c_int64)]
+
+
+class tp_device_group(C.Structure):
+    _fields_ = [("key", C.c_int64), ("devices", C.POINTER(C.c_int64)), ("num_devices", C.c_int64)]
+
+
+class tp_sharding_spec(C.Structure):
+    _fields_ = [("device", C.POINTER(C.c_int64)), ("num_device", C.c_int64),
+                ("device_map", C.POINTER(tp_device_group)), ("num_groups", C.c_int64),
+                ("sharded_dim", C.POINTER(tp_sharded_dim)), ("num_sharded_dim", C.c_int64)]
+
+
+class tp_process_mesh(C.Structure):
+    _fields_ = [("shape", C.POINTER(C.c_int64)), ("ndim", C.c_int64), ("process_ids", C.POINTER(C.c_int64))]
+
+
+class tp_layout(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("spec", tp_sharding_spec), ("mesh", tp_process_mesh),
+                ("dims_mapping", C.POINTER(C.c_int64))]
+
+
+class tp_mlp_args(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("act", C.c_int32),
+                ("M", C.c_int64), ("H", C.c_int64), ("F", C.c_int64),
+                ("X", C.c_void_p), ("A_i", C.c_void_p), ("B_i", C.c_void_p),
+                ("Y_ws", C.c_void_p), ("Z_i", C.c_void_p),
+                ("row_chunks", C.c_int64), ("col_chunks", C.c_int64), ("P", C.c_int64),
+                ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p)]
+
+
+class tp_kernel_stat(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("min_ms", C.c_double),
+                ("max_ms", C.c_double), ("work", C.c_double)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sharded_gemm_amd.build` "
+                           "(there is no fallback path)")
+    lib = C.CDLL(path)
+    i64p = C.POINTER(C.c_int64)
+    lib.tp_last_error.restype = C.c_char_p
+    lib.tp_last_error.argtypes = []
+    lib.tp_version.restype = C.c_char_p
+    lib.tp_version.argtypes = []
+    lib.tp_layout_plan.restype = C.c_int
+    lib.tp_layout_plan.argtypes = [i64p, C.c_int64, C.POINTER(tp_layout), i64p, i64p, C.c_int64, i64p, C.c_int64]
+    lib.tp_shard_materialize.restype = C.c_int
+    lib.tp_shard_materialize.argtypes = [C.c_void_p, C.c_int32, i64p, C.c_int64, C.POINTER(tp_layout),
+                                         C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
+    lib.tp_partial_reduce.restype = C.c_int
+    lib.tp_partial_reduce.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                      C.c_int32, C.c_int64, C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
+    lib.tp_colrow_mlp.restype = C.c_int
+    lib.tp_colrow_mlp.argtypes = [C.POINTER(tp_mlp_args), C.c_void_p, C.c_void_p]
+    lib.tp_timing_enable.restype = C.c_int
+    lib.tp_timing_enable.argtypes = [C.c_int32]
+    lib.tp_timing_read.restype = C.c_int
+    lib.tp_timing_read.argtypes = [C.POINTER(tp_kernel_stat)]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != TP_OK:
+        raise TpError(rc, load().tp_last_error().decode())
+
+
+def _i64_array(vals):
+    vals = [int(v) for v in vals]
+    return (C.c_int64 * max(1, len(vals)))(*vals)
+
+
+def make_layout(layout: dict):
+    """Build a ``tp_layout`` from a dict.  Returns ``(struct, keepalive)``.
+
+    ShardingSpec form::   {"device": [...], "device_map": {-1: [...]},
+                           "sharded_dim": [{"axis": a, "num_shards": n, "dim_value": d}
+                                           or {"axis": a, "simple_sharding": [{...}, ...]}]}
+    Mesh form::           {"mesh_shape": [...], "process_ids": [...], "dims_mapping": [...]}
+    """
+    keep = []
+    lay = tp_layout()
+    if "dims_mapping" in layout:
+        lay.kind = TP_LAYOUT_DIMS_MAPPING
+        shp = _i64_array(layout["mesh_shape"])
+        ids = _i64_array(layout["process_ids"])
+        dm = _i64_array(layout["dims_mapping"])
+        keep += [shp, ids, dm]
+        lay.mesh = tp_process_mesh(C.cast(shp, C.POINTER(C.c_int64)), len(layout["mesh_shape"]),
+                                   C.cast(ids, C.POINTER(C.c_int64)))
+        lay.dims_mapping = C.cast(dm, C.POINTER(C.c_int64))
+        return lay, keep
+    lay.kind = TP_LAYOUT_SPEC
+    dev = _i64_array(layout.get("device", []))
+    keep.append(dev)
+    groups = list(layout.get("device_map", {}).items())
+    garr = (tp_device_group * max(1, len(groups)))()
+    for g, (key, ids) in enumerate(groups):
+        arr = _i64_array(ids)
+        keep.append(arr)
+        garr[g] = tp_device_group(int(key), C.cast(arr, C.POINTER(C.c_int64)), len(ids))
+    keep.append(garr)
+    sds = list(layout.get("sharded_dim", []))
+    sarr = (tp_sharded_dim * max(1, len(sds)))()
+    for m, sd in enumerate(sds):
+        ss = sd["simple_sharding"] if "simple_sharding" in sd else [
+            {"num_shards": sd["num_shards"], "dim_value": sd.get("dim_value", 0)}]
+        ssarr = (tp_simple_sharding * max(1, len(ss)))()
+        for q, e in enumerate(ss):
+            ssarr[q] = tp_simple_sharding(int(e.get("dim_value", 0) or 0), int(e["num_shards"]))
+        keep.append(ssarr)
+        sarr[m] = tp_sharded_dim(int(sd["axis"]), C.cast(ssarr, C.POINTER(tp_simple_sharding)), len(ss))
+    keep.append(sarr)
+    lay.spec = tp_sharding_spec(C.cast(dev, C.POINTER(C.c_int64)), len(layout.get("device", [])),
+                                C.cast(garr, C.POINTER(tp_device_group)), len(groups),
+                                C.cast(sarr, C.POINTER(tp_sharded_dim)), len(sds))
+    return lay, keep
+
+
+def tp_layout_plan(shape, layout: dict, num_dst: int = 0, max_shards: int = 4096):
+    """Host-only plan: ``(num_shards, boxes[k][axis] = (start, stop), shard_of_device)``."""
+    lib = load()
+    lay, keep = make_layout(layout)
+    shp = _i64_array(shape)
+    ndim = len(shape)
+    n = C.c_int64(0)
+    boxes = (C.c_int64 * max(1, max_shards * 2 * max(ndim, 1)))()
+    sod = (C.c_int64 * max(1, num_dst))()
+    _check(lib.tp_layout_plan(C.cast(shp, C.POINTER(C.c_int64)), ndim, C.byref(lay), C.byref(n),
+                              C.cast(boxes, C.POINTER(C.c_int64)), max_shards,
+                              C.cast(sod, C.POINTER(C.c_int64)), num_dst))
+    k = min(n.value, max_shards)
+    out_boxes = [[(boxes[(s * ndim + i) * 2], boxes[(s * ndim + i) * 2 + 1]) for i in range(ndim)]
+                 for s in range(k)]
+    return n.value, out_boxes, [sod[d] for d in range(num_dst)]
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return TP_F32
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def tp_shard_materialize(src, layout: dict, dst, stream=None):
+    """Split/replicate ``src`` into ``dst`` (dict or list: device id -> tensor)."""
+    lib = load()
+    lay, keep = make_layout(layout)
+    items = dst.items() if isinstance(dst, dict) else enumerate(dst)
+    items = list(items)
+    num_dst = (max(d for d, _ in items) + 1) if items else 0
+    ptrs = (C.c_void_p * max(1, num_dst))()
+    for d, t in items:
+        ptrs[d] = _ptr(t) if t is not None else None
+    shp = _i64_array(src.shape)
+    _check(lib.tp_shard_materialize(C.c_void_p(_ptr(src)), _dtype_code(src), C.cast(shp, C.POINTER(C.c_int64)),
+                                    src.dim(), C.byref(lay), C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst,
+                                    _stream_ptr(stream)))
+
+
+def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, ld_in=None, ld_out=None,
+                      stream=None):
+    """Sum fp32 ``partials`` (list of tensors or raw device pointers) into ``out`` (list).
+
+    With tensors, rows/cols/ld default to the 2-D shape of partials[0]."""
+    lib = load()
+    P = len(partials)
+    t0 = partials[0]
+    is_tensor = hasattr(t0, "data_ptr")
+    if rows is None:
+        rows, cols = int(t0.shape[0]), int(t0.shape[1])
+    if ld_in is None:
+        ld_in = int(t0.stride(0)) if is_tensor else cols
+    if ld_out is None:
+        ld_out = int(out[0].stride(0)) if hasattr(out[0], "data_ptr") else cols
+    pin = (C.c_void_p * P)(*[(p.data_ptr() if hasattr(p, "data_ptr") else p) for p in partials])
+    pout = (C.c_void_p * len(out))(*[(o.data_ptr() if hasattr(o, "data_ptr") else o) for o in out])
+    _check(lib.tp_partial_reduce(C.cast(pin, C.POINTER(C.c_void_p)), P, rows, cols, ld_in, mode, len(out),
+                                 C.cast(pout, C.POINTER(C.c_void_p)), ld_out, _stream_ptr(stream)))
+
+
+def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
+                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None):
+    """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers)."""
+    lib = load()
+    M, H = int(X.shape[0]), int(X.shape[1])
+    F = int(A_i.shape[1])
+    peers = list(peer_partials)
+    if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Y_ws.shape) != (M, F) \
+            or tuple(Z_i.shape) != (M, H):
+        raise ValueError("shapes must be X[M,H], A_i[H,F], B_i[F,H], Y_ws[M,F], Z_i[M,H]")
+    if not (X.dtype == A_i.dtype == B_i.dtype == Y_ws.dtype):
+        raise TypeError("X, A_i, B_i and Y_ws must share one dtype")
+    import torch
+    for t in [Z_i, *peers] + ([Z_out] if Z_out is not None else []):
+        if t.dtype != torch.float32 or tuple(t.shape) != (M, H):
+            raise TypeError("Z_i, peer partials and Z_out must be fp32 [M, H]")
+    parr = (C.c_void_p * max(1, len(peers)))(*[_ptr(p) for p in peers])
+    args = tp_mlp_args(dtype=_dtype_code(X), act=act, M=M, H=H, F=F,
+                       X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
+                       row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
+                       peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
+                       Z_out=_ptr(Z_out))
+    sc = _stream_ptr(s_compute)
+    sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
+    _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
+
+
+def tp_timing_enable(on: bool = True):
+    _check(load().tp_timing_enable(1 if on else 0))
+
+
+def tp_timing_read():
+    """{kernel name: dict(launches, total_ms, min_ms, max_ms, work)} since the last read."""
+    arr = (tp_kernel_stat * len(TP_KERNEL_NAMES))()
+    _check(load().tp_timing_read(C.cast(arr, C.POINTER(tp_kernel_stat))))
+    return {name: dict(launches=arr[k].launches, total_ms=arr[k].total_ms, min_ms=arr[k].min_ms,
+                       max_ms=arr[k].max_ms, work=arr[k].work) for k, name in enumerate(TP_KERNEL_NAMES)}
+
+
+def version() -> str:
+    return load().tp_version().decode()

@@ -1,0 +1,271 @@
+// The C ABI: argument validation, then enqueue.  Every entry point checks all
+// of its arguments before it launches anything, so an error leaves outputs
+// untouched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "gemm.h"
+#include "plan.h"
+#include "shard.h"
+#include "timing.h"
+
+namespace tpshard {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+constexpr int64_t kMaxP = 64;
+constexpr int64_t kMaxSplits = 64;
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Events for the two-stream schedule, kept per device and reused across calls
+// (a stream wait captures the event's state when it is enqueued, so an event
+// may be re-recorded as soon as the wait that consumes it has been enqueued).
+struct EventPool {
+  std::map<int, std::vector<hipEvent_t>> by_device;
+  ~EventPool() {
+    for (auto& kv : by_device)
+      for (hipEvent_t e : kv.second) (void)hipEventDestroy(e);
+  }
+};
+thread_local EventPool g_events;
+
+int get_events(size_t n, hipEvent_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  auto& v = g_events.by_device[dev];
+  while (v.size() < n) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    v.push_back(ev);
+  }
+  *out = v.data();
+  return TP_OK;
+}
+
+int64_t matrix_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((rows - 1) * ld + cols) * esize;
+}
+
+}  // namespace
+
+}  // namespace tpshard
+
+using namespace tpshard;
+
+extern "C" {
+
+const char *tp_last_error(void) { return g_last_error.c_str(); }
+
+const char *tp_version(void) { return "tpshard 0.1 gfx950"; }
+
+int tp_layout_plan(const int64_t *shape, int64_t ndim, const tp_layout *layout, int64_t *num_shards_out,
+                   int64_t *boxes, int64_t max_shards, int64_t *shard_of_device, int64_t num_dst) {
+  clear_error();
+  if (!num_shards_out) return fail(TP_ERR_ARG, "num_shards_out is NULL");
+  if (max_shards < 0 || num_dst < 0) return fail(TP_ERR_ARG, "negative output capacity");
+  ShardPlan plan;
+  const int rc = build_plan(shape, ndim, layout, &plan);
+  if (rc != TP_OK) return rc;
+  *num_shards_out = plan.nshards();
+  if (boxes) {
+    const int64_t n = std::min(max_shards, plan.nshards());
+    for (int64_t k = 0; k < n; ++k)
+      for (int i = 0; i < plan.ndim; ++i) {
+        boxes[(k * plan.ndim + i) * 2] = plan.offset[k * plan.ndim + i];
+        boxes[(k * plan.ndim + i) * 2 + 1] = plan.offset[k * plan.ndim + i] + plan.extent[i];
+      }
+  }
+  if (shard_of_device) {
+    for (int64_t d = 0; d < num_dst; ++d) shard_of_device[d] = -1;
+    for (int64_t k = 0; k < plan.nshards(); ++k)
+      for (int64_t d : plan.devices[k])
+        if (d < num_dst) shard_of_device[d] = k;
+  }
+  return TP_OK;
+}
+
+int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, int64_t ndim,
+                         const tp_layout *layout, void *const *dst, int64_t num_dst, tp_stream_t stream) {
+  clear_error();
+  const int64_t esize = dtype_size(dtype);
+  if (!esize) return fail(TP_ERR_ARG, "unknown dtype %d", dtype);
+  ShardPlan plan;
+  int rc = build_plan(shape, ndim, layout, &plan);
+  if (rc != TP_OK) return rc;
+  int64_t numel = 1, shard_elems = 1;
+  for (int i = 0; i < plan.ndim; ++i) {
+    numel *= plan.shape[i];
+    shard_elems *= plan.extent[i];
+  }
+  if (!src && numel > 0) return fail(TP_ERR_ARG, "src is NULL");
+  if (plan.max_device >= num_dst)
+    return fail(TP_ERR_ARG, "num_dst = %lld but the layout names device %lld", (long long)num_dst, (long long)plan.max_device);
+  if (plan.max_device >= 0 && !dst) return fail(TP_ERR_ARG, "dst is NULL");
+  std::vector<int64_t> named;
+  for (const auto& grp : plan.devices)
+    for (int64_t d : grp) {
+      if (!dst[d] && shard_elems > 0) return fail(TP_ERR_ARG, "dst[%lld] is NULL", (long long)d);
+      named.push_back(d);
+    }
+  const int64_t src_bytes = numel * esize, shard_bytes = shard_elems * esize;
+  for (size_t i = 0; i < named.size(); ++i) {
+    if (overlaps(dst[named[i]], shard_bytes, src, src_bytes))
+      return fail(TP_ERR_ARG, "dst[%lld] overlaps src", (long long)named[i]);
+    for (size_t j = 0; j < i; ++j)
+      if (overlaps(dst[named[i]], shard_bytes, dst[named[j]], shard_bytes))
+        return fail(TP_ERR_ARG, "dst[%lld] overlaps dst[%lld]", (long long)named[i], (long long)named[j]);
+  }
+  return shard_materialize_launch(plan, src, esize, dst, static_cast<hipStream_t>(stream));
+}
+
+int tp_partial_reduce(const float *const *partials, int64_t P, int64_t rows, int64_t cols, int64_t ld_in,
+                      int32_t mode, int64_t num_splits, float *const *out, int64_t ld_out, tp_stream_t stream) {
+  clear_error();
+  if (P < 1) return fail(TP_ERR_ARG, "P = %lld < 1", (long long)P);
+  if (P > kMaxP) return fail(TP_ERR_UNSUPPORTED, "P = %lld > %lld", (long long)P, (long long)kMaxP);
+  if (!partials) return fail(TP_ERR_ARG, "partials is NULL");
+  if (rows < 0 || cols < 0) return fail(TP_ERR_ARG, "negative size");
+  if (ld_in < cols || ld_out < cols || ld_in < 1 || ld_out < 1) return fail(TP_ERR_ARG, "row stride smaller than cols");
+  if (mode != TP_REDUCE_FULL && mode != TP_REDUCE_SPLIT) return fail(TP_ERR_ARG, "unknown mode %d", mode);
+  if (num_splits < 1) return fail(TP_ERR_ARG, "num_splits = %lld < 1", (long long)num_splits);
+  if (mode == TP_REDUCE_FULL && num_splits != 1) return fail(TP_ERR_ARG, "FULL mode needs num_splits = 1");
+  if (num_splits > kMaxSplits) return fail(TP_ERR_UNSUPPORTED, "num_splits = %lld > %lld", (long long)num_splits, (long long)kMaxSplits);
+  if (rows % num_splits) return fail(TP_ERR_INDIVISIBLE, "%lld rows not divisible by %lld splits", (long long)rows, (long long)num_splits);
+  if (!out) return fail(TP_ERR_ARG, "out is NULL");
+  const int64_t rps = rows / num_splits;
+  const int64_t in_bytes = matrix_bytes(rows, cols, ld_in, 4), out_bytes = matrix_bytes(rps, cols, ld_out, 4);
+  for (int64_t p = 0; p < P; ++p)
+    if (!partials[p] && in_bytes) return fail(TP_ERR_ARG, "partials[%lld] is NULL", (long long)p);
+  for (int64_t j = 0; j < num_splits; ++j) {
+    if (!out[j] && out_bytes) return fail(TP_ERR_ARG, "out[%lld] is NULL", (long long)j);
+    for (int64_t p = 0; p < P; ++p) {
+      const bool in_place = mode == TP_REDUCE_FULL && p == 0 && out[j] == partials[0] && ld_out == ld_in;
+      if (!in_place && overlaps(out[j], out_bytes, partials[p], in_bytes))
+        return fail(TP_ERR_ARG, "out[%lld] overlaps partials[%lld]", (long long)j, (long long)p);
+    }
+    for (int64_t i = 0; i < j; ++i)
+      if (overlaps(out[j], out_bytes, out[i], out_bytes)) return fail(TP_ERR_ARG, "out[%lld] overlaps out[%lld]", (long long)j, (long long)i);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t t0 = timing_begin(s);
+  const int rc = partial_reduce_launch(partials, static_cast<int>(P), rows, cols, ld_in, out,
+                                       static_cast<int>(num_splits), rps, ld_out, s);
+  if (rc == TP_OK) timing_end(t0, s, TP_KERNEL_REDUCE, 4.0 * (P + 1) * rows * cols);
+  return rc;
+}
+
+int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_reduce) {
+  clear_error();
+  if (!a) return fail(TP_ERR_ARG, "args is NULL");
+  const int64_t es = dtype_size(a->dtype);
+  if (!es) return fail(TP_ERR_ARG, "unknown dtype %d", a->dtype);
+  if (a->act != TP_ACT_NONE && a->act != TP_ACT_GELU_ERF) return fail(TP_ERR_ARG, "unknown act %d", a->act);
+  if (a->M < 1 || a->H < 1 || a->F < 1) return fail(TP_ERR_ARG, "M, H, F must be >= 1");
+  if (!a->X || !a->A_i || !a->B_i || !a->Y_ws || !a->Z_i) return fail(TP_ERR_ARG, "X, A_i, B_i, Y_ws and Z_i must be non-NULL");
+  if (a->row_chunks < 1 || a->col_chunks < 1) return fail(TP_ERR_ARG, "row_chunks and col_chunks must be >= 1");
+  if (a->M % a->row_chunks) return fail(TP_ERR_INDIVISIBLE, "row_chunks %lld does not divide M = %lld", (long long)a->row_chunks, (long long)a->M);
+  if (a->H % a->col_chunks) return fail(TP_ERR_INDIVISIBLE, "col_chunks %lld does not divide H = %lld", (long long)a->col_chunks, (long long)a->H);
+  if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
+  if (a->P > 1 && (!a->peer_partials || !a->Z_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out");
+  const int64_t M = a->M, H = a->H, F = a->F;
+  if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
+      (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
+    return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
+  const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
+  struct Buf { const void *p; int64_t n; const char *name; };
+  std::vector<Buf> ins = {{a->X, bx, "X"}, {a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
+  for (int64_t p = 1; p < a->P; ++p) {
+    if (!a->peer_partials[p - 1]) return fail(TP_ERR_ARG, "peer_partials[%lld] is NULL", (long long)(p - 1));
+    ins.push_back({a->peer_partials[p - 1], bz, "peer partial"});
+  }
+  std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
+  if (a->P > 1 && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Buf& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, in.name);
+    for (size_t j = 0; j < i; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+
+  hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
+  const bool two = (s0 != s1) && a->P > 1;
+  const int64_t R = a->row_chunks, C = a->col_chunks, Mr = M / R, Hc = H / C;
+  hipEvent_t *ev = nullptr;
+  if (two) {
+    const int rc = get_events(static_cast<size_t>(R * C + 1), &ev);
+    if (rc != TP_OK) return rc;
+  }
+  const bool bf16 = a->dtype == TP_BF16;
+  const int epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? kEpiGeluBf16 : kEpiIdentBf16)
+                        : (a->act == TP_ACT_GELU_ERF ? kEpiGeluF32 : kEpiPlainF32);
+  const int epi2 = bf16 ? kEpiF32 : kEpiPlainF32;
+  std::vector<const float *> parts(static_cast<size_t>(a->P));
+  for (int64_t r = 0; r < R; ++r) {
+    GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
+                static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
+    hipEvent_t t0 = timing_begin(s0);
+    hipError_t e = gemm_launch(g1, epi1, s0);
+    if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
+    timing_end(t0, s0, TP_KERNEL_GEMM1, 2.0 * Mr * F * H);
+    for (int64_t c = 0; c < C; ++c) {
+      const int64_t zoff = r * Mr * H + c * Hc;
+      GemmArgs g2{static_cast<const char *>(a->Y_ws) + r * Mr * F * es, static_cast<const char *>(a->B_i) + c * Hc * es,
+                  a->Z_i + zoff, Mr, Hc, F, F, H, H};
+      t0 = timing_begin(s0);
+      e = gemm_launch(g2, epi2, s0);
+      if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+      timing_end(t0, s0, TP_KERNEL_GEMM2, 2.0 * Mr * Hc * F);
+      if (a->P == 1) continue;
+      hipStream_t sr = s0;
+      if (two) {
+        hipEvent_t done = ev[r * C + c];
+        if ((e = hipEventRecord(done, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = hipStreamWaitEvent(s1, done, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        sr = s1;
+      }
+      parts[0] = a->Z_i + zoff;
+      for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_partials[p - 1] + zoff;
+      float *dst = a->Z_out + zoff;
+      hipEvent_t t1 = timing_begin(sr);
+      const int rc = partial_reduce_launch(parts.data(), static_cast<int>(a->P), Mr, Hc, H, &dst, 1, Mr, H, sr);
+      if (rc != TP_OK) return rc;
+      timing_end(t1, sr, TP_KERNEL_REDUCE, 4.0 * (a->P + 1) * Mr * Hc);
+    }
+  }
+  if (two) {
+    hipEvent_t joined = ev[R * C];
+    hipError_t e;
+    if ((e = hipEventRecord(joined, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s0, joined, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  return TP_OK;
+}
+
+}  // extern "C"

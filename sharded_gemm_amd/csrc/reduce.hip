@@ -1,0 +1,124 @@
+// Partial-sum reduction: out = sum over p of partial_p, fp32, ascending p
+// ([SBP] "SBP": partial-sum pieces add up to the tensor; [CAI] section 2.1:
+// one all-reduce sums the row-parallel partials; sections 3 and 5.3: the
+// reduce-scatter form leaves rank j with row block j).
+//
+// Pure HBM streaming: each lane owns UNROLL output vectors, issues the loads
+// of every partial for all of them before it adds anything (P x UNROLL loads
+// in flight per lane), then adds in ascending p and stores.  Rows may be
+// strided (ld), which is how a column block of a wider matrix is reduced.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "common.h"
+#include "shard.h"
+
+namespace tpshard {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxP = 64;
+constexpr int kMaxOut = 64;
+constexpr int kGroup = 8;   // partials loaded together before adding
+
+struct RedArgs {
+  const float *in[kMaxP];
+  float *out[kMaxOut];
+  int32_t P;
+  uint32_t cols_v;          // vectors per row
+  uint32_t total_v;         // rows * cols_v
+  uint32_t rows_per_out;
+  int64_t ld_in, ld_out;    // elements
+};
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int VW> struct FVec;
+template <> struct FVec<4> { typedef f32x4_t T; };
+template <> struct FVec<1> { typedef float T; };
+
+template <int VW, int UNROLL>
+__global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
+  typedef typename FVec<VW>::T V;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < a.total_v; base += stride * UNROLL) {
+    int64_t in_off[UNROLL];
+    bool ok[UNROLL];
+    uint32_t row[UNROLL], col[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const uint32_t idx = base + u * stride;
+      ok[u] = idx < a.total_v;
+      row[u] = ok[u] ? idx / a.cols_v : 0;
+      col[u] = ok[u] ? idx - row[u] * a.cols_v : 0;
+      in_off[u] = static_cast<int64_t>(row[u]) * a.ld_in + static_cast<int64_t>(col[u]) * VW;
+    }
+    V acc[UNROLL];
+    for (int p0 = 0; p0 < a.P; p0 += kGroup) {
+      V v[kGroup][UNROLL];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+          if (p0 + g < a.P && ok[u]) v[g][u] = *reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+          if (p0 + g < a.P) acc[u] = (p0 + g == 0) ? v[g][u] : acc[u] + v[g][u];
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      if (!ok[u]) continue;
+      const uint32_t j = row[u] / a.rows_per_out;
+      const int64_t r = row[u] - static_cast<int64_t>(j) * a.rows_per_out;
+      float *dst = a.out[j] + r * a.ld_out + static_cast<int64_t>(col[u]) * VW;
+      __builtin_nontemporal_store(acc[u], reinterpret_cast<V *>(dst));
+    }
+  }
+}
+
+}  // namespace
+
+int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
+                          float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
+                          hipStream_t stream) {
+  if (rows == 0 || cols == 0) return TP_OK;
+  RedArgs a{};
+  auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  bool vec = (cols % 4 == 0) && (ld_in % 4 == 0) && (ld_out % 4 == 0);
+  for (int p = 0; p < P; ++p) {
+    a.in[p] = partials[p];
+    vec = vec && al16(partials[p]);
+  }
+  for (int j = 0; j < nout; ++j) {
+    a.out[j] = out[j];
+    vec = vec && al16(out[j]);
+  }
+  const int vw = vec ? 4 : 1;
+  const int64_t cols_v = cols / vw;
+  const int64_t total_v = rows * cols_v;
+  if (total_v >= (int64_t(1) << 31) || rows_per_out >= (int64_t(1) << 31))
+    return fail(TP_ERR_UNSUPPORTED, "reduce of %lld x %lld exceeds the 32-bit index range", (long long)rows, (long long)cols);
+  a.P = P;
+  a.cols_v = static_cast<uint32_t>(cols_v);
+  a.total_v = static_cast<uint32_t>(total_v);
+  a.rows_per_out = static_cast<uint32_t>(rows_per_out);
+  a.ld_in = ld_in;
+  a.ld_out = ld_out;
+  constexpr int kUnroll = 2;
+  const int64_t want = (total_v + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(want, 16384)));
+  if (vec)
+    hipLaunchKernelGGL((reduce_kernel<4, kUnroll>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<1, kUnroll>), grid, dim3(kThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "reduce launch: %s", hipGetErrorString(e));
+  return TP_OK;
+}
+
+}  // namespace tpshard

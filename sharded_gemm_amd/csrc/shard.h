@@ -1,0 +1,24 @@
+// Launch interfaces of the layout and reduction kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace tpshard {
+
+// Copies every shard of `plan` from src into dst[device] for each receiving
+// device.  Arguments already validated.  Returns TP_OK or a negative status.
+int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esize, void *const *dst,
+                             hipStream_t stream);
+
+// out_row_block(row) <- sum over p of partials[p][row, :], ascending p, fp32.
+// rows_per_out rows go to each out[j]; out[j] has row stride ld_out.
+// Arguments already validated (1 <= P <= 64, 1 <= nout <= 64).
+int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
+                          float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
+                          hipStream_t stream);
+
+}  // namespace tpshard

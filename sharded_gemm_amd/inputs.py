@@ -27,15 +27,21 @@ def seed_for(cfg: int, slot: int) -> int:
     return 1000 * int(cfg) + int(slot)
 
 
-def _gen(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def _gen(seed: int, device: str = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return g
 
 
-def normal(shape, seed: int, std: float = 1.0, dtype: str = "f32") -> torch.Tensor:
-    """N(0, std^2) samples drawn in fp32, then rounded (RNE) to ``dtype``."""
-    t = torch.randn(tuple(shape), generator=_gen(seed), dtype=torch.float32)
+def normal(shape, seed: int, std: float = 1.0, dtype: str = "f32", device: str = "cpu") -> torch.Tensor:
+    """N(0, std^2) samples drawn in fp32, then rounded (RNE) to ``dtype``.
+
+    ``device="cuda"`` draws with torch's GPU generator (different numbers for
+    the same seed, still deterministic); used only for large inputs whose CPU
+    draw would be slow.  Copy the result to the host to feed the oracle the
+    same bytes.
+    """
+    t = torch.randn(tuple(shape), generator=_gen(seed, device), dtype=torch.float32, device=device)
     if std != 1.0:
         t.mul_(float(std))
     return t.to(_DTYPES[dtype]).contiguous()

@@ -1,0 +1,209 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol the header declares, plans layouts exactly as the oracle does,
+and rejects bad arguments with the oracle's error kinds before touching HIP."""
+import ctypes as C
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import sharded_gemm_amd as tp
+from sharded_gemm_amd import _abi
+from oracle import layout as L
+
+import test_oracle_layout as TL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _ensure_built():
+    if not os.path.exists(_abi.LIB_PATH):
+        from sharded_gemm_amd import build
+        build.build()
+
+
+def setup_module(_):
+    _ensure_built()
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "tpshard.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    lib = _abi.load()
+    names = _header_functions()
+    assert set(names) == set(_abi.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert tp.version().startswith("tpshard")
+
+
+def _oracle_plan(shape, spec):
+    boxes, groups = L.shard_boxes(shape, spec)
+    return boxes, groups
+
+
+@pytest.mark.parametrize("with_map", [False, True])
+def test_plan_matches_oracle_brute_force(with_map):
+    rnd = random.Random(5 + with_map)
+    for shape, axes, counts in TL._all_cases(max_cases=600, seed=13):
+        nsh = int(np.prod(counts)) if counts else 1
+        if with_map:
+            devs = list(range(2 * nsh))
+            rnd.shuffle(devs)
+            spec = {"device": [-(k + 1) for k in range(nsh)],
+                    "device_map": {-(k + 1): [devs[2 * k], devs[2 * k + 1]] for k in range(nsh)}}
+        else:
+            devs = list(range(nsh))
+            rnd.shuffle(devs)
+            spec = {"device": devs}
+        spec["sharded_dim"] = [{"axis": a - len(shape) if k % 2 else a, "num_shards": n}
+                               for k, (a, n) in enumerate(zip(axes, counts))]
+        boxes, groups = _oracle_plan(shape, spec)
+        ndst = max(max(g) for g in groups) + 2
+        n, cboxes, sod = tp.tp_layout_plan(shape, spec, num_dst=ndst)
+        assert n == len(boxes)
+        assert [tuple(map(tuple, b)) for b in cboxes] == [tuple(b) for b in boxes]
+        for k, grp in enumerate(groups):
+            for d in grp:
+                assert sod[d] == k
+        assert sum(1 for s in sod if s >= 0) == sum(len(g) for g in groups)
+
+
+def test_plan_mesh_matches_oracle():
+    t = np.arange(4 * 6 * 8, dtype=np.float32).reshape(4, 6, 8)
+    for mesh, dm in [([2, 4], [0, -1, 1]), ([2, 2], [1, -1, 0]), ([2, 3], [-1, 1, 0]), ([3, 2], [-1, 0, -1]),
+                     ([2, 2, 2], [2, -1, 0]), ([4], [-1, -1, -1])]:
+        ids = list(range(10, 10 + int(np.prod(mesh))))
+        try:
+            ref = L.split_dims_mapping(t, mesh, ids, dm)
+        except L.OracleLayoutError as e:
+            with pytest.raises(tp.TpError) as ce:
+                tp.tp_layout_plan(t.shape, {"mesh_shape": mesh, "process_ids": ids, "dims_mapping": dm})
+            assert ce.value.kind == e.kind
+            continue
+        n, boxes, sod = tp.tp_layout_plan(t.shape, {"mesh_shape": mesh, "process_ids": ids, "dims_mapping": dm},
+                                          num_dst=max(ids) + 1)
+        for d in ids:
+            box = boxes[sod[d]]
+            assert np.array_equal(t[tuple(slice(a, b) for a, b in box)], ref[d])
+
+
+@pytest.mark.parametrize("spec,shape,kind", TL.test_rejections.pytestmark[0].args[1])
+def test_plan_rejects_like_oracle(spec, shape, kind):
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_layout_plan(shape, spec, num_dst=8)
+    assert e.value.kind == kind
+
+
+@pytest.mark.parametrize("mesh,ids,dm,shape,kind", TL.test_mesh_rejections.pytestmark[0].args[1])
+def test_mesh_rejects_like_oracle(mesh, ids, dm, shape, kind):
+    if len(ids) != int(np.prod(mesh)) or len(dm) != len(shape):
+        pytest.skip("array length is implied by the C arguments")
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_layout_plan(shape, {"mesh_shape": mesh, "process_ids": ids, "dims_mapping": dm})
+    assert e.value.kind == kind
+
+
+# --- argument validation of the launching entry points (returns before any HIP call) ---
+
+FAKE = 1 << 40   # device-looking addresses; never dereferenced on these paths
+
+
+def _mlp_args(**kw):
+    a = _abi.tp_mlp_args(dtype=_abi.TP_BF16, act=_abi.TP_ACT_GELU_ERF, M=64, H=64, F=64,
+                         X=FAKE, A_i=FAKE + (1 << 20), B_i=FAKE + (2 << 20), Y_ws=FAKE + (3 << 20),
+                         Z_i=FAKE + (4 << 20), row_chunks=1, col_chunks=1, P=1, peer_partials=None, Z_out=None)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _abi.TP_ERR_ARG),
+    (dict(act=5), _abi.TP_ERR_ARG),
+    (dict(M=0), _abi.TP_ERR_ARG),
+    (dict(X=None), _abi.TP_ERR_ARG),
+    (dict(row_chunks=3), _abi.TP_ERR_INDIVISIBLE),
+    (dict(col_chunks=5), _abi.TP_ERR_INDIVISIBLE),
+    (dict(row_chunks=0), _abi.TP_ERR_ARG),
+    (dict(P=2), _abi.TP_ERR_ARG),
+    (dict(P=65), _abi.TP_ERR_ARG),
+    (dict(Y_ws=FAKE + 100), _abi.TP_ERR_ARG),          # overlaps X
+    (dict(Z_i=FAKE + (3 << 20) + 64), _abi.TP_ERR_ARG),  # overlaps Y_ws
+])
+def test_mlp_validation(kw, code):
+    lib = _abi.load()
+    a = _mlp_args(**kw)
+    assert lib.tp_colrow_mlp(C.byref(a), None, None) == code
+    assert lib.tp_last_error().decode() != ""
+
+
+def test_mlp_peer_validation():
+    lib = _abi.load()
+    peers = (C.c_void_p * 1)(None)
+    a = _mlp_args(P=2, peer_partials=C.cast(peers, C.POINTER(C.c_void_p)), Z_out=FAKE + (9 << 20))
+    assert lib.tp_colrow_mlp(C.byref(a), None, None) == _abi.TP_ERR_ARG
+    peers[0] = FAKE + (4 << 20) + 8   # overlaps Z_i
+    assert lib.tp_colrow_mlp(C.byref(a), None, None) == _abi.TP_ERR_ARG
+
+
+def _reduce(P=2, rows=8, cols=8, ld_in=8, mode=0, S=1, ld_out=8, parts=None, outs=None):
+    lib = _abi.load()
+    parts = parts if parts is not None else [FAKE + p * (1 << 20) for p in range(P)]
+    outs = outs if outs is not None else [FAKE + (100 << 20) + j * (1 << 20) for j in range(S)]
+    pin = (C.c_void_p * max(1, len(parts)))(*parts)
+    pout = (C.c_void_p * max(1, len(outs)))(*outs)
+    return lib.tp_partial_reduce(C.cast(pin, C.POINTER(C.c_void_p)), P, rows, cols, ld_in, mode, S,
+                                 C.cast(pout, C.POINTER(C.c_void_p)), ld_out, None)
+
+
+def test_reduce_validation():
+    assert _reduce(P=0) == _abi.TP_ERR_ARG
+    assert _reduce(P=65) == _abi.TP_ERR_UNSUPPORTED
+    assert _reduce(ld_in=4) == _abi.TP_ERR_ARG
+    assert _reduce(mode=3) == _abi.TP_ERR_ARG
+    assert _reduce(mode=0, S=2) == _abi.TP_ERR_ARG
+    assert _reduce(mode=1, S=3) == _abi.TP_ERR_INDIVISIBLE
+    assert _reduce(mode=1, S=65, rows=65) == _abi.TP_ERR_UNSUPPORTED
+    assert _reduce(parts=[FAKE, None]) == _abi.TP_ERR_ARG
+    assert _reduce(outs=[FAKE + 16]) == _abi.TP_ERR_ARG        # overlaps partial 0, not in place
+    assert _reduce(mode=1, S=2, outs=[FAKE + (100 << 20), FAKE + (100 << 20) + 32]) == _abi.TP_ERR_ARG
+
+
+def test_materialize_validation():
+    lib = _abi.load()
+    spec = {"device": [0, 1], "sharded_dim": [{"axis": 0, "num_shards": 2}]}
+    lay, keep = _abi.make_layout(spec)
+    shape = (C.c_int64 * 2)(4, 4)
+    good = (C.c_void_p * 2)(FAKE + (1 << 20), FAKE + (2 << 20))
+    dptr = C.cast(good, C.POINTER(C.c_void_p))
+    sp = C.cast(shape, C.POINTER(C.c_int64))
+    assert lib.tp_shard_materialize(C.c_void_p(FAKE), 9, sp, 2, C.byref(lay), dptr, 2, None) == _abi.TP_ERR_ARG
+    assert lib.tp_shard_materialize(None, 0, sp, 2, C.byref(lay), dptr, 2, None) == _abi.TP_ERR_ARG
+    assert lib.tp_shard_materialize(C.c_void_p(FAKE), 0, sp, 2, C.byref(lay), dptr, 1, None) == _abi.TP_ERR_ARG
+    bad = (C.c_void_p * 2)(FAKE + (1 << 20), None)
+    assert lib.tp_shard_materialize(C.c_void_p(FAKE), 0, sp, 2, C.byref(lay),
+                                    C.cast(bad, C.POINTER(C.c_void_p)), 2, None) == _abi.TP_ERR_ARG
+    ovl = (C.c_void_p * 2)(FAKE + 8, FAKE + (2 << 20))
+    assert lib.tp_shard_materialize(C.c_void_p(FAKE), 0, sp, 2, C.byref(lay),
+                                    C.cast(ovl, C.POINTER(C.c_void_p)), 2, None) == _abi.TP_ERR_ARG
+    ind = (C.c_int64 * 2)(3, 4)
+    assert lib.tp_shard_materialize(C.c_void_p(FAKE), 0, C.cast(ind, C.POINTER(C.c_int64)), 2, C.byref(lay),
+                                    dptr, 2, None) == _abi.TP_ERR_INDIVISIBLE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = _abi._lib
+    try:
+        _abi._lib = None
+        with pytest.raises(RuntimeError):
+            _abi.load(str(tmp_path / "nope.so"))
+    finally:
+        _abi._lib = saved

@@ -1,0 +1,217 @@
+"""GPU parity of tp_colrow_mlp (GEMM1 + GeLU, GEMM2, two-stream chunked
+reduce) against the MLP oracle."""
+import numpy as np
+import pytest
+import torch
+
+import sharded_gemm_amd as tp
+from sharded_gemm_amd import inputs
+from sharded_gemm_amd.workloads import GPT2_SMALL, GPT3_175B, GPT3_6P7B, TINY
+from oracle import layout as L
+from oracle import mlp as O
+from oracle import reduce as R
+
+from gpu_helpers import Guarded, announce, bits, rel_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2   # max|err|/max|ref|, bf16 inputs, fp32 accumulation, Y rounded to bf16
+TOL_F32 = 1e-5    # same measure, fp32 throughout
+
+
+def setup_module(_):
+    require_gpu()
+
+
+def run_rank(X, A_i, B_i, *, R=1, C=1, peers=(), act=tp.TP_ACT_GELU_ERF, two_streams=False):
+    """One tp_colrow_mlp call into canary-guarded outputs; returns CPU copies."""
+    M, H = X.shape
+    F = A_i.shape[1]
+    Y = Guarded((M, F), X.dtype)
+    Z = Guarded((M, H), torch.float32)
+    Zo = Guarded((M, H), torch.float32) if peers else None
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream() if two_streams else s0
+    tp.tp_colrow_mlp(X, A_i, B_i, Y.t, Z.t, row_chunks=R, col_chunks=C, peer_partials=list(peers),
+                     Z_out=Zo.t if Zo is not None else None, act=act, s_compute=s0, s_reduce=s1)
+    torch.cuda.synchronize()
+    for g in (Y, Z) + ((Zo,) if Zo is not None else ()):
+        assert g.guards_intact(), "write outside an output buffer"
+    return Y.t.cpu(), Z.t.cpu(), (Zo.t.cpu() if Zo is not None else None)
+
+
+def _bf16_exact(x64):
+    """RNE rounding of exact fp64 values to bf16 (the same decision the kernel takes)."""
+    return torch.from_numpy(np.asarray(x64)).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- exact cases
+
+@pytest.mark.parametrize("M,H,F", [(300, 264, 136), (256, 512, 512), (77, 45, 51), (1, 8, 8), (513, 1040, 264)])
+def test_hidden_integer_exact(M, H, F):
+    """Small-integer inputs make X A_i exact in fp32, so Y must equal the
+    RNE-to-bf16 rounding of the oracle's exact value, bit for bit."""
+    announce(f"mlp hidden integer exact M={M} H={H} F={F}")
+    X = inputs.small_ints((M, H), seed=101, lo=-4, hi=4, dtype="bf16")
+    A = inputs.small_ints((H, F), seed=102, lo=-4, hi=4, dtype="bf16")
+    B = inputs.small_ints((F, H), seed=103, lo=-4, hi=4, dtype="bf16")
+    Y, _, _ = run_rank(X.cuda(), A.cuda(), B.cuda(), act=tp.TP_ACT_NONE)
+    ref = _bf16_exact(O.hidden(X, A, O.GELU_NONE))
+    assert np.array_equal(bits(Y), bits(ref))
+
+
+def _one_hot_columns(H, F, seed):
+    """A [H, F] with one small nonzero integer per column: X A stays a small
+    integer, exactly representable in bf16."""
+    g = torch.Generator().manual_seed(seed)
+    rows = torch.randint(0, H, (F,), generator=g)
+    vals = torch.randint(1, 5, (F,), generator=g) * (torch.randint(0, 2, (F,), generator=g) * 2 - 1)
+    A = torch.zeros((H, F))
+    A[rows, torch.arange(F)] = vals.float()
+    return A.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,H,F,Rc,Cc,P", [(512, 384, 256, 2, 3, 3), (93, 72, 40, 3, 2, 2),
+                                            (50, 30, 22, 2, 3, 2), (1024, 1024, 512, 4, 4, 8)])
+def test_chain_integer_exact(M, H, F, Rc, Cc, P):
+    """Exact whole chain: Y small integers, fp32 sums exact, so Z_i and Z_out
+    must equal the oracle bit for bit, chunked, on two streams."""
+    announce(f"mlp chain integer exact M={M} H={H} F={F} R={Rc} C={Cc} P={P}")
+    X = inputs.small_ints((M, H), seed=201, lo=-4, hi=4, dtype="bf16")
+    A = _one_hot_columns(H, F, 202)
+    B = inputs.small_ints((F, H), seed=203, lo=-4, hi=4, dtype="bf16")
+    peers_cpu = [inputs.small_ints((M, H), seed=210 + p, lo=-512, hi=512) for p in range(P - 1)]
+    Y, Z, Zo = run_rank(X.cuda(), A.cuda(), B.cuda(), R=Rc, C=Cc, peers=[p.cuda() for p in peers_cpu],
+                        act=tp.TP_ACT_NONE, two_streams=True)
+    z_ref = O.mlp_rank(X, A, B, O.GELU_NONE)
+    assert np.array_equal(Z.numpy().astype(np.float64), z_ref)
+    assert np.array_equal(Zo.numpy().astype(np.float64), R.reduce_full([z_ref] + peers_cpu))
+
+
+# ------------------------------------------------------------ tolerance cases
+
+@pytest.mark.parametrize("M,H,F,Rc,Cc", [(300, 264, 136, 3, 2), (77, 45, 51, 1, 1), (128, 4096, 64, 2, 4),
+                                         (2050, 520, 776, 2, 1), (1, 1, 1, 1, 1)])
+def test_ragged_bf16(M, H, F, Rc, Cc):
+    announce(f"mlp ragged bf16 M={M} H={H} F={F} R={Rc} C={Cc}")
+    X = inputs.normal((M, H), 301, 1.0, "bf16")
+    A = inputs.normal((H, F), 302, 1.0 / np.sqrt(H), "bf16")
+    B = inputs.normal((F, H), 303, 1.0 / np.sqrt(F), "bf16")
+    peers_cpu = [inputs.normal((M, H), 310 + p) for p in range(2)]
+    Y, Z, Zo = run_rank(X.cuda(), A.cuda(), B.cuda(), R=Rc, C=Cc, peers=[p.cuda() for p in peers_cpu],
+                        two_streams=True)
+    y_ref = O.hidden(X, A)
+    z_ref = O.mlp_rank(X, A, B)
+    assert rel_err(Y.float(), y_ref) <= TOL_BF16
+    assert rel_err(Z, z_ref) <= TOL_BF16
+    assert rel_err(Zo, R.reduce_full([z_ref] + peers_cpu)) <= TOL_BF16
+
+
+def test_tiny_fp32_two_ranks():
+    """The tiny fp32 workload: X[64,256], A[256,1024] cut by columns into 2,
+    B[1024,256] cut by rows into 2 (cut on the GPU), both ranks, summed."""
+    w = TINY
+    announce("mlp tiny fp32 P=2")
+    X = inputs.normal((w.M, w.H), inputs.seed_for(1, inputs.SLOT_X), w.std_x)
+    A = inputs.normal((w.H, w.P * w.F), inputs.seed_for(1, inputs.SLOT_A), w.std_a)
+    B = inputs.normal((w.P * w.F, w.H), inputs.seed_for(1, inputs.SLOT_B), w.std_b)
+    sa = {"device": [0, 1], "sharded_dim": [{"axis": 1, "num_shards": 2}]}
+    sb = {"device": [0, 1], "sharded_dim": [{"axis": 0, "num_shards": 2}]}
+    A_sh = {d: torch.empty((w.H, w.F), device="cuda") for d in range(2)}
+    B_sh = {d: torch.empty((w.F, w.H), device="cuda") for d in range(2)}
+    tp.tp_shard_materialize(A.cuda(), sa, A_sh)
+    tp.tp_shard_materialize(B.cuda(), sb, B_sh)
+    Xg = X.cuda()
+    _, Z1, _ = run_rank(Xg, A_sh[1], B_sh[1])
+    Y0, Z0, Zo = run_rank(Xg, A_sh[0], B_sh[0], peers=[Z1.cuda()], two_streams=True)
+    oa, ob = L.split(A, sa), L.split(B, sb)
+    assert rel_err(Y0, O.hidden(X, oa[0])) <= TOL_F32
+    assert rel_err(Z0, O.mlp_rank(X, oa[0], ob[0])) <= TOL_F32
+    assert rel_err(Zo, O.mlp_all_ranks(X, [oa[0], oa[1]], [ob[0], ob[1]])) <= TOL_F32
+    assert rel_err(Zo, O.mlp_unsharded(X, A, B)) <= TOL_F32
+
+
+def test_gpt2_small_tp4_full():
+    """GPT-2-small MLP at TP=4, every element of every rank: weights cut on the
+    GPU from the full A [768,3072] and B [3072,768]; ranks 1..3 first, then
+    rank 0 reduces all four partials."""
+    w = GPT2_SMALL
+    announce("mlp gpt2-small tp4 full size")
+    X = inputs.normal((w.M, w.H), inputs.seed_for(2, inputs.SLOT_X), w.std_x, "bf16")
+    A = inputs.normal((w.H, w.P * w.F), inputs.seed_for(2, inputs.SLOT_A), w.std_a, "bf16")
+    B = inputs.normal((w.P * w.F, w.H), inputs.seed_for(2, inputs.SLOT_B), w.std_b, "bf16")
+    sa = {"device": list(range(4)), "sharded_dim": [{"axis": 1, "num_shards": 4}]}
+    sb = {"device": list(range(4)), "sharded_dim": [{"axis": 0, "num_shards": 4}]}
+    A_sh = {d: torch.empty((w.H, w.F), dtype=torch.bfloat16, device="cuda") for d in range(4)}
+    B_sh = {d: torch.empty((w.F, w.H), dtype=torch.bfloat16, device="cuda") for d in range(4)}
+    tp.tp_shard_materialize(A.cuda(), sa, A_sh)
+    tp.tp_shard_materialize(B.cuda(), sb, B_sh)
+    Xg = X.cuda()
+    peers = [run_rank(Xg, A_sh[i], B_sh[i])[1].cuda() for i in range(1, 4)]
+    Y0, Z0, Zo = run_rank(Xg, A_sh[0], B_sh[0], peers=peers, two_streams=True)
+    oa, ob = L.split(A, sa), L.split(B, sb)
+    assert rel_err(Y0.float(), O.hidden(X, oa[0])) <= TOL_BF16
+    assert rel_err(Z0, O.mlp_rank(X, oa[0], ob[0])) <= TOL_BF16
+    full = O.mlp_all_ranks(X, [oa[i] for i in range(4)], [ob[i] for i in range(4)])
+    assert rel_err(Zo, full) <= TOL_BF16
+    assert rel_err(Zo, O.mlp_unsharded(X, A, B)) <= TOL_BF16
+
+
+def _sample_rows(M, Rc, per_chunk):
+    """Rows of each row chunk: its first and last row plus evenly spread ones."""
+    Mr = M // Rc
+    rows = []
+    for r in range(Rc):
+        rows += list(np.unique(np.linspace(r * Mr, (r + 1) * Mr - 1, per_chunk).astype(np.int64)))
+    return np.array(rows)
+
+
+def _large_case(w, per_chunk):
+    announce(f"mlp {w.name}: inputs")
+    X = inputs.normal((w.M, w.H), inputs.seed_for(w.cfg, inputs.SLOT_X), w.std_x, "bf16", device="cuda")
+    As = [inputs.normal((w.H, w.F), inputs.seed_for(w.cfg, inputs.SLOT_A_SHARD + i), w.std_a, "bf16", device="cuda")
+          for i in range(w.P)]
+    Bs = [inputs.normal((w.F, w.H), inputs.seed_for(w.cfg, inputs.SLOT_B_SHARD + i), w.std_b, "bf16", device="cuda")
+          for i in range(w.P)]
+    announce(f"mlp {w.name}: ranks 1..{w.P - 1} (untimed peers)")
+    peers = [run_rank(X, As[i], Bs[i])[1].cuda() for i in range(1, w.P)]
+    announce(f"mlp {w.name}: rank 0, R={w.R} C={w.C}, two streams")
+    Y0, Z0, Zo = run_rank(X, As[0], Bs[0], R=w.R, C=w.C, peers=peers, two_streams=True)
+    announce(f"mlp {w.name}: rank 0 unchunked, one stream")
+    Y0s, Z0s, Zos = run_rank(X, As[0], Bs[0], R=1, C=1, peers=peers, two_streams=False)
+    # Chunking and stream overlap never change a bit.
+    assert np.array_equal(bits(Y0), bits(Y0s))
+    assert np.array_equal(bits(Z0), bits(Z0s))
+    assert np.array_equal(bits(Zo), bits(Zos))
+    rows = _sample_rows(w.M, w.R, per_chunk)
+    Xc = X.cpu()
+    announce(f"mlp {w.name}: oracle on {len(rows)} sampled rows")
+    z0_ref = O.mlp_rank_rows(Xc, As[0].cpu(), Bs[0].cpu(), rows)
+    assert rel_err(Z0[rows], z0_ref) <= TOL_BF16
+    assert rel_err(Y0[rows].float(), O.hidden(Xc[rows], As[0].cpu())) <= TOL_BF16
+    acc = z0_ref.copy()
+    for i in range(1, w.P):
+        acc += O.mlp_rank_rows(Xc, As[i].cpu(), Bs[i].cpu(), rows)
+    assert rel_err(Zo[rows], acc) <= TOL_BF16
+
+
+def test_gpt3_6p7b_tp8_rowsplit():
+    _large_case(GPT3_6P7B, per_chunk=32)
+
+
+def test_gpt3_175b_tp8_2d():
+    _large_case(GPT3_175B, per_chunk=16)
+
+
+def test_error_leaves_outputs_untouched():
+    announce("mlp error path")
+    X = torch.zeros((30, 16), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((16, 8), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
+    Y = Guarded((30, 8), torch.bfloat16)
+    Z = Guarded((30, 16), torch.float32)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_colrow_mlp(X, A, B, Y.t, Z.t, row_chunks=4)
+    assert e.value.kind == "indivisible"
+    torch.cuda.synchronize()
+    assert Y.body_untouched() and Z.body_untouched()

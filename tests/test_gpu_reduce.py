@@ -1,0 +1,96 @@
+"""GPU parity of tp_partial_reduce against the reduction oracle."""
+import numpy as np
+import pytest
+import torch
+
+import sharded_gemm_amd as tp
+from sharded_gemm_amd import inputs
+from sharded_gemm_amd.workloads import RESHARD
+from oracle import reduce as R
+
+from gpu_helpers import Guarded, announce, bits, rel_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-6   # max|err| / max|ref| for fp32 sums vs the fp64 oracle
+
+
+def setup_module(_):
+    require_gpu()
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 13])
+@pytest.mark.parametrize("rows,cols,ld", [(1, 1, 1), (7, 3, 5), (64, 1027, 1027), (300, 256, 384),
+                                          (129, 768, 768), (4, 4100, 4104)])
+def test_full(P, rows, cols, ld):
+    announce(f"reduce FULL P={P} rows={rows} cols={cols} ld={ld}")
+    parts_cpu = [inputs.normal((rows, ld), seed=5000 + p) for p in range(P)]
+    parts = [p.cuda() for p in parts_cpu]
+    out = Guarded((rows, ld), torch.float32)
+    tp.tp_partial_reduce(parts, [out.t], tp.TP_REDUCE_FULL, rows=rows, cols=cols, ld_in=ld, ld_out=ld)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    got = out.t.cpu()
+    ref = R.reduce_full([p[:, :cols] for p in parts_cpu])
+    assert rel_err(got[:, :cols], ref) <= TOL
+    if ld > cols:   # padding columns are not written
+        pad = bits(got[:, cols:])
+        assert (pad == np.int32(0x7FC0DEAD)).all()
+
+
+def test_integer_partials_bit_exact():
+    announce("reduce FULL integer partials, bit-exact")
+    P, rows, cols = 8, 333, 517
+    parts_cpu = [inputs.small_ints((rows, cols), seed=6000 + p, lo=-1024, hi=1024) for p in range(P)]
+    out = torch.empty((rows, cols), device="cuda")
+    tp.tp_partial_reduce([p.cuda() for p in parts_cpu], [out])
+    ref = R.reduce_full(parts_cpu)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+def test_in_place():
+    announce("reduce FULL in place")
+    parts_cpu = [inputs.normal((96, 200), seed=7000 + p) for p in range(4)]
+    parts = [p.cuda() for p in parts_cpu]
+    tp.tp_partial_reduce(parts, [parts[0]])
+    assert rel_err(parts[0].cpu(), R.reduce_full(parts_cpu)) <= TOL
+
+
+@pytest.mark.parametrize("P,S,rows,cols", [(2, 2, 8, 5), (4, 4, 64, 1000), (3, 6, 96, 64)])
+def test_split_small(P, S, rows, cols):
+    announce(f"reduce SPLIT P={P} S={S} {rows}x{cols}")
+    parts_cpu = [inputs.normal((rows, cols), seed=8000 + p) for p in range(P)]
+    outs = [Guarded((rows // S, cols), torch.float32) for _ in range(S)]
+    tp.tp_partial_reduce([p.cuda() for p in parts_cpu], [o.t for o in outs], tp.TP_REDUCE_SPLIT)
+    torch.cuda.synchronize()
+    ref = R.reduce_split(parts_cpu, S)
+    for j in range(S):
+        assert outs[j].guards_intact()
+        assert rel_err(outs[j].t.cpu(), ref[j]) <= TOL
+
+
+def test_split_full_size():
+    """8 fp32 partials [8192, 8192] -> 8 row shards [1024, 8192]."""
+    w = RESHARD
+    announce("reduce SPLIT full size 8 x [8192,8192] -> 8 x [1024,8192]")
+    parts = [inputs.normal(w.partial_shape, inputs.seed_for(4, inputs.SLOT_PARTIAL + p), device="cuda")
+             for p in range(w.num_partials)]
+    rows = w.partial_shape[0] // w.num_splits
+    outs = [torch.empty((rows, w.partial_shape[1]), device="cuda") for _ in range(w.num_splits)]
+    tp.tp_partial_reduce(parts, outs, tp.TP_REDUCE_SPLIT)
+    torch.cuda.synchronize()
+    parts_cpu = [p.cpu() for p in parts]
+    ref = R.reduce_split(parts_cpu, w.num_splits)
+    for j in range(w.num_splits):
+        assert rel_err(outs[j].cpu(), ref[j]) <= TOL, j
+
+
+def test_error_leaves_output_untouched():
+    announce("reduce error path")
+    parts = [torch.zeros((6, 4), device="cuda") for _ in range(2)]
+    outs = [Guarded((2, 4), torch.float32) for _ in range(4)]
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_partial_reduce(parts, [o.t for o in outs], tp.TP_REDUCE_SPLIT)   # 6 rows, 4 splits
+    assert e.value.kind == "indivisible"
+    torch.cuda.synchronize()
+    assert all(o.body_untouched() for o in outs)

@@ -26,6 +26,18 @@ def test_gelu_closed_forms():
     assert np.allclose(O.gelu(xs), ref, rtol=1e-14, atol=1e-15)
 
 
+def _loops_hidden(X, A, act):
+    M, H, F = len(X), len(X[0]), len(A[0])
+    Y = [[0.0] * F for _ in range(M)]
+    for m in range(M):
+        for f in range(F):
+            s = 0.0
+            for h in range(H):
+                s += X[m][h] * A[h][f]
+            Y[m][f] = 0.5 * s * (1.0 + math.erf(s / math.sqrt(2.0))) if act else s
+    return np.array(Y)
+
+
 def _loops(X, A, B, act):
     M, H = len(X), len(X[0])
     F = len(A[0])
@@ -59,6 +71,9 @@ def test_brute_force_tiny_shapes(act):
         ref = _loops(X.tolist(), A.tolist(), B.tolist(), act)
         assert got.shape == (M, H + 1)
         assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+        y = O.hidden(X, A, act)
+        assert y.shape == (M, F)
+        assert np.allclose(y, _loops_hidden(X.tolist(), A.tolist(), act), rtol=1e-12, atol=1e-12)
 
 
 def test_worked_integer_example():

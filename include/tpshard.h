@@ -197,7 +197,10 @@ typedef struct {
  * s_compute moves on to the next block ([DOM] "forward": the all-reduce of one
  * micro-batch hides behind the next one's GeMM-GeLU-GeMM).  Before returning,
  * s_compute is made to wait for s_reduce, so completion of s_compute means the
- * whole call is done.  s_reduce may equal s_compute (serial schedule).
+ * whole call is done.  s_reduce may equal s_compute (serial schedule); with a
+ * single block (R = C = 1) the reduce runs on s_compute, as nothing could
+ * overlap it.  The calls are capturable into a HIP graph (no memsets, no
+ * allocation, no host synchronisation).
  * Chunking never changes a result bit: each output element is accumulated in
  * the same order whatever R and C are.
  * Errors: TP_ERR_ARG (null or overlapping buffers, bad dtype/act, sizes < 1,

@@ -215,8 +215,11 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   }
 
   hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
-  const bool two = (s0 != s1) && a->P > 1;
   const int64_t R = a->row_chunks, C = a->col_chunks, Mr = M / R, Hc = H / C;
+  // The reduce stream only pays when a later block's GEMMs can run beside an
+  // earlier block's reduce; with a single block the hand-off (an event record
+  // and a cross-queue wait, about 10 us each way on MI355X) is pure latency.
+  const bool two = (s0 != s1) && a->P > 1 && R * C > 1;
   hipEvent_t *ev = nullptr;
   if (two) {
     const int rc = get_events(static_cast<size_t>(R * C + 1), &ev);

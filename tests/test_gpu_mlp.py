@@ -215,3 +215,40 @@ def test_error_leaves_outputs_untouched():
     assert e.value.kind == "indivisible"
     torch.cuda.synchronize()
     assert Y.body_untouched() and Z.body_untouched()
+
+
+def test_graph_replay_matches_eager():
+    """The two-stream chunked call captured into a HIP graph: every replay,
+    with eager work and host synchronisation in between, equals the eager call."""
+    announce("mlp graph capture and replay")
+    M, H, F, Rc, Cc = 1024, 512, 384, 2, 2
+    X = inputs.normal((M, H), 401, 1.0, "bf16").cuda()
+    A = inputs.normal((H, F), 402, 0.05, "bf16").cuda()
+    B = inputs.normal((F, H), 403, 0.05, "bf16").cuda()
+    peers = [inputs.normal((M, H), 410 + p).cuda() for p in range(3)]
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    Zo = torch.empty((M, H), device="cuda")
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def call():
+        tp.tp_colrow_mlp(X, A, B, Y, Z, row_chunks=Rc, col_chunks=Cc, peer_partials=peers, Z_out=Zo,
+                         s_compute=s0, s_reduce=s1)
+
+    call()
+    torch.cuda.synchronize()
+    ref_y, ref_z, ref_zo = Y.clone(), Z.clone(), Zo.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s0):
+        call()
+    for rep in range(3):
+        for t in (Y, Z, Zo):
+            t.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s0):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), ref_y.view(torch.int16)), rep
+        assert torch.equal(Z.view(torch.int32), ref_z.view(torch.int32)), rep
+        assert torch.equal(Zo.view(torch.int32), ref_zo.view(torch.int32)), rep
+        peers[0].add_(0.0)   # eager work between replays

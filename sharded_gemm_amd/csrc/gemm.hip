@@ -1,25 +1,40 @@
 // Dense GEMMs of the column->row MLP on gfx950.
 //
-//   C[M,N] = act(A[M,K] * W[K,N])      A row-major (K contiguous, row stride lda)
+//   C[M,N] = epi(A[M,K] * W[K,N])      A row-major (K contiguous, row stride lda)
 //                                      W row-major (N contiguous, row stride ldw)
 //
 // GEMM1 of the MLP is X * A_i followed by GeLU, stored as bf16 ([CAI] section
 // 2, column-parallel linear; [DOM] "GeMM GeLU GeMM"); GEMM2 is Y * B_i stored
 // as the fp32 partial ([CAI] section 2.1, row-parallel linear).
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  A workgroup of
-// 4 waves (2 x 2) owns a BM x BN output tile; K advances 64 at a time through
-// a double-buffered LDS stage.  Both operands sit in LDS K-contiguous (the W
-// tile is transposed in registers, 8x8 bf16 at a time, on its way from global
-// memory), so each lane reads its MFMA operand with one 16-byte LDS load.  An
-// XOR swizzle of the 16-byte chunks keeps those loads and the stores free of
-// bank conflicts.  The MFMA gets W as its first operand and A as its second,
-// which hands every lane one output row and four adjacent output columns, so
-// the epilogue writes 16 bytes (fp32) or 8 bytes (bf16) per lane.
+// Main path (bf16_gemm_dma): v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+//  * 8 waves per workgroup (2 per SIMD) in a 2 x 4 grid over the output tile,
+//    so one wave's MFMAs cover the other wave's memory instructions.
+//  * Both operand tiles go global -> LDS with the LDS-DMA load
+//    (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane),
+//    into an S-slot ring; no VGPRs stage the data and nothing waits on a load
+//    until its slot is needed.  These loads are issued from inline assembly:
+//    the compiler, when it sees the builtin form, waits for every
+//    outstanding DMA (vmcnt(0)) before each LDS read, which would empty the
+//    ring; here the kernel counts vmcnt itself, per stage.
+//  * A (K contiguous) is read with ds_read_b128; W stays N-contiguous in LDS
+//    and is read with the gfx950 transposing read ds_read_b64_tr_b16, which
+//    hands each lane the 4 consecutive k of one column n (two reads make the 8
+//    k an MFMA operand needs), so no transpose pass exists anywhere.
+//  * XOR swizzles on 16-byte chunks keep the DMA writes and both kinds of LDS
+//    read free of bank conflicts.
+//  * Fragments are double-buffered in registers across k steps: the LDS reads
+//    of step u+1 are in flight while the MFMAs of step u run.
+//  * The MFMA gets W as its first operand and A as its second, so each lane
+//    owns one output row and four adjacent columns: 16-byte (fp32) or 8-byte
+//    (bf16) stores.
+// Ragged path (bf16_gemm_ragged): the same MFMA on a 128 x 128 tile with
+// register-staged, bounds-checked loads, for shapes the DMA path cannot take
+// (K not a multiple of 32, N not a multiple of 8, misaligned pointers).
 //
-// Every output element is accumulated over k in the same order (64-wide
-// stages, ascending) whatever the tile shape, so results do not depend on the
-// tile configuration or on how the caller chunks M and N.
+// Both paths accumulate every output element over k in the same order (32-wide
+// k steps, ascending), so results are bit-identical whichever path or tile
+// shape runs, and do not depend on how the caller chunks M and N.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -29,6 +44,7 @@
 namespace tpshard {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -110,7 +126,7 @@ __device__ __forceinline__ void tile_coords(int bid, int ntiles, int tiles_m, in
   *tn = local / gm;
 }
 
-// ---- the bf16 MFMA kernel ----------------------------------------------
+// ---- ragged path: register-staged, bounds-checked ------------------------
 
 template <int BM, int BN, bool VEC, int EPI>
 struct Bf16Gemm {
@@ -283,7 +299,7 @@ struct Bf16Gemm {
 };
 
 template <int BM, int BN, bool VEC, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) bf16_gemm_kernel(GemmArgs p) {
+__global__ void __launch_bounds__(kThreads, 1) bf16_gemm_ragged(GemmArgs p) {
   using G = Bf16Gemm<BM, BN, VEC, EPI>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::LDS_STAGE];
 
@@ -314,6 +330,199 @@ __global__ void __launch_bounds__(kThreads, 1) bf16_gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
   G::epilogue(p, m0, n0, acc);
+}
+
+
+// ---- main path: LDS-DMA ring, 8 waves ------------------------------------
+
+#define TP_LDS __attribute__((address_space(3)))
+
+// One LDS-DMA load: this lane's 16 bytes at g land at LDS byte address
+// lds + 16 * lane.  lds must be wave-uniform (it goes to M0).
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int BK, int S>
+struct DmaCfg {
+  static constexpr int WAVES_M = 2, WAVES_N = 4, NW = 8, THREADS = 512;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
+  static constexpr int KK = BK / 32;                   // MFMA k-steps per stage
+  static constexpr int AROW = BK * 2, ACH = BK / 8;    // A tile: bytes, 16B chunks per row
+  static constexpr int ARPI = 1024 / AROW;             // A rows per DMA instruction
+  static constexpr int WROW = BN * 2, WCH = BN / 8;    // W tile row (one k): bytes, chunks
+  static constexpr int WRPI = 1024 / WROW;             // W rows per DMA instruction
+  static constexpr int A_BYTES = BM * AROW, STAGE = A_BYTES + BK * WROW;
+  static constexpr int A_PW = A_BYTES / 1024 / NW;     // DMA instructions per wave per stage
+  static constexpr int W_PW = BK * WROW / 1024 / NW;
+  static constexpr int L = A_PW + W_PW;
+  static_assert((BK == 32 || BK == 64) && WN % 16 == 0 && WM % 16 == 0 && WCH >= 8, "tile shape");
+  static_assert(A_PW >= 1 && W_PW >= 1 && A_PW * NW * 1024 == A_BYTES && W_PW * NW * 1024 == BK * WROW, "DMA split");
+  static_assert((S - 1) * L < 64, "vmcnt range");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
+};
+
+// A-tile swizzle: with 4 chunks per row (BK = 32) two rows share a 128-byte
+// bank window, with 8 chunks (BK = 64) one row fills it.
+template <int BK>
+__device__ __forceinline__ int a_swz(int row) {
+  return BK == 32 ? ((row >> 1) & 3) : (row & 7);
+}
+
+template <int BM, int BN, int BK, int S, int EPI>
+__global__ void __launch_bounds__(512, 1) bf16_gemm_dma(GemmArgs p) {
+  using C = DmaCfg<BM, BN, BK, S>;
+  constexpr int KK = C::KK;
+  __shared__ __attribute__((aligned(1024))) char smem[S * C::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int tiles_m = static_cast<int>((p.M + BM - 1) / BM);
+  const int tiles_n = static_cast<int>((p.N + BN - 1) / BN);
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TP_LDS char *)smem));
+  const uint16_t *A = static_cast<const uint16_t *>(p.a);
+  const uint16_t *W = static_cast<const uint16_t *>(p.w);
+
+  // Source of each of this lane's DMA pieces (elements, before the stage's k
+  // offset).  Lane order fixes the LDS position, so the swizzle is applied by
+  // choosing which chunk a lane fetches.  Rows past M and columns past N are
+  // clamped onto valid memory: they only feed outputs that are never stored.
+  int64_t a_src[C::A_PW], w_src[C::W_PW];
+#pragma unroll
+  for (int q = 0; q < C::A_PW; ++q) {
+    const int row = (wave * C::A_PW + q) * C::ARPI + lane / C::ACH;
+    const int chunk = (lane % C::ACH) ^ a_swz<BK>(row);
+    const int64_t gm = (m0 + row < p.M) ? m0 + row : p.M - 1;
+    a_src[q] = gm * p.lda + chunk * 8;
+  }
+#pragma unroll
+  for (int q = 0; q < C::W_PW; ++q) {
+    const int row = (wave * C::W_PW + q) * C::WRPI + lane / C::WCH;
+    const int chunk = (lane % C::WCH) ^ (2 * (row & 3));
+    const int64_t gn = (n0 + chunk * 8 < p.N) ? n0 + chunk * 8 : p.N - 8;
+    w_src[q] = static_cast<int64_t>(row) * p.ldw + gn;
+  }
+  auto issue = [&](int st, int slot) {
+    const int64_t k0 = static_cast<int64_t>(st) * BK;
+    const uint32_t base = lds0 + slot * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::A_PW; ++q) lds_dma16(A + a_src[q] + k0, base + (wave * C::A_PW + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < C::W_PW; ++q)
+      lds_dma16(W + w_src[q] + k0 * p.ldw, base + C::A_BYTES + (wave * C::W_PW + q) * 1024);
+  };
+
+  // LDS byte offsets (within a stage) of this lane's operand fragments.
+  // A: lane reads row (lane & 15) of a 16-row block, k chunk (lane >> 4).
+  // W: ds_read_b64_tr_b16 over 16 lanes g: lane 4r + q reads k row 8g + r (+4)
+  // at columns 4q..4q+3; lane j of the group then holds column j, 4 k values.
+  uint32_t a_off[KK][C::TM], w_off[KK][C::TN][2];
+  {
+    const int g = lane >> 4, r = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const int row = wm * C::WM + i * 16 + (lane & 15), chunk = kk * 4 + (lane >> 4);
+        a_off[kk][i] = row * C::AROW + ((chunk ^ a_swz<BK>(row)) << 4);
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int col = wn * C::WN + j * 16 + 4 * q;
+        const int chunk = col >> 3, byte = (col & 7) * 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = kk * 32 + 8 * g + r + 4 * h;
+          w_off[kk][j][h] = C::A_BYTES + k * C::WROW + ((chunk ^ (2 * (k & 3))) << 4) + byte;
+        }
+      }
+    }
+  }
+  auto read = [&](int u, bf16x8_t (&fa)[C::TM], bf16x8_t (&fb)[C::TN]) {
+    const int kk = KK == 1 ? 0 : (u & 1);
+    const TP_LDS char *base = (const TP_LDS char *)smem + ((u / KK) % S) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) fa[i] = *(const TP_LDS bf16x8_t *)(base + a_off[kk][i]);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + w_off[kk][j][0]));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + w_off[kk][j][1]));
+      fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  f32x4_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const bf16x8_t (&fa)[C::TM], const bf16x8_t (&fb)[C::TN]) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+
+  // Stage t lives in slot t % S.  The barrier that opens stage t (after this
+  // wave's loads of stage t have landed: vmcnt) also proves every wave has
+  // read stage t-1 into registers, so stage t+S-1 is issued into its slot.
+  const int nst = static_cast<int>(p.K / BK), nu = nst * KK;
+  auto open_stage = [&](int st) {
+    if (st + S - 2 < nst) wait_vmcnt<(S - 2) * C::L>(); else wait_vmcnt<0>();
+    __syncthreads();
+    if (st + S - 1 < nst) issue(st + S - 1, (st + S - 1) % S);
+  };
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    if (st < nst) issue(st, st);
+  if (nst >= S) wait_vmcnt<(S - 1) * C::L>(); else wait_vmcnt<0>();
+  __syncthreads();
+  bf16x8_t fa0[C::TM], fb0[C::TN], fa1[C::TM], fb1[C::TN];
+  read(0, fa0, fb0);
+  int u = 0;
+  for (; u + 2 <= nu; u += 2) {
+    if ((u + 1) % KK == 0) open_stage((u + 1) / KK);
+    read(u + 1, fa1, fb1);
+    mma(fa0, fb0);
+    if (u + 2 < nu) {
+      if ((u + 2) % KK == 0) open_stage((u + 2) / KK);
+      read(u + 2, fa0, fb0);
+    }
+    mma(fa1, fb1);
+  }
+  if (u < nu) mma(fa0, fb0);
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int64_t m = m0 + wm * C::WM + i * 16 + (lane & 15);
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int64_t n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
+      if (n >= p.N) continue;   // N is a multiple of 8 on this path
+      f32x4_t v = acc[i][j];
+      if constexpr (EPI == kEpiF32) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + m * p.ldc + n) = v;
+      } else {
+        if constexpr (EPI == kEpiGeluBf16)
+          v = f32x4_t{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.c) + m * p.ldc + n) =
+            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
+  }
 }
 
 // ---- plain fp32 kernel (tiny fp32 workload) ------------------------------
@@ -369,45 +578,59 @@ __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, bool VEC, int EPI>
-hipError_t launch_bf16(const GemmArgs& p, hipStream_t s) {
+template <int BM, int BN, int BK, int S, int EPI>
+hipError_t launch_dma(const GemmArgs& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((bf16_gemm_kernel<BM, BN, VEC, EPI>), dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((bf16_gemm_dma<BM, BN, BK, S, EPI>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
 template <int EPI>
-hipError_t dispatch_bf16(const GemmArgs& p, bool vec, hipStream_t s) {
-  // Shapes that break 16-byte alignment take the element-wise loader, on the
-  // small tile only (they are rare, and it keeps register pressure low).
-  if (!vec) return launch_bf16<128, 128, false, EPI>(p, s);
-  // Pick the largest tile that still gives at least one workgroup per CU;
-  // fall back to the smallest tile for small problems.
-  const int64_t t256x256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  const int64_t t256x128 = ((p.M + 255) / 256) * ((p.N + 127) / 128);
-  if (t256x256 >= 256) return launch_bf16<256, 256, true, EPI>(p, s);
-  if (t256x128 >= 256) return launch_bf16<256, 128, true, EPI>(p, s);
-  return launch_bf16<128, 128, true, EPI>(p, s);
+hipError_t launch_ragged(const GemmArgs& p, bool vec, hipStream_t s) {
+  const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+  if (vec)
+    hipLaunchKernelGGL((bf16_gemm_ragged<128, 128, true, EPI>), dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((bf16_gemm_ragged<128, 128, false, EPI>), dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// Tile choice for the DMA path: estimated time = (waves of workgroups over the
+// 256 CUs) x (work per tile) / (relative per-CU throughput of that tile, as
+// measured on MI355X: the larger tile reuses each operand byte more).
+constexpr int kCUs = 256;
+
+template <int EPI>
+hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s) {
+  if (!dma_ok) return launch_ragged<EPI>(p, vec, s);
+  auto cost = [&](int bm, int bn, double eff) {
+    const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    return static_cast<double>((tiles + kCUs - 1) / kCUs) * bm * bn / eff;
+  };
+  const double c256 = cost(256, 256, 1.0), c128w = cost(256, 128, 0.85), c128 = cost(128, 128, 0.7);
+  if (c256 <= c128w && c256 <= c128) return launch_dma<256, 256, 64, 2, EPI>(p, s);
+  if (c128w <= c128) return launch_dma<256, 128, 64, 3, EPI>(p, s);
+  return launch_dma<128, 128, 32, 8, EPI>(p, s);
 }
 
 }  // namespace
 
-bool gemm_vec_ok(const GemmArgs& p, int64_t esize) {
+bool gemm_vec_ok(const GemmArgs& p, int64_t out_esize) {
   auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  const int64_t per16 = 16 / esize;
-  return al(p.a) && al(p.w) && (p.K % 8 == 0) && (p.N % 8 == 0) && (p.lda % 8 == 0) && (p.ldw % 8 == 0) &&
-         (p.ldc % per16 == 0) && al(p.c);
+  return al(p.a) && al(p.w) && al(p.c) && (p.K % 8 == 0) && (p.N % 8 == 0) && (p.lda % 8 == 0) &&
+         (p.ldw % 8 == 0) && (p.ldc % (16 / out_esize) == 0);
 }
 
 hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  if (epi == kEpiF32 || epi == kEpiGeluBf16) {
-    // the output store width of the vector path is 16 bytes (fp32) or 8 bytes (bf16)
+  if (epi == kEpiF32 || epi == kEpiGeluBf16 || epi == kEpiIdentBf16) {
     const bool vec = gemm_vec_ok(p, epi == kEpiF32 ? 4 : 2);
-    if (epi == kEpiF32) return dispatch_bf16<kEpiF32>(p, vec, s);
-    return dispatch_bf16<kEpiGeluBf16>(p, vec, s);
+    // The DMA path reads whole 32-deep k steps and 8-column groups unchecked.
+    const bool dma_ok = vec && p.K % 32 == 0 && p.K > 0;
+    if (epi == kEpiF32) return dispatch_bf16<kEpiF32>(p, dma_ok, vec, s);
+    if (epi == kEpiGeluBf16) return dispatch_bf16<kEpiGeluBf16>(p, dma_ok, vec, s);
+    return dispatch_bf16<kEpiIdentBf16>(p, dma_ok, vec, s);
   }
-  if (epi == kEpiIdentBf16) return dispatch_bf16<kEpiIdentBf16>(p, gemm_vec_ok(p, 2), s);
   const int64_t tiles = ((p.M + kF32Tile - 1) / kF32Tile) * ((p.N + kF32Tile - 1) / kF32Tile);
   const dim3 grid(static_cast<unsigned>(tiles));
   if (epi == kEpiGeluF32)

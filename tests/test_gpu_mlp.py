@@ -47,7 +47,8 @@ def _bf16_exact(x64):
 
 # ---------------------------------------------------------------- exact cases
 
-@pytest.mark.parametrize("M,H,F", [(300, 264, 136), (256, 512, 512), (77, 45, 51), (1, 8, 8), (513, 1040, 264)])
+@pytest.mark.parametrize("M,H,F", [(300, 264, 136), (256, 512, 512), (77, 45, 51), (1, 8, 8), (513, 1040, 264),
+                                   (333, 320, 200), (515, 256, 96), (1000, 512, 264), (4100, 1024, 776)])
 def test_hidden_integer_exact(M, H, F):
     """Small-integer inputs make X A_i exact in fp32, so Y must equal the
     RNE-to-bf16 rounding of the oracle's exact value, bit for bit."""
@@ -72,7 +73,8 @@ def _one_hot_columns(H, F, seed):
 
 
 @pytest.mark.parametrize("M,H,F,Rc,Cc,P", [(512, 384, 256, 2, 3, 3), (93, 72, 40, 3, 2, 2),
-                                            (50, 30, 22, 2, 3, 2), (1024, 1024, 512, 4, 4, 8)])
+                                            (50, 30, 22, 2, 3, 2), (1024, 1024, 512, 4, 4, 8),
+                                            (515, 256, 96, 1, 2, 2), (1030, 640, 320, 2, 5, 4)])
 def test_chain_integer_exact(M, H, F, Rc, Cc, P):
     """Exact whole chain: Y small integers, fp32 sums exact, so Z_i and Z_out
     must equal the oracle bit for bit, chunked, on two streams."""
@@ -91,7 +93,8 @@ def test_chain_integer_exact(M, H, F, Rc, Cc, P):
 # ------------------------------------------------------------ tolerance cases
 
 @pytest.mark.parametrize("M,H,F,Rc,Cc", [(300, 264, 136, 3, 2), (77, 45, 51, 1, 1), (128, 4096, 64, 2, 4),
-                                         (2050, 520, 776, 2, 1), (1, 1, 1, 1, 1)])
+                                         (2050, 520, 776, 2, 1), (1, 1, 1, 1, 1), (333, 320, 200, 1, 1),
+                                         (1500, 2048, 1024, 3, 2)])
 def test_ragged_bf16(M, H, F, Rc, Cc):
     announce(f"mlp ragged bf16 M={M} H={H} F={F} R={Rc} C={Cc}")
     X = inputs.normal((M, H), 301, 1.0, "bf16")

@@ -20,6 +20,8 @@ Prints one JSON line (last line of stdout).
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -217,6 +219,47 @@ WORKLOADS = {
 
 # --------------------------------------------------------------------------- roofline
 
+COPY_CALIBRATION_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """A plain 256 MiB copy through the layout kernel (a one-device broadcast):
+    its FETCH_SIZE / WRITE_SIZE readings calibrate the traffic counters."""
+    src = torch.empty(COPY_CALIBRATION_BYTES // 4, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    spec = {"device": [-1], "device_map": {-1: [0]}, "sharded_dim": []}
+    for _ in range(3):
+        tp.tp_shard_materialize(src, spec, {0: dst})
+    torch.cuda.synchronize()
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources (device code and its launch dispatch); traffic
+    figures taken on other sources are stale."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "sharded_gemm_amd", "csrc", "*.hip")))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or it was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic__{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
 def kernel_table(stats, steps):
     out = {}
     for name, st in stats.items():
@@ -232,17 +275,18 @@ def kernel_table(stats, steps):
     return out
 
 
-def roofline(kernels, dtype):
+def roofline(kernels, dtype, workload):
     if not kernels:
         return None
     name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     k = kernels[name]
+    traffic = measured_traffic(workload, name)
     if k["unit"] == "TFLOP/s":
         peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
         return {"kernel": name, "bound": "mfma" if dtype == "bf16" else "alu", "achieved": k["achieved"],
-                "peak": peak, "unit": "TFLOP/s", "frac": k["achieved"] / peak, "traffic": None}
+                "peak": peak, "unit": "TFLOP/s", "frac": k["achieved"] / peak, "traffic": traffic}
     return {"kernel": name, "bound": "hbm", "achieved": k["achieved"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": k["achieved"] / PEAK_HBM_GBS, "traffic": None}
+            "frac": k["achieved"] / PEAK_HBM_GBS, "traffic": traffic}
 
 
 # --------------------------------------------------------------------------- main
@@ -255,6 +299,8 @@ def main():
     ap.add_argument("--workload", default=GPT2_SMALL.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 256 MiB plain copy (for calibrating traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -269,6 +315,9 @@ def main():
         build.build()
     tp.load()
 
+    if args.copy_calibration:
+        log("[bench] 256 MiB copy for counter calibration")
+        copy_calibration()
     log(f"[bench] workload {args.workload}: setting up")
     wl = WORKLOADS[args.workload]()
     dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
@@ -366,7 +415,7 @@ def main():
     rec = {"metric": METRIC, "value": value, "unit": wl.unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded N(0,1)/N(0,0.02) tensors)",
-           "config": wl.config(), "roofline": roofline(kernels, dtype), "cpu_baseline": cpu,
+           "config": wl.config(), "roofline": roofline(kernels, dtype, args.workload), "cpu_baseline": cpu,
            "kernels": kernels, "timed_as": "hip graph replay" if use_graph else "eager launches",
            "ms_per_step_eager": ms_eager_plain, "ms_per_step_graph": ms_graph,
            "ms_per_step_eager_with_kernel_events": ms_eager,

@@ -60,7 +60,9 @@ int get_events(size_t n, hipEvent_t **out) {
   auto& v = g_events.by_device[dev];
   while (v.size() < n) {
     hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    // Hand-offs between two streams of one device need a device-scope release
+    // only (the partial is read by the next kernel on this device).
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventReleaseToDevice);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
     v.push_back(ev);
   }

@@ -29,8 +29,10 @@ hipEvent_t take_event() {
     g_timing.free_events.pop_back();
     return e;
   }
+  // Timing-only events: no system-scope fence, so recording one neither
+  // writes back nor invalidates caches around the kernel being timed.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

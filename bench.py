@@ -54,6 +54,9 @@ def log(msg):
 class MlpStep:
     """Per-rank MLP step, optionally preceded by cutting the weights."""
 
+    serial = False
+    reduce_wgs = 0
+
     def __init__(self, w, split_weights: bool):
         self.w = w
         dev = "cuda"
@@ -98,7 +101,8 @@ class MlpStep:
             tp.tp_shard_materialize(self.B, self.sb, self.Bs, stream=self.s0)
         tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
                          col_chunks=self.w.C, peer_partials=self.peers, Z_out=self.Zo,
-                         s_compute=self.s0, s_reduce=self.s1)
+                         s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
+                         reduce_workgroups=self.reduce_wgs)
 
     @property
     def work(self):
@@ -110,6 +114,7 @@ class MlpStep:
         w = self.w
         return {"workload": w.name, "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F, "tp": w.P,
                 "row_chunks": w.R, "col_chunks": w.C, "weights_cut_each_step": self.split,
+                "reduce_stream": "compute" if self.serial else "second",
                 "peers": "virtual ranks 1..P-1, partials precomputed by the same path"}
 
     def cpu_baseline(self, budget_s):
@@ -299,6 +304,9 @@ def main():
     ap.add_argument("--workload", default=GPT2_SMALL.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    ap.add_argument("--serial", action="store_true", help="run the reduce on the compute stream")
+    ap.add_argument("--reduce-wgs", type=int, default=0,
+                    help="cap on the reduce kernel's workgroups beside the GEMMs (0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB plain copy (for calibrating traffic counters)")
     args = ap.parse_args()
@@ -320,6 +328,7 @@ def main():
         copy_calibration()
     log(f"[bench] workload {args.workload}: setting up")
     wl = WORKLOADS[args.workload]()
+    wl.serial, wl.reduce_wgs = args.serial, args.reduce_wgs
     dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -385,6 +394,9 @@ def main():
 
     log(f"[bench] timing {args.steps} eager steps with per-kernel events")
     tp.tp_timing_enable(True)
+    for _ in range(args.steps):      # creates the timing events outside the timed region
+        wl.step()
+    torch.cuda.synchronize()
     tp.tp_timing_read()
     torch.cuda.synchronize()
     t1 = time.perf_counter()

@@ -188,6 +188,9 @@ typedef struct {
                         fp32: the partials of virtual ranks 1..P-1 */
   float *Z_out;      /* [M,H] fp32, required when P > 1: Z_i + sum of peers, written
                         block (r,c) by block on s_reduce; may equal Z_i */
+  int64_t reduce_workgroups; /* upper bound on the reduce kernel's workgroups when it runs
+                        beside the GEMMs on s_reduce (it then shares the CUs with
+                        them); 0 = library default (256); >= 0 */
 } tp_mlp_args;
 
 /*

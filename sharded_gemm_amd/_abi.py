@@ -81,7 +81,8 @@ class tp_mlp_args(C.Structure):
                 ("X", C.c_void_p), ("A_i", C.c_void_p), ("B_i", C.c_void_p),
                 ("Y_ws", C.c_void_p), ("Z_i", C.c_void_p),
                 ("row_chunks", C.c_int64), ("col_chunks", C.c_int64), ("P", C.c_int64),
-                ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p)]
+                ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
+                ("reduce_workgroups", C.c_int64)]
 
 
 class tp_kernel_stat(C.Structure):
@@ -263,7 +264,7 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
 
 
 def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
-                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None):
+                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0):
     """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers)."""
     lib = load()
     M, H = int(X.shape[0]), int(X.shape[1])
@@ -283,7 +284,7 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
                        X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
-                       Z_out=_ptr(Z_out))
+                       Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups)
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))

@@ -36,6 +36,11 @@ namespace {
 
 constexpr int64_t kMaxP = 64;
 constexpr int64_t kMaxSplits = 64;
+// Workgroups of a reduce that runs beside the GEMMs.  The large GEMM tiles fill
+// every SIMD's register file, so the reduce mostly takes CUs between GEMM
+// workgroups; one workgroup per CU back-fills those gaps without crowding out
+// the next GEMM (measured on MI355X against 32 ... 16384).
+constexpr int64_t kReduceBesideGemm = 256;
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -196,6 +201,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   if (a->H % a->col_chunks) return fail(TP_ERR_INDIVISIBLE, "col_chunks %lld does not divide H = %lld", (long long)a->col_chunks, (long long)a->H);
   if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
   if (a->P > 1 && (!a->peer_partials || !a->Z_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out");
+  if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
   const int64_t M = a->M, H = a->H, F = a->F;
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
       (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
@@ -259,7 +265,8 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
       for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_partials[p - 1] + zoff;
       float *dst = a->Z_out + zoff;
       hipEvent_t t1 = timing_begin(sr);
-      const int rc = partial_reduce_launch(parts.data(), static_cast<int>(a->P), Mr, Hc, H, &dst, 1, Mr, H, sr);
+      const int rc = partial_reduce_launch(parts.data(), static_cast<int>(a->P), Mr, Hc, H, &dst, 1, Mr, H, sr,
+                                           two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0);
       if (rc != TP_OK) return rc;
       timing_end(t1, sr, TP_KERNEL_REDUCE, 4.0 * (a->P + 1) * Mr * Hc);
     }

@@ -352,9 +352,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int BK, int S>
+template <int BM, int BN, int BK, int S, int WAVES_M_ = 2, int WAVES_N_ = 4>
 struct DmaCfg {
-  static constexpr int WAVES_M = 2, WAVES_N = 4, NW = 8, THREADS = 512;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N, THREADS = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
   static constexpr int KK = BK / 32;                   // MFMA k-steps per stage
   static constexpr int AROW = BK * 2, ACH = BK / 8;    // A tile: bytes, 16B chunks per row
@@ -378,9 +378,9 @@ __device__ __forceinline__ int a_swz(int row) {
   return BK == 32 ? ((row >> 1) & 3) : (row & 7);
 }
 
-template <int BM, int BN, int BK, int S, int EPI>
-__global__ void __launch_bounds__(512, 1) bf16_gemm_dma(GemmArgs p) {
-  using C = DmaCfg<BM, BN, BK, S>;
+template <int BM, int BN, int BK, int S, int EPI, int WAVES_M = 2, int WAVES_N = 4>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmArgs p) {
+  using C = DmaCfg<BM, BN, BK, S, WAVES_M, WAVES_N>;
   constexpr int KK = C::KK;
   __shared__ __attribute__((aligned(1024))) char smem[S * C::STAGE];
   const int lane = threadIdx.x & 63;
@@ -424,6 +424,7 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_dma(GemmArgs p) {
       lds_dma16(W + w_src[q] + k0 * p.ldw, base + C::A_BYTES + (wave * C::W_PW + q) * 1024);
   };
 
+  static_assert(C::THREADS == 64 * WAVES_M * WAVES_N, "launch shape");
   // LDS byte offsets (within a stage) of this lane's operand fragments.
   // A: lane reads row (lane & 15) of a 16-row block, k chunk (lane >> 4).
   // W: ds_read_b64_tr_b16 over 16 lanes g: lane 4r + q reads k row 8g + r (+4)
@@ -578,10 +579,11 @@ __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int BK, int S, int EPI>
+template <int BM, int BN, int BK, int S, int EPI, int WAVES_M = 2, int WAVES_N = 4>
 hipError_t launch_dma(const GemmArgs& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((bf16_gemm_dma<BM, BN, BK, S, EPI>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((bf16_gemm_dma<BM, BN, BK, S, EPI, WAVES_M, WAVES_N>), dim3(static_cast<unsigned>(tiles)),
+                     dim3(64 * WAVES_M * WAVES_N), 0, s, p);
   return hipGetLastError();
 }
 
@@ -607,7 +609,17 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
     const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
     return static_cast<double>((tiles + kCUs - 1) / kCUs) * bm * bn / eff;
   };
-  const double c256 = cost(256, 256, 1.0), c128w = cost(256, 128, 0.85), c128 = cost(128, 128, 0.7);
+  // The tiles staging K 64 at a time need K % 64 == 0.
+  const bool k64 = p.K % 64 == 0;
+  // Problems too small to give every CU a 128 x 128 tile run 64 x 64 tiles
+  // (4 waves, 32 KiB of LDS): several workgroups then share each CU and hide
+  // one another's pipeline fill and write-out, which dominate at this size.
+  if (((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs) {
+    if (k64) return launch_dma<64, 64, 64, 2, EPI, 2, 2>(p, s);
+    return launch_dma<64, 64, 32, 4, EPI, 2, 2>(p, s);
+  }
+  const double c256 = k64 ? cost(256, 256, 1.0) : 1e300, c128w = k64 ? cost(256, 128, 0.85) : 1e300;
+  const double c128 = cost(128, 128, 0.7);
   if (c256 <= c128w && c256 <= c128) return launch_dma<256, 256, 64, 2, EPI>(p, s);
   if (c128w <= c128) return launch_dma<256, 128, 64, 3, EPI>(p, s);
   return launch_dma<128, 128, 32, 8, EPI>(p, s);

@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
 
 int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
                           float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
-                          hipStream_t stream) {
+                          hipStream_t stream, int64_t max_wgs) {
   if (rows == 0 || cols == 0) return TP_OK;
   RedArgs a{};
   auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
@@ -111,7 +111,8 @@ int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int
   a.ld_out = ld_out;
   constexpr int kUnroll = 2;
   const int64_t want = (total_v + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(want, 16384)));
+  const int64_t cap = max_wgs > 0 ? std::min<int64_t>(max_wgs, 16384) : 16384;
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(want, cap)));
   if (vec)
     hipLaunchKernelGGL((reduce_kernel<4, kUnroll>), grid, dim3(kThreads), 0, stream, a);
   else

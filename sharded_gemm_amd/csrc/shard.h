@@ -17,8 +17,9 @@ int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esi
 // out_row_block(row) <- sum over p of partials[p][row, :], ascending p, fp32.
 // rows_per_out rows go to each out[j]; out[j] has row stride ld_out.
 // Arguments already validated (1 <= P <= 64, 1 <= nout <= 64).
+// max_wgs > 0 caps the grid (the kernel strides over the rest).
 int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
                           float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
-                          hipStream_t stream);
+                          hipStream_t stream, int64_t max_wgs = 0);
 
 }  // namespace tpshard

@@ -119,7 +119,8 @@ FAKE = 1 << 40   # device-looking addresses; never dereferenced on these paths
 def _mlp_args(**kw):
     a = _abi.tp_mlp_args(dtype=_abi.TP_BF16, act=_abi.TP_ACT_GELU_ERF, M=64, H=64, F=64,
                          X=FAKE, A_i=FAKE + (1 << 20), B_i=FAKE + (2 << 20), Y_ws=FAKE + (3 << 20),
-                         Z_i=FAKE + (4 << 20), row_chunks=1, col_chunks=1, P=1, peer_partials=None, Z_out=None)
+                         Z_i=FAKE + (4 << 20), row_chunks=1, col_chunks=1, P=1, peer_partials=None, Z_out=None,
+                         reduce_workgroups=0)
     for k, v in kw.items():
         setattr(a, k, v)
     return a
@@ -137,6 +138,7 @@ def _mlp_args(**kw):
     (dict(P=65), _abi.TP_ERR_ARG),
     (dict(Y_ws=FAKE + 100), _abi.TP_ERR_ARG),          # overlaps X
     (dict(Z_i=FAKE + (3 << 20) + 64), _abi.TP_ERR_ARG),  # overlaps Y_ws
+    (dict(reduce_workgroups=-1), _abi.TP_ERR_ARG),
 ])
 def test_mlp_validation(kw, code):
     lib = _abi.load()

@@ -9,7 +9,8 @@
 // A workgroup streams a slice of one shard with the widest vector the
 // alignment allows (16, 8, 4 or 2 bytes per lane) and writes each element to
 // every device of the shard's group, so the source is read exactly once.
-// Destinations are written with non-temporal stores: they are not re-read.
+// The source is read once and destinations written once, so both use
+// non-temporal accesses.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -26,7 +27,7 @@ namespace tpshard {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 1;   // one vector per lane, one-shot grid: measured best on MI355X
 constexpr int kMaxShardsPerLaunch = 32;
 constexpr int kMaxDstPerLaunch = 64;
 
@@ -73,7 +74,7 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(MatArgs a) {
           off += static_cast<int64_t>(r - q * a.oext[i]) * a.ostride_b[i];
           r = q;
         }
-        v[u] = *reinterpret_cast<const V *>(src + off);
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + off));
       }
     }
     for (int d = d0; d < d1; ++d) {
@@ -178,7 +179,7 @@ int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esi
       ++k;
     }
     const int64_t want = (total_v + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-    const int64_t cap = std::max<int64_t>(1, 8192 / ns);
+    const int64_t cap = std::max<int64_t>(1, (1 << 20) / ns);
     const dim3 grid(static_cast<unsigned>(std::min(want, cap)), static_cast<unsigned>(ns));
     hipEvent_t t0 = timing_begin(stream);
     switch (vb) {

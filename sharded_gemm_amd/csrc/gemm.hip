@@ -37,6 +37,7 @@
 // shape runs, and do not depend on how the caller chunks M and N.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "gemm.h"
@@ -360,12 +361,11 @@ struct DmaCfg {
   static constexpr int AROW = BK * 2, ACH = BK / 8;    // A tile: bytes, 16B chunks per row
   static constexpr int ARPI = 1024 / AROW;             // A rows per DMA instruction
   static constexpr int WROW = BN * 2, WCH = BN / 8;    // W tile row (one k): bytes, chunks
-  static constexpr int WRPI = 1024 / WROW;             // W rows per DMA instruction
   static constexpr int A_BYTES = BM * AROW, STAGE = A_BYTES + BK * WROW;
   static constexpr int A_PW = A_BYTES / 1024 / NW;     // DMA instructions per wave per stage
   static constexpr int W_PW = BK * WROW / 1024 / NW;
   static constexpr int L = A_PW + W_PW;
-  static_assert((BK == 32 || BK == 64) && WN % 16 == 0 && WM % 16 == 0 && WCH >= 8, "tile shape");
+  static_assert((BK == 32 || BK == 64) && WN % 16 == 0 && WM % 16 == 0 && WCH % 8 == 0, "tile shape");
   static_assert(A_PW >= 1 && W_PW >= 1 && A_PW * NW * 1024 == A_BYTES && W_PW * NW * 1024 == BK * WROW, "DMA split");
   static_assert((S - 1) * L < 64, "vmcnt range");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
@@ -409,8 +409,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   }
 #pragma unroll
   for (int q = 0; q < C::W_PW; ++q) {
-    const int row = (wave * C::W_PW + q) * C::WRPI + lane / C::WCH;
-    const int chunk = (lane % C::WCH) ^ (2 * (row & 3));
+    // W rows need not divide the 1 KiB an instruction writes (BN = 192: 384 B),
+    // so the row and chunk come from this lane's byte offset in the W tile.
+    const int byte = (wave * C::W_PW + q) * 1024 + lane * 16;
+    const int row = byte / C::WROW;
+    const int chunk = ((byte % C::WROW) >> 4) ^ (2 * (row & 3));
     const int64_t gn = (n0 + chunk * 8 < p.N) ? n0 + chunk * 8 : p.N - 8;
     w_src[q] = static_cast<int64_t>(row) * p.ldw + gn;
   }
@@ -618,10 +621,12 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
     if (k64) return launch_dma<64, 64, 64, 2, EPI, 2, 2>(p, s);
     return launch_dma<64, 64, 32, 4, EPI, 2, 2>(p, s);
   }
-  const double c256 = k64 ? cost(256, 256, 1.0) : 1e300, c128w = k64 ? cost(256, 128, 0.85) : 1e300;
-  const double c128 = cost(128, 128, 0.7);
-  if (c256 <= c128w && c256 <= c128) return launch_dma<256, 256, 64, 2, EPI>(p, s);
-  if (c128w <= c128) return launch_dma<256, 128, 64, 3, EPI>(p, s);
+  const double c256 = k64 ? cost(256, 256, 1.0) : 1e300, c192 = k64 ? cost(256, 192, 0.95) : 1e300;
+  const double c128w = k64 ? cost(256, 128, 0.85) : 1e300, c128 = cost(128, 128, 0.7);
+  const double best = std::min(std::min(c256, c192), std::min(c128w, c128));
+  if (c256 == best) return launch_dma<256, 256, 64, 2, EPI>(p, s);
+  if (c192 == best) return launch_dma<256, 192, 64, 2, EPI>(p, s);
+  if (c128w == best) return launch_dma<256, 128, 64, 3, EPI>(p, s);
   return launch_dma<128, 128, 32, 8, EPI>(p, s);
 }
 

@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdint>
 
 #include "gemm.h"
@@ -353,6 +354,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left alone).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
 template <int BM, int BN, int BK, int S, int WAVES_M_ = 2, int WAVES_N_ = 4>
 struct DmaCfg {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N, THREADS = 64 * NW;
@@ -362,12 +368,17 @@ struct DmaCfg {
   static constexpr int ARPI = 1024 / AROW;             // A rows per DMA instruction
   static constexpr int WROW = BN * 2, WCH = BN / 8;    // W tile row (one k): bytes, chunks
   static constexpr int A_BYTES = BM * AROW, STAGE = A_BYTES + BK * WROW;
-  static constexpr int A_PW = A_BYTES / 1024 / NW;     // DMA instructions per wave per stage
-  static constexpr int W_PW = BK * WROW / 1024 / NW;
-  static constexpr int L = A_PW + W_PW;
+  // DMA instructions (1 KiB each) per stage: the A pieces split evenly over
+  // the waves; the W pieces are dealt round-robin, so when they do not divide
+  // evenly the first W_REM waves issue one more than the rest.
+  static constexpr int NA = A_BYTES / 1024, NWP = BK * WROW / 1024;
+  static constexpr int A_PW = NA / NW;
+  static constexpr int W_PW = (NWP + NW - 1) / NW, W_REM = NWP % NW;
+  static constexpr int L_HI = A_PW + W_PW, L_LO = W_REM ? L_HI - 1 : L_HI;   // per-wave DMA count
   static_assert((BK == 32 || BK == 64) && WN % 16 == 0 && WM % 16 == 0 && WCH % 8 == 0, "tile shape");
-  static_assert(A_PW >= 1 && W_PW >= 1 && A_PW * NW * 1024 == A_BYTES && W_PW * NW * 1024 == BK * WROW, "DMA split");
-  static_assert((S - 1) * L < 64, "vmcnt range");
+  static_assert(A_PW >= 1 && NA % NW == 0 && NA * 1024 == A_BYTES && NWP * 1024 == BK * WROW && NWP >= NW,
+                "DMA split");
+  static_assert((S - 1) * L_HI < 64, "vmcnt range");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
 };
 
@@ -394,6 +405,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TP_LDS char *)smem));
   const uint16_t *A = static_cast<const uint16_t *>(p.a);
   const uint16_t *W = static_cast<const uint16_t *>(p.w);
+  // The output stride is only used after the main loop; left to the compiler
+  // its scalar load would still be in flight when the loop starts, and since
+  // scalar loads return out of order the first LDS wait of every iteration
+  // would have to drain all reads (lgkmcnt(0)).  Make it arrive here.
+  const int64_t ldc = p.ldc;
+  asm volatile("" ::"s"(ldc));
 
   // Source of each of this lane's DMA pieces (elements, before the stage's k
   // offset).  Lane order fixes the LDS position, so the swizzle is applied by
@@ -411,7 +428,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   for (int q = 0; q < C::W_PW; ++q) {
     // W rows need not divide the 1 KiB an instruction writes (BN = 192: 384 B),
     // so the row and chunk come from this lane's byte offset in the W tile.
-    const int byte = (wave * C::W_PW + q) * 1024 + lane * 16;
+    // A piece index past the tile (the short waves' last slot) is never issued.
+    const int byte = min(wave + q * C::NW, C::NWP - 1) * 1024 + lane * 16;
     const int row = byte / C::WROW;
     const int chunk = ((byte % C::WROW) >> 4) ^ (2 * (row & 3));
     const int64_t gn = (n0 + chunk * 8 < p.N) ? n0 + chunk * 8 : p.N - 8;
@@ -424,7 +442,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
     for (int q = 0; q < C::A_PW; ++q) lds_dma16(A + a_src[q] + k0, base + (wave * C::A_PW + q) * 1024);
 #pragma unroll
     for (int q = 0; q < C::W_PW; ++q)
-      lds_dma16(W + w_src[q] + k0 * p.ldw, base + C::A_BYTES + (wave * C::W_PW + q) * 1024);
+      if (C::W_REM == 0 || q + 1 < C::W_PW || wave < C::W_REM)
+        lds_dma16(W + w_src[q] + k0 * p.ldw, base + C::A_BYTES + (wave + q * C::NW) * 1024);
+  };
+  // s_waitcnt vmcnt(n * this wave's DMA count per stage).
+  const bool dma_hi = C::W_REM == 0 || wave < C::W_REM;
+  auto wait_stages = [&](auto n) {
+    constexpr int N = decltype(n)::value;
+    if (dma_hi) wait_vmcnt<N * C::L_HI>(); else wait_vmcnt<N * C::L_LO>();
   };
 
   static_assert(C::THREADS == 64 * WAVES_M * WAVES_N, "launch shape");
@@ -481,17 +506,19 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
 
   // Stage t lives in slot t % S.  The barrier that opens stage t (after this
   // wave's loads of stage t have landed: vmcnt) also proves every wave has
-  // read stage t-1 into registers, so stage t+S-1 is issued into its slot.
+  // read stage t-1 into registers (lgkmcnt(0) before it: the DMA is invisible
+  // to the compiler's own waits), so stage t+S-1 is issued into its slot.
   const int nst = static_cast<int>(p.K / BK), nu = nst * KK;
   auto open_stage = [&](int st) {
-    if (st + S - 2 < nst) wait_vmcnt<(S - 2) * C::L>(); else wait_vmcnt<0>();
+    if (st + S - 2 < nst) wait_stages(std::integral_constant<int, S - 2>{}); else wait_vmcnt<0>();
+    wait_lgkmcnt0();
     __syncthreads();
     if (st + S - 1 < nst) issue(st + S - 1, (st + S - 1) % S);
   };
 #pragma unroll
   for (int st = 0; st < S; ++st)
     if (st < nst) issue(st, st);
-  if (nst >= S) wait_vmcnt<(S - 1) * C::L>(); else wait_vmcnt<0>();
+  if (nst >= S) wait_stages(std::integral_constant<int, S - 1>{}); else wait_vmcnt<0>();
   __syncthreads();
   bf16x8_t fa0[C::TM], fb0[C::TN], fa1[C::TM], fb1[C::TN];
   read(0, fa0, fb0);
@@ -518,11 +545,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
       if (n >= p.N) continue;   // N is a multiple of 8 on this path
       f32x4_t v = acc[i][j];
       if constexpr (EPI == kEpiF32) {
-        *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + m * p.ldc + n) = v;
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + m * ldc + n) = v;
       } else {
         if constexpr (EPI == kEpiGeluBf16)
           v = f32x4_t{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
-        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.c) + m * p.ldc + n) =
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.c) + m * ldc + n) =
             u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }

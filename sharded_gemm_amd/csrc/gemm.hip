@@ -28,6 +28,12 @@
 //  * The MFMA gets W as its first operand and A as its second, so each lane
 //    owns one output row and four adjacent columns: 16-byte (fp32) or 8-byte
 //    (bf16) stores.
+// Ping-pong path (bf16_gemm_pp) for the 256-row tiles: the same tile, DMA and
+// LDS layout, but the two waves sharing a SIMD run in opposite phases.  The
+// waves of tile rows 0..127 (group A) and of rows 128..255 (group B) sit one
+// barrier apart: between two barriers one group runs its MFMAs while the other
+// reads its next stage from LDS, so the MFMA pipe is fed while LDS reads and
+// their waits happen.  Group A issues all of a stage's DMA.
 // Ragged path (bf16_gemm_ragged): the same MFMA on a 128 x 128 tile with
 // register-staged, bounds-checked loads, for shapes the DMA path cannot take
 // (K not a multiple of 32, N not a multiple of 8, misaligned pointers).
@@ -496,11 +502,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Rows inner: consecutive MFMAs share the W operand (measured a few percent
+  // faster than sharing the A operand on the 8 x 3 wave tile).
   auto mma = [&](const bf16x8_t (&fa)[C::TM], const bf16x8_t (&fb)[C::TN]) {
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+    for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j)
+      for (int i = 0; i < C::TM; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
@@ -554,6 +562,185 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
       }
     }
   }
+}
+
+// ---- ping-pong path -------------------------------------------------------
+
+// DMA of 16 bytes at sbase + voff (32-bit byte offset) into LDS M0 + 16 * lane.
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// Barriers of the schedule, each with the wait it needs folded in, so no LDS
+// read or DMA can be moved across it.
+__device__ __forceinline__ void barrier_lgkm0() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void barrier_vm0() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void barrier_raw() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The ping-pong kernel: BK = 64, two slots, 8 waves (2 x 4).
+template <int BM, int BN, int EPI>
+__global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
+  constexpr int BK = 64, S = 2;
+  using C = DmaCfg<BM, BN, BK, S, 2, 4>;
+  constexpr int NG = 4;                              // waves of the issuing group
+  constexpr int A_PW = C::NA / NG, W_PW = C::NWP / NG, L = A_PW + W_PW;
+  static_assert(C::NA % NG == 0 && C::NWP % NG == 0, "DMA split");
+  __shared__ __attribute__((aligned(1024))) char smem[S * C::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / 4, wn = wave % 4;
+  const bool grpA = wm == 0;
+  const int tiles_m = static_cast<int>((p.M + BM - 1) / BM);
+  const int tiles_n = static_cast<int>((p.N + BN - 1) / BN);
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TP_LDS char *)smem));
+  const int64_t ldc = p.ldc;
+  asm volatile("" ::"s"(ldc));
+
+  // Group A's DMA pieces as 32-bit byte offsets from the operand bases (the
+  // launcher only picks this kernel when every offset fits).
+  uint32_t a_src[A_PW], w_src[W_PW];
+#pragma unroll
+  for (int q = 0; q < A_PW; ++q) {
+    const int row = ((wave & 3) * A_PW + q) * C::ARPI + lane / C::ACH;
+    const int chunk = (lane % C::ACH) ^ a_swz<BK>(row);
+    const int64_t gm = (m0 + row < p.M) ? m0 + row : p.M - 1;
+    a_src[q] = static_cast<uint32_t>((gm * p.lda + chunk * 8) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < W_PW; ++q) {
+    const int byte = ((wave & 3) * W_PW + q) * 1024 + lane * 16;
+    const int row = byte / C::WROW;
+    const int chunk = ((byte % C::WROW) >> 4) ^ (2 * (row & 3));
+    const int64_t gn = (n0 + chunk * 8 < p.N) ? n0 + chunk * 8 : p.N - 8;
+    w_src[q] = static_cast<uint32_t>((static_cast<int64_t>(row) * p.ldw + gn) * 2);
+  }
+  const uint32_t a_step = BK * 2, w_step = static_cast<uint32_t>(BK * p.ldw * 2);
+  auto issue = [&](int st, int slot) {
+    const uint32_t base = lds0 + slot * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < A_PW; ++q)
+      lds_dma16_s(p.a, a_src[q] + st * a_step, base + ((wave & 3) * A_PW + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < W_PW; ++q)
+      lds_dma16_s(p.w, w_src[q] + st * w_step, base + C::A_BYTES + ((wave & 3) * W_PW + q) * 1024);
+  };
+
+  // LDS byte offsets of this lane's W fragments (as in bf16_gemm_dma).
+  uint32_t w_off[C::TN];
+  {
+    const int g = lane >> 4, r = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int col = wn * C::WN + j * 16 + 4 * q;
+      const int chunk = col >> 3, byte = (col & 7) * 2;
+      const int k = 8 * g + r;
+      w_off[j] = C::A_BYTES + k * C::WROW + ((chunk ^ (2 * (k & 3))) << 4) + byte;
+    }
+  }
+  // Both k-steps of the stage in slot `slot`: W rows move by 32 per k-step
+  // (k & 3, and so the swizzle, unchanged).
+  bf16x8_t fa[2][C::TM], fb[2][C::TN];
+  auto read_stage = [&](int slot) {
+    const TP_LDS char *base = (const TP_LDS char *)smem + slot * C::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const int row = wm * C::WM + i * 16 + (lane & 15), chunk = kk * 4 + (lane >> 4);
+        const uint32_t off = row * C::AROW + ((chunk ^ a_swz<BK>(row)) << 4);
+        fa[kk][i] = *(const TP_LDS bf16x8_t *)(base + off);
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const uint32_t o = w_off[j] + kk * 32 * C::WROW;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + o));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + o + 4 * C::WROW));
+        fb[kk][j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+  f32x4_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto mma_stage = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+  };
+
+  // Schedule (barriers counted from 0; both groups execute 2 * nst + 1):
+  //   A: issue 0,1 | wait | #0 | M_0 #1 C_0 #2 | M_1 #3 C_1 #4 | ... | M_{n-1} #2n-1 C_{n-1} #2n
+  //   B:              | #0 | #1 | M_0 #2 C_0 #3 | ... | M_{n-1} #2n C_{n-1}
+  // Between two barriers one group runs MFMAs while the other reads LDS.
+  // A issues stage t+1 in M_t into the slot of stage t-1, which both groups
+  // finished reading before #2t; A waits for it at the end of C_t.
+  const int nst = static_cast<int>(p.K / BK);
+  if (grpA) {
+    issue(0, 0);
+    if (nst > 1) { issue(1, 1); wait_vmcnt<L>(); } else { wait_vmcnt<0>(); }
+  }
+  barrier_raw();
+  if (!grpA) barrier_raw();
+  for (int t = 0; t < nst; ++t) {
+    if (grpA && t >= 1 && t + 1 < nst) issue(t + 1, (t + 1) & 1);
+    read_stage(t & 1);
+    barrier_lgkm0();
+    mma_stage();
+    if (grpA) {
+      barrier_vm0();
+    } else if (t + 1 < nst) {
+      barrier_raw();
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int64_t m = m0 + wm * C::WM + i * 16 + (lane & 15);
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int64_t n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
+      if (n >= p.N) continue;
+      f32x4_t v = acc[i][j];
+      if constexpr (EPI == kEpiF32) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + m * ldc + n) = v;
+      } else {
+        if constexpr (EPI == kEpiGeluBf16)
+          v = f32x4_t{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.c) + m * ldc + n) =
+            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int EPI>
+hipError_t launch_pp(const GemmArgs &p, hipStream_t s) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((bf16_gemm_pp<BM, BN, EPI>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
+  return hipGetLastError();
 }
 
 // ---- plain fp32 kernel (tiny fp32 workload) ------------------------------
@@ -651,8 +838,10 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   const double c256 = k64 ? cost(256, 256, 1.0) : 1e300, c192 = k64 ? cost(256, 192, 0.95) : 1e300;
   const double c128w = k64 ? cost(256, 128, 0.85) : 1e300, c128 = cost(128, 128, 0.7);
   const double best = std::min(std::min(c256, c192), std::min(c128w, c128));
-  if (c256 == best) return launch_dma<256, 256, 64, 2, EPI>(p, s);
-  if (c192 == best) return launch_dma<256, 192, 64, 2, EPI>(p, s);
+  // The ping-pong kernel addresses operands with 32-bit byte offsets.
+  const bool off32 = p.M * p.lda * 2 < (int64_t{1} << 31) && p.K * p.ldw * 2 < (int64_t{1} << 31);
+  if (c256 == best) return off32 ? launch_pp<256, 256, EPI>(p, s) : launch_dma<256, 256, 64, 2, EPI>(p, s);
+  if (c192 == best) return off32 ? launch_pp<256, 192, EPI>(p, s) : launch_dma<256, 192, 64, 2, EPI>(p, s);
   if (c128w == best) return launch_dma<256, 128, 64, 3, EPI>(p, s);
   return launch_dma<128, 128, 32, 8, EPI>(p, s);
 }

@@ -48,7 +48,11 @@ def _bf16_exact(x64):
 # ---------------------------------------------------------------- exact cases
 
 @pytest.mark.parametrize("M,H,F", [(300, 264, 136), (256, 512, 512), (77, 45, 51), (1, 8, 8), (513, 1040, 264),
-                                   (333, 320, 200), (515, 256, 96), (1000, 512, 264), (4100, 1024, 776)])
+                                   (333, 320, 200), (515, 256, 96), (1000, 512, 264), (4100, 1024, 776),
+                                   # ping-pong kernel, 256 x 256 tiles (ragged M and N; 1, 2 and 7 stages)
+                                   (4100, 64, 6152), (4100, 128, 6152), (4100, 448, 6152),
+                                   # ping-pong kernel, 256 x 192 tiles
+                                   (2000, 128, 6136), (2000, 320, 6136)])
 def test_hidden_integer_exact(M, H, F):
     """Small-integer inputs make X A_i exact in fp32, so Y must equal the
     RNE-to-bf16 rounding of the oracle's exact value, bit for bit."""
@@ -74,7 +78,9 @@ def _one_hot_columns(H, F, seed):
 
 @pytest.mark.parametrize("M,H,F,Rc,Cc,P", [(512, 384, 256, 2, 3, 3), (93, 72, 40, 3, 2, 2),
                                             (50, 30, 22, 2, 3, 2), (1024, 1024, 512, 4, 4, 8),
-                                            (515, 256, 96, 1, 2, 2), (1030, 640, 320, 2, 5, 4)])
+                                            (515, 256, 96, 1, 2, 2), (1030, 640, 320, 2, 5, 4),
+                                            # GEMM2 on the ping-pong kernel (fp32 out): 256 x 192, 256 x 256
+                                            (2000, 6136, 128, 1, 1, 2), (4100, 6152, 64, 1, 1, 2)])
 def test_chain_integer_exact(M, H, F, Rc, Cc, P):
     """Exact whole chain: Y small integers, fp32 sums exact, so Z_i and Z_out
     must equal the oracle bit for bit, chunked, on two streams."""

@@ -12,7 +12,8 @@ Modules
   reduce  -- partial-sum -> full and partial-sum -> split reduction
              (OneFlow SBP "partial"; ColossalAI 1D-TP all-reduce)
   mlp     -- GeLU and one rank's column->row MLP share, plus the all-rank sum
-             (ColossalAI 1D tensor parallelism, sections 2 and 2.1)
+             (ColossalAI 1D tensor parallelism, sections 2 and 2.1), and its
+             backward (section 2.2; DeepSpeed-Domino, backward)
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against the pages' worked examples, closed forms, invariants, library special

@@ -11,6 +11,10 @@ Sources:
 * ONNX multi-device proposal, operator-group rules: unary elementwise ops
   (Erf among them) accept any input sharding, so GeLU commutes with the column
   split; MatMul with a sharded K axis yields a partial sum.
+* ColossalAI 1D tensor parallelism, section 2.2, and the DeepSpeed-Domino
+  article, "backward": the column-parallel layer's input gradient is a partial
+  per rank that an all-reduce sums; each gradient matmul splits into an
+  input-gradient GEMM and an independent weight-gradient GEMM.
 
 GeLU is never written out on the pages; the reading taken is the exact form
 x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).  Everything is evaluated in float64
@@ -82,3 +86,49 @@ def mlp_rank_rows(X, A_i, B_i, rows, act=GELU_ERF):
     """
     x = _f64(X)[np.asarray(rows, dtype=np.int64)]
     return mlp_rank(x, A_i, B_i, act)
+
+
+# ---- backward ([CAI] section 2.2; Domino article, "backward") --------------
+#
+# The loss is reached through Z, with dZ = dL/dZ given.  Since the forward is
+# Z = sum_i act(X A_i) B_i, rank i's share of the chain rule is
+#   dY_i = dZ B_i^T                  (row-parallel layer: no communication)
+#   dH_i = dY_i * act'(X A_i)        (elementwise through the activation)
+#   dX_i = dH_i A_i^T                (a partial: dX is the sum over ranks, the
+#                                     all-reduce of the column-parallel layer)
+#   dA_i = X^T dH_i,  dB_i = Y_i^T dZ   (weight gradients, no communication)
+
+
+def gelu_deriv(x):
+    """d/dx [x Phi(x)] = Phi(x) + x phi(x), phi the standard normal density, float64."""
+    x = np.asarray(x, dtype=np.float64)
+    cdf = 0.5 * (1.0 + _erf(x / math.sqrt(2.0)))
+    pdf = np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+    return cdf + x * pdf
+
+
+def backward_rank(X, A_i, B_i, dZ, act=GELU_ERF):
+    """Gradients of one rank's share, float64.
+
+    Returns a dict with dH (gradient at the pre-activation X A_i, [M, F]),
+    dX_i (this rank's partial input gradient, [M, H]), dA_i ([H, F]) and
+    dB_i ([F, H]).
+    """
+    x, a, b, dz = _f64(X), _f64(A_i), _f64(B_i), _f64(dZ)
+    if x.shape[1] != a.shape[0] or a.shape[1] != b.shape[0] or b.shape[1] != x.shape[1] or dz.shape != (x.shape[0], b.shape[1]):
+        raise ValueError("shape mismatch")
+    h = x @ a
+    y = gelu(h) if act == GELU_ERF else h
+    dy = dz @ b.T
+    dh = dy * gelu_deriv(h) if act == GELU_ERF else dy
+    return {"dH": dh, "dX_i": dh @ a.T, "dA_i": x.T @ dh, "dB_i": y.T @ dz}
+
+
+def backward_all_ranks(X, A_shards, B_shards, dZ, act=GELU_ERF):
+    """dX = sum over ranks of dX_i (the all-reduced input gradient), with the
+    per-rank weight gradients."""
+    outs = [backward_rank(X, a, b, dZ, act) for a, b in zip(A_shards, B_shards)]
+    dX = outs[0]["dX_i"].copy()
+    for o in outs[1:]:
+        dX += o["dX_i"]
+    return dX, [o["dA_i"] for o in outs], [o["dB_i"] for o in outs]

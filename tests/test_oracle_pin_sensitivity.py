@@ -114,3 +114,51 @@ def test_reduce_split_wrong_block(monkeypatch):
     real = R.reduce_split
     monkeypatch.setattr(R, "reduce_split", lambda parts, s: list(reversed(real(parts, s))))
     assert _fails(TR.test_split_blocks_concatenate_to_full)
+
+
+# ---- backward --------------------------------------------------------------
+
+import test_oracle_backward as TB  # noqa: E402
+
+
+def test_gelu_deriv_missing_density_term(monkeypatch):
+    monkeypatch.setattr(O, "gelu_deriv", lambda x: 0.5 * (1 + erf(np.asarray(x, float) / math.sqrt(2))))
+    assert _fails(TB.test_gelu_deriv_closed_forms)
+    assert _fails(TB.test_backward_matches_finite_differences, O.GELU_ERF, 3, 4, 5)
+
+
+def test_gelu_deriv_wrong_sign(monkeypatch):
+    real = O.gelu_deriv
+    monkeypatch.setattr(O, "gelu_deriv", lambda x: real(-np.asarray(x, float)))
+    assert _fails(TB.test_gelu_deriv_matches_finite_difference)
+
+
+def test_backward_skips_activation_derivative(monkeypatch):
+    def bad(X, A_i, B_i, dZ, act=O.GELU_ERF):
+        x, a, b, dz = O._f64(X), O._f64(A_i), O._f64(B_i), O._f64(dZ)
+        h = x @ a
+        y = O.gelu(h) if act == O.GELU_ERF else h
+        dh = dz @ b.T
+        return {"dH": dh, "dX_i": dh @ a.T, "dA_i": x.T @ dh, "dB_i": y.T @ dz}
+    monkeypatch.setattr(O, "backward_rank", bad)
+    assert _fails(TB.test_backward_matches_finite_differences, O.GELU_ERF, 3, 4, 5)
+
+
+def test_backward_weight_gradient_uses_pre_activation(monkeypatch):
+    real = O.backward_rank
+
+    def bad(X, A_i, B_i, dZ, act=O.GELU_ERF):
+        g = real(X, A_i, B_i, dZ, act)
+        g["dB_i"] = (O._f64(X) @ O._f64(A_i)).T @ O._f64(dZ)   # H instead of Y = act(H)
+        return g
+    monkeypatch.setattr(O, "backward_rank", bad)
+    assert _fails(TB.test_backward_matches_finite_differences, O.GELU_ERF, 3, 4, 5)
+
+
+def test_backward_rank_sum_drops_a_rank(monkeypatch):
+    real = O.backward_all_ranks
+
+    def bad(X, A_shards, B_shards, dZ, act=O.GELU_ERF):
+        return real(X, A_shards[:-1], B_shards[:-1], dZ, act)[0], *real(X, A_shards, B_shards, dZ, act)[1:]
+    monkeypatch.setattr(O, "backward_all_ranks", bad)
+    assert _fails(TB.test_sum_of_rank_gradients_is_the_unsharded_gradient, 3)

@@ -191,6 +191,9 @@ typedef struct {
   int64_t reduce_workgroups; /* upper bound on the reduce kernel's workgroups when it runs
                         beside the GEMMs on s_reduce (it then shares the CUs with
                         them); 0 = library default (256); >= 0 */
+  void *H_out;       /* optional [M, F] (dtype): X A_i before the activation, rounded to
+                        dtype (RNE), kept for the backward pass; NULL = not stored.
+                        Must be NULL when act = TP_ACT_NONE (H would equal Y). */
 } tp_mlp_args;
 
 /*
@@ -212,10 +215,61 @@ typedef struct {
  */
 int tp_colrow_mlp(const tp_mlp_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
 
+/* ---- backward of one rank's column->row MLP ------------------------- */
+typedef struct {
+  int32_t dtype;     /* as in the forward: TP_BF16 (X, A_i, B_i, H_i, Y_i, dZ, dH_ws bf16,
+                        fp32 accumulate) or TP_F32 (all fp32) */
+  int32_t act;       /* the forward's activation */
+  int64_t M, H, F;   /* X[M,H], A_i[H,F], B_i[F,H]; all >= 1 */
+  const void *X;     /* [M, H] the forward's input */
+  const void *A_i;   /* [H, F] this rank's column slice of A */
+  const void *B_i;   /* [F, H] this rank's row slice of B */
+  const void *H_i;   /* [M, F] the forward's pre-activation X A_i (its H_out); required for
+                        TP_ACT_GELU_ERF, ignored for TP_ACT_NONE */
+  const void *Y_i;   /* [M, F] the forward's Y = act(X A_i) (its Y_ws) */
+  const void *dZ;    /* [M, H] gradient of the loss with respect to the MLP output Z (the
+                        sum over ranks, so the same on every rank) */
+  void *dH_ws;       /* [M, F] caller-owned workspace; on completion holds the gradient at
+                        the pre-activation, (dZ B_i^T) * act'(H_i), rounded to dtype */
+  float *dX_i;       /* [M, H] fp32: this rank's partial input gradient dH A_i^T ([CAI]
+                        section 2.2: the column-parallel layer's input gradient is a
+                        partial that must be summed over ranks) */
+  float *dA_i;       /* [H, F] fp32 weight gradient X^T dH */
+  float *dB_i;       /* [F, H] fp32 weight gradient Y_i^T dZ */
+  int32_t accumulate;/* 1: dA_i and dB_i are added to (gradient accumulation across
+                        micro-batches); 0: overwritten */
+  int64_t row_chunks;/* R >= 1, divides M: independent row chunks ([DOM] micro-batches) */
+  int64_t P;         /* tensor-parallel degree, 1..64; 1 = no reduction of dX */
+  const float *const *peer_dX; /* host array of P-1 device pointers, each [M,H] fp32: the
+                        input-gradient partials of virtual ranks 1..P-1 */
+  float *dX_out;     /* [M,H] fp32, required when P > 1: dX_i + sum of peers, written chunk
+                        by chunk on s_reduce; may equal dX_i */
+  int64_t reduce_workgroups; /* as in the forward; 0 = library default; >= 0 */
+} tp_mlp_bwd_args;
+
+/*
+ * Enqueue the backward of one rank's MLP share ([CAI] section 2.2; [DOM]
+ * "backward": each gradient GEMM splits into an input-gradient GEMM and an
+ * independent weight-gradient GEMM, so the reduction of one micro-batch's input
+ * gradient hides behind that micro-batch's weight-gradient GEMMs).  For each row
+ * chunk r, on s_compute: dH[r] = (dZ[r] B_i^T) * act'(H_i[r]) (one GEMM, the
+ * derivative applied to its fp32 accumulator), dX_i[r] = dH[r] A_i^T; then, when
+ * P > 1, s_reduce waits for chunk r and reduces dX[r] into dX_out while
+ * s_compute runs dA_i += X[r]^T dH[r] and dB_i += Y_i[r]^T dZ[r].  The weight
+ * gradients continue one fp32 accumulation across chunks (each GEMM starts
+ * from the previous chunk's result), so the result does not depend on R.
+ * Before returning, s_compute waits for s_reduce.  Capturable into a HIP graph.
+ * Errors: TP_ERR_ARG (null or overlapping buffers, bad dtype/act, sizes < 1,
+ *         P out of range), TP_ERR_INDIVISIBLE (R does not divide M), TP_ERR_HIP.
+ */
+int tp_colrow_mlp_backward(const tp_mlp_bwd_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
+
 /* ---- per-kernel timing (measurement support) ---------------------------- */
-/* Kernel families timed by the optional instrumentation below. */
+/* Kernel families timed by the optional instrumentation below: the forward's
+ * GEMMs, the backward's input-gradient GEMMs (dH and dX) and its
+ * weight-gradient GEMMs (dA and dB). */
 enum { TP_KERNEL_MATERIALIZE = 0, TP_KERNEL_GEMM1 = 1, TP_KERNEL_GEMM2 = 2, TP_KERNEL_REDUCE = 3,
-       TP_KERNEL_KINDS = 4 };
+       TP_KERNEL_GEMM_DGRAD = 4, TP_KERNEL_GEMM_WGRAD = 5, TP_KERNEL_KINDS = 6 };
 
 typedef struct {
   int64_t launches;  /* kernel launches timed since the last read */

@@ -35,9 +35,9 @@ TP_ACT_GELU_ERF = 1
 
 # Every symbol include/tpshard.h declares.
 EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_shard_materialize",
-           "tp_partial_reduce", "tp_colrow_mlp", "tp_timing_enable", "tp_timing_read")
+           "tp_partial_reduce", "tp_colrow_mlp", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
-TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce")
+TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad")
 
 
 class TpError(RuntimeError):
@@ -82,6 +82,17 @@ class tp_mlp_args(C.Structure):
                 ("Y_ws", C.c_void_p), ("Z_i", C.c_void_p),
                 ("row_chunks", C.c_int64), ("col_chunks", C.c_int64), ("P", C.c_int64),
                 ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
+                ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p)]
+
+
+class tp_mlp_bwd_args(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("act", C.c_int32),
+                ("M", C.c_int64), ("H", C.c_int64), ("F", C.c_int64),
+                ("X", C.c_void_p), ("A_i", C.c_void_p), ("B_i", C.c_void_p),
+                ("H_i", C.c_void_p), ("Y_i", C.c_void_p), ("dZ", C.c_void_p),
+                ("dH_ws", C.c_void_p), ("dX_i", C.c_void_p), ("dA_i", C.c_void_p), ("dB_i", C.c_void_p),
+                ("accumulate", C.c_int32), ("row_chunks", C.c_int64), ("P", C.c_int64),
+                ("peer_dX", C.POINTER(C.c_void_p)), ("dX_out", C.c_void_p),
                 ("reduce_workgroups", C.c_int64)]
 
 
@@ -117,6 +128,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
                                       C.c_int32, C.c_int64, C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
     lib.tp_colrow_mlp.restype = C.c_int
     lib.tp_colrow_mlp.argtypes = [C.POINTER(tp_mlp_args), C.c_void_p, C.c_void_p]
+    lib.tp_colrow_mlp_backward.argtypes = [C.POINTER(tp_mlp_bwd_args), C.c_void_p, C.c_void_p]
+    lib.tp_colrow_mlp_backward.restype = C.c_int
     lib.tp_timing_enable.restype = C.c_int
     lib.tp_timing_enable.argtypes = [C.c_int32]
     lib.tp_timing_read.restype = C.c_int
@@ -264,8 +277,9 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
 
 
 def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
-                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0):
-    """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers)."""
+                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0, H_out=None):
+    """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers);
+    optionally H_out = X A_i (the pre-activation kept for the backward)."""
     lib = load()
     M, H = int(X.shape[0]), int(X.shape[1])
     F = int(A_i.shape[1])
@@ -275,6 +289,8 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
         raise ValueError("shapes must be X[M,H], A_i[H,F], B_i[F,H], Y_ws[M,F], Z_i[M,H]")
     if not (X.dtype == A_i.dtype == B_i.dtype == Y_ws.dtype):
         raise TypeError("X, A_i, B_i and Y_ws must share one dtype")
+    if H_out is not None and (H_out.dtype != X.dtype or tuple(H_out.shape) != (M, F)):
+        raise TypeError("H_out must be [M, F] in the input dtype")
     import torch
     for t in [Z_i, *peers] + ([Z_out] if Z_out is not None else []):
         if t.dtype != torch.float32 or tuple(t.shape) != (M, H):
@@ -284,10 +300,46 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
                        X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
-                       Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups)
+                       Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out))
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
+
+
+def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *, row_chunks=1, peer_dX=(),
+                           dX_out=None, act=TP_ACT_GELU_ERF, accumulate=False, s_compute=None, s_reduce=None,
+                           reduce_workgroups=0):
+    """Backward of one rank's MLP share: dH_ws = (dZ B_i^T) * act'(H_i); dX_i = dH_ws A_i^T;
+    dX_out = dX_i + sum(peers); dA_i (+)= X^T dH_ws; dB_i (+)= Y_i^T dZ."""
+    lib = load()
+    M, H = int(X.shape[0]), int(X.shape[1])
+    F = int(A_i.shape[1])
+    peers = list(peer_dX)
+    if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Y_i.shape) != (M, F) \
+            or tuple(dZ.shape) != (M, H) or tuple(dH_ws.shape) != (M, F) or tuple(dX_i.shape) != (M, H) \
+            or tuple(dA_i.shape) != (H, F) or tuple(dB_i.shape) != (F, H) \
+            or (H_i is not None and tuple(H_i.shape) != (M, F)):
+        raise ValueError("shapes must be X, dZ, dX_i [M,H]; A_i, dA_i [H,F]; B_i, dB_i [F,H]; H_i, Y_i, dH_ws [M,F]")
+    ins = [X, A_i, B_i, Y_i, dZ, dH_ws] + ([H_i] if H_i is not None else [])
+    if any(t.dtype != X.dtype for t in ins):
+        raise TypeError("X, A_i, B_i, H_i, Y_i, dZ and dH_ws must share one dtype")
+    import torch
+    for t in [dX_i, dA_i, dB_i, *peers] + ([dX_out] if dX_out is not None else []):
+        if t.dtype != torch.float32:
+            raise TypeError("dX_i, dA_i, dB_i, peer dX and dX_out must be fp32")
+    for t in peers + ([dX_out] if dX_out is not None else []):
+        if tuple(t.shape) != (M, H):
+            raise ValueError("peer dX and dX_out must be [M, H]")
+    parr = (C.c_void_p * max(1, len(peers)))(*[_ptr(p) for p in peers])
+    args = tp_mlp_bwd_args(dtype=_dtype_code(X), act=act, M=M, H=H, F=F,
+                           X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), H_i=_ptr(H_i), Y_i=_ptr(Y_i), dZ=_ptr(dZ),
+                           dH_ws=_ptr(dH_ws), dX_i=_ptr(dX_i), dA_i=_ptr(dA_i), dB_i=_ptr(dB_i),
+                           accumulate=1 if accumulate else 0, row_chunks=row_chunks, P=1 + len(peers),
+                           peer_dX=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
+                           dX_out=_ptr(dX_out), reduce_workgroups=reduce_workgroups)
+    sc = _stream_ptr(s_compute)
+    sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
+    _check(lib.tp_colrow_mlp_backward(C.byref(args), sc, sr))
 
 
 def tp_timing_enable(on: bool = True):

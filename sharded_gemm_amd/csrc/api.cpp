@@ -202,6 +202,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
   if (a->P > 1 && (!a->peer_partials || !a->Z_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out");
   if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
+  if (a->H_out && a->act == TP_ACT_NONE) return fail(TP_ERR_ARG, "H_out needs an activation (it would equal Y)");
   const int64_t M = a->M, H = a->H, F = a->F;
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
       (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
@@ -215,6 +216,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   }
   std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
   if (a->P > 1 && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
+  if (a->H_out) outs.push_back({a->H_out, by, "H_out"});
   for (size_t i = 0; i < outs.size(); ++i) {
     for (const Buf& in : ins)
       if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, in.name);
@@ -234,13 +236,18 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
     if (rc != TP_OK) return rc;
   }
   const bool bf16 = a->dtype == TP_BF16;
-  const int epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? kEpiGeluBf16 : kEpiIdentBf16)
-                        : (a->act == TP_ACT_GELU_ERF ? kEpiGeluF32 : kEpiPlainF32);
+  const bool save = a->H_out != nullptr;
+  const int epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveBf16 : kEpiGeluBf16) : kEpiIdentBf16)
+                        : (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveF32 : kEpiGeluF32) : kEpiPlainF32);
   const int epi2 = bf16 ? kEpiF32 : kEpiPlainF32;
   std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t r = 0; r < R; ++r) {
     GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
                 static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
+    if (save) {
+      g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
+      g1.ldaux = F;
+    }
     hipEvent_t t0 = timing_begin(s0);
     hipError_t e = gemm_launch(g1, epi1, s0);
     if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
@@ -273,6 +280,124 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   }
   if (two) {
     hipEvent_t joined = ev[R * C];
+    hipError_t e;
+    if ((e = hipEventRecord(joined, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s0, joined, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  return TP_OK;
+}
+
+int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_stream_t s_reduce) {
+  clear_error();
+  if (!a) return fail(TP_ERR_ARG, "args is NULL");
+  const int64_t es = dtype_size(a->dtype);
+  if (!es) return fail(TP_ERR_ARG, "unknown dtype %d", a->dtype);
+  if (a->act != TP_ACT_NONE && a->act != TP_ACT_GELU_ERF) return fail(TP_ERR_ARG, "unknown act %d", a->act);
+  if (a->M < 1 || a->H < 1 || a->F < 1) return fail(TP_ERR_ARG, "M, H, F must be >= 1");
+  if (!a->X || !a->A_i || !a->B_i || !a->Y_i || !a->dZ || !a->dH_ws || !a->dX_i || !a->dA_i || !a->dB_i)
+    return fail(TP_ERR_ARG, "X, A_i, B_i, Y_i, dZ, dH_ws, dX_i, dA_i and dB_i must be non-NULL");
+  const bool gelu = a->act == TP_ACT_GELU_ERF;
+  if (gelu && !a->H_i) return fail(TP_ERR_ARG, "H_i (the forward's pre-activation) is needed for the GeLU derivative");
+  if (a->accumulate != 0 && a->accumulate != 1) return fail(TP_ERR_ARG, "accumulate must be 0 or 1");
+  if (a->row_chunks < 1) return fail(TP_ERR_ARG, "row_chunks must be >= 1");
+  if (a->M % a->row_chunks) return fail(TP_ERR_INDIVISIBLE, "row_chunks %lld does not divide M = %lld", (long long)a->row_chunks, (long long)a->M);
+  if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
+  if (a->P > 1 && (!a->peer_dX || !a->dX_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_dX and dX_out");
+  if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
+  const int64_t M = a->M, H = a->H, F = a->F;
+  if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) || (M / a->row_chunks) * H >= (int64_t(1) << 31))
+    return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
+  const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
+  struct Buf { const void *p; int64_t n; const char *name; };
+  std::vector<Buf> ins = {{a->X, bx, "X"}, {a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}, {a->Y_i, by, "Y_i"}, {a->dZ, bx, "dZ"}};
+  if (gelu) ins.push_back({a->H_i, by, "H_i"});
+  for (int64_t p = 1; p < a->P; ++p) {
+    if (!a->peer_dX[p - 1]) return fail(TP_ERR_ARG, "peer_dX[%lld] is NULL", (long long)(p - 1));
+    ins.push_back({a->peer_dX[p - 1], bz, "peer dX"});
+  }
+  std::vector<Buf> outs = {{a->dH_ws, by, "dH_ws"}, {a->dX_i, bz, "dX_i"}, {a->dA_i, H * F * 4, "dA_i"},
+                           {a->dB_i, F * H * 4, "dB_i"}};
+  if (a->P > 1 && a->dX_out != a->dX_i) outs.push_back({a->dX_out, bz, "dX_out"});
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Buf& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, in.name);
+    for (size_t j = 0; j < i; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+
+  hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
+  const int64_t R = a->row_chunks, Mr = M / R;
+  // As in the forward: a second stream only pays when a chunk's reduce can run
+  // beside GEMMs, which here are that chunk's weight-gradient GEMMs.
+  const bool two = (s0 != s1) && a->P > 1;
+  hipEvent_t *ev = nullptr;
+  if (two) {
+    const int rc = get_events(static_cast<size_t>(R + 1), &ev);
+    if (rc != TP_OK) return rc;
+  }
+  const bool bf16 = a->dtype == TP_BF16;
+  const int epi_dh = bf16 ? (gelu ? kEpiDGeluBf16 : kEpiIdentBf16) : (gelu ? kEpiDGeluF32 : kEpiPlainF32);
+  const int epi_f32 = bf16 ? kEpiF32 : kEpiPlainF32;
+  const char *X = static_cast<const char *>(a->X), *Yi = static_cast<const char *>(a->Y_i);
+  const char *dZ = static_cast<const char *>(a->dZ);
+  char *dH = static_cast<char *>(a->dH_ws);
+  std::vector<const float *> parts(static_cast<size_t>(a->P));
+  for (int64_t r = 0; r < R; ++r) {
+    // dH[r] = (dZ[r] B_i^T) * act'(H_i[r]): B_i is [F][H], i.e. W^T for W = B_i^T.
+    GemmArgs gd{dZ + r * Mr * H * es, a->B_i, dH + r * Mr * F * es, Mr, F, H, H, H, F};
+    gd.w_t = 1;
+    if (gelu) {
+      gd.aux = const_cast<char *>(static_cast<const char *>(a->H_i)) + r * Mr * F * es;
+      gd.ldaux = F;
+    }
+    hipEvent_t t0 = timing_begin(s0);
+    hipError_t e = gemm_launch(gd, epi_dh, s0);
+    if (e != hipSuccess) return hip_fail(e, "dH GEMM launch");
+    timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD, 2.0 * Mr * F * H);
+    // dX_i[r] = dH[r] A_i^T: A_i is [H][F], i.e. W^T for W = A_i^T.
+    GemmArgs gx{dH + r * Mr * F * es, a->A_i, a->dX_i + r * Mr * H, Mr, H, F, F, F, H};
+    gx.w_t = 1;
+    t0 = timing_begin(s0);
+    e = gemm_launch(gx, epi_f32, s0);
+    if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
+    timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD, 2.0 * Mr * H * F);
+    if (a->P > 1) {
+      hipStream_t sr = s0;
+      if (two) {
+        hipEvent_t done = ev[r];
+        if ((e = hipEventRecord(done, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = hipStreamWaitEvent(s1, done, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        sr = s1;
+      }
+      parts[0] = a->dX_i + r * Mr * H;
+      for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_dX[p - 1] + r * Mr * H;
+      float *dst = a->dX_out + r * Mr * H;
+      hipEvent_t t1 = timing_begin(sr);
+      const int rc = partial_reduce_launch(parts.data(), static_cast<int>(a->P), Mr, H, H, &dst, 1, Mr, H, sr,
+                                           two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0);
+      if (rc != TP_OK) return rc;
+      timing_end(t1, sr, TP_KERNEL_REDUCE, 4.0 * (a->P + 1) * Mr * H);
+    }
+    // Weight gradients, contracting over this chunk's rows and continuing the
+    // previous chunk's accumulation: dA_i += X[r]^T dH[r], dB_i += Y_i[r]^T dZ[r].
+    const int cont = (r > 0 || a->accumulate) ? 1 : 0;
+    GemmArgs ga{X + r * Mr * H * es, dH + r * Mr * F * es, a->dA_i, H, F, Mr, H, F, F};
+    ga.a_t = 1;
+    ga.acc_init = cont;
+    t0 = timing_begin(s0);
+    e = gemm_launch(ga, epi_f32, s0);
+    if (e != hipSuccess) return hip_fail(e, "dA GEMM launch");
+    timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * Mr);
+    GemmArgs gb{Yi + r * Mr * F * es, dZ + r * Mr * H * es, a->dB_i, F, H, Mr, F, H, H};
+    gb.a_t = 1;
+    gb.acc_init = cont;
+    t0 = timing_begin(s0);
+    e = gemm_launch(gb, epi_f32, s0);
+    if (e != hipSuccess) return hip_fail(e, "dB GEMM launch");
+    timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * F * H * Mr);
+  }
+  if (two) {
+    hipEvent_t joined = ev[R];
     hipError_t e;
     if ((e = hipEventRecord(joined, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(s0, joined, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");

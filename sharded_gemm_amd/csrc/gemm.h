@@ -7,22 +7,36 @@
 
 namespace tpshard {
 
-// C[M,N] = epilogue(A[M,K] * W[K,N]); all row-major with the given row strides
-// (in elements).  A, W are bf16 for the bf16 epilogues and fp32 for the fp32 ones.
+// C[M,N] = epilogue(A[M,K] * W[K,N]) with row strides in elements.
+//   a_t = 0: A is stored [M][lda] (k contiguous);   a_t = 1: A is stored [K][lda] (m contiguous), i.e. A^T is given.
+//   w_t = 0: W is stored [K][ldw] (n contiguous);   w_t = 1: W is stored [N][ldw] (k contiguous), i.e. W^T is given.
+// C is stored [M][ldc].  A, W are bf16 for the bf16 epilogues and fp32 for the fp32 ones.
 struct GemmArgs {
   const void *a;
   const void *w;
   void *c;
   int64_t M, N, K;
   int64_t lda, ldw, ldc;
+  int a_t = 0, w_t = 0;
+  // Second tensor of the epilogue, stored [M][ldaux] like C: the pre-activation
+  // written by the saving GeLU epilogues, read by the GeLU-derivative ones.
+  void *aux = nullptr;
+  int64_t ldaux = 0;
+  // fp32 outputs only: the accumulator starts from C's current contents
+  // (C += A W, continuing the same k order), else from zero.
+  int acc_init = 0;
 };
 
 enum {
-  kEpiGeluBf16 = 0,   // bf16 inputs, C = bf16(GeLU(acc))
-  kEpiIdentBf16 = 1,  // bf16 inputs, C = bf16(acc)
-  kEpiF32 = 2,        // bf16 inputs, C = acc (fp32)
-  kEpiGeluF32 = 3,    // fp32 inputs, C = GeLU(acc) (fp32)
-  kEpiPlainF32 = 4,   // fp32 inputs, C = acc (fp32)
+  kEpiGeluBf16 = 0,      // bf16 inputs, C = bf16(GeLU(acc))
+  kEpiIdentBf16 = 1,     // bf16 inputs, C = bf16(acc)
+  kEpiF32 = 2,           // bf16 inputs, C = acc (fp32)
+  kEpiGeluF32 = 3,       // fp32 inputs, C = GeLU(acc) (fp32)
+  kEpiPlainF32 = 4,      // fp32 inputs, C = acc (fp32)
+  kEpiGeluSaveBf16 = 5,  // bf16 inputs, C = bf16(GeLU(acc)), aux = bf16(acc)
+  kEpiDGeluBf16 = 6,     // bf16 inputs, C = bf16(acc * GeLU'(aux)), aux bf16
+  kEpiGeluSaveF32 = 7,   // fp32 inputs, C = GeLU(acc), aux = acc (fp32)
+  kEpiDGeluF32 = 8,      // fp32 inputs, C = acc * GeLU'(aux), aux fp32
 };
 
 // Enqueues the GEMM on stream s; returns the launch status.

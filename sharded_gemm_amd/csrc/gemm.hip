@@ -1,11 +1,18 @@
-// Dense GEMMs of the column->row MLP on gfx950.
+// Dense GEMMs of the column->row MLP on gfx950, forward and backward.
 //
-//   C[M,N] = epi(A[M,K] * W[K,N])      A row-major (K contiguous, row stride lda)
-//                                      W row-major (N contiguous, row stride ldw)
+//   C[M,N] = epi(A[M,K] * W[K,N])
 //
-// GEMM1 of the MLP is X * A_i followed by GeLU, stored as bf16 ([CAI] section
-// 2, column-parallel linear; [DOM] "GeMM GeLU GeMM"); GEMM2 is Y * B_i stored
-// as the fp32 partial ([CAI] section 2.1, row-parallel linear).
+// Each operand is given either k-contiguous (A as [M][lda], or W as W^T
+// [N][ldw]) or m/n-contiguous (A as A^T [K][lda], or W as [K][ldw]); the
+// layout flags of GemmArgs say which.
+//
+// Forward: GEMM1 is X * A_i followed by GeLU, stored as bf16 ([CAI] section 2,
+// column-parallel linear; [DOM] "GeMM GeLU GeMM"); GEMM2 is Y * B_i stored as
+// the fp32 partial ([CAI] section 2.1, row-parallel linear).
+// Backward ([CAI] section 2.2, [DOM] backward): dY = dZ * B_i^T with the GeLU
+// derivative fused (W given transposed), dX_i = dH * A_i^T (W transposed),
+// dA_i = X^T * dH and dB_i = Y^T * dZ (A transposed, accumulating over token
+// chunks).
 //
 // Main path (bf16_gemm_dma): v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 //  * 8 waves per workgroup (2 per SIMD) in a 2 x 4 grid over the output tile,
@@ -17,10 +24,11 @@
 //    the compiler, when it sees the builtin form, waits for every
 //    outstanding DMA (vmcnt(0)) before each LDS read, which would empty the
 //    ring; here the kernel counts vmcnt itself, per stage.
-//  * A (K contiguous) is read with ds_read_b128; W stays N-contiguous in LDS
-//    and is read with the gfx950 transposing read ds_read_b64_tr_b16, which
-//    hands each lane the 4 consecutive k of one column n (two reads make the 8
-//    k an MFMA operand needs), so no transpose pass exists anywhere.
+//  * A k-contiguous operand tile is read with ds_read_b128.  An m/n-contiguous
+//    one stays that way in LDS and is read with the gfx950 transposing read
+//    ds_read_b64_tr_b16, which hands each lane the 4 consecutive k of one
+//    row / column (two reads make the 8 k an MFMA operand needs), so no
+//    transpose pass exists anywhere.
 //  * XOR swizzles on 16-byte chunks keep the DMA writes and both kinds of LDS
 //    read free of bank conflicts.
 //  * Fragments are double-buffered in registers across k steps: the LDS reads
@@ -38,14 +46,15 @@
 // register-staged, bounds-checked loads, for shapes the DMA path cannot take
 // (K not a multiple of 32, N not a multiple of 8, misaligned pointers).
 //
-// Both paths accumulate every output element over k in the same order (32-wide
+// All paths accumulate every output element over k in the same order (32-wide
 // k steps, ascending), so results are bit-identical whichever path or tile
-// shape runs, and do not depend on how the caller chunks M and N.
+// shape runs, do not depend on how the caller chunks M and N, and continuing
+// from C (acc_init) equals one pass over the concatenated k range.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <type_traits>
 #include <cstdint>
+#include <type_traits>
 
 #include "gemm.h"
 
@@ -57,10 +66,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+#define TP_LDS __attribute__((address_space(3)))
+
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 64;
+
+// fp32 output continuing from C's contents (GemmArgs::acc_init): its own
+// instantiation, so the forward's kernels carry no code for it (it costs the
+// largest tiles their last free registers).
+constexpr int kEpiF32Acc = 100;
 
 // ---- numerics ----------------------------------------------------------
 
@@ -86,6 +102,13 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752440f));
 }
 
+// GeLU'(x) = Phi(x) + x * phi(x), phi the standard normal density
+// exp(-x^2/2) / sqrt(2 pi), in fp32.
+__device__ __forceinline__ float gelu_erf_deriv(float x) {
+  const float cdf = 0.5f * (1.0f + erf_as7126(x * 0.70710678118654752440f));
+  return cdf + x * 0.39894228040143267794f * __expf(-0.5f * x * x);
+}
+
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -98,20 +121,71 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
 }
 
-// ---- LDS addressing ----------------------------------------------------
-// Each operand tile row holds 64 bf16 = 128 bytes = 8 chunks of 16 bytes.
-// Chunk c of row r lives at chunk position c ^ swz(r).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-// X tile rows are written 8 lanes per row and read 16 rows per lane group:
-// rows r..r+7 must land on distinct chunk positions.
-__device__ __forceinline__ uint32_t lds_off_a(int r, int c) {
-  return static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) << 4));
+// ---- epilogue ------------------------------------------------------------
+// The 4 accumulator values of one lane are C[m][n .. n+3].  `full`: all four
+// columns lie inside N and the rows are aligned for vector access.
+
+__device__ __forceinline__ void store_bf16x4(uint16_t *dst, f32x4_t v, bool full, int64_t left) {
+  if (full) {
+    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < left) dst[e] = static_cast<uint16_t>(bf16_bits_rne(v[e]));
+  }
 }
 
-// W tile rows (one per output column n) are written by lanes whose n differ by
-// 8 and read by lanes whose n differ by 1: mix both bit groups.
-__device__ __forceinline__ uint32_t lds_off_b(int n, int c) {
-  return static_cast<uint32_t>(n * 128 + ((c ^ ((n ^ (n >> 3)) & 7)) << 4));
+__device__ __forceinline__ f32x4_t load_bf16x4(const uint16_t *src, bool full, int64_t left) {
+  f32x4_t v{0.f, 0.f, 0.f, 0.f};
+  if (full) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t *>(src);
+    v = f32x4_t{bf16_to_f32(w[0] & 0xffffu), bf16_to_f32(w[0] >> 16), bf16_to_f32(w[1] & 0xffffu),
+                bf16_to_f32(w[1] >> 16)};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < left) v[e] = bf16_to_f32(src[e]);
+  }
+  return v;
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_store(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v, bool full) {
+  const int64_t left = p.N - n;
+  if constexpr (EPI == kEpiF32 || EPI == kEpiF32Acc) {
+    float *C = static_cast<float *>(p.c) + m * ldc + n;
+    if (full) {
+      *reinterpret_cast<f32x4_t *>(C) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < left) C[e] = v[e];
+    }
+  } else {
+    if constexpr (EPI == kEpiGeluSaveBf16)
+      store_bf16x4(static_cast<uint16_t *>(p.aux) + m * p.ldaux + n, v, full, left);
+    if constexpr (EPI == kEpiDGeluBf16) {
+      const f32x4_t h = load_bf16x4(static_cast<const uint16_t *>(p.aux) + m * p.ldaux + n, full, left);
+      v = f32x4_t{v[0] * gelu_erf_deriv(h[0]), v[1] * gelu_erf_deriv(h[1]), v[2] * gelu_erf_deriv(h[2]),
+                  v[3] * gelu_erf_deriv(h[3])};
+    }
+    if constexpr (EPI == kEpiGeluBf16 || EPI == kEpiGeluSaveBf16)
+      v = f32x4_t{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
+    store_bf16x4(static_cast<uint16_t *>(p.c) + m * ldc + n, v, full, left);
+  }
+}
+
+// Starting accumulator of an fp32-output tile when C += A W is asked for.
+__device__ __forceinline__ f32x4_t acc_start(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, bool full) {
+  const float *C = static_cast<const float *>(p.c) + m * ldc + n;
+  if (full) return *reinterpret_cast<const f32x4_t *>(C);
+  f32x4_t v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (n + e < p.N) v[e] = C[e];
+  return v;
 }
 
 // ---- XCD-aware tile order ------------------------------------------------
@@ -135,7 +209,24 @@ __device__ __forceinline__ void tile_coords(int bid, int ntiles, int tiles_m, in
 }
 
 // ---- ragged path: register-staged, bounds-checked ------------------------
+// LDS holds, per stage, X rows [m][k] and W columns [n][k] (k contiguous, 64
+// bf16 per row, chunk c of row r at chunk position c ^ swz(r)).
 
+// X tile rows are written 8 lanes per row and read 16 rows per lane group:
+// rows r..r+7 must land on distinct chunk positions.
+__device__ __forceinline__ uint32_t lds_off_a(int r, int c) {
+  return static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) << 4));
+}
+
+// W tile rows (one per output column n) are written by lanes whose n differ by
+// 8 and read by lanes whose n differ by 1: mix both bit groups.
+__device__ __forceinline__ uint32_t lds_off_b(int n, int c) {
+  return static_cast<uint32_t>(n * 128 + ((c ^ ((n ^ (n >> 3)) & 7)) << 4));
+}
+
+// VEC: 16-byte loads along the contiguous dimension (both operands in the
+// forward layout, aligned).  Otherwise every element is loaded on its own
+// through the layout's strides, for any layout and alignment.
 template <int BM, int BN, bool VEC, int EPI>
 struct Bf16Gemm {
   static constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
@@ -160,6 +251,9 @@ struct Bf16Gemm {
     const int t = threadIdx.x;
     const uint16_t *A = static_cast<const uint16_t *>(p.a);
     const uint16_t *W = static_cast<const uint16_t *>(p.w);
+    // Element strides: A(m, k) = A[m * sam + k * sak], W(k, n) = W[k * swk + n * swn].
+    const int64_t sam = p.a_t ? 1 : p.lda, sak = p.a_t ? p.lda : 1;
+    const int64_t swk = p.w_t ? 1 : p.ldw, swn = p.w_t ? p.ldw : 1;
 #pragma unroll
     for (int q = 0; q < A_CHUNKS; ++q) {
       const int idx = t + kThreads * q;
@@ -175,8 +269,8 @@ struct Bf16Gemm {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t k = gk + 2 * e;
-          const uint32_t lo = (gm < p.M && k < p.K) ? A[gm * p.lda + k] : 0u;
-          const uint32_t hi = (gm < p.M && k + 1 < p.K) ? A[gm * p.lda + k + 1] : 0u;
+          const uint32_t lo = (gm < p.M && k < p.K) ? A[gm * sam + k * sak] : 0u;
+          const uint32_t hi = (gm < p.M && k + 1 < p.K) ? A[gm * sam + (k + 1) * sak] : 0u;
           v[e] = lo | (hi << 16);
         }
         g.a[q] = u32x4_t{v[0], v[1], v[2], v[3]};
@@ -196,8 +290,8 @@ struct Bf16Gemm {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t n = gn + 2 * e;
-          const uint32_t lo = (gk < p.K && n < p.N) ? W[gk * p.ldw + n] : 0u;
-          const uint32_t hi = (gk < p.K && n + 1 < p.N) ? W[gk * p.ldw + n + 1] : 0u;
+          const uint32_t lo = (gk < p.K && n < p.N) ? W[gk * swk + n * swn] : 0u;
+          const uint32_t hi = (gk < p.K && n + 1 < p.N) ? W[gk * swk + (n + 1) * swn] : 0u;
           v[e] = lo | (hi << 16);
         }
         g.w[q] = u32x4_t{v[0], v[1], v[2], v[3]};
@@ -267,42 +361,24 @@ struct Bf16Gemm {
     }
   }
 
-  __device__ __forceinline__ static void epilogue(const GemmArgs& p, int m0, int n0, const f32x4_t (&acc)[TM][TN]) {
+  // Row m and first column n of accumulator (i, j) of this lane.
+  __device__ __forceinline__ static void coords(int m0, int n0, int i, int j, int64_t *m, int64_t *n) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    *m = m0 + wm * WM + i * 16 + (lane & 15);
+    *n = n0 + wn * WN + j * 16 + 4 * (lane >> 4);
+  }
+
+  __device__ __forceinline__ static void epilogue(const GemmArgs& p, int m0, int n0, const f32x4_t (&acc)[TM][TN]) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + wm * WM + i * 16 + (lane & 15);
-      if (m >= p.M) continue;
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wn * WN + j * 16 + 4 * (lane >> 4);
-        f32x4_t v = acc[i][j];
-        if constexpr (EPI == kEpiGeluBf16) {
-          v = f32x4_t{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
-        }
-        if constexpr (EPI == kEpiF32) {
-          float *C = static_cast<float *>(p.c) + m * p.ldc + n;
-          if (VEC && n + 3 < p.N) {
-            *reinterpret_cast<f32x4_t *>(C) = v;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) C[e] = v[e];
-          }
-        } else {
-          uint16_t *C = static_cast<uint16_t *>(p.c) + m * p.ldc + n;
-          if (VEC && n + 3 < p.N) {
-            *reinterpret_cast<u32x2_t *>(C) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) C[e] = static_cast<uint16_t>(bf16_bits_rne(v[e]));
-          }
-        }
+        int64_t m, n;
+        coords(m0, n0, i, j, &m, &n);
+        if (m < p.M && n < p.N) epi_store<EPI>(p, p.ldc, m, n, acc[i][j], VEC && n + 3 < p.N);
       }
-    }
   }
 };
 
@@ -321,7 +397,14 @@ __global__ void __launch_bounds__(kThreads, 1) bf16_gemm_ragged(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < G::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < G::TN; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (EPI == kEpiF32Acc) {
+        int64_t m, n;
+        G::coords(m0, n0, i, j, &m, &n);
+        if (m < p.M && n < p.N) acc[i][j] = acc_start(p, p.ldc, m, n, VEC && n + 3 < p.N);
+      }
+    }
 
   const int nk = static_cast<int>((p.K + kBK - 1) / kBK);
   typename G::Regs g;
@@ -340,10 +423,7 @@ __global__ void __launch_bounds__(kThreads, 1) bf16_gemm_ragged(GemmArgs p) {
   G::epilogue(p, m0, n0, acc);
 }
 
-
 // ---- main path: LDS-DMA ring, 8 waves ------------------------------------
-
-#define TP_LDS __attribute__((address_space(3)))
 
 // One LDS-DMA load: this lane's 16 bytes at g land at LDS byte address
 // lds + 16 * lane.  lds must be wave-uniform (it goes to M0).
@@ -365,39 +445,88 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-template <int BM, int BN, int BK, int S, int WAVES_M_ = 2, int WAVES_N_ = 4>
+// One operand's tile of a stage in LDS.  ROWS is the output extent it feeds
+// (BM for A, BN for W).
+//  * KC (k-contiguous in memory): ROWS LDS rows of BK k (2 * BK bytes each);
+//    chunk c of row r sits at c ^ swz(r), so that the 8 rows a DMA instruction
+//    or a 16-lane read group touches hit distinct banks; fragments are one
+//    ds_read_b128 per lane (row = lane & 15, k chunk = lane >> 4).
+//  * otherwise (row/column-contiguous): BK LDS rows (one per k) of ROWS
+//    elements; chunk c of k-row r sits at c ^ 2 (r & 3), so the 4 k-rows a
+//    transposing read touches hit distinct banks; a fragment is two
+//    ds_read_b64_tr_b16 (lane 4 r + q of group g reads k-row 8 g + r (+4),
+//    columns 4 q .. 4 q + 3; lane j of the group then holds column j, 4 k).
+// DMA pieces are 1 KiB: lane l of piece p covers tile bytes 1024 p + 16 l.
+template <int ROWS, int BK, bool KC>
+struct OpTile {
+  static constexpr int BYTES = ROWS * BK * 2;
+  static constexpr int PIECES = BYTES / 1024;
+  static constexpr int RB = KC ? BK * 2 : ROWS * 2;   // bytes per LDS row
+  static_assert(BYTES % 1024 == 0 && RB % 16 == 0, "operand tile");
+  static_assert(KC || (RB / 16) % 8 == 0, "row-contiguous tiles need 8-chunk rows for their swizzle");
+
+  __device__ __forceinline__ static int swz(int r) {
+    return KC ? (BK == 32 ? ((r >> 1) & 3) : (r & 7)) : 2 * (r & 3);
+  }
+  // Element offset, from the operand base at k = 0, of this lane's 16 bytes
+  // of piece `piece` for the tile whose first row (m or n) is row0.  Rows (KC)
+  // or 8-column groups (otherwise) past nrows are clamped onto valid memory:
+  // they only feed outputs that are never stored.
+  __device__ __forceinline__ static int64_t src(int piece, int lane, int64_t row0, int64_t nrows, int64_t ld) {
+    const int byte = piece * 1024 + lane * 16;
+    const int r = byte / RB, c = ((byte % RB) >> 4) ^ swz(r);
+    if constexpr (KC) {
+      const int64_t g = (row0 + r < nrows) ? row0 + r : nrows - 1;
+      return g * ld + c * 8;
+    } else {
+      const int64_t g = (row0 + c * 8 < nrows) ? row0 + c * 8 : nrows - 8;
+      return static_cast<int64_t>(r) * ld + g;
+    }
+  }
+  // Element advance of the source per stage (k0 -> k0 + BK).
+  __device__ __forceinline__ static int64_t step(int64_t ld) { return KC ? BK : BK * ld; }
+  // MFMA operand fragment of the 16 rows starting at tile row `row`, k-step kk.
+  __device__ __forceinline__ static bf16x8_t frag(const TP_LDS char *base, int row, int kk, int lane) {
+    if constexpr (KC) {
+      const int r = row + (lane & 15), c = kk * 4 + (lane >> 4);
+      return *(const TP_LDS bf16x8_t *)(base + r * RB + ((c ^ swz(r)) << 4));
+    } else {
+      const int col = row + 4 * (lane & 3);
+      const int k = kk * 32 + 8 * (lane >> 4) + ((lane & 15) >> 2);
+      const int o = k * RB + (((col >> 3) ^ swz(k)) << 4) + (col & 7) * 2;   // k + 4: same swizzle
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + o));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + o + 4 * RB));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+};
+
+// AT: A given transposed (m-contiguous); WT: W given transposed (k-contiguous).
+template <int BM, int BN, int BK, int S, bool AT, bool WT, int WAVES_M_ = 2, int WAVES_N_ = 4>
 struct DmaCfg {
+  using TA = OpTile<BM, BK, !AT>;
+  using TW = OpTile<BN, BK, WT>;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N, THREADS = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
   static constexpr int KK = BK / 32;                   // MFMA k-steps per stage
-  static constexpr int AROW = BK * 2, ACH = BK / 8;    // A tile: bytes, 16B chunks per row
-  static constexpr int ARPI = 1024 / AROW;             // A rows per DMA instruction
-  static constexpr int WROW = BN * 2, WCH = BN / 8;    // W tile row (one k): bytes, chunks
-  static constexpr int A_BYTES = BM * AROW, STAGE = A_BYTES + BK * WROW;
-  // DMA instructions (1 KiB each) per stage: the A pieces split evenly over
-  // the waves; the W pieces are dealt round-robin, so when they do not divide
-  // evenly the first W_REM waves issue one more than the rest.
-  static constexpr int NA = A_BYTES / 1024, NWP = BK * WROW / 1024;
-  static constexpr int A_PW = NA / NW;
-  static constexpr int W_PW = (NWP + NW - 1) / NW, W_REM = NWP % NW;
+  static constexpr int STAGE = TA::BYTES + TW::BYTES;
+  // The A pieces split evenly over the waves; the W pieces are dealt
+  // round-robin, so when they do not divide evenly the first W_REM waves
+  // issue one more than the rest.
+  static constexpr int A_PW = TA::PIECES / NW;
+  static constexpr int W_PW = (TW::PIECES + NW - 1) / NW, W_REM = TW::PIECES % NW;
   static constexpr int L_HI = A_PW + W_PW, L_LO = W_REM ? L_HI - 1 : L_HI;   // per-wave DMA count
-  static_assert((BK == 32 || BK == 64) && WN % 16 == 0 && WM % 16 == 0 && WCH % 8 == 0, "tile shape");
-  static_assert(A_PW >= 1 && NA % NW == 0 && NA * 1024 == A_BYTES && NWP * 1024 == BK * WROW && NWP >= NW,
-                "DMA split");
+  static_assert((BK == 32 || BK == 64) && WN % 16 == 0 && WM % 16 == 0, "tile shape");
+  static_assert(A_PW >= 1 && TA::PIECES % NW == 0 && TW::PIECES >= NW, "DMA split");
   static_assert((S - 1) * L_HI < 64, "vmcnt range");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
 };
 
-// A-tile swizzle: with 4 chunks per row (BK = 32) two rows share a 128-byte
-// bank window, with 8 chunks (BK = 64) one row fills it.
-template <int BK>
-__device__ __forceinline__ int a_swz(int row) {
-  return BK == 32 ? ((row >> 1) & 3) : (row & 7);
-}
-
-template <int BM, int BN, int BK, int S, int EPI, int WAVES_M = 2, int WAVES_N = 4>
+template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmArgs p) {
-  using C = DmaCfg<BM, BN, BK, S, WAVES_M, WAVES_N>;
+  using C = DmaCfg<BM, BN, BK, S, AT, WT, WAVES_M, WAVES_N>;
+  using TA = typename C::TA;
+  using TW = typename C::TW;
   constexpr int KK = C::KK;
   __shared__ __attribute__((aligned(1024))) char smem[S * C::STAGE];
   const int lane = threadIdx.x & 63;
@@ -418,38 +547,25 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   const int64_t ldc = p.ldc;
   asm volatile("" ::"s"(ldc));
 
-  // Source of each of this lane's DMA pieces (elements, before the stage's k
-  // offset).  Lane order fixes the LDS position, so the swizzle is applied by
-  // choosing which chunk a lane fetches.  Rows past M and columns past N are
-  // clamped onto valid memory: they only feed outputs that are never stored.
+  // Source of each of this lane's DMA pieces (elements, at k = 0).  Lane order
+  // fixes the LDS position, so the swizzle is applied by choosing which chunk
+  // a lane fetches.  A piece index past the W tile (the short waves' last
+  // slot) is never issued.
   int64_t a_src[C::A_PW], w_src[C::W_PW];
 #pragma unroll
-  for (int q = 0; q < C::A_PW; ++q) {
-    const int row = (wave * C::A_PW + q) * C::ARPI + lane / C::ACH;
-    const int chunk = (lane % C::ACH) ^ a_swz<BK>(row);
-    const int64_t gm = (m0 + row < p.M) ? m0 + row : p.M - 1;
-    a_src[q] = gm * p.lda + chunk * 8;
-  }
+  for (int q = 0; q < C::A_PW; ++q) a_src[q] = TA::src(wave * C::A_PW + q, lane, m0, p.M, p.lda);
 #pragma unroll
-  for (int q = 0; q < C::W_PW; ++q) {
-    // W rows need not divide the 1 KiB an instruction writes (BN = 192: 384 B),
-    // so the row and chunk come from this lane's byte offset in the W tile.
-    // A piece index past the tile (the short waves' last slot) is never issued.
-    const int byte = min(wave + q * C::NW, C::NWP - 1) * 1024 + lane * 16;
-    const int row = byte / C::WROW;
-    const int chunk = ((byte % C::WROW) >> 4) ^ (2 * (row & 3));
-    const int64_t gn = (n0 + chunk * 8 < p.N) ? n0 + chunk * 8 : p.N - 8;
-    w_src[q] = static_cast<int64_t>(row) * p.ldw + gn;
-  }
+  for (int q = 0; q < C::W_PW; ++q)
+    w_src[q] = TW::src(min(wave + q * C::NW, TW::PIECES - 1), lane, n0, p.N, p.ldw);
+  const int64_t a_step = TA::step(p.lda), w_step = TW::step(p.ldw);
   auto issue = [&](int st, int slot) {
-    const int64_t k0 = static_cast<int64_t>(st) * BK;
     const uint32_t base = lds0 + slot * C::STAGE;
 #pragma unroll
-    for (int q = 0; q < C::A_PW; ++q) lds_dma16(A + a_src[q] + k0, base + (wave * C::A_PW + q) * 1024);
+    for (int q = 0; q < C::A_PW; ++q) lds_dma16(A + a_src[q] + st * a_step, base + (wave * C::A_PW + q) * 1024);
 #pragma unroll
     for (int q = 0; q < C::W_PW; ++q)
       if (C::W_REM == 0 || q + 1 < C::W_PW || wave < C::W_REM)
-        lds_dma16(W + w_src[q] + k0 * p.ldw, base + C::A_BYTES + (wave + q * C::NW) * 1024);
+        lds_dma16(W + w_src[q] + st * w_step, base + TA::BYTES + (wave + q * C::NW) * 1024);
   };
   // s_waitcnt vmcnt(n * this wave's DMA count per stage).
   const bool dma_hi = C::W_REM == 0 || wave < C::W_REM;
@@ -459,49 +575,30 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   };
 
   static_assert(C::THREADS == 64 * WAVES_M * WAVES_N, "launch shape");
-  // LDS byte offsets (within a stage) of this lane's operand fragments.
-  // A: lane reads row (lane & 15) of a 16-row block, k chunk (lane >> 4).
-  // W: ds_read_b64_tr_b16 over 16 lanes g: lane 4r + q reads k row 8g + r (+4)
-  // at columns 4q..4q+3; lane j of the group then holds column j, 4 k values.
-  uint32_t a_off[KK][C::TM], w_off[KK][C::TN][2];
-  {
-    const int g = lane >> 4, r = (lane & 15) >> 2, q = lane & 3;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const int row = wm * C::WM + i * 16 + (lane & 15), chunk = kk * 4 + (lane >> 4);
-        a_off[kk][i] = row * C::AROW + ((chunk ^ a_swz<BK>(row)) << 4);
-      }
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int col = wn * C::WN + j * 16 + 4 * q;
-        const int chunk = col >> 3, byte = (col & 7) * 2;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = kk * 32 + 8 * g + r + 4 * h;
-          w_off[kk][j][h] = C::A_BYTES + k * C::WROW + ((chunk ^ (2 * (k & 3))) << 4) + byte;
-        }
-      }
-    }
-  }
   auto read = [&](int u, bf16x8_t (&fa)[C::TM], bf16x8_t (&fb)[C::TN]) {
     const int kk = KK == 1 ? 0 : (u & 1);
     const TP_LDS char *base = (const TP_LDS char *)smem + ((u / KK) % S) * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) fa[i] = *(const TP_LDS bf16x8_t *)(base + a_off[kk][i]);
+    for (int i = 0; i < C::TM; ++i) fa[i] = TA::frag(base, wm * C::WM + i * 16, kk, lane);
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + w_off[kk][j][0]));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + w_off[kk][j][1]));
-      fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    for (int j = 0; j < C::TN; ++j) fb[j] = TW::frag(base + TA::BYTES, wn * C::WN + j * 16, kk, lane);
+  };
+  auto coords = [&](int i, int j, int64_t *m, int64_t *n) {
+    *m = m0 + wm * C::WM + i * 16 + (lane & 15);
+    *n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
   };
   f32x4_t acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TN; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (EPI == kEpiF32Acc) {
+        int64_t m, n;
+        coords(i, j, &m, &n);
+        if (m < p.M && n < p.N) acc[i][j] = acc_start(p, ldc, m, n, true);
+      }
+    }
   // Rows inner: consecutive MFMAs share the W operand (measured a few percent
   // faster than sharing the A operand on the 8 x 3 wave tile).
   auto mma = [&](const bf16x8_t (&fa)[C::TM], const bf16x8_t (&fb)[C::TN]) {
@@ -544,24 +641,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   if (u < nu) mma(fa0, fb0);
 
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int64_t m = m0 + wm * C::WM + i * 16 + (lane & 15);
-    if (m >= p.M) continue;
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
-      const int64_t n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
-      if (n >= p.N) continue;   // N is a multiple of 8 on this path
-      f32x4_t v = acc[i][j];
-      if constexpr (EPI == kEpiF32) {
-        *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + m * ldc + n) = v;
-      } else {
-        if constexpr (EPI == kEpiGeluBf16)
-          v = f32x4_t{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
-        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.c) + m * ldc + n) =
-            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
+      int64_t m, n;
+      coords(i, j, &m, &n);
+      if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);   // N % 8 == 0 on this path
     }
-  }
 }
 
 // ---- ping-pong path -------------------------------------------------------
@@ -591,13 +677,15 @@ __device__ __forceinline__ void barrier_raw() {
 }
 
 // The ping-pong kernel: BK = 64, two slots, 8 waves (2 x 4).
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, bool AT, bool WT>
 __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
   constexpr int BK = 64, S = 2;
-  using C = DmaCfg<BM, BN, BK, S, 2, 4>;
+  using C = DmaCfg<BM, BN, BK, S, AT, WT, 2, 4>;
+  using TA = typename C::TA;
+  using TW = typename C::TW;
   constexpr int NG = 4;                              // waves of the issuing group
-  constexpr int A_PW = C::NA / NG, W_PW = C::NWP / NG, L = A_PW + W_PW;
-  static_assert(C::NA % NG == 0 && C::NWP % NG == 0, "DMA split");
+  constexpr int A_PW = TA::PIECES / NG, W_PW = TW::PIECES / NG, L = A_PW + W_PW;
+  static_assert(TA::PIECES % NG == 0 && TW::PIECES % NG == 0, "DMA split");
   __shared__ __attribute__((aligned(1024))) char smem[S * C::STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -616,21 +704,13 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
   // launcher only picks this kernel when every offset fits).
   uint32_t a_src[A_PW], w_src[W_PW];
 #pragma unroll
-  for (int q = 0; q < A_PW; ++q) {
-    const int row = ((wave & 3) * A_PW + q) * C::ARPI + lane / C::ACH;
-    const int chunk = (lane % C::ACH) ^ a_swz<BK>(row);
-    const int64_t gm = (m0 + row < p.M) ? m0 + row : p.M - 1;
-    a_src[q] = static_cast<uint32_t>((gm * p.lda + chunk * 8) * 2);
-  }
+  for (int q = 0; q < A_PW; ++q)
+    a_src[q] = static_cast<uint32_t>(TA::src((wave & 3) * A_PW + q, lane, m0, p.M, p.lda) * 2);
 #pragma unroll
-  for (int q = 0; q < W_PW; ++q) {
-    const int byte = ((wave & 3) * W_PW + q) * 1024 + lane * 16;
-    const int row = byte / C::WROW;
-    const int chunk = ((byte % C::WROW) >> 4) ^ (2 * (row & 3));
-    const int64_t gn = (n0 + chunk * 8 < p.N) ? n0 + chunk * 8 : p.N - 8;
-    w_src[q] = static_cast<uint32_t>((static_cast<int64_t>(row) * p.ldw + gn) * 2);
-  }
-  const uint32_t a_step = BK * 2, w_step = static_cast<uint32_t>(BK * p.ldw * 2);
+  for (int q = 0; q < W_PW; ++q)
+    w_src[q] = static_cast<uint32_t>(TW::src((wave & 3) * W_PW + q, lane, n0, p.N, p.ldw) * 2);
+  const uint32_t a_step = static_cast<uint32_t>(TA::step(p.lda) * 2);
+  const uint32_t w_step = static_cast<uint32_t>(TW::step(p.ldw) * 2);
   auto issue = [&](int st, int slot) {
     const uint32_t base = lds0 + slot * C::STAGE;
 #pragma unroll
@@ -638,48 +718,37 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
       lds_dma16_s(p.a, a_src[q] + st * a_step, base + ((wave & 3) * A_PW + q) * 1024);
 #pragma unroll
     for (int q = 0; q < W_PW; ++q)
-      lds_dma16_s(p.w, w_src[q] + st * w_step, base + C::A_BYTES + ((wave & 3) * W_PW + q) * 1024);
+      lds_dma16_s(p.w, w_src[q] + st * w_step, base + TA::BYTES + ((wave & 3) * W_PW + q) * 1024);
   };
 
-  // LDS byte offsets of this lane's W fragments (as in bf16_gemm_dma).
-  uint32_t w_off[C::TN];
-  {
-    const int g = lane >> 4, r = (lane & 15) >> 2, q = lane & 3;
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int col = wn * C::WN + j * 16 + 4 * q;
-      const int chunk = col >> 3, byte = (col & 7) * 2;
-      const int k = 8 * g + r;
-      w_off[j] = C::A_BYTES + k * C::WROW + ((chunk ^ (2 * (k & 3))) << 4) + byte;
-    }
-  }
-  // Both k-steps of the stage in slot `slot`: W rows move by 32 per k-step
-  // (k & 3, and so the swizzle, unchanged).
+  // Both k-steps of the stage in slot `slot`.
   bf16x8_t fa[2][C::TM], fb[2][C::TN];
   auto read_stage = [&](int slot) {
     const TP_LDS char *base = (const TP_LDS char *)smem + slot * C::STAGE;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const int row = wm * C::WM + i * 16 + (lane & 15), chunk = kk * 4 + (lane >> 4);
-        const uint32_t off = row * C::AROW + ((chunk ^ a_swz<BK>(row)) << 4);
-        fa[kk][i] = *(const TP_LDS bf16x8_t *)(base + off);
-      }
+      for (int i = 0; i < C::TM; ++i) fa[kk][i] = TA::frag(base, wm * C::WM + i * 16, kk, lane);
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const uint32_t o = w_off[j] + kk * 32 * C::WROW;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + o));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4_t *)(base + o + 4 * C::WROW));
-        fb[kk][j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+      for (int j = 0; j < C::TN; ++j) fb[kk][j] = TW::frag(base + TA::BYTES, wn * C::WN + j * 16, kk, lane);
     }
+  };
+  auto coords = [&](int i, int j, int64_t *m, int64_t *n) {
+    *m = m0 + wm * C::WM + i * 16 + (lane & 15);
+    *n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
   };
   f32x4_t acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TN; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (EPI == kEpiF32Acc) {
+        int64_t m, n;
+        coords(i, j, &m, &n);
+        if (m < p.M && n < p.N) acc[i][j] = acc_start(p, ldc, m, n, true);
+      }
+    }
   auto mma_stage = [&]() {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -716,35 +785,18 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
   }
 
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int64_t m = m0 + wm * C::WM + i * 16 + (lane & 15);
-    if (m >= p.M) continue;
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
-      const int64_t n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
-      if (n >= p.N) continue;
-      f32x4_t v = acc[i][j];
-      if constexpr (EPI == kEpiF32) {
-        *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + m * ldc + n) = v;
-      } else {
-        if constexpr (EPI == kEpiGeluBf16)
-          v = f32x4_t{gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3])};
-        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(p.c) + m * ldc + n) =
-            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
+      int64_t m, n;
+      coords(i, j, &m, &n);
+      if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);
     }
-  }
-}
-
-template <int BM, int BN, int EPI>
-hipError_t launch_pp(const GemmArgs &p, hipStream_t s) {
-  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((bf16_gemm_pp<BM, BN, EPI>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
-  return hipGetLastError();
 }
 
 // ---- plain fp32 kernel (tiny fp32 workload) ------------------------------
-// 64 x 64 tile, 256 threads of 4 x 4 outputs, K staged 16 at a time.
+// 64 x 64 tile, 256 threads of 4 x 4 outputs, K staged 16 at a time; any
+// operand layout (element strides).
 
 constexpr int kF32Tile = 64;
 constexpr int kF32BK = 16;
@@ -755,18 +807,28 @@ __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
   __shared__ float Ws[kF32BK][kF32Tile + 4];
   const float *A = static_cast<const float *>(p.a);
   const float *W = static_cast<const float *>(p.w);
+  const int64_t sam = p.a_t ? 1 : p.lda, sak = p.a_t ? p.lda : 1;
+  const int64_t swk = p.w_t ? 1 : p.ldw, swn = p.w_t ? p.ldw : 1;
   const int tiles_n = static_cast<int>((p.N + kF32Tile - 1) / kF32Tile);
   const int64_t m0 = static_cast<int64_t>(blockIdx.x / tiles_n) * kF32Tile;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x % tiles_n) * kF32Tile;
   const int t = threadIdx.x;
   const int tr = t / 16, tc = t % 16;
-  float acc[4][4] = {};
+  float *C = static_cast<float *>(p.c);
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t m = m0 + tr * 4 + i, n = n0 + tc * 4 + j;
+      acc[i][j] = (EPI == kEpiPlainF32 && p.acc_init && m < p.M && n < p.N) ? C[m * p.ldc + n] : 0.f;
+    }
   for (int64_t k0 = 0; k0 < p.K; k0 += kF32BK) {
     for (int e = t; e < kF32BK * kF32Tile; e += kThreads) {
       const int r = e / kF32BK, k = e % kF32BK;      // A element (row r, k)
-      As[k][r] = (m0 + r < p.M && k0 + k < p.K) ? A[(m0 + r) * p.lda + k0 + k] : 0.f;
+      As[k][r] = (m0 + r < p.M && k0 + k < p.K) ? A[(m0 + r) * sam + (k0 + k) * sak] : 0.f;
       const int kk = e / kF32Tile, n = e % kF32Tile;  // W element (k, col n)
-      Ws[kk][n] = (k0 + kk < p.K && n0 + n < p.N) ? W[(k0 + kk) * p.ldw + n0 + n] : 0.f;
+      Ws[kk][n] = (k0 + kk < p.K && n0 + n < p.N) ? W[(k0 + kk) * swk + (n0 + n) * swn] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -783,7 +845,7 @@ __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
     }
     __syncthreads();
   }
-  float *C = static_cast<float *>(p.c);
+  float *X = static_cast<float *>(p.aux);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + tr * 4 + i;
@@ -791,16 +853,30 @@ __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t n = n0 + tc * 4 + j;
-      if (n < p.N) C[m * p.ldc + n] = (EPI == kEpiGeluF32) ? gelu_erf(acc[i][j]) : acc[i][j];
+      if (n >= p.N) continue;
+      float v = acc[i][j];
+      if constexpr (EPI == kEpiGeluSaveF32) X[m * p.ldaux + n] = v;
+      if constexpr (EPI == kEpiDGeluF32) v *= gelu_erf_deriv(X[m * p.ldaux + n]);
+      if constexpr (EPI == kEpiGeluF32 || EPI == kEpiGeluSaveF32) v = gelu_erf(v);
+      C[m * p.ldc + n] = v;
     }
   }
 }
 
-template <int BM, int BN, int BK, int S, int EPI, int WAVES_M = 2, int WAVES_N = 4>
+// ---- launchers and tile choice ---------------------------------------------
+
+template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
 hipError_t launch_dma(const GemmArgs& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((bf16_gemm_dma<BM, BN, BK, S, EPI, WAVES_M, WAVES_N>), dim3(static_cast<unsigned>(tiles)),
+  hipLaunchKernelGGL((bf16_gemm_dma<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>), dim3(static_cast<unsigned>(tiles)),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int EPI, bool AT, bool WT>
+hipError_t launch_pp(const GemmArgs& p, hipStream_t s) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((bf16_gemm_pp<BM, BN, EPI, AT, WT>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -819,7 +895,7 @@ hipError_t launch_ragged(const GemmArgs& p, bool vec, hipStream_t s) {
 // measured on MI355X: the larger tile reuses each operand byte more).
 constexpr int kCUs = 256;
 
-template <int EPI>
+template <int EPI, bool AT, bool WT>
 hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s) {
   if (!dma_ok) return launch_ragged<EPI>(p, vec, s);
   auto cost = [&](int bm, int bn, double eff) {
@@ -832,45 +908,86 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   // (4 waves, 32 KiB of LDS): several workgroups then share each CU and hide
   // one another's pipeline fill and write-out, which dominate at this size.
   if (((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs) {
-    if (k64) return launch_dma<64, 64, 64, 2, EPI, 2, 2>(p, s);
-    return launch_dma<64, 64, 32, 4, EPI, 2, 2>(p, s);
+    if (k64) return launch_dma<64, 64, 64, 2, EPI, AT, WT, 2, 2>(p, s);
+    return launch_dma<64, 64, 32, 4, EPI, AT, WT, 2, 2>(p, s);
   }
-  const double c256 = k64 ? cost(256, 256, 1.0) : 1e300, c192 = k64 ? cost(256, 192, 0.95) : 1e300;
+  // The ping-pong kernel addresses operands with 32-bit byte offsets.
+  const int64_t a_span = (AT ? p.K : p.M) * p.lda * 2, w_span = (WT ? p.N : p.K) * p.ldw * 2;
+  const bool off32 = a_span < (int64_t{1} << 31) && w_span < (int64_t{1} << 31);
+  // The 256 x 256 tile keeps its 128 accumulators in registers only without
+  // the transposing reads of A and without the accumulator prologue.
+  constexpr bool big_ok = !AT && EPI != kEpiF32Acc;
+  const double c256 = big_ok && k64 && off32 ? cost(256, 256, 1.0) : 1e300;
+  const double c192 = k64 && off32 ? cost(256, 192, 0.95) : 1e300;
   const double c128w = k64 ? cost(256, 128, 0.85) : 1e300, c128 = cost(128, 128, 0.7);
   const double best = std::min(std::min(c256, c192), std::min(c128w, c128));
-  // The ping-pong kernel addresses operands with 32-bit byte offsets.
-  const bool off32 = p.M * p.lda * 2 < (int64_t{1} << 31) && p.K * p.ldw * 2 < (int64_t{1} << 31);
-  if (c256 == best) return off32 ? launch_pp<256, 256, EPI>(p, s) : launch_dma<256, 256, 64, 2, EPI>(p, s);
-  if (c192 == best) return off32 ? launch_pp<256, 192, EPI>(p, s) : launch_dma<256, 192, 64, 2, EPI>(p, s);
-  if (c128w == best) return launch_dma<256, 128, 64, 3, EPI>(p, s);
-  return launch_dma<128, 128, 32, 8, EPI>(p, s);
+  if constexpr (big_ok)
+    if (c256 == best) return launch_pp<256, 256, EPI, AT, WT>(p, s);
+  if (c192 == best) return launch_pp<256, 192, EPI, AT, WT>(p, s);
+  if (c128w == best) return launch_dma<256, 128, 64, 3, EPI, AT, WT>(p, s);
+  return launch_dma<128, 128, 32, 8, EPI, AT, WT>(p, s);
 }
+
+bool aligned16(const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
 }  // namespace
 
-bool gemm_vec_ok(const GemmArgs& p, int64_t out_esize) {
-  auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  return al(p.a) && al(p.w) && al(p.c) && (p.K % 8 == 0) && (p.N % 8 == 0) && (p.lda % 8 == 0) &&
-         (p.ldw % 8 == 0) && (p.ldc % (16 / out_esize) == 0);
+// Conditions for 16-byte access along every operand's contiguous dimension
+// and for whole-vector output (and aux) rows.
+bool gemm_vec_ok(const GemmArgs& p, int64_t out_esize, bool uses_aux) {
+  bool ok = aligned16(p.a) && aligned16(p.w) && aligned16(p.c) && (p.K % 8 == 0) && (p.N % 8 == 0) &&
+            (p.lda % 8 == 0) && (p.ldw % 8 == 0) && (p.ldc % (16 / out_esize) == 0);
+  if (p.a_t) ok = ok && p.M % 8 == 0;
+  if (uses_aux) ok = ok && aligned16(p.aux) && p.ldaux % 8 == 0;
+  return ok;
 }
 
-hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s) {
+hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  if (epi == kEpiF32 || epi == kEpiGeluBf16 || epi == kEpiIdentBf16) {
-    const bool vec = gemm_vec_ok(p, epi == kEpiF32 ? 4 : 2);
-    // The DMA path reads whole 32-deep k steps and 8-column groups unchecked.
-    const bool dma_ok = vec && p.K % 32 == 0 && p.K > 0;
-    if (epi == kEpiF32) return dispatch_bf16<kEpiF32>(p, dma_ok, vec, s);
-    if (epi == kEpiGeluBf16) return dispatch_bf16<kEpiGeluBf16>(p, dma_ok, vec, s);
-    return dispatch_bf16<kEpiIdentBf16>(p, dma_ok, vec, s);
+  int epi = epi_in;
+  const bool fp32 = epi == kEpiGeluF32 || epi == kEpiPlainF32 || epi == kEpiGeluSaveF32 || epi == kEpiDGeluF32;
+  if (fp32) {
+    const int64_t tiles = ((p.M + kF32Tile - 1) / kF32Tile) * ((p.N + kF32Tile - 1) / kF32Tile);
+    const dim3 grid(static_cast<unsigned>(tiles));
+    switch (epi) {
+      case kEpiGeluF32: hipLaunchKernelGGL((f32_gemm_kernel<kEpiGeluF32>), grid, dim3(kThreads), 0, s, p); break;
+      case kEpiGeluSaveF32: hipLaunchKernelGGL((f32_gemm_kernel<kEpiGeluSaveF32>), grid, dim3(kThreads), 0, s, p); break;
+      case kEpiDGeluF32: hipLaunchKernelGGL((f32_gemm_kernel<kEpiDGeluF32>), grid, dim3(kThreads), 0, s, p); break;
+      default: hipLaunchKernelGGL((f32_gemm_kernel<kEpiPlainF32>), grid, dim3(kThreads), 0, s, p); break;
+    }
+    return hipGetLastError();
   }
-  const int64_t tiles = ((p.M + kF32Tile - 1) / kF32Tile) * ((p.N + kF32Tile - 1) / kF32Tile);
-  const dim3 grid(static_cast<unsigned>(tiles));
-  if (epi == kEpiGeluF32)
-    hipLaunchKernelGGL((f32_gemm_kernel<kEpiGeluF32>), grid, dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((f32_gemm_kernel<kEpiPlainF32>), grid, dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  if (epi == kEpiF32 && p.acc_init) epi = kEpiF32Acc;
+  const bool uses_aux = epi == kEpiGeluSaveBf16 || epi == kEpiDGeluBf16;
+  const bool vec = gemm_vec_ok(p, epi == kEpiF32 || epi == kEpiF32Acc ? 4 : 2, uses_aux);
+  // The DMA path reads whole 32-deep k steps and 8-column groups unchecked.
+  const bool dma_ok = vec && p.K % 32 == 0 && p.K > 0;
+  // Forward layout: vector loads on the ragged path too.
+  if (!p.a_t && !p.w_t) {
+    switch (epi) {
+      case kEpiGeluBf16: return dispatch_bf16<kEpiGeluBf16, false, false>(p, dma_ok, vec, s);
+      case kEpiIdentBf16: return dispatch_bf16<kEpiIdentBf16, false, false>(p, dma_ok, vec, s);
+      case kEpiF32: return dispatch_bf16<kEpiF32, false, false>(p, dma_ok, vec, s);
+      case kEpiF32Acc: return dispatch_bf16<kEpiF32Acc, false, false>(p, dma_ok, vec, s);
+      case kEpiGeluSaveBf16: return dispatch_bf16<kEpiGeluSaveBf16, false, false>(p, dma_ok, vec, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  // Backward layouts: input gradients (W given transposed) and weight
+  // gradients (A given transposed).  Their ragged path loads element-wise.
+  if (!p.a_t && p.w_t) {
+    switch (epi) {
+      case kEpiDGeluBf16: return dispatch_bf16<kEpiDGeluBf16, false, true>(p, dma_ok, false, s);
+      case kEpiIdentBf16: return dispatch_bf16<kEpiIdentBf16, false, true>(p, dma_ok, false, s);
+      case kEpiF32: return dispatch_bf16<kEpiF32, false, true>(p, dma_ok, false, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (p.a_t && !p.w_t) {
+    if (epi == kEpiF32) return dispatch_bf16<kEpiF32, true, false>(p, dma_ok, false, s);
+    if (epi == kEpiF32Acc) return dispatch_bf16<kEpiF32Acc, true, false>(p, dma_ok, false, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tpshard

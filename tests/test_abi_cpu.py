@@ -209,3 +209,54 @@ def test_missing_library_fails_loudly(tmp_path):
             _abi.load(str(tmp_path / "nope.so"))
     finally:
         _abi._lib = saved
+
+
+def test_forward_saved_preactivation_validation():
+    lib = _abi.load()
+    assert lib.tp_colrow_mlp(C.byref(_mlp_args(act=_abi.TP_ACT_NONE, H_out=FAKE + (9 << 20))), None, None) == _abi.TP_ERR_ARG
+    # H_out overlapping Y_ws
+    assert lib.tp_colrow_mlp(C.byref(_mlp_args(H_out=FAKE + (3 << 20) + 64)), None, None) == _abi.TP_ERR_ARG
+
+
+def _bwd_args(**kw):
+    a = _abi.tp_mlp_bwd_args(dtype=_abi.TP_BF16, act=_abi.TP_ACT_GELU_ERF, M=64, H=64, F=64,
+                             X=FAKE, A_i=FAKE + (1 << 20), B_i=FAKE + (2 << 20), H_i=FAKE + (3 << 20),
+                             Y_i=FAKE + (4 << 20), dZ=FAKE + (5 << 20), dH_ws=FAKE + (6 << 20),
+                             dX_i=FAKE + (7 << 20), dA_i=FAKE + (8 << 20), dB_i=FAKE + (9 << 20),
+                             accumulate=0, row_chunks=1, P=1, peer_dX=None, dX_out=None, reduce_workgroups=0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _abi.TP_ERR_ARG),
+    (dict(act=5), _abi.TP_ERR_ARG),
+    (dict(M=0), _abi.TP_ERR_ARG),
+    (dict(dZ=None), _abi.TP_ERR_ARG),
+    (dict(dB_i=None), _abi.TP_ERR_ARG),
+    (dict(H_i=None), _abi.TP_ERR_ARG),                    # the GeLU derivative needs the pre-activation
+    (dict(accumulate=2), _abi.TP_ERR_ARG),
+    (dict(row_chunks=3), _abi.TP_ERR_INDIVISIBLE),
+    (dict(row_chunks=0), _abi.TP_ERR_ARG),
+    (dict(P=2), _abi.TP_ERR_ARG),                         # P > 1 needs peers and dX_out
+    (dict(P=65), _abi.TP_ERR_ARG),
+    (dict(dH_ws=FAKE + 100), _abi.TP_ERR_ARG),            # overlaps X
+    (dict(dA_i=FAKE + (9 << 20) + 64), _abi.TP_ERR_ARG),  # overlaps dB_i
+    (dict(dX_i=FAKE + (5 << 20)), _abi.TP_ERR_ARG),       # overlaps dZ
+    (dict(reduce_workgroups=-1), _abi.TP_ERR_ARG),
+])
+def test_backward_validation(kw, code):
+    lib = _abi.load()
+    a = _bwd_args(**kw)
+    assert lib.tp_colrow_mlp_backward(C.byref(a), None, None) == code
+    assert lib.tp_last_error().decode() != ""
+
+
+def test_backward_peer_validation():
+    lib = _abi.load()
+    peers = (C.c_void_p * 1)(None)
+    a = _bwd_args(P=2, peer_dX=C.cast(peers, C.POINTER(C.c_void_p)), dX_out=FAKE + (20 << 20))
+    assert lib.tp_colrow_mlp_backward(C.byref(a), None, None) == _abi.TP_ERR_ARG
+    peers[0] = FAKE + (7 << 20) + 8   # overlaps dX_i
+    assert lib.tp_colrow_mlp_backward(C.byref(a), None, None) == _abi.TP_ERR_ARG

@@ -152,6 +152,95 @@ class MlpStep:
                            f"os.cpu_count()={os.cpu_count()}")}
 
 
+class BwdStep:
+    """Backward of one rank's MLP share (dH, dX with its reduce over the ranks
+    on the second stream, dA, dB), for the per-rank shape of an MLP workload."""
+
+    serial = False
+    reduce_wgs = 0
+
+    def __init__(self, w):
+        self.w = w
+        dev = "cuda"
+        dt = "bf16" if w.dtype == "bf16" else "f32"
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        gen_dev = "cuda" if w.cfg in (3, 5) else "cpu"
+        self.X = inputs.normal((w.M, w.H), inputs.seed_for(w.cfg, inputs.SLOT_X), w.std_x, dt, gen_dev).to(dev)
+        self.dZ = inputs.normal((w.M, w.H), inputs.seed_for(w.cfg, inputs.SLOT_DZ), 1.0, dt, gen_dev).to(dev)
+        self.As = [inputs.normal((w.H, w.F), inputs.seed_for(w.cfg, inputs.SLOT_A_SHARD + i), w.std_a, dt,
+                                 gen_dev).to(dev) for i in range(w.P)]
+        self.Bs = [inputs.normal((w.F, w.H), inputs.seed_for(w.cfg, inputs.SLOT_B_SHARD + i), w.std_b, dt,
+                                 gen_dev).to(dev) for i in range(w.P)]
+        z = torch.empty((w.M, w.H), device=dev)
+        self.Y = torch.empty((w.M, w.F), dtype=tdt, device=dev)
+        self.Hs = torch.empty((w.M, w.F), dtype=tdt, device=dev)
+        self.dH = torch.empty((w.M, w.F), dtype=tdt, device=dev)
+        self.dX = torch.empty((w.M, w.H), device=dev)
+        self.dXo = torch.empty((w.M, w.H), device=dev)
+        self.dA = torch.empty((w.H, w.F), device=dev)
+        self.dB = torch.empty((w.F, w.H), device=dev)
+        # peers' input-gradient partials: their forward and backward, once, untimed, by the same path
+        self.peers = []
+        for i in range(1, w.P):
+            tp.tp_colrow_mlp(self.X, self.As[i], self.Bs[i], self.Y, z, row_chunks=w.R, H_out=self.Hs)
+            dx = torch.empty((w.M, w.H), device=dev)
+            tp.tp_colrow_mlp_backward(self.X, self.As[i], self.Bs[i], self.Hs, self.Y, self.dZ, self.dH, dx,
+                                      self.dA, self.dB, row_chunks=w.R)
+            self.peers.append(dx)
+        tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, z, row_chunks=w.R, H_out=self.Hs)
+        torch.cuda.synchronize()
+        self.s0 = torch.cuda.Stream()
+        self.s1 = torch.cuda.Stream()
+
+    def result(self):
+        return self.dA
+
+    def step(self):
+        tp.tp_colrow_mlp_backward(self.X, self.As[0], self.Bs[0], self.Hs, self.Y, self.dZ, self.dH, self.dX,
+                                  self.dA, self.dB, row_chunks=self.w.R, peer_dX=self.peers, dX_out=self.dXo,
+                                  s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
+                                  reduce_workgroups=self.reduce_wgs)
+
+    @property
+    def work(self):
+        return 2.0 * self.w.flops_per_rank      # four GEMMs of 2 M H F each
+
+    unit = "TFLOP/s"
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name + "-bwd", "pass": "backward", "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F,
+                "tp": w.P, "row_chunks": w.R, "reduce_stream": "compute" if self.serial else "second",
+                "peers": "virtual ranks 1..P-1, input-gradient partials precomputed by the same path"}
+
+    def cpu_baseline(self, budget_s):
+        """The oracle's backward on a row sample (dH, dX of those rows and their
+        contributions to dA, dB), fp64."""
+        from threadpoolctl import threadpool_info
+        from oracle import mlp as O
+        from oracle import reduce as R
+        w = self.w
+        rows = w.M if w.M * w.H * w.F <= 4096 * 768 * 768 else 256
+        sample_rows = np.linspace(0, w.M - 1, rows).astype(np.int64)
+        Xs, dZs = self.X.cpu()[sample_rows], self.dZ.cpu()[sample_rows]
+        A0, B0 = self.As[0].cpu(), self.Bs[0].cpu()
+        peers = [inputs.normal((rows, w.H), 98000 + p) for p in range(w.P - 1)]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            g = O.backward_rank(Xs, A0, B0, dZs)
+            R.reduce_full([g["dX_i"]] + peers)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        return {"value": 8.0 * rows * w.H * w.F / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": (f"{rows} of {w.M} token rows of the per-rank MLP backward (fp64, numpy BLAS: "
+                           f"dH, dX and those rows' share of dA and dB), plus the {w.P}-way sum of dX; "
+                           f"{reps} repetitions, {dt * 1e3:.1f} ms each; host "
+                           f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}")}
+
+
 class ReshardStep:
     """The 2x4-mesh layout workload: fused split+replicate, then split reduce."""
 
@@ -219,6 +308,9 @@ WORKLOADS = {
     GPT3_175B.name: lambda: MlpStep(GPT3_175B, split_weights=False),
     TINY.name: lambda: MlpStep(TINY, split_weights=True),
     RESHARD.name: lambda: ReshardStep(RESHARD),
+    GPT2_SMALL.name + "-bwd": lambda: BwdStep(GPT2_SMALL),
+    GPT3_6P7B.name + "-bwd": lambda: BwdStep(GPT3_6P7B),
+    GPT3_175B.name + "-bwd": lambda: BwdStep(GPT3_175B),
 }
 
 

@@ -19,6 +19,7 @@ SLOT_LAYOUT = 4
 SLOT_A_SHARD = 10
 SLOT_B_SHARD = 30
 SLOT_PARTIAL = 50
+SLOT_DZ = 5            # the output gradient of the backward workloads
 
 _DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 

@@ -162,6 +162,24 @@ int tp_partial_reduce(const float *const *partials, int64_t P, int64_t rows, int
                       int64_t ld_in, int32_t mode, int64_t num_splits, float *const *out,
                       int64_t ld_out, tp_stream_t stream);
 
+/* Reduction operator of a partial tensor ([SBP] "SBP": besides sum, min and
+ * max also apply to partial values). */
+enum { TP_REDUCE_OP_SUM = 0, TP_REDUCE_OP_MAX = 1, TP_REDUCE_OP_MIN = 2 };
+
+/*
+ * tp_partial_reduce with a choice of operator and an optional bias:
+ *   out = op over p of partials[p]  (+ bias[col], added once to the reduced value)
+ * MAX / MIN take fmaxf / fminf (a NaN element loses to a number); SUM is the
+ * fp32 sum in ascending p.  bias: NULL or a device array of `cols` fp32 values,
+ * the row-parallel layer's bias, which acts on the full output ([CAI] section
+ * 5.2), so it is added after the reduction and not per partial.  bias must not
+ * overlap any output.  Other arguments, conventions and errors as
+ * tp_partial_reduce; TP_ERR_ARG for an unknown op.
+ */
+int tp_partial_reduce_ex(const float *const *partials, int64_t P, int64_t rows, int64_t cols,
+                         int64_t ld_in, int32_t mode, int64_t num_splits, float *const *out,
+                         int64_t ld_out, int32_t op, const float *bias, tp_stream_t stream);
+
 /* ---- one rank's column->row MLP ------------------------------------ */
 enum { TP_ACT_NONE = 0, TP_ACT_GELU_ERF = 1 };
 
@@ -194,6 +212,9 @@ typedef struct {
   void *H_out;       /* optional [M, F] (dtype): X A_i before the activation, rounded to
                         dtype (RNE), kept for the backward pass; NULL = not stored.
                         Must be NULL when act = TP_ACT_NONE (H would equal Y). */
+  const float *bias; /* optional [H] fp32: the row-parallel layer's bias, added once to the
+                        full sum ([CAI] section 5.2), so Z_out = sum of partials + bias;
+                        NULL = none.  Needs Z_out (for any P); Z_i stays bias-free. */
 } tp_mlp_args;
 
 /*

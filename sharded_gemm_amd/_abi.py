@@ -32,10 +32,13 @@ TP_REDUCE_FULL = 0
 TP_REDUCE_SPLIT = 1
 TP_ACT_NONE = 0
 TP_ACT_GELU_ERF = 1
+TP_REDUCE_OP_SUM = 0
+TP_REDUCE_OP_MAX = 1
+TP_REDUCE_OP_MIN = 2
 
 # Every symbol include/tpshard.h declares.
 EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_shard_materialize",
-           "tp_partial_reduce", "tp_colrow_mlp", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
+           "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
 TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad")
 
@@ -82,7 +85,7 @@ class tp_mlp_args(C.Structure):
                 ("Y_ws", C.c_void_p), ("Z_i", C.c_void_p),
                 ("row_chunks", C.c_int64), ("col_chunks", C.c_int64), ("P", C.c_int64),
                 ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
-                ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p)]
+                ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p), ("bias", C.c_void_p)]
 
 
 class tp_mlp_bwd_args(C.Structure):
@@ -126,6 +129,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.tp_partial_reduce.restype = C.c_int
     lib.tp_partial_reduce.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                                       C.c_int32, C.c_int64, C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
+    lib.tp_partial_reduce_ex.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                         C.c_int32, C.c_int64, C.POINTER(C.c_void_p), C.c_int64, C.c_int32,
+                                         C.c_void_p, C.c_void_p]
+    lib.tp_partial_reduce_ex.restype = C.c_int
     lib.tp_colrow_mlp.restype = C.c_int
     lib.tp_colrow_mlp.argtypes = [C.POINTER(tp_mlp_args), C.c_void_p, C.c_void_p]
     lib.tp_colrow_mlp_backward.argtypes = [C.POINTER(tp_mlp_bwd_args), C.c_void_p, C.c_void_p]
@@ -256,8 +263,9 @@ def tp_shard_materialize(src, layout: dict, dst, stream=None):
 
 
 def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, ld_in=None, ld_out=None,
-                      stream=None):
-    """Sum fp32 ``partials`` (list of tensors or raw device pointers) into ``out`` (list).
+                      stream=None, op=TP_REDUCE_OP_SUM, bias=None):
+    """Reduce fp32 ``partials`` (list of tensors or raw device pointers) into ``out`` (list)
+    with ``op`` (sum, max or min), then add ``bias`` (fp32 [cols]) if given.
 
     With tensors, rows/cols/ld default to the 2-D shape of partials[0]."""
     lib = load()
@@ -272,13 +280,18 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
         ld_out = int(out[0].stride(0)) if hasattr(out[0], "data_ptr") else cols
     pin = (C.c_void_p * P)(*[(p.data_ptr() if hasattr(p, "data_ptr") else p) for p in partials])
     pout = (C.c_void_p * len(out))(*[(o.data_ptr() if hasattr(o, "data_ptr") else o) for o in out])
-    _check(lib.tp_partial_reduce(C.cast(pin, C.POINTER(C.c_void_p)), P, rows, cols, ld_in, mode, len(out),
-                                 C.cast(pout, C.POINTER(C.c_void_p)), ld_out, _stream_ptr(stream)))
+    if op == TP_REDUCE_OP_SUM and bias is None:
+        _check(lib.tp_partial_reduce(C.cast(pin, C.POINTER(C.c_void_p)), P, rows, cols, ld_in, mode, len(out),
+                                     C.cast(pout, C.POINTER(C.c_void_p)), ld_out, _stream_ptr(stream)))
+    else:
+        _check(lib.tp_partial_reduce_ex(C.cast(pin, C.POINTER(C.c_void_p)), P, rows, cols, ld_in, mode, len(out),
+                                        C.cast(pout, C.POINTER(C.c_void_p)), ld_out, op, _ptr(bias),
+                                        _stream_ptr(stream)))
 
 
 def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
-                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0, H_out=None):
-    """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers);
+                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0, H_out=None, bias=None):
+    """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers) (+ bias);
     optionally H_out = X A_i (the pre-activation kept for the backward)."""
     lib = load()
     M, H = int(X.shape[0]), int(X.shape[1])
@@ -300,7 +313,7 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
                        X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
-                       Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out))
+                       Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias))
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))

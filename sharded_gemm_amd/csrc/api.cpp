@@ -154,7 +154,16 @@ int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, i
 
 int tp_partial_reduce(const float *const *partials, int64_t P, int64_t rows, int64_t cols, int64_t ld_in,
                       int32_t mode, int64_t num_splits, float *const *out, int64_t ld_out, tp_stream_t stream) {
+  return tp_partial_reduce_ex(partials, P, rows, cols, ld_in, mode, num_splits, out, ld_out, TP_REDUCE_OP_SUM,
+                              nullptr, stream);
+}
+
+int tp_partial_reduce_ex(const float *const *partials, int64_t P, int64_t rows, int64_t cols, int64_t ld_in,
+                         int32_t mode, int64_t num_splits, float *const *out, int64_t ld_out, int32_t op,
+                         const float *bias, tp_stream_t stream) {
   clear_error();
+  if (op != TP_REDUCE_OP_SUM && op != TP_REDUCE_OP_MAX && op != TP_REDUCE_OP_MIN)
+    return fail(TP_ERR_ARG, "unknown reduce op %d", op);
   if (P < 1) return fail(TP_ERR_ARG, "P = %lld < 1", (long long)P);
   if (P > kMaxP) return fail(TP_ERR_UNSUPPORTED, "P = %lld > %lld", (long long)P, (long long)kMaxP);
   if (!partials) return fail(TP_ERR_ARG, "partials is NULL");
@@ -179,11 +188,12 @@ int tp_partial_reduce(const float *const *partials, int64_t P, int64_t rows, int
     }
     for (int64_t i = 0; i < j; ++i)
       if (overlaps(out[j], out_bytes, out[i], out_bytes)) return fail(TP_ERR_ARG, "out[%lld] overlaps out[%lld]", (long long)j, (long long)i);
+    if (bias && overlaps(out[j], out_bytes, bias, cols * 4)) return fail(TP_ERR_ARG, "out[%lld] overlaps bias", (long long)j);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t t0 = timing_begin(s);
   const int rc = partial_reduce_launch(partials, static_cast<int>(P), rows, cols, ld_in, out,
-                                       static_cast<int>(num_splits), rps, ld_out, s);
+                                       static_cast<int>(num_splits), rps, ld_out, s, 0, op, bias);
   if (rc == TP_OK) timing_end(t0, s, TP_KERNEL_REDUCE, 4.0 * (P + 1) * rows * cols);
   return rc;
 }
@@ -201,6 +211,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   if (a->H % a->col_chunks) return fail(TP_ERR_INDIVISIBLE, "col_chunks %lld does not divide H = %lld", (long long)a->col_chunks, (long long)a->H);
   if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
   if (a->P > 1 && (!a->peer_partials || !a->Z_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out");
+  if (a->bias && !a->Z_out) return fail(TP_ERR_ARG, "a bias needs Z_out (it is added to the full sum)");
   if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
   if (a->H_out && a->act == TP_ACT_NONE) return fail(TP_ERR_ARG, "H_out needs an activation (it would equal Y)");
   const int64_t M = a->M, H = a->H, F = a->F;
@@ -214,8 +225,10 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
     if (!a->peer_partials[p - 1]) return fail(TP_ERR_ARG, "peer_partials[%lld] is NULL", (long long)(p - 1));
     ins.push_back({a->peer_partials[p - 1], bz, "peer partial"});
   }
+  if (a->bias) ins.push_back({a->bias, H * 4, "bias"});
+  const bool reduce = a->P > 1 || a->bias;
   std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
-  if (a->P > 1 && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
+  if (reduce && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
   if (a->H_out) outs.push_back({a->H_out, by, "H_out"});
   for (size_t i = 0; i < outs.size(); ++i) {
     for (const Buf& in : ins)
@@ -229,7 +242,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   // The reduce stream only pays when a later block's GEMMs can run beside an
   // earlier block's reduce; with a single block the hand-off (an event record
   // and a cross-queue wait, about 10 us each way on MI355X) is pure latency.
-  const bool two = (s0 != s1) && a->P > 1 && R * C > 1;
+  const bool two = (s0 != s1) && reduce && R * C > 1;
   hipEvent_t *ev = nullptr;
   if (two) {
     const int rc = get_events(static_cast<size_t>(R * C + 1), &ev);
@@ -260,7 +273,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
       e = gemm_launch(g2, epi2, s0);
       if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
       timing_end(t0, s0, TP_KERNEL_GEMM2, 2.0 * Mr * Hc * F);
-      if (a->P == 1) continue;
+      if (!reduce) continue;
       hipStream_t sr = s0;
       if (two) {
         hipEvent_t done = ev[r * C + c];
@@ -273,7 +286,8 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
       float *dst = a->Z_out + zoff;
       hipEvent_t t1 = timing_begin(sr);
       const int rc = partial_reduce_launch(parts.data(), static_cast<int>(a->P), Mr, Hc, H, &dst, 1, Mr, H, sr,
-                                           two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0);
+                                           two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0,
+                                           TP_REDUCE_OP_SUM, a->bias ? a->bias + c * Hc : nullptr);
       if (rc != TP_OK) return rc;
       timing_end(t1, sr, TP_KERNEL_REDUCE, 4.0 * (a->P + 1) * Mr * Hc);
     }

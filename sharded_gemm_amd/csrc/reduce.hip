@@ -1,7 +1,9 @@
-// Partial-sum reduction: out = sum over p of partial_p, fp32, ascending p
-// ([SBP] "SBP": partial-sum pieces add up to the tensor; [CAI] section 2.1:
-// one all-reduce sums the row-parallel partials; sections 3 and 5.3: the
-// reduce-scatter form leaves rank j with row block j).
+// Partial reduction: out = op over p of partial_p (+ bias[col]), fp32,
+// ascending p ([SBP] "SBP": partial-sum pieces add up to the tensor, and min
+// and max apply to partial tensors the same way; [CAI] section 2.1: one
+// all-reduce sums the row-parallel partials; section 5.2: the row-parallel
+// layer's bias acts on the full output, so it is added once after the sum;
+// sections 3 and 5.3: the reduce-scatter form leaves rank j with row block j).
 //
 // Pure HBM streaming: each lane owns UNROLL output vectors, issues the loads
 // of every partial for all of them before it adds anything (P x UNROLL loads
@@ -13,6 +15,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "common.h"
 #include "shard.h"
@@ -29,6 +32,7 @@ constexpr int kGroup = 8;   // partials loaded together before adding
 struct RedArgs {
   const float *in[kMaxP];
   float *out[kMaxOut];
+  const float *bias;        // [cols], or null
   int32_t P;
   uint32_t cols_v;          // vectors per row
   uint32_t total_v;         // rows * cols_v
@@ -42,7 +46,22 @@ template <int VW> struct FVec;
 template <> struct FVec<4> { typedef f32x4_t T; };
 template <> struct FVec<1> { typedef float T; };
 
-template <int VW, int UNROLL>
+// OP: 0 sum, 1 max, 2 min (fmaxf / fminf: a NaN partial loses to a number).
+template <int OP, class V>
+__device__ __forceinline__ V combine(V acc, V v) {
+  if constexpr (OP == 0) {
+    return acc + v;
+  } else if constexpr (sizeof(V) == sizeof(float)) {
+    return OP == 1 ? fmaxf(acc, v) : fminf(acc, v);
+  } else {
+    V r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = OP == 1 ? fmaxf(acc[e], v[e]) : fminf(acc[e], v[e]);
+    return r;
+  }
+}
+
+template <int VW, int UNROLL, int OP, bool BIAS>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
   typedef typename FVec<VW>::T V;
   const uint32_t stride = gridDim.x * kThreads;
@@ -71,7 +90,12 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
       for (int g = 0; g < kGroup; ++g)
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-          if (p0 + g < a.P) acc[u] = (p0 + g == 0) ? v[g][u] : acc[u] + v[g][u];
+          if (p0 + g < a.P) acc[u] = (p0 + g == 0) ? v[g][u] : combine<OP>(acc[u], v[g][u]);
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        if (ok[u]) acc[u] = acc[u] + *reinterpret_cast<const V *>(a.bias + static_cast<int64_t>(col[u]) * VW);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
@@ -88,11 +112,12 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
 
 int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
                           float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
-                          hipStream_t stream, int64_t max_wgs) {
+                          hipStream_t stream, int64_t max_wgs, int op, const float *bias) {
   if (rows == 0 || cols == 0) return TP_OK;
   RedArgs a{};
   auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  bool vec = (cols % 4 == 0) && (ld_in % 4 == 0) && (ld_out % 4 == 0);
+  bool vec = (cols % 4 == 0) && (ld_in % 4 == 0) && (ld_out % 4 == 0) && (!bias || al16(bias));
+  a.bias = bias;
   for (int p = 0; p < P; ++p) {
     a.in[p] = partials[p];
     vec = vec && al16(partials[p]);
@@ -118,10 +143,20 @@ int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int
   const int64_t want = (total_v + kThreads * kUnroll - 1) / (kThreads * kUnroll);
   const int64_t cap = max_wgs > 0 ? std::min<int64_t>(max_wgs, 1 << 20) : (1 << 20);
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>(want, cap)));
-  if (vec)
-    hipLaunchKernelGGL((reduce_kernel<4, kUnroll>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((reduce_kernel<1, kUnroll>), grid, dim3(kThreads), 0, stream, a);
+  auto go = [&](auto vw, auto o, auto b) {
+    hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value>), grid,
+                       dim3(kThreads), 0, stream, a);
+  };
+  using std::integral_constant;
+  auto by_op = [&](auto vw, auto b) {
+    if (op == 1) go(vw, integral_constant<int, 1>{}, b);
+    else if (op == 2) go(vw, integral_constant<int, 2>{}, b);
+    else go(vw, integral_constant<int, 0>{}, b);
+  };
+  auto by_bias = [&](auto vw) {
+    if (bias) by_op(vw, std::true_type{}); else by_op(vw, std::false_type{});
+  };
+  if (vec) by_bias(integral_constant<int, 4>{}); else by_bias(integral_constant<int, 1>{});
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TP_ERR_HIP, "reduce launch: %s", hipGetErrorString(e));
   return TP_OK;

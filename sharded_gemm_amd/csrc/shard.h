@@ -14,12 +14,12 @@ namespace tpshard {
 int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esize, void *const *dst,
                              hipStream_t stream);
 
-// out_row_block(row) <- sum over p of partials[p][row, :], ascending p, fp32.
-// rows_per_out rows go to each out[j]; out[j] has row stride ld_out.
-// Arguments already validated (1 <= P <= 64, 1 <= nout <= 64).
-// max_wgs > 0 caps the grid (the kernel strides over the rest).
+// out_row_block(row) <- op over p of partials[p][row, :] (+ bias[:]), ascending
+// p, fp32; op 0 sum, 1 max, 2 min.  rows_per_out rows go to each out[j]; out[j]
+// has row stride ld_out.  Arguments already validated (1 <= P <= 64,
+// 1 <= nout <= 64).  max_wgs > 0 caps the grid (the kernel strides over the rest).
 int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
                           float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
-                          hipStream_t stream, int64_t max_wgs = 0);
+                          hipStream_t stream, int64_t max_wgs = 0, int op = 0, const float *bias = nullptr);
 
 }  // namespace tpshard

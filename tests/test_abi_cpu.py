@@ -260,3 +260,28 @@ def test_backward_peer_validation():
     assert lib.tp_colrow_mlp_backward(C.byref(a), None, None) == _abi.TP_ERR_ARG
     peers[0] = FAKE + (7 << 20) + 8   # overlaps dX_i
     assert lib.tp_colrow_mlp_backward(C.byref(a), None, None) == _abi.TP_ERR_ARG
+
+
+def _reduce_ex(op=0, bias=None, **kw):
+    lib = _abi.load()
+    P, rows, cols = 2, 8, 8
+    parts = [FAKE + p * (1 << 20) for p in range(P)]
+    outs = kw.get("outs", [FAKE + (100 << 20)])
+    pin = (C.c_void_p * P)(*parts)
+    pout = (C.c_void_p * len(outs))(*outs)
+    return lib.tp_partial_reduce_ex(C.cast(pin, C.POINTER(C.c_void_p)), P, rows, cols, cols, 0, 1,
+                                    C.cast(pout, C.POINTER(C.c_void_p)), cols, op, bias, None)
+
+
+def test_reduce_ex_validation():
+    assert _reduce_ex(op=3) == _abi.TP_ERR_ARG
+    assert _reduce_ex(op=-1) == _abi.TP_ERR_ARG
+    assert _reduce_ex(op=1, bias=FAKE + (100 << 20) + 16) == _abi.TP_ERR_ARG   # bias inside the output
+
+
+def test_mlp_bias_needs_z_out():
+    lib = _abi.load()
+    assert lib.tp_colrow_mlp(C.byref(_mlp_args(bias=FAKE + (30 << 20))), None, None) == _abi.TP_ERR_ARG
+    # bias overlapping Z_out
+    a = _mlp_args(bias=FAKE + (9 << 20) + 4, Z_out=FAKE + (9 << 20))
+    assert lib.tp_colrow_mlp(C.byref(a), None, None) == _abi.TP_ERR_ARG

@@ -261,3 +261,25 @@ def test_graph_replay_matches_eager():
         assert torch.equal(Z.view(torch.int32), ref_z.view(torch.int32)), rep
         assert torch.equal(Zo.view(torch.int32), ref_zo.view(torch.int32)), rep
         peers[0].add_(0.0)   # eager work between replays
+
+
+@pytest.mark.parametrize("M,H,F,Rc,Cc,P", [(515, 256, 96, 1, 1, 1), (512, 384, 256, 2, 3, 3), (1030, 640, 320, 2, 5, 4)])
+def test_row_parallel_bias_integer_exact(M, H, F, Rc, Cc, P):
+    """Z_out = Z_i + peers + bias ([CAI] section 5.2: the bias acts on the full
+    output, added once); Z_i itself stays bias-free.  Integers: exact."""
+    announce(f"mlp bias integer exact M={M} H={H} F={F} R={Rc} C={Cc} P={P}")
+    X = inputs.small_ints((M, H), seed=251, lo=-4, hi=4, dtype="bf16")
+    A = _one_hot_columns(H, F, 252)
+    B = inputs.small_ints((F, H), seed=253, lo=-4, hi=4, dtype="bf16")
+    bias_cpu = inputs.small_ints((H,), seed=254, lo=-64, hi=64)
+    peers_cpu = [inputs.small_ints((M, H), seed=260 + p, lo=-512, hi=512) for p in range(P - 1)]
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    Zo = torch.empty((M, H), device="cuda")
+    tp.tp_colrow_mlp(X.cuda(), A.cuda(), B.cuda(), Y, Z, row_chunks=Rc, col_chunks=Cc,
+                     peer_partials=[p.cuda() for p in peers_cpu], Z_out=Zo, act=tp.TP_ACT_NONE,
+                     s_reduce=torch.cuda.Stream(), bias=bias_cpu.cuda())
+    torch.cuda.synchronize()
+    z_ref = O.mlp_rank(X, A, B, O.GELU_NONE)
+    assert np.array_equal(Z.cpu().numpy().astype(np.float64), z_ref)
+    assert np.array_equal(Zo.cpu().numpy().astype(np.float64), R.reduce_full([z_ref] + peers_cpu, "sum", bias_cpu))

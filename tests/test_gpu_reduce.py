@@ -94,3 +94,64 @@ def test_error_leaves_output_untouched():
     assert e.value.kind == "indivisible"
     torch.cuda.synchronize()
     assert all(o.body_untouched() for o in outs)
+
+
+# ---- partial max / min and the bias ------------------------------------------
+
+OPS = {tp.TP_REDUCE_OP_SUM: "sum", tp.TP_REDUCE_OP_MAX: "max", tp.TP_REDUCE_OP_MIN: "min"}
+
+
+@pytest.mark.parametrize("op", [tp.TP_REDUCE_OP_MAX, tp.TP_REDUCE_OP_MIN])
+@pytest.mark.parametrize("P,rows,cols,ld", [(1, 5, 3, 3), (3, 64, 1027, 1027), (8, 300, 256, 384), (13, 129, 768, 768)])
+def test_max_min_bit_exact(op, P, rows, cols, ld):
+    """max / min pick one of the inputs, so the result is bit-exact."""
+    announce(f"reduce FULL op={OPS[op]} P={P} rows={rows} cols={cols} ld={ld}")
+    parts_cpu = [inputs.normal((rows, ld), seed=8000 + p) for p in range(P)]
+    out = Guarded((rows, ld), torch.float32)
+    tp.tp_partial_reduce([p.cuda() for p in parts_cpu], [out.t], rows=rows, cols=cols, ld_in=ld, ld_out=ld, op=op)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    ref = R.reduce_full([p[:, :cols] for p in parts_cpu], OPS[op])
+    assert np.array_equal(out.t.cpu()[:, :cols].numpy().astype(np.float64), ref)
+
+
+def test_max_min_nan_loses_to_a_number():
+    announce("reduce max/min with NaN")
+    a = torch.tensor([[float("nan"), 1.0, float("nan"), -3.0]], device="cuda")
+    b = torch.tensor([[2.0, float("nan"), float("nan"), 5.0]], device="cuda")
+    for op in (tp.TP_REDUCE_OP_MAX, tp.TP_REDUCE_OP_MIN):
+        out = torch.empty_like(a)
+        tp.tp_partial_reduce([a, b], [out], op=op)
+        ref = R.reduce_full([a.cpu(), b.cpu()], OPS[op])
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+@pytest.mark.parametrize("op", [tp.TP_REDUCE_OP_SUM, tp.TP_REDUCE_OP_MAX, tp.TP_REDUCE_OP_MIN])
+@pytest.mark.parametrize("mode,S,rows,cols,boff", [("full", 1, 96, 1000, 0), ("full", 1, 33, 517, 0),
+                                                   ("full", 1, 96, 1000, 1), ("split", 4, 64, 1000, 0),
+                                                   ("split", 8, 8192, 1024, 0)])
+def test_bias_integer_exact(op, mode, S, rows, cols, boff):
+    """out = op over partials + bias, on integers: exact.  boff = 1 misaligns the
+    bias by one element (scalar path)."""
+    announce(f"reduce {mode} op={OPS[op]} + bias rows={rows} cols={cols} S={S} bias offset {boff}")
+    P = 5
+    parts_cpu = [inputs.small_ints((rows, cols), seed=8100 + p, lo=-1000, hi=1000) for p in range(P)]
+    bias_cpu = inputs.small_ints((cols + boff,), seed=8199, lo=-100, hi=100)
+    bias = bias_cpu.cuda()
+    outs = [torch.empty((rows // S, cols), device="cuda") for _ in range(S)]
+    tp.tp_partial_reduce([p.cuda() for p in parts_cpu], outs, tp.TP_REDUCE_FULL if mode == "full" else tp.TP_REDUCE_SPLIT,
+                         op=op, bias=bias[boff:])
+    ref = R.reduce_split(parts_cpu, S, OPS[op], bias_cpu[boff:])
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o.cpu().numpy().astype(np.float64), r)
+
+
+def test_bias_with_random_sum():
+    announce("reduce FULL sum + bias, random")
+    parts_cpu = [inputs.normal((512, 768), seed=8300 + p) for p in range(4)]
+    bias_cpu = inputs.normal((768,), seed=8399)
+    out = torch.empty((512, 768), device="cuda")
+    tp.tp_partial_reduce([p.cuda() for p in parts_cpu], [out], bias=bias_cpu.cuda())
+    assert rel_err(out.cpu(), R.reduce_full(parts_cpu, "sum", bias_cpu)) <= TOL

@@ -162,3 +162,25 @@ def test_backward_rank_sum_drops_a_rank(monkeypatch):
         return real(X, A_shards[:-1], B_shards[:-1], dZ, act)[0], *real(X, A_shards, B_shards, dZ, act)[1:]
     monkeypatch.setattr(O, "backward_all_ranks", bad)
     assert _fails(TB.test_sum_of_rank_gradients_is_the_unsharded_gradient, 3)
+
+
+# ---- partial max / min, bias -------------------------------------------------
+
+def test_reduce_max_as_min(monkeypatch):
+    real = R.reduce_full
+
+    def bad(parts, op="sum", bias=None):
+        return real(parts, {"max": "min", "min": "max"}.get(op, op), bias)
+    monkeypatch.setattr(R, "reduce_full", bad)
+    assert _fails(TR.test_max_min_brute_force)
+
+
+def test_bias_added_per_partial(monkeypatch):
+    real = R.reduce_full
+
+    def bad(parts, op="sum", bias=None):
+        if bias is None:
+            return real(parts, op)
+        return real([np.asarray(p) + np.asarray(bias) for p in parts], op)
+    monkeypatch.setattr(R, "reduce_full", bad)
+    assert _fails(TR.test_bias_is_added_once_after_the_sum)

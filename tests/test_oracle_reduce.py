@@ -53,3 +53,63 @@ def test_split_rejections():
         R.reduce_full([])
     with pytest.raises(OracleLayoutError):
         R.reduce_full([p, np.zeros((2, 6), np.float32)])
+
+
+# ---- partial max / min and the row-parallel bias ----------------------------
+
+def test_max_min_brute_force():
+    """Element by element with Python's own max / min over the P values."""
+    rng = np.random.default_rng(5)
+    parts = [rng.integers(-9, 10, size=(3, 4)).astype(np.float32) for _ in range(5)]
+    mx, mn = R.reduce_full(parts, "max"), R.reduce_full(parts, "min")
+    for i in range(3):
+        for j in range(4):
+            vals = [float(p[i, j]) for p in parts]
+            assert mx[i, j] == max(vals) and mn[i, j] == min(vals)
+
+
+def test_max_min_invariants():
+    rng = np.random.default_rng(6)
+    parts = [rng.standard_normal((16, 8)) for _ in range(7)]
+    mx, mn = R.reduce_full(parts, "max"), R.reduce_full(parts, "min")
+    st = np.stack(parts)
+    assert (st <= mx).all() and (st >= mn).all()
+    assert ((st == mx).any(axis=0)).all() and ((st == mn).any(axis=0)).all()   # attained by some partial
+    # max(a) = -min(-a)
+    assert np.array_equal(mx, -R.reduce_full([-p for p in parts], "min"))
+    assert np.array_equal(R.reduce_full(parts[:1], "max"), parts[0])
+    # max(x, -x) = |x| and min(x, -x) = -|x|
+    assert np.array_equal(R.reduce_full([parts[0], -parts[0]], "max"), np.abs(parts[0]))
+    assert np.array_equal(R.reduce_full([parts[0], -parts[0]], "min"), -np.abs(parts[0]))
+
+
+def test_max_ignores_nan_against_a_number():
+    a = np.array([[np.nan, 1.0]])
+    b = np.array([[2.0, np.nan]])
+    assert np.array_equal(R.reduce_full([a, b], "max"), np.array([[2.0, 1.0]]))
+    assert np.array_equal(R.reduce_full([a, b], "min"), np.array([[2.0, 1.0]]))
+
+
+def test_bias_is_added_once_after_the_sum():
+    """[CAI] section 5.2: the row-parallel layer's output with bias b is
+    Y B + b for the full Y B; the ranks' partials sum to Y B, so b is added
+    to the reduced value once (adding it per partial would count it P times)."""
+    rng = np.random.default_rng(8)
+    M, H, F, P = 5, 6, 3, 4
+    Y = rng.standard_normal((M, P * F))
+    B = rng.standard_normal((P * F, H))
+    b = rng.standard_normal(H)
+    parts = [Y[:, i * F:(i + 1) * F] @ B[i * F:(i + 1) * F, :] for i in range(P)]
+    # the unsharded linear layer, row by row
+    ref = np.array([[sum(Y[m, k] * B[k, h] for k in range(P * F)) + b[h] for h in range(H)] for m in range(M)])
+    assert np.allclose(R.reduce_full(parts, "sum", b), ref, atol=1e-12)
+    blocks = R.reduce_split(parts, 5, "sum", b)
+    assert np.allclose(np.concatenate(blocks), ref, atol=1e-12)
+
+
+def test_op_rejections():
+    with pytest.raises(OracleLayoutError) as e:
+        R.reduce_full([np.zeros((2, 2))], "prod")
+    assert e.value.kind == "arg"
+    with pytest.raises(OracleLayoutError):
+        R.reduce_full([np.zeros((2, 2))], "sum", np.zeros(3))

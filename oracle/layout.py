@@ -12,6 +12,10 @@ Sources, cited by page title and section:
   full copy) and section "2D SBP" (ranks matrix, placement.hierarchy).
 * Paddle "SPMD 推导规则与 Pipeline 调度", sections "ProcessMesh" and
   "dims_mapping".
+* ColossalAI 1D tensor parallelism, sections 5.1 (``gather_output``: the
+  column layer's split outputs all-gathered along the last axis) and 5.3
+  (sequence parallelism: the input all-gathered along the sequence axis); the
+  gather functions below assemble that all-gathered tensor.
 
 A spec is a plain dict::
 
@@ -166,6 +170,38 @@ def split(tensor, spec):
     return out
 
 
+def _place(out, box, piece, who):
+    piece = _as_numpy(piece)
+    ext = tuple(b - a for a, b in box)
+    if piece.shape != ext:
+        raise OracleLayoutError("arg", f"piece of {who} has shape {piece.shape}, the layout gives {ext}")
+    out[tuple(slice(a, b) for a, b in box)] = piece
+
+
+def gather(pieces, shape, spec):
+    """The inverse of ``split``: the logical tensor assembled from its pieces.
+
+    ``pieces`` maps device id -> that device's shard.  OneFlow's SBP section
+    defines split pieces as blocks that concatenate back to the logical tensor
+    and broadcast pieces as full copies, so the logical tensor is every
+    distinct shard written into its box.  ColossalAI's ``gather_output`` and
+    the all-gather of sequence parallelism (sections 5.1 and 5.3) produce this
+    tensor on every rank.  Replicas of a shard are equal by definition; the
+    copy taken is the one on the first device the shard's group lists.
+    """
+    boxes, groups = shard_boxes(shape, spec)
+    shape = tuple(int(d) for d in shape)
+    first = None
+    for grp in groups:
+        if grp[0] not in pieces:
+            raise OracleLayoutError("arg", f"no piece for device {grp[0]}")
+        first = _as_numpy(pieces[grp[0]]) if first is None else first
+    out = np.zeros(shape, dtype=first.dtype if first is not None else np.float32)
+    for box, grp in zip(boxes, groups):
+        _place(out, box, pieces[grp[0]], f"device {grp[0]}")
+    return out
+
+
 # --------------------------------------------------------------------------
 # ProcessMesh + dims_mapping (Paddle SPMD-rules page; OneFlow 2D SBP)
 # --------------------------------------------------------------------------
@@ -232,4 +268,34 @@ def split_dims_mapping(tensor, mesh_dims, process_ids, dims_mapping):
                 w = shape[i] // mesh_dims[j]
                 sl.append(slice(coord[j] * w, (coord[j] + 1) * w))
         out[process_ids[linear]] = np.ascontiguousarray(t[tuple(sl)]).copy()
+    return out
+
+
+def gather_dims_mapping(pieces, shape, mesh_dims, process_ids, dims_mapping):
+    """The inverse of ``split_dims_mapping``: the logical tensor from
+    ``{process id: local tensor}``.  Processes whose mesh coordinates differ
+    only along mesh dims no tensor axis uses hold the same block; the block is
+    taken from the first of them in row-major mesh order."""
+    shape = [int(d) for d in shape]
+    mesh_dims = [int(m) for m in mesh_dims]
+    process_ids = [int(p) for p in process_ids]
+    dims_mapping = [int(j) for j in dims_mapping]
+    _check_mesh(shape, mesh_dims, process_ids, dims_mapping)
+    out = None
+    done = set()
+    for linear, coord in enumerate(itertools.product(*[range(m) for m in mesh_dims])):
+        block = tuple(coord[j] if j >= 0 else 0 for j in dims_mapping)
+        if block in done:
+            continue
+        done.add(block)
+        pid = process_ids[linear]
+        if pid not in pieces:
+            raise OracleLayoutError("arg", f"no piece for process {pid}")
+        if out is None:
+            out = np.zeros(shape, dtype=_as_numpy(pieces[pid]).dtype)
+        box = []
+        for i, j in enumerate(dims_mapping):
+            w = shape[i] // mesh_dims[j] if j >= 0 else shape[i]
+            box.append((block[i] * w, block[i] * w + w) if j >= 0 else (0, shape[i]))
+        _place(out, box, pieces[pid], f"process {pid}")
     return out

@@ -184,3 +184,48 @@ def test_bias_added_per_partial(monkeypatch):
         return real([np.asarray(p) + np.asarray(bias) for p in parts], op)
     monkeypatch.setattr(R, "reduce_full", bad)
     assert _fails(TR.test_bias_is_added_once_after_the_sum)
+
+
+def test_gather_takes_last_replica(monkeypatch):
+    import test_oracle_gather as TG
+
+    def bad(pieces, shape, spec):
+        boxes, groups = L.shard_boxes(shape, spec)
+        out = np.zeros(tuple(shape))
+        for box, grp in zip(boxes, groups):
+            out[tuple(slice(a, b) for a, b in box)] = pieces[grp[-1]]
+        return out
+    monkeypatch.setattr(L, "gather", bad)
+    assert _fails(TG.test_replica_taken_from_first_listed_device)
+
+
+def test_gather_pieces_in_reverse_boxes(monkeypatch):
+    import test_oracle_gather as TG
+    real = L.shard_boxes
+
+    def bad_gather(pieces, shape, spec):
+        boxes, groups = real(shape, spec)
+        out = np.zeros(tuple(shape), dtype=np.float32)
+        for box, grp in zip(reversed(boxes), groups):
+            out[tuple(slice(a, b) for a, b in box)] = pieces[grp[0]]
+        return out
+    monkeypatch.setattr(L, "gather", bad_gather)
+    case = [c for c in TL._load()["cases"] if c["name"] == "E1_axis0"][0]
+    assert _fails(TG.test_page_examples_gather_back, case)
+
+
+def test_gather_dims_mapping_later_replica_overwrites(monkeypatch):
+    import itertools
+    import test_oracle_gather as TG
+
+    def bad(pieces, shape, mesh_dims, process_ids, dims_mapping):
+        out = np.zeros(tuple(shape))
+        for linear, coord in enumerate(itertools.product(*[range(m) for m in mesh_dims])):
+            sl = []
+            for i, j in enumerate(dims_mapping):
+                w = shape[i] // mesh_dims[j] if j >= 0 else shape[i]
+                sl.append(slice(coord[j] * w, coord[j] * w + w) if j >= 0 else slice(0, shape[i]))
+            out[tuple(sl)] = pieces[process_ids[linear]]
+        return out
+    monkeypatch.setattr(L, "gather_dims_mapping", bad)
+    assert _fails(TG.test_replica_taken_from_first_listed_device)

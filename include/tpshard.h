@@ -141,6 +141,30 @@ int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, i
                          const tp_layout *layout, void *const *dst, int64_t num_dst,
                          tp_stream_t stream);
 
+/* ---- gather (the inverse of materialisation) ------------------------- */
+/*
+ * Assemble the full row-major tensor of shape[ndim] from its per-device shards
+ * and write it to each of num_out outputs: the all-gather of a layout ([SBP]
+ * "SBP": split pieces concatenate back to the logical tensor, broadcast pieces
+ * are copies of it; [CAI] section 5.1, gather_output: the column layer's
+ * split outputs all-gathered along the last axis; section 5.3: the
+ * sequence-parallel input all-gathered along the sequence axis).
+ *   src: host array of num_src device pointers, indexed by physical device id
+ *        as in tp_shard_materialize; src[d] holds device d's shard row-major.
+ *        Each distinct shard is read once, from the first device its group
+ *        lists (replicas are copies by definition and are not compared);
+ *        entries of other devices are not read and may be NULL.
+ *   out: host array of num_out >= 1 device pointers, each receiving the whole
+ *        tensor; outputs must not overlap each other or a shard that is read.
+ * Bits are copied, never converted (dtype TP_F32 or TP_BF16).
+ * Errors: as tp_layout_plan, plus TP_ERR_ARG for a null or too-short src, a
+ *         NULL src of a read device, num_out < 1, a NULL or overlapping
+ *         output, a bad dtype; TP_ERR_HIP.
+ */
+int tp_shard_gather(const void *const *src, int64_t num_src, int32_t dtype, const int64_t *shape,
+                    int64_t ndim, const tp_layout *layout, void *const *out, int64_t num_out,
+                    tp_stream_t stream);
+
 /* ---- partial-sum reduction ------------------------------------------- */
 enum { TP_REDUCE_FULL = 0, TP_REDUCE_SPLIT = 1 };
 /*
@@ -214,7 +238,22 @@ typedef struct {
                         Must be NULL when act = TP_ACT_NONE (H would equal Y). */
   const float *bias; /* optional [H] fp32: the row-parallel layer's bias, added once to the
                         full sum ([CAI] section 5.2), so Z_out = sum of partials + bias;
-                        NULL = none.  Needs Z_out (for any P); Z_i stays bias-free. */
+                        NULL = none.  Needs Z_out or Z_split (for any P); Z_i stays
+                        bias-free. */
+  /* Sequence parallelism ([CAI] section 5.3: the column layer all-gathers its
+   * input along the sequence axis, the row layer reduce-scatters its output
+   * instead of all-reducing it).  X and Z are [M, H] with the token (sequence)
+   * axis outermost, so sequence block j is rows [j*M/S, (j+1)*M/S). */
+  int64_t seq_splits;/* S: 0 or 1 = off; else 2..64, divides M, and the row chunks and
+                        the sequence blocks nest (M/R divides M/S or M/S divides M/R) */
+  const void *const *X_shards; /* optional host array of S device pointers, each [M/S, H]
+                        (dtype): sequence block j of the input.  When set the call
+                        all-gathers them into X, which is then a caller-owned
+                        [M, H] workspace the call writes, chunk r on s_reduce before
+                        chunk r's first GEMM on s_compute reads it */
+  float *const *Z_split; /* optional host array of S device pointers, each [M/S, H] fp32:
+                        the reduce-scattered output, block j = rows [j*M/S, (j+1)*M/S)
+                        of Z_i + peers (+ bias).  Replaces Z_out, which must be NULL. */
 } tp_mlp_args;
 
 /*
@@ -229,10 +268,14 @@ typedef struct {
  * overlap it.  The calls are capturable into a HIP graph (no memsets, no
  * allocation, no host synchronisation).
  * Chunking never changes a result bit: each output element is accumulated in
- * the same order whatever R and C are.
+ * the same order whatever R and C are.  With sequence parallelism (S > 1) the
+ * gather of chunk r+1's input rows runs on s_reduce beside chunk r's GEMMs,
+ * and each block's reduction is written to the sequence blocks it covers.
  * Errors: TP_ERR_ARG (null or overlapping buffers, bad dtype/act, sizes < 1,
- *         P out of range), TP_ERR_INDIVISIBLE (R does not divide M, C does not
- *         divide H), TP_ERR_HIP.
+ *         P or S out of range, X_shards or Z_split without S > 1, Z_out with
+ *         Z_split), TP_ERR_INDIVISIBLE (R does not divide M, C does not divide
+ *         H, S does not divide M), TP_ERR_UNSUPPORTED (row chunks and sequence
+ *         blocks that do not nest), TP_ERR_HIP.
  */
 int tp_colrow_mlp(const tp_mlp_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
 
@@ -266,6 +309,16 @@ typedef struct {
   float *dX_out;     /* [M,H] fp32, required when P > 1: dX_i + sum of peers, written chunk
                         by chunk on s_reduce; may equal dX_i */
   int64_t reduce_workgroups; /* as in the forward; 0 = library default; >= 0 */
+  /* Sequence parallelism ([CAI] section 5.3: in the backward the row layer
+   * all-gathers the output gradient and the column layer reduce-scatters the
+   * input gradient).  X is the forward's gathered [M, H] input. */
+  int64_t seq_splits;/* S: 0 or 1 = off; else as in the forward */
+  const void *const *dZ_shards; /* optional host array of S device pointers, each [M/S, H]
+                        (dtype): sequence block j of dZ.  When set the call all-gathers
+                        them into dZ, which is then a caller-owned [M, H] workspace */
+  float *const *dX_split; /* optional host array of S device pointers, each [M/S, H] fp32:
+                        the reduce-scattered input gradient (replaces dX_out, which
+                        must be NULL) */
 } tp_mlp_bwd_args;
 
 /*
@@ -280,17 +333,23 @@ typedef struct {
  * gradients continue one fp32 accumulation across chunks (each GEMM starts
  * from the previous chunk's result), so the result does not depend on R.
  * Before returning, s_compute waits for s_reduce.  Capturable into a HIP graph.
+ * With sequence parallelism, chunk r's rows of dZ are gathered on s_reduce
+ * ahead of chunk r's GEMMs and dX is reduce-scattered into dX_split.
  * Errors: TP_ERR_ARG (null or overlapping buffers, bad dtype/act, sizes < 1,
- *         P out of range), TP_ERR_INDIVISIBLE (R does not divide M), TP_ERR_HIP.
+ *         P or S out of range, dZ_shards or dX_split without S > 1, dX_out with
+ *         dX_split), TP_ERR_INDIVISIBLE (R or S does not divide M),
+ *         TP_ERR_UNSUPPORTED (row chunks and sequence blocks that do not nest),
+ *         TP_ERR_HIP.
  */
 int tp_colrow_mlp_backward(const tp_mlp_bwd_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
 
 /* ---- per-kernel timing (measurement support) ---------------------------- */
 /* Kernel families timed by the optional instrumentation below: the forward's
  * GEMMs, the backward's input-gradient GEMMs (dH and dX) and its
- * weight-gradient GEMMs (dA and dB). */
+ * weight-gradient GEMMs (dA and dB), and the gather kernel. */
 enum { TP_KERNEL_MATERIALIZE = 0, TP_KERNEL_GEMM1 = 1, TP_KERNEL_GEMM2 = 2, TP_KERNEL_REDUCE = 3,
-       TP_KERNEL_GEMM_DGRAD = 4, TP_KERNEL_GEMM_WGRAD = 5, TP_KERNEL_KINDS = 6 };
+       TP_KERNEL_GEMM_DGRAD = 4, TP_KERNEL_GEMM_WGRAD = 5, TP_KERNEL_GATHER = 6,
+       TP_KERNEL_KINDS = 7 };
 
 typedef struct {
   int64_t launches;  /* kernel launches timed since the last read */

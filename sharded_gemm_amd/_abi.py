@@ -37,10 +37,10 @@ TP_REDUCE_OP_MAX = 1
 TP_REDUCE_OP_MIN = 2
 
 # Every symbol include/tpshard.h declares.
-EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_shard_materialize",
+EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_shard_materialize", "tp_shard_gather",
            "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
-TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad")
+TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather")
 
 
 class TpError(RuntimeError):
@@ -85,7 +85,8 @@ class tp_mlp_args(C.Structure):
                 ("Y_ws", C.c_void_p), ("Z_i", C.c_void_p),
                 ("row_chunks", C.c_int64), ("col_chunks", C.c_int64), ("P", C.c_int64),
                 ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
-                ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p), ("bias", C.c_void_p)]
+                ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p), ("bias", C.c_void_p),
+                ("seq_splits", C.c_int64), ("X_shards", C.POINTER(C.c_void_p)), ("Z_split", C.POINTER(C.c_void_p))]
 
 
 class tp_mlp_bwd_args(C.Structure):
@@ -96,7 +97,8 @@ class tp_mlp_bwd_args(C.Structure):
                 ("dH_ws", C.c_void_p), ("dX_i", C.c_void_p), ("dA_i", C.c_void_p), ("dB_i", C.c_void_p),
                 ("accumulate", C.c_int32), ("row_chunks", C.c_int64), ("P", C.c_int64),
                 ("peer_dX", C.POINTER(C.c_void_p)), ("dX_out", C.c_void_p),
-                ("reduce_workgroups", C.c_int64)]
+                ("reduce_workgroups", C.c_int64),
+                ("seq_splits", C.c_int64), ("dZ_shards", C.POINTER(C.c_void_p)), ("dX_split", C.POINTER(C.c_void_p))]
 
 
 class tp_kernel_stat(C.Structure):
@@ -126,6 +128,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.tp_shard_materialize.restype = C.c_int
     lib.tp_shard_materialize.argtypes = [C.c_void_p, C.c_int32, i64p, C.c_int64, C.POINTER(tp_layout),
                                          C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
+    lib.tp_shard_gather.restype = C.c_int
+    lib.tp_shard_gather.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int32, i64p, C.c_int64, C.POINTER(tp_layout),
+                                    C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
     lib.tp_partial_reduce.restype = C.c_int
     lib.tp_partial_reduce.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                                       C.c_int32, C.c_int64, C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
@@ -262,6 +267,43 @@ def tp_shard_materialize(src, layout: dict, dst, stream=None):
                                     _stream_ptr(stream)))
 
 
+def tp_shard_gather(src, layout: dict, out, shape, stream=None):
+    """All-gather: write the full tensor of ``shape`` assembled from the shards in
+    ``src`` (dict or list: device id -> tensor, None where not read) into every
+    tensor of the list ``out``."""
+    lib = load()
+    lay, keep = make_layout(layout)
+    items = list(src.items() if isinstance(src, dict) else enumerate(src))
+    num_src = (max(d for d, _ in items) + 1) if items else 0
+    ptrs = (C.c_void_p * max(1, num_src))()
+    dtype = None
+    for d, t in items:
+        ptrs[d] = _ptr(t) if t is not None else None
+        if t is not None and dtype is None:
+            dtype = _dtype_code(t)
+    outs = list(out)
+    if dtype is None:
+        dtype = _dtype_code(outs[0])
+    optr = (C.c_void_p * max(1, len(outs)))(*[_ptr(t) for t in outs])
+    shp = _i64_array(shape)
+    _check(lib.tp_shard_gather(C.cast(ptrs, C.POINTER(C.c_void_p)), num_src, dtype, C.cast(shp, C.POINTER(C.c_int64)),
+                               len(shape), C.byref(lay), C.cast(optr, C.POINTER(C.c_void_p)), len(outs),
+                               _stream_ptr(stream)))
+
+
+def _seq_arrays(shards, split):
+    """(S, ctypes array or None, ctypes array or None) for the sequence-parallel fields."""
+    shards = list(shards) if shards is not None else None
+    split = list(split) if split is not None else None
+    lens = {len(x) for x in (shards, split) if x is not None}
+    if len(lens) > 1:
+        raise ValueError("the input shards and the split outputs must have the same count")
+    S = lens.pop() if lens else 0
+    def arr(xs):
+        return C.cast((C.c_void_p * len(xs))(*[_ptr(t) for t in xs]), C.POINTER(C.c_void_p)) if xs else None
+    return S, arr(shards), arr(split)
+
+
 def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, ld_in=None, ld_out=None,
                       stream=None, op=TP_REDUCE_OP_SUM, bias=None):
     """Reduce fp32 ``partials`` (list of tensors or raw device pointers) into ``out`` (list)
@@ -290,9 +332,14 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
 
 
 def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
-                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0, H_out=None, bias=None):
+                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0, H_out=None, bias=None,
+                  X_shards=None, Z_split=None):
     """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers) (+ bias);
-    optionally H_out = X A_i (the pre-activation kept for the backward)."""
+    optionally H_out = X A_i (the pre-activation kept for the backward).
+
+    Sequence parallelism: with ``X_shards`` (S tensors [M/S, H]) X is a workspace
+    the call fills by all-gathering them; with ``Z_split`` (S tensors [M/S, H] fp32)
+    the sum is reduce-scattered into the blocks instead of written to Z_out."""
     lib = load()
     M, H = int(X.shape[0]), int(X.shape[1])
     F = int(A_i.shape[1])
@@ -314,6 +361,8 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
                        Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias))
+    S, xs, zs = _seq_arrays(X_shards, Z_split)
+    args.seq_splits, args.X_shards, args.Z_split = S, xs, zs
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
@@ -321,9 +370,12 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
 
 def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *, row_chunks=1, peer_dX=(),
                            dX_out=None, act=TP_ACT_GELU_ERF, accumulate=False, s_compute=None, s_reduce=None,
-                           reduce_workgroups=0):
+                           reduce_workgroups=0, dZ_shards=None, dX_split=None):
     """Backward of one rank's MLP share: dH_ws = (dZ B_i^T) * act'(H_i); dX_i = dH_ws A_i^T;
-    dX_out = dX_i + sum(peers); dA_i (+)= X^T dH_ws; dB_i (+)= Y_i^T dZ."""
+    dX_out = dX_i + sum(peers); dA_i (+)= X^T dH_ws; dB_i (+)= Y_i^T dZ.
+
+    Sequence parallelism: with ``dZ_shards`` dZ is a workspace the call fills by
+    all-gathering them; with ``dX_split`` the input gradient is reduce-scattered."""
     lib = load()
     M, H = int(X.shape[0]), int(X.shape[1])
     F = int(A_i.shape[1])
@@ -350,6 +402,8 @@ def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *
                            accumulate=1 if accumulate else 0, row_chunks=row_chunks, P=1 + len(peers),
                            peer_dX=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
                            dX_out=_ptr(dX_out), reduce_workgroups=reduce_workgroups)
+    S, gs, xs = _seq_arrays(dZ_shards, dX_split)
+    args.seq_splits, args.dZ_shards, args.dX_split = S, gs, xs
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     _check(lib.tp_colrow_mlp_backward(C.byref(args), sc, sr))

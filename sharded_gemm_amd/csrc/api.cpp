@@ -80,6 +80,93 @@ int64_t matrix_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
   return ((rows - 1) * ld + cols) * esize;
 }
 
+struct Buf { const void *p; int64_t n; const char *name; };
+
+// Every output is disjoint from every input and from every other output.
+int check_disjoint(const std::vector<Buf>& ins, const std::vector<Buf>& outs) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Buf& in : ins)
+      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, in.name);
+    for (size_t j = 0; j < i; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  return TP_OK;
+}
+
+// Sequence blocks of an [M, .] tensor with the token axis outermost: S blocks
+// of Ms rows.  S = 1 means sequence parallelism is off.
+struct SeqSplit {
+  int64_t S = 1, Ms = 0;
+};
+
+int check_seq(int64_t seq_splits, int64_t M, int64_t R, const void *shards, const void *split, const void *full_out,
+              const char *shards_name, const char *split_name, const char *full_name, SeqSplit *sq) {
+  if (seq_splits < 0 || seq_splits > kMaxSplits)
+    return fail(TP_ERR_ARG, "seq_splits = %lld outside [0, %lld]", (long long)seq_splits, (long long)kMaxSplits);
+  sq->S = seq_splits > 1 ? seq_splits : 1;
+  sq->Ms = M / sq->S;
+  if (sq->S == 1) {
+    if (shards || split) return fail(TP_ERR_ARG, "%s and %s need seq_splits > 1", shards_name, split_name);
+    return TP_OK;
+  }
+  if (M % sq->S) return fail(TP_ERR_INDIVISIBLE, "seq_splits %lld does not divide M = %lld", (long long)sq->S, (long long)M);
+  const int64_t Mr = M / R;
+  if (sq->Ms % Mr && Mr % sq->Ms)
+    return fail(TP_ERR_UNSUPPORTED, "row chunks of %lld rows and sequence blocks of %lld rows do not nest", (long long)Mr, (long long)sq->Ms);
+  if (split && full_out) return fail(TP_ERR_ARG, "%s and %s are exclusive", split_name, full_name);
+  return TP_OK;
+}
+
+// Rows [r0, r0 + rows) of the full [M, H] tensor `full`, gathered from its
+// sequence blocks of Ms rows.  The row range and the blocks nest, so it is
+// max(1, rows / Ms) equal contiguous pieces: the gather of a [rows, H] tensor
+// split along its first axis, piece k coming from block (r0 + k*seg) / Ms.
+int gather_rows(const void *const *blocks, int64_t Ms, int64_t r0, int64_t rows, int64_t H, int64_t es, void *full,
+                hipStream_t s) {
+  const int64_t seg = std::min(rows, Ms), nseg = rows / seg;
+  ShardPlan plan;
+  plan.ndim = 2;
+  plan.shape[0] = rows;
+  plan.shape[1] = H;
+  plan.extent[0] = seg;
+  plan.extent[1] = H;
+  std::vector<const void *> src(static_cast<size_t>(nseg));
+  for (int64_t k = 0; k < nseg; ++k) {
+    const int64_t g = r0 + k * seg, j = g / Ms;
+    src[k] = static_cast<const char *>(blocks[j]) + (g - j * Ms) * H * es;
+    plan.offset.push_back(k * seg);
+    plan.offset.push_back(0);
+    plan.devices.push_back({k});
+  }
+  plan.max_device = nseg - 1;
+  void *dst = static_cast<char *>(full) + r0 * H * es;
+  return shard_gather_launch(plan, src.data(), es, &dst, 1, s);
+}
+
+// Reduce rows [r0, r0 + rows) x columns [c0, c0 + cols) of the P partials
+// (row stride ld) into the full output, or into the sequence blocks of Ms rows
+// the row range covers (the reduce-scatter).
+int reduce_rows(const float *const *parts, int64_t P, int64_t r0, int64_t rows, int64_t c0, int64_t cols, int64_t ld,
+                float *full, float *const *split, int64_t Ms, hipStream_t s, int64_t max_wgs, const float *bias) {
+  std::vector<float *> dst;
+  int64_t per = rows;
+  if (!split) {
+    dst.push_back(full + r0 * ld + c0);
+  } else {
+    per = std::min(rows, Ms);
+    for (int64_t k = 0; k < rows / per; ++k) {
+      const int64_t g = r0 + k * per, j = g / Ms;
+      dst.push_back(split[j] + (g - j * Ms) * ld + c0);
+    }
+  }
+  hipEvent_t t1 = timing_begin(s);
+  const int rc = partial_reduce_launch(parts, static_cast<int>(P), rows, cols, ld, dst.data(), static_cast<int>(dst.size()),
+                                       per, ld, s, max_wgs, TP_REDUCE_OP_SUM, bias);
+  if (rc != TP_OK) return rc;
+  timing_end(t1, s, TP_KERNEL_REDUCE, 4.0 * (P + 1) * rows * cols);
+  return TP_OK;
+}
+
 }  // namespace
 
 }  // namespace tpshard
@@ -152,6 +239,37 @@ int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, i
   return shard_materialize_launch(plan, src, esize, dst, static_cast<hipStream_t>(stream));
 }
 
+int tp_shard_gather(const void *const *src, int64_t num_src, int32_t dtype, const int64_t *shape, int64_t ndim,
+                    const tp_layout *layout, void *const *out, int64_t num_out, tp_stream_t stream) {
+  clear_error();
+  const int64_t esize = dtype_size(dtype);
+  if (!esize) return fail(TP_ERR_ARG, "unknown dtype %d", dtype);
+  ShardPlan plan;
+  int rc = build_plan(shape, ndim, layout, &plan);
+  if (rc != TP_OK) return rc;
+  int64_t numel = 1, shard_elems = 1;
+  for (int i = 0; i < plan.ndim; ++i) {
+    numel *= plan.shape[i];
+    shard_elems *= plan.extent[i];
+  }
+  if (num_out < 1 || !out) return fail(TP_ERR_ARG, "need num_out >= 1 outputs");
+  if (plan.max_device >= num_src)
+    return fail(TP_ERR_ARG, "num_src = %lld but the layout names device %lld", (long long)num_src, (long long)plan.max_device);
+  if (plan.max_device >= 0 && !src) return fail(TP_ERR_ARG, "src is NULL");
+  const int64_t full_bytes = numel * esize, shard_bytes = shard_elems * esize;
+  std::vector<Buf> ins, outs;
+  for (const auto& grp : plan.devices) {
+    if (!src[grp[0]] && shard_bytes > 0) return fail(TP_ERR_ARG, "src[%lld] is NULL", (long long)grp[0]);
+    ins.push_back({src[grp[0]], shard_bytes, "a shard"});
+  }
+  for (int64_t j = 0; j < num_out; ++j) {
+    if (!out[j] && full_bytes > 0) return fail(TP_ERR_ARG, "out[%lld] is NULL", (long long)j);
+    outs.push_back({out[j], full_bytes, "an output"});
+  }
+  if ((rc = check_disjoint(ins, outs)) != TP_OK) return rc;
+  return shard_gather_launch(plan, src, esize, out, num_out, static_cast<hipStream_t>(stream));
+}
+
 int tp_partial_reduce(const float *const *partials, int64_t P, int64_t rows, int64_t cols, int64_t ld_in,
                       int32_t mode, int64_t num_splits, float *const *out, int64_t ld_out, tp_stream_t stream) {
   return tp_partial_reduce_ex(partials, P, rows, cols, ld_in, mode, num_splits, out, ld_out, TP_REDUCE_OP_SUM,
@@ -210,8 +328,12 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   if (a->M % a->row_chunks) return fail(TP_ERR_INDIVISIBLE, "row_chunks %lld does not divide M = %lld", (long long)a->row_chunks, (long long)a->M);
   if (a->H % a->col_chunks) return fail(TP_ERR_INDIVISIBLE, "col_chunks %lld does not divide H = %lld", (long long)a->col_chunks, (long long)a->H);
   if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
-  if (a->P > 1 && (!a->peer_partials || !a->Z_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out");
-  if (a->bias && !a->Z_out) return fail(TP_ERR_ARG, "a bias needs Z_out (it is added to the full sum)");
+  SeqSplit sq;
+  int rc = check_seq(a->seq_splits, a->M, a->row_chunks, a->X_shards, a->Z_split, a->Z_out, "X_shards", "Z_split", "Z_out", &sq);
+  if (rc != TP_OK) return rc;
+  const bool has_out = a->Z_out || a->Z_split;
+  if (a->P > 1 && (!a->peer_partials || !has_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out (or Z_split)");
+  if (a->bias && !has_out) return fail(TP_ERR_ARG, "a bias needs Z_out or Z_split (it is added to the full sum)");
   if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
   if (a->H_out && a->act == TP_ACT_NONE) return fail(TP_ERR_ARG, "H_out needs an activation (it would equal Y)");
   const int64_t M = a->M, H = a->H, F = a->F;
@@ -219,35 +341,64 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
       (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
     return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
   const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
-  struct Buf { const void *p; int64_t n; const char *name; };
-  std::vector<Buf> ins = {{a->X, bx, "X"}, {a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
+  const bool gather = a->X_shards != nullptr;
+  std::vector<Buf> ins = {{a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
+  std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
+  (gather ? outs : ins).push_back({a->X, bx, "X"});
+  if (gather) {
+    for (int64_t j = 0; j < sq.S; ++j) {
+      if (!a->X_shards[j]) return fail(TP_ERR_ARG, "X_shards[%lld] is NULL", (long long)j);
+      ins.push_back({a->X_shards[j], sq.Ms * H * es, "X shard"});
+    }
+  }
   for (int64_t p = 1; p < a->P; ++p) {
     if (!a->peer_partials[p - 1]) return fail(TP_ERR_ARG, "peer_partials[%lld] is NULL", (long long)(p - 1));
     ins.push_back({a->peer_partials[p - 1], bz, "peer partial"});
   }
   if (a->bias) ins.push_back({a->bias, H * 4, "bias"});
-  const bool reduce = a->P > 1 || a->bias;
-  std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
-  if (reduce && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
-  if (a->H_out) outs.push_back({a->H_out, by, "H_out"});
-  for (size_t i = 0; i < outs.size(); ++i) {
-    for (const Buf& in : ins)
-      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, in.name);
-    for (size_t j = 0; j < i; ++j)
-      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  const bool reduce = a->P > 1 || a->bias || a->Z_split;
+  if (reduce && a->Z_out && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
+  if (a->Z_split) {
+    for (int64_t j = 0; j < sq.S; ++j) {
+      if (!a->Z_split[j]) return fail(TP_ERR_ARG, "Z_split[%lld] is NULL", (long long)j);
+      outs.push_back({a->Z_split[j], sq.Ms * H * 4, "Z_split block"});
+    }
   }
+  if (a->H_out) outs.push_back({a->H_out, by, "H_out"});
+  if ((rc = check_disjoint(ins, outs)) != TP_OK) return rc;
 
   hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
   const int64_t R = a->row_chunks, C = a->col_chunks, Mr = M / R, Hc = H / C;
   // The reduce stream only pays when a later block's GEMMs can run beside an
-  // earlier block's reduce; with a single block the hand-off (an event record
-  // and a cross-queue wait, about 10 us each way on MI355X) is pure latency.
-  const bool two = (s0 != s1) && reduce && R * C > 1;
+  // earlier block's reduce or gather; with a single block the hand-off (an
+  // event record and a cross-queue wait, about 10 us each way on MI355X) is
+  // pure latency.
+  const bool two = (s0 != s1) && (reduce || gather) && R * C > 1;
   hipEvent_t *ev = nullptr;
   if (two) {
-    const int rc = get_events(static_cast<size_t>(R * C + 1), &ev);
-    if (rc != TP_OK) return rc;
+    if ((rc = get_events(static_cast<size_t>(R * C + R + 2), &ev)) != TP_OK) return rc;
   }
+  hipEvent_t *ev_red = ev, *ev_gat = two ? ev + R * C : nullptr;
+  hipEvent_t ev_fork = two ? ev[R * C + R] : nullptr, ev_join = two ? ev[R * C + R + 1] : nullptr;
+  hipError_t e;
+  // The gather stream must see what the caller enqueued on s_compute (the
+  // shards, and the end of any earlier use of X).
+  if (two && gather) {
+    if ((e = hipEventRecord(ev_fork, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s1, ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  auto gather_chunk = [&](int64_t r) -> int {
+    hipStream_t sg = two ? s1 : s0;
+    const int grc = gather_rows(a->X_shards, sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->X), sg);
+    if (grc != TP_OK) return grc;
+    if (two) {
+      hipError_t ge = hipEventRecord(ev_gat[r], s1);
+      if (ge != hipSuccess) return hip_fail(ge, "hipEventRecord");
+    }
+    return TP_OK;
+  };
+  if (gather && (rc = gather_chunk(0)) != TP_OK) return rc;
+
   const bool bf16 = a->dtype == TP_BF16;
   const bool save = a->H_out != nullptr;
   const int epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveBf16 : kEpiGeluBf16) : kEpiIdentBf16)
@@ -255,6 +406,9 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   const int epi2 = bf16 ? kEpiF32 : kEpiPlainF32;
   std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t r = 0; r < R; ++r) {
+    // The next chunk's input rows travel on s_reduce while this chunk computes.
+    if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
+    if (gather && two && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
     GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
                 static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
     if (save) {
@@ -262,7 +416,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
       g1.ldaux = F;
     }
     hipEvent_t t0 = timing_begin(s0);
-    hipError_t e = gemm_launch(g1, epi1, s0);
+    e = gemm_launch(g1, epi1, s0);
     if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
     timing_end(t0, s0, TP_KERNEL_GEMM1, 2.0 * Mr * F * H);
     for (int64_t c = 0; c < C; ++c) {
@@ -276,27 +430,21 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
       if (!reduce) continue;
       hipStream_t sr = s0;
       if (two) {
-        hipEvent_t done = ev[r * C + c];
-        if ((e = hipEventRecord(done, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        if ((e = hipStreamWaitEvent(s1, done, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        if ((e = hipEventRecord(ev_red[r * C + c], s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = hipStreamWaitEvent(s1, ev_red[r * C + c], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
         sr = s1;
       }
       parts[0] = a->Z_i + zoff;
       for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_partials[p - 1] + zoff;
-      float *dst = a->Z_out + zoff;
-      hipEvent_t t1 = timing_begin(sr);
-      const int rc = partial_reduce_launch(parts.data(), static_cast<int>(a->P), Mr, Hc, H, &dst, 1, Mr, H, sr,
-                                           two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0,
-                                           TP_REDUCE_OP_SUM, a->bias ? a->bias + c * Hc : nullptr);
+      rc = reduce_rows(parts.data(), a->P, r * Mr, Mr, c * Hc, Hc, H, a->Z_out, a->Z_split, sq.Ms, sr,
+                       two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0,
+                       a->bias ? a->bias + c * Hc : nullptr);
       if (rc != TP_OK) return rc;
-      timing_end(t1, sr, TP_KERNEL_REDUCE, 4.0 * (a->P + 1) * Mr * Hc);
     }
   }
   if (two) {
-    hipEvent_t joined = ev[R * C];
-    hipError_t e;
-    if ((e = hipEventRecord(joined, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = hipStreamWaitEvent(s0, joined, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if ((e = hipEventRecord(ev_join, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s0, ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
   return TP_OK;
 }
@@ -316,39 +464,70 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   if (a->row_chunks < 1) return fail(TP_ERR_ARG, "row_chunks must be >= 1");
   if (a->M % a->row_chunks) return fail(TP_ERR_INDIVISIBLE, "row_chunks %lld does not divide M = %lld", (long long)a->row_chunks, (long long)a->M);
   if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
-  if (a->P > 1 && (!a->peer_dX || !a->dX_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_dX and dX_out");
+  SeqSplit sq;
+  int rc = check_seq(a->seq_splits, a->M, a->row_chunks, a->dZ_shards, a->dX_split, a->dX_out, "dZ_shards", "dX_split", "dX_out", &sq);
+  if (rc != TP_OK) return rc;
+  if (a->P > 1 && (!a->peer_dX || !(a->dX_out || a->dX_split))) return fail(TP_ERR_ARG, "P > 1 needs peer_dX and dX_out (or dX_split)");
   if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
   const int64_t M = a->M, H = a->H, F = a->F;
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) || (M / a->row_chunks) * H >= (int64_t(1) << 31))
     return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
   const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
-  struct Buf { const void *p; int64_t n; const char *name; };
-  std::vector<Buf> ins = {{a->X, bx, "X"}, {a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}, {a->Y_i, by, "Y_i"}, {a->dZ, bx, "dZ"}};
+  const bool gather = a->dZ_shards != nullptr;
+  std::vector<Buf> ins = {{a->X, bx, "X"}, {a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}, {a->Y_i, by, "Y_i"}};
+  std::vector<Buf> outs = {{a->dH_ws, by, "dH_ws"}, {a->dX_i, bz, "dX_i"}, {a->dA_i, H * F * 4, "dA_i"},
+                           {a->dB_i, F * H * 4, "dB_i"}};
+  (gather ? outs : ins).push_back({a->dZ, bx, "dZ"});
+  if (gather) {
+    for (int64_t j = 0; j < sq.S; ++j) {
+      if (!a->dZ_shards[j]) return fail(TP_ERR_ARG, "dZ_shards[%lld] is NULL", (long long)j);
+      ins.push_back({a->dZ_shards[j], sq.Ms * H * es, "dZ shard"});
+    }
+  }
   if (gelu) ins.push_back({a->H_i, by, "H_i"});
   for (int64_t p = 1; p < a->P; ++p) {
     if (!a->peer_dX[p - 1]) return fail(TP_ERR_ARG, "peer_dX[%lld] is NULL", (long long)(p - 1));
     ins.push_back({a->peer_dX[p - 1], bz, "peer dX"});
   }
-  std::vector<Buf> outs = {{a->dH_ws, by, "dH_ws"}, {a->dX_i, bz, "dX_i"}, {a->dA_i, H * F * 4, "dA_i"},
-                           {a->dB_i, F * H * 4, "dB_i"}};
-  if (a->P > 1 && a->dX_out != a->dX_i) outs.push_back({a->dX_out, bz, "dX_out"});
-  for (size_t i = 0; i < outs.size(); ++i) {
-    for (const Buf& in : ins)
-      if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, in.name);
-    for (size_t j = 0; j < i; ++j)
-      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return fail(TP_ERR_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  const bool reduce = a->P > 1 || a->dX_split;
+  if (reduce && a->dX_out && a->dX_out != a->dX_i) outs.push_back({a->dX_out, bz, "dX_out"});
+  if (a->dX_split) {
+    for (int64_t j = 0; j < sq.S; ++j) {
+      if (!a->dX_split[j]) return fail(TP_ERR_ARG, "dX_split[%lld] is NULL", (long long)j);
+      outs.push_back({a->dX_split[j], sq.Ms * H * 4, "dX_split block"});
+    }
   }
+  if ((rc = check_disjoint(ins, outs)) != TP_OK) return rc;
 
   hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
   const int64_t R = a->row_chunks, Mr = M / R;
-  // As in the forward: a second stream only pays when a chunk's reduce can run
-  // beside GEMMs, which here are that chunk's weight-gradient GEMMs.
-  const bool two = (s0 != s1) && a->P > 1;
+  // As in the forward: a second stream only pays when its work can run beside
+  // GEMMs: a chunk's reduce beside that chunk's weight-gradient GEMMs, the
+  // next chunk's gather beside this chunk's GEMMs.
+  const bool two = (s0 != s1) && (reduce || (gather && R > 1));
   hipEvent_t *ev = nullptr;
   if (two) {
-    const int rc = get_events(static_cast<size_t>(R + 1), &ev);
-    if (rc != TP_OK) return rc;
+    if ((rc = get_events(static_cast<size_t>(2 * R + 2), &ev)) != TP_OK) return rc;
   }
+  hipEvent_t *ev_red = ev, *ev_gat = two ? ev + R : nullptr;
+  hipEvent_t ev_fork = two ? ev[2 * R] : nullptr, ev_join = two ? ev[2 * R + 1] : nullptr;
+  hipError_t e;
+  if (two && gather) {
+    if ((e = hipEventRecord(ev_fork, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s1, ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  auto gather_chunk = [&](int64_t r) -> int {
+    hipStream_t sg = two ? s1 : s0;
+    const int grc = gather_rows(a->dZ_shards, sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->dZ), sg);
+    if (grc != TP_OK) return grc;
+    if (two) {
+      hipError_t ge = hipEventRecord(ev_gat[r], s1);
+      if (ge != hipSuccess) return hip_fail(ge, "hipEventRecord");
+    }
+    return TP_OK;
+  };
+  if (gather && (rc = gather_chunk(0)) != TP_OK) return rc;
+
   const bool bf16 = a->dtype == TP_BF16;
   const int epi_dh = bf16 ? (gelu ? kEpiDGeluBf16 : kEpiIdentBf16) : (gelu ? kEpiDGeluF32 : kEpiPlainF32);
   const int epi_f32 = bf16 ? kEpiF32 : kEpiPlainF32;
@@ -357,6 +536,8 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   char *dH = static_cast<char *>(a->dH_ws);
   std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t r = 0; r < R; ++r) {
+    if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
+    if (gather && two && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
     // dH[r] = (dZ[r] B_i^T) * act'(H_i[r]): B_i is [F][H], i.e. W^T for W = B_i^T.
     GemmArgs gd{dZ + r * Mr * H * es, a->B_i, dH + r * Mr * F * es, Mr, F, H, H, H, F};
     gd.w_t = 1;
@@ -365,7 +546,7 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
       gd.ldaux = F;
     }
     hipEvent_t t0 = timing_begin(s0);
-    hipError_t e = gemm_launch(gd, epi_dh, s0);
+    e = gemm_launch(gd, epi_dh, s0);
     if (e != hipSuccess) return hip_fail(e, "dH GEMM launch");
     timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD, 2.0 * Mr * F * H);
     // dX_i[r] = dH[r] A_i^T: A_i is [H][F], i.e. W^T for W = A_i^T.
@@ -375,22 +556,18 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
     e = gemm_launch(gx, epi_f32, s0);
     if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
     timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD, 2.0 * Mr * H * F);
-    if (a->P > 1) {
+    if (reduce) {
       hipStream_t sr = s0;
       if (two) {
-        hipEvent_t done = ev[r];
-        if ((e = hipEventRecord(done, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        if ((e = hipStreamWaitEvent(s1, done, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        if ((e = hipEventRecord(ev_red[r], s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = hipStreamWaitEvent(s1, ev_red[r], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
         sr = s1;
       }
       parts[0] = a->dX_i + r * Mr * H;
       for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_dX[p - 1] + r * Mr * H;
-      float *dst = a->dX_out + r * Mr * H;
-      hipEvent_t t1 = timing_begin(sr);
-      const int rc = partial_reduce_launch(parts.data(), static_cast<int>(a->P), Mr, H, H, &dst, 1, Mr, H, sr,
-                                           two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0);
+      rc = reduce_rows(parts.data(), a->P, r * Mr, Mr, 0, H, H, a->dX_out, a->dX_split, sq.Ms, sr,
+                       two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0, nullptr);
       if (rc != TP_OK) return rc;
-      timing_end(t1, sr, TP_KERNEL_REDUCE, 4.0 * (a->P + 1) * Mr * H);
     }
     // Weight gradients, contracting over this chunk's rows and continuing the
     // previous chunk's accumulation: dA_i += X[r]^T dH[r], dB_i += Y_i[r]^T dZ[r].
@@ -411,10 +588,8 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
     timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * F * H * Mr);
   }
   if (two) {
-    hipEvent_t joined = ev[R];
-    hipError_t e;
-    if ((e = hipEventRecord(joined, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = hipStreamWaitEvent(s0, joined, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if ((e = hipEventRecord(ev_join, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s0, ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
   return TP_OK;
 }

@@ -14,6 +14,12 @@ namespace tpshard {
 int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esize, void *const *dst,
                              hipStream_t stream);
 
+// Writes the full tensor of `plan` into each of out[0..nout) from the shards:
+// shard k is read from src[first device of its group].  Arguments already
+// validated.  Returns TP_OK or a negative status.
+int shard_gather_launch(const ShardPlan& plan, const void *const *src, int64_t esize, void *const *out, int64_t nout,
+                        hipStream_t stream);
+
 // out_row_block(row) <- op over p of partials[p][row, :] (+ bias[:]), ascending
 // p, fp32; op 0 sum, 1 max, 2 min.  rows_per_out rows go to each out[j]; out[j]
 // has row stride ld_out.  Arguments already validated (1 <= P <= 64,

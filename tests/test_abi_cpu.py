@@ -42,6 +42,11 @@ def test_header_symbols_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert tp.version().startswith("tpshard")
+    # Every entry point has its prototype declared on the binding side, so
+    # 64-bit sizes and pointers are never passed as C ints.
+    for n in names:
+        assert getattr(lib, n).argtypes is not None, n
+        assert getattr(lib, n).restype is not None, n
 
 
 def _oracle_plan(shape, spec):
@@ -285,3 +290,55 @@ def test_mlp_bias_needs_z_out():
     # bias overlapping Z_out
     a = _mlp_args(bias=FAKE + (9 << 20) + 4, Z_out=FAKE + (9 << 20))
     assert lib.tp_colrow_mlp(C.byref(a), None, None) == _abi.TP_ERR_ARG
+
+
+def _ptrs(xs):
+    return C.cast((C.c_void_p * max(1, len(xs)))(*xs), C.POINTER(C.c_void_p))
+
+
+def test_gather_validation():
+    lib = _abi.load()
+    spec = {"device": [-1, -2], "device_map": {-1: [0, 1], -2: [2, 3]}, "sharded_dim": [{"axis": 0, "num_shards": 2}]}
+    lay, keep = _abi.make_layout(spec)
+    sp = C.cast((C.c_int64 * 2)(4, 4), C.POINTER(C.c_int64))
+    src_ok = [FAKE + (1 << 20), None, FAKE + (2 << 20), None]    # replicas 1 and 3 are not read
+    out_ok = [FAKE + (10 << 20), FAKE + (11 << 20)]
+
+    def g(src=src_ok, nsrc=4, dtype=0, out=out_ok, nout=None, shape=sp):
+        return lib.tp_shard_gather(_ptrs(src), nsrc, dtype, shape, 2, C.byref(lay), _ptrs(out),
+                                   len(out) if nout is None else nout, None)
+    assert g(dtype=9) == _abi.TP_ERR_ARG
+    assert g(nsrc=3) == _abi.TP_ERR_ARG                       # the layout names device 3
+    assert g(src=[None, FAKE, FAKE + (2 << 20), None]) == _abi.TP_ERR_ARG   # device 0 is read
+    assert g(nout=0) == _abi.TP_ERR_ARG
+    assert g(out=[FAKE + (10 << 20), None]) == _abi.TP_ERR_ARG
+    assert g(out=[FAKE + (10 << 20), FAKE + (10 << 20) + 32]) == _abi.TP_ERR_ARG   # outputs overlap
+    assert g(out=[FAKE + (1 << 20) + 8]) == _abi.TP_ERR_ARG                        # output overlaps a shard
+    assert g(shape=C.cast((C.c_int64 * 2)(3, 4), C.POINTER(C.c_int64))) == _abi.TP_ERR_INDIVISIBLE
+
+
+def test_sequence_parallel_validation():
+    lib = _abi.load()
+    xs = [FAKE + (40 << 20) + j * (1 << 20) for j in range(4)]
+    zs = [FAKE + (50 << 20) + j * (1 << 20) for j in range(4)]
+
+    def fwd(**kw):
+        return lib.tp_colrow_mlp(C.byref(_mlp_args(**kw)), None, None)
+    assert fwd(X_shards=_ptrs(xs)) == _abi.TP_ERR_ARG                          # S not set
+    assert fwd(seq_splits=65, X_shards=_ptrs(xs)) == _abi.TP_ERR_ARG
+    assert fwd(seq_splits=-1) == _abi.TP_ERR_ARG
+    assert fwd(seq_splits=3, X_shards=_ptrs(xs)) == _abi.TP_ERR_INDIVISIBLE     # 3 does not divide 64
+    assert fwd(seq_splits=4, row_chunks=1, M=64, Z_split=_ptrs(zs), Z_out=FAKE + (60 << 20)) == _abi.TP_ERR_ARG
+    assert fwd(seq_splits=4, X_shards=_ptrs([xs[0], None, xs[2], xs[3]])) == _abi.TP_ERR_ARG
+    assert fwd(seq_splits=4, X_shards=_ptrs([xs[0], xs[1], FAKE + 8, xs[3]])) == _abi.TP_ERR_ARG   # shard inside X (written)
+    assert fwd(seq_splits=4, Z_split=_ptrs([zs[0], zs[0] + 64, zs[2], zs[3]])) == _abi.TP_ERR_ARG   # blocks overlap
+    # 24 rows: chunks of 8 (R = 3) and sequence blocks of 6 (S = 4) do not nest
+    assert fwd(M=24, seq_splits=4, row_chunks=3, X_shards=_ptrs(xs)) == _abi.TP_ERR_UNSUPPORTED
+
+    def bwd(**kw):
+        return lib.tp_colrow_mlp_backward(C.byref(_bwd_args(**kw)), None, None)
+    assert bwd(dX_split=_ptrs(zs)) == _abi.TP_ERR_ARG
+    assert bwd(seq_splits=3, dZ_shards=_ptrs(xs)) == _abi.TP_ERR_INDIVISIBLE
+    assert bwd(seq_splits=4, dX_split=_ptrs(zs), dX_out=FAKE + (60 << 20)) == _abi.TP_ERR_ARG
+    assert bwd(seq_splits=4, dZ_shards=_ptrs([xs[0], FAKE + (5 << 20) + 8, xs[2], xs[3]])) == _abi.TP_ERR_ARG  # in dZ
+    assert bwd(M=24, seq_splits=4, row_chunks=3, dZ_shards=_ptrs(xs)) == _abi.TP_ERR_UNSUPPORTED

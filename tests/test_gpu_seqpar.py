@@ -1,0 +1,202 @@
+"""GPU parity of the sequence-parallel MLP (ColossalAI section 5.3: the column
+layer all-gathers its input along the sequence axis and the row layer
+reduce-scatters its output; in the backward the output gradient is
+all-gathered and the input gradient reduce-scattered) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import sharded_gemm_amd as tp
+from sharded_gemm_amd import inputs
+from oracle import mlp as O
+from oracle import reduce as R
+
+from gpu_helpers import Guarded, announce, bits, rel_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+
+
+def setup_module(_):
+    require_gpu()
+
+
+def _one_hot(H, F, seed):
+    g = torch.Generator().manual_seed(seed)
+    rows = torch.randint(0, H, (F,), generator=g)
+    vals = torch.randint(1, 5, (F,), generator=g) * (torch.randint(0, 2, (F,), generator=g) * 2 - 1)
+    A = torch.zeros((H, F))
+    A[rows, torch.arange(F)] = vals.float()
+    return A.to(torch.bfloat16)
+
+
+def _f64(t):
+    return t.double().numpy()
+
+
+def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bias=None, two_streams=True):
+    """tp_colrow_mlp with X_shards and Z_split into guarded buffers; returns CPU
+    copies (X gathered, Y, Z_i, [Z blocks])."""
+    S = len(X_blocks)
+    Ms, H = X_blocks[0].shape
+    M, F = Ms * S, A.shape[1]
+    Xw = Guarded((M, H), X_blocks[0].dtype)
+    Y = Guarded((M, F), X_blocks[0].dtype)
+    Z = Guarded((M, H), torch.float32)
+    Zs = [Guarded((Ms, H), torch.float32) for _ in range(S)]
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream() if two_streams else s0
+    tp.tp_colrow_mlp(Xw.t, A, B, Y.t, Z.t, row_chunks=Rc, col_chunks=Cc, peer_partials=list(peers), act=act,
+                     s_compute=s0, s_reduce=s1, bias=bias, X_shards=list(X_blocks), Z_split=[g.t for g in Zs])
+    torch.cuda.synchronize()
+    for g in [Xw, Y, Z] + Zs:
+        assert g.guards_intact(), "write outside an output buffer"
+    return Xw.t.cpu(), Y.t.cpu(), Z.t.cpu(), [g.t.cpu() for g in Zs]
+
+
+@pytest.mark.parametrize("M,H,F,Rc,Cc,P,S", [
+    (512, 384, 256, 2, 3, 4, 4),      # a row chunk spans two sequence blocks
+    (1024, 256, 128, 4, 1, 2, 2),     # a sequence block holds two row chunks
+    (96, 72, 40, 3, 2, 3, 3),         # chunks and blocks coincide
+    (1030, 640, 320, 2, 5, 5, 2),     # ragged tiles
+    (256, 128, 64, 1, 1, 2, 4),       # one block: serial schedule
+    (4096, 768, 768, 2, 1, 4, 4),     # GPT-2-small shape
+])
+def test_forward_integer_exact(M, H, F, Rc, Cc, P, S):
+    """Integer chain: the gathered X equals the concatenated blocks, Z_i the
+    oracle's partial and block j the oracle's rows j of the full sum."""
+    announce(f"seqpar forward integer exact M={M} H={H} F={F} R={Rc} C={Cc} P={P} S={S}")
+    Ms = M // S
+    Xb = [inputs.small_ints((Ms, H), seed=600 + j, lo=-4, hi=4, dtype="bf16") for j in range(S)]
+    A = _one_hot(H, F, 650)
+    B = inputs.small_ints((F, H), seed=651, lo=-4, hi=4, dtype="bf16")
+    peers = [inputs.small_ints((M, H), seed=660 + p, lo=-512, hi=512) for p in range(P - 1)]
+    bias = inputs.small_ints((H,), seed=659, lo=-64, hi=64)
+    Xg, Y, Z, Zs = sp_forward([x.cuda() for x in Xb], A.cuda(), B.cuda(), [p.cuda() for p in peers], Rc=Rc, Cc=Cc,
+                              act=tp.TP_ACT_NONE, bias=bias.cuda())
+    X = torch.cat(Xb)
+    assert np.array_equal(bits(Xg), bits(X))
+    z_ref = O.mlp_rank(X, A, B, O.GELU_NONE)
+    assert np.array_equal(_f64(Z), z_ref)
+    ref = R.reduce_split([z_ref] + [_f64(p) for p in peers], S, "sum", _f64(bias))
+    for j in range(S):
+        assert np.array_equal(_f64(Zs[j]), ref[j]), j
+
+
+def test_forward_gelu_matches_unsplit_path_bitwise():
+    """GeLU on random bf16 inputs: the sequence-parallel call gives the same bits
+    as gathering X by hand and running the all-reduce form, and the blocks are
+    within tolerance of the oracle."""
+    announce("seqpar forward gelu vs unsplit path")
+    M, H, F, P, S, Rc = 2048, 768, 768, 4, 4, 2
+    Xb = [inputs.normal((M // S, H), seed=700 + j, dtype="bf16") for j in range(S)]
+    A = inputs.normal((H, F), seed=710, std=0.02, dtype="bf16")
+    B = inputs.normal((F, H), seed=711, std=0.02, dtype="bf16")
+    peers = [inputs.normal((M, H), seed=720 + p) for p in range(P - 1)]
+    Xg, Y, Z, Zs = sp_forward([x.cuda() for x in Xb], A.cuda(), B.cuda(), [p.cuda() for p in peers], Rc=Rc)
+    X = torch.cat(Xb).cuda()
+    Y2 = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z2 = torch.empty((M, H), device="cuda")
+    Zo = torch.empty((M, H), device="cuda")
+    tp.tp_colrow_mlp(X, A.cuda(), B.cuda(), Y2, Z2, row_chunks=Rc, peer_partials=[p.cuda() for p in peers], Z_out=Zo,
+                     s_reduce=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(Y), bits(Y2.cpu()))
+    assert np.array_equal(bits(Z), bits(Z2.cpu()))
+    full = torch.cat(Zs)
+    assert np.array_equal(bits(full), bits(Zo.cpu()))
+    rows = np.arange(0, M, 37)
+    ref = O.mlp_rank_rows(torch.cat(Xb), A, B, rows) + sum(_f64(p)[rows] for p in peers)
+    assert rel_err(full[torch.from_numpy(rows)], ref) <= TOL_BF16
+
+
+def sp_backward(X, A, B, Y, dZ_blocks, peers, *, Rc=1, act=tp.TP_ACT_NONE, H_i=None, two_streams=True):
+    S = len(dZ_blocks)
+    Ms, H = dZ_blocks[0].shape
+    M, F = Ms * S, A.shape[1]
+    dZw = Guarded((M, H), X.dtype)
+    dH = Guarded((M, F), X.dtype)
+    dX = Guarded((M, H), torch.float32)
+    dA = Guarded((H, F), torch.float32)
+    dB = Guarded((F, H), torch.float32)
+    dXs = [Guarded((Ms, H), torch.float32) for _ in range(S)]
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream() if two_streams else s0
+    tp.tp_colrow_mlp_backward(X, A, B, H_i, Y, dZw.t, dH.t, dX.t, dA.t, dB.t, row_chunks=Rc, peer_dX=list(peers),
+                              act=act, s_compute=s0, s_reduce=s1, dZ_shards=list(dZ_blocks),
+                              dX_split=[g.t for g in dXs])
+    torch.cuda.synchronize()
+    for g in [dZw, dH, dX, dA, dB] + dXs:
+        assert g.guards_intact(), "write outside an output buffer"
+    return dZw.t.cpu(), dX.t.cpu(), dA.t.cpu(), dB.t.cpu(), [g.t.cpu() for g in dXs]
+
+
+@pytest.mark.parametrize("M,H,F,Rc,P,S", [
+    (512, 384, 256, 2, 4, 4), (1024, 256, 128, 4, 2, 2), (300, 264, 136, 3, 3, 3), (256, 128, 64, 1, 1, 4),
+    (4096, 768, 768, 2, 4, 8),
+])
+def test_backward_integer_exact(M, H, F, Rc, P, S):
+    """Integer chain through the backward: dZ gathered from its blocks, the
+    weight gradients and the reduce-scattered input gradient exact."""
+    announce(f"seqpar backward integer exact M={M} H={H} F={F} R={Rc} P={P} S={S}")
+    Ms = M // S
+    X = inputs.small_ints((M, H), seed=801, lo=-4, hi=4, dtype="bf16")
+    A = _one_hot(H, F, 802)
+    B = _one_hot(H, F, 803).t().contiguous()
+    dZb = [inputs.small_ints((Ms, H), seed=810 + j, lo=-4, hi=4, dtype="bf16") for j in range(S)]
+    peers = [inputs.small_ints((M, H), seed=830 + p, lo=-512, hi=512) for p in range(P - 1)]
+    Xd, Ad, Bd = X.cuda(), A.cuda(), B.cuda()
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    tp.tp_colrow_mlp(Xd, Ad, Bd, Y, Z, act=tp.TP_ACT_NONE)
+    dZg, dX, dA, dB, dXs = sp_backward(Xd, Ad, Bd, Y, [d.cuda() for d in dZb], [p.cuda() for p in peers], Rc=Rc)
+    dZ = torch.cat(dZb)
+    assert np.array_equal(bits(dZg), bits(dZ))
+    g = O.backward_rank(X, A, B, dZ, O.GELU_NONE)
+    assert np.array_equal(_f64(dX), g["dX_i"])
+    assert np.array_equal(_f64(dA), g["dA_i"])
+    assert np.array_equal(_f64(dB), g["dB_i"])
+    ref = R.reduce_split([g["dX_i"]] + [_f64(p) for p in peers], S)
+    for j in range(S):
+        assert np.array_equal(_f64(dXs[j]), ref[j]), j
+
+
+def test_backward_gelu_tolerance():
+    announce("seqpar backward gelu tolerance")
+    M, H, F, P, S, Rc = 1024, 512, 384, 2, 4, 2
+    X = inputs.normal((M, H), seed=851, dtype="bf16")
+    A = inputs.normal((H, F), seed=852, std=0.05, dtype="bf16")
+    B = inputs.normal((F, H), seed=853, std=0.05, dtype="bf16")
+    dZb = [inputs.normal((M // S, H), seed=860 + j, dtype="bf16") for j in range(S)]
+    peers = [inputs.normal((M, H), seed=870)]
+    Xd, Ad, Bd = X.cuda(), A.cuda(), B.cuda()
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    Hs = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    tp.tp_colrow_mlp(Xd, Ad, Bd, Y, Z, H_out=Hs)
+    dZg, dX, dA, dB, dXs = sp_backward(Xd, Ad, Bd, Y, [d.cuda() for d in dZb], [p.cuda() for p in peers], Rc=Rc,
+                                       act=tp.TP_ACT_GELU_ERF, H_i=Hs)
+    g = O.backward_rank(X, A, B, torch.cat(dZb), O.GELU_ERF)
+    assert rel_err(dA, g["dA_i"]) <= TOL_BF16
+    assert rel_err(dB, g["dB_i"]) <= TOL_BF16
+    assert rel_err(torch.cat(dXs), g["dX_i"] + _f64(peers[0])) <= TOL_BF16
+
+
+def test_error_leaves_outputs_untouched():
+    """Chunks of 8 rows and blocks of 6 do not nest: rejected before any launch."""
+    announce("seqpar error path")
+    M, H, F, S = 24, 16, 16, 4
+    Xb = [torch.zeros((M // S, H), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    A = torch.zeros((H, F), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((F, H), dtype=torch.bfloat16, device="cuda")
+    Xw = Guarded((M, H), torch.bfloat16)
+    Y = Guarded((M, F), torch.bfloat16)
+    Z = Guarded((M, H), torch.float32)
+    Zs = [Guarded((M // S, H), torch.float32) for _ in range(S)]
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_colrow_mlp(Xw.t, A, B, Y.t, Z.t, row_chunks=3, X_shards=Xb, Z_split=[g.t for g in Zs])
+    assert e.value.kind == "unsupported"
+    torch.cuda.synchronize()
+    for g in [Xw, Y, Z] + Zs:
+        assert g.body_untouched() and g.guards_intact()

@@ -52,13 +52,17 @@ def log(msg):
 # --------------------------------------------------------------------------- workloads
 
 class MlpStep:
-    """Per-rank MLP step, optionally preceded by cutting the weights."""
+    """Per-rank MLP step, optionally preceded by cutting the weights.  With
+    ``seq`` the step is the sequence-parallel form: the input arrives as P
+    sequence blocks that the call all-gathers, and the output is
+    reduce-scattered into P blocks."""
 
     serial = False
     reduce_wgs = 0
 
-    def __init__(self, w, split_weights: bool):
+    def __init__(self, w, split_weights: bool, seq: bool = False):
         self.w = w
+        self.seq = seq
         dev = "cuda"
         dt = "bf16" if w.dtype == "bf16" else "f32"
         tdt = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -88,21 +92,26 @@ class MlpStep:
             z = torch.empty((w.M, w.H), device=dev)
             tp.tp_colrow_mlp(self.X, self.As[i], self.Bs[i], self.Y, z, row_chunks=w.R, col_chunks=w.C)
             self.peers.append(z)
+        if seq:
+            # every rank's sequence block as its own buffer; X becomes the gather workspace
+            self.Xb = [b.clone() for b in torch.chunk(self.X, w.P)]
+            self.Zs = [torch.empty((w.M // w.P, w.H), device=dev) for _ in range(w.P)]
         torch.cuda.synchronize()
         self.s0 = torch.cuda.Stream()     # a side stream: graph capture needs one
         self.s1 = torch.cuda.Stream()
 
     def result(self):
-        return self.Zo
+        return self.Zs[-1] if self.seq else self.Zo
 
     def step(self):
         if self.split:
             tp.tp_shard_materialize(self.A, self.sa, self.As, stream=self.s0)
             tp.tp_shard_materialize(self.B, self.sb, self.Bs, stream=self.s0)
         tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
-                         col_chunks=self.w.C, peer_partials=self.peers, Z_out=self.Zo,
+                         col_chunks=self.w.C, peer_partials=self.peers, Z_out=None if self.seq else self.Zo,
                          s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
-                         reduce_workgroups=self.reduce_wgs)
+                         reduce_workgroups=self.reduce_wgs, X_shards=self.Xb if self.seq else None,
+                         Z_split=self.Zs if self.seq else None)
 
     @property
     def work(self):
@@ -112,10 +121,14 @@ class MlpStep:
 
     def config(self):
         w = self.w
-        return {"workload": w.name, "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F, "tp": w.P,
-                "row_chunks": w.R, "col_chunks": w.C, "weights_cut_each_step": self.split,
-                "reduce_stream": "compute" if self.serial else "second",
-                "peers": "virtual ranks 1..P-1, partials precomputed by the same path"}
+        cfg = {"workload": w.name + ("-sp" if self.seq else ""), "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F,
+               "tp": w.P, "row_chunks": w.R, "col_chunks": w.C, "weights_cut_each_step": self.split,
+               "reduce_stream": "compute" if self.serial else "second",
+               "peers": "virtual ranks 1..P-1, partials precomputed by the same path"}
+        if self.seq:
+            cfg["sequence_parallel"] = {"blocks": w.P, "input": "all-gathered from P sequence blocks",
+                                        "output": "reduce-scattered into P sequence blocks"}
+        return cfg
 
     def cpu_baseline(self, budget_s):
         """The oracle on this step (sampled rows for the large shapes), fp64."""
@@ -131,13 +144,20 @@ class MlpStep:
         peers = [inputs.normal((rows, w.H), 99000 + p) for p in range(w.P - 1)]
         Ac = self.A.cpu() if self.split else None
         Bc = self.B.cpu() if self.split else None
+        gspec = {"device": list(range(w.P)), "sharded_dim": [{"axis": 0, "num_shards": w.P}]}
+        xblocks = dict(enumerate(np.split(Xc[sample_rows].float().numpy(), w.P))) if self.seq else None
         reps, t0 = 0, time.perf_counter()
         while True:
             if self.split:
                 L.split(Ac, self.sa)
                 L.split(Bc, self.sb)
+            if self.seq:
+                L.gather(xblocks, (rows, w.H), gspec)
             z = O.mlp_rank_rows(Xc, A0, B0, sample_rows)
-            R.reduce_full([z] + peers)
+            if self.seq:
+                R.reduce_split([z] + peers, w.P)
+            else:
+                R.reduce_full([z] + peers)
             reps += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -147,6 +167,7 @@ class MlpStep:
         return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                 "sample": (f"{rows} of {w.M} token rows of the per-rank MLP (fp64, numpy BLAS), "
                            f"{'plus cutting the full weights into shards, ' if self.split else ''}"
+                           f"{'plus the all-gather of those rows from P blocks, ' if self.seq else ''}"
                            f"plus the {w.P}-way partial sum of those rows; {reps} repetitions, "
                            f"{dt * 1e3:.1f} ms each; host {platform.processor() or platform.machine()}, "
                            f"os.cpu_count()={os.cpu_count()}")}
@@ -159,8 +180,9 @@ class BwdStep:
     serial = False
     reduce_wgs = 0
 
-    def __init__(self, w):
+    def __init__(self, w, seq: bool = False):
         self.w = w
+        self.seq = seq
         dev = "cuda"
         dt = "bf16" if w.dtype == "bf16" else "f32"
         tdt = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -188,6 +210,10 @@ class BwdStep:
                                       self.dA, self.dB, row_chunks=w.R)
             self.peers.append(dx)
         tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, z, row_chunks=w.R, H_out=self.Hs)
+        if seq:
+            # dZ arrives as P sequence blocks (dZ becomes the gather workspace); dX leaves as P blocks
+            self.dZb = [b.clone() for b in torch.chunk(self.dZ, w.P)]
+            self.dXs = [torch.empty((w.M // w.P, w.H), device=dev) for _ in range(w.P)]
         torch.cuda.synchronize()
         self.s0 = torch.cuda.Stream()
         self.s1 = torch.cuda.Stream()
@@ -197,9 +223,11 @@ class BwdStep:
 
     def step(self):
         tp.tp_colrow_mlp_backward(self.X, self.As[0], self.Bs[0], self.Hs, self.Y, self.dZ, self.dH, self.dX,
-                                  self.dA, self.dB, row_chunks=self.w.R, peer_dX=self.peers, dX_out=self.dXo,
+                                  self.dA, self.dB, row_chunks=self.w.R, peer_dX=self.peers,
+                                  dX_out=None if self.seq else self.dXo,
                                   s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
-                                  reduce_workgroups=self.reduce_wgs)
+                                  reduce_workgroups=self.reduce_wgs, dZ_shards=self.dZb if self.seq else None,
+                                  dX_split=self.dXs if self.seq else None)
 
     @property
     def work(self):
@@ -209,9 +237,14 @@ class BwdStep:
 
     def config(self):
         w = self.w
-        return {"workload": w.name + "-bwd", "pass": "backward", "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F,
-                "tp": w.P, "row_chunks": w.R, "reduce_stream": "compute" if self.serial else "second",
-                "peers": "virtual ranks 1..P-1, input-gradient partials precomputed by the same path"}
+        cfg = {"workload": w.name + ("-sp" if self.seq else "") + "-bwd", "pass": "backward", "tokens": w.M,
+               "hidden": w.H, "ffn_per_rank": w.F, "tp": w.P, "row_chunks": w.R,
+               "reduce_stream": "compute" if self.serial else "second",
+               "peers": "virtual ranks 1..P-1, input-gradient partials precomputed by the same path"}
+        if self.seq:
+            cfg["sequence_parallel"] = {"blocks": w.P, "output_gradient": "all-gathered from P sequence blocks",
+                                        "input_gradient": "reduce-scattered into P sequence blocks"}
+        return cfg
 
     def cpu_baseline(self, budget_s):
         """The oracle's backward on a row sample (dH, dX of those rows and their
@@ -311,6 +344,11 @@ WORKLOADS = {
     GPT2_SMALL.name + "-bwd": lambda: BwdStep(GPT2_SMALL),
     GPT3_6P7B.name + "-bwd": lambda: BwdStep(GPT3_6P7B),
     GPT3_175B.name + "-bwd": lambda: BwdStep(GPT3_175B),
+    GPT2_SMALL.name + "-sp": lambda: MlpStep(GPT2_SMALL, split_weights=True, seq=True),
+    GPT3_6P7B.name + "-sp": lambda: MlpStep(GPT3_6P7B, split_weights=False, seq=True),
+    GPT3_175B.name + "-sp": lambda: MlpStep(GPT3_175B, split_weights=False, seq=True),
+    GPT3_6P7B.name + "-sp-bwd": lambda: BwdStep(GPT3_6P7B, seq=True),
+    GPT3_175B.name + "-sp-bwd": lambda: BwdStep(GPT3_175B, seq=True),
 }
 
 

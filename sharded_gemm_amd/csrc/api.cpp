@@ -381,23 +381,26 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   hipEvent_t *ev_red = ev, *ev_gat = two ? ev + R * C : nullptr;
   hipEvent_t ev_fork = two ? ev[R * C + R] : nullptr, ev_join = two ? ev[R * C + R + 1] : nullptr;
   hipError_t e;
-  // The gather stream must see what the caller enqueued on s_compute (the
-  // shards, and the end of any earlier use of X).
-  if (two && gather) {
-    if ((e = hipEventRecord(ev_fork, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = hipStreamWaitEvent(s1, ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-  }
+  // Chunk 0's rows are needed before anything can compute, so they are
+  // gathered on s_compute itself; later chunks travel on s_reduce beside the
+  // GEMMs, after chunk 0's gather (the two would only split the bandwidth)
+  // and after whatever the caller enqueued on s_compute (the shards, and the
+  // end of any earlier use of X).
   auto gather_chunk = [&](int64_t r) -> int {
-    hipStream_t sg = two ? s1 : s0;
-    const int grc = gather_rows(a->X_shards, sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->X), sg);
+    const bool side = two && r > 0;
+    const int grc = gather_rows(a->X_shards, sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->X), side ? s1 : s0);
     if (grc != TP_OK) return grc;
-    if (two) {
+    if (side) {
       hipError_t ge = hipEventRecord(ev_gat[r], s1);
       if (ge != hipSuccess) return hip_fail(ge, "hipEventRecord");
     }
     return TP_OK;
   };
   if (gather && (rc = gather_chunk(0)) != TP_OK) return rc;
+  if (two && gather && R > 1) {
+    if ((e = hipEventRecord(ev_fork, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s1, ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
 
   const bool bf16 = a->dtype == TP_BF16;
   const bool save = a->H_out != nullptr;
@@ -408,7 +411,8 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   for (int64_t r = 0; r < R; ++r) {
     // The next chunk's input rows travel on s_reduce while this chunk computes.
     if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
-    if (gather && two && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if (gather && two && r > 0 && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
     GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
                 static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
     if (save) {
@@ -512,15 +516,15 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   hipEvent_t *ev_red = ev, *ev_gat = two ? ev + R : nullptr;
   hipEvent_t ev_fork = two ? ev[2 * R] : nullptr, ev_join = two ? ev[2 * R + 1] : nullptr;
   hipError_t e;
-  if (two && gather) {
+  if (two && gather && R > 1) {
     if ((e = hipEventRecord(ev_fork, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(s1, ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
   auto gather_chunk = [&](int64_t r) -> int {
-    hipStream_t sg = two ? s1 : s0;
-    const int grc = gather_rows(a->dZ_shards, sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->dZ), sg);
+    const bool side = two && r > 0;
+    const int grc = gather_rows(a->dZ_shards, sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->dZ), side ? s1 : s0);
     if (grc != TP_OK) return grc;
-    if (two) {
+    if (side) {
       hipError_t ge = hipEventRecord(ev_gat[r], s1);
       if (ge != hipSuccess) return hip_fail(ge, "hipEventRecord");
     }
@@ -537,7 +541,8 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t r = 0; r < R; ++r) {
     if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
-    if (gather && two && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if (gather && two && r > 0 && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
     // dH[r] = (dZ[r] B_i^T) * act'(H_i[r]): B_i is [F][H], i.e. W^T for W = B_i^T.
     GemmArgs gd{dZ + r * Mr * H * es, a->B_i, dH + r * Mr * F * es, Mr, F, H, H, H, F};
     gd.w_t = 1;

@@ -18,7 +18,7 @@ from oracle import reduce as R
 def _fails(fn, *args):
     try:
         fn(*args)
-    except (AssertionError, ValueError, IndexError):
+    except (AssertionError, ValueError, IndexError, pytest.fail.Exception):
         return True
     return False
 
@@ -229,3 +229,35 @@ def test_gather_dims_mapping_later_replica_overwrites(monkeypatch):
         return out
     monkeypatch.setattr(L, "gather_dims_mapping", bad)
     assert _fails(TG.test_replica_taken_from_first_listed_device)
+
+
+def test_checker_union_instead_of_intersection(monkeypatch):
+    import test_oracle_checker as TK
+    from oracle import checker as K
+    real = K.broadcast_binary
+
+    def bad(shape1, spec1, shape2, spec2):
+        out_shape, shards = real(shape1, spec1, shape2, spec2)
+        every = sorted({d for _, devs in shards for d in devs})
+        return out_shape, [(box, every) for box, _ in shards]
+    monkeypatch.setattr(K, "broadcast_binary", bad)
+    assert _fails(TK.test_page_composition_example)
+
+
+def test_checker_merge_ignores_conflict(monkeypatch):
+    import test_oracle_checker as TK
+    from oracle import checker as K
+
+    def bad(x_map, y_map, mesh_ndim):
+        k = x_map[-1] if x_map[-1] >= 0 else y_map[-2]
+        return list(x_map[:-1]) + [y_map[-1]], ([k] if k >= 0 else [])
+    monkeypatch.setattr(K, "matmul_dims_mapping", bad)
+    assert _fails(TK.test_matmul_rejections, [0, 1], [0, -1], "spec")
+
+
+def test_checker_drops_partial(monkeypatch):
+    import test_oracle_checker as TK
+    from oracle import checker as K
+    real = K.matmul_dims_mapping
+    monkeypatch.setattr(K, "matmul_dims_mapping", lambda x, y, q: (real(x, y, q)[0], []))
+    assert _fails(TK.test_brute_force_matmul_local_products, [2, 2])

@@ -122,6 +122,50 @@ int tp_layout_plan(const int64_t *shape, int64_t ndim, const tp_layout *layout,
                    int64_t *num_shards_out, int64_t *boxes, int64_t max_shards,
                    int64_t *shard_of_device, int64_t num_dst);
 
+/* ---- host sharding checker ---------------------------------------------- */
+/*
+ * Output sharding of a broadcasting binary elementwise operator (Add, Mul, ...)
+ * whose inputs of shape1[ndim1] and shape2[ndim2] carry layout1 and layout2
+ * ([ONNX] sharding formalism, "validity check" and the broadcasting n-ary
+ * group; its composition example Add([M,1], [1,N])).  Host only.
+ * Inputs align on their trailing axes (output rank r = max(ndim1, ndim2)).  An
+ * axis where both inputs have the full size must be cut into the same number
+ * of pieces by both; an axis of size 1 is broadcast.  Output shards are listed
+ * row-major over the output axes; shard k lives on the devices that hold both
+ * input shards it is computed from.
+ *   out_shape[r]          the broadcast output shape
+ *   *num_shards_out       S, the number of output shards
+ *   boxes[(k*r + a)*2 ..] (start, stop) on axis a, for k < min(S, max_shards)
+ *   dev_offsets[k]        for k <= min(S, max_shards): shard k's devices are
+ *                         devices[dev_offsets[k] .. dev_offsets[k+1]), sorted;
+ *                         entries at or beyond max_devices are not written
+ * boxes, dev_offsets and devices may be NULL.
+ * Errors: TP_ERR_ARG (NULL outputs, shapes that do not broadcast), everything
+ *         tp_layout_plan reports for either layout, TP_ERR_SPEC (a
+ *         non-broadcast axis cut differently; an output shard whose input
+ *         shards share no device).
+ */
+int tp_check_broadcast_binary(const int64_t *shape1, int64_t ndim1, const tp_layout *layout1,
+                              const int64_t *shape2, int64_t ndim2, const tp_layout *layout2,
+                              int64_t *out_shape, int64_t *num_shards_out, int64_t *boxes, int64_t max_shards,
+                              int64_t *dev_offsets, int64_t *devices, int64_t max_devices);
+
+/*
+ * dims_mapping of Z = matmul(X[..., M, K], Y[..., K, N]) on a mesh of mesh_ndim
+ * dims ([SPMD] rules for computing operators: einsum ...mk,...kn->...mn, merge
+ * the inputs' mappings per axis, read the output's off the merged axes).  Host
+ * only.  x_map and y_map have ndim >= 2 entries (leading batch axes, then the
+ * matrix axes); values in [-1, mesh_ndim-1].  On success z_map[ndim] holds the
+ * output mapping and *partial_mesh_dim the mesh dim that cuts the contracted
+ * axis K (the output is then a partial sum over it), or -1.
+ * Errors: TP_ERR_ARG (NULL pointers, ndim or mesh_ndim out of range),
+ *         TP_ERR_SPEC (a value out of range, a mesh dim used twice in one
+ *         mapping, an axis the two inputs cut by different mesh dims, which
+ *         needs a reshard, or one mesh dim cutting two einsum axes).
+ */
+int tp_infer_matmul_dims_mapping(const int64_t *x_map, const int64_t *y_map, int64_t ndim, int64_t mesh_ndim,
+                                 int64_t *z_map, int64_t *partial_mesh_dim);
+
 /* ---- shard materialisation ------------------------------------------- */
 /*
  * Split and replicate a row-major tensor src[shape] (dtype TP_F32 or TP_BF16;

@@ -37,7 +37,7 @@ TP_REDUCE_OP_MAX = 1
 TP_REDUCE_OP_MIN = 2
 
 # Every symbol include/tpshard.h declares.
-EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_shard_materialize", "tp_shard_gather",
+EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_binary", "tp_infer_matmul_dims_mapping", "tp_shard_materialize", "tp_shard_gather",
            "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
 TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather")
@@ -131,6 +131,12 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.tp_shard_gather.restype = C.c_int
     lib.tp_shard_gather.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int32, i64p, C.c_int64, C.POINTER(tp_layout),
                                     C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
+    lib.tp_check_broadcast_binary.restype = C.c_int
+    lib.tp_check_broadcast_binary.argtypes = [i64p, C.c_int64, C.POINTER(tp_layout), i64p, C.c_int64,
+                                              C.POINTER(tp_layout), i64p, i64p, i64p, C.c_int64, i64p, i64p,
+                                              C.c_int64]
+    lib.tp_infer_matmul_dims_mapping.restype = C.c_int
+    lib.tp_infer_matmul_dims_mapping.argtypes = [i64p, i64p, C.c_int64, C.c_int64, i64p, i64p]
     lib.tp_partial_reduce.restype = C.c_int
     lib.tp_partial_reduce.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                                       C.c_int32, C.c_int64, C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
@@ -265,6 +271,50 @@ def tp_shard_materialize(src, layout: dict, dst, stream=None):
     _check(lib.tp_shard_materialize(C.c_void_p(_ptr(src)), _dtype_code(src), C.cast(shp, C.POINTER(C.c_int64)),
                                     src.dim(), C.byref(lay), C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst,
                                     _stream_ptr(stream)))
+
+
+def tp_check_broadcast_binary(shape1, layout1: dict, shape2, layout2: dict):
+    """Output sharding of a broadcasting binary elementwise op: (out_shape,
+    [(box, devices)]) with boxes as ((start, stop), ...) row-major over the
+    output shards.  Host only."""
+    lib = load()
+    l1, k1 = make_layout(layout1)
+    l2, k2 = make_layout(layout2)
+    s1, s2 = _i64_array(shape1), _i64_array(shape2)
+    r = max(len(shape1), len(shape2))
+    out_shape = (C.c_int64 * max(1, r))()
+    n = C.c_int64()
+    args = [C.cast(s1, C.POINTER(C.c_int64)), len(shape1), C.byref(l1), C.cast(s2, C.POINTER(C.c_int64)),
+            len(shape2), C.byref(l2), C.cast(out_shape, C.POINTER(C.c_int64)), C.byref(n)]
+    _check(lib.tp_check_broadcast_binary(*args, None, 0, None, None, 0))
+    S = n.value
+    boxes = (C.c_int64 * max(1, 2 * r * S))()
+    offs = (C.c_int64 * (S + 1))()
+    _check(lib.tp_check_broadcast_binary(*args, C.cast(boxes, C.POINTER(C.c_int64)), S,
+                                         C.cast(offs, C.POINTER(C.c_int64)), None, 0))
+    devs = (C.c_int64 * max(1, offs[S]))()
+    _check(lib.tp_check_broadcast_binary(*args, C.cast(boxes, C.POINTER(C.c_int64)), S,
+                                         C.cast(offs, C.POINTER(C.c_int64)), C.cast(devs, C.POINTER(C.c_int64)),
+                                         offs[S]))
+    shards = []
+    for k in range(S):
+        box = tuple((boxes[(k * r + a) * 2], boxes[(k * r + a) * 2 + 1]) for a in range(r))
+        shards.append((box, [devs[i] for i in range(offs[k], offs[k + 1])]))
+    return [out_shape[a] for a in range(r)], shards
+
+
+def tp_infer_matmul_dims_mapping(x_map, y_map, mesh_ndim):
+    """(z_map, partial_mesh_dim) of matmul(X[..., M, K], Y[..., K, N]).  Host only."""
+    lib = load()
+    nd = len(x_map)
+    if len(y_map) != nd:
+        raise ValueError("x_map and y_map need the same length")
+    xa, ya = _i64_array(x_map), _i64_array(y_map)
+    z = (C.c_int64 * max(1, nd))()
+    part = C.c_int64()
+    _check(lib.tp_infer_matmul_dims_mapping(C.cast(xa, C.POINTER(C.c_int64)), C.cast(ya, C.POINTER(C.c_int64)), nd,
+                                            mesh_ndim, C.cast(z, C.POINTER(C.c_int64)), C.byref(part)))
+    return [z[i] for i in range(nd)], part.value
 
 
 def tp_shard_gather(src, layout: dict, out, shape, stream=None):

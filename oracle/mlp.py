@@ -11,6 +11,9 @@ Sources:
 * ONNX multi-device proposal, operator-group rules: unary elementwise ops
   (Erf among them) accept any input sharding, so GeLU commutes with the column
   split; MatMul with a sharded K axis yields a partial sum.
+* DeepSpeed-Domino article, design of the row-wise split of X: no dependency
+  across row chunks within a layer or between layers, so a stack of layers
+  consumes each layer's reduced output chunk by chunk (inter_layer_overlap).
 * ColossalAI 1D tensor parallelism, section 2.2, and the DeepSpeed-Domino
   article, "backward": the column-parallel layer's input gradient is a partial
   per rank that an all-reduce sums; each gradient matmul splits into an
@@ -86,6 +89,56 @@ def mlp_rank_rows(X, A_i, B_i, rows, act=GELU_ERF):
     """
     x = _f64(X)[np.asarray(rows, dtype=np.int64)]
     return mlp_rank(x, A_i, B_i, act)
+
+
+# ---- a stack of layers ([DOM] "row-wise split of inputs X", inter-layer) ----
+#
+# Layer l+1 reads layer l's full output: the all-reduced sum of the ranks'
+# partials plus the row layer's bias, stored in the input precision (rounded
+# to nearest even for bf16), which is what the next GEMM consumes.
+
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 (8 significant bits, ties to
+    even; bf16 has float32's exponent range, subnormal step 2**-133), returned
+    as float64.  NaN stays NaN; beyond the largest finite bf16 gives inf."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])                          # |x| = m 2**e, 0.5 <= m < 1
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))    # spacing of bf16 values near x
+    r = np.rint(x[fin] / step) * step                # np.rint rounds half to even
+    big = np.ldexp(1.0, 128) - np.ldexp(1.0, 128 - 9)  # halfway past the largest finite bf16
+    r = np.where(np.abs(x[fin]) >= big, np.copysign(np.inf, x[fin]), r)
+    out[fin] = r
+    return out
+
+
+def round_to(x, dtype):
+    """The stored value of x in ``dtype`` ("bf16", "f32", or "f64": unrounded), float64."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def mlp_stack(X, layers, dtype="bf16"):
+    """Forward through a stack of layers; ``layers`` is a list of dicts with
+    A_i, B_i, peers (the other ranks' partials of that layer, list), bias
+    (or None) and act.  Returns (Z_l, X_{l+1}) per layer: the full output in
+    float64 and the next layer's input, that output stored in ``dtype``."""
+    x = _f64(X)
+    out = []
+    for layer in layers:
+        z = mlp_rank(x, layer["A_i"], layer["B_i"], layer.get("act", GELU_ERF))
+        for p in layer.get("peers", []):
+            z = z + _f64(p)
+        if layer.get("bias") is not None:
+            z = z + _f64(layer["bias"])[None, :]
+        x = round_to(z, dtype)
+        out.append((z, x))
+    return out
 
 
 # ---- backward ([CAI] section 2.2; Domino article, "backward") --------------

@@ -261,3 +261,33 @@ def test_checker_drops_partial(monkeypatch):
     real = K.matmul_dims_mapping
     monkeypatch.setattr(K, "matmul_dims_mapping", lambda x, y, q: (real(x, y, q)[0], []))
     assert _fails(TK.test_brute_force_matmul_local_products, [2, 2])
+
+
+def test_round_bf16_truncates(monkeypatch):
+    import test_oracle_stack as TS
+
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        m, e = np.frexp(x)
+        return np.ldexp(np.trunc(m * 256.0) / 256.0, e)
+    monkeypatch.setattr(O, "round_bf16", bad)
+    assert _fails(TS.test_round_bf16_hand_worked, 259.0, 260.0)
+
+
+def test_stack_drops_bias_from_next_input(monkeypatch):
+    import test_oracle_stack as TS
+
+    def bad(X, layers, dtype="bf16"):
+        x = O._f64(X)
+        out = []
+        for layer in layers:
+            z = O.mlp_rank(x, layer["A_i"], layer["B_i"], layer.get("act", O.GELU_ERF))
+            for p in layer.get("peers", []):
+                z = z + O._f64(p)
+            x = O.round_to(z, dtype)
+            if layer.get("bias") is not None:
+                z = z + O._f64(layer["bias"])[None, :]
+            out.append((z, x))
+        return out
+    monkeypatch.setattr(O, "mlp_stack", bad)
+    assert _fails(TS.test_sharded_stack_is_the_unsharded_network, O.GELU_NONE)

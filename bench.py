@@ -274,6 +274,92 @@ class BwdStep:
                            f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}")}
 
 
+class StackStep:
+    """Two forward layers of an MLP workload's per-rank shape chained with
+    tp_colrow_mlp_stack: layer 2 reads layer 1's reduced output (rounded to
+    bf16 by the reduce), and layer 1's later row chunks reduce beside layer
+    2's earlier GEMMs (the inter-layer overlap)."""
+
+    serial = False
+    reduce_wgs = 0
+    L = 2
+
+    def __init__(self, w):
+        self.w = w
+        dev = "cuda"
+        gen_dev = "cuda" if w.cfg in (3, 5) else "cpu"
+        self.X = inputs.normal((w.M, w.H), inputs.seed_for(w.cfg, inputs.SLOT_X), w.std_x, "bf16", gen_dev).to(dev)
+        self.layers = []
+        self.Y = torch.empty((w.M, w.F), dtype=torch.bfloat16, device=dev)
+        self.Z = torch.empty((w.M, w.H), device=dev)
+        x = self.X
+        for l in range(self.L):
+            As = [inputs.normal((w.H, w.F), inputs.seed_for(w.cfg, inputs.SLOT_A_SHARD + i) + 7919 * l, w.std_a,
+                                "bf16", gen_dev).to(dev) for i in range(w.P)]
+            Bs = [inputs.normal((w.F, w.H), inputs.seed_for(w.cfg, inputs.SLOT_B_SHARD + i) + 7919 * l, w.std_b,
+                                "bf16", gen_dev).to(dev) for i in range(w.P)]
+            # peers' partials of this layer's input: computed once, untimed, by the same path
+            peers = []
+            for i in range(1, w.P):
+                z = torch.empty((w.M, w.H), device=dev)
+                tp.tp_colrow_mlp(x, As[i], Bs[i], self.Y, z, row_chunks=w.R)
+                peers.append(z)
+            xn = torch.empty((w.M, w.H), dtype=torch.bfloat16, device=dev)
+            zo = torch.empty((w.M, w.H), device=dev)
+            tp.tp_colrow_mlp(x, As[0], Bs[0], self.Y, self.Z, row_chunks=w.R, peer_partials=peers, Z_out=zo, X_next=xn)
+            self.layers.append(dict(X=x, A_i=As[0], B_i=Bs[0], Y_ws=self.Y, Z_i=self.Z, row_chunks=w.R, col_chunks=w.C,
+                                    peer_partials=peers, Z_out=zo, X_next=xn))
+            x = xn
+        torch.cuda.synchronize()
+        self.s0 = torch.cuda.Stream()
+        self.s1 = torch.cuda.Stream()
+
+    def result(self):
+        return self.layers[-1]["Z_out"]
+
+    def step(self):
+        tp.tp_colrow_mlp_stack([dict(l, reduce_workgroups=self.reduce_wgs) for l in self.layers], s_compute=self.s0,
+                               s_reduce=self.s0 if self.serial else self.s1)
+
+    @property
+    def work(self):
+        return float(self.L * self.w.flops_per_rank)
+
+    unit = "TFLOP/s"
+
+    def config(self):
+        w = self.w
+        return {"workload": f"{w.name}-{self.L}layer", "layers": self.L, "tokens": w.M, "hidden": w.H,
+                "ffn_per_rank": w.F, "tp": w.P, "row_chunks": w.R, "col_chunks": w.C,
+                "reduce_stream": "compute" if self.serial else "second",
+                "overlap": "inter-layer (layer l+1 chunk r waits only for layer l chunk r)",
+                "peers": "virtual ranks 1..P-1, partials of each layer's input precomputed by the same path"}
+
+    def cpu_baseline(self, budget_s):
+        """The oracle's stack on a row sample (rows are independent through the stack)."""
+        from threadpoolctl import threadpool_info
+        from oracle import mlp as O
+        w = self.w
+        rows = 256
+        sample_rows = np.linspace(0, w.M - 1, rows).astype(np.int64)
+        idx = torch.from_numpy(sample_rows).cuda()
+        layers = [{"A_i": l["A_i"].cpu(), "B_i": l["B_i"].cpu(),
+                   "peers": [p.index_select(0, idx).cpu() for p in l["peer_partials"]]} for l in self.layers]
+        Xs = self.X.index_select(0, idx).cpu()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            O.mlp_stack(Xs, layers)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        return {"value": self.L * 4.0 * rows * w.H * w.F / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": (f"{rows} of {w.M} token rows through the {self.L}-layer stack (fp64, numpy BLAS), with "
+                           f"the {w.P}-way sums; {reps} repetitions, {dt * 1e3:.1f} ms each")}
+
+
 class ReshardStep:
     """The 2x4-mesh layout workload: fused split+replicate, then split reduce."""
 
@@ -348,6 +434,9 @@ WORKLOADS = {
     GPT3_6P7B.name + "-sp": lambda: MlpStep(GPT3_6P7B, split_weights=False, seq=True),
     GPT3_175B.name + "-sp": lambda: MlpStep(GPT3_175B, split_weights=False, seq=True),
     GPT3_6P7B.name + "-sp-bwd": lambda: BwdStep(GPT3_6P7B, seq=True),
+    GPT2_SMALL.name + "-2layer": lambda: StackStep(GPT2_SMALL),
+    GPT3_6P7B.name + "-2layer": lambda: StackStep(GPT3_6P7B),
+    GPT3_175B.name + "-2layer": lambda: StackStep(GPT3_175B),
     GPT3_175B.name + "-sp-bwd": lambda: BwdStep(GPT3_175B, seq=True),
 }
 

@@ -298,6 +298,9 @@ typedef struct {
   float *const *Z_split; /* optional host array of S device pointers, each [M/S, H] fp32:
                         the reduce-scattered output, block j = rows [j*M/S, (j+1)*M/S)
                         of Z_i + peers (+ bias).  Replaces Z_out, which must be NULL. */
+  void *X_next;      /* optional [M, H] in dtype: the full sum (+ bias) rounded to dtype
+                        (RNE for bf16), written by the same reduction, i.e. the next
+                        layer's input; Z_out may then be NULL.  Not with Z_split. */
 } tp_mlp_args;
 
 /*
@@ -322,6 +325,23 @@ typedef struct {
  *         blocks that do not nest), TP_ERR_HIP.
  */
 int tp_colrow_mlp(const tp_mlp_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
+
+/*
+ * Enqueue num_layers forward layers, layer l+1 reading layer l's output
+ * (layers[l].X_next == layers[l+1].X, same dtype, M, H and row_chunks), with
+ * Domino's inter-layer overlap ([DOM] "row-wise split of inputs X": no data
+ * dependency across row chunks, so the reduction of layer l's chunk r runs on
+ * s_reduce beside the GEMMs of layer l+1's earlier chunks; DominoTransformer's
+ * inter_layer_overlap_forward).  Chunk r of layer l+1 waits only for chunk r
+ * of layer l.  Each layer is validated as by tp_colrow_mlp (sequence
+ * parallelism is not supported inside a stack); buffers other than a layer's
+ * own inputs and outputs may be shared between layers (one Y_ws for all, X
+ * buffers used in turn), since each chunk's reuse is ordered by the schedule.
+ * The result of every layer equals what tp_colrow_mlp gives it, bit for bit.
+ * Errors: as tp_colrow_mlp, prefixed with the layer; TP_ERR_ARG for a broken
+ *         link between layers; TP_ERR_UNSUPPORTED for seq_splits > 1.
+ */
+int tp_colrow_mlp_stack(const tp_mlp_args *layers, int64_t num_layers, tp_stream_t s_compute, tp_stream_t s_reduce);
 
 /* ---- backward of one rank's column->row MLP ------------------------- */
 typedef struct {

@@ -38,7 +38,7 @@ TP_REDUCE_OP_MIN = 2
 
 # Every symbol include/tpshard.h declares.
 EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_binary", "tp_infer_matmul_dims_mapping", "tp_shard_materialize", "tp_shard_gather",
-           "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
+           "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_stack", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
 TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather")
 
@@ -86,7 +86,8 @@ class tp_mlp_args(C.Structure):
                 ("row_chunks", C.c_int64), ("col_chunks", C.c_int64), ("P", C.c_int64),
                 ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
                 ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p), ("bias", C.c_void_p),
-                ("seq_splits", C.c_int64), ("X_shards", C.POINTER(C.c_void_p)), ("Z_split", C.POINTER(C.c_void_p))]
+                ("seq_splits", C.c_int64), ("X_shards", C.POINTER(C.c_void_p)), ("Z_split", C.POINTER(C.c_void_p)),
+                ("X_next", C.c_void_p)]
 
 
 class tp_mlp_bwd_args(C.Structure):
@@ -146,6 +147,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.tp_partial_reduce_ex.restype = C.c_int
     lib.tp_colrow_mlp.restype = C.c_int
     lib.tp_colrow_mlp.argtypes = [C.POINTER(tp_mlp_args), C.c_void_p, C.c_void_p]
+    lib.tp_colrow_mlp_stack.restype = C.c_int
+    lib.tp_colrow_mlp_stack.argtypes = [C.POINTER(tp_mlp_args), C.c_int64, C.c_void_p, C.c_void_p]
     lib.tp_colrow_mlp_backward.argtypes = [C.POINTER(tp_mlp_bwd_args), C.c_void_p, C.c_void_p]
     lib.tp_colrow_mlp_backward.restype = C.c_int
     lib.tp_timing_enable.restype = C.c_int
@@ -381,16 +384,10 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
                                         _stream_ptr(stream)))
 
 
-def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
-                  act=TP_ACT_GELU_ERF, s_compute=None, s_reduce=None, reduce_workgroups=0, H_out=None, bias=None,
-                  X_shards=None, Z_split=None):
-    """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers) (+ bias);
-    optionally H_out = X A_i (the pre-activation kept for the backward).
-
-    Sequence parallelism: with ``X_shards`` (S tensors [M/S, H]) X is a workspace
-    the call fills by all-gathering them; with ``Z_split`` (S tensors [M/S, H] fp32)
-    the sum is reduce-scattered into the blocks instead of written to Z_out."""
-    lib = load()
+def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
+              act=TP_ACT_GELU_ERF, reduce_workgroups=0, H_out=None, bias=None, X_shards=None, Z_split=None,
+              X_next=None):
+    """(tp_mlp_args, keep-alive list) for one forward layer, shapes checked."""
     M, H = int(X.shape[0]), int(X.shape[1])
     F = int(A_i.shape[1])
     peers = list(peer_partials)
@@ -399,8 +396,13 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
         raise ValueError("shapes must be X[M,H], A_i[H,F], B_i[F,H], Y_ws[M,F], Z_i[M,H]")
     if not (X.dtype == A_i.dtype == B_i.dtype == Y_ws.dtype):
         raise TypeError("X, A_i, B_i and Y_ws must share one dtype")
-    if H_out is not None and (H_out.dtype != X.dtype or tuple(H_out.shape) != (M, F)):
-        raise TypeError("H_out must be [M, F] in the input dtype")
+    for t in (H_out, X_next):
+        if t is not None and t.dtype != X.dtype:
+            raise TypeError("H_out and X_next are in the input dtype")
+    if H_out is not None and tuple(H_out.shape) != (M, F):
+        raise ValueError("H_out must be [M, F]")
+    if X_next is not None and tuple(X_next.shape) != (M, H):
+        raise ValueError("X_next must be [M, H]")
     import torch
     for t in [Z_i, *peers] + ([Z_out] if Z_out is not None else []):
         if t.dtype != torch.float32 or tuple(t.shape) != (M, H):
@@ -410,12 +412,40 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_pa
                        X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
-                       Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias))
+                       Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias),
+                       X_next=_ptr(X_next))
     S, xs, zs = _seq_arrays(X_shards, Z_split)
     args.seq_splits, args.X_shards, args.Z_split = S, xs, zs
+    return args, [parr, xs, zs]
+
+
+def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, **kw):
+    """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers) (+ bias);
+    optionally H_out = X A_i (the pre-activation kept for the backward) and X_next = the
+    sum rounded to the input dtype (the next layer's input).
+
+    Keywords: row_chunks, col_chunks, peer_partials, Z_out, act, reduce_workgroups, H_out,
+    bias, X_shards, Z_split, X_next.  Sequence parallelism: with ``X_shards`` (S tensors
+    [M/S, H]) X is a workspace the call fills by all-gathering them; with ``Z_split``
+    (S tensors [M/S, H] fp32) the sum is reduce-scattered into the blocks instead of
+    written to Z_out."""
+    lib = load()
+    args, keep = _mlp_args(X, A_i, B_i, Y_ws, Z_i, **kw)
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
+
+
+def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None):
+    """Forward layers in sequence with the inter-layer overlap; ``layers`` is a list
+    of dicts of tp_colrow_mlp's arguments (X, A_i, B_i, Y_ws, Z_i and keywords), each
+    layer but the last writing the next one's X through X_next."""
+    lib = load()
+    built = [_mlp_args(**dict(layer)) for layer in layers]
+    arr = (tp_mlp_args * max(1, len(built)))(*[b[0] for b in built])
+    sc = _stream_ptr(s_compute)
+    sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
+    _check(lib.tp_colrow_mlp_stack(arr, len(built), sc, sr))
 
 
 def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *, row_chunks=1, peer_dX=(),

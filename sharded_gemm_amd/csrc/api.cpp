@@ -36,6 +36,7 @@ namespace {
 
 constexpr int64_t kMaxP = 64;
 constexpr int64_t kMaxSplits = 64;
+constexpr int64_t kMaxLayers = 1024;
 // Workgroups of a reduce that runs beside the GEMMs.  The large GEMM tiles fill
 // every SIMD's register file, so the reduce mostly takes CUs between GEMM
 // workgroups; one workgroup per CU back-fills those gaps without crowding out
@@ -145,13 +146,16 @@ int gather_rows(const void *const *blocks, int64_t Ms, int64_t r0, int64_t rows,
 
 // Reduce rows [r0, r0 + rows) x columns [c0, c0 + cols) of the P partials
 // (row stride ld) into the full output, or into the sequence blocks of Ms rows
-// the row range covers (the reduce-scatter).
+// the row range covers (the reduce-scatter).  `full` may be NULL when `lo`
+// (the same rows of a second full-size output in lo_dtype, row stride ld) takes
+// the result instead.
 int reduce_rows(const float *const *parts, int64_t P, int64_t r0, int64_t rows, int64_t c0, int64_t cols, int64_t ld,
-                float *full, float *const *split, int64_t Ms, hipStream_t s, int64_t max_wgs, const float *bias) {
+                float *full, float *const *split, int64_t Ms, hipStream_t s, int64_t max_wgs, const float *bias,
+                void *lo = nullptr, int lo_dtype = 0) {
   std::vector<float *> dst;
   int64_t per = rows;
   if (!split) {
-    dst.push_back(full + r0 * ld + c0);
+    dst.push_back(full ? full + r0 * ld + c0 : nullptr);
   } else {
     per = std::min(rows, Ms);
     for (int64_t k = 0; k < rows / per; ++k) {
@@ -159,11 +163,133 @@ int reduce_rows(const float *const *parts, int64_t P, int64_t r0, int64_t rows, 
       dst.push_back(split[j] + (g - j * Ms) * ld + c0);
     }
   }
+  void *lo_at = lo ? static_cast<char *>(lo) + (r0 * ld + c0) * dtype_size(lo_dtype) : nullptr;
   hipEvent_t t1 = timing_begin(s);
   const int rc = partial_reduce_launch(parts, static_cast<int>(P), rows, cols, ld, dst.data(), static_cast<int>(dst.size()),
-                                       per, ld, s, max_wgs, TP_REDUCE_OP_SUM, bias);
+                                       per, ld, s, max_wgs, TP_REDUCE_OP_SUM, bias, lo_at, lo_dtype, ld);
   if (rc != TP_OK) return rc;
-  timing_end(t1, s, TP_KERNEL_REDUCE, 4.0 * (P + 1) * rows * cols);
+  const double out_bytes = (full || split ? 4.0 : 0.0) + (lo ? static_cast<double>(dtype_size(lo_dtype)) : 0.0);
+  timing_end(t1, s, TP_KERNEL_REDUCE, (4.0 * P + out_bytes) * rows * cols);
+  return TP_OK;
+}
+
+// One forward layer, validated: sizes, the chunking and what the call writes.
+struct MlpPlan {
+  int64_t es = 0, M = 0, H = 0, F = 0, R = 1, C = 1, Mr = 0, Hc = 0;
+  bool gather = false, reduce = false;
+  int epi1 = 0, epi2 = 0;
+  SeqSplit sq;
+};
+
+int validate_mlp(const tp_mlp_args *a, MlpPlan *pl) {
+  if (!a) return fail(TP_ERR_ARG, "args is NULL");
+  const int64_t es = dtype_size(a->dtype);
+  if (!es) return fail(TP_ERR_ARG, "unknown dtype %d", a->dtype);
+  if (a->act != TP_ACT_NONE && a->act != TP_ACT_GELU_ERF) return fail(TP_ERR_ARG, "unknown act %d", a->act);
+  if (a->M < 1 || a->H < 1 || a->F < 1) return fail(TP_ERR_ARG, "M, H, F must be >= 1");
+  if (!a->X || !a->A_i || !a->B_i || !a->Y_ws || !a->Z_i) return fail(TP_ERR_ARG, "X, A_i, B_i, Y_ws and Z_i must be non-NULL");
+  if (a->row_chunks < 1 || a->col_chunks < 1) return fail(TP_ERR_ARG, "row_chunks and col_chunks must be >= 1");
+  if (a->M % a->row_chunks) return fail(TP_ERR_INDIVISIBLE, "row_chunks %lld does not divide M = %lld", (long long)a->row_chunks, (long long)a->M);
+  if (a->H % a->col_chunks) return fail(TP_ERR_INDIVISIBLE, "col_chunks %lld does not divide H = %lld", (long long)a->col_chunks, (long long)a->H);
+  if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
+  SeqSplit sq;
+  int rc = check_seq(a->seq_splits, a->M, a->row_chunks, a->X_shards, a->Z_split, a->Z_out, "X_shards", "Z_split", "Z_out", &sq);
+  if (rc != TP_OK) return rc;
+  if (a->X_next && a->Z_split) return fail(TP_ERR_UNSUPPORTED, "X_next with a reduce-scattered output (Z_split)");
+  const bool has_out = a->Z_out || a->Z_split || a->X_next;
+  if (a->P > 1 && (!a->peer_partials || !has_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out (or Z_split, or X_next)");
+  if (a->bias && !has_out) return fail(TP_ERR_ARG, "a bias needs Z_out, Z_split or X_next (it is added to the full sum)");
+  if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
+  if (a->H_out && a->act == TP_ACT_NONE) return fail(TP_ERR_ARG, "H_out needs an activation (it would equal Y)");
+  const int64_t M = a->M, H = a->H, F = a->F;
+  if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
+      (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
+    return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
+  const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
+  const bool gather = a->X_shards != nullptr;
+  std::vector<Buf> ins = {{a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
+  std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
+  (gather ? outs : ins).push_back({a->X, bx, "X"});
+  if (gather) {
+    for (int64_t j = 0; j < sq.S; ++j) {
+      if (!a->X_shards[j]) return fail(TP_ERR_ARG, "X_shards[%lld] is NULL", (long long)j);
+      ins.push_back({a->X_shards[j], sq.Ms * H * es, "X shard"});
+    }
+  }
+  for (int64_t p = 1; p < a->P; ++p) {
+    if (!a->peer_partials[p - 1]) return fail(TP_ERR_ARG, "peer_partials[%lld] is NULL", (long long)(p - 1));
+    ins.push_back({a->peer_partials[p - 1], bz, "peer partial"});
+  }
+  if (a->bias) ins.push_back({a->bias, H * 4, "bias"});
+  const bool reduce = a->P > 1 || a->bias || a->Z_split || a->X_next;
+  if (reduce && a->Z_out && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
+  if (a->Z_split) {
+    for (int64_t j = 0; j < sq.S; ++j) {
+      if (!a->Z_split[j]) return fail(TP_ERR_ARG, "Z_split[%lld] is NULL", (long long)j);
+      outs.push_back({a->Z_split[j], sq.Ms * H * 4, "Z_split block"});
+    }
+  }
+  if (a->X_next) outs.push_back({a->X_next, bx, "X_next"});
+  if (a->H_out) outs.push_back({a->H_out, by, "H_out"});
+  if ((rc = check_disjoint(ins, outs)) != TP_OK) return rc;
+
+  const bool bf16 = a->dtype == TP_BF16;
+  const bool save = a->H_out != nullptr;
+  pl->es = es;
+  pl->M = M;
+  pl->H = H;
+  pl->F = F;
+  pl->R = a->row_chunks;
+  pl->C = a->col_chunks;
+  pl->Mr = M / pl->R;
+  pl->Hc = H / pl->C;
+  pl->gather = gather;
+  pl->reduce = reduce;
+  pl->sq = sq;
+  pl->epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveBf16 : kEpiGeluBf16) : kEpiIdentBf16)
+                  : (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveF32 : kEpiGeluF32) : kEpiPlainF32);
+  pl->epi2 = bf16 ? kEpiF32 : kEpiPlainF32;
+  return TP_OK;
+}
+
+// Row chunk r of one forward layer: GEMM1 and, per column block, GEMM2 and its
+// reduction (handed to s1 through ev_blocks[c] when `two`).
+int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0, hipStream_t s1, bool two,
+                  hipEvent_t *ev_blocks) {
+  const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
+  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
+              static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
+  if (a->H_out) {
+    g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
+    g1.ldaux = F;
+  }
+  hipEvent_t t0 = timing_begin(s0);
+  hipError_t e = gemm_launch(g1, pl.epi1, s0);
+  if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
+  timing_end(t0, s0, TP_KERNEL_GEMM1, 2.0 * Mr * F * H);
+  std::vector<const float *> parts(static_cast<size_t>(a->P));
+  for (int64_t c = 0; c < pl.C; ++c) {
+    const int64_t zoff = r * Mr * H + c * Hc;
+    GemmArgs g2{static_cast<const char *>(a->Y_ws) + r * Mr * F * es, static_cast<const char *>(a->B_i) + c * Hc * es,
+                a->Z_i + zoff, Mr, Hc, F, F, H, H};
+    t0 = timing_begin(s0);
+    e = gemm_launch(g2, pl.epi2, s0);
+    if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+    timing_end(t0, s0, TP_KERNEL_GEMM2, 2.0 * Mr * Hc * F);
+    if (!pl.reduce) continue;
+    hipStream_t sr = s0;
+    if (two) {
+      if ((e = hipEventRecord(ev_blocks[c], s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipStreamWaitEvent(s1, ev_blocks[c], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+      sr = s1;
+    }
+    parts[0] = a->Z_i + zoff;
+    for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_partials[p - 1] + zoff;
+    const int rc = reduce_rows(parts.data(), a->P, r * Mr, Mr, c * Hc, Hc, H, a->Z_out, a->Z_split, pl.sq.Ms, sr,
+                               two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0,
+                               a->bias ? a->bias + c * Hc : nullptr, a->X_next, a->dtype);
+    if (rc != TP_OK) return rc;
+  }
   return TP_OK;
 }
 
@@ -318,62 +444,17 @@ int tp_partial_reduce_ex(const float *const *partials, int64_t P, int64_t rows, 
 
 int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_reduce) {
   clear_error();
-  if (!a) return fail(TP_ERR_ARG, "args is NULL");
-  const int64_t es = dtype_size(a->dtype);
-  if (!es) return fail(TP_ERR_ARG, "unknown dtype %d", a->dtype);
-  if (a->act != TP_ACT_NONE && a->act != TP_ACT_GELU_ERF) return fail(TP_ERR_ARG, "unknown act %d", a->act);
-  if (a->M < 1 || a->H < 1 || a->F < 1) return fail(TP_ERR_ARG, "M, H, F must be >= 1");
-  if (!a->X || !a->A_i || !a->B_i || !a->Y_ws || !a->Z_i) return fail(TP_ERR_ARG, "X, A_i, B_i, Y_ws and Z_i must be non-NULL");
-  if (a->row_chunks < 1 || a->col_chunks < 1) return fail(TP_ERR_ARG, "row_chunks and col_chunks must be >= 1");
-  if (a->M % a->row_chunks) return fail(TP_ERR_INDIVISIBLE, "row_chunks %lld does not divide M = %lld", (long long)a->row_chunks, (long long)a->M);
-  if (a->H % a->col_chunks) return fail(TP_ERR_INDIVISIBLE, "col_chunks %lld does not divide H = %lld", (long long)a->col_chunks, (long long)a->H);
-  if (a->P < 1 || a->P > kMaxP) return fail(TP_ERR_ARG, "P = %lld outside [1, %lld]", (long long)a->P, (long long)kMaxP);
-  SeqSplit sq;
-  int rc = check_seq(a->seq_splits, a->M, a->row_chunks, a->X_shards, a->Z_split, a->Z_out, "X_shards", "Z_split", "Z_out", &sq);
+  MlpPlan pl;
+  int rc = validate_mlp(a, &pl);
   if (rc != TP_OK) return rc;
-  const bool has_out = a->Z_out || a->Z_split;
-  if (a->P > 1 && (!a->peer_partials || !has_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out (or Z_split)");
-  if (a->bias && !has_out) return fail(TP_ERR_ARG, "a bias needs Z_out or Z_split (it is added to the full sum)");
-  if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
-  if (a->H_out && a->act == TP_ACT_NONE) return fail(TP_ERR_ARG, "H_out needs an activation (it would equal Y)");
-  const int64_t M = a->M, H = a->H, F = a->F;
-  if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
-      (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
-    return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
-  const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
-  const bool gather = a->X_shards != nullptr;
-  std::vector<Buf> ins = {{a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
-  std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
-  (gather ? outs : ins).push_back({a->X, bx, "X"});
-  if (gather) {
-    for (int64_t j = 0; j < sq.S; ++j) {
-      if (!a->X_shards[j]) return fail(TP_ERR_ARG, "X_shards[%lld] is NULL", (long long)j);
-      ins.push_back({a->X_shards[j], sq.Ms * H * es, "X shard"});
-    }
-  }
-  for (int64_t p = 1; p < a->P; ++p) {
-    if (!a->peer_partials[p - 1]) return fail(TP_ERR_ARG, "peer_partials[%lld] is NULL", (long long)(p - 1));
-    ins.push_back({a->peer_partials[p - 1], bz, "peer partial"});
-  }
-  if (a->bias) ins.push_back({a->bias, H * 4, "bias"});
-  const bool reduce = a->P > 1 || a->bias || a->Z_split;
-  if (reduce && a->Z_out && a->Z_out != a->Z_i) outs.push_back({a->Z_out, bz, "Z_out"});
-  if (a->Z_split) {
-    for (int64_t j = 0; j < sq.S; ++j) {
-      if (!a->Z_split[j]) return fail(TP_ERR_ARG, "Z_split[%lld] is NULL", (long long)j);
-      outs.push_back({a->Z_split[j], sq.Ms * H * 4, "Z_split block"});
-    }
-  }
-  if (a->H_out) outs.push_back({a->H_out, by, "H_out"});
-  if ((rc = check_disjoint(ins, outs)) != TP_OK) return rc;
-
   hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
-  const int64_t R = a->row_chunks, C = a->col_chunks, Mr = M / R, Hc = H / C;
+  const int64_t R = pl.R, C = pl.C, Mr = pl.Mr, H = pl.H, es = pl.es;
+  const bool gather = pl.gather;
   // The reduce stream only pays when a later block's GEMMs can run beside an
   // earlier block's reduce or gather; with a single block the hand-off (an
   // event record and a cross-queue wait, about 10 us each way on MI355X) is
   // pure latency.
-  const bool two = (s0 != s1) && (reduce || gather) && R * C > 1;
+  const bool two = (s0 != s1) && (pl.reduce || gather) && R * C > 1;
   hipEvent_t *ev = nullptr;
   if (two) {
     if ((rc = get_events(static_cast<size_t>(R * C + R + 2), &ev)) != TP_OK) return rc;
@@ -388,7 +469,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   // end of any earlier use of X).
   auto gather_chunk = [&](int64_t r) -> int {
     const bool side = two && r > 0;
-    const int grc = gather_rows(a->X_shards, sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->X), side ? s1 : s0);
+    const int grc = gather_rows(a->X_shards, pl.sq.Ms, r * Mr, Mr, H, es, const_cast<void *>(a->X), side ? s1 : s0);
     if (grc != TP_OK) return grc;
     if (side) {
       hipError_t ge = hipEventRecord(ev_gat[r], s1);
@@ -401,54 +482,75 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
     if ((e = hipEventRecord(ev_fork, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(s1, ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
-
-  const bool bf16 = a->dtype == TP_BF16;
-  const bool save = a->H_out != nullptr;
-  const int epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveBf16 : kEpiGeluBf16) : kEpiIdentBf16)
-                        : (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveF32 : kEpiGeluF32) : kEpiPlainF32);
-  const int epi2 = bf16 ? kEpiF32 : kEpiPlainF32;
-  std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t r = 0; r < R; ++r) {
     // The next chunk's input rows travel on s_reduce while this chunk computes.
     if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
     if (gather && two && r > 0 && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess)
       return hip_fail(e, "hipStreamWaitEvent");
-    GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
-                static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
-    if (save) {
-      g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
-      g1.ldaux = F;
-    }
-    hipEvent_t t0 = timing_begin(s0);
-    e = gemm_launch(g1, epi1, s0);
-    if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
-    timing_end(t0, s0, TP_KERNEL_GEMM1, 2.0 * Mr * F * H);
-    for (int64_t c = 0; c < C; ++c) {
-      const int64_t zoff = r * Mr * H + c * Hc;
-      GemmArgs g2{static_cast<const char *>(a->Y_ws) + r * Mr * F * es, static_cast<const char *>(a->B_i) + c * Hc * es,
-                  a->Z_i + zoff, Mr, Hc, F, F, H, H};
-      t0 = timing_begin(s0);
-      e = gemm_launch(g2, epi2, s0);
-      if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
-      timing_end(t0, s0, TP_KERNEL_GEMM2, 2.0 * Mr * Hc * F);
-      if (!reduce) continue;
-      hipStream_t sr = s0;
-      if (two) {
-        if ((e = hipEventRecord(ev_red[r * C + c], s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        if ((e = hipStreamWaitEvent(s1, ev_red[r * C + c], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-        sr = s1;
-      }
-      parts[0] = a->Z_i + zoff;
-      for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_partials[p - 1] + zoff;
-      rc = reduce_rows(parts.data(), a->P, r * Mr, Mr, c * Hc, Hc, H, a->Z_out, a->Z_split, sq.Ms, sr,
-                       two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0,
-                       a->bias ? a->bias + c * Hc : nullptr);
-      if (rc != TP_OK) return rc;
-    }
+    if ((rc = enqueue_chunk(a, pl, r, s0, s1, two, two ? ev_red + r * C : nullptr)) != TP_OK) return rc;
   }
   if (two) {
     if ((e = hipEventRecord(ev_join, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(s0, ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  return TP_OK;
+}
+
+int tp_colrow_mlp_stack(const tp_mlp_args *layers, int64_t num_layers, tp_stream_t s_compute, tp_stream_t s_reduce) {
+  clear_error();
+  if (!layers || num_layers < 1 || num_layers > kMaxLayers)
+    return fail(TP_ERR_ARG, "need 1 <= num_layers <= %lld and a non-NULL layer array", (long long)kMaxLayers);
+  std::vector<MlpPlan> pl(static_cast<size_t>(num_layers));
+  int rc;
+  for (int64_t l = 0; l < num_layers; ++l) {
+    if ((rc = validate_mlp(&layers[l], &pl[l])) != TP_OK) {
+      const std::string msg = tp_last_error();
+      return fail(rc, "layer %lld: %s", (long long)l, msg.c_str());
+    }
+    if (layers[l].seq_splits > 1) return fail(TP_ERR_UNSUPPORTED, "layer %lld: sequence parallelism inside a stack", (long long)l);
+  }
+  for (int64_t l = 0; l + 1 < num_layers; ++l) {
+    const tp_mlp_args &cur = layers[l], &nxt = layers[l + 1];
+    if (!cur.X_next || cur.X_next != nxt.X)
+      return fail(TP_ERR_ARG, "layer %lld must write the next layer's input (X_next == layer %lld's X)", (long long)l,
+                  (long long)(l + 1));
+    if (cur.dtype != nxt.dtype || cur.M != nxt.M || cur.H != nxt.H || cur.row_chunks != nxt.row_chunks)
+      return fail(TP_ERR_ARG, "layers %lld and %lld differ in dtype, M, H or row_chunks", (long long)l, (long long)(l + 1));
+  }
+  hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
+  const int64_t R = pl[0].R;
+  bool any_reduce = false, any_split = R > 1;
+  int64_t nev = 1;
+  for (const MlpPlan& p : pl) {
+    any_reduce = any_reduce || p.reduce;
+    any_split = any_split || p.C > 1;
+    nev += R * p.C + R;
+  }
+  // [DOM] inter-layer overlap: chunk r of layer l+1 needs only chunk r of
+  // layer l's reduced output, so the reduction of layer l's later chunks runs
+  // on s_reduce beside layer l+1's GEMMs of the earlier ones.
+  const bool two = (s0 != s1) && any_reduce && any_split;
+  hipEvent_t *ev = nullptr;
+  if (two && (rc = get_events(static_cast<size_t>(nev), &ev)) != TP_OK) return rc;
+  hipError_t e;
+  int64_t at = 0;
+  hipEvent_t *prev_done = nullptr;
+  for (int64_t l = 0; l < num_layers; ++l) {
+    hipEvent_t *blocks = two ? ev + at : nullptr;
+    hipEvent_t *done = two ? ev + at + R * pl[l].C : nullptr;
+    at += R * pl[l].C + R;
+    for (int64_t r = 0; r < R; ++r) {
+      if (two && prev_done && (e = hipStreamWaitEvent(s0, prev_done[r], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      if ((rc = enqueue_chunk(&layers[l], pl[l], r, s0, s1, two, two ? blocks + r * pl[l].C : nullptr)) != TP_OK) return rc;
+      if (two && pl[l].reduce && (e = hipEventRecord(done[r], s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    prev_done = two ? done : nullptr;
+  }
+  if (two) {
+    hipEvent_t joined = ev[nev - 1];
+    if ((e = hipEventRecord(joined, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(s0, joined, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
   return TP_OK;
 }

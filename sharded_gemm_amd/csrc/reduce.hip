@@ -10,7 +10,9 @@
 // in flight per lane), then adds in ascending p and stores.  Inputs are read
 // once and outputs written once, so both bypass cache retention (non-temporal).
 // Rows may be strided (ld), which is how a column block of a wider matrix is
-// reduced.
+// reduced.  Besides (or instead of) the fp32 result the kernel can write a
+// copy in the next layer's input precision (bf16, rounded to nearest even, or
+// fp32), so a stack of layers needs no separate conversion pass.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -33,6 +35,8 @@ struct RedArgs {
   const float *in[kMaxP];
   float *out[kMaxOut];
   const float *bias;        // [cols], or null
+  void *lo;                 // second output (bf16 or fp32), FULL mode only, or null
+  int64_t ld_lo;            // elements
   int32_t P;
   uint32_t cols_v;          // vectors per row
   uint32_t total_v;         // rows * cols_v
@@ -61,7 +65,32 @@ __device__ __forceinline__ V combine(V acc, V v) {
   }
 }
 
-template <int VW, int UNROLL, int OP, bool BIAS>
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// LO: 0 no second output, 1 bf16 copy, 2 fp32 copy.  HI: write the fp32 result.
+template <int LO, class V>
+__device__ __forceinline__ void store_lo(void *base, int64_t off, V v) {
+  if constexpr (LO == 2) {
+    __builtin_nontemporal_store(v, reinterpret_cast<V *>(static_cast<float *>(base) + off));
+  } else if constexpr (LO == 1) {
+    if constexpr (sizeof(V) == sizeof(float)) {
+      static_cast<uint16_t *>(base)[off] = static_cast<uint16_t>(bf16_rne(v));
+    } else {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      u32x2_t w;
+      w[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+      w[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(base) + off));
+    }
+  }
+}
+
+template <int VW, int UNROLL, int OP, bool BIAS, bool HI, int LO>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
   typedef typename FVec<VW>::T V;
   const uint32_t stride = gridDim.x * kThreads;
@@ -102,8 +131,11 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
       if (!ok[u]) continue;
       const uint32_t j = row[u] / a.rows_per_out;
       const int64_t r = row[u] - static_cast<int64_t>(j) * a.rows_per_out;
-      float *dst = a.out[j] + r * a.ld_out + static_cast<int64_t>(col[u]) * VW;
-      __builtin_nontemporal_store(acc[u], reinterpret_cast<V *>(dst));
+      if constexpr (HI) {
+        float *dst = a.out[j] + r * a.ld_out + static_cast<int64_t>(col[u]) * VW;
+        __builtin_nontemporal_store(acc[u], reinterpret_cast<V *>(dst));
+      }
+      if constexpr (LO != 0) store_lo<LO>(a.lo, static_cast<int64_t>(row[u]) * a.ld_lo + static_cast<int64_t>(col[u]) * VW, acc[u]);
     }
   }
 }
@@ -112,19 +144,25 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
 
 int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
                           float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
-                          hipStream_t stream, int64_t max_wgs, int op, const float *bias) {
+                          hipStream_t stream, int64_t max_wgs, int op, const float *bias, void *lo, int lo_dtype,
+                          int64_t ld_lo) {
   if (rows == 0 || cols == 0) return TP_OK;
   RedArgs a{};
   auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const bool hi = out[0] != nullptr;
+  const int lo_kind = lo ? (lo_dtype == TP_BF16 ? 1 : 2) : 0;
   bool vec = (cols % 4 == 0) && (ld_in % 4 == 0) && (ld_out % 4 == 0) && (!bias || al16(bias));
+  if (lo_kind) vec = vec && (ld_lo % 4 == 0) && (reinterpret_cast<uintptr_t>(lo) & (lo_kind == 1 ? 7u : 15u)) == 0;
   a.bias = bias;
+  a.lo = lo;
+  a.ld_lo = ld_lo;
   for (int p = 0; p < P; ++p) {
     a.in[p] = partials[p];
     vec = vec && al16(partials[p]);
   }
   for (int j = 0; j < nout; ++j) {
     a.out[j] = out[j];
-    vec = vec && al16(out[j]);
+    vec = vec && (!hi || al16(out[j]));
   }
   const int vw = vec ? 4 : 1;
   const int64_t cols_v = cols / vw;
@@ -143,15 +181,21 @@ int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int
   const int64_t want = (total_v + kThreads * kUnroll - 1) / (kThreads * kUnroll);
   const int64_t cap = max_wgs > 0 ? std::min<int64_t>(max_wgs, 1 << 20) : (1 << 20);
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>(want, cap)));
-  auto go = [&](auto vw, auto o, auto b) {
-    hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value>), grid,
-                       dim3(kThreads), 0, stream, a);
+  auto go = [&](auto vw, auto o, auto b, auto h, auto l) {
+    hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value,
+                                      decltype(h)::value, decltype(l)::value>),
+                       grid, dim3(kThreads), 0, stream, a);
   };
   using std::integral_constant;
+  // The second output exists for sums only (a layer's output feeding the next layer).
   auto by_op = [&](auto vw, auto b) {
-    if (op == 1) go(vw, integral_constant<int, 1>{}, b);
-    else if (op == 2) go(vw, integral_constant<int, 2>{}, b);
-    else go(vw, integral_constant<int, 0>{}, b);
+    if (op == 1) go(vw, integral_constant<int, 1>{}, b, std::true_type{}, integral_constant<int, 0>{});
+    else if (op == 2) go(vw, integral_constant<int, 2>{}, b, std::true_type{}, integral_constant<int, 0>{});
+    else if (lo_kind == 0) go(vw, integral_constant<int, 0>{}, b, std::true_type{}, integral_constant<int, 0>{});
+    else if (lo_kind == 1 && hi) go(vw, integral_constant<int, 0>{}, b, std::true_type{}, integral_constant<int, 1>{});
+    else if (lo_kind == 1) go(vw, integral_constant<int, 0>{}, b, std::false_type{}, integral_constant<int, 1>{});
+    else if (hi) go(vw, integral_constant<int, 0>{}, b, std::true_type{}, integral_constant<int, 2>{});
+    else go(vw, integral_constant<int, 0>{}, b, std::false_type{}, integral_constant<int, 2>{});
   };
   auto by_bias = [&](auto vw) {
     if (bias) by_op(vw, std::true_type{}); else by_op(vw, std::false_type{});

@@ -24,8 +24,12 @@ int shard_gather_launch(const ShardPlan& plan, const void *const *src, int64_t e
 // p, fp32; op 0 sum, 1 max, 2 min.  rows_per_out rows go to each out[j]; out[j]
 // has row stride ld_out.  Arguments already validated (1 <= P <= 64,
 // 1 <= nout <= 64).  max_wgs > 0 caps the grid (the kernel strides over the rest).
+// lo (sum only, nout = 1): also write the result to lo[row * ld_lo + col] in
+// lo_dtype (TP_BF16, rounded to nearest even, or TP_F32); out[0] may then be
+// NULL to write lo alone.
 int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int64_t cols, int64_t ld_in,
                           float *const *out, int nout, int64_t rows_per_out, int64_t ld_out,
-                          hipStream_t stream, int64_t max_wgs = 0, int op = 0, const float *bias = nullptr);
+                          hipStream_t stream, int64_t max_wgs = 0, int op = 0, const float *bias = nullptr,
+                          void *lo = nullptr, int lo_dtype = 0, int64_t ld_lo = 0);
 
 }  // namespace tpshard

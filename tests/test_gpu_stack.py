@@ -1,0 +1,162 @@
+"""GPU parity of tp_colrow_mlp_stack (layers chained through the reduce's
+fused next-layer input, with the inter-layer overlap) and of the X_next
+output, against the oracle's layer stack."""
+import numpy as np
+import pytest
+import torch
+
+import sharded_gemm_amd as tp
+from sharded_gemm_amd import inputs
+from oracle import mlp as O
+
+from gpu_helpers import Guarded, announce, bits, rel_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+
+
+def setup_module(_):
+    require_gpu()
+
+
+def _pm1_one_hot(H, F, seed):
+    """[H, F] with a single +-1 per column: X A picks (and maybe negates) one
+    column of X, so Y is exactly representable whatever X holds."""
+    g = torch.Generator().manual_seed(seed)
+    rows = torch.randint(0, H, (F,), generator=g)
+    sign = torch.randint(0, 2, (F,), generator=g) * 2 - 1
+    A = torch.zeros((H, F))
+    A[rows, torch.arange(F)] = sign.float()
+    return A.to(torch.bfloat16)
+
+
+def _layers_integer(M, H, Fs, P, seed):
+    """Per layer: A (+-1 one-hot), B in {-1, 0, 1}, P-1 integer peers, a bias."""
+    out = []
+    for l, F in enumerate(Fs):
+        s = seed + 100 * l
+        out.append({"A_i": _pm1_one_hot(H, F, s),
+                    "B_i": inputs.small_ints((F, H), seed=s + 1, lo=-1, hi=1, dtype="bf16"),
+                    "peers": [inputs.small_ints((M, H), seed=s + 10 + p, lo=-64, hi=64) for p in range(P - 1)],
+                    "bias": inputs.small_ints((H,), seed=s + 2, lo=-8, hi=8)})
+    return out
+
+
+def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, keep_z=True):
+    """The stack on the GPU into guarded buffers; returns per layer (Z_out, X_next) CPU copies."""
+    M, H = X0.shape
+    dt = X0.dtype
+    xs = [X0.cuda()] + [Guarded((M, H), dt) for _ in layers]
+    zs = [Guarded((M, H), torch.float32) for _ in layers] if keep_z else [None] * len(layers)
+    Y = torch.empty((M, max(l["A_i"].shape[1] for l in layers)), dtype=dt, device="cuda")
+    Zi = torch.empty((M, H), device="cuda")
+    args = []
+    for l, layer in enumerate(layers):
+        F = layer["A_i"].shape[1]
+        args.append(dict(X=xs[l] if l == 0 else xs[l].t, A_i=layer["A_i"].cuda(), B_i=layer["B_i"].cuda(),
+                         Y_ws=Y[:, :F] if F == Y.shape[1] else torch.empty((M, F), dtype=dt, device="cuda"),
+                         Z_i=Zi, row_chunks=R, col_chunks=C, peer_partials=[p.cuda() for p in layer["peers"]],
+                         Z_out=zs[l].t if keep_z else None, act=act,
+                         bias=layer["bias"].cuda() if layer.get("bias") is not None else None,
+                         X_next=xs[l + 1].t))
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream() if two_streams else s0
+    tp.tp_colrow_mlp_stack(args, s_compute=s0, s_reduce=s1)
+    torch.cuda.synchronize()
+    res = []
+    for l in range(len(layers)):
+        assert xs[l + 1].guards_intact()
+        if keep_z:
+            assert zs[l].guards_intact()
+        res.append((zs[l].t.cpu() if keep_z else None, xs[l + 1].t.cpu()))
+    return res
+
+
+@pytest.mark.parametrize("M,H,Fs,R,C,P,two", [
+    (512, 256, [128, 96], 2, 1, 4, True),      # inter-layer overlap over two row chunks
+    (768, 384, [64, 64, 32], 3, 2, 3, True),
+    (300, 264, [136, 64], 3, 2, 2, True),      # ragged tiles
+    (256, 128, [64, 64], 1, 1, 2, True),       # one block: serial schedule
+    (512, 256, [128, 128], 2, 2, 4, False),    # one stream
+    (4096, 768, [768, 768], 2, 1, 4, True),    # GPT-2-small shape
+])
+def test_stack_integer_exact(M, H, Fs, R, C, P, two):
+    """Exact integers through every layer: each Z_out and each next-layer input
+    (the sum rounded to bf16, RNE on both sides of the same exact value) equals
+    the oracle's bit for bit."""
+    announce(f"stack integer exact M={M} H={H} F={Fs} R={R} C={C} P={P} two={two}")
+    X0 = inputs.small_ints((M, H), seed=1201, lo=-4, hi=4, dtype="bf16")
+    layers = _layers_integer(M, H, Fs, P, 1300)
+    got = run_stack(X0, layers, R=R, C=C, two_streams=two)
+    ref = O.mlp_stack(X0, [dict(l, act=O.GELU_NONE) for l in layers], dtype="bf16")
+    for l, ((z, xn), (zr, xr)) in enumerate(zip(got, ref)):
+        assert np.array_equal(z.double().numpy(), zr), l
+        assert np.array_equal(bits(xn), bits(torch.from_numpy(xr).to(torch.bfloat16))), l
+
+
+def test_stack_equals_layer_by_layer_calls_bitwise():
+    """GeLU, random bf16: the stack gives the same bits as one tp_colrow_mlp call
+    per layer (the overlap changes the schedule, not the arithmetic)."""
+    announce("stack vs single-layer calls, gelu")
+    M, H, F, P, R = 2048, 512, 384, 4, 2
+    X0 = inputs.normal((M, H), seed=1401, dtype="bf16")
+    layers = [{"A_i": inputs.normal((H, F), seed=1410 + l, std=0.05, dtype="bf16"),
+               "B_i": inputs.normal((F, H), seed=1420 + l, std=0.05, dtype="bf16"),
+               "peers": [inputs.normal((M, H), seed=1430 + 10 * l + p) for p in range(P - 1)],
+               "bias": inputs.normal((H,), seed=1450 + l)} for l in range(3)]
+    got = run_stack(X0, layers, R=R, act=tp.TP_ACT_GELU_ERF)
+    x = X0.cuda()
+    for l, layer in enumerate(layers):
+        Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+        Zi = torch.empty((M, H), device="cuda")
+        Zo = torch.empty((M, H), device="cuda")
+        xn = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        tp.tp_colrow_mlp(x, layer["A_i"].cuda(), layer["B_i"].cuda(), Y, Zi, row_chunks=R,
+                         peer_partials=[p.cuda() for p in layer["peers"]], Z_out=Zo, bias=layer["bias"].cuda(),
+                         X_next=xn, s_reduce=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(got[l][0]), bits(Zo.cpu())), l
+        assert np.array_equal(bits(got[l][1]), bits(xn.cpu())), l
+        x = xn
+    ref = O.mlp_stack(X0, layers, dtype="bf16")
+    assert rel_err(got[-1][0], ref[-1][0]) <= TOL_BF16
+
+
+def test_x_next_only_and_fp32():
+    """Z_out omitted (X_next alone); and the fp32 path, whose X_next is an fp32 copy."""
+    announce("stack X_next only; fp32 stack")
+    M, H, F, P = 512, 256, 128, 2
+    X0 = inputs.small_ints((M, H), seed=1501, lo=-4, hi=4, dtype="bf16")
+    layers = _layers_integer(M, H, [F, F], P, 1600)
+    got = run_stack(X0, layers, R=2, keep_z=False)
+    ref = O.mlp_stack(X0, [dict(l, act=O.GELU_NONE) for l in layers], dtype="bf16")
+    for (_, xn), (_, xr) in zip(got, ref):
+        assert np.array_equal(bits(xn), bits(torch.from_numpy(xr).to(torch.bfloat16)))
+    X0f = inputs.normal((64, 256), seed=1701)
+    lf = [{"A_i": inputs.normal((256, 512), seed=1710 + l, std=1 / 16), "B_i": inputs.normal((512, 256), seed=1720 + l, std=1 / 32),
+           "peers": [inputs.normal((64, 256), seed=1730 + l)], "bias": None} for l in range(2)]
+    got = run_stack(X0f, lf, R=2, act=tp.TP_ACT_GELU_ERF)
+    ref = O.mlp_stack(X0f, lf, dtype="f32")
+    assert rel_err(got[-1][0], ref[-1][0]) <= 1e-5
+    assert np.array_equal(bits(got[0][0]), bits(got[0][1]))    # the fp32 copy is the fp32 sum
+
+
+def test_broken_link_leaves_outputs_untouched():
+    announce("stack error path")
+    M, H, F = 64, 32, 16
+    X = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((H, F), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((F, H), dtype=torch.bfloat16, device="cuda")
+    Y = Guarded((M, F), torch.bfloat16)
+    Z = Guarded((M, H), torch.float32)
+    Xn = Guarded((M, H), torch.bfloat16)
+    other = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    layers = [dict(X=X, A_i=A, B_i=B, Y_ws=Y.t, Z_i=Z.t, X_next=Xn.t),
+              dict(X=other, A_i=A, B_i=B, Y_ws=Y.t, Z_i=Z.t)]
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_colrow_mlp_stack(layers)
+    assert e.value.kind == "arg"
+    torch.cuda.synchronize()
+    for g in (Y, Z, Xn):
+        assert g.body_untouched() and g.guards_intact()

@@ -121,6 +121,15 @@ def test_mesh_rejects_like_oracle(mesh, ids, dm, shape, kind):
 FAKE = 1 << 40   # device-looking addresses; never dereferenced on these paths
 
 
+@pytest.fixture(autouse=True)
+def _no_visible_gpu():
+    """These tests hand the library made-up device addresses and expect it to
+    refuse them before any launch; where a GPU is visible a mistake in such a
+    test could reach a kernel, so they run only where none is."""
+    if torch.cuda.is_available():
+        pytest.skip("validation tests with made-up device addresses run on hosts without a GPU")
+
+
 def _mlp_args(**kw):
     a = _abi.tp_mlp_args(dtype=_abi.TP_BF16, act=_abi.TP_ACT_GELU_ERF, M=64, H=64, F=64,
                          X=FAKE, A_i=FAKE + (1 << 20), B_i=FAKE + (2 << 20), Y_ws=FAKE + (3 << 20),
@@ -342,3 +351,34 @@ def test_sequence_parallel_validation():
     assert bwd(seq_splits=4, dX_split=_ptrs(zs), dX_out=FAKE + (60 << 20)) == _abi.TP_ERR_ARG
     assert bwd(seq_splits=4, dZ_shards=_ptrs([xs[0], FAKE + (5 << 20) + 8, xs[2], xs[3]])) == _abi.TP_ERR_ARG  # in dZ
     assert bwd(M=24, seq_splits=4, row_chunks=3, dZ_shards=_ptrs(xs)) == _abi.TP_ERR_UNSUPPORTED
+
+
+def test_32bit_index_limits_are_rejected():
+    """Sizes past the kernels' 32-bit indexing are refused before any launch."""
+    lib = _abi.load()
+    # an MLP whose row chunk times column block reaches 2**31 elements
+    assert lib.tp_colrow_mlp(C.byref(_mlp_args(M=1 << 16, H=1 << 15, F=64)), None, None) == _abi.TP_ERR_UNSUPPORTED
+    # a reduce of 2**33 elements: 2**31 four-wide vectors
+    parts = [FAKE, FAKE + (1 << 36)]
+    outs = [FAKE + (2 << 36)]
+    assert _reduce(P=2, rows=1 << 17, cols=1 << 16, ld_in=1 << 16, ld_out=1 << 16, parts=parts, outs=outs) == \
+        _abi.TP_ERR_UNSUPPORTED
+    # a shard of 2**36 bytes (bf16): 2**32 sixteen-byte vectors
+    spec = {"device": [0], "sharded_dim": []}
+    lay, keep = _abi.make_layout(spec)
+    shape = (C.c_int64 * 1)(1 << 35)
+    dst = (C.c_void_p * 1)(FAKE + (1 << 38))
+    assert lib.tp_shard_materialize(C.c_void_p(FAKE), _abi.TP_BF16, C.cast(shape, C.POINTER(C.c_int64)), 1,
+                                    C.byref(lay), C.cast(dst, C.POINTER(C.c_void_p)), 1, None) == _abi.TP_ERR_UNSUPPORTED
+
+
+def test_group_beyond_launch_table_is_rejected():
+    """One shard replicated to more than 64 devices cannot be written by one
+    launch: rejected before any launch."""
+    lib = _abi.load()
+    spec = {"device": [-1], "device_map": {-1: list(range(65))}, "sharded_dim": []}
+    lay, keep = _abi.make_layout(spec)
+    shape = (C.c_int64 * 1)(64)
+    dst = (C.c_void_p * 65)(*[FAKE + (d + 1) * (1 << 20) for d in range(65)])
+    assert lib.tp_shard_materialize(C.c_void_p(FAKE), _abi.TP_F32, C.cast(shape, C.POINTER(C.c_int64)), 1,
+                                    C.byref(lay), C.cast(dst, C.POINTER(C.c_void_p)), 65, None) == _abi.TP_ERR_UNSUPPORTED

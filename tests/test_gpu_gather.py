@@ -189,3 +189,19 @@ def test_empty_tensor_is_a_no_op():
     tp.tp_shard_gather({0: torch.empty((0, 2), device="cuda"), 1: torch.empty((0, 2), device="cuda")}, spec,
                        [torch.empty((0, 4), device="cuda")], (0, 4))
     torch.cuda.synchronize()
+
+
+def test_rank8_many_shards_and_outputs():
+    """Rank 8, 256 shards with replicas, gathered into 65 outputs (two groups of
+    at most 64 per launch) and several launches of at most 32 shards."""
+    shape = (2, 2, 2, 2, 2, 2, 2, 64)
+    nsh = 256
+    spec = {"device": [-(k + 1) for k in range(nsh)],
+            "device_map": {-(k + 1): [2 * k + 1, 2 * k] for k in range(nsh)},
+            "sharded_dim": [{"axis": a, "num_shards": 2} for a in range(8)]}
+    announce("gather rank 8, 256 shards, 65 outputs")
+    pieces = _pieces(shape, spec, torch.float32, seed=9600)
+    got = _run(pieces, spec, shape, torch.float32, nout=65)
+    ref = _oracle(pieces, spec, shape)
+    for g in got:
+        _same_bits(g, ref, torch.float32)

@@ -186,3 +186,17 @@ def test_empty_tensor_is_a_no_op():
     outs = {d: torch.empty((0, 2), device="cuda") for d in range(2)}
     tp.tp_shard_materialize(src, {"device": [0, 1], "sharded_dim": [{"axis": 1, "num_shards": 2}]}, outs)
     torch.cuda.synchronize()
+
+
+def test_rank8_many_shards_and_replicas():
+    """Rank 8 (the largest), every axis cut in two: 256 shards, each to a pair
+    of devices (512 destinations), so the copy spans several launches of at
+    most 32 shards and 64 destinations."""
+    shape = (2, 2, 2, 2, 2, 2, 2, 64)
+    nsh = 256
+    spec = {"device": [-(k + 1) for k in range(nsh)],
+            "device_map": {-(k + 1): [2 * k + 1, 2 * k] for k in range(nsh)},
+            "sharded_dim": [{"axis": a, "num_shards": 2} for a in range(8)]}
+    announce("layout rank 8, 256 shards x 2 replicas")
+    src = inputs.normal(shape, seed=7900)
+    _compare_with_oracle(src, _run(src, spec, torch.float32), L.split(src, spec))

@@ -283,3 +283,17 @@ def test_row_parallel_bias_integer_exact(M, H, F, Rc, Cc, P):
     z_ref = O.mlp_rank(X, A, B, O.GELU_NONE)
     assert np.array_equal(Z.cpu().numpy().astype(np.float64), z_ref)
     assert np.array_equal(Zo.cpu().numpy().astype(np.float64), R.reduce_full([z_ref] + peers_cpu, "sum", bias_cpu))
+
+
+def test_max_ranks_integer_exact():
+    """P = 64 virtual ranks (63 peers), chunked, on two streams: exact."""
+    announce("mlp P=64 integer exact")
+    M, H, F, P = 256, 128, 64, 64
+    X = inputs.small_ints((M, H), seed=281, lo=-4, hi=4, dtype="bf16")
+    A = _one_hot_columns(H, F, 282)
+    B = inputs.small_ints((F, H), seed=283, lo=-4, hi=4, dtype="bf16")
+    peers_cpu = [inputs.small_ints((M, H), seed=300 + p, lo=-512, hi=512) for p in range(P - 1)]
+    Y, Z, Zo = run_rank(X.cuda(), A.cuda(), B.cuda(), R=2, C=2, peers=[p.cuda() for p in peers_cpu],
+                        act=tp.TP_ACT_NONE, two_streams=True)
+    z_ref = O.mlp_rank(X, A, B, O.GELU_NONE)
+    assert np.array_equal(Zo.numpy().astype(np.float64), R.reduce_full([z_ref] + peers_cpu))

@@ -155,3 +155,24 @@ def test_bias_with_random_sum():
     out = torch.empty((512, 768), device="cuda")
     tp.tp_partial_reduce([p.cuda() for p in parts_cpu], [out], bias=bias_cpu.cuda())
     assert rel_err(out.cpu(), R.reduce_full(parts_cpu, "sum", bias_cpu)) <= TOL
+
+
+# ---- maximum sizes ------------------------------------------------------------
+
+def test_max_partials_and_splits_integer_exact():
+    """P = 64 partials (eight load groups) and S = 64 output blocks, the
+    largest the library takes: integer sums, exact."""
+    announce("reduce P=64 FULL and P=64 S=64 SPLIT")
+    P, rows, cols = 64, 256, 520
+    parts_cpu = [inputs.small_ints((rows, cols), seed=8500 + p, lo=-1000, hi=1000) for p in range(P)]
+    parts = [p.cuda() for p in parts_cpu]
+    out = Guarded((rows, cols), torch.float32)
+    tp.tp_partial_reduce(parts, [out.t])
+    blocks = [Guarded((rows // 64, cols), torch.float32) for _ in range(64)]
+    tp.tp_partial_reduce(parts, [b.t for b in blocks], tp.TP_REDUCE_SPLIT)
+    torch.cuda.synchronize()
+    full = R.reduce_full(parts_cpu)
+    assert out.guards_intact() and np.array_equal(out.t.cpu().numpy().astype(np.float64), full)
+    ref = R.reduce_split(parts_cpu, 64)
+    for b, r in zip(blocks, ref):
+        assert b.guards_intact() and np.array_equal(b.t.cpu().numpy().astype(np.float64), r)

@@ -52,7 +52,9 @@ def _bf16_exact(x64):
                                    # ping-pong kernel, 256 x 256 tiles (ragged M and N; 1, 2 and 7 stages)
                                    (4100, 64, 6152), (4100, 128, 6152), (4100, 448, 6152),
                                    # ping-pong kernel, 256 x 192 tiles
-                                   (2000, 128, 6136), (2000, 320, 6136)])
+                                   (2000, 128, 6136), (2000, 320, 6136),
+                                   # ping-pong kernel, 256 x 128 tiles (ragged M and N)
+                                   (4000, 64, 2000), (4000, 192, 2000)])
 def test_hidden_integer_exact(M, H, F):
     """Small-integer inputs make X A_i exact in fp32, so Y must equal the
     RNE-to-bf16 rounding of the oracle's exact value, bit for bit."""
@@ -80,7 +82,9 @@ def _one_hot_columns(H, F, seed):
                                             (50, 30, 22, 2, 3, 2), (1024, 1024, 512, 4, 4, 8),
                                             (515, 256, 96, 1, 2, 2), (1030, 640, 320, 2, 5, 4),
                                             # GEMM2 on the ping-pong kernel (fp32 out): 256 x 192, 256 x 256
-                                            (2000, 6136, 128, 1, 1, 2), (4100, 6152, 64, 1, 1, 2)])
+                                            (2000, 6136, 128, 1, 1, 2), (4100, 6152, 64, 1, 1, 2),
+                                            # GEMM2 on the ping-pong kernel, 256 x 128 tiles
+                                            (4000, 2000, 64, 1, 1, 2)])
 def test_chain_integer_exact(M, H, F, Rc, Cc, P):
     """Exact whole chain: Y small integers, fp32 sums exact, so Z_i and Z_out
     must equal the oracle bit for bit, chunked, on two streams."""

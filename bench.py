@@ -518,6 +518,57 @@ def roofline(kernels, dtype, workload):
             "frac": k["achieved"] / PEAK_HBM_GBS, "traffic": traffic}
 
 
+# --------------------------------------------------------------------------- torch context
+
+def torch_context(wl, reps=20):
+    """torch.matmul (hipBLASLt) on the step's GEMM shapes and a torch sum of the
+    P partials of one reduce block, timed with events on one stream.  Context
+    only: these are library calls, not part of the path."""
+    w = wl.w
+    s = torch.cuda.Stream()
+    Mr, Hc = w.M // w.R, w.H // w.C
+    X = wl.X[:Mr]
+    A, B = wl.As[0], wl.Bs[0]
+    Y = torch.empty((Mr, w.F), dtype=X.dtype, device="cuda")
+    parts = [wl.Z[:Mr]] + [p[:Mr] for p in wl.peers]
+
+    def t(fn):
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                fn()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    ms = t(lambda: torch.matmul(X, A, out=Y))
+    out["gemm1_matmul"] = {"shape": [Mr, w.F, w.H], "ms": ms, "TFLOP/s": 2.0 * Mr * w.F * w.H / ms / 1e9}
+    Bc = B[:, :Hc].contiguous()
+    Z = torch.empty((Mr, Hc), dtype=X.dtype, device="cuda")
+    ms = t(lambda: torch.matmul(Y, Bc, out=Z))
+    out["gemm2_matmul"] = {"shape": [Mr, Hc, w.F], "ms": ms, "TFLOP/s": 2.0 * Mr * Hc * w.F / ms / 1e9,
+                           "note": "bf16 output (torch.matmul has no fp32 output for bf16 inputs)"}
+    if len(parts) > 1:
+        acc = torch.empty_like(parts[0])
+
+        def tsum():
+            torch.add(parts[0], parts[1], out=acc)
+            for p in parts[2:]:
+                acc.add_(p)
+        ms = t(tsum)
+        nbytes = 4.0 * (len(parts) + 1) * Mr * w.H
+        rb = 4.0 * (3 * (len(parts) - 1)) * Mr * w.H
+        out["reduce_torch_add"] = {"partials": len(parts), "ms": ms, "GB/s_algorithmic": nbytes / ms / 1e6,
+                                   "GB/s_moved": rb / ms / 1e6}
+    for k, v in out.items():
+        log(f"[bench] torch context {k}: {v}")
+    return out
+
+
 # --------------------------------------------------------------------------- main
 
 def main():
@@ -533,6 +584,9 @@ def main():
                     help="cap on the reduce kernel's workgroups beside the GEMMs (0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB plain copy (for calibrating traffic counters)")
+    ap.add_argument("--torch-context", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) and a torch sum of the partials on the same shapes "
+                         "(context only; MLP workloads)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -648,6 +702,8 @@ def main():
         log("[bench] timing the CPU oracle")
         cpu = wl.cpu_baseline(args.cpu_budget)
 
+    context = torch_context(wl) if args.torch_context and isinstance(wl, MlpStep) else None
+
     rec = {"metric": METRIC, "value": value, "unit": wl.unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded N(0,1)/N(0,0.02) tensors)",
@@ -656,6 +712,8 @@ def main():
            "ms_per_step_eager": ms_eager_plain, "ms_per_step_graph": ms_graph,
            "ms_per_step_eager_with_kernel_events": ms_eager,
            "device": torch.cuda.get_device_name(0)}
+    if context is not None:
+        rec["torch_context"] = context
     print(json.dumps(rec), flush=True)
 
 

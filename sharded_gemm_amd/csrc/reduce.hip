@@ -73,10 +73,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 // LO: 0 no second output, 1 bf16 copy, 2 fp32 copy.  HI: write the fp32 result.
+// The second output is the next layer's input, read by its GEMM right after,
+// so it is stored through the caches (the fp32 result streams past them).
 template <int LO, class V>
 __device__ __forceinline__ void store_lo(void *base, int64_t off, V v) {
   if constexpr (LO == 2) {
-    __builtin_nontemporal_store(v, reinterpret_cast<V *>(static_cast<float *>(base) + off));
+    *reinterpret_cast<V *>(static_cast<float *>(base) + off) = v;
   } else if constexpr (LO == 1) {
     if constexpr (sizeof(V) == sizeof(float)) {
       static_cast<uint16_t *>(base)[off] = static_cast<uint16_t>(bf16_rne(v));
@@ -85,7 +87,7 @@ __device__ __forceinline__ void store_lo(void *base, int64_t off, V v) {
       u32x2_t w;
       w[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
       w[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(base) + off));
+      *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(base) + off) = w;
     }
   }
 }

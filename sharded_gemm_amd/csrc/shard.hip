@@ -13,7 +13,9 @@
 // device its group lists) and writes it into its box of every output.  A
 // workgroup streams a slice of one shard with the widest vector the alignment
 // allows (16, 8, 4 or 2 bytes per lane).  Every byte is read once and written
-// once per destination, so both sides use non-temporal accesses.
+// once per destination: loads are non-temporal, and so are the stores of
+// large copies; a copy of at most 64 MiB keeps its output in the caches for
+// the kernel that reads it next.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -82,7 +84,16 @@ template <> struct VecOf<8> { typedef u32x2_t T; };
 template <> struct VecOf<4> { typedef uint32_t T; };
 template <> struct VecOf<2> { typedef uint16_t T; };
 
-template <int VB>
+// NT: non-temporal stores (large copies); otherwise the copy stays in the
+// caches for the kernel that reads it next (a weight cut feeding a GEMM).
+template <int VB, bool NT>
+__device__ __forceinline__ void store_vec(typename VecOf<VB>::T v, char *p) {
+  typedef typename VecOf<VB>::T V;
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
+  else *reinterpret_cast<V *>(p) = v;
+}
+
+template <int VB, bool NT>
 __global__ void __launch_bounds__(kThreads) materialize_kernel(MatArgs a) {
   typedef typename VecOf<VB>::T V;
   const int s = blockIdx.y;
@@ -92,11 +103,11 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(MatArgs a) {
   for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < a.w.total_v; idx += stride) {
     const V v = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + box_offset<VB>(a.w, idx)));
     for (int d = d0; d < d1; ++d)
-      __builtin_nontemporal_store(v, reinterpret_cast<V *>(a.dst[d] + static_cast<int64_t>(idx) * VB));
+      store_vec<VB, NT>(v, a.dst[d] + static_cast<int64_t>(idx) * VB);
   }
 }
 
-template <int VB>
+template <int VB, bool NT>
 __global__ void __launch_bounds__(kThreads) gather_kernel(GatherArgs a) {
   typedef typename VecOf<VB>::T V;
   const int s = blockIdx.y;
@@ -106,7 +117,7 @@ __global__ void __launch_bounds__(kThreads) gather_kernel(GatherArgs a) {
   for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < a.w.total_v; idx += stride) {
     const V v = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + static_cast<int64_t>(idx) * VB));
     const int64_t off = base + box_offset<VB>(a.w, idx);
-    for (int d = 0; d < a.nout; ++d) __builtin_nontemporal_store(v, reinterpret_cast<V *>(a.out[d] + off));
+    for (int d = 0; d < a.nout; ++d) store_vec<VB, NT>(v, a.out[d] + off);
   }
 }
 
@@ -190,6 +201,17 @@ int fill_walk(const Geometry& g, int64_t esize, int vb, BoxWalk *w) {
   return TP_OK;
 }
 
+// Copies writing up to this many bytes keep their output in the caches (the
+// kernel that consumes it, e.g. the GEMM reading a freshly cut weight, runs
+// next); larger ones stream past the caches.
+constexpr int64_t kCachedCopyBytes = int64_t(64) << 20;
+
+template <class K, class Args>
+void launch_vb(K k_nt, K k_cached, bool nt, dim3 grid, hipStream_t s, const Args& a) {
+  if (nt) hipLaunchKernelGGL(k_nt, grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_cached, grid, dim3(kThreads), 0, s, a);
+}
+
 dim3 copy_grid(uint32_t total_v, int nshards) {
   const int64_t want = (static_cast<int64_t>(total_v) + kThreads - 1) / kThreads;
   const int64_t cap = std::max<int64_t>(1, (1 << 20) / nshards);
@@ -210,6 +232,7 @@ int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esi
   int rc = fill_walk(g, esize, vb, &a.w);
   if (rc != TP_OK) return rc;
   a.src = static_cast<const char *>(src);
+  const bool nt = static_cast<int64_t>(pieces.size()) * g.shard_elems * esize > kCachedCopyBytes;
 
   // Batch shards into launches bounded by the argument tables.
   int64_t k = 0;
@@ -230,10 +253,10 @@ int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esi
     const dim3 grid = copy_grid(a.w.total_v, ns);
     hipEvent_t t0 = timing_begin(stream);
     switch (vb) {
-      case 16: hipLaunchKernelGGL(materialize_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
-      case 8: hipLaunchKernelGGL(materialize_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL(materialize_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL(materialize_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+      case 16: launch_vb(materialize_kernel<16, true>, materialize_kernel<16, false>, nt, grid, stream, a); break;
+      case 8: launch_vb(materialize_kernel<8, true>, materialize_kernel<8, false>, nt, grid, stream, a); break;
+      case 4: launch_vb(materialize_kernel<4, true>, materialize_kernel<4, false>, nt, grid, stream, a); break;
+      default: launch_vb(materialize_kernel<2, true>, materialize_kernel<2, false>, nt, grid, stream, a); break;
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "materialize launch: %s", hipGetErrorString(e));
@@ -253,6 +276,7 @@ int shard_gather_launch(const ShardPlan& plan, const void *const *src, int64_t e
   GatherArgs a{};
   int rc = fill_walk(g, esize, vb, &a.w);
   if (rc != TP_OK) return rc;
+  const bool nt = nout * plan.nshards() * g.shard_elems * esize > kCachedCopyBytes;
 
   // Outputs in groups of kMaxDstPerLaunch (a shard is re-read per group),
   // shards in groups of kMaxShardsPerLaunch.
@@ -268,10 +292,10 @@ int shard_gather_launch(const ShardPlan& plan, const void *const *src, int64_t e
       const dim3 grid = copy_grid(a.w.total_v, ns);
       hipEvent_t t0 = timing_begin(stream);
       switch (vb) {
-        case 16: hipLaunchKernelGGL(gather_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL(gather_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL(gather_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+        case 16: launch_vb(gather_kernel<16, true>, gather_kernel<16, false>, nt, grid, stream, a); break;
+        case 8: launch_vb(gather_kernel<8, true>, gather_kernel<8, false>, nt, grid, stream, a); break;
+        case 4: launch_vb(gather_kernel<4, true>, gather_kernel<4, false>, nt, grid, stream, a); break;
+        default: launch_vb(gather_kernel<2, true>, gather_kernel<2, false>, nt, grid, stream, a); break;
       }
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return fail(TP_ERR_HIP, "gather launch: %s", hipGetErrorString(e));

@@ -92,7 +92,7 @@ __device__ __forceinline__ void store_lo(void *base, int64_t off, V v) {
   }
 }
 
-template <int VW, int UNROLL, int OP, bool BIAS, bool HI, int LO>
+template <int VW, int UNROLL, int OP, bool BIAS, bool HI, int LO, bool NT = true>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
   typedef typename FVec<VW>::T V;
   const uint32_t stride = gridDim.x * kThreads;
@@ -116,7 +116,8 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
           if (p0 + g < a.P && ok[u])
-            v[g][u] = __builtin_nontemporal_load(reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]));
+            v[g][u] = NT ? __builtin_nontemporal_load(reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]))
+                         : *reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]);
 #pragma unroll
       for (int g = 0; g < kGroup; ++g)
 #pragma unroll
@@ -135,7 +136,8 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
       const int64_t r = row[u] - static_cast<int64_t>(j) * a.rows_per_out;
       if constexpr (HI) {
         float *dst = a.out[j] + r * a.ld_out + static_cast<int64_t>(col[u]) * VW;
-        __builtin_nontemporal_store(acc[u], reinterpret_cast<V *>(dst));
+        if constexpr (NT) __builtin_nontemporal_store(acc[u], reinterpret_cast<V *>(dst));
+        else *reinterpret_cast<V *>(dst) = acc[u];
       }
       if constexpr (LO != 0) store_lo<LO>(a.lo, static_cast<int64_t>(row[u]) * a.ld_lo + static_cast<int64_t>(col[u]) * VW, acc[u]);
     }
@@ -183,10 +185,19 @@ int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int
   const int64_t want = (total_v + kThreads * kUnroll - 1) / (kThreads * kUnroll);
   const int64_t cap = max_wgs > 0 ? std::min<int64_t>(max_wgs, 1 << 20) : (1 << 20);
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>(want, cap)));
+  // Small reduces (inputs and outputs within kCachedBytes) use cached loads and
+  // stores: their inputs were just written or are still in the caches.
+  constexpr int64_t kCachedBytes = int64_t(128) << 20;
+  const bool nt = 4.0 * (P + nout) * static_cast<double>(rows) * cols > static_cast<double>(kCachedBytes);
   auto go = [&](auto vw, auto o, auto b, auto h, auto l) {
-    hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value,
-                                      decltype(h)::value, decltype(l)::value>),
-                       grid, dim3(kThreads), 0, stream, a);
+    if (nt)
+      hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value,
+                                        decltype(h)::value, decltype(l)::value, true>),
+                         grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value,
+                                        decltype(h)::value, decltype(l)::value, false>),
+                         grid, dim3(kThreads), 0, stream, a);
   };
   using std::integral_constant;
   // The second output exists for sums only (a layer's output feeding the next layer).

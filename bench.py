@@ -105,8 +105,8 @@ class MlpStep:
 
     def step(self):
         if self.split:
-            tp.tp_shard_materialize(self.A, self.sa, self.As, stream=self.s0)
-            tp.tp_shard_materialize(self.B, self.sb, self.Bs, stream=self.s0)
+            # both weight cuts in one batched call (one launch)
+            tp.tp_shard_materialize_batch([(self.A, self.sa, self.As), (self.B, self.sb, self.Bs)], stream=self.s0)
         tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
                          col_chunks=self.w.C, peer_partials=self.peers, Z_out=None if self.seq else self.Zo,
                          s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,

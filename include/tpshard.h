@@ -185,6 +185,30 @@ int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, i
                          const tp_layout *layout, void *const *dst, int64_t num_dst,
                          tp_stream_t stream);
 
+/* One tensor of tp_shard_materialize_batch: the arguments of
+ * tp_shard_materialize. */
+typedef struct {
+  const void *src;
+  int32_t dtype;
+  const int64_t *shape;
+  int64_t ndim;
+  const tp_layout *layout;
+  void *const *dst;
+  int64_t num_dst;
+} tp_materialize_item;
+
+/*
+ * tp_shard_materialize for several tensors (each with its own layout and
+ * destinations), e.g. the column and row cuts of both weights of a layer.
+ * Every item is validated before anything is enqueued; the shards are then
+ * packed into as few launches as possible (shards of up to four tensors share
+ * one), which saves the fixed cost of a launch per tensor.  No destination
+ * may overlap another destination or any item's source.  num_items = 0 is a
+ * no-op.
+ * Errors: as tp_shard_materialize, the message naming the item.
+ */
+int tp_shard_materialize_batch(const tp_materialize_item *items, int64_t num_items, tp_stream_t stream);
+
 /* ---- gather (the inverse of materialisation) ------------------------- */
 /*
  * Assemble the full row-major tensor of shape[ndim] from its per-device shards

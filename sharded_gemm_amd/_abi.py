@@ -37,7 +37,7 @@ TP_REDUCE_OP_MAX = 1
 TP_REDUCE_OP_MIN = 2
 
 # Every symbol include/tpshard.h declares.
-EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_binary", "tp_infer_matmul_dims_mapping", "tp_shard_materialize", "tp_shard_gather",
+EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_binary", "tp_infer_matmul_dims_mapping", "tp_shard_materialize", "tp_shard_materialize_batch", "tp_shard_gather",
            "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_stack", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
 TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather")
@@ -102,6 +102,11 @@ class tp_mlp_bwd_args(C.Structure):
                 ("seq_splits", C.c_int64), ("dZ_shards", C.POINTER(C.c_void_p)), ("dX_split", C.POINTER(C.c_void_p))]
 
 
+class tp_materialize_item(C.Structure):
+    _fields_ = [("src", C.c_void_p), ("dtype", C.c_int32), ("shape", C.POINTER(C.c_int64)), ("ndim", C.c_int64),
+                ("layout", C.POINTER(tp_layout)), ("dst", C.POINTER(C.c_void_p)), ("num_dst", C.c_int64)]
+
+
 class tp_kernel_stat(C.Structure):
     _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("min_ms", C.c_double),
                 ("max_ms", C.c_double), ("work", C.c_double)]
@@ -129,6 +134,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.tp_shard_materialize.restype = C.c_int
     lib.tp_shard_materialize.argtypes = [C.c_void_p, C.c_int32, i64p, C.c_int64, C.POINTER(tp_layout),
                                          C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
+    lib.tp_shard_materialize_batch.restype = C.c_int
+    lib.tp_shard_materialize_batch.argtypes = [C.POINTER(tp_materialize_item), C.c_int64, C.c_void_p]
     lib.tp_shard_gather.restype = C.c_int
     lib.tp_shard_gather.argtypes = [C.POINTER(C.c_void_p), C.c_int64, C.c_int32, i64p, C.c_int64, C.POINTER(tp_layout),
                                     C.POINTER(C.c_void_p), C.c_int64, C.c_void_p]
@@ -274,6 +281,27 @@ def tp_shard_materialize(src, layout: dict, dst, stream=None):
     _check(lib.tp_shard_materialize(C.c_void_p(_ptr(src)), _dtype_code(src), C.cast(shp, C.POINTER(C.c_int64)),
                                     src.dim(), C.byref(lay), C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst,
                                     _stream_ptr(stream)))
+
+
+def tp_shard_materialize_batch(jobs, stream=None):
+    """Several tp_shard_materialize calls in one: ``jobs`` is a list of
+    (src, layout, dst) with dst a dict or list (device id -> tensor)."""
+    lib = load()
+    keep, items = [], []
+    for src, layout, dst in jobs:
+        lay, k = make_layout(layout)
+        pairs = list(dst.items() if isinstance(dst, dict) else enumerate(dst))
+        num_dst = (max(d for d, _ in pairs) + 1) if pairs else 0
+        ptrs = (C.c_void_p * max(1, num_dst))()
+        for d, t in pairs:
+            ptrs[d] = _ptr(t) if t is not None else None
+        shp = _i64_array(src.shape)
+        keep += [lay, k, ptrs, shp]
+        items.append(tp_materialize_item(src=_ptr(src), dtype=_dtype_code(src), shape=C.cast(shp, C.POINTER(C.c_int64)),
+                                         ndim=src.dim(), layout=C.pointer(lay),
+                                         dst=C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst=num_dst))
+    arr = (tp_materialize_item * max(1, len(items)))(*items)
+    _check(lib.tp_shard_materialize_batch(arr, len(items), _stream_ptr(stream)))
 
 
 def tp_check_broadcast_binary(shape1, layout1: dict, shape2, layout2: dict):

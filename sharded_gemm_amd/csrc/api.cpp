@@ -333,36 +333,48 @@ int tp_layout_plan(const int64_t *shape, int64_t ndim, const tp_layout *layout, 
 
 int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, int64_t ndim,
                          const tp_layout *layout, void *const *dst, int64_t num_dst, tp_stream_t stream) {
+  const tp_materialize_item item{src, dtype, shape, ndim, layout, dst, num_dst};
+  return tp_shard_materialize_batch(&item, 1, stream);
+}
+
+int tp_shard_materialize_batch(const tp_materialize_item *items, int64_t num_items, tp_stream_t stream) {
   clear_error();
-  const int64_t esize = dtype_size(dtype);
-  if (!esize) return fail(TP_ERR_ARG, "unknown dtype %d", dtype);
-  ShardPlan plan;
-  int rc = build_plan(shape, ndim, layout, &plan);
-  if (rc != TP_OK) return rc;
-  int64_t numel = 1, shard_elems = 1;
-  for (int i = 0; i < plan.ndim; ++i) {
-    numel *= plan.shape[i];
-    shard_elems *= plan.extent[i];
-  }
-  if (!src && numel > 0) return fail(TP_ERR_ARG, "src is NULL");
-  if (plan.max_device >= num_dst)
-    return fail(TP_ERR_ARG, "num_dst = %lld but the layout names device %lld", (long long)num_dst, (long long)plan.max_device);
-  if (plan.max_device >= 0 && !dst) return fail(TP_ERR_ARG, "dst is NULL");
-  std::vector<int64_t> named;
-  for (const auto& grp : plan.devices)
-    for (int64_t d : grp) {
-      if (!dst[d] && shard_elems > 0) return fail(TP_ERR_ARG, "dst[%lld] is NULL", (long long)d);
-      named.push_back(d);
+  if (num_items < 0 || (num_items > 0 && !items)) return fail(TP_ERR_ARG, "need num_items >= 0 and an item array");
+  std::vector<ShardPlan> plans(static_cast<size_t>(num_items));
+  std::vector<MatJob> jobs;
+  std::vector<Buf> ins, outs;
+  for (int64_t i = 0; i < num_items; ++i) {
+    const tp_materialize_item& it = items[i];
+    const int64_t esize = dtype_size(it.dtype);
+    if (!esize) return fail(TP_ERR_ARG, "item %lld: unknown dtype %d", (long long)i, it.dtype);
+    ShardPlan& plan = plans[i];
+    int rc = build_plan(it.shape, it.ndim, it.layout, &plan);
+    if (rc != TP_OK) {
+      if (num_items == 1) return rc;
+      const std::string msg = tp_last_error();
+      return fail(rc, "item %lld: %s", (long long)i, msg.c_str());
     }
-  const int64_t src_bytes = numel * esize, shard_bytes = shard_elems * esize;
-  for (size_t i = 0; i < named.size(); ++i) {
-    if (overlaps(dst[named[i]], shard_bytes, src, src_bytes))
-      return fail(TP_ERR_ARG, "dst[%lld] overlaps src", (long long)named[i]);
-    for (size_t j = 0; j < i; ++j)
-      if (overlaps(dst[named[i]], shard_bytes, dst[named[j]], shard_bytes))
-        return fail(TP_ERR_ARG, "dst[%lld] overlaps dst[%lld]", (long long)named[i], (long long)named[j]);
+    int64_t numel = 1, shard_elems = 1;
+    for (int a = 0; a < plan.ndim; ++a) {
+      numel *= plan.shape[a];
+      shard_elems *= plan.extent[a];
+    }
+    if (!it.src && numel > 0) return fail(TP_ERR_ARG, "item %lld: src is NULL", (long long)i);
+    if (plan.max_device >= it.num_dst)
+      return fail(TP_ERR_ARG, "item %lld: num_dst = %lld but the layout names device %lld", (long long)i,
+                  (long long)it.num_dst, (long long)plan.max_device);
+    if (plan.max_device >= 0 && !it.dst) return fail(TP_ERR_ARG, "item %lld: dst is NULL", (long long)i);
+    for (const auto& grp : plan.devices)
+      for (int64_t d : grp) {
+        if (!it.dst[d] && shard_elems > 0) return fail(TP_ERR_ARG, "item %lld: dst[%lld] is NULL", (long long)i, (long long)d);
+        outs.push_back({it.dst[d], shard_elems * esize, "a destination"});
+      }
+    ins.push_back({it.src, numel * esize, "a source"});
+    jobs.push_back({&plan, it.src, esize, it.dst});
   }
-  return shard_materialize_launch(plan, src, esize, dst, static_cast<hipStream_t>(stream));
+  const int rc = check_disjoint(ins, outs);
+  if (rc != TP_OK) return rc;
+  return shard_materialize_batch_launch(jobs.data(), static_cast<int>(jobs.size()), static_cast<hipStream_t>(stream));
 }
 
 int tp_shard_gather(const void *const *src, int64_t num_src, int32_t dtype, const int64_t *shape, int64_t ndim,

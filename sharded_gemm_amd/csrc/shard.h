@@ -14,6 +14,18 @@ namespace tpshard {
 int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esize, void *const *dst,
                              hipStream_t stream);
 
+// One tensor of a batched materialisation.
+struct MatJob {
+  const ShardPlan *plan;
+  const void *src;
+  int64_t esize;
+  void *const *dst;
+};
+
+// shard_materialize_launch for several tensors at once, packed into as few
+// launches as the argument tables allow (shards of up to 4 tensors share one).
+int shard_materialize_batch_launch(const MatJob *jobs, int njobs, hipStream_t stream);
+
 // Writes the full tensor of `plan` into each of out[0..nout) from the shards:
 // shard k is read from src[first device of its group].  Arguments already
 // validated.  Returns TP_OK or a negative status.

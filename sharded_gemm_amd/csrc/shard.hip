@@ -34,6 +34,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxShardsPerLaunch = 32;
 constexpr int kMaxDstPerLaunch = 64;
+constexpr int kMaxWalksPerLaunch = 4;   // tensors (shard geometries) per materialize launch
 
 // Where the elements of one shard sit in the full tensor.
 struct BoxWalk {
@@ -60,9 +61,9 @@ __device__ __forceinline__ int64_t box_offset(const BoxWalk& w, uint32_t idx) {
 }
 
 struct MatArgs {
-  BoxWalk w;
-  const char *src;
-  int64_t src_base_b[kMaxShardsPerLaunch];   // byte offset of each shard's box origin
+  BoxWalk w[kMaxWalksPerLaunch];             // one per tensor in the launch
+  const char *src[kMaxShardsPerLaunch];      // each shard's box origin in its tensor
+  int32_t walk[kMaxShardsPerLaunch];         // which of w each shard follows
   int32_t dst_begin[kMaxShardsPerLaunch + 1];
   char *dst[kMaxDstPerLaunch];
 };
@@ -97,11 +98,12 @@ template <int VB, bool NT>
 __global__ void __launch_bounds__(kThreads) materialize_kernel(MatArgs a) {
   typedef typename VecOf<VB>::T V;
   const int s = blockIdx.y;
-  const char *src = a.src + a.src_base_b[s];
+  const char *src = a.src[s];
+  const BoxWalk& w = a.w[a.walk[s]];
   const int d0 = a.dst_begin[s], d1 = a.dst_begin[s + 1];
   const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < a.w.total_v; idx += stride) {
-    const V v = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + box_offset<VB>(a.w, idx)));
+  for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < w.total_v; idx += stride) {
+    const V v = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + box_offset<VB>(w, idx)));
     for (int d = d0; d < d1; ++d)
       store_vec<VB, NT>(v, a.dst[d] + static_cast<int64_t>(idx) * VB);
   }
@@ -220,37 +222,38 @@ dim3 copy_grid(uint32_t total_v, int nshards) {
 
 }  // namespace
 
-int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esize, void *const *dst,
-                             hipStream_t stream) {
-  const Geometry g = geometry(plan);
-  if (g.shard_elems == 0 || plan.nshards() == 0) return TP_OK;
-  std::vector<const void *> pieces;
-  for (const auto& grp : plan.devices)
-    for (int64_t d : grp) pieces.push_back(dst[d]);
-  const int vb = vector_bytes(plan, g, esize, src, pieces);
-  MatArgs a{};
-  int rc = fill_walk(g, esize, vb, &a.w);
-  if (rc != TP_OK) return rc;
-  a.src = static_cast<const char *>(src);
-  const bool nt = static_cast<int64_t>(pieces.size()) * g.shard_elems * esize > kCachedCopyBytes;
+int shard_materialize_batch_launch(const MatJob *jobs, int njobs, hipStream_t stream) {
+  std::vector<Geometry> geo;
+  std::vector<int> live;
+  int vb = 16;
+  int64_t written = 0;
+  for (int j = 0; j < njobs; ++j) {
+    const MatJob& jb = jobs[j];
+    geo.push_back(geometry(*jb.plan));
+    if (geo.back().shard_elems == 0 || jb.plan->nshards() == 0) continue;
+    std::vector<const void *> pieces;
+    for (const auto& grp : jb.plan->devices)
+      for (int64_t d : grp) pieces.push_back(jb.dst[d]);
+    vb = std::min(vb, vector_bytes(*jb.plan, geo.back(), jb.esize, jb.src, pieces));
+    written += static_cast<int64_t>(pieces.size()) * geo.back().shard_elems * jb.esize;
+    live.push_back(j);
+  }
+  if (live.empty()) return TP_OK;
+  std::vector<BoxWalk> walks(static_cast<size_t>(njobs));
+  for (int j : live) {
+    const int rc = fill_walk(geo[j], jobs[j].esize, vb, &walks[j]);
+    if (rc != TP_OK) return rc;
+  }
+  const bool nt = written > kCachedCopyBytes;
 
-  // Batch shards into launches bounded by the argument tables.
-  int64_t k = 0;
-  while (k < plan.nshards()) {
-    int ns = 0, nd = 0;
-    a.dst_begin[0] = 0;
-    while (k < plan.nshards() && ns < kMaxShardsPerLaunch) {
-      const auto& grp = plan.devices[k];
-      if (nd + static_cast<int>(grp.size()) > kMaxDstPerLaunch) {
-        if (ns > 0) break;
-        return fail(TP_ERR_UNSUPPORTED, "a shard is replicated to more than %d devices", kMaxDstPerLaunch);
-      }
-      a.src_base_b[ns] = box_origin(plan, g, k) * esize;
-      for (int64_t d : grp) a.dst[nd++] = static_cast<char *>(dst[d]);
-      a.dst_begin[++ns] = nd;
-      ++k;
-    }
-    const dim3 grid = copy_grid(a.w.total_v, ns);
+  // Pack shards (of one or several tensors) into launches bounded by the argument tables.
+  MatArgs a{};
+  int ns = 0, nd = 0, nw = 0, walk_job[kMaxWalksPerLaunch] = {};
+  uint32_t max_v = 0;
+  double bytes = 0;
+  auto flush = [&]() -> int {
+    if (ns == 0) return TP_OK;
+    const dim3 grid = copy_grid(max_v, ns);
     hipEvent_t t0 = timing_begin(stream);
     switch (vb) {
       case 16: launch_vb(materialize_kernel<16, true>, materialize_kernel<16, false>, nt, grid, stream, a); break;
@@ -260,9 +263,51 @@ int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esi
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "materialize launch: %s", hipGetErrorString(e));
-    timing_end(t0, stream, TP_KERNEL_MATERIALIZE, static_cast<double>(ns + nd) * g.shard_elems * esize);
+    timing_end(t0, stream, TP_KERNEL_MATERIALIZE, bytes);
+    ns = nd = nw = 0;
+    max_v = 0;
+    bytes = 0;
+    a.dst_begin[0] = 0;
+    return TP_OK;
+  };
+  a.dst_begin[0] = 0;
+  for (int j : live) {
+    const MatJob& jb = jobs[j];
+    const ShardPlan& plan = *jb.plan;
+    const int64_t shard_bytes = geo[j].shard_elems * jb.esize;
+    for (int64_t k = 0; k < plan.nshards(); ++k) {
+      const auto& grp = plan.devices[k];
+      if (static_cast<int>(grp.size()) > kMaxDstPerLaunch)
+        return fail(TP_ERR_UNSUPPORTED, "a shard is replicated to more than %d devices", kMaxDstPerLaunch);
+      int wi = -1;
+      for (int q = 0; q < nw; ++q)
+        if (walk_job[q] == j) wi = q;
+      if (ns == kMaxShardsPerLaunch || nd + static_cast<int>(grp.size()) > kMaxDstPerLaunch ||
+          (wi < 0 && nw == kMaxWalksPerLaunch)) {
+        const int rc = flush();
+        if (rc != TP_OK) return rc;
+        wi = -1;
+      }
+      if (wi < 0) {
+        wi = nw++;
+        walk_job[wi] = j;
+        a.w[wi] = walks[j];
+        max_v = std::max(max_v, walks[j].total_v);
+      }
+      a.src[ns] = static_cast<const char *>(jb.src) + box_origin(plan, geo[j], k) * jb.esize;
+      a.walk[ns] = wi;
+      for (int64_t d : grp) a.dst[nd++] = static_cast<char *>(jb.dst[d]);
+      a.dst_begin[++ns] = nd;
+      bytes += static_cast<double>(1 + grp.size()) * shard_bytes;
+    }
   }
-  return TP_OK;
+  return flush();
+}
+
+int shard_materialize_launch(const ShardPlan& plan, const void *src, int64_t esize, void *const *dst,
+                             hipStream_t stream) {
+  const MatJob job{&plan, src, esize, dst};
+  return shard_materialize_batch_launch(&job, 1, stream);
 }
 
 int shard_gather_launch(const ShardPlan& plan, const void *const *src, int64_t esize, void *const *out, int64_t nout,

@@ -382,3 +382,26 @@ def test_group_beyond_launch_table_is_rejected():
     dst = (C.c_void_p * 65)(*[FAKE + (d + 1) * (1 << 20) for d in range(65)])
     assert lib.tp_shard_materialize(C.c_void_p(FAKE), _abi.TP_F32, C.cast(shape, C.POINTER(C.c_int64)), 1,
                                     C.byref(lay), C.cast(dst, C.POINTER(C.c_void_p)), 65, None) == _abi.TP_ERR_UNSUPPORTED
+
+
+def test_materialize_batch_validation():
+    lib = _abi.load()
+    spec = {"device": [0, 1], "sharded_dim": [{"axis": 0, "num_shards": 2}]}
+    lay, keep = _abi.make_layout(spec)
+    shape = (C.c_int64 * 2)(4, 4)
+    d1 = (C.c_void_p * 2)(FAKE + (1 << 20), FAKE + (2 << 20))
+    d2 = (C.c_void_p * 2)(FAKE + (3 << 20), FAKE + (4 << 20))
+
+    def item(src, dst, dtype=_abi.TP_F32):
+        return _abi.tp_materialize_item(src=src, dtype=dtype, shape=C.cast(shape, C.POINTER(C.c_int64)), ndim=2,
+                                        layout=C.pointer(lay), dst=C.cast(dst, C.POINTER(C.c_void_p)), num_dst=2)
+    arr = (_abi.tp_materialize_item * 2)(item(FAKE, d1), item(FAKE + (5 << 20), d2, dtype=9))
+    assert lib.tp_shard_materialize_batch(arr, 2, None) == _abi.TP_ERR_ARG            # item 1: bad dtype
+    assert "item 1" in lib.tp_last_error().decode()
+    arr = (_abi.tp_materialize_item * 2)(item(FAKE, d1), item(FAKE + (1 << 20) + 8, d2))
+    assert lib.tp_shard_materialize_batch(arr, 2, None) == _abi.TP_ERR_ARG            # item 1 reads item 0's output
+    dsame = (C.c_void_p * 2)(FAKE + (1 << 20), FAKE + (6 << 20))
+    arr = (_abi.tp_materialize_item * 2)(item(FAKE, d1), item(FAKE + (5 << 20), dsame))
+    assert lib.tp_shard_materialize_batch(arr, 2, None) == _abi.TP_ERR_ARG            # two items write one buffer
+    assert lib.tp_shard_materialize_batch(None, 1, None) == _abi.TP_ERR_ARG
+    assert lib.tp_shard_materialize_batch(arr, -1, None) == _abi.TP_ERR_ARG

@@ -200,3 +200,48 @@ def test_rank8_many_shards_and_replicas():
     announce("layout rank 8, 256 shards x 2 replicas")
     src = inputs.normal(shape, seed=7900)
     _compare_with_oracle(src, _run(src, spec, torch.float32), L.split(src, spec))
+
+
+def test_batch_equals_single_calls_and_oracle():
+    """Several tensors in one tp_shard_materialize_batch call (mixed dtypes and
+    layouts, six tensors so that the packing spills over launches): every
+    destination equals the oracle's split."""
+    announce("layout batch of 6 tensors")
+    jobs, refs = [], []
+    specs = [
+        ((768, 3072), {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 1, "num_shards": 4}]}, "bf16"),
+        ((3072, 768), {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 0, "num_shards": 4}]}, "bf16"),
+        ((6, 4, 10), {"device": list(range(10)), "sharded_dim": [{"axis": 2, "num_shards": 5}, {"axis": 0, "num_shards": 2}]}, "f32"),
+        ((2, 2, 2, 2, 2, 2, 2, 64), {"device": list(range(128)), "sharded_dim": [{"axis": a, "num_shards": 2} for a in range(7)]}, "f32"),
+        ((33, 7, 64), {"device": [-1, -2, -3], "device_map": {-1: [0, 5], -2: [1, 4], -3: [2, 3]},
+                       "sharded_dim": [{"axis": 0, "num_shards": 3}]}, "bf16"),
+        ((4, 4), {"device": [-1], "device_map": {-1: [0, 1, 2]}, "sharded_dim": []}, "f32"),
+    ]
+    for i, (shape, spec, dt) in enumerate(specs):
+        src = inputs.normal(shape, seed=9800 + i, dtype=dt)
+        ref = L.split(src, spec)
+        dst = {d: Guarded(v.shape, src.dtype) for d, v in ref.items()}
+        jobs.append((src.cuda(), spec, {d: g.t for d, g in dst.items()}))
+        refs.append((src, ref, dst))
+    tp.tp_shard_materialize_batch(jobs)
+    torch.cuda.synchronize()
+    for src, ref, dst in refs:
+        for d, g in dst.items():
+            assert g.guards_intact()
+        _compare_with_oracle(src, {d: g.t.cpu() for d, g in dst.items()}, ref)
+
+
+def test_batch_error_leaves_every_item_untouched():
+    announce("layout batch error path")
+    ok_src = torch.arange(16, dtype=torch.float32, device="cuda").view(4, 4)
+    ok_out = {d: Guarded((2, 4), torch.float32) for d in range(2)}
+    bad_src = torch.arange(12, dtype=torch.float32, device="cuda").view(3, 4)
+    bad_out = {d: Guarded((1, 4), torch.float32) for d in range(2)}
+    spec = {"device": [0, 1], "sharded_dim": [{"axis": 0, "num_shards": 2}]}
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_shard_materialize_batch([(ok_src, spec, {d: g.t for d, g in ok_out.items()}),
+                                       (bad_src, spec, {d: g.t for d, g in bad_out.items()})])
+    assert e.value.kind == "indivisible"
+    torch.cuda.synchronize()
+    for g in list(ok_out.values()) + list(bad_out.values()):
+        assert g.body_untouched() and g.guards_intact()

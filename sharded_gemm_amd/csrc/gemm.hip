@@ -693,10 +693,12 @@ __device__ __forceinline__ void barrier_vm_n(int n) {
   }
 }
 
-// The ping-pong kernel: 8 waves (2 x 4), BK = 64 or 32, S slots.
-template <int BM, int BN, int EPI, bool AT, bool WT, int BK = 64, int S = 2>
+// The ping-pong kernel: 8 waves (WGM x 8/WGM), BK = 64 or 32, S slots.  Waves
+// 0-3 form the group that issues the DMA, waves 4-7 the other; wave w runs on
+// SIMD w % 4, so each SIMD holds one wave of each group in either layout.
+template <int BM, int BN, int EPI, bool AT, bool WT, int BK = 64, int S = 2, int WGM = 2>
 __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
-  using C = DmaCfg<BM, BN, BK, S, AT, WT, 2, 4>;
+  using C = DmaCfg<BM, BN, BK, S, AT, WT, WGM, 8 / WGM>;
   using TA = typename C::TA;
   using TW = typename C::TW;
   constexpr int KK = C::KK;
@@ -707,8 +709,8 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[S * C::STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / 4, wn = wave % 4;
-  const bool grpA = wm == 0;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const bool grpA = wave < 4;
   const int tiles_m = static_cast<int>((p.M + BM - 1) / BM);
   const int tiles_n = static_cast<int>((p.N + BN - 1) / BN);
   int tm, tn;
@@ -897,10 +899,10 @@ hipError_t launch_dma(const GemmArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int EPI, bool AT, bool WT, int BK = 64, int S = 2>
+template <int BM, int BN, int EPI, bool AT, bool WT, int BK = 64, int S = 2, int WGM = 2>
 hipError_t launch_pp(const GemmArgs& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((bf16_gemm_pp<BM, BN, EPI, AT, WT, BK, S>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((bf16_gemm_pp<BM, BN, EPI, AT, WT, BK, S, WGM>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
@@ -950,8 +952,14 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   if (c192 == best) return launch_pp<256, 192, EPI, AT, WT>(p, s);
   // 256 x 128 tiles: the ping-pong kernel where its 32-bit offsets reach
   // (measured 10-12% faster than the single-group kernel on 4096 x 2048 x 4096).
+  // With an operand read transposed (the backward's GEMMs) 4 x 2 waves, whose
+  // 64 x 64 wave tiles read a fifth fewer LDS bytes, are 7-11% faster; the
+  // forward keeps 2 x 4.
   if (c128w == best) {
-    if (off32) return launch_pp<256, 128, EPI, AT, WT>(p, s);
+    if (off32) {
+      if constexpr (AT || WT) return launch_pp<256, 128, EPI, AT, WT, 64, 2, 4>(p, s);
+      return launch_pp<256, 128, EPI, AT, WT>(p, s);
+    }
     return launch_dma<256, 128, 64, 3, EPI, AT, WT>(p, s);
   }
   return launch_dma<128, 128, 32, 8, EPI, AT, WT>(p, s);

@@ -949,7 +949,11 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   const double best = std::min(std::min(c256, c192), std::min(c128w, c128));
   if constexpr (big_ok)
     if (c256 == best) return launch_pp<256, 256, EPI, AT, WT>(p, s);
-  if (c192 == best) return launch_pp<256, 192, EPI, AT, WT>(p, s);
+  if (c192 == best) {
+    // A read transposed (weight gradients): 4 x 2 waves, 2-3% faster.
+    if constexpr (AT) return launch_pp<256, 192, EPI, AT, WT, 64, 2, 4>(p, s);
+    else return launch_pp<256, 192, EPI, AT, WT>(p, s);
+  }
   // 256 x 128 tiles: the ping-pong kernel where its 32-bit offsets reach
   // (measured 10-12% faster than the single-group kernel on 4096 x 2048 x 4096).
   // With an operand read transposed (the backward's GEMMs) 4 x 2 waves, whose
@@ -958,7 +962,7 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   if (c128w == best) {
     if (off32) {
       if constexpr (AT || WT) return launch_pp<256, 128, EPI, AT, WT, 64, 2, 4>(p, s);
-      return launch_pp<256, 128, EPI, AT, WT>(p, s);
+      else return launch_pp<256, 128, EPI, AT, WT>(p, s);
     }
     return launch_dma<256, 128, 64, 3, EPI, AT, WT>(p, s);
   }

@@ -86,6 +86,8 @@ def _f64(t):
     (4096, 256, 6144, 2, 2),
     # every GEMM on the ping-pong kernel's 256 x 128 tiles (dA, dB with A transposed; accumulating for R = 2)
     (4000, 2000, 2000, 1, 2), (4000, 2000, 2000, 2, 2),
+    # dA on 256 x 192 tiles with A transposed, accumulating over two chunks
+    (512, 2048, 6144, 2, 2),
 ])
 def test_backward_integer_exact(M, H, F, Rc, P):
     """One-hot A_i (columns) and B_i (rows) keep every value a small integer:

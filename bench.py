@@ -103,15 +103,24 @@ class MlpStep:
     def result(self):
         return self.Zs[-1] if self.seq else self.Zo
 
-    def step(self):
+    def prepare(self):
+        """Marshal the step's library calls once (the buffers never move)."""
+        self.cut = None
         if self.split:
             # both weight cuts in one batched call (one launch)
-            tp.tp_shard_materialize_batch([(self.A, self.sa, self.As), (self.B, self.sb, self.Bs)], stream=self.s0)
-        tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
-                         col_chunks=self.w.C, peer_partials=self.peers, Z_out=None if self.seq else self.Zo,
-                         s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
-                         reduce_workgroups=self.reduce_wgs, X_shards=self.Xb if self.seq else None,
-                         Z_split=self.Zs if self.seq else None)
+            self.cut = tp.tp_shard_materialize_batch([(self.A, self.sa, self.As), (self.B, self.sb, self.Bs)],
+                                                     stream=self.s0, prepare=True)
+        self.mlp = tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
+                                    col_chunks=self.w.C, peer_partials=self.peers,
+                                    Z_out=None if self.seq else self.Zo, s_compute=self.s0,
+                                    s_reduce=self.s0 if self.serial else self.s1,
+                                    reduce_workgroups=self.reduce_wgs, X_shards=self.Xb if self.seq else None,
+                                    Z_split=self.Zs if self.seq else None, prepare=True)
+
+    def step(self):
+        if self.cut is not None:
+            self.cut()
+        self.mlp()
 
     @property
     def work(self):
@@ -607,6 +616,8 @@ def main():
     log(f"[bench] workload {args.workload}: setting up")
     wl = WORKLOADS[args.workload]()
     wl.serial, wl.reduce_wgs = args.serial, args.reduce_wgs
+    if hasattr(wl, "prepare"):
+        wl.prepare()
     dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

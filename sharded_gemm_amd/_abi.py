@@ -283,9 +283,26 @@ def tp_shard_materialize(src, layout: dict, dst, stream=None):
                                     _stream_ptr(stream)))
 
 
-def tp_shard_materialize_batch(jobs, stream=None):
+class Prepared:
+    """A library call whose arguments were marshalled once: calling it passes
+    the same argument structures again (the tensors they point to must stay
+    alive and in place), so a loop pays one C call per launch sequence."""
+
+    def __init__(self, fn, args, keep, streams):
+        self._fn, self._args, self._keep, self._streams = fn, args, keep, streams
+
+    def __call__(self, *streams):
+        ptrs = [_stream_ptr(s) for s in streams] if streams else self._streams
+        if len(ptrs) < len(self._streams):
+            ptrs = list(ptrs) + [ptrs[-1]] * (len(self._streams) - len(ptrs))
+        _check(self._fn(*self._args, *ptrs))
+
+
+def tp_shard_materialize_batch(jobs, stream=None, prepare=False):
     """Several tp_shard_materialize calls in one: ``jobs`` is a list of
-    (src, layout, dst) with dst a dict or list (device id -> tensor)."""
+    (src, layout, dst) with dst a dict or list (device id -> tensor).  With
+    ``prepare=True`` nothing runs; a ``Prepared`` call taking the stream is
+    returned."""
     lib = load()
     keep, items = [], []
     for src, layout, dst in jobs:
@@ -301,6 +318,8 @@ def tp_shard_materialize_batch(jobs, stream=None):
                                          ndim=src.dim(), layout=C.pointer(lay),
                                          dst=C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst=num_dst))
     arr = (tp_materialize_item * max(1, len(items)))(*items)
+    if prepare:
+        return Prepared(lib.tp_shard_materialize_batch, (arr, len(items)), keep, [_stream_ptr(stream)])
     _check(lib.tp_shard_materialize_batch(arr, len(items), _stream_ptr(stream)))
 
 
@@ -447,7 +466,7 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
     return args, [parr, xs, zs]
 
 
-def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, **kw):
+def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, prepare=False, **kw):
     """One rank's MLP share: Y_ws = act(X A_i); Z_i = Y_ws B_i; Z_out = Z_i + sum(peers) (+ bias);
     optionally H_out = X A_i (the pre-activation kept for the backward) and X_next = the
     sum rounded to the input dtype (the next layer's input).
@@ -456,11 +475,14 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, **kw
     bias, X_shards, Z_split, X_next.  Sequence parallelism: with ``X_shards`` (S tensors
     [M/S, H]) X is a workspace the call fills by all-gathering them; with ``Z_split``
     (S tensors [M/S, H] fp32) the sum is reduce-scattered into the blocks instead of
-    written to Z_out."""
+    written to Z_out.  With ``prepare=True`` nothing runs; a ``Prepared`` call taking
+    (s_compute, s_reduce) is returned."""
     lib = load()
     args, keep = _mlp_args(X, A_i, B_i, Y_ws, Z_i, **kw)
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
+    if prepare:
+        return Prepared(lib.tp_colrow_mlp, (C.byref(args),), keep + [args], [sc, sr])
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
 
 

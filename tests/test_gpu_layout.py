@@ -245,3 +245,18 @@ def test_batch_error_leaves_every_item_untouched():
     torch.cuda.synchronize()
     for g in list(ok_out.values()) + list(bad_out.values()):
         assert g.body_untouched() and g.guards_intact()
+
+
+def test_prepared_batch_replays():
+    announce("layout prepared batch")
+    A = inputs.normal((768, 3072), seed=9900, dtype="bf16").cuda()
+    sa = {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 1, "num_shards": 4}]}
+    outs = {d: torch.empty((768, 768), dtype=torch.bfloat16, device="cuda") for d in range(4)}
+    call = tp.tp_shard_materialize_batch([(A, sa, outs)], prepare=True)
+    ref = L.split(A.cpu(), sa)
+    for _ in range(2):
+        for o in outs.values():
+            o.zero_()
+        call(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        _compare_with_oracle(A.cpu(), {d: o.cpu() for d, o in outs.items()}, ref)

@@ -301,3 +301,27 @@ def test_max_ranks_integer_exact():
                         act=tp.TP_ACT_NONE, two_streams=True)
     z_ref = O.mlp_rank(X, A, B, O.GELU_NONE)
     assert np.array_equal(Zo.numpy().astype(np.float64), R.reduce_full([z_ref] + peers_cpu))
+
+
+def test_prepared_call_matches_direct_call():
+    """A call marshalled once (prepare=True) and replayed gives the same bits as
+    the direct call, on each replay."""
+    announce("mlp prepared call")
+    M, H, F = 512, 384, 256
+    X = inputs.normal((M, H), seed=291, dtype="bf16").cuda()
+    A = inputs.normal((H, F), seed=292, std=0.05, dtype="bf16").cuda()
+    B = inputs.normal((F, H), seed=293, std=0.05, dtype="bf16").cuda()
+    peer = inputs.normal((M, H), seed=294).cuda()
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    Zo = torch.empty((M, H), device="cuda")
+    tp.tp_colrow_mlp(X, A, B, Y, Z, row_chunks=2, peer_partials=[peer], Z_out=Zo)
+    torch.cuda.synchronize()
+    ref = Zo.clone()
+    call = tp.tp_colrow_mlp(X, A, B, Y, Z, row_chunks=2, peer_partials=[peer], Z_out=Zo, prepare=True)
+    s1 = torch.cuda.Stream()
+    for _ in range(3):
+        Zo.zero_()
+        call(torch.cuda.current_stream(), s1)
+        torch.cuda.synchronize()
+        assert torch.equal(Zo.view(torch.int32), ref.view(torch.int32))

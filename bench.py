@@ -230,13 +230,16 @@ class BwdStep:
     def result(self):
         return self.dA
 
+    def prepare(self):
+        """Marshal the step's library call once (the buffers never move)."""
+        self.call = tp.tp_colrow_mlp_backward(
+            self.X, self.As[0], self.Bs[0], self.Hs, self.Y, self.dZ, self.dH, self.dX, self.dA, self.dB,
+            row_chunks=self.w.R, peer_dX=self.peers, dX_out=None if self.seq else self.dXo, s_compute=self.s0,
+            s_reduce=self.s0 if self.serial else self.s1, reduce_workgroups=self.reduce_wgs,
+            dZ_shards=self.dZb if self.seq else None, dX_split=self.dXs if self.seq else None, prepare=True)
+
     def step(self):
-        tp.tp_colrow_mlp_backward(self.X, self.As[0], self.Bs[0], self.Hs, self.Y, self.dZ, self.dH, self.dX,
-                                  self.dA, self.dB, row_chunks=self.w.R, peer_dX=self.peers,
-                                  dX_out=None if self.seq else self.dXo,
-                                  s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
-                                  reduce_workgroups=self.reduce_wgs, dZ_shards=self.dZb if self.seq else None,
-                                  dX_split=self.dXs if self.seq else None)
+        self.call()
 
     @property
     def work(self):
@@ -326,9 +329,14 @@ class StackStep:
     def result(self):
         return self.layers[-1]["Z_out"]
 
+    def prepare(self):
+        """Marshal the step's library call once (the buffers never move)."""
+        self.call = tp.tp_colrow_mlp_stack([dict(l, reduce_workgroups=self.reduce_wgs) for l in self.layers],
+                                           s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
+                                           prepare=True)
+
     def step(self):
-        tp.tp_colrow_mlp_stack([dict(l, reduce_workgroups=self.reduce_wgs) for l in self.layers], s_compute=self.s0,
-                               s_reduce=self.s0 if self.serial else self.s1)
+        self.call()
 
     @property
     def work(self):

@@ -486,7 +486,7 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, prep
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
 
 
-def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None):
+def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None, prepare=False):
     """Forward layers in sequence with the inter-layer overlap; ``layers`` is a list
     of dicts of tp_colrow_mlp's arguments (X, A_i, B_i, Y_ws, Z_i and keywords), each
     layer but the last writing the next one's X through X_next."""
@@ -495,12 +495,14 @@ def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None):
     arr = (tp_mlp_args * max(1, len(built)))(*[b[0] for b in built])
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
+    if prepare:
+        return Prepared(lib.tp_colrow_mlp_stack, (arr, len(built)), [built], [sc, sr])
     _check(lib.tp_colrow_mlp_stack(arr, len(built), sc, sr))
 
 
 def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *, row_chunks=1, peer_dX=(),
                            dX_out=None, act=TP_ACT_GELU_ERF, accumulate=False, s_compute=None, s_reduce=None,
-                           reduce_workgroups=0, dZ_shards=None, dX_split=None):
+                           reduce_workgroups=0, dZ_shards=None, dX_split=None, prepare=False):
     """Backward of one rank's MLP share: dH_ws = (dZ B_i^T) * act'(H_i); dX_i = dH_ws A_i^T;
     dX_out = dX_i + sum(peers); dA_i (+)= X^T dH_ws; dB_i (+)= Y_i^T dZ.
 
@@ -536,6 +538,8 @@ def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *
     args.seq_splits, args.dZ_shards, args.dX_split = S, gs, xs
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
+    if prepare:
+        return Prepared(lib.tp_colrow_mlp_backward, (C.byref(args),), [args, parr, gs, xs], [sc, sr])
     _check(lib.tp_colrow_mlp_backward(C.byref(args), sc, sr))
 
 

@@ -243,3 +243,30 @@ def test_backward_error_path():
     torch.cuda.synchronize()
     for g in (dH, dX, dA, dB):
         assert g.body_untouched() and g.guards_intact()
+
+
+def test_prepared_backward_replays():
+    """A backward call marshalled once (prepare=True) and replayed twice, its
+    outputs overwritten between the replays, gives the direct call's bits."""
+    announce("backward prepared call")
+    M, H, F, P = 1024, 512, 384, 3
+    X = inputs.normal((M, H), 601, 1.0, "bf16").cuda()
+    A = inputs.normal((H, F), 602, 1.0 / np.sqrt(H), "bf16").cuda()
+    B = inputs.normal((F, H), 603, 1.0 / np.sqrt(F), "bf16").cuda()
+    dZ = inputs.normal((M, H), 604, 1.0, "bf16").cuda()
+    peers = [inputs.normal((M, H), 610 + p).cuda() for p in range(P - 1)]
+    Y, Hs = forward(X, A, B)
+    ref = backward(X, A, B, Hs, Y, dZ, R=2, peers=peers)
+    outs = [torch.empty((M, F), dtype=torch.bfloat16, device="cuda"), torch.empty((M, H), device="cuda"),
+            torch.empty((M, H), device="cuda"), torch.empty((H, F), device="cuda"), torch.empty((F, H), device="cuda")]
+    dH, dX, dXo, dA, dB = outs
+    call = tp.tp_colrow_mlp_backward(X, A, B, Hs, Y, dZ, dH, dX, dA, dB, row_chunks=2, peer_dX=peers, dX_out=dXo,
+                                     s_compute=torch.cuda.current_stream(), s_reduce=torch.cuda.Stream(),
+                                     prepare=True)
+    for _ in range(2):
+        for o in outs:
+            o.fill_(float("nan"))
+        call()
+        torch.cuda.synchronize()
+        for a, b in zip([o.cpu() for o in outs], ref):
+            assert np.array_equal(bits(a), bits(b))

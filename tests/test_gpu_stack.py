@@ -43,8 +43,10 @@ def _layers_integer(M, H, Fs, P, seed):
     return out
 
 
-def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, keep_z=True):
-    """The stack on the GPU into guarded buffers; returns per layer (Z_out, X_next) CPU copies."""
+def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, keep_z=True, prepared=False):
+    """The stack on the GPU into guarded buffers; returns per layer (Z_out, X_next)
+    CPU copies.  prepared: marshal the call once and replay it twice, the
+    outputs overwritten with NaN in between."""
     M, H = X0.shape
     dt = X0.dtype
     xs = [X0.cuda()] + [Guarded((M, H), dt) for _ in layers]
@@ -62,7 +64,14 @@ def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, kee
                          X_next=xs[l + 1].t))
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream() if two_streams else s0
-    tp.tp_colrow_mlp_stack(args, s_compute=s0, s_reduce=s1)
+    if prepared:
+        call = tp.tp_colrow_mlp_stack(args, s_compute=s0, s_reduce=s1, prepare=True)
+        for _ in range(2):
+            for t in xs[1:] + (zs if keep_z else []):
+                t.t.fill_(float("nan"))
+            call()
+    else:
+        tp.tp_colrow_mlp_stack(args, s_compute=s0, s_reduce=s1)
     torch.cuda.synchronize()
     res = []
     for l in range(len(layers)):
@@ -121,6 +130,22 @@ def test_stack_equals_layer_by_layer_calls_bitwise():
         x = xn
     ref = O.mlp_stack(X0, layers, dtype="bf16")
     assert rel_err(got[-1][0], ref[-1][0]) <= TOL_BF16
+
+
+def test_prepared_stack_replays():
+    """The stack marshalled once (prepare=True) and replayed gives the direct call's bits."""
+    announce("stack prepared call")
+    M, H, F, P = 1024, 256, 192, 3
+    X0 = inputs.normal((M, H), seed=1601, dtype="bf16")
+    layers = [{"A_i": inputs.normal((H, F), seed=1610 + l, std=0.05, dtype="bf16"),
+               "B_i": inputs.normal((F, H), seed=1620 + l, std=0.05, dtype="bf16"),
+               "peers": [inputs.normal((M, H), seed=1630 + 10 * l + p) for p in range(P - 1)],
+               "bias": inputs.normal((H,), seed=1650 + l)} for l in range(2)]
+    ref = run_stack(X0, layers, R=2, act=tp.TP_ACT_GELU_ERF)
+    got = run_stack(X0, layers, R=2, act=tp.TP_ACT_GELU_ERF, prepared=True)
+    for (z, xn), (zr, xr) in zip(got, ref):
+        assert np.array_equal(bits(z), bits(zr))
+        assert np.array_equal(bits(xn), bits(xr))
 
 
 def test_x_next_only_and_fp32():

@@ -65,11 +65,14 @@ __device__ __forceinline__ V combine(V acc, V v) {
   }
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 in one word (lo in the low half), round to nearest,
+// ties to even, a NaN kept a NaN with its quiet bit set: gfx950's packed
+// conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // LO: 0 no second output, 1 bf16 copy, 2 fp32 copy.  HI: write the fp32 result.
@@ -81,12 +84,12 @@ __device__ __forceinline__ void store_lo(void *base, int64_t off, V v) {
     *reinterpret_cast<V *>(static_cast<float *>(base) + off) = v;
   } else if constexpr (LO == 1) {
     if constexpr (sizeof(V) == sizeof(float)) {
-      static_cast<uint16_t *>(base)[off] = static_cast<uint16_t>(bf16_rne(v));
+      static_cast<uint16_t *>(base)[off] = static_cast<uint16_t>(bf16_pack2(v, 0.f) & 0xffffu);
     } else {
       typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
       u32x2_t w;
-      w[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-      w[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+      w[0] = bf16_pack2(v[0], v[1]);
+      w[1] = bf16_pack2(v[2], v[3]);
       *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(base) + off) = w;
     }
   }

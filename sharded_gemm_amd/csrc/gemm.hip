@@ -834,16 +834,20 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
 }
 
 // ---- plain fp32 kernel (tiny fp32 workload) ------------------------------
-// 64 x 64 tile, 256 threads of 4 x 4 outputs, K staged 16 at a time; any
-// operand layout (element strides).
+// 32 x 32 tile, 256 threads of 2 x 2 outputs, K staged 64 at a time through
+// LDS with the next slab's loads in flight (registers) while the current one
+// is consumed; any operand layout (element strides).  The small tile gives the
+// fp32 problems here (a few hundred rows and columns) enough workgroups; every
+// output still accumulates k in ascending order with one fma per k.
 
-constexpr int kF32Tile = 64;
-constexpr int kF32BK = 16;
+constexpr int kF32Tile = 32;
+constexpr int kF32BK = 64;
 
 template <int EPI>
 __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
-  __shared__ float As[kF32BK][kF32Tile + 4];
-  __shared__ float Ws[kF32BK][kF32Tile + 4];
+  constexpr int PER = kF32BK * kF32Tile / kThreads;   // slab elements per thread, per operand
+  __shared__ float As[kF32BK][kF32Tile + 1];
+  __shared__ float Ws[kF32BK][kF32Tile + 1];
   const float *A = static_cast<const float *>(p.a);
   const float *W = static_cast<const float *>(p.w);
   const int64_t sam = p.a_t ? 1 : p.lda, sak = p.a_t ? p.lda : 1;
@@ -854,44 +858,55 @@ __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
   const int t = threadIdx.x;
   const int tr = t / 16, tc = t % 16;
   float *C = static_cast<float *>(p.c);
-  float acc[4][4];
+  float acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + tr * 4 + i, n = n0 + tc * 4 + j;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t m = m0 + tr * 2 + i, n = n0 + tc * 2 + j;
       acc[i][j] = (EPI == kEpiPlainF32 && p.acc_init && m < p.M && n < p.N) ? C[m * p.ldc + n] : 0.f;
     }
+  // Slab element q of this thread: A at (row e / BK, k e % BK), W at (k e / TILE, col e % TILE), e = t + q * threads.
+  float ra[PER], rw[PER];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = t + q * kThreads;
+      const int r = e / kF32BK, k = e % kF32BK;
+      ra[q] = (m0 + r < p.M && k0 + k < p.K) ? A[(m0 + r) * sam + (k0 + k) * sak] : 0.f;
+      const int kk = e / kF32Tile, n = e % kF32Tile;
+      rw[q] = (k0 + kk < p.K && n0 + n < p.N) ? W[(k0 + kk) * swk + (n0 + n) * swn] : 0.f;
+    }
+  };
+  load(0);
   for (int64_t k0 = 0; k0 < p.K; k0 += kF32BK) {
-    for (int e = t; e < kF32BK * kF32Tile; e += kThreads) {
-      const int r = e / kF32BK, k = e % kF32BK;      // A element (row r, k)
-      As[k][r] = (m0 + r < p.M && k0 + k < p.K) ? A[(m0 + r) * sam + (k0 + k) * sak] : 0.f;
-      const int kk = e / kF32Tile, n = e % kF32Tile;  // W element (k, col n)
-      Ws[kk][n] = (k0 + kk < p.K && n0 + n < p.N) ? W[(k0 + kk) * swk + (n0 + n) * swn] : 0.f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = t + q * kThreads;
+      As[e % kF32BK][e / kF32BK] = ra[q];
+      Ws[e / kF32Tile][e % kF32Tile] = rw[q];
     }
     __syncthreads();
+    if (k0 + kF32BK < p.K) load(k0 + kF32BK);
 #pragma unroll
     for (int k = 0; k < kF32BK; ++k) {
-      float a[4], w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[k][tr * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = Ws[k][tc * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+      const float a0 = As[k][tr * 2], a1 = As[k][tr * 2 + 1];
+      const float w0 = Ws[k][tc * 2], w1 = Ws[k][tc * 2 + 1];
+      acc[0][0] = fmaf(a0, w0, acc[0][0]);
+      acc[0][1] = fmaf(a0, w1, acc[0][1]);
+      acc[1][0] = fmaf(a1, w0, acc[1][0]);
+      acc[1][1] = fmaf(a1, w1, acc[1][1]);
     }
     __syncthreads();
   }
   float *X = static_cast<float *>(p.aux);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + tr * 4 + i;
+  for (int i = 0; i < 2; ++i) {
+    const int64_t m = m0 + tr * 2 + i;
     if (m >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + tc * 4 + j;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + tc * 2 + j;
       if (n >= p.N) continue;
       float v = acc[i][j];
       if constexpr (EPI == kEpiGeluSaveF32) X[m * p.ldaux + n] = v;

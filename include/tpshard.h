@@ -300,7 +300,8 @@ typedef struct {
                         block (r,c) by block on s_reduce; may equal Z_i */
   int64_t reduce_workgroups; /* upper bound on the reduce kernel's workgroups when it runs
                         beside the GEMMs on s_reduce (it then shares the CUs with
-                        them); 0 = library default (256); >= 0 */
+                        them); 0 = library default: 256 beside a GEMM, a one-shot
+                        grid for the final block, which nothing follows; >= 0 */
   void *H_out;       /* optional [M, F] (dtype): X A_i before the activation, rounded to
                         dtype (RNE), kept for the backward pass; NULL = not stored.
                         Must be NULL when act = TP_ACT_NONE (H would equal Y). */

@@ -253,9 +253,11 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl) {
 }
 
 // Row chunk r of one forward layer: GEMM1 and, per column block, GEMM2 and its
-// reduction (handed to s1 through ev_blocks[c] when `two`).
+// reduction (handed to s1 through ev_blocks[c] when `two`).  `last`: nothing
+// follows this chunk on s0, so its final block's reduction runs alone and takes
+// the whole chip (a one-shot grid) instead of the share sized to run beside a GEMM.
 int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0, hipStream_t s1, bool two,
-                  hipEvent_t *ev_blocks) {
+                  hipEvent_t *ev_blocks, bool last) {
   const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
   GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
               static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
@@ -285,8 +287,10 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     }
     parts[0] = a->Z_i + zoff;
     for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_partials[p - 1] + zoff;
+    const bool beside = two && !(last && c + 1 == pl.C);
+    const int64_t wgs = a->reduce_workgroups ? a->reduce_workgroups : (beside ? kReduceBesideGemm : 0);
     const int rc = reduce_rows(parts.data(), a->P, r * Mr, Mr, c * Hc, Hc, H, a->Z_out, a->Z_split, pl.sq.Ms, sr,
-                               two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0,
+                               two ? wgs : 0,
                                a->bias ? a->bias + c * Hc : nullptr, a->X_next, a->dtype);
     if (rc != TP_OK) return rc;
   }
@@ -499,7 +503,7 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
     if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
     if (gather && two && r > 0 && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess)
       return hip_fail(e, "hipStreamWaitEvent");
-    if ((rc = enqueue_chunk(a, pl, r, s0, s1, two, two ? ev_red + r * C : nullptr)) != TP_OK) return rc;
+    if ((rc = enqueue_chunk(a, pl, r, s0, s1, two, two ? ev_red + r * C : nullptr, r + 1 == R)) != TP_OK) return rc;
   }
   if (two) {
     if ((e = hipEventRecord(ev_join, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -554,7 +558,9 @@ int tp_colrow_mlp_stack(const tp_mlp_args *layers, int64_t num_layers, tp_stream
     for (int64_t r = 0; r < R; ++r) {
       if (two && prev_done && (e = hipStreamWaitEvent(s0, prev_done[r], 0)) != hipSuccess)
         return hip_fail(e, "hipStreamWaitEvent");
-      if ((rc = enqueue_chunk(&layers[l], pl[l], r, s0, s1, two, two ? blocks + r * pl[l].C : nullptr)) != TP_OK) return rc;
+      const bool last = l + 1 == num_layers && r + 1 == R;
+      if ((rc = enqueue_chunk(&layers[l], pl[l], r, s0, s1, two, two ? blocks + r * pl[l].C : nullptr, last)) != TP_OK)
+        return rc;
       if (two && pl[l].reduce && (e = hipEventRecord(done[r], s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
     prev_done = two ? done : nullptr;

@@ -283,15 +283,34 @@ def tp_shard_materialize(src, layout: dict, dst, stream=None):
                                     _stream_ptr(stream)))
 
 
+def _tensors(*objs):
+    """The tensors among objs, looking one level into lists, tuples and dict values."""
+    out = []
+    for o in objs:
+        if hasattr(o, "data_ptr"):
+            out.append(o)
+        elif isinstance(o, dict):
+            out += [v for v in o.values() if hasattr(v, "data_ptr")]
+        elif isinstance(o, (list, tuple)):
+            out += [v for v in o if hasattr(v, "data_ptr")]
+    return out
+
+
 class Prepared:
     """A library call whose arguments were marshalled once: calling it passes
-    the same argument structures again (the tensors they point to must stay
-    alive and in place), so a loop pays one C call per launch sequence."""
+    the same argument structures again, so a loop pays one C call per launch
+    sequence.  It holds references to the tensors it points into, and a replay
+    after any of them has moved (resized or re-pointed) raises instead of
+    touching stale memory."""
 
-    def __init__(self, fn, args, keep, streams):
+    def __init__(self, fn, args, keep, streams, tensors=()):
         self._fn, self._args, self._keep, self._streams = fn, args, keep, streams
+        self._tensors = [(t, t.data_ptr()) for t in tensors]
 
     def __call__(self, *streams):
+        for t, p in self._tensors:
+            if t.data_ptr() != p:
+                raise TpError(-1, "a tensor of a prepared call has moved since it was prepared")
         ptrs = [_stream_ptr(s) for s in streams] if streams else self._streams
         if len(ptrs) < len(self._streams):
             ptrs = list(ptrs) + [ptrs[-1]] * (len(self._streams) - len(ptrs))
@@ -319,7 +338,8 @@ def tp_shard_materialize_batch(jobs, stream=None, prepare=False):
                                          dst=C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst=num_dst))
     arr = (tp_materialize_item * max(1, len(items)))(*items)
     if prepare:
-        return Prepared(lib.tp_shard_materialize_batch, (arr, len(items)), keep, [_stream_ptr(stream)])
+        return Prepared(lib.tp_shard_materialize_batch, (arr, len(items)), keep, [_stream_ptr(stream)],
+                        _tensors(*[j[0] for j in jobs], *[j[2] for j in jobs]))
     _check(lib.tp_shard_materialize_batch(arr, len(items), _stream_ptr(stream)))
 
 
@@ -482,7 +502,8 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, prep
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     if prepare:
-        return Prepared(lib.tp_colrow_mlp, (C.byref(args),), keep + [args], [sc, sr])
+        return Prepared(lib.tp_colrow_mlp, (C.byref(args),), keep + [args], [sc, sr],
+                        _tensors(X, A_i, B_i, Y_ws, Z_i, *kw.values()))
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
 
 
@@ -496,7 +517,8 @@ def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None, prepare=False):
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     if prepare:
-        return Prepared(lib.tp_colrow_mlp_stack, (arr, len(built)), [built], [sc, sr])
+        return Prepared(lib.tp_colrow_mlp_stack, (arr, len(built)), [built], [sc, sr],
+                        _tensors(*[v for layer in layers for v in dict(layer).values()]))
     _check(lib.tp_colrow_mlp_stack(arr, len(built), sc, sr))
 
 
@@ -539,7 +561,9 @@ def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
     if prepare:
-        return Prepared(lib.tp_colrow_mlp_backward, (C.byref(args),), [args, parr, gs, xs], [sc, sr])
+        return Prepared(lib.tp_colrow_mlp_backward, (C.byref(args),), [args, parr, gs, xs], [sc, sr],
+                        _tensors(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, peers, dX_out, dZ_shards,
+                                 dX_split))
     _check(lib.tp_colrow_mlp_backward(C.byref(args), sc, sr))
 
 

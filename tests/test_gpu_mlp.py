@@ -325,3 +325,7 @@ def test_prepared_call_matches_direct_call():
         call(torch.cuda.current_stream(), s1)
         torch.cuda.synchronize()
         assert torch.equal(Zo.view(torch.int32), ref.view(torch.int32))
+    # An output re-pointed to new storage: the replay refuses before launching anything.
+    Zo.set_(torch.empty_like(Zo))
+    with pytest.raises(tp.TpError, match="moved"):
+        call()

@@ -25,6 +25,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -475,15 +476,24 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace collapsed (string literals
+    in these kernels hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
-    """Hash of the kernel sources (device code and its launch dispatch); traffic
-    figures taken on other sources are stale."""
+    """Hash of the kernel sources' code (device code and its launch dispatch;
+    comments and layout do not count); traffic figures taken on other code are
+    stale."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "sharded_gemm_amd", "csrc", "*.hip")))
     for f in files:
-        with open(f, "rb") as fh:
+        with open(f, encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -41,7 +41,10 @@
 // waves of tile rows 0..127 (group A) and of rows 128..255 (group B) sit one
 // barrier apart: between two barriers one group runs its MFMAs while the other
 // reads its next stage from LDS, so the MFMA pipe is fed while LDS reads and
-// their waits happen.  Group A issues all of a stage's DMA.
+// their waits happen.  Group A issues all of a stage's DMA.  On MI355X this
+// loop is bound by the LDS read rate (128 bytes per clock per CU; the eight
+// 128 x BN/4 wave blocks read 160-192 KiB of fragments per 64-deep stage)
+// together with the DMA issue, not by the MFMA pipe.
 // Ragged path (bf16_gemm_ragged): the same MFMA on a 128 x 128 tile with
 // register-staged, bounds-checked loads, for shapes the DMA path cannot take
 // (K not a multiple of 32, N not a multiple of 8, misaligned pointers).

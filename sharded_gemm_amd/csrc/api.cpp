@@ -700,17 +700,25 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
     GemmArgs ga{X + r * Mr * H * es, dH + r * Mr * F * es, a->dA_i, H, F, Mr, H, F, F};
     ga.a_t = 1;
     ga.acc_init = cont;
-    t0 = timing_begin(s0);
-    e = gemm_launch(ga, epi_f32, s0);
-    if (e != hipSuccess) return hip_fail(e, "dA GEMM launch");
-    timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * Mr);
     GemmArgs gb{Yi + r * Mr * F * es, dZ + r * Mr * H * es, a->dB_i, F, H, Mr, F, H, H};
     gb.a_t = 1;
     gb.acc_init = cont;
-    t0 = timing_begin(s0);
-    e = gemm_launch(gb, epi_f32, s0);
-    if (e != hipSuccess) return hip_fail(e, "dB GEMM launch");
-    timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * F * H * Mr);
+    if (gemm_pair_ok(ga, gb, epi_f32)) {
+      // Both too small to fill the chip alone: one grouped launch.
+      t0 = timing_begin(s0);
+      e = gemm_launch_pair(ga, gb, epi_f32, s0);
+      if (e != hipSuccess) return hip_fail(e, "dA/dB GEMM launch");
+      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * Mr * 2);
+    } else {
+      t0 = timing_begin(s0);
+      e = gemm_launch(ga, epi_f32, s0);
+      if (e != hipSuccess) return hip_fail(e, "dA GEMM launch");
+      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * Mr);
+      t0 = timing_begin(s0);
+      e = gemm_launch(gb, epi_f32, s0);
+      if (e != hipSuccess) return hip_fail(e, "dB GEMM launch");
+      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * F * H * Mr);
+    }
   }
   if (two) {
     if ((e = hipEventRecord(ev_join, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -538,8 +538,10 @@ struct DmaCfg {
   static_assert(S * STAGE <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmArgs p) {
+// One workgroup's tile `bid` of the problem p (the body of the single-group
+// kernels below).
+template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M, int WAVES_N>
+__device__ __forceinline__ void dma_tile(const GemmArgs& p, int bid) {
   using C = DmaCfg<BM, BN, BK, S, AT, WT, WAVES_M, WAVES_N>;
   using TA = typename C::TA;
   using TW = typename C::TW;
@@ -551,7 +553,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   const int tiles_m = static_cast<int>((p.M + BM - 1) / BM);
   const int tiles_n = static_cast<int>((p.N + BN - 1) / BN);
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
+  tile_coords(bid, tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TP_LDS char *)smem));
   const uint16_t *A = static_cast<const uint16_t *>(p.a);
@@ -664,6 +666,27 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
       coords(i, j, &m, &n);
       if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);   // N % 8 == 0 on this path
     }
+}
+
+template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmArgs p) {
+  dma_tile<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>(p, blockIdx.x);
+}
+
+// Two independent problems of one shape class in one launch (a grouped GEMM):
+// workgroups [0, tiles0) take the first problem's tiles, the rest the
+// second's.  Two GEMMs that each leave CUs idle (a few hundred small tiles)
+// then share the chip instead of running one after the other.
+struct GemmPair {
+  GemmArgs p[2];
+  int32_t tiles0;
+};
+
+template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma_pair(GemmPair g) {
+  const int bid = blockIdx.x;
+  if (bid < g.tiles0) dma_tile<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>(g.p[0], bid);
+  else dma_tile<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>(g.p[1], bid - g.tiles0);
 }
 
 // ---- ping-pong path -------------------------------------------------------
@@ -930,6 +953,16 @@ hipError_t launch_dma(const GemmArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
+hipError_t launch_dma_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
+  const int64_t ta = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int64_t tb = ((b.M + BM - 1) / BM) * ((b.N + BN - 1) / BN);
+  const GemmPair g{{a, b}, static_cast<int32_t>(ta)};
+  hipLaunchKernelGGL((bf16_gemm_dma_pair<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>),
+                     dim3(static_cast<unsigned>(ta + tb)), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int EPI, bool AT, bool WT, int BK = 64, int S = 2, int WGM = 2>
 hipError_t launch_pp(const GemmArgs& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -1060,6 +1093,27 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
     if (epi == kEpiF32Acc) return dispatch_bf16<kEpiF32Acc, true, false>(p, dma_ok, false, s);
   }
   return hipErrorInvalidValue;
+}
+
+// The grouped launch covers the weight gradients of a small layer: bf16
+// operands, A given transposed, fp32 output (fresh or continued, the same for
+// both), both problems on the small-tile path with the same k depth, so both
+// would run the same kernel on their own.
+bool gemm_pair_ok(const GemmArgs& a, const GemmArgs& b, int epi) {
+  auto small = [](const GemmArgs& p) { return ((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs; };
+  return epi == kEpiF32 && a.a_t && b.a_t && !a.w_t && !b.w_t && a.acc_init == b.acc_init && a.K == b.K &&
+         a.M > 0 && a.N > 0 && b.M > 0 && b.N > 0 && a.K > 0 && a.K % 32 == 0 && small(a) && small(b) &&
+         gemm_vec_ok(a, 4, false) && gemm_vec_ok(b, 4, false);
+}
+
+hipError_t gemm_launch_pair(const GemmArgs& a, const GemmArgs& b, int epi, hipStream_t s) {
+  if (!gemm_pair_ok(a, b, epi)) return hipErrorInvalidValue;
+  const bool k64 = a.K % 64 == 0;
+  if (a.acc_init)
+    return k64 ? launch_dma_pair<64, 64, 64, 2, kEpiF32Acc, true, false, 2, 2>(a, b, s)
+               : launch_dma_pair<64, 64, 32, 4, kEpiF32Acc, true, false, 2, 2>(a, b, s);
+  return k64 ? launch_dma_pair<64, 64, 64, 2, kEpiF32, true, false, 2, 2>(a, b, s)
+             : launch_dma_pair<64, 64, 32, 4, kEpiF32, true, false, 2, 2>(a, b, s);
 }
 
 }  // namespace tpshard

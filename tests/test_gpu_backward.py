@@ -88,6 +88,10 @@ def _f64(t):
     (4000, 2000, 2000, 1, 2), (4000, 2000, 2000, 2, 2),
     # dA on 256 x 192 tiles with A transposed, accumulating over two chunks
     (512, 2048, 6144, 2, 2),
+    # dA and dB in one grouped launch, 45 tiles each (the second problem's tiles start off the XCD stride)
+    (256, 576, 320, 1, 2),
+    # the same, 32-deep stages (96 tokens per chunk), accumulating over two chunks
+    (192, 576, 320, 2, 2),
 ])
 def test_backward_integer_exact(M, H, F, Rc, P):
     """One-hot A_i (columns) and B_i (rows) keep every value a small integer:

@@ -703,10 +703,11 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
     GemmArgs gb{Yi + r * Mr * F * es, dZ + r * Mr * H * es, a->dB_i, F, H, Mr, F, H, H};
     gb.a_t = 1;
     gb.acc_init = cont;
-    if (gemm_pair_ok(ga, gb, epi_f32)) {
+    const GemmArgs pair[2] = {ga, gb};
+    if (gemm_group_ok(pair, 2, epi_f32)) {
       // Both too small to fill the chip alone: one grouped launch.
       t0 = timing_begin(s0);
-      e = gemm_launch_pair(ga, gb, epi_f32, s0);
+      e = gemm_launch_group(pair, 2, epi_f32, s0);
       if (e != hipSuccess) return hip_fail(e, "dA/dB GEMM launch");
       timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * Mr * 2);
     } else {

@@ -42,10 +42,11 @@ enum {
 // Enqueues the GEMM on stream s; returns the launch status.
 hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s);
 
-// Two independent GEMMs in one launch (same results as two gemm_launch calls),
-// for pairs gemm_pair_ok accepts: small weight-gradient problems that would
-// each leave CUs idle.  gemm_launch_pair returns hipErrorInvalidValue otherwise.
-bool gemm_pair_ok(const GemmArgs& a, const GemmArgs& b, int epi);
-hipError_t gemm_launch_pair(const GemmArgs& a, const GemmArgs& b, int epi, hipStream_t s);
+// Up to 16 independent GEMMs in one launch (same results as one gemm_launch
+// call each), for groups gemm_group_ok accepts: small weight-gradient problems
+// that would each leave CUs idle.  gemm_launch_group returns
+// hipErrorInvalidValue otherwise.
+bool gemm_group_ok(const GemmArgs *ps, int n, int epi);
+hipError_t gemm_launch_group(const GemmArgs *ps, int n, int epi, hipStream_t s);
 
 }  // namespace tpshard

@@ -673,20 +673,24 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
   dma_tile<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>(p, blockIdx.x);
 }
 
-// Two independent problems of one shape class in one launch (a grouped GEMM):
-// workgroups [0, tiles0) take the first problem's tiles, the rest the
-// second's.  Two GEMMs that each leave CUs idle (a few hundred small tiles)
-// then share the chip instead of running one after the other.
-struct GemmPair {
-  GemmArgs p[2];
-  int32_t tiles0;
+// Independent problems of one shape class in one launch (a grouped GEMM):
+// problem q takes workgroups [start[q], start[q+1]).  GEMMs that each leave CUs
+// idle (a few hundred small tiles) then share the chip instead of running one
+// after the other.
+constexpr int kMaxGroup = 16;
+struct GemmGroup {
+  GemmArgs p[kMaxGroup];
+  int32_t start[kMaxGroup + 1];
+  int32_t n;
 };
 
 template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma_pair(GemmPair g) {
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma_group(GemmGroup g) {
   const int bid = blockIdx.x;
-  if (bid < g.tiles0) dma_tile<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>(g.p[0], bid);
-  else dma_tile<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>(g.p[1], bid - g.tiles0);
+  int q = 0;
+  while (q + 1 < g.n && bid >= g.start[q + 1]) ++q;   // uniform: one problem per workgroup
+  const GemmArgs *p = g.p + q;                          // stays in the argument segment
+  dma_tile<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>(*p, bid - g.start[q]);
 }
 
 // ---- ping-pong path -------------------------------------------------------
@@ -954,12 +958,18 @@ hipError_t launch_dma(const GemmArgs& p, hipStream_t s) {
 }
 
 template <int BM, int BN, int BK, int S, int EPI, bool AT, bool WT, int WAVES_M = 2, int WAVES_N = 4>
-hipError_t launch_dma_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
-  const int64_t ta = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const int64_t tb = ((b.M + BM - 1) / BM) * ((b.N + BN - 1) / BN);
-  const GemmPair g{{a, b}, static_cast<int32_t>(ta)};
-  hipLaunchKernelGGL((bf16_gemm_dma_pair<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>),
-                     dim3(static_cast<unsigned>(ta + tb)), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+hipError_t launch_dma_group(const GemmArgs *ps, int n, hipStream_t s) {
+  GemmGroup g{};
+  g.n = n;
+  int64_t total = 0;
+  for (int q = 0; q < n; ++q) {
+    g.p[q] = ps[q];
+    g.start[q] = static_cast<int32_t>(total);
+    total += ((ps[q].M + BM - 1) / BM) * ((ps[q].N + BN - 1) / BN);
+  }
+  g.start[n] = static_cast<int32_t>(total);
+  hipLaunchKernelGGL((bf16_gemm_dma_group<BM, BN, BK, S, EPI, AT, WT, WAVES_M, WAVES_N>),
+                     dim3(static_cast<unsigned>(total)), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1097,23 +1107,30 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
 
 // The grouped launch covers the weight gradients of a small layer: bf16
 // operands, A given transposed, fp32 output (fresh or continued, the same for
-// both), both problems on the small-tile path with the same k depth, so both
-// would run the same kernel on their own.
-bool gemm_pair_ok(const GemmArgs& a, const GemmArgs& b, int epi) {
-  auto small = [](const GemmArgs& p) { return ((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs; };
-  return epi == kEpiF32 && a.a_t && b.a_t && !a.w_t && !b.w_t && a.acc_init == b.acc_init && a.K == b.K &&
-         a.M > 0 && a.N > 0 && b.M > 0 && b.N > 0 && a.K > 0 && a.K % 32 == 0 && small(a) && small(b) &&
-         gemm_vec_ok(a, 4, false) && gemm_vec_ok(b, 4, false);
+// all), every problem on the small-tile path with the same k depth, so each
+// would run the same kernel on its own.
+bool gemm_group_ok(const GemmArgs *ps, int n, int epi) {
+  if (n < 1 || n > kMaxGroup || epi != kEpiF32) return false;
+  int64_t total = 0;
+  for (int q = 0; q < n; ++q) {
+    const GemmArgs& p = ps[q];
+    const bool small = ((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs;
+    if (!p.a_t || p.w_t || p.acc_init != ps[0].acc_init || p.K != ps[0].K || p.M <= 0 || p.N <= 0 || p.K <= 0 ||
+        p.K % 32 != 0 || !small || !gemm_vec_ok(p, 4, false))
+      return false;
+    total += ((p.M + 63) / 64) * ((p.N + 63) / 64);
+  }
+  return total < (int64_t{1} << 31);
 }
 
-hipError_t gemm_launch_pair(const GemmArgs& a, const GemmArgs& b, int epi, hipStream_t s) {
-  if (!gemm_pair_ok(a, b, epi)) return hipErrorInvalidValue;
-  const bool k64 = a.K % 64 == 0;
-  if (a.acc_init)
-    return k64 ? launch_dma_pair<64, 64, 64, 2, kEpiF32Acc, true, false, 2, 2>(a, b, s)
-               : launch_dma_pair<64, 64, 32, 4, kEpiF32Acc, true, false, 2, 2>(a, b, s);
-  return k64 ? launch_dma_pair<64, 64, 64, 2, kEpiF32, true, false, 2, 2>(a, b, s)
-             : launch_dma_pair<64, 64, 32, 4, kEpiF32, true, false, 2, 2>(a, b, s);
+hipError_t gemm_launch_group(const GemmArgs *ps, int n, int epi, hipStream_t s) {
+  if (!gemm_group_ok(ps, n, epi)) return hipErrorInvalidValue;
+  const bool k64 = ps[0].K % 64 == 0;
+  if (ps[0].acc_init)
+    return k64 ? launch_dma_group<64, 64, 64, 2, kEpiF32Acc, true, false, 2, 2>(ps, n, s)
+               : launch_dma_group<64, 64, 32, 4, kEpiF32Acc, true, false, 2, 2>(ps, n, s);
+  return k64 ? launch_dma_group<64, 64, 64, 2, kEpiF32, true, false, 2, 2>(ps, n, s)
+             : launch_dma_group<64, 64, 32, 4, kEpiF32, true, false, 2, 2>(ps, n, s);
 }
 
 }  // namespace tpshard

@@ -134,6 +134,14 @@ def test_tiny_fp32_two_ranks():
     B_sh = {d: torch.empty((w.F, w.H), device="cuda") for d in range(2)}
     tp.tp_shard_materialize(A.cuda(), sa, A_sh)
     tp.tp_shard_materialize(B.cuda(), sb, B_sh)
+    # the bench cuts both weights in one batched launch: same bits
+    A_b = {d: torch.empty_like(A_sh[d]) for d in range(4)}
+    B_b = {d: torch.empty_like(B_sh[d]) for d in range(4)}
+    tp.tp_shard_materialize_batch([(A.cuda(), sa, A_b), (B.cuda(), sb, B_b)])
+    torch.cuda.synchronize()
+    for d in range(4):
+        assert torch.equal(A_b[d].view(torch.int16), A_sh[d].view(torch.int16))
+        assert torch.equal(B_b[d].view(torch.int16), B_sh[d].view(torch.int16))
     Xg = X.cuda()
     _, Z1, _ = run_rank(Xg, A_sh[1], B_sh[1])
     Y0, Z0, Zo = run_rank(Xg, A_sh[0], B_sh[0], peers=[Z1.cuda()], two_streams=True)
@@ -159,6 +167,14 @@ def test_gpt2_small_tp4_full():
     B_sh = {d: torch.empty((w.F, w.H), dtype=torch.bfloat16, device="cuda") for d in range(4)}
     tp.tp_shard_materialize(A.cuda(), sa, A_sh)
     tp.tp_shard_materialize(B.cuda(), sb, B_sh)
+    # the bench cuts both weights in one batched launch: same bits
+    A_b = {d: torch.empty_like(A_sh[d]) for d in range(4)}
+    B_b = {d: torch.empty_like(B_sh[d]) for d in range(4)}
+    tp.tp_shard_materialize_batch([(A.cuda(), sa, A_b), (B.cuda(), sb, B_b)])
+    torch.cuda.synchronize()
+    for d in range(4):
+        assert torch.equal(A_b[d].view(torch.int16), A_sh[d].view(torch.int16))
+        assert torch.equal(B_b[d].view(torch.int16), B_sh[d].view(torch.int16))
     Xg = X.cuda()
     peers = [run_rank(Xg, A_sh[i], B_sh[i])[1].cuda() for i in range(1, 4)]
     Y0, Z0, Zo = run_rank(Xg, A_sh[0], B_sh[0], peers=peers, two_streams=True)

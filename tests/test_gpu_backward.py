@@ -153,6 +153,30 @@ def test_backward_gelu(M, H, F, Rc, P):
     assert rel_err(dXo, R.reduce_full([g["dX_i"]] + [p.double().numpy() for p in peers])) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,H,F,Rc,P", [(77, 45, 51, 1, 2), (300, 264, 136, 3, 2), (130, 129, 65, 2, 3),
+                                        (1, 1, 1, 1, 2)])
+def test_backward_gelu_fp32_ragged(M, H, F, Rc, P):
+    """fp32 throughout, sizes off the 32 x 32 tile and the 64-deep k slab: the
+    fused GeLU derivative, transposed operands of the weight gradients and
+    their accumulation over row chunks."""
+    announce(f"backward gelu fp32 M={M} H={H} F={F} R={Rc} P={P}")
+    X = inputs.normal((M, H), 521, 1.0)
+    A = inputs.normal((H, F), 522, 1.0 / np.sqrt(H))
+    B = inputs.normal((F, H), 523, 1.0 / np.sqrt(F))
+    dZ = inputs.normal((M, H), 524, 1.0)
+    peers = [inputs.normal((M, H), 530 + p) for p in range(P - 1)]
+    Xd, Ad, Bd, dZd = X.cuda(), A.cuda(), B.cuda(), dZ.cuda()
+    Y, Hs = forward(Xd, Ad, Bd)
+    assert rel_err(Hs, O.hidden(X, A, O.GELU_NONE)) <= TOL_F32
+    dH, dX, dXo, dA, dB = backward(Xd, Ad, Bd, Hs, Y, dZd, R=Rc, peers=[p.cuda() for p in peers])
+    g = O.backward_rank(X, A, B, dZ)
+    assert rel_err(dH, g["dH"]) <= TOL_F32
+    assert rel_err(dX, g["dX_i"]) <= TOL_F32
+    assert rel_err(dA, g["dA_i"]) <= TOL_F32
+    assert rel_err(dB, g["dB_i"]) <= TOL_F32
+    assert rel_err(dXo, R.reduce_full([g["dX_i"]] + [p.double().numpy() for p in peers])) <= TOL_F32
+
+
 def test_backward_chunks_do_not_change_a_bit():
     """Row chunks split dH and dX by rows and continue one accumulation of the
     weight gradients, so R = 1, 2, 4 give identical bits (serial or two streams)."""

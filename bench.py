@@ -43,6 +43,10 @@ METRIC = "per-rank TP-MLP TFLOP/s (% bf16 MFMA peak) + shard/reduce GB/s (% HBM)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# GEMM2 with the reduction in its epilogue moves far more bytes than its flops
+# need time for (GPT-2 shape: about 70 MB against 4.8 GFLOP), so the library
+# counts its work in bytes and it is priced against HBM.
+BYTE_KERNELS = ("gemm2_reduce",)
 
 
 def log(msg):
@@ -60,6 +64,7 @@ class MlpStep:
 
     serial = False
     reduce_wgs = 0
+    reduce_fusion = tp.TP_REDUCE_FUSION_AUTO
 
     def __init__(self, w, split_weights: bool, seq: bool = False):
         self.w = w
@@ -116,7 +121,8 @@ class MlpStep:
                                     Z_out=None if self.seq else self.Zo, s_compute=self.s0,
                                     s_reduce=self.s0 if self.serial else self.s1,
                                     reduce_workgroups=self.reduce_wgs, X_shards=self.Xb if self.seq else None,
-                                    Z_split=self.Zs if self.seq else None, prepare=True)
+                                    Z_split=self.Zs if self.seq else None, reduce_fusion=self.reduce_fusion,
+                                    prepare=True)
 
     def step(self):
         if self.cut is not None:
@@ -134,6 +140,7 @@ class MlpStep:
         cfg = {"workload": w.name + ("-sp" if self.seq else ""), "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F,
                "tp": w.P, "row_chunks": w.R, "col_chunks": w.C, "weights_cut_each_step": self.split,
                "reduce_stream": "compute" if self.serial else "second",
+               "reduce_fusion": "auto" if self.reduce_fusion == tp.TP_REDUCE_FUSION_AUTO else "off",
                "peers": "virtual ranks 1..P-1, partials precomputed by the same path"}
         if self.seq:
             cfg["sequence_parallel"] = {"blocks": w.P, "input": "all-gathered from P sequence blocks",
@@ -295,6 +302,7 @@ class StackStep:
 
     serial = False
     reduce_wgs = 0
+    reduce_fusion = tp.TP_REDUCE_FUSION_AUTO
     L = 2
 
     def __init__(self, w):
@@ -332,7 +340,8 @@ class StackStep:
 
     def prepare(self):
         """Marshal the step's library call once (the buffers never move)."""
-        self.call = tp.tp_colrow_mlp_stack([dict(l, reduce_workgroups=self.reduce_wgs) for l in self.layers],
+        self.call = tp.tp_colrow_mlp_stack([dict(l, reduce_workgroups=self.reduce_wgs, reduce_fusion=self.reduce_fusion)
+                                            for l in self.layers],
                                            s_compute=self.s0, s_reduce=self.s0 if self.serial else self.s1,
                                            prepare=True)
 
@@ -516,7 +525,7 @@ def kernel_table(stats, steps):
     for name, st in stats.items():
         if st["launches"] == 0:
             continue
-        is_gemm = name.startswith("gemm")
+        is_gemm = name.startswith("gemm") and name not in BYTE_KERNELS
         avg_ms = st["total_ms"] / st["launches"]
         rate = st["work"] / (st["total_ms"] * 1e-3)
         out[name] = {"launches_per_step": st["launches"] / steps, "avg_ms": avg_ms,
@@ -530,7 +539,8 @@ def roofline(kernels, dtype, workload):
     """Roofline entry of the dominant kernel.  In an MLP step that is the slower
     of the two GEMMs (together more than half the step; the weight cuts are two
     short launches whose per-launch event overhead would otherwise let them
-    overtake a GEMM from run to run); elsewhere the kernel with the most time."""
+    overtake a GEMM from run to run), GEMM2 counting with the reduction when
+    that runs in its epilogue; elsewhere the kernel with the most time."""
     if not kernels:
         return None
     pool = [k for k in kernels if k.startswith("gemm")] or list(kernels)
@@ -607,6 +617,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--serial", action="store_true", help="run the reduce on the compute stream")
+    ap.add_argument("--no-reduce-fusion", action="store_true",
+                    help="always run the forward's reduction as its own kernel, never in GEMM2's epilogue")
     ap.add_argument("--reduce-wgs", type=int, default=0,
                     help="cap on the reduce kernel's workgroups beside the GEMMs (0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -634,6 +646,8 @@ def main():
     log(f"[bench] workload {args.workload}: setting up")
     wl = WORKLOADS[args.workload]()
     wl.serial, wl.reduce_wgs = args.serial, args.reduce_wgs
+    if args.no_reduce_fusion:
+        wl.reduce_fusion = tp.TP_REDUCE_FUSION_OFF
     if hasattr(wl, "prepare"):
         wl.prepare()
     dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"

@@ -326,7 +326,18 @@ typedef struct {
   void *X_next;      /* optional [M, H] in dtype: the full sum (+ bias) rounded to dtype
                         (RNE for bf16), written by the same reduction, i.e. the next
                         layer's input; Z_out may then be NULL.  Not with Z_split. */
+  int32_t reduce_fusion; /* TP_REDUCE_FUSION_AUTO (0): where a block's reduction would
+                        run with nothing beside it (the serial schedule, or the final
+                        block of the two-stream one), GEMM2 adds the peers' partials
+                        and the bias in its epilogue and writes Z_out / X_next itself.
+                        Taken for bf16 operands, P <= 4, a full (not split) output,
+                        16-byte aligned rows, F a multiple of 32 and blocks of fewer
+                        than 256 output tiles of 128 x 128; otherwise,
+                        and always with TP_REDUCE_FUSION_OFF (1), a separate
+                        reduction kernel runs.  Both give the same bits. */
 } tp_mlp_args;
+
+enum { TP_REDUCE_FUSION_AUTO = 0, TP_REDUCE_FUSION_OFF = 1 };
 
 /*
  * Enqueue one rank's MLP share: for each row chunk r, Y[r] = act(X[r] A_i) on
@@ -435,10 +446,12 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *args, tp_stream_t s_compute, t
 /* ---- per-kernel timing (measurement support) ---------------------------- */
 /* Kernel families timed by the optional instrumentation below: the forward's
  * GEMMs, the backward's input-gradient GEMMs (dH and dX) and its
- * weight-gradient GEMMs (dA and dB), and the gather kernel. */
+ * weight-gradient GEMMs (dA and dB), the gather kernel, and GEMM2 with the
+ * reduction folded into its epilogue (memory-bound: its work counts bytes,
+ * the operands and the peers' partials read once and each output written once). */
 enum { TP_KERNEL_MATERIALIZE = 0, TP_KERNEL_GEMM1 = 1, TP_KERNEL_GEMM2 = 2, TP_KERNEL_REDUCE = 3,
        TP_KERNEL_GEMM_DGRAD = 4, TP_KERNEL_GEMM_WGRAD = 5, TP_KERNEL_GATHER = 6,
-       TP_KERNEL_KINDS = 7 };
+       TP_KERNEL_GEMM2_REDUCE = 7, TP_KERNEL_KINDS = 8 };
 
 typedef struct {
   int64_t launches;  /* kernel launches timed since the last read */

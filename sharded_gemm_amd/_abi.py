@@ -40,7 +40,10 @@ TP_REDUCE_OP_MIN = 2
 EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_binary", "tp_infer_matmul_dims_mapping", "tp_shard_materialize", "tp_shard_materialize_batch", "tp_shard_gather",
            "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_stack", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
-TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather")
+TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather", "gemm2_reduce")
+
+TP_REDUCE_FUSION_AUTO = 0
+TP_REDUCE_FUSION_OFF = 1
 
 
 class TpError(RuntimeError):
@@ -87,7 +90,7 @@ class tp_mlp_args(C.Structure):
                 ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
                 ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p), ("bias", C.c_void_p),
                 ("seq_splits", C.c_int64), ("X_shards", C.POINTER(C.c_void_p)), ("Z_split", C.POINTER(C.c_void_p)),
-                ("X_next", C.c_void_p)]
+                ("X_next", C.c_void_p), ("reduce_fusion", C.c_int32)]
 
 
 class tp_mlp_bwd_args(C.Structure):
@@ -453,7 +456,7 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
 
 def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
               act=TP_ACT_GELU_ERF, reduce_workgroups=0, H_out=None, bias=None, X_shards=None, Z_split=None,
-              X_next=None):
+              X_next=None, reduce_fusion=TP_REDUCE_FUSION_AUTO):
     """(tp_mlp_args, keep-alive list) for one forward layer, shapes checked."""
     M, H = int(X.shape[0]), int(X.shape[1])
     F = int(A_i.shape[1])
@@ -480,7 +483,7 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
                        Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias),
-                       X_next=_ptr(X_next))
+                       X_next=_ptr(X_next), reduce_fusion=reduce_fusion)
     S, xs, zs = _seq_arrays(X_shards, Z_split)
     args.seq_splits, args.X_shards, args.Z_split = S, xs, zs
     return args, [parr, xs, zs]
@@ -492,7 +495,9 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, prep
     sum rounded to the input dtype (the next layer's input).
 
     Keywords: row_chunks, col_chunks, peer_partials, Z_out, act, reduce_workgroups, H_out,
-    bias, X_shards, Z_split, X_next.  Sequence parallelism: with ``X_shards`` (S tensors
+    bias, X_shards, Z_split, X_next, reduce_fusion (TP_REDUCE_FUSION_AUTO lets GEMM2's
+    epilogue take the reduction where nothing would run beside it; TP_REDUCE_FUSION_OFF
+    keeps the separate reduction kernel; same bits either way).  Sequence parallelism: with ``X_shards`` (S tensors
     [M/S, H]) X is a workspace the call fills by all-gathering them; with ``Z_split``
     (S tensors [M/S, H] fp32) the sum is reduce-scattered into the blocks instead of
     written to Z_out.  With ``prepare=True`` nothing runs; a ``Prepared`` call taking

@@ -200,6 +200,8 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl) {
   if (a->P > 1 && (!a->peer_partials || !has_out)) return fail(TP_ERR_ARG, "P > 1 needs peer_partials and Z_out (or Z_split, or X_next)");
   if (a->bias && !has_out) return fail(TP_ERR_ARG, "a bias needs Z_out, Z_split or X_next (it is added to the full sum)");
   if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
+  if (a->reduce_fusion != TP_REDUCE_FUSION_AUTO && a->reduce_fusion != TP_REDUCE_FUSION_OFF)
+    return fail(TP_ERR_ARG, "unknown reduce_fusion %d", a->reduce_fusion);
   if (a->H_out && a->act == TP_ACT_NONE) return fail(TP_ERR_ARG, "H_out needs an activation (it would equal Y)");
   const int64_t M = a->M, H = a->H, F = a->F;
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
@@ -274,6 +276,34 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     const int64_t zoff = r * Mr * H + c * Hc;
     GemmArgs g2{static_cast<const char *>(a->Y_ws) + r * Mr * F * es, static_cast<const char *>(a->B_i) + c * Hc * es,
                 a->Z_i + zoff, Mr, Hc, F, F, H, H};
+    // The block's reduction folds into GEMM2's epilogue where it would run
+    // with nothing beside it anyway (the serial schedule and the final block):
+    // one launch fewer and no second read of the partial just written.
+    const bool final_block = last && c + 1 == pl.C;
+    if (pl.reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && (!two || final_block) && !a->Z_split &&
+        pl.epi2 == kEpiF32 && a->P - 1 <= kMaxFusedPeers) {
+      GemmArgs gr = g2;
+      gr.red.np = static_cast<int32_t>(a->P - 1);
+      for (int64_t p = 1; p < a->P; ++p) gr.red.peer[p - 1] = a->peer_partials[p - 1] + zoff;
+      gr.red.out = a->Z_out ? a->Z_out + zoff : nullptr;
+      gr.red.bias = a->bias ? a->bias + c * Hc : nullptr;
+      gr.red.lo = a->X_next ? static_cast<char *>(a->X_next) + zoff * es : nullptr;
+      gr.red.lo_bf16 = a->dtype == TP_BF16;
+      if (gemm_red_ok(gr)) {
+        t0 = timing_begin(s0);
+        e = gemm_launch(gr, kEpiF32Red, s0);
+        if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+        // Memory-bound: its work is bytes (Y rows and B columns, the peers'
+        // blocks and the bias read once, every output written once).
+        const double cells = static_cast<double>(Mr) * Hc;
+        const double bytes = es * (static_cast<double>(Mr) * F + static_cast<double>(F) * Hc) +
+                             4.0 * gr.red.np * cells + (gr.red.out != gr.c ? 4.0 * cells : 0.0) +
+                             (gr.red.out ? 4.0 * cells : 0.0) + (gr.red.lo ? es * cells : 0.0) +
+                             (gr.red.bias ? 4.0 * Hc : 0.0);
+        timing_end(t0, s0, TP_KERNEL_GEMM2_REDUCE, bytes);
+        continue;
+      }
+    }
     t0 = timing_begin(s0);
     e = gemm_launch(g2, pl.epi2, s0);
     if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
@@ -287,7 +317,7 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     }
     parts[0] = a->Z_i + zoff;
     for (int64_t p = 1; p < a->P; ++p) parts[p] = a->peer_partials[p - 1] + zoff;
-    const bool beside = two && !(last && c + 1 == pl.C);
+    const bool beside = two && !final_block;
     const int64_t wgs = a->reduce_workgroups ? a->reduce_workgroups : (beside ? kReduceBesideGemm : 0);
     const int rc = reduce_rows(parts.data(), a->P, r * Mr, Mr, c * Hc, Hc, H, a->Z_out, a->Z_split, pl.sq.Ms, sr,
                                two ? wgs : 0,

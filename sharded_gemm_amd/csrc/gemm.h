@@ -11,6 +11,20 @@ namespace tpshard {
 //   a_t = 0: A is stored [M][lda] (k contiguous);   a_t = 1: A is stored [K][lda] (m contiguous), i.e. A^T is given.
 //   w_t = 0: W is stored [K][ldw] (n contiguous);   w_t = 1: W is stored [N][ldw] (k contiguous), i.e. W^T is given.
 // C is stored [M][ldc].  A, W are bf16 for the bf16 epilogues and fp32 for the fp32 ones.
+// The partial sum folded into an fp32-output epilogue (kEpiF32Red): with v the
+// tile's result as stored in C, out = (((v + peer[0]) + peer[1]) + ...) + bias[n],
+// the order of the separate reduction kernel, so the two agree bit for bit.
+// Peers, out and lo are [M][ldc] like C; bias is indexed by column.
+constexpr int kMaxFusedPeers = 3;
+struct EpiReduce {
+  const float *peer[kMaxFusedPeers];
+  float *out;          // fp32 sum, or null; may equal C (then C receives the sum only)
+  const float *bias;   // or null
+  void *lo;            // copy of the sum in bf16 (RNE) or fp32, or null
+  int32_t np;          // peers used, 0..kMaxFusedPeers
+  int32_t lo_bf16;     // lo holds bf16 (else fp32)
+};
+
 struct GemmArgs {
   const void *a;
   const void *w;
@@ -25,6 +39,8 @@ struct GemmArgs {
   // fp32 outputs only: the accumulator starts from C's current contents
   // (C += A W, continuing the same k order), else from zero.
   int acc_init = 0;
+  // kEpiF32Red only.
+  EpiReduce red{};
 };
 
 enum {
@@ -37,12 +53,19 @@ enum {
   kEpiDGeluBf16 = 6,     // bf16 inputs, C = bf16(acc * GeLU'(aux)), aux bf16
   kEpiGeluSaveF32 = 7,   // fp32 inputs, C = GeLU(acc), aux = acc (fp32)
   kEpiDGeluF32 = 8,      // fp32 inputs, C = acc * GeLU'(aux), aux fp32
+  kEpiF32Red = 9,        // bf16 inputs, C = acc (fp32) and the partial sum of red (forward layout only)
 };
 
 // Enqueues the GEMM on stream s; returns the launch status.
 hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s);
 
-// Up to 16 independent GEMMs in one launch (same results as one gemm_launch
+// Whether gemm_launch takes p with kEpiF32Red: the forward layout with whole
+// 16-byte vectors along every row of C, the peers, out, bias and lo, on the
+// small-tile path (fewer 128 x 128 tiles than CUs, K % 32 == 0), where the
+// peers' loads fit beside the accumulators without costing occupancy.
+bool gemm_red_ok(const GemmArgs& p);
+
+// Up to 4 independent GEMMs in one launch (same results as one gemm_launch
 // call each), for groups gemm_group_ok accepts: small weight-gradient problems
 // that would each leave CUs idle.  gemm_launch_group returns
 // hipErrorInvalidValue otherwise.

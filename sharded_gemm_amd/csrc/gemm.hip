@@ -167,10 +167,67 @@ __device__ __forceinline__ f32x4_t load_bf16x4(const uint16_t *src, bool full, i
   return v;
 }
 
+// kEpiF32Red: store the partial v, then its sum with the peers' partials and
+// the bias, added in the separate reduction's order.  This whole-vector form
+// takes the peers' vectors already loaded.
+__device__ __forceinline__ void epi_store_red_vec(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v,
+                                                  const f32x4_t (&pv)[kMaxFusedPeers]) {
+  const EpiReduce& r = p.red;
+  const int64_t off = m * ldc + n;
+  if (r.out != p.c) *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + off) = v;
+  f32x4_t sum = v;
+#pragma unroll
+  for (int q = 0; q < kMaxFusedPeers; ++q)
+    if (q < r.np) sum = sum + pv[q];
+  if (r.bias) sum = sum + *reinterpret_cast<const f32x4_t *>(r.bias + n);
+  // The fp32 sum streams past the caches; the next layer's copy, read by its
+  // GEMM next, goes through them (as in the separate reduction).
+  if (r.out) __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out + off));
+  if (r.lo) {
+    if (r.lo_bf16)
+      *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(r.lo) + off) =
+          u32x2_t{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+    else
+      *reinterpret_cast<f32x4_t *>(static_cast<float *>(r.lo) + off) = sum;
+  }
+}
+
+// Loads the peers' vectors itself (all before the first add), or goes element
+// by element past the last column.
+__device__ __forceinline__ void epi_store_red(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v,
+                                              bool full) {
+  const EpiReduce& r = p.red;
+  const int64_t off = m * ldc + n, left = p.N - n;
+  float *C = static_cast<float *>(p.c) + off;
+  if (full) {
+    f32x4_t pv[kMaxFusedPeers];
+#pragma unroll
+    for (int q = 0; q < kMaxFusedPeers; ++q)
+      if (q < r.np) pv[q] = *reinterpret_cast<const f32x4_t *>(r.peer[q] + off);
+    epi_store_red_vec(p, ldc, m, n, v, pv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (e >= left) continue;
+      if (r.out != p.c) C[e] = v[e];
+      float sum = v[e];
+      for (int q = 0; q < r.np; ++q) sum = sum + r.peer[q][off + e];
+      if (r.bias) sum = sum + r.bias[n + e];
+      if (r.out) r.out[off + e] = sum;
+      if (r.lo) {
+        if (r.lo_bf16) static_cast<uint16_t *>(r.lo)[off + e] = static_cast<uint16_t>(bf16_bits_rne(sum));
+        else static_cast<float *>(r.lo)[off + e] = sum;
+      }
+    }
+  }
+}
+
 template <int EPI>
 __device__ __forceinline__ void epi_store(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v, bool full) {
   const int64_t left = p.N - n;
-  if constexpr (EPI == kEpiF32 || EPI == kEpiF32Acc) {
+  if constexpr (EPI == kEpiF32Red) {
+    epi_store_red(p, ldc, m, n, v, full);
+  } else if constexpr (EPI == kEpiF32 || EPI == kEpiF32Acc) {
     float *C = static_cast<float *>(p.c) + m * ldc + n;
     if (full) {
       *reinterpret_cast<f32x4_t *>(C) = v;
@@ -632,11 +689,49 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, int bid) {
   // read stage t-1 into registers (lgkmcnt(0) before it: the DMA is invisible
   // to the compiler's own waits), so stage t+S-1 is issued into its slot.
   const int nst = static_cast<int>(p.K / BK), nu = nst * KK;
+
+  // The partial sum of kEpiF32Red reads the peers' partials of this tile.
+  // With two slots they stream in during the main loop rather than after it:
+  // each stage opening issues one 16-byte load per lane (vector j = fragment
+  // j / np, peer j % np) right after that stage's DMA, so the next opening,
+  // which needs that DMA, may leave exactly this one younger load in flight
+  // (loads complete in issue order).  The load is issued for every lane (rows
+  // past M read row M - 1, never stored), so the wave always counts it.
+  // Vectors the stage openings do not reach are loaded in the epilogue.
+  constexpr bool PF = EPI == kEpiF32Red && S == 2;
+  constexpr int NF = C::TM * C::TN;
+  f32x4_t pv[PF ? NF : 1][kMaxFusedPeers];
+  const int np = PF ? p.red.np : 0;
+  int pf_issued = 0, pf_pending = 0;
+  auto peer_vec = [&](int f, int q) {
+    int64_t m, n;
+    coords(f / C::TN, f % C::TN, &m, &n);
+    m = m < p.M ? m : p.M - 1;
+    n = n < p.N ? n : p.N - 4;   // N % 8 == 0 on this path
+    return *reinterpret_cast<const f32x4_t *>(p.red.peer[q] + m * ldc + n);
+  };
+  auto prefetch = [&]() {
+    pf_pending = 0;
+    if (pf_issued >= NF * np) return;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int q = 0; q < kMaxFusedPeers; ++q)
+        if (q < np && f * np + q == pf_issued) pv[f][q] = peer_vec(f, q);
+    ++pf_issued;
+    pf_pending = 1;
+  };
+
   auto open_stage = [&](int st) {
-    if (st + S - 2 < nst) wait_stages(std::integral_constant<int, S - 2>{}); else wait_vmcnt<0>();
+    if constexpr (PF) {
+      if (pf_pending) wait_vmcnt<1>(); else wait_vmcnt<0>();
+    } else {
+      if (st + S - 2 < nst) wait_stages(std::integral_constant<int, S - 2>{}); else wait_vmcnt<0>();
+    }
     wait_lgkmcnt0();
     __syncthreads();
     if (st + S - 1 < nst) issue(st + S - 1, (st + S - 1) % S);
+    if constexpr (PF) prefetch();
   };
 #pragma unroll
   for (int st = 0; st < S; ++st)
@@ -658,13 +753,23 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, int bid) {
   }
   if (u < nu) mma(fa0, fb0);
 
+  if constexpr (PF) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int q = 0; q < kMaxFusedPeers; ++q)
+        if (q < np && f * np + q >= pf_issued) pv[f][q] = peer_vec(f, q);
+  }
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
       int64_t m, n;
       coords(i, j, &m, &n);
-      if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);   // N % 8 == 0 on this path
+      if (m < p.M && n < p.N) {   // N % 8 == 0 on this path
+        if constexpr (PF) epi_store_red_vec(p, ldc, m, n, acc[i][j], pv[i * C::TN + j]);
+        else epi_store<EPI>(p, ldc, m, n, acc[i][j], true);
+      }
     }
 }
 
@@ -677,7 +782,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) bf16_gemm_dma(GemmA
 // problem q takes workgroups [start[q], start[q+1]).  GEMMs that each leave CUs
 // idle (a few hundred small tiles) then share the chip instead of running one
 // after the other.
-constexpr int kMaxGroup = 16;
+constexpr int kMaxGroup = 4;
 struct GemmGroup {
   GemmArgs p[kMaxGroup];
   int32_t start[kMaxGroup + 1];
@@ -1074,7 +1179,7 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
   }
   if (epi == kEpiF32 && p.acc_init) epi = kEpiF32Acc;
   const bool uses_aux = epi == kEpiGeluSaveBf16 || epi == kEpiDGeluBf16;
-  const bool vec = gemm_vec_ok(p, epi == kEpiF32 || epi == kEpiF32Acc ? 4 : 2, uses_aux);
+  const bool vec = gemm_vec_ok(p, epi == kEpiF32 || epi == kEpiF32Acc || epi == kEpiF32Red ? 4 : 2, uses_aux);
   // The DMA path reads whole 32-deep k steps and 8-column groups unchecked.
   const bool dma_ok = vec && p.K % 32 == 0 && p.K > 0;
   // Forward layout: vector loads on the ragged path too.
@@ -1085,6 +1190,10 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
       case kEpiF32: return dispatch_bf16<kEpiF32, false, false>(p, dma_ok, vec, s);
       case kEpiF32Acc: return dispatch_bf16<kEpiF32Acc, false, false>(p, dma_ok, vec, s);
       case kEpiGeluSaveBf16: return dispatch_bf16<kEpiGeluSaveBf16, false, false>(p, dma_ok, vec, s);
+      case kEpiF32Red:
+        if (!gemm_red_ok(p)) return hipErrorInvalidValue;
+        if (p.K % 64 == 0) return launch_dma<64, 64, 64, 2, kEpiF32Red, false, false, 2, 2>(p, s);
+        return launch_dma<64, 64, 32, 4, kEpiF32Red, false, false, 2, 2>(p, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1103,6 +1212,19 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
     if (epi == kEpiF32Acc) return dispatch_bf16<kEpiF32Acc, true, false>(p, dma_ok, false, s);
   }
   return hipErrorInvalidValue;
+}
+
+bool gemm_red_ok(const GemmArgs& p) {
+  const EpiReduce& r = p.red;
+  const bool small = ((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs;
+  if (p.a_t || p.w_t || p.acc_init || r.np < 0 || r.np > kMaxFusedPeers || !small || p.K <= 0 || p.K % 32 != 0 ||
+      !gemm_vec_ok(p, 4, false))
+    return false;
+  bool ok = !r.bias || aligned16(r.bias);
+  for (int q = 0; q < r.np; ++q) ok = ok && r.peer[q] && aligned16(r.peer[q]);
+  if (r.out) ok = ok && aligned16(r.out);
+  if (r.lo) ok = ok && (reinterpret_cast<uintptr_t>(r.lo) & (r.lo_bf16 ? 7u : 15u)) == 0;
+  return ok;
 }
 
 // The grouped launch covers the weight gradients of a small layer: bf16

@@ -49,6 +49,23 @@ def test_header_symbols_exported():
         assert getattr(lib, n).restype is not None, n
 
 
+def test_kernel_kinds_match_header():
+    """The binding's per-kernel timing names follow the header's TP_KERNEL_*
+    enum, value for value, and the table is TP_KERNEL_KINDS long."""
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tpshard.h")).read(), flags=re.S)
+    kinds = {name.lower(): int(v) for name, v in re.findall(r"\bTP_KERNEL_([A-Z0-9_]+)\s*=\s*(\d+)", src)}
+    n = kinds.pop("kinds")
+    assert len(_abi.TP_KERNEL_NAMES) == n
+    assert {name: k for k, name in enumerate(_abi.TP_KERNEL_NAMES)} == kinds
+
+
+def test_reduce_fusion_constants_match_header():
+    src = open(os.path.join(ROOT, "include", "tpshard.h")).read()
+    vals = dict(re.findall(r"\b(TP_REDUCE_FUSION_[A-Z]+)\s*=\s*(\d+)", src))
+    assert {k: int(v) for k, v in vals.items()} == {"TP_REDUCE_FUSION_AUTO": tp.TP_REDUCE_FUSION_AUTO,
+                                                     "TP_REDUCE_FUSION_OFF": tp.TP_REDUCE_FUSION_OFF}
+
+
 def _oracle_plan(shape, spec):
     boxes, groups = L.shard_boxes(shape, spec)
     return boxes, groups
@@ -153,6 +170,8 @@ def _mlp_args(**kw):
     (dict(Y_ws=FAKE + 100), _abi.TP_ERR_ARG),          # overlaps X
     (dict(Z_i=FAKE + (3 << 20) + 64), _abi.TP_ERR_ARG),  # overlaps Y_ws
     (dict(reduce_workgroups=-1), _abi.TP_ERR_ARG),
+    (dict(reduce_fusion=2), _abi.TP_ERR_ARG),
+    (dict(reduce_fusion=-1), _abi.TP_ERR_ARG),
 ])
 def test_mlp_validation(kw, code):
     lib = _abi.load()

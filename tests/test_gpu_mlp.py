@@ -323,6 +323,96 @@ def test_row_parallel_bias_integer_exact(M, H, F, Rc, Cc, P):
     assert np.array_equal(Zo.cpu().numpy().astype(np.float64), R.reduce_full([z_ref] + peers_cpu, "sum", bias_cpu))
 
 
+def _run_fusion(X, A, B, peers, *, fusion, R=1, C=1, bias=None, z_out=True, in_place=False, x_next=False,
+                two=False):
+    """One call into guarded outputs; returns the CPU copies of Z, Z_out and X_next."""
+    M, H = X.shape
+    F = A.shape[1]
+    Y = Guarded((M, F), X.dtype)
+    Z = Guarded((M, H), torch.float32)
+    Zo = Guarded((M, H), torch.float32) if (z_out and not in_place) else None
+    Xn = Guarded((M, H), X.dtype) if x_next else None
+    s0 = torch.cuda.current_stream()
+    tp.tp_colrow_mlp(X, A, B, Y.t, Z.t, row_chunks=R, col_chunks=C, peer_partials=list(peers),
+                     Z_out=Z.t if in_place else (Zo.t if Zo is not None else None), bias=bias,
+                     X_next=Xn.t if Xn is not None else None, reduce_fusion=fusion,
+                     s_compute=s0, s_reduce=torch.cuda.Stream() if two else s0)
+    torch.cuda.synchronize()
+    outs = [g for g in (Y, Z, Zo, Xn) if g is not None]
+    assert all(g.guards_intact() for g in outs), "write outside an output buffer"
+    return [g.t.cpu() if g is not None else None for g in (Y, Z, Zo, Xn)]
+
+
+@pytest.mark.parametrize("M,H,F,P,Rc,Cc,opts", [
+    (4096, 768, 768, 4, 1, 1, {}),                                  # the GPT-2-small rank at TP = 4
+    (300, 264, 160, 3, 1, 1, {"bias": True, "x_next": True}),      # ragged rows, bias, bf16 next input
+    (512, 384, 256, 4, 1, 1, {"in_place": True}),                  # Z_out = Z_i
+    (512, 384, 256, 2, 1, 1, {"z_out": False, "x_next": True}),    # only the next layer's input
+    (515, 256, 96, 1, 1, 1, {"bias": True}),                       # no peers: the bias alone
+    (1000, 512, 256, 4, 2, 2, {"bias": True, "two": True}),        # only the final block folds
+    (512, 384, 256, 5, 1, 1, {}),                                  # 4 peers: separate reduction
+    (520, 392, 200, 3, 1, 1, {}),                                  # K % 32 != 0: separate reduction
+])
+def test_reduce_fusion_same_bits(M, H, F, P, Rc, Cc, opts):
+    """GEMM2 with the block's reduction folded into its epilogue writes the
+    same bits as GEMM2 followed by the separate reduction kernel: Z_i, Z_out
+    (or Z_i in place) and X_next; both against the oracle."""
+    announce(f"mlp reduce fusion M={M} H={H} F={F} P={P} R={Rc} C={Cc} {sorted(opts)}")
+    X = inputs.normal((M, H), 341, 1.0, "bf16")
+    A = inputs.normal((H, F), 342, 1.0 / np.sqrt(H), "bf16")
+    B = inputs.normal((F, H), 343, 1.0 / np.sqrt(F), "bf16")
+    peers_cpu = [inputs.normal((M, H), 350 + p) for p in range(P - 1)]
+    bias_cpu = inputs.normal((H,), 349) if opts.get("bias") else None
+    kw = {k: v for k, v in opts.items() if k != "bias"}
+    kw.update(R=Rc, C=Cc, bias=bias_cpu.cuda() if bias_cpu is not None else None)
+    Xd, Ad, Bd, peers = X.cuda(), A.cuda(), B.cuda(), [p.cuda() for p in peers_cpu]
+    fused = _run_fusion(Xd, Ad, Bd, peers, fusion=tp.TP_REDUCE_FUSION_AUTO, **kw)
+    apart = _run_fusion(Xd, Ad, Bd, peers, fusion=tp.TP_REDUCE_FUSION_OFF, **kw)
+    for a, b in zip(fused, apart):
+        assert (a is None) == (b is None)
+        if a is not None:
+            assert np.array_equal(bits(a), bits(b))
+    Y, Z, Zo, Xn = fused
+    z_ref = O.mlp_rank(X, A, B)
+    total = R.reduce_full([z_ref] + peers_cpu, "sum", bias_cpu)
+    assert rel_err(Z, total if opts.get("in_place") else z_ref) <= TOL_BF16
+    if Zo is not None:
+        assert rel_err(Zo, total) <= TOL_BF16
+    if Xn is not None:
+        assert rel_err(Xn.float(), total) <= TOL_BF16
+
+
+def test_timing_reports_the_fused_kernel():
+    """With the reduction in GEMM2's epilogue the per-kernel timing sees one
+    gemm2_reduce launch whose work is its algorithmic bytes (Y and B_i read,
+    the peers' partials read, Z_i and Z_out written); with fusion off, a GEMM2
+    and a reduce launch."""
+    announce("mlp timing of the fused kernel")
+    M, H, F, P = 512, 384, 256, 3
+    X = inputs.normal((M, H), 361, 1.0, "bf16").cuda()
+    A = inputs.normal((H, F), 362, 1.0 / np.sqrt(H), "bf16").cuda()
+    B = inputs.normal((F, H), 363, 1.0 / np.sqrt(F), "bf16").cuda()
+    peers = [inputs.normal((M, H), 370 + p).cuda() for p in range(P - 1)]
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z, Zo = torch.empty((M, H), device="cuda"), torch.empty((M, H), device="cuda")
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        tp.tp_colrow_mlp(X, A, B, Y, Z, peer_partials=peers, Z_out=Zo)
+        fused = tp.tp_timing_read()
+        tp.tp_colrow_mlp(X, A, B, Y, Z, peer_partials=peers, Z_out=Zo, reduce_fusion=tp.TP_REDUCE_FUSION_OFF)
+        apart = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    assert fused["gemm2_reduce"]["launches"] == 1
+    assert fused["gemm2"]["launches"] == 0 and fused["reduce"]["launches"] == 0
+    assert fused["gemm2_reduce"]["work"] == 2 * (M * F + F * H) + 4 * (P - 1) * M * H + 2 * 4 * M * H
+    assert fused["gemm2_reduce"]["total_ms"] > 0
+    assert apart["gemm2_reduce"]["launches"] == 0
+    assert apart["gemm2"]["launches"] == 1 and apart["reduce"]["launches"] == 1
+    assert apart["gemm2"]["work"] == 2 * M * H * F
+
+
 def test_max_ranks_integer_exact():
     """P = 64 virtual ranks (63 peers), chunked, on two streams: exact."""
     announce("mlp P=64 integer exact")

@@ -65,6 +65,10 @@ class MlpStep:
     serial = False
     reduce_wgs = 0
     reduce_fusion = tp.TP_REDUCE_FUSION_AUTO
+    # The row-parallel all-reduce works in place on the partial output, as
+    # torch.distributed.all_reduce does; separate_output keeps Z_i and writes
+    # the sum to its own buffer instead.
+    separate_output = False
 
     def __init__(self, w, split_weights: bool, seq: bool = False):
         self.w = w
@@ -106,8 +110,11 @@ class MlpStep:
         self.s0 = torch.cuda.Stream()     # a side stream: graph capture needs one
         self.s1 = torch.cuda.Stream()
 
+    def _z_out(self):
+        return self.Zo if self.separate_output else self.Z
+
     def result(self):
-        return self.Zs[-1] if self.seq else self.Zo
+        return self.Zs[-1] if self.seq else self._z_out()
 
     def prepare(self):
         """Marshal the step's library calls once (the buffers never move)."""
@@ -118,7 +125,7 @@ class MlpStep:
                                                      stream=self.s0, prepare=True)
         self.mlp = tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
                                     col_chunks=self.w.C, peer_partials=self.peers,
-                                    Z_out=None if self.seq else self.Zo, s_compute=self.s0,
+                                    Z_out=None if self.seq else self._z_out(), s_compute=self.s0,
                                     s_reduce=self.s0 if self.serial else self.s1,
                                     reduce_workgroups=self.reduce_wgs, X_shards=self.Xb if self.seq else None,
                                     Z_split=self.Zs if self.seq else None, reduce_fusion=self.reduce_fusion,
@@ -141,6 +148,8 @@ class MlpStep:
                "tp": w.P, "row_chunks": w.R, "col_chunks": w.C, "weights_cut_each_step": self.split,
                "reduce_stream": "compute" if self.serial else "second",
                "reduce_fusion": "auto" if self.reduce_fusion == tp.TP_REDUCE_FUSION_AUTO else "off",
+               "reduce_output": ("reduce-scattered blocks" if self.seq else
+                                 "separate buffer" if self.separate_output else "in place over the partial (all-reduce)"),
                "peers": "virtual ranks 1..P-1, partials precomputed by the same path"}
         if self.seq:
             cfg["sequence_parallel"] = {"blocks": w.P, "input": "all-gathered from P sequence blocks",
@@ -535,7 +544,7 @@ def kernel_table(stats, steps):
     return out
 
 
-def roofline(kernels, dtype, workload):
+def roofline(kernels, dtype, workload, default_schedule=True):
     """Roofline entry of the dominant kernel.  In an MLP step that is the slower
     of the two GEMMs (together more than half the step; the weight cuts are two
     short launches whose per-launch event overhead would otherwise let them
@@ -546,7 +555,9 @@ def roofline(kernels, dtype, workload):
     pool = [k for k in kernels if k.startswith("gemm")] or list(kernels)
     name = max(pool, key=lambda k: kernels[k]["ms_per_step"])
     k = kernels[name]
-    traffic = measured_traffic(workload, name)
+    # The counters were taken with the default schedule and outputs; another
+    # schedule moves other bytes.
+    traffic = measured_traffic(workload, name) if default_schedule else None
     if k["unit"] == "TFLOP/s":
         peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
         return {"kernel": name, "bound": "mfma" if dtype == "bf16" else "alu", "achieved": k["achieved"],
@@ -617,6 +628,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--serial", action="store_true", help="run the reduce on the compute stream")
+    ap.add_argument("--separate-output", action="store_true",
+                    help="write the reduced output to its own buffer instead of in place over the partial")
     ap.add_argument("--no-reduce-fusion", action="store_true",
                     help="always run the forward's reduction as its own kernel, never in GEMM2's epilogue")
     ap.add_argument("--reduce-wgs", type=int, default=0,
@@ -648,6 +661,7 @@ def main():
     wl.serial, wl.reduce_wgs = args.serial, args.reduce_wgs
     if args.no_reduce_fusion:
         wl.reduce_fusion = tp.TP_REDUCE_FUSION_OFF
+    wl.separate_output = args.separate_output
     if hasattr(wl, "prepare"):
         wl.prepare()
     dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
@@ -750,7 +764,8 @@ def main():
     rec = {"metric": METRIC, "value": value, "unit": wl.unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded N(0,1)/N(0,0.02) tensors)",
-           "config": wl.config(), "roofline": roofline(kernels, dtype, args.workload), "cpu_baseline": cpu,
+           "config": wl.config(), "roofline": roofline(kernels, dtype, args.workload, default_schedule=not (
+               args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output)), "cpu_baseline": cpu,
            "kernels": kernels, "timed_as": "hip graph replay" if use_graph else "eager launches",
            "ms_per_step_eager": ms_eager_plain, "ms_per_step_graph": ms_graph,
            "ms_per_step_eager_with_kernel_events": ms_eager,

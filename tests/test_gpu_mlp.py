@@ -202,6 +202,14 @@ def test_gpt2_small_tp4_full():
     full = O.mlp_all_ranks(X, [oa[i] for i in range(4)], [ob[i] for i in range(4)])
     assert rel_err(Zo, full) <= TOL_BF16
     assert rel_err(Zo, O.mlp_unsharded(X, A, B)) <= TOL_BF16
+    # the sum in place over the partial (the all-reduce's form, as timed): same bits
+    Yg = torch.empty((w.M, w.F), dtype=torch.bfloat16, device="cuda")
+    Zg = Guarded((w.M, w.H), torch.float32)
+    tp.tp_colrow_mlp(Xg, A_sh[0], B_sh[0], Yg, Zg.t, peer_partials=peers, Z_out=Zg.t,
+                     s_reduce=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert Zg.guards_intact()
+    assert np.array_equal(bits(Zg.t.cpu()), bits(Zo))
 
 
 def _sample_rows(M, Rc, per_chunk):
@@ -230,6 +238,15 @@ def _large_case(w, per_chunk):
     assert np.array_equal(bits(Y0), bits(Y0s))
     assert np.array_equal(bits(Z0), bits(Z0s))
     assert np.array_equal(bits(Zo), bits(Zos))
+    announce(f"mlp {w.name}: rank 0, R={w.R} C={w.C}, two streams, sum in place over the partial")
+    Yi = torch.empty((w.M, w.F), dtype=torch.bfloat16, device="cuda")
+    Zi = Guarded((w.M, w.H), torch.float32)
+    tp.tp_colrow_mlp(X, As[0], Bs[0], Yi, Zi.t, row_chunks=w.R, col_chunks=w.C, peer_partials=peers, Z_out=Zi.t,
+                     s_reduce=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert Zi.guards_intact()
+    assert np.array_equal(bits(Zi.t.cpu()), bits(Zo))
+    del Yi, Zi
     rows = _sample_rows(w.M, w.R, per_chunk)
     Xc = X.cpu()
     announce(f"mlp {w.name}: oracle on {len(rows)} sampled rows")

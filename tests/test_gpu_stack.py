@@ -43,7 +43,8 @@ def _layers_integer(M, H, Fs, P, seed):
     return out
 
 
-def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, keep_z=True, prepared=False):
+def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, keep_z=True, prepared=False,
+              fusion=tp.TP_REDUCE_FUSION_AUTO):
     """The stack on the GPU into guarded buffers; returns per layer (Z_out, X_next)
     CPU copies.  prepared: marshal the call once and replay it twice, the
     outputs overwritten with NaN in between."""
@@ -61,7 +62,7 @@ def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, kee
                          Z_i=Zi, row_chunks=R, col_chunks=C, peer_partials=[p.cuda() for p in layer["peers"]],
                          Z_out=zs[l].t if keep_z else None, act=act,
                          bias=layer["bias"].cuda() if layer.get("bias") is not None else None,
-                         X_next=xs[l + 1].t))
+                         X_next=xs[l + 1].t, reduce_fusion=fusion))
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream() if two_streams else s0
     if prepared:
@@ -130,6 +131,28 @@ def test_stack_equals_layer_by_layer_calls_bitwise():
         x = xn
     ref = O.mlp_stack(X0, layers, dtype="bf16")
     assert rel_err(got[-1][0], ref[-1][0]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("R,keep_z", [(1, True), (2, True), (1, False)])
+def test_stack_reduce_fusion_same_bits(R, keep_z):
+    """Layers whose reduction runs in GEMM2's epilogue (every layer with one
+    block; the last block of the last layer with two row chunks) give the bits
+    of the separate reduction kernel, Z_out and the bf16 next input alike."""
+    announce(f"stack reduce fusion R={R} keep_z={keep_z}")
+    M, H, F, P = 1024, 384, 256, 4
+    X0 = inputs.normal((M, H), seed=1701, dtype="bf16")
+    layers = [{"A_i": inputs.normal((H, F), seed=1710 + l, std=0.05, dtype="bf16"),
+               "B_i": inputs.normal((F, H), seed=1720 + l, std=0.05, dtype="bf16"),
+               "peers": [inputs.normal((M, H), seed=1730 + 10 * l + p) for p in range(P - 1)],
+               "bias": inputs.normal((H,), seed=1750 + l)} for l in range(2)]
+    fused = run_stack(X0, layers, R=R, act=tp.TP_ACT_GELU_ERF, keep_z=keep_z)
+    apart = run_stack(X0, layers, R=R, act=tp.TP_ACT_GELU_ERF, keep_z=keep_z, fusion=tp.TP_REDUCE_FUSION_OFF)
+    for (z, xn), (zr, xr) in zip(fused, apart):
+        if keep_z:
+            assert np.array_equal(bits(z), bits(zr))
+        assert np.array_equal(bits(xn), bits(xr))
+    ref = O.mlp_stack(X0, layers, dtype="bf16")
+    assert rel_err(fused[-1][1].float(), ref[-1][0]) <= TOL_BF16
 
 
 def test_prepared_stack_replays():

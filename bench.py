@@ -46,7 +46,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # GEMM2 with the reduction in its epilogue moves far more bytes than its flops
 # need time for (GPT-2 shape: about 70 MB against 4.8 GFLOP), so the library
 # counts its work in bytes and it is priced against HBM.
-BYTE_KERNELS = ("gemm2_reduce",)
+BYTE_KERNELS = ("gemm2_reduce", "gemm_dgrad_reduce")
 
 
 def log(msg):
@@ -205,6 +205,8 @@ class BwdStep:
 
     serial = False
     reduce_wgs = 0
+    reduce_fusion = tp.TP_REDUCE_FUSION_AUTO
+    separate_output = False   # as in MlpStep: the input gradient's sum goes in place by default
 
     def __init__(self, w, seq: bool = False):
         self.w = w
@@ -251,9 +253,11 @@ class BwdStep:
         """Marshal the step's library call once (the buffers never move)."""
         self.call = tp.tp_colrow_mlp_backward(
             self.X, self.As[0], self.Bs[0], self.Hs, self.Y, self.dZ, self.dH, self.dX, self.dA, self.dB,
-            row_chunks=self.w.R, peer_dX=self.peers, dX_out=None if self.seq else self.dXo, s_compute=self.s0,
+            row_chunks=self.w.R, peer_dX=self.peers,
+            dX_out=None if self.seq else (self.dXo if self.separate_output else self.dX), s_compute=self.s0,
             s_reduce=self.s0 if self.serial else self.s1, reduce_workgroups=self.reduce_wgs,
-            dZ_shards=self.dZb if self.seq else None, dX_split=self.dXs if self.seq else None, prepare=True)
+            dZ_shards=self.dZb if self.seq else None, dX_split=self.dXs if self.seq else None,
+            reduce_fusion=self.reduce_fusion, prepare=True)
 
     def step(self):
         self.call()
@@ -269,6 +273,9 @@ class BwdStep:
         cfg = {"workload": w.name + ("-sp" if self.seq else "") + "-bwd", "pass": "backward", "tokens": w.M,
                "hidden": w.H, "ffn_per_rank": w.F, "tp": w.P, "row_chunks": w.R,
                "reduce_stream": "compute" if self.serial else "second",
+               "reduce_fusion": "auto" if self.reduce_fusion == tp.TP_REDUCE_FUSION_AUTO else "off",
+               "reduce_output": ("reduce-scattered blocks" if self.seq else
+                                 "separate buffer" if self.separate_output else "in place over the partial (all-reduce)"),
                "peers": "virtual ranks 1..P-1, input-gradient partials precomputed by the same path"}
         if self.seq:
             cfg["sequence_parallel"] = {"blocks": w.P, "output_gradient": "all-gathered from P sequence blocks",

@@ -419,6 +419,15 @@ typedef struct {
   float *const *dX_split; /* optional host array of S device pointers, each [M/S, H] fp32:
                         the reduce-scattered input gradient (replaces dX_out, which
                         must be NULL) */
+  int32_t reduce_fusion; /* TP_REDUCE_FUSION_AUTO (0): the dX GEMM adds the peers' input
+                        gradients in its epilogue and writes dX_out itself, and the
+                        call runs on s_compute alone, when every chunk qualifies:
+                        bf16, P <= 4, dX_out (not dX_split), 16-byte aligned rows,
+                        F a multiple of 32 and fewer than 256 output tiles of
+                        128 x 128 per chunk (small layers, whose GEMMs are too short
+                        for the hand-off to s_reduce to pay); otherwise, and always
+                        with TP_REDUCE_FUSION_OFF (1), the reduction runs on
+                        s_reduce beside the weight-gradient GEMMs.  Same bits. */
 } tp_mlp_bwd_args;
 
 /*
@@ -432,6 +441,8 @@ typedef struct {
  * s_compute runs dA_i += X[r]^T dH[r] and dB_i += Y_i[r]^T dZ[r].  The weight
  * gradients continue one fp32 accumulation across chunks (each GEMM starts
  * from the previous chunk's result), so the result does not depend on R.
+ * Small layers instead sum dX over the ranks in the dX GEMM's epilogue on
+ * s_compute (reduce_fusion), with the same bits.
  * Before returning, s_compute waits for s_reduce.  Capturable into a HIP graph.
  * With sequence parallelism, chunk r's rows of dZ are gathered on s_reduce
  * ahead of chunk r's GEMMs and dX is reduce-scattered into dX_split.
@@ -446,12 +457,14 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *args, tp_stream_t s_compute, t
 /* ---- per-kernel timing (measurement support) ---------------------------- */
 /* Kernel families timed by the optional instrumentation below: the forward's
  * GEMMs, the backward's input-gradient GEMMs (dH and dX) and its
- * weight-gradient GEMMs (dA and dB), the gather kernel, and GEMM2 with the
- * reduction folded into its epilogue (memory-bound: its work counts bytes,
- * the operands and the peers' partials read once and each output written once). */
+ * weight-gradient GEMMs (dA and dB), the gather kernel, GEMM2 with the
+ * reduction folded into its epilogue and the dX GEMM with the input gradient's
+ * reduction folded into its epilogue (both memory-bound: their work counts
+ * bytes, the operands and the peers' partials read once and each output
+ * written once). */
 enum { TP_KERNEL_MATERIALIZE = 0, TP_KERNEL_GEMM1 = 1, TP_KERNEL_GEMM2 = 2, TP_KERNEL_REDUCE = 3,
        TP_KERNEL_GEMM_DGRAD = 4, TP_KERNEL_GEMM_WGRAD = 5, TP_KERNEL_GATHER = 6,
-       TP_KERNEL_GEMM2_REDUCE = 7, TP_KERNEL_KINDS = 8 };
+       TP_KERNEL_GEMM2_REDUCE = 7, TP_KERNEL_GEMM_DGRAD_REDUCE = 8, TP_KERNEL_KINDS = 9 };
 
 typedef struct {
   int64_t launches;  /* kernel launches timed since the last read */

@@ -40,7 +40,8 @@ TP_REDUCE_OP_MIN = 2
 EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_binary", "tp_infer_matmul_dims_mapping", "tp_shard_materialize", "tp_shard_materialize_batch", "tp_shard_gather",
            "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_stack", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
-TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather", "gemm2_reduce")
+TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather", "gemm2_reduce",
+                   "gemm_dgrad_reduce")
 
 TP_REDUCE_FUSION_AUTO = 0
 TP_REDUCE_FUSION_OFF = 1
@@ -102,7 +103,8 @@ class tp_mlp_bwd_args(C.Structure):
                 ("accumulate", C.c_int32), ("row_chunks", C.c_int64), ("P", C.c_int64),
                 ("peer_dX", C.POINTER(C.c_void_p)), ("dX_out", C.c_void_p),
                 ("reduce_workgroups", C.c_int64),
-                ("seq_splits", C.c_int64), ("dZ_shards", C.POINTER(C.c_void_p)), ("dX_split", C.POINTER(C.c_void_p))]
+                ("seq_splits", C.c_int64), ("dZ_shards", C.POINTER(C.c_void_p)), ("dX_split", C.POINTER(C.c_void_p)),
+                ("reduce_fusion", C.c_int32)]
 
 
 class tp_materialize_item(C.Structure):
@@ -529,9 +531,11 @@ def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None, prepare=False):
 
 def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *, row_chunks=1, peer_dX=(),
                            dX_out=None, act=TP_ACT_GELU_ERF, accumulate=False, s_compute=None, s_reduce=None,
-                           reduce_workgroups=0, dZ_shards=None, dX_split=None, prepare=False):
+                           reduce_workgroups=0, dZ_shards=None, dX_split=None,
+                           reduce_fusion=TP_REDUCE_FUSION_AUTO, prepare=False):
     """Backward of one rank's MLP share: dH_ws = (dZ B_i^T) * act'(H_i); dX_i = dH_ws A_i^T;
     dX_out = dX_i + sum(peers); dA_i (+)= X^T dH_ws; dB_i (+)= Y_i^T dZ.
+    reduce_fusion as in tp_colrow_mlp (for the sum of dX).
 
     Sequence parallelism: with ``dZ_shards`` dZ is a workspace the call fills by
     all-gathering them; with ``dX_split`` the input gradient is reduce-scattered."""
@@ -560,7 +564,7 @@ def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *
                            dH_ws=_ptr(dH_ws), dX_i=_ptr(dX_i), dA_i=_ptr(dA_i), dB_i=_ptr(dB_i),
                            accumulate=1 if accumulate else 0, row_chunks=row_chunks, P=1 + len(peers),
                            peer_dX=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
-                           dX_out=_ptr(dX_out), reduce_workgroups=reduce_workgroups)
+                           dX_out=_ptr(dX_out), reduce_workgroups=reduce_workgroups, reduce_fusion=reduce_fusion)
     S, gs, xs = _seq_arrays(dZ_shards, dX_split)
     args.seq_splits, args.dZ_shards, args.dX_split = S, gs, xs
     sc = _stream_ptr(s_compute)

@@ -623,6 +623,8 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   if (rc != TP_OK) return rc;
   if (a->P > 1 && (!a->peer_dX || !(a->dX_out || a->dX_split))) return fail(TP_ERR_ARG, "P > 1 needs peer_dX and dX_out (or dX_split)");
   if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
+  if (a->reduce_fusion != TP_REDUCE_FUSION_AUTO && a->reduce_fusion != TP_REDUCE_FUSION_OFF)
+    return fail(TP_ERR_ARG, "unknown reduce_fusion %d", a->reduce_fusion);
   const int64_t M = a->M, H = a->H, F = a->F;
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) || (M / a->row_chunks) * H >= (int64_t(1) << 31))
     return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
@@ -655,10 +657,28 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
 
   hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
   const int64_t R = a->row_chunks, Mr = M / R;
+  const bool bf16 = a->dtype == TP_BF16;
+  // dX_i[r] = dH[r] A_i^T: A_i is [H][F], i.e. W^T for W = A_i^T.  With the
+  // reduction folded in, the epilogue also sums the peers' dX[r] into dX_out.
+  auto dx_gemm = [&](int64_t r, bool fused) {
+    GemmArgs gx{static_cast<const char *>(a->dH_ws) + r * Mr * F * es, a->A_i, a->dX_i + r * Mr * H, Mr, H, F, F, F, H};
+    gx.w_t = 1;
+    if (fused) {
+      gx.red.np = static_cast<int32_t>(a->P - 1);
+      for (int64_t p = 1; p < a->P; ++p) gx.red.peer[p - 1] = a->peer_dX[p - 1] + r * Mr * H;
+      gx.red.out = a->dX_out + r * Mr * H;
+    }
+    return gx;
+  };
+  // Small layers sum dX in the dX GEMM's epilogue: their GEMMs are too short
+  // for the hand-off to s_reduce and back to pay for the overlap it buys.
+  bool fuse = reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && bf16 && !a->dX_split && a->dX_out &&
+              a->P - 1 <= kMaxFusedPeers;
+  for (int64_t r = 0; fuse && r < R; ++r) fuse = gemm_red_ok(dx_gemm(r, true));
   // As in the forward: a second stream only pays when its work can run beside
   // GEMMs: a chunk's reduce beside that chunk's weight-gradient GEMMs, the
   // next chunk's gather beside this chunk's GEMMs.
-  const bool two = (s0 != s1) && (reduce || (gather && R > 1));
+  const bool two = (s0 != s1) && ((reduce && !fuse) || (gather && R > 1));
   hipEvent_t *ev = nullptr;
   if (two) {
     if ((rc = get_events(static_cast<size_t>(2 * R + 2), &ev)) != TP_OK) return rc;
@@ -682,7 +702,6 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   };
   if (gather && (rc = gather_chunk(0)) != TP_OK) return rc;
 
-  const bool bf16 = a->dtype == TP_BF16;
   const int epi_dh = bf16 ? (gelu ? kEpiDGeluBf16 : kEpiIdentBf16) : (gelu ? kEpiDGeluF32 : kEpiPlainF32);
   const int epi_f32 = bf16 ? kEpiF32 : kEpiPlainF32;
   const char *X = static_cast<const char *>(a->X), *Yi = static_cast<const char *>(a->Y_i);
@@ -704,14 +723,22 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
     e = gemm_launch(gd, epi_dh, s0);
     if (e != hipSuccess) return hip_fail(e, "dH GEMM launch");
     timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD, 2.0 * Mr * F * H);
-    // dX_i[r] = dH[r] A_i^T: A_i is [H][F], i.e. W^T for W = A_i^T.
-    GemmArgs gx{dH + r * Mr * F * es, a->A_i, a->dX_i + r * Mr * H, Mr, H, F, F, F, H};
-    gx.w_t = 1;
-    t0 = timing_begin(s0);
-    e = gemm_launch(gx, epi_f32, s0);
-    if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
-    timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD, 2.0 * Mr * H * F);
-    if (reduce) {
+    if (fuse) {
+      const GemmArgs gx = dx_gemm(r, true);
+      t0 = timing_begin(s0);
+      e = gemm_launch(gx, kEpiF32Red, s0);
+      if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
+      const double cells = static_cast<double>(Mr) * H;
+      timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD_REDUCE,
+                 es * (static_cast<double>(Mr) * F + static_cast<double>(F) * H) + 4.0 * gx.red.np * cells +
+                     (gx.red.out != gx.c ? 4.0 * cells : 0.0) + 4.0 * cells);
+    } else {
+      t0 = timing_begin(s0);
+      e = gemm_launch(dx_gemm(r, false), epi_f32, s0);
+      if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
+      timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD, 2.0 * Mr * H * F);
+    }
+    if (reduce && !fuse) {
       hipStream_t sr = s0;
       if (two) {
         if ((e = hipEventRecord(ev_red[r], s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -53,13 +53,13 @@ enum {
   kEpiDGeluBf16 = 6,     // bf16 inputs, C = bf16(acc * GeLU'(aux)), aux bf16
   kEpiGeluSaveF32 = 7,   // fp32 inputs, C = GeLU(acc), aux = acc (fp32)
   kEpiDGeluF32 = 8,      // fp32 inputs, C = acc * GeLU'(aux), aux fp32
-  kEpiF32Red = 9,        // bf16 inputs, C = acc (fp32) and the partial sum of red (forward layout only)
+  kEpiF32Red = 9,        // bf16 inputs, C = acc (fp32) and the partial sum of red (A not transposed)
 };
 
 // Enqueues the GEMM on stream s; returns the launch status.
 hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s);
 
-// Whether gemm_launch takes p with kEpiF32Red: the forward layout with whole
+// Whether gemm_launch takes p with kEpiF32Red: A not transposed, whole
 // 16-byte vectors along every row of C, the peers, out, bias and lo, on the
 // small-tile path (fewer 128 x 128 tiles than CUs, K % 32 == 0), where the
 // peers' loads fit beside the accumulators without costing occupancy.

@@ -1201,6 +1201,10 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
   // gradients (A given transposed).  Their ragged path loads element-wise.
   if (!p.a_t && p.w_t) {
     switch (epi) {
+      case kEpiF32Red:
+        if (!gemm_red_ok(p)) return hipErrorInvalidValue;
+        if (p.K % 64 == 0) return launch_dma<64, 64, 64, 2, kEpiF32Red, false, true, 2, 2>(p, s);
+        return launch_dma<64, 64, 32, 4, kEpiF32Red, false, true, 2, 2>(p, s);
       case kEpiDGeluBf16: return dispatch_bf16<kEpiDGeluBf16, false, true>(p, dma_ok, false, s);
       case kEpiIdentBf16: return dispatch_bf16<kEpiIdentBf16, false, true>(p, dma_ok, false, s);
       case kEpiF32: return dispatch_bf16<kEpiF32, false, true>(p, dma_ok, false, s);
@@ -1217,7 +1221,7 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
 bool gemm_red_ok(const GemmArgs& p) {
   const EpiReduce& r = p.red;
   const bool small = ((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs;
-  if (p.a_t || p.w_t || p.acc_init || r.np < 0 || r.np > kMaxFusedPeers || !small || p.K <= 0 || p.K % 32 != 0 ||
+  if (p.a_t || p.acc_init || r.np < 0 || r.np > kMaxFusedPeers || !small || p.K <= 0 || p.K % 32 != 0 ||
       !gemm_vec_ok(p, 4, false))
     return false;
   bool ok = !r.bias || aligned16(r.bias);

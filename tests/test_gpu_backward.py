@@ -177,6 +177,81 @@ def test_backward_gelu_fp32_ragged(M, H, F, Rc, P):
     assert rel_err(dXo, R.reduce_full([g["dX_i"]] + [p.double().numpy() for p in peers])) <= TOL_F32
 
 
+def _bwd_fusion(Xd, Ad, Bd, Hs, Y, dZd, peers, *, fusion, R=1, in_place=False):
+    M, H = Xd.shape
+    F = Ad.shape[1]
+    dH = Guarded((M, F), Xd.dtype)
+    dX = Guarded((M, H), torch.float32)
+    dXo = None if in_place else Guarded((M, H), torch.float32)
+    dA, dB = Guarded((H, F), torch.float32), Guarded((F, H), torch.float32)
+    tp.tp_colrow_mlp_backward(Xd, Ad, Bd, Hs, Y, dZd, dH.t, dX.t, dA.t, dB.t, row_chunks=R, peer_dX=peers,
+                              dX_out=dX.t if in_place else dXo.t, reduce_fusion=fusion,
+                              s_compute=torch.cuda.current_stream(), s_reduce=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    outs = [g for g in (dH, dX, dXo, dA, dB) if g is not None]
+    assert all(g.guards_intact() for g in outs), "write outside an output buffer"
+    return [g.t.cpu() for g in outs]
+
+
+@pytest.mark.parametrize("M,H,F,P,Rc,in_place", [
+    (4096, 768, 768, 4, 1, False),    # the GPT-2-small rank at TP = 4
+    (4096, 768, 768, 4, 1, True),     # dX_out = dX_i (the all-reduce's form)
+    (512, 384, 256, 3, 2, False),     # every chunk folds
+    (300, 264, 160, 2, 3, False),     # ragged rows
+    (512, 384, 256, 5, 1, False),     # 4 peers: reduction on s_reduce
+    (520, 392, 200, 3, 1, False),     # K % 32 != 0: reduction on s_reduce
+])
+def test_backward_reduce_fusion_same_bits(M, H, F, P, Rc, in_place):
+    """The dX GEMM with the ranks' sum in its epilogue gives the bits of the dX
+    GEMM followed by the separate reduction: dH, dX_i, dX_out, dA_i, dB_i."""
+    announce(f"backward reduce fusion M={M} H={H} F={F} P={P} R={Rc} in_place={in_place}")
+    X = inputs.normal((M, H), 541, 1.0, "bf16")
+    A = inputs.normal((H, F), 542, 1.0 / np.sqrt(H), "bf16")
+    B = inputs.normal((F, H), 543, 1.0 / np.sqrt(F), "bf16")
+    dZ = inputs.normal((M, H), 544, 1.0, "bf16")
+    peers_cpu = [inputs.normal((M, H), 550 + p) for p in range(P - 1)]
+    Xd, Ad, Bd, dZd = X.cuda(), A.cuda(), B.cuda(), dZ.cuda()
+    peers = [p.cuda() for p in peers_cpu]
+    Y, Hs = forward(Xd, Ad, Bd)
+    fused = _bwd_fusion(Xd, Ad, Bd, Hs, Y, dZd, peers, fusion=tp.TP_REDUCE_FUSION_AUTO, R=Rc, in_place=in_place)
+    apart = _bwd_fusion(Xd, Ad, Bd, Hs, Y, dZd, peers, fusion=tp.TP_REDUCE_FUSION_OFF, R=Rc, in_place=in_place)
+    for a, b in zip(fused, apart):
+        assert np.array_equal(bits(a), bits(b))
+    g = O.backward_rank(X, A, B, dZ)
+    total = R.reduce_full([g["dX_i"]] + [p.double().numpy() for p in peers_cpu])
+    dX_sum = fused[1] if in_place else fused[2]
+    assert rel_err(dX_sum, total) <= TOL_BF16
+    assert rel_err(fused[-2], g["dA_i"]) <= TOL_BF16 and rel_err(fused[-1], g["dB_i"]) <= TOL_BF16
+
+
+def test_backward_timing_reports_the_fused_kernel():
+    """Per-kernel timing sees one gemm_dgrad_reduce launch per chunk, whose work
+    is its algorithmic bytes, and no separate reduction."""
+    announce("backward timing of the fused kernel")
+    M, H, F, P, Rc = 512, 384, 256, 3, 2
+    X = inputs.normal((M, H), 561, 1.0, "bf16").cuda()
+    A = inputs.normal((H, F), 562, 1.0 / np.sqrt(H), "bf16").cuda()
+    B = inputs.normal((F, H), 563, 1.0 / np.sqrt(F), "bf16").cuda()
+    dZ = inputs.normal((M, H), 564, 1.0, "bf16").cuda()
+    peers = [inputs.normal((M, H), 570 + p).cuda() for p in range(P - 1)]
+    Y, Hs = forward(X, A, B)
+    dH = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    dX, dXo = torch.empty((M, H), device="cuda"), torch.empty((M, H), device="cuda")
+    dA, dB = torch.empty((H, F), device="cuda"), torch.empty((F, H), device="cuda")
+    torch.cuda.synchronize()
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        tp.tp_colrow_mlp_backward(X, A, B, Hs, Y, dZ, dH, dX, dA, dB, row_chunks=Rc, peer_dX=peers, dX_out=dXo)
+        st = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    Mr = M // Rc
+    assert st["gemm_dgrad_reduce"]["launches"] == Rc and st["reduce"]["launches"] == 0
+    assert st["gemm_dgrad"]["launches"] == Rc          # the dH GEMMs
+    assert st["gemm_dgrad_reduce"]["work"] == Rc * (2 * (Mr * F + F * H) + 4 * (P - 1) * Mr * H + 2 * 4 * Mr * H)
+
+
 def test_backward_chunks_do_not_change_a_bit():
     """Row chunks split dH and dX by rows and continue one accumulation of the
     weight gradients, so R = 1, 2, 4 give identical bits (serial or two streams)."""

@@ -120,8 +120,10 @@ class MlpStep:
         """Marshal the step's library calls once (the buffers never move)."""
         self.cut = None
         if self.split:
-            # both weight cuts in one batched call (one launch)
-            self.cut = tp.tp_shard_materialize_batch([(self.A, self.sa, self.As), (self.B, self.sb, self.Bs)],
+            # rank 0's column shard of A and row shard of B in one batched call
+            # (one launch): each rank materialises its own share
+            self.cut = tp.tp_shard_materialize_batch([(self.A, self.sa, {0: self.As[0]}, 0),
+                                                      (self.B, self.sb, {0: self.Bs[0]}, 0)],
                                                      stream=self.s0, prepare=True)
         self.mlp = tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
                                     col_chunks=self.w.C, peer_partials=self.peers,
@@ -145,7 +147,8 @@ class MlpStep:
     def config(self):
         w = self.w
         cfg = {"workload": w.name + ("-sp" if self.seq else ""), "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F,
-               "tp": w.P, "row_chunks": w.R, "col_chunks": w.C, "weights_cut_each_step": self.split,
+               "tp": w.P, "row_chunks": w.R, "col_chunks": w.C,
+               "weights_cut_each_step": "rank 0's shards of A and B" if self.split else False,
                "reduce_stream": "compute" if self.serial else "second",
                "reduce_fusion": "auto" if self.reduce_fusion == tp.TP_REDUCE_FUSION_AUTO else "off",
                "reduce_output": ("reduce-scattered blocks" if self.seq else
@@ -192,7 +195,7 @@ class MlpStep:
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
         return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                 "sample": (f"{rows} of {w.M} token rows of the per-rank MLP (fp64, numpy BLAS), "
-                           f"{'plus cutting the full weights into shards, ' if self.split else ''}"
+                           f"{'plus cutting the full weights into the shards of every rank (the oracle has no one-device form), ' if self.split else ''}"
                            f"{'plus the all-gather of those rows from P blocks, ' if self.seq else ''}"
                            f"plus the {w.P}-way partial sum of those rows; {reps} repetitions, "
                            f"{dt * 1e3:.1f} ms each; host {platform.processor() or platform.machine()}, "

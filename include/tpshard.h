@@ -186,7 +186,7 @@ int tp_shard_materialize(const void *src, int32_t dtype, const int64_t *shape, i
                          tp_stream_t stream);
 
 /* One tensor of tp_shard_materialize_batch: the arguments of
- * tp_shard_materialize. */
+ * tp_shard_materialize, and optionally one device's share alone. */
 typedef struct {
   const void *src;
   int32_t dtype;
@@ -195,6 +195,13 @@ typedef struct {
   const tp_layout *layout;
   void *const *dst;
   int64_t num_dst;
+  int32_t local_only;    /* 0 (a zero-initialised item): every device the layout names
+                            receives its shard, as tp_shard_materialize.  1: only
+                            local_device's shard is read and written, the share one
+                            process materialises for its own device in SPMD execution
+                            ([SPMD] "dims_mapping": each process holds its own slice);
+                            the other dst entries are ignored (may be NULL) */
+  int64_t local_device;  /* with local_only: a device id the layout names, < num_dst */
 } tp_materialize_item;
 
 /*

@@ -109,7 +109,8 @@ class tp_mlp_bwd_args(C.Structure):
 
 class tp_materialize_item(C.Structure):
     _fields_ = [("src", C.c_void_p), ("dtype", C.c_int32), ("shape", C.POINTER(C.c_int64)), ("ndim", C.c_int64),
-                ("layout", C.POINTER(tp_layout)), ("dst", C.POINTER(C.c_void_p)), ("num_dst", C.c_int64)]
+                ("layout", C.POINTER(tp_layout)), ("dst", C.POINTER(C.c_void_p)), ("num_dst", C.c_int64),
+                ("local_only", C.c_int32), ("local_device", C.c_int64)]
 
 
 class tp_kernel_stat(C.Structure):
@@ -324,12 +325,15 @@ class Prepared:
 
 def tp_shard_materialize_batch(jobs, stream=None, prepare=False):
     """Several tp_shard_materialize calls in one: ``jobs`` is a list of
-    (src, layout, dst) with dst a dict or list (device id -> tensor).  With
-    ``prepare=True`` nothing runs; a ``Prepared`` call taking the stream is
-    returned."""
+    (src, layout, dst) with dst a dict or list (device id -> tensor), or of
+    (src, layout, dst, local_device) to write only that device's share (the
+    other entries of dst may be absent).  With ``prepare=True`` nothing runs; a
+    ``Prepared`` call taking the stream is returned."""
     lib = load()
     keep, items = [], []
-    for src, layout, dst in jobs:
+    for job in jobs:
+        src, layout, dst = job[:3]
+        local = job[3] if len(job) > 3 else None
         lay, k = make_layout(layout)
         pairs = list(dst.items() if isinstance(dst, dict) else enumerate(dst))
         num_dst = (max(d for d, _ in pairs) + 1) if pairs else 0
@@ -340,7 +344,9 @@ def tp_shard_materialize_batch(jobs, stream=None, prepare=False):
         keep += [lay, k, ptrs, shp]
         items.append(tp_materialize_item(src=_ptr(src), dtype=_dtype_code(src), shape=C.cast(shp, C.POINTER(C.c_int64)),
                                          ndim=src.dim(), layout=C.pointer(lay),
-                                         dst=C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst=num_dst))
+                                         dst=C.cast(ptrs, C.POINTER(C.c_void_p)), num_dst=num_dst,
+                                         local_only=0 if local is None else 1,
+                                         local_device=0 if local is None else int(local)))
     arr = (tp_materialize_item * max(1, len(items)))(*items)
     if prepare:
         return Prepared(lib.tp_shard_materialize_batch, (arr, len(items)), keep, [_stream_ptr(stream)],

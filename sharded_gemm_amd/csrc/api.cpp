@@ -394,6 +394,33 @@ int tp_shard_materialize_batch(const tp_materialize_item *items, int64_t num_ite
       shard_elems *= plan.extent[a];
     }
     if (!it.src && numel > 0) return fail(TP_ERR_ARG, "item %lld: src is NULL", (long long)i);
+    if (it.local_only != 0 && it.local_only != 1)
+      return fail(TP_ERR_ARG, "item %lld: local_only must be 0 or 1", (long long)i);
+    if (it.local_only) {
+      // One device's share: keep the shards whose group holds it, written to it alone.
+      if (it.local_device < 0 || it.local_device >= it.num_dst)
+        return fail(TP_ERR_ARG, "item %lld: local_device %lld outside [0, num_dst)", (long long)i,
+                    (long long)it.local_device);
+      ShardPlan mine;
+      mine.ndim = plan.ndim;
+      for (int a = 0; a < plan.ndim; ++a) {
+        mine.shape[a] = plan.shape[a];
+        mine.extent[a] = plan.extent[a];
+      }
+      for (int64_t k = 0; k < plan.nshards(); ++k)
+        for (int64_t d : plan.devices[k])
+          if (d == it.local_device) {
+            mine.offset.insert(mine.offset.end(), plan.offset.begin() + k * plan.ndim,
+                               plan.offset.begin() + (k + 1) * plan.ndim);
+            mine.devices.push_back({d});
+            mine.max_device = d;
+            break;
+          }
+      if (mine.devices.empty())
+        return fail(TP_ERR_ARG, "item %lld: the layout does not name local_device %lld", (long long)i,
+                    (long long)it.local_device);
+      plan = std::move(mine);
+    }
     if (plan.max_device >= it.num_dst)
       return fail(TP_ERR_ARG, "item %lld: num_dst = %lld but the layout names device %lld", (long long)i,
                   (long long)it.num_dst, (long long)plan.max_device);

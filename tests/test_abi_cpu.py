@@ -234,6 +234,30 @@ def test_materialize_validation():
                                     dptr, 2, None) == _abi.TP_ERR_INDIVISIBLE
 
 
+def test_materialize_local_device_validation():
+    """local_only must be 0 or 1; local_device must lie in [0, num_dst) and be
+    named by the layout; with it, the other dst entries may be NULL."""
+    lib = _abi.load()
+    spec = {"device": [0, 1], "sharded_dim": [{"axis": 0, "num_shards": 2}]}
+    lay, keep = _abi.make_layout(spec)
+    shape = (C.c_int64 * 2)(4, 4)
+    sp = C.cast(shape, C.POINTER(C.c_int64))
+
+    def item(ptrs, n, only, dev):
+        arr = (C.c_void_p * max(1, n))(*ptrs)
+        return arr, _abi.tp_materialize_item(src=FAKE, dtype=_abi.TP_F32, shape=sp, ndim=2, layout=C.pointer(lay),
+                                             dst=C.cast(arr, C.POINTER(C.c_void_p)), num_dst=n, local_only=only,
+                                             local_device=dev)
+    for only, dev, n in ((2, 0, 2), (1, -1, 2), (1, 2, 2), (1, 3, 4)):
+        arr, it = item([FAKE + (1 << 20)] * n, n, only, dev)
+        assert lib.tp_shard_materialize_batch(C.byref(it), 1, None) == _abi.TP_ERR_ARG, (only, dev, n)
+        assert lib.tp_last_error().decode() != ""
+    # device 1's share alone with dst[0] NULL is accepted by validation; a NULL
+    # dst[1] is not
+    arr, it = item([None, None], 2, 1, 1)
+    assert lib.tp_shard_materialize_batch(C.byref(it), 1, None) == _abi.TP_ERR_ARG
+
+
 def test_missing_library_fails_loudly(tmp_path):
     saved = _abi._lib
     try:

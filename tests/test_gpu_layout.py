@@ -231,6 +231,43 @@ def test_batch_equals_single_calls_and_oracle():
         _compare_with_oracle(src, {d: g.t.cpu() for d, g in dst.items()}, ref)
 
 
+def test_local_device_share_equals_its_shard():
+    """An item with local_device writes that device's shard alone (the share
+    one process materialises for itself), equal to the oracle's, for split,
+    2-D split and replicated layouts; a device of a replicated group gets the
+    group's shard."""
+    announce("layout local-device shares")
+    specs = [
+        ((768, 3072), {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 1, "num_shards": 4}]}, "bf16"),
+        ((3072, 768), {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 0, "num_shards": 4}]}, "bf16"),
+        ((6, 4, 10), {"device": list(range(10)), "sharded_dim": [{"axis": 2, "num_shards": 5}, {"axis": 0, "num_shards": 2}]}, "f32"),
+        ((33, 7, 64), {"device": [-1, -2, -3], "device_map": {-1: [0, 5], -2: [1, 4], -3: [2, 3]},
+                       "sharded_dim": [{"axis": 0, "num_shards": 3}]}, "bf16"),
+        ((4, 4), {"device": [-1], "device_map": {-1: [0, 1, 2]}, "sharded_dim": []}, "f32"),
+    ]
+    for i, (shape, spec, dt) in enumerate(specs):
+        src = inputs.normal(shape, seed=9900 + i, dtype=dt)
+        ref = L.split(src, spec)
+        srcg = src.cuda()
+        for d in sorted(ref)[:: max(1, len(ref) // 3)]:
+            mine = Guarded(ref[d].shape, src.dtype)
+            tp.tp_shard_materialize_batch([(srcg, spec, {d: mine.t}, d)])
+            torch.cuda.synchronize()
+            assert mine.guards_intact()
+            _compare_with_oracle(src, {d: mine.t.cpu()}, {d: ref[d]})
+
+
+def test_local_device_not_named_is_rejected():
+    spec = {"device": [0, 1], "sharded_dim": [{"axis": 0, "num_shards": 2}]}
+    out = Guarded((2, 4), torch.float32)
+    src = torch.arange(16, dtype=torch.float32, device="cuda").view(4, 4)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_shard_materialize_batch([(src, spec, {2: out.t}, 2)])
+    assert e.value.kind == "arg"
+    torch.cuda.synchronize()
+    assert out.body_untouched() and out.guards_intact()
+
+
 def test_batch_error_leaves_every_item_untouched():
     announce("layout batch error path")
     ok_src = torch.arange(16, dtype=torch.float32, device="cuda").view(4, 4)

@@ -367,6 +367,8 @@ def _run_fusion(X, A, B, peers, *, fusion, R=1, C=1, bias=None, z_out=True, in_p
     (512, 384, 256, 2, 1, 1, {"z_out": False, "x_next": True}),    # only the next layer's input
     (515, 256, 96, 1, 1, 1, {"bias": True}),                       # no peers: the bias alone
     (1000, 512, 256, 4, 2, 2, {"bias": True, "two": True}),        # only the final block folds
+    (1000, 512, 256, 3, 2, 2, {"bias": True, "x_next": True}),     # serial: every block folds at its column offset
+    (300, 264, 192, 4, 3, 3, {"x_next": True, "in_place": True}),  # serial, ragged rows, 3 x 3 blocks, in place
     (512, 384, 256, 5, 1, 1, {}),                                  # 4 peers: separate reduction
     (520, 392, 200, 3, 1, 1, {}),                                  # K % 32 != 0: separate reduction
 ])

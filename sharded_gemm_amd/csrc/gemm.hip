@@ -192,41 +192,21 @@ __device__ __forceinline__ void epi_store_red_vec(const GemmArgs& p, int64_t ldc
   }
 }
 
-// Loads the peers' vectors itself (all before the first add), or goes element
-// by element past the last column.
-__device__ __forceinline__ void epi_store_red(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v,
-                                              bool full) {
-  const EpiReduce& r = p.red;
-  const int64_t off = m * ldc + n, left = p.N - n;
-  float *C = static_cast<float *>(p.c) + off;
-  if (full) {
-    f32x4_t pv[kMaxFusedPeers];
+// The same with the peers' vectors loaded here, all before the first add.
+// kEpiF32Red runs on the DMA path only, where every lane stores whole vectors.
+__device__ __forceinline__ void epi_store_red(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v) {
+  f32x4_t pv[kMaxFusedPeers];
 #pragma unroll
-    for (int q = 0; q < kMaxFusedPeers; ++q)
-      if (q < r.np) pv[q] = *reinterpret_cast<const f32x4_t *>(r.peer[q] + off);
-    epi_store_red_vec(p, ldc, m, n, v, pv);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (e >= left) continue;
-      if (r.out != p.c) C[e] = v[e];
-      float sum = v[e];
-      for (int q = 0; q < r.np; ++q) sum = sum + r.peer[q][off + e];
-      if (r.bias) sum = sum + r.bias[n + e];
-      if (r.out) r.out[off + e] = sum;
-      if (r.lo) {
-        if (r.lo_bf16) static_cast<uint16_t *>(r.lo)[off + e] = static_cast<uint16_t>(bf16_bits_rne(sum));
-        else static_cast<float *>(r.lo)[off + e] = sum;
-      }
-    }
-  }
+  for (int q = 0; q < kMaxFusedPeers; ++q)
+    if (q < p.red.np) pv[q] = *reinterpret_cast<const f32x4_t *>(p.red.peer[q] + m * ldc + n);
+  epi_store_red_vec(p, ldc, m, n, v, pv);
 }
 
 template <int EPI>
 __device__ __forceinline__ void epi_store(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v, bool full) {
   const int64_t left = p.N - n;
   if constexpr (EPI == kEpiF32Red) {
-    epi_store_red(p, ldc, m, n, v, full);
+    epi_store_red(p, ldc, m, n, v);
   } else if constexpr (EPI == kEpiF32 || EPI == kEpiF32Acc) {
     float *C = static_cast<float *>(p.c) + m * ldc + n;
     if (full) {
@@ -457,6 +437,7 @@ struct Bf16Gemm {
 
 template <int BM, int BN, bool VEC, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) bf16_gemm_ragged(GemmArgs p) {
+  static_assert(EPI != kEpiF32Red, "the fused reduction stores whole vectors: DMA path only");
   using G = Bf16Gemm<BM, BN, VEC, EPI>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::LDS_STAGE];
 

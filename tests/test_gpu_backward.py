@@ -252,6 +252,30 @@ def test_backward_timing_reports_the_fused_kernel():
     assert st["gemm_dgrad_reduce"]["work"] == Rc * (2 * (Mr * F + F * H) + 4 * (P - 1) * Mr * H + 2 * 4 * Mr * H)
 
 
+@pytest.mark.parametrize("P,fused", [(4, True), (5, False)])
+def test_backward_fusion_taken_where_the_rule_says(P, fused):
+    """The dX sum folds into the dX GEMM for P <= 4, and runs as its own kernel
+    on s_reduce for P = 5."""
+    announce(f"backward fusion rule P={P}")
+    M, H, F = 512, 384, 256
+    z = lambda *shape, dt=torch.bfloat16: torch.zeros(shape, dtype=dt, device="cuda")
+    X, A, B, dZ = z(M, H), z(H, F), z(F, H), z(M, H)
+    Y, Hs, dH = z(M, F), z(M, F), z(M, F)
+    dX, dA, dB = z(M, H, dt=torch.float32), z(H, F, dt=torch.float32), z(F, H, dt=torch.float32)
+    peers = [z(M, H, dt=torch.float32) for _ in range(P - 1)]
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        tp.tp_colrow_mlp_backward(X, A, B, Hs, Y, dZ, dH, dX, dA, dB, peer_dX=peers, dX_out=dX,
+                                  s_reduce=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        st = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    assert st["gemm_dgrad_reduce"]["launches"] == (1 if fused else 0)
+    assert st["reduce"]["launches"] == (0 if fused else 1)
+
+
 def test_backward_chunks_do_not_change_a_bit():
     """Row chunks split dH and dX by rows and continue one accumulation of the
     weight gradients, so R = 1, 2, 4 give identical bits (serial or two streams)."""

@@ -432,6 +432,30 @@ def test_timing_reports_the_fused_kernel():
     assert apart["gemm2"]["work"] == 2 * M * H * F
 
 
+@pytest.mark.parametrize("M,H,F,P,fused", [(512, 384, 256, 4, True), (512, 384, 256, 5, False),
+                                            (520, 392, 200, 3, False), (512, 384, 256, 1, False)])
+def test_fusion_taken_where_the_rule_says(M, H, F, P, fused):
+    """The reduction runs in GEMM2's epilogue for P <= 4 with F % 32 == 0 on a
+    small block, and as its own kernel otherwise (P = 1 has nothing to sum)."""
+    announce(f"mlp fusion rule M={M} H={H} F={F} P={P}")
+    X = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((H, F), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((F, H), dtype=torch.bfloat16, device="cuda")
+    peers = [torch.zeros((M, H), device="cuda") for _ in range(P - 1)]
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        tp.tp_colrow_mlp(X, A, B, Y, Z, peer_partials=peers, Z_out=Z if P > 1 else None)
+        st = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    assert st["gemm2_reduce"]["launches"] == (1 if fused else 0)
+    assert st["gemm2"]["launches"] == (0 if fused else 1)
+    assert st["reduce"]["launches"] == (1 if (P > 1 and not fused) else 0)
+
+
 def test_max_ranks_integer_exact():
     """P = 64 virtual ranks (63 peers), chunked, on two streams: exact."""
     announce("mlp P=64 integer exact")

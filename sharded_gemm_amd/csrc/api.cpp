@@ -280,16 +280,34 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     // with nothing beside it anyway (the serial schedule and the final block):
     // one launch fewer and no second read of the partial just written.
     const bool final_block = last && c + 1 == pl.C;
-    if (pl.reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && (!two || final_block) && !a->Z_split &&
+    if (pl.reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && (!two || final_block) &&
         pl.epi2 == kEpiF32 && a->P - 1 <= kMaxFusedPeers) {
       GemmArgs gr = g2;
       gr.red.np = static_cast<int32_t>(a->P - 1);
       for (int64_t p = 1; p < a->P; ++p) gr.red.peer[p - 1] = a->peer_partials[p - 1] + zoff;
-      gr.red.out = a->Z_out ? a->Z_out + zoff : nullptr;
+      gr.red.nout = 1;
+      gr.red.rows_per_out = static_cast<int32_t>(Mr);
+      bool fits = true;
+      if (a->Z_split) {
+        // Reduce-scattered: the chunk lies in one sequence block, or covers
+        // whole ones (the two nest).
+        const int64_t Ms = pl.sq.Ms, g0 = r * Mr, j0 = g0 / Ms;
+        if (Mr <= Ms) {
+          gr.red.out[0] = a->Z_split[j0] + (g0 - j0 * Ms) * H + c * Hc;
+        } else if (Mr / Ms <= kMaxFusedOuts) {
+          gr.red.nout = static_cast<int32_t>(Mr / Ms);
+          gr.red.rows_per_out = static_cast<int32_t>(Ms);
+          for (int64_t k = 0; k < Mr / Ms; ++k) gr.red.out[k] = a->Z_split[j0 + k] + c * Hc;
+        } else {
+          fits = false;
+        }
+      } else {
+        gr.red.out[0] = a->Z_out ? a->Z_out + zoff : nullptr;
+      }
       gr.red.bias = a->bias ? a->bias + c * Hc : nullptr;
       gr.red.lo = a->X_next ? static_cast<char *>(a->X_next) + zoff * es : nullptr;
       gr.red.lo_bf16 = a->dtype == TP_BF16;
-      if (gemm_red_ok(gr)) {
+      if (fits && gemm_red_ok(gr)) {
         t0 = timing_begin(s0);
         e = gemm_launch(gr, kEpiF32Red, s0);
         if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
@@ -297,8 +315,8 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
         // blocks and the bias read once, every output written once).
         const double cells = static_cast<double>(Mr) * Hc;
         const double bytes = es * (static_cast<double>(Mr) * F + static_cast<double>(F) * Hc) +
-                             4.0 * gr.red.np * cells + (gr.red.out != gr.c ? 4.0 * cells : 0.0) +
-                             (gr.red.out ? 4.0 * cells : 0.0) + (gr.red.lo ? es * cells : 0.0) +
+                             4.0 * gr.red.np * cells + (gr.red.out[0] != gr.c ? 4.0 * cells : 0.0) +
+                             (gr.red.out[0] ? 4.0 * cells : 0.0) + (gr.red.lo ? es * cells : 0.0) +
                              (gr.red.bias ? 4.0 * Hc : 0.0);
         timing_end(t0, s0, TP_KERNEL_GEMM2_REDUCE, bytes);
         continue;
@@ -693,7 +711,8 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
     if (fused) {
       gx.red.np = static_cast<int32_t>(a->P - 1);
       for (int64_t p = 1; p < a->P; ++p) gx.red.peer[p - 1] = a->peer_dX[p - 1] + r * Mr * H;
-      gx.red.out = a->dX_out + r * Mr * H;
+      gx.red.out[0] = a->dX_out + r * Mr * H;
+      gx.red.nout = 1;
     }
     return gx;
   };
@@ -758,7 +777,7 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
       const double cells = static_cast<double>(Mr) * H;
       timing_end(t0, s0, TP_KERNEL_GEMM_DGRAD_REDUCE,
                  es * (static_cast<double>(Mr) * F + static_cast<double>(F) * H) + 4.0 * gx.red.np * cells +
-                     (gx.red.out != gx.c ? 4.0 * cells : 0.0) + 4.0 * cells);
+                     (gx.red.out[0] != gx.c ? 4.0 * cells : 0.0) + 4.0 * cells);
     } else {
       t0 = timing_begin(s0);
       e = gemm_launch(dx_gemm(r, false), epi_f32, s0);

@@ -14,15 +14,21 @@ namespace tpshard {
 // The partial sum folded into an fp32-output epilogue (kEpiF32Red): with v the
 // tile's result as stored in C, out = (((v + peer[0]) + peer[1]) + ...) + bias[n],
 // the order of the separate reduction kernel, so the two agree bit for bit.
-// Peers, out and lo are [M][ldc] like C; bias is indexed by column.
+// Peers and lo are [M][ldc] like C; bias is indexed by column.  The fp32 sum
+// goes to out[0] ([M][ldc]), or, reduce-scattered, row m to out[m / rows_per_out]
+// at row m % rows_per_out (each [rows_per_out][ldc]).
 constexpr int kMaxFusedPeers = 3;
+constexpr int kMaxFusedOuts = 4;
 struct EpiReduce {
   const float *peer[kMaxFusedPeers];
-  float *out;          // fp32 sum, or null; may equal C (then C receives the sum only)
-  const float *bias;   // or null
-  void *lo;            // copy of the sum in bf16 (RNE) or fp32, or null
-  int32_t np;          // peers used, 0..kMaxFusedPeers
-  int32_t lo_bf16;     // lo holds bf16 (else fp32)
+  float *out[kMaxFusedOuts];   // fp32 sum, or out[0] null for none; a single out may equal C
+                               // (then C receives the sum only)
+  const float *bias;           // or null
+  void *lo;                    // copy of the sum in bf16 (RNE) or fp32, or null (single out only)
+  int32_t np;                  // peers used, 0..kMaxFusedPeers
+  int32_t lo_bf16;             // lo holds bf16 (else fp32)
+  int32_t nout;                // outputs, 1..kMaxFusedOuts
+  int32_t rows_per_out;        // rows of each output when nout > 1
 };
 
 struct GemmArgs {

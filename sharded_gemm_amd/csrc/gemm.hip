@@ -174,7 +174,7 @@ __device__ __forceinline__ void epi_store_red_vec(const GemmArgs& p, int64_t ldc
                                                   const f32x4_t (&pv)[kMaxFusedPeers]) {
   const EpiReduce& r = p.red;
   const int64_t off = m * ldc + n;
-  if (r.out != p.c) *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + off) = v;
+  if (r.out[0] != p.c) *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + off) = v;
   f32x4_t sum = v;
 #pragma unroll
   for (int q = 0; q < kMaxFusedPeers; ++q)
@@ -182,7 +182,12 @@ __device__ __forceinline__ void epi_store_red_vec(const GemmArgs& p, int64_t ldc
   if (r.bias) sum = sum + *reinterpret_cast<const f32x4_t *>(r.bias + n);
   // The fp32 sum streams past the caches; the next layer's copy, read by its
   // GEMM next, goes through them (as in the separate reduction).
-  if (r.out) __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out + off));
+  if (r.nout > 1) {
+    const int64_t j = m / r.rows_per_out;
+    __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out[j] + (m - j * r.rows_per_out) * ldc + n));
+  } else if (r.out[0]) {
+    __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out[0] + off));
+  }
   if (r.lo) {
     if (r.lo_bf16)
       *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(r.lo) + off) =
@@ -1207,7 +1212,14 @@ bool gemm_red_ok(const GemmArgs& p) {
     return false;
   bool ok = !r.bias || aligned16(r.bias);
   for (int q = 0; q < r.np; ++q) ok = ok && r.peer[q] && aligned16(r.peer[q]);
-  if (r.out) ok = ok && aligned16(r.out);
+  if (r.nout < 1 || r.nout > kMaxFusedOuts) return false;
+  if (r.nout > 1) {
+    // Reduce-scattered: whole blocks of rows per output, no second copy.
+    if (r.lo || r.rows_per_out < 1 || static_cast<int64_t>(r.rows_per_out) * r.nout != p.M) return false;
+    for (int j = 0; j < r.nout; ++j) ok = ok && r.out[j] && aligned16(r.out[j]);
+  } else if (r.out[0]) {
+    ok = ok && aligned16(r.out[0]);
+  }
   if (r.lo) ok = ok && (reinterpret_cast<uintptr_t>(r.lo) & (r.lo_bf16 ? 7u : 15u)) == 0;
   return ok;
 }

@@ -35,7 +35,8 @@ def _f64(t):
     return t.double().numpy()
 
 
-def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bias=None, two_streams=True):
+def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bias=None, two_streams=True,
+               fusion=tp.TP_REDUCE_FUSION_AUTO):
     """tp_colrow_mlp with X_shards and Z_split into guarded buffers; returns CPU
     copies (X gathered, Y, Z_i, [Z blocks])."""
     S = len(X_blocks)
@@ -48,7 +49,8 @@ def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bia
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream() if two_streams else s0
     tp.tp_colrow_mlp(Xw.t, A, B, Y.t, Z.t, row_chunks=Rc, col_chunks=Cc, peer_partials=list(peers), act=act,
-                     s_compute=s0, s_reduce=s1, bias=bias, X_shards=list(X_blocks), Z_split=[g.t for g in Zs])
+                     s_compute=s0, s_reduce=s1, bias=bias, X_shards=list(X_blocks), Z_split=[g.t for g in Zs],
+                     reduce_fusion=fusion)
     torch.cuda.synchronize()
     for g in [Xw, Y, Z] + Zs:
         assert g.guards_intact(), "write outside an output buffer"
@@ -82,6 +84,31 @@ def test_forward_integer_exact(M, H, F, Rc, Cc, P, S):
     ref = R.reduce_split([z_ref] + [_f64(p) for p in peers], S, "sum", _f64(bias))
     for j in range(S):
         assert np.array_equal(_f64(Zs[j]), ref[j]), j
+
+
+@pytest.mark.parametrize("M,H,F,Rc,Cc,P,S", [
+    (4096, 768, 768, 1, 1, 4, 4),     # GPT-2-small: each row of the chunk to one of 4 blocks
+    (1024, 384, 256, 2, 2, 4, 4),     # a chunk covers 2 blocks, 2 column blocks
+    (1024, 384, 256, 4, 1, 3, 2),     # a chunk lies inside one block
+    (1200, 264, 160, 1, 1, 2, 8),     # 8 blocks in the chunk: separate reduce-scatter
+])
+def test_forward_reduce_fusion_same_bits(M, H, F, Rc, Cc, P, S):
+    """The reduce-scatter folded into GEMM2's epilogue (serial schedule: every
+    block folds) gives the separate kernel's bits in every sequence block."""
+    announce(f"seqpar reduce fusion M={M} H={H} F={F} R={Rc} C={Cc} P={P} S={S}")
+    Ms = M // S
+    Xb = [inputs.normal((Ms, H), seed=780 + j, dtype="bf16").cuda() for j in range(S)]
+    A = inputs.normal((H, F), seed=790, std=0.05, dtype="bf16").cuda()
+    B = inputs.normal((F, H), seed=791, std=0.05, dtype="bf16").cuda()
+    peers = [inputs.normal((M, H), seed=795 + p).cuda() for p in range(P - 1)]
+    bias = inputs.normal((H,), seed=799).cuda()
+    kw = dict(Rc=Rc, Cc=Cc, bias=bias, two_streams=False)
+    got = sp_forward(Xb, A, B, peers, **kw)
+    ref = sp_forward(Xb, A, B, peers, fusion=tp.TP_REDUCE_FUSION_OFF, **kw)
+    for a, b in zip(got[:3], ref[:3]):
+        assert np.array_equal(bits(a), bits(b))
+    for j in range(S):
+        assert np.array_equal(bits(got[3][j]), bits(ref[3][j])), j
 
 
 def test_forward_gelu_matches_unsplit_path_bitwise():

@@ -60,6 +60,7 @@ enum {
   kEpiGeluSaveF32 = 7,   // fp32 inputs, C = GeLU(acc), aux = acc (fp32)
   kEpiDGeluF32 = 8,      // fp32 inputs, C = acc * GeLU'(aux), aux fp32
   kEpiF32Red = 9,        // bf16 inputs, C = acc (fp32) and the partial sum of red (A not transposed)
+  kEpiF32RedSplit = 10,  // kEpiF32Red's reduce-scattered form (red.nout > 1); chosen inside gemm_launch
 };
 
 // Enqueues the GEMM on stream s; returns the launch status.

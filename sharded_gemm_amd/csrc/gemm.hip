@@ -170,6 +170,8 @@ __device__ __forceinline__ f32x4_t load_bf16x4(const uint16_t *src, bool full, i
 // kEpiF32Red: store the partial v, then its sum with the peers' partials and
 // the bias, added in the separate reduction's order.  This whole-vector form
 // takes the peers' vectors already loaded.
+// SPLIT: the sum reduce-scattered over red.out[] (kEpiF32RedSplit).
+template <bool SPLIT>
 __device__ __forceinline__ void epi_store_red_vec(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v,
                                                   const f32x4_t (&pv)[kMaxFusedPeers]) {
   const EpiReduce& r = p.red;
@@ -182,7 +184,7 @@ __device__ __forceinline__ void epi_store_red_vec(const GemmArgs& p, int64_t ldc
   if (r.bias) sum = sum + *reinterpret_cast<const f32x4_t *>(r.bias + n);
   // The fp32 sum streams past the caches; the next layer's copy, read by its
   // GEMM next, goes through them (as in the separate reduction).
-  if (r.nout > 1) {
+  if constexpr (SPLIT) {
     const int64_t j = m / r.rows_per_out;
     __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out[j] + (m - j * r.rows_per_out) * ldc + n));
   } else if (r.out[0]) {
@@ -199,19 +201,20 @@ __device__ __forceinline__ void epi_store_red_vec(const GemmArgs& p, int64_t ldc
 
 // The same with the peers' vectors loaded here, all before the first add.
 // kEpiF32Red runs on the DMA path only, where every lane stores whole vectors.
+template <bool SPLIT>
 __device__ __forceinline__ void epi_store_red(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v) {
   f32x4_t pv[kMaxFusedPeers];
 #pragma unroll
   for (int q = 0; q < kMaxFusedPeers; ++q)
     if (q < p.red.np) pv[q] = *reinterpret_cast<const f32x4_t *>(p.red.peer[q] + m * ldc + n);
-  epi_store_red_vec(p, ldc, m, n, v, pv);
+  epi_store_red_vec<SPLIT>(p, ldc, m, n, v, pv);
 }
 
 template <int EPI>
 __device__ __forceinline__ void epi_store(const GemmArgs& p, int64_t ldc, int64_t m, int64_t n, f32x4_t v, bool full) {
   const int64_t left = p.N - n;
-  if constexpr (EPI == kEpiF32Red) {
-    epi_store_red(p, ldc, m, n, v);
+  if constexpr (EPI == kEpiF32Red || EPI == kEpiF32RedSplit) {
+    epi_store_red<EPI == kEpiF32RedSplit>(p, ldc, m, n, v);
   } else if constexpr (EPI == kEpiF32 || EPI == kEpiF32Acc) {
     float *C = static_cast<float *>(p.c) + m * ldc + n;
     if (full) {
@@ -442,7 +445,7 @@ struct Bf16Gemm {
 
 template <int BM, int BN, bool VEC, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) bf16_gemm_ragged(GemmArgs p) {
-  static_assert(EPI != kEpiF32Red, "the fused reduction stores whole vectors: DMA path only");
+  static_assert(EPI != kEpiF32Red && EPI != kEpiF32RedSplit, "the fused reduction stores whole vectors: DMA path only");
   using G = Bf16Gemm<BM, BN, VEC, EPI>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::LDS_STAGE];
 
@@ -684,7 +687,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, int bid) {
   // (loads complete in issue order).  The load is issued for every lane (rows
   // past M read row M - 1, never stored), so the wave always counts it.
   // Vectors the stage openings do not reach are loaded in the epilogue.
-  constexpr bool PF = EPI == kEpiF32Red && S == 2;
+  constexpr bool PF = (EPI == kEpiF32Red || EPI == kEpiF32RedSplit) && S == 2;
   constexpr int NF = C::TM * C::TN;
   f32x4_t pv[PF ? NF : 1][kMaxFusedPeers];
   const int np = PF ? p.red.np : 0;
@@ -753,7 +756,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, int bid) {
       int64_t m, n;
       coords(i, j, &m, &n);
       if (m < p.M && n < p.N) {   // N % 8 == 0 on this path
-        if constexpr (PF) epi_store_red_vec(p, ldc, m, n, acc[i][j], pv[i * C::TN + j]);
+        if constexpr (PF) epi_store_red_vec<EPI == kEpiF32RedSplit>(p, ldc, m, n, acc[i][j], pv[i * C::TN + j]);
         else epi_store<EPI>(p, ldc, m, n, acc[i][j], true);
       }
     }
@@ -1178,6 +1181,10 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
       case kEpiGeluSaveBf16: return dispatch_bf16<kEpiGeluSaveBf16, false, false>(p, dma_ok, vec, s);
       case kEpiF32Red:
         if (!gemm_red_ok(p)) return hipErrorInvalidValue;
+        if (p.red.nout > 1) {
+          if (p.K % 64 == 0) return launch_dma<64, 64, 64, 2, kEpiF32RedSplit, false, false, 2, 2>(p, s);
+          return launch_dma<64, 64, 32, 4, kEpiF32RedSplit, false, false, 2, 2>(p, s);
+        }
         if (p.K % 64 == 0) return launch_dma<64, 64, 64, 2, kEpiF32Red, false, false, 2, 2>(p, s);
         return launch_dma<64, 64, 32, 4, kEpiF32Red, false, false, 2, 2>(p, s);
       default: return hipErrorInvalidValue;
@@ -1212,7 +1219,7 @@ bool gemm_red_ok(const GemmArgs& p) {
     return false;
   bool ok = !r.bias || aligned16(r.bias);
   for (int q = 0; q < r.np; ++q) ok = ok && r.peer[q] && aligned16(r.peer[q]);
-  if (r.nout < 1 || r.nout > kMaxFusedOuts) return false;
+  if (r.nout < 1 || r.nout > kMaxFusedOuts || (p.w_t && r.nout > 1)) return false;
   if (r.nout > 1) {
     // Reduce-scattered: whole blocks of rows per output, no second copy.
     if (r.lo || r.rows_per_out < 1 || static_cast<int64_t>(r.rows_per_out) * r.nout != p.M) return false;

@@ -337,8 +337,8 @@ typedef struct {
                         run with nothing beside it (the serial schedule, or the final
                         block of the two-stream one), GEMM2 adds the peers' partials
                         and the bias in its epilogue and writes Z_out / X_next itself.
-                        Taken for bf16 operands, P <= 4, Z_out or a Z_split whose
-                        chunk spans at most 4 sequence blocks, 16-byte aligned rows,
+                        Taken for P <= 4 and Z_out or a Z_split whose chunk spans at
+                        most 4 sequence blocks; for bf16 also 16-byte aligned rows,
                         F a multiple of 32 and blocks of fewer than 256 output tiles
                         of 128 x 128; otherwise,
                         and always with TP_REDUCE_FUSION_OFF (1), a separate

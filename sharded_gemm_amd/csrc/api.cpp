@@ -281,7 +281,8 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     // one launch fewer and no second read of the partial just written.
     const bool final_block = last && c + 1 == pl.C;
     if (pl.reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && (!two || final_block) &&
-        pl.epi2 == kEpiF32 && a->P - 1 <= kMaxFusedPeers) {
+        (pl.epi2 == kEpiF32 || pl.epi2 == kEpiPlainF32) && a->P - 1 <= kMaxFusedPeers) {
+      const bool f32 = pl.epi2 == kEpiPlainF32;
       GemmArgs gr = g2;
       gr.red.np = static_cast<int32_t>(a->P - 1);
       for (int64_t p = 1; p < a->P; ++p) gr.red.peer[p - 1] = a->peer_partials[p - 1] + zoff;
@@ -307,9 +308,9 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
       gr.red.bias = a->bias ? a->bias + c * Hc : nullptr;
       gr.red.lo = a->X_next ? static_cast<char *>(a->X_next) + zoff * es : nullptr;
       gr.red.lo_bf16 = a->dtype == TP_BF16;
-      if (fits && gemm_red_ok(gr)) {
+      if (fits && (f32 ? gemm_red_ok_f32(gr) : gemm_red_ok(gr))) {
         t0 = timing_begin(s0);
-        e = gemm_launch(gr, kEpiF32Red, s0);
+        e = gemm_launch(gr, f32 ? kEpiPlainF32Red : kEpiF32Red, s0);
         if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
         // Memory-bound: its work is bytes (Y rows and B columns, the peers'
         // blocks and the bias read once, every output written once).

@@ -61,6 +61,7 @@ enum {
   kEpiDGeluF32 = 8,      // fp32 inputs, C = acc * GeLU'(aux), aux fp32
   kEpiF32Red = 9,        // bf16 inputs, C = acc (fp32) and the partial sum of red (A not transposed)
   kEpiF32RedSplit = 10,  // kEpiF32Red's reduce-scattered form (red.nout > 1); chosen inside gemm_launch
+  kEpiPlainF32Red = 11,  // fp32 inputs, C = acc (fp32) and the partial sum of red (forward layout)
 };
 
 // Enqueues the GEMM on stream s; returns the launch status.
@@ -71,6 +72,8 @@ hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s);
 // small-tile path (fewer 128 x 128 tiles than CUs, K % 32 == 0), where the
 // peers' loads fit beside the accumulators without costing occupancy.
 bool gemm_red_ok(const GemmArgs& p);
+// The same for kEpiPlainF32Red (the fp32 kernel, any alignment and size).
+bool gemm_red_ok_f32(const GemmArgs& p);
 
 // Up to 4 independent GEMMs in one launch (same results as one gemm_launch
 // call each), for groups gemm_group_ok accepts: small weight-gradient problems

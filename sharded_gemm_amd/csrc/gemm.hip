@@ -1033,6 +1033,23 @@ __global__ void __launch_bounds__(kThreads) f32_gemm_kernel(GemmArgs p) {
       const int64_t n = n0 + tc * 2 + j;
       if (n >= p.N) continue;
       float v = acc[i][j];
+      if constexpr (EPI == kEpiPlainF32Red) {
+        // The partial, then its sum in the separate reduction's order.
+        const EpiReduce& r = p.red;
+        const int64_t off = m * p.ldc + n;
+        if (r.out[0] != p.c) C[off] = v;
+        float sum = v;
+        for (int q = 0; q < r.np; ++q) sum = sum + r.peer[q][off];
+        if (r.bias) sum = sum + r.bias[n];
+        if (r.nout > 1) {
+          const int64_t jo = m / r.rows_per_out;
+          r.out[jo][(m - jo * r.rows_per_out) * p.ldc + n] = sum;
+        } else if (r.out[0]) {
+          r.out[0][off] = sum;
+        }
+        if (r.lo) static_cast<float *>(r.lo)[off] = sum;
+        continue;
+      }
       if constexpr (EPI == kEpiGeluSaveF32) X[m * p.ldaux + n] = v;
       if constexpr (EPI == kEpiDGeluF32) v *= gelu_erf_deriv(X[m * p.ldaux + n]);
       if constexpr (EPI == kEpiGeluF32 || EPI == kEpiGeluSaveF32) v = gelu_erf(v);
@@ -1154,7 +1171,9 @@ bool gemm_vec_ok(const GemmArgs& p, int64_t out_esize, bool uses_aux) {
 hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   int epi = epi_in;
-  const bool fp32 = epi == kEpiGeluF32 || epi == kEpiPlainF32 || epi == kEpiGeluSaveF32 || epi == kEpiDGeluF32;
+  const bool fp32 = epi == kEpiGeluF32 || epi == kEpiPlainF32 || epi == kEpiGeluSaveF32 || epi == kEpiDGeluF32 ||
+                    epi == kEpiPlainF32Red;
+  if (epi == kEpiPlainF32Red && !gemm_red_ok_f32(p)) return hipErrorInvalidValue;
   if (fp32) {
     const int64_t tiles = ((p.M + kF32Tile - 1) / kF32Tile) * ((p.N + kF32Tile - 1) / kF32Tile);
     const dim3 grid(static_cast<unsigned>(tiles));
@@ -1162,6 +1181,7 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
       case kEpiGeluF32: hipLaunchKernelGGL((f32_gemm_kernel<kEpiGeluF32>), grid, dim3(kThreads), 0, s, p); break;
       case kEpiGeluSaveF32: hipLaunchKernelGGL((f32_gemm_kernel<kEpiGeluSaveF32>), grid, dim3(kThreads), 0, s, p); break;
       case kEpiDGeluF32: hipLaunchKernelGGL((f32_gemm_kernel<kEpiDGeluF32>), grid, dim3(kThreads), 0, s, p); break;
+      case kEpiPlainF32Red: hipLaunchKernelGGL((f32_gemm_kernel<kEpiPlainF32Red>), grid, dim3(kThreads), 0, s, p); break;
       default: hipLaunchKernelGGL((f32_gemm_kernel<kEpiPlainF32>), grid, dim3(kThreads), 0, s, p); break;
     }
     return hipGetLastError();
@@ -1229,6 +1249,20 @@ bool gemm_red_ok(const GemmArgs& p) {
   }
   if (r.lo) ok = ok && (reinterpret_cast<uintptr_t>(r.lo) & (r.lo_bf16 ? 7u : 15u)) == 0;
   return ok;
+}
+
+bool gemm_red_ok_f32(const GemmArgs& p) {
+  const EpiReduce& r = p.red;
+  if (p.a_t || p.w_t || p.acc_init || r.np < 0 || r.np > kMaxFusedPeers || r.nout < 1 || r.nout > kMaxFusedOuts)
+    return false;
+  for (int q = 0; q < r.np; ++q)
+    if (!r.peer[q]) return false;
+  if (r.nout > 1) {
+    if (r.lo || r.rows_per_out < 1 || static_cast<int64_t>(r.rows_per_out) * r.nout != p.M) return false;
+    for (int j = 0; j < r.nout; ++j)
+      if (!r.out[j]) return false;
+  }
+  return true;
 }
 
 // The grouped launch covers the weight gradients of a small layer: bf16

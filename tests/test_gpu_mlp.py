@@ -401,6 +401,36 @@ def test_reduce_fusion_same_bits(M, H, F, P, Rc, Cc, opts):
         assert rel_err(Xn.float(), total) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,H,F,P,Rc,Cc,opts", [
+    (64, 256, 512, 2, 1, 1, {}),                                   # the tiny fp32 workload's rank
+    (77, 45, 51, 3, 1, 1, {"bias": True, "x_next": True}),         # ragged everything, fp32 next input
+    (130, 129, 65, 4, 1, 1, {"in_place": True}),                   # Z_out = Z_i
+    (130, 128, 65, 3, 2, 2, {"bias": True}),                       # serial: every block folds
+    (130, 128, 65, 3, 2, 2, {"bias": True, "two": True}),          # only the final block folds
+])
+def test_reduce_fusion_same_bits_fp32(M, H, F, P, Rc, Cc, opts):
+    """fp32 throughout: the fp32 kernel's epilogue sum equals the separate
+    reduction bit for bit, and the oracle within the fp32 tolerance."""
+    announce(f"mlp reduce fusion fp32 M={M} H={H} F={F} P={P} R={Rc} C={Cc} {sorted(opts)}")
+    X = inputs.normal((M, H), 381, 1.0)
+    A = inputs.normal((H, F), 382, 1.0 / np.sqrt(H))
+    B = inputs.normal((F, H), 383, 1.0 / np.sqrt(F))
+    peers_cpu = [inputs.normal((M, H), 390 + p) for p in range(P - 1)]
+    bias_cpu = inputs.normal((H,), 389) if opts.get("bias") else None
+    kw = {k: v for k, v in opts.items() if k != "bias"}
+    kw.update(R=Rc, C=Cc, bias=bias_cpu.cuda() if bias_cpu is not None else None)
+    Xd, Ad, Bd, peers = X.cuda(), A.cuda(), B.cuda(), [p.cuda() for p in peers_cpu]
+    fused = _run_fusion(Xd, Ad, Bd, peers, fusion=tp.TP_REDUCE_FUSION_AUTO, **kw)
+    apart = _run_fusion(Xd, Ad, Bd, peers, fusion=tp.TP_REDUCE_FUSION_OFF, **kw)
+    for a, b in zip(fused, apart):
+        assert (a is None) == (b is None)
+        if a is not None:
+            assert np.array_equal(bits(a), bits(b))
+    total = R.reduce_full([O.mlp_rank(X, A, B)] + peers_cpu, "sum", bias_cpu)
+    out = fused[1] if opts.get("in_place") else (fused[2] if fused[2] is not None else fused[3])
+    assert rel_err(out, total) <= TOL_F32
+
+
 def test_timing_reports_the_fused_kernel():
     """With the reduction in GEMM2's epilogue the per-kernel timing sees one
     gemm2_reduce launch whose work is its algorithmic bytes (Y and B_i read,

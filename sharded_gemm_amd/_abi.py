@@ -422,14 +422,39 @@ def tp_shard_gather(src, layout: dict, out, shape, stream=None):
                                _stream_ptr(stream)))
 
 
-def _seq_arrays(shards, split):
-    """(S, ctypes array or None, ctypes array or None) for the sequence-parallel fields."""
+def _check_bias(bias, cols):
+    """A row-parallel bias is a contiguous fp32 vector of the output's width."""
+    if bias is None:
+        return
+    import torch
+    if not hasattr(bias, "data_ptr") or bias.dtype != torch.float32:
+        raise TypeError("bias must be an fp32 tensor")
+    if tuple(bias.shape) != (int(cols),) or not bias.is_contiguous():
+        raise ValueError(f"bias must be a contiguous fp32 [{int(cols)}]")
+
+
+def _seq_arrays(shards, split, M=None, H=None, in_dtype=None, shards_name="X_shards", split_name="Z_split"):
+    """(S, ctypes array or None, ctypes array or None) for the sequence-parallel
+    fields.  Each block is a contiguous [M/S, H] tensor: the shards in the
+    input dtype, the split outputs fp32 (the library trusts these sizes)."""
+    import torch
     shards = list(shards) if shards is not None else None
     split = list(split) if split is not None else None
     lens = {len(x) for x in (shards, split) if x is not None}
     if len(lens) > 1:
         raise ValueError("the input shards and the split outputs must have the same count")
     S = lens.pop() if lens else 0
+    if S and M is not None:
+        if M % S:
+            raise ValueError(f"{S} sequence blocks do not divide M = {M}")
+        want = (M // S, H)
+        for name, xs, dt in ((shards_name, shards, in_dtype), (split_name, split, torch.float32)):
+            for t in xs or ():
+                if not hasattr(t, "data_ptr") or t.dtype != dt:
+                    raise TypeError(f"every {name} block must be a {dt} tensor")
+                if tuple(t.shape) != want or not t.is_contiguous():
+                    raise ValueError(f"every {name} block must be a contiguous [{want[0]}, {want[1]}]")
+
     def arr(xs):
         return C.cast((C.c_void_p * len(xs))(*[_ptr(t) for t in xs]), C.POINTER(C.c_void_p)) if xs else None
     return S, arr(shards), arr(split)
@@ -451,6 +476,7 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
         ld_in = int(t0.stride(0)) if is_tensor else cols
     if ld_out is None:
         ld_out = int(out[0].stride(0)) if hasattr(out[0], "data_ptr") else cols
+    _check_bias(bias, cols)
     pin = (C.c_void_p * P)(*[(p.data_ptr() if hasattr(p, "data_ptr") else p) for p in partials])
     pout = (C.c_void_p * len(out))(*[(o.data_ptr() if hasattr(o, "data_ptr") else o) for o in out])
     if op == TP_REDUCE_OP_SUM and bias is None:
@@ -485,6 +511,8 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
     for t in [Z_i, *peers] + ([Z_out] if Z_out is not None else []):
         if t.dtype != torch.float32 or tuple(t.shape) != (M, H):
             raise TypeError("Z_i, peer partials and Z_out must be fp32 [M, H]")
+    _check_bias(bias, H)
+    S, xs, zs = _seq_arrays(X_shards, Z_split, M, H, X.dtype, "X_shards", "Z_split")
     parr = (C.c_void_p * max(1, len(peers)))(*[_ptr(p) for p in peers])
     args = tp_mlp_args(dtype=_dtype_code(X), act=act, M=M, H=H, F=F,
                        X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
@@ -492,7 +520,6 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
                        Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias),
                        X_next=_ptr(X_next), reduce_fusion=reduce_fusion)
-    S, xs, zs = _seq_arrays(X_shards, Z_split)
     args.seq_splits, args.X_shards, args.Z_split = S, xs, zs
     return args, [parr, xs, zs]
 
@@ -571,7 +598,7 @@ def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *
                            accumulate=1 if accumulate else 0, row_chunks=row_chunks, P=1 + len(peers),
                            peer_dX=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
                            dX_out=_ptr(dX_out), reduce_workgroups=reduce_workgroups, reduce_fusion=reduce_fusion)
-    S, gs, xs = _seq_arrays(dZ_shards, dX_split)
+    S, gs, xs = _seq_arrays(dZ_shards, dX_split, M, H, X.dtype, "dZ_shards", "dX_split")
     args.seq_splits, args.dZ_shards, args.dX_split = S, gs, xs
     sc = _stream_ptr(s_compute)
     sr = _stream_ptr(s_reduce) if s_reduce is not None else sc

@@ -448,3 +448,60 @@ def test_materialize_batch_validation():
     assert lib.tp_shard_materialize_batch(arr, 2, None) == _abi.TP_ERR_ARG            # two items write one buffer
     assert lib.tp_shard_materialize_batch(None, 1, None) == _abi.TP_ERR_ARG
     assert lib.tp_shard_materialize_batch(arr, -1, None) == _abi.TP_ERR_ARG
+
+
+def test_binding_checks_sequence_blocks_and_bias():
+    """The binding refuses sequence blocks and biases whose dtype, shape or
+    layout differ from what the library assumes (it trusts their sizes), before
+    any call into it.  Host tensors: nothing here reaches a kernel."""
+    M, H, F, S = 64, 32, 16, 4
+    X = torch.zeros((M, H), dtype=torch.bfloat16)
+    A = torch.zeros((H, F), dtype=torch.bfloat16)
+    B = torch.zeros((F, H), dtype=torch.bfloat16)
+    Y = torch.zeros((M, F), dtype=torch.bfloat16)
+    Z = torch.zeros((M, H))
+    xs = [torch.zeros((M // S, H), dtype=torch.bfloat16) for _ in range(S)]
+    zs = [torch.zeros((M // S, H)) for _ in range(S)]
+
+    def fwd(**kw):
+        tp.tp_colrow_mlp(X, A, B, Y, Z, **kw)
+    with pytest.raises(TypeError):
+        fwd(Z_split=[z.to(torch.bfloat16) for z in zs])                  # bf16 split output
+    with pytest.raises(ValueError):
+        fwd(Z_split=[torch.zeros((M // S - 1, H)) for _ in range(S)])    # short blocks
+    with pytest.raises(ValueError):
+        fwd(Z_split=[torch.zeros((H, M // S)).t() for _ in range(S)])    # not contiguous
+    with pytest.raises(ValueError):
+        fwd(X_shards=[torch.zeros((M // 3, H), dtype=torch.bfloat16) for _ in range(3)])   # 3 does not divide 64
+    with pytest.raises(TypeError):
+        fwd(X_shards=[x.float() for x in xs])                            # not X's dtype
+    with pytest.raises(ValueError):
+        fwd(X_shards=xs, Z_split=zs[:2])                                 # counts differ
+    with pytest.raises(TypeError):
+        fwd(Z_out=torch.zeros((M, H)), bias=torch.zeros(H, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fwd(Z_out=torch.zeros((M, H)), bias=torch.zeros(H - 1))
+    with pytest.raises(ValueError):
+        fwd(Z_out=torch.zeros((M, H)), bias=torch.zeros((H, 2))[:, 0])   # strided
+
+    with pytest.raises(TypeError):
+        tp.tp_partial_reduce([Z, Z.clone()], [torch.zeros((M, H))], bias=torch.zeros(H, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        tp.tp_partial_reduce([Z, Z.clone()], [torch.zeros((M, H))], bias=torch.zeros(H + 1))
+
+    dZ = torch.zeros((M, H), dtype=torch.bfloat16)
+    dH = torch.zeros((M, F), dtype=torch.bfloat16)
+    dX = torch.zeros((M, H))
+    dA = torch.zeros((H, F))
+    dB = torch.zeros((F, H))
+
+    def bwd(**kw):
+        tp.tp_colrow_mlp_backward(X, A, B, Y, Y, dZ, dH, dX, dA, dB, **kw)
+    with pytest.raises(TypeError):
+        bwd(dX_split=[z.to(torch.bfloat16) for z in zs])
+    with pytest.raises(ValueError):
+        bwd(dX_split=[torch.zeros((M // S, H + 1)) for _ in range(S)])
+    with pytest.raises(TypeError):
+        bwd(dZ_shards=[x.float() for x in xs])
+    with pytest.raises(ValueError):
+        bwd(dZ_shards=[torch.zeros((M // S + 1, H), dtype=torch.bfloat16) for _ in range(S)])

@@ -2,18 +2,26 @@
 """Throughput of one rank's tensor-parallel MLP share and its layout kernels
 on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-extras]
+                    [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input.
-It is timed both as eager launches and as a captured HIP graph replay; the
-faster mode gives the value and is named in "timed_as".
-Default workload (GPT-2-small MLP at TP=4, 4096 tokens): cut this rank's
-A_i/B_i out of the full weights (split along columns / rows into 4 shards
-each), run GEMM1 + GeLU and GEMM2 on the compute stream, and sum the 4 fp32
-partials (this rank's and 3 peers' computed beforehand by the same path) on a
-second stream.  The value is per-rank MLP TFLOP/s (2 GEMMs, 2*M*H*F flops
-each) over the whole step.  Per-kernel durations come from HIP events that
-the library records around each of its launches inside the timed region.
+The headline workload is the GPT-3 175B per-rank MLP at TP = 8 with the
+Domino 2D split (X in 2 row chunks, B_i in 2 column blocks): GEMM1 + GeLU per
+row chunk, GEMM2 per block into the fp32 partial, and each block's 8-way
+partial sum on a second stream beside the next block's GEMMs.  The value is
+per-rank MLP TFLOP/s (2 GEMMs of 2*M*H*F flops) over K consecutive steps,
+timed both as eager launches and as a HIP graph replay (the faster counts,
+named in "timed_as").
+
+Besides that, every workload reports per-step medians with p10/p90, warm
+(steps back to back) and cold (512 MiB written between steps, so nothing of
+the step's inputs is left in L2 or the MALL), the serial schedule's makespan
+next to the two-stream one, and each kernel's rate from HIP events the
+library records around its launches, as a fraction of its roofline.  The
+other four workloads (tiny fp32, GPT-2 small, GPT-3 6.7B, the reshard) follow
+under "configs" unless --no-extras.  The CPU oracle is timed on a row sample,
+with all threads and with one.
 
 Prints one JSON line (last line of stdout).
 """
@@ -37,7 +45,8 @@ sys.path.insert(0, ROOT)
 
 import sharded_gemm_amd as tp  # noqa: E402
 from sharded_gemm_amd import _abi, inputs  # noqa: E402
-from sharded_gemm_amd.workloads import GPT2_SMALL, GPT3_175B, GPT3_6P7B, RESHARD, TINY  # noqa: E402
+from sharded_gemm_amd.workloads import (GPT2_SMALL, GPT3_175B, GPT3_6P7B, RESHARD, TINY,  # noqa: E402
+                                        TINY_LAYOUT_SPECS)
 
 METRIC = "per-rank TP-MLP TFLOP/s (% bf16 MFMA peak) + shard/reduce GB/s (% HBM)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
@@ -55,6 +64,12 @@ def log(msg):
 
 
 # --------------------------------------------------------------------------- workloads
+
+def _device_boxes(shape, spec):
+    """{device: box} of a layout, from the library's host-only planner."""
+    n, boxes, sod = tp.tp_layout_plan(shape, spec, num_dst=16)
+    return {d: boxes[k] for d, k in enumerate(sod) if k >= 0}
+
 
 class MlpStep:
     """Per-rank MLP step, optionally preceded by cutting the weights.  With
@@ -106,6 +121,14 @@ class MlpStep:
             # every rank's sequence block as its own buffer; X becomes the gather workspace
             self.Xb = [b.clone() for b in torch.chunk(self.X, w.P)]
             self.Zs = [torch.empty((w.M // w.P, w.H), device=dev) for _ in range(w.P)]
+        # The tiny workload's step also cuts the 2 x 2 tensor of the ShardingSpec
+        # examples (axis 0, axis 1, both axes, broadcast, split + broadcast).
+        self.layouts = None
+        if w.cfg == 1:
+            src = inputs.arange_tensor((2, 2)).to(dev)
+            self.layouts = [(src, spec, {d: torch.empty(tuple(b - a for a, b in box), device=dev)
+                                         for d, box in _device_boxes((2, 2), spec).items()})
+                            for spec in TINY_LAYOUT_SPECS.values()]
         torch.cuda.synchronize()
         self.s0 = torch.cuda.Stream()     # a side stream: graph capture needs one
         self.s1 = torch.cuda.Stream()
@@ -119,6 +142,9 @@ class MlpStep:
     def prepare(self):
         """Marshal the step's library calls once (the buffers never move)."""
         self.cut = None
+        self.cut_layouts = None
+        if self.layouts:
+            self.cut_layouts = tp.tp_shard_materialize_batch(self.layouts, stream=self.s0, prepare=True)
         if self.split:
             # rank 0's column shard of A and row shard of B in one batched call
             # (one launch): each rank materialises its own share
@@ -134,6 +160,8 @@ class MlpStep:
                                     prepare=True)
 
     def step(self):
+        if self.cut_layouts is not None:
+            self.cut_layouts()
         if self.cut is not None:
             self.cut()
         self.mlp()
@@ -157,9 +185,11 @@ class MlpStep:
         if self.seq:
             cfg["sequence_parallel"] = {"blocks": w.P, "input": "all-gathered from P sequence blocks",
                                         "output": "reduce-scattered into P sequence blocks"}
+        if self.layouts:
+            cfg["layouts_cut_each_step"] = "the 2 x 2 tensor under the " + ", ".join(TINY_LAYOUT_SPECS) + " specs"
         return cfg
 
-    def cpu_baseline(self, budget_s):
+    def cpu_baseline(self, budget_s, rows=None):
         """The oracle on this step (sampled rows for the large shapes), fp64."""
         from threadpoolctl import threadpool_info
         from oracle import layout as L
@@ -168,7 +198,8 @@ class MlpStep:
         w = self.w
         Xc = self.X.cpu()
         A0, B0 = self.As[0].cpu(), self.Bs[0].cpu()
-        rows = w.M if w.M * w.H * w.F <= 4096 * 768 * 768 else 256
+        if rows is None:
+            rows = w.M if w.M * w.H * w.F <= 4096 * 768 * 768 else 256
         sample_rows = np.linspace(0, w.M - 1, rows).astype(np.int64)
         peers = [inputs.normal((rows, w.H), 99000 + p) for p in range(w.P - 1)]
         Ac = self.A.cpu() if self.split else None
@@ -177,6 +208,9 @@ class MlpStep:
         xblocks = dict(enumerate(np.split(Xc[sample_rows].float().numpy(), w.P))) if self.seq else None
         reps, t0 = 0, time.perf_counter()
         while True:
+            if self.layouts:
+                for src, spec, _ in self.layouts:
+                    L.split(src.cpu(), spec)
             if self.split:
                 L.split(Ac, self.sa)
                 L.split(Bc, self.sb)
@@ -194,7 +228,7 @@ class MlpStep:
         flops = 4.0 * rows * w.H * w.F
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
         return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-                "sample": (f"{rows} of {w.M} token rows of the per-rank MLP (fp64, numpy BLAS), "
+                "sample": (f"{rows} of {w.M} token rows of the per-rank MLP (fp64, numpy's BLAS), "
                            f"{'plus cutting the full weights into the shards of every rank (the oracle has no one-device form), ' if self.split else ''}"
                            f"{'plus the all-gather of those rows from P blocks, ' if self.seq else ''}"
                            f"plus the {w.P}-way partial sum of those rows; {reps} repetitions, "
@@ -539,7 +573,15 @@ def measured_traffic(workload, kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def kernel_table(stats, steps):
+def _peak(unit, dtype):
+    if unit == "GB/s":
+        return "hbm", PEAK_HBM_GBS
+    return ("mfma", PEAK_BF16_TFLOPS) if dtype == "bf16" else ("alu", PEAK_F32_TFLOPS)
+
+
+def kernel_table(stats, steps, dtype):
+    """Per library kernel: launches per step, average duration (HIP events on
+    the launching stream) and the algorithmic rate with its roofline fraction."""
     out = {}
     for name, st in stats.items():
         if st["launches"] == 0:
@@ -547,19 +589,20 @@ def kernel_table(stats, steps):
         is_gemm = name.startswith("gemm") and name not in BYTE_KERNELS
         avg_ms = st["total_ms"] / st["launches"]
         rate = st["work"] / (st["total_ms"] * 1e-3)
+        unit = "TFLOP/s" if is_gemm else "GB/s"
+        bound, peak = _peak(unit, dtype)
+        achieved = rate / (1e12 if is_gemm else 1e9)
         out[name] = {"launches_per_step": st["launches"] / steps, "avg_ms": avg_ms,
-                     "ms_per_step": st["total_ms"] / steps,
-                     "achieved": rate / (1e12 if is_gemm else 1e9),
-                     "unit": "TFLOP/s" if is_gemm else "GB/s"}
+                     "ms_per_step": st["total_ms"] / steps, "work_per_launch": st["work"] / st["launches"],
+                     "achieved": achieved, "unit": unit, "bound": bound, "peak": peak, "frac": achieved / peak}
     return out
 
 
-def roofline(kernels, dtype, workload, default_schedule=True):
-    """Roofline entry of the dominant kernel.  In an MLP step that is the slower
-    of the two GEMMs (together more than half the step; the weight cuts are two
-    short launches whose per-launch event overhead would otherwise let them
-    overtake a GEMM from run to run), GEMM2 counting with the reduction when
-    that runs in its epilogue; elsewhere the kernel with the most time."""
+def roofline(kernels, dtype, workload, default_schedule=True, timing="cold"):
+    """Roofline entry of the dominant kernel: the kernel with the most time per
+    step among the GEMMs (together most of an MLP step), GEMM2 counting with
+    the reduction when that runs in its epilogue; elsewhere the kernel with the
+    most time."""
     if not kernels:
         return None
     pool = [k for k in kernels if k.startswith("gemm")] or list(kernels)
@@ -568,12 +611,9 @@ def roofline(kernels, dtype, workload, default_schedule=True):
     # The counters were taken with the default schedule and outputs; another
     # schedule moves other bytes.
     traffic = measured_traffic(workload, name) if default_schedule else None
-    if k["unit"] == "TFLOP/s":
-        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
-        return {"kernel": name, "bound": "mfma" if dtype == "bf16" else "alu", "achieved": k["achieved"],
-                "peak": peak, "unit": "TFLOP/s", "frac": k["achieved"] / peak, "traffic": traffic}
-    return {"kernel": name, "bound": "hbm", "achieved": k["achieved"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": k["achieved"] / PEAK_HBM_GBS, "traffic": traffic}
+    return {"kernel": name, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"], "unit": k["unit"],
+            "frac": k["frac"], "traffic": traffic, "avg_ms": k["avg_ms"],
+            "work_per_launch": k["work_per_launch"], "timing": timing}
 
 
 # --------------------------------------------------------------------------- torch context
@@ -627,16 +667,197 @@ def torch_context(wl, reps=20):
     return out
 
 
+# --------------------------------------------------------------------------- timing
+
+FLUSH_BYTES = 512 << 20
+HEADLINE = GPT3_175B.name
+EXTRAS = (TINY.name, GPT2_SMALL.name, GPT3_6P7B.name, RESHARD.name)
+
+
+class Flusher:
+    """512 MiB read and written on a stream between timed steps: twice the
+    256 MB MALL, so a step timed after it finds none of its inputs in L2 or
+    the MALL (cold-cache timing)."""
+
+    def __init__(self):
+        self.buf = torch.zeros(FLUSH_BYTES // 4, device="cuda")
+
+    def __call__(self, stream):
+        with torch.cuda.stream(stream):
+            self.buf.add_(1.0)
+
+
+def spread(ms):
+    """Median, p10 and p90 of per-step times (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "n": int(a.size)}
+
+
+def capture(wl):
+    """The step captured into a HIP graph on the workload's compute stream, or
+    None when capture fails or a replay differs from the eager result."""
+    try:
+        eager_out = wl.result().clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=wl.s0):
+            wl.step()
+        with torch.cuda.stream(wl.s0):
+            for _ in range(3):
+                graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(eager_out.view(torch.int32), wl.result().view(torch.int32)):
+            raise RuntimeError("graph replay differs from the eager step")
+        return graph
+    except Exception as e:  # report and time eagerly
+        log(f"[bench] graph capture unavailable ({e}); timing eager steps")
+        return None
+
+
+def measure(wl, steps, warmup, flusher, kernel_tables=True):
+    """Time one workload: K consecutive steps (eager and graph replay; the
+    faster gives ms_per_step), per-step times warm and cold in that mode, and
+    the library's per-kernel events, warm and cold (eager launches)."""
+    if hasattr(wl, "prepare"):
+        wl.prepare()
+    dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    graph = capture(wl)
+    s0 = wl.s0
+
+    def one(use_graph):
+        if use_graph:
+            with torch.cuda.stream(s0):
+                graph.replay()
+        else:
+            wl.step()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def consecutive(use_graph):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(s0)
+        for _ in range(steps):
+            one(use_graph)
+        stop.record(s0)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps, (time.perf_counter() - t0) / steps
+
+    ms_eager, _ = consecutive(False)
+    ms_graph = consecutive(True)[0] if graph is not None else None
+    use_graph = ms_graph is not None and ms_graph < ms_eager
+    ms = ms_graph if use_graph else ms_eager
+
+    def per_step(cold, use_graph):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            if cold:
+                flusher(s0)
+            e0.record(s0)
+            one(use_graph)
+            e1.record(s0)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    warm = per_step(False, use_graph)
+    cold = per_step(True, use_graph)
+
+    def kernels(cold):
+        tp.tp_timing_enable(True)
+        for _ in range(2):            # creates the timing events outside the measured steps
+            wl.step()
+        torch.cuda.synchronize()
+        tp.tp_timing_read()
+        for _ in range(steps):
+            if cold:
+                flusher(s0)
+            wl.step()
+        torch.cuda.synchronize()
+        tp.tp_timing_enable(False)
+        return kernel_table(tp.tp_timing_read(), steps, dtype)
+
+    out = {"ms_per_step": ms, "timed_as": "hip graph replay" if use_graph else "eager launches",
+           "ms_per_step_eager": ms_eager, "ms_per_step_graph": ms_graph,
+           "step_ms": {"warm": spread(warm), "cold": spread(cold)}, "dtype": dtype}
+    if kernel_tables:
+        out["kernels_cold"] = kernels(True)
+        out["kernels_warm"] = kernels(False)
+    return out
+
+
+def rate(wl, ms):
+    return wl.work / (ms * 1e-3) / (1e12 if wl.unit == "TFLOP/s" else 1e9)
+
+
+def run_workload(name, steps, warmup, flusher, args, serial_too=True):
+    """Set up, time and summarise one workload (and, for a chunked MLP, its
+    serial schedule); returns (workload object, summary dict)."""
+    log(f"[bench] workload {name}: setting up")
+    wl = WORKLOADS[name]()
+    wl.serial, wl.reduce_wgs = args.serial, args.reduce_wgs
+    if args.no_reduce_fusion:
+        wl.reduce_fusion = tp.TP_REDUCE_FUSION_OFF
+    wl.separate_output = args.separate_output
+    log(f"[bench] workload {name}: timing")
+    m = measure(wl, steps, warmup, flusher)
+    default_schedule = not (args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output)
+    summ = {"config": wl.config(), "value": rate(wl, m["ms_per_step"]), "unit": wl.unit,
+            "ms_per_step": m["ms_per_step"], "timed_as": m["timed_as"],
+            "ms_per_step_eager": m["ms_per_step_eager"], "ms_per_step_graph": m["ms_per_step_graph"],
+            "step_ms": m["step_ms"], "value_cold_median": rate(wl, m["step_ms"]["cold"]["median"]),
+            "roofline": roofline(m["kernels_cold"], m["dtype"], name, default_schedule),
+            "kernels": m["kernels_cold"], "kernels_warm": m["kernels_warm"], "dtype": m["dtype"]}
+    for k, v in m["kernels_cold"].items():
+        log(f"[bench]   {k:18s} {v['launches_per_step']:.0f}/step  avg {v['avg_ms'] * 1e3:9.1f} us  "
+            f"{v['achieved']:9.1f} {v['unit']}  ({100 * v['frac']:.1f}% of {v['peak']:.0f}, cold)")
+    log(f"[bench]   step {m['ms_per_step'] * 1e3:.1f} us ({m['timed_as']}); per step warm median "
+        f"{m['step_ms']['warm']['median'] * 1e3:.1f} us, cold median {m['step_ms']['cold']['median'] * 1e3:.1f} us")
+    two_blocks = isinstance(wl, (MlpStep, BwdStep, StackStep)) and wl.w.R * getattr(wl.w, "C", 1) > 1
+    if serial_too and two_blocks and not args.serial:
+        log(f"[bench] workload {name}: serial schedule")
+        wl.serial = True
+        ms = measure(wl, steps, warmup, flusher, kernel_tables=False)
+        wl.serial = False
+        summ["serial"] = {"ms_per_step": ms["ms_per_step"], "timed_as": ms["timed_as"], "step_ms": ms["step_ms"],
+                          "value": rate(wl, ms["ms_per_step"])}
+        summ["overlap_saves"] = {"warm_median_ms": ms["step_ms"]["warm"]["median"] - m["step_ms"]["warm"]["median"],
+                                 "cold_median_ms": ms["step_ms"]["cold"]["median"] - m["step_ms"]["cold"]["median"]}
+        log(f"[bench]   serial {ms['ms_per_step'] * 1e3:.1f} us against {m['ms_per_step'] * 1e3:.1f} us on two streams")
+        if hasattr(wl, "prepare"):
+            wl.prepare()
+    return wl, summ
+
+
+def cpu_baselines(wl, budget_s, single_thread=True):
+    """The oracle timed with every BLAS thread, and with one (fewer sampled rows)."""
+    from threadpoolctl import threadpool_limits
+    log("[bench] timing the CPU oracle (all threads)")
+    cpu = wl.cpu_baseline(budget_s)
+    if single_thread:
+        log("[bench] timing the CPU oracle (one thread)")
+        with threadpool_limits(limits=1):
+            kw = {"rows": 32} if isinstance(wl, MlpStep) and wl.w.M * wl.w.H * wl.w.F > 4096 * 768 * 768 else {}
+            one = wl.cpu_baseline(budget_s, **kw)
+        cpu["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+    return cpu
+
+
 # --------------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=GPT2_SMALL.name, choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only --workload (the default run also times the other four configurations)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing per thread setting")
     ap.add_argument("--serial", action="store_true", help="run the reduce on the compute stream")
     ap.add_argument("--separate-output", action="store_true",
                     help="write the reduced output to its own buffer instead of in place over the partial")
@@ -646,9 +867,8 @@ def main():
                     help="cap on the reduce kernel's workgroups beside the GEMMs (0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB plain copy (for calibrating traffic counters)")
-    ap.add_argument("--torch-context", action="store_true",
-                    help="also time torch.matmul (hipBLASLt) and a torch sum of the partials on the same shapes "
-                         "(context only; MLP workloads)")
+    ap.add_argument("--no-torch-context", action="store_true",
+                    help="skip timing torch.matmul (hipBLASLt) and a torch sum on the headline's shapes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -666,122 +886,41 @@ def main():
     if args.copy_calibration:
         log("[bench] 256 MiB copy for counter calibration")
         copy_calibration()
-    log(f"[bench] workload {args.workload}: setting up")
-    wl = WORKLOADS[args.workload]()
-    wl.serial, wl.reduce_wgs = args.serial, args.reduce_wgs
-    if args.no_reduce_fusion:
-        wl.reduce_fusion = tp.TP_REDUCE_FUSION_OFF
-    wl.separate_output = args.separate_output
-    if hasattr(wl, "prepare"):
-        wl.prepare()
-    dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        wl.step()
-    torch.cuda.synchronize()
+    flusher = Flusher()
+    wl, head = run_workload(args.workload, args.steps, args.warmup, flusher, args)
+    cpu = None if args.no_cpu_baseline else cpu_baselines(wl, args.cpu_budget)
+    context = (torch_context(wl) if not args.no_torch_context and isinstance(wl, MlpStep) and wl.w.dtype == "bf16"
+               else None)
+    del wl
+    torch.cuda.empty_cache()
 
-    # The step is captured once into a HIP graph (the hot path is launch-bound
-    # at these sizes) and the timed region replays it; a second timed region
-    # runs the same steps eagerly with per-kernel HIP events for the table.
-    graph = None
-    try:
-        eager_out = wl.result().clone()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=wl.s0):
-            wl.step()
-        with torch.cuda.stream(wl.s0):
-            for _ in range(3):
-                graph.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(eager_out.view(torch.int32), wl.result().view(torch.int32)):
-            raise RuntimeError("graph replay differs from the eager step")
-    except Exception as e:  # report and time eagerly
-        log(f"[bench] graph capture unavailable ({e}); timing eager steps")
-        graph = None
+    configs = {}
+    if not args.no_extras and args.workload == HEADLINE:
+        for name in EXTRAS:
+            w2, summ = run_workload(name, args.steps, args.warmup, flusher, args)
+            if not args.no_cpu_baseline:
+                summ["cpu_baseline"] = cpu_baselines(w2, min(3.0, args.cpu_budget), single_thread=False)
+            configs[name] = summ
+            del w2
+            torch.cuda.empty_cache()
 
-    def run(k):
-        if graph is None:
-            for _ in range(k):
-                wl.step()
-        else:
-            with torch.cuda.stream(wl.s0):
-                for _ in range(k):
-                    graph.replay()
-
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-
-    def timed(use_graph):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record(wl.s0)
-        if use_graph:
-            run(args.steps)
-        else:
-            for _ in range(args.steps):
-                wl.step()
-        stop.record(wl.s0)
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps, (time.perf_counter() - t0) / args.steps
-
-    # Both execution modes run the same kernels on the same data; the faster is
-    # the value (a captured graph removes host launch gaps, but its replay does
-    # not overlap the two streams the way eager launches do).
-    log(f"[bench] timing {args.steps} eager steps")
-    ms_eager_plain, wall_eager_plain = timed(False)
-    ms_graph = None
-    if graph is not None:
-        log(f"[bench] timing {args.steps} graph replays")
-        ms_graph, wall_graph = timed(True)
-    use_graph = ms_graph is not None and ms_graph < ms_eager_plain
-    ms_per_step = ms_graph if use_graph else ms_eager_plain
-    wall = wall_graph if use_graph else wall_eager_plain
-
-    log(f"[bench] timing {args.steps} eager steps with per-kernel events")
-    tp.tp_timing_enable(True)
-    for _ in range(args.steps):      # creates the timing events outside the timed region
-        wl.step()
-    torch.cuda.synchronize()
-    tp.tp_timing_read()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    start.record(wl.s0)
-    for _ in range(args.steps):
-        wl.step()
-    stop.record(wl.s0)
-    torch.cuda.synchronize()
-    wall_eager = time.perf_counter() - t1
-    tp.tp_timing_enable(False)
-    stats = tp.tp_timing_read()
-    ms_eager = start.elapsed_time(stop) / args.steps
-
-    value = wl.work / (ms_per_step * 1e-3) / (1e12 if wl.unit == "TFLOP/s" else 1e9)
-    kernels = kernel_table(stats, args.steps)
-    for name, k in kernels.items():
-        log(f"[bench] {name:12s} {k['launches_per_step']:.0f}/step  avg {k['avg_ms'] * 1e3:9.1f} us  "
-            f"{k['achieved']:9.1f} {k['unit']}")
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({'graph replay' if use_graph else 'eager'}; eager "
-        f"{ms_eager_plain * 1e3:.1f} us, graph {ms_graph * 1e3 if ms_graph else float('nan'):.1f} us; "
-        f"eager with kernel events {ms_eager * 1e3:.1f} us)")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        cpu = wl.cpu_baseline(args.cpu_budget)
-
-    context = torch_context(wl) if args.torch_context and isinstance(wl, MlpStep) else None
-
-    rec = {"metric": METRIC, "value": value, "unit": wl.unit, "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded N(0,1)/N(0,0.02) tensors)",
-           "config": wl.config(), "roofline": roofline(kernels, dtype, args.workload, default_schedule=not (
-               args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output)), "cpu_baseline": cpu,
-           "kernels": kernels, "timed_as": "hip graph replay" if use_graph else "eager launches",
-           "ms_per_step_eager": ms_eager_plain, "ms_per_step_graph": ms_graph,
-           "ms_per_step_eager_with_kernel_events": ms_eager,
-           "device": torch.cuda.get_device_name(0)}
+    rec = {"metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic (seeded N(0,1)/N(0,0.02) tensors)",
+           "config": head["config"], "roofline": head["roofline"], "cpu_baseline": cpu}
+    for k in ("timed_as", "ms_per_step_eager", "ms_per_step_graph", "step_ms", "value_cold_median", "serial",
+              "overlap_saves", "kernels", "kernels_warm"):
+        if k in head:
+            rec[k] = head[k]
+    rec["timing"] = ("value: K consecutive steps (the faster of eager launches and a HIP graph replay); step_ms: "
+                     "per-step HIP events, warm = back to back, cold = after 512 MiB written; kernels: the "
+                     "library's HIP events around each launch on its stream, cold; roofline: the dominant "
+                     "kernel of the cold table")
     if context is not None:
         rec["torch_context"] = context
+    if configs:
+        rec["configs"] = configs
+    rec["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(rec), flush=True)
 
 

@@ -28,7 +28,7 @@ def test_fused_kernel_is_priced_against_hbm():
     st = _stats(materialize=dict(launches=1, total_ms=0.004, work=4.72e6),
                 gemm1=dict(launches=1, total_ms=0.012, work=4.83e9),
                 gemm2_reduce=dict(launches=1, total_ms=0.0165, work=57.8e6))
-    k = bench.kernel_table(st, 1)
+    k = bench.kernel_table(st, 1, "bf16")
     assert k["gemm1"]["unit"] == "TFLOP/s" and abs(k["gemm1"]["achieved"] - 402.5) < 1
     assert k["gemm2_reduce"]["unit"] == "GB/s" and abs(k["gemm2_reduce"]["achieved"] - 3503.0) < 1
     r = bench.roofline(k, "bf16", "no-such-workload")
@@ -38,7 +38,7 @@ def test_fused_kernel_is_priced_against_hbm():
 
 def test_traffic_only_for_the_default_schedule(monkeypatch):
     monkeypatch.setattr(bench, "measured_traffic", lambda workload, kernel: 123.0)
-    k = bench.kernel_table(_stats(gemm1=dict(launches=1, total_ms=0.01, work=1e9)), 1)
+    k = bench.kernel_table(_stats(gemm1=dict(launches=1, total_ms=0.01, work=1e9)), 1, "bf16")
     assert bench.roofline(k, "bf16", "w")["traffic"] == 123.0
     assert bench.roofline(k, "bf16", "w", default_schedule=False)["traffic"] is None
 
@@ -48,3 +48,33 @@ def test_source_hash_ignores_comments_and_layout():
     b = "int f(int x) { return x + 1; }"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only("int f(int x) { return x + 2; }")
+
+
+def test_fractions_per_kernel_family():
+    """Each kernel carries its own roofline: bf16 GEMMs against the MFMA peak,
+    fp32 GEMMs (the tiny workload) against the fp32 vector peak, layout and
+    reduce kernels against HBM."""
+    st = _stats(materialize=dict(launches=2, total_ms=0.2, work=1.6e9),
+                gemm1=dict(launches=2, total_ms=0.5, work=6.2e11),
+                reduce=dict(launches=4, total_ms=0.4, work=1.8e9))
+    k = bench.kernel_table(st, 2, "bf16")
+    assert k["gemm1"]["bound"] == "mfma" and k["gemm1"]["peak"] == bench.PEAK_BF16_TFLOPS
+    assert abs(k["gemm1"]["frac"] - (6.2e11 / 0.5e-3 / 1e12) / 2500.0) < 1e-9
+    assert k["reduce"]["bound"] == "hbm" and abs(k["reduce"]["achieved"] - 4500.0) < 1e-6
+    assert k["materialize"]["launches_per_step"] == 1.0 and k["reduce"]["work_per_launch"] == 4.5e8
+    f = bench.kernel_table(_stats(gemm1=dict(launches=1, total_ms=0.01, work=1e8)), 1, "f32")
+    assert f["gemm1"]["bound"] == "alu" and f["gemm1"]["peak"] == bench.PEAK_F32_TFLOPS
+    r = bench.roofline(k, "bf16", "w")
+    assert r["kernel"] == "gemm1" and r["avg_ms"] == 0.25 and r["timing"] == "cold"
+
+
+def test_spread_reports_median_and_percentiles():
+    s = bench.spread([1.0, 2.0, 3.0, 4.0, 100.0])
+    assert s["median"] == 3.0 and s["n"] == 5
+    assert 1.0 <= s["p10"] <= 2.0 and 4.0 <= s["p90"] <= 100.0
+
+
+def test_default_workload_is_the_largest_single_gpu_configuration():
+    assert bench.HEADLINE == "gpt3-175b-tp8-2d-r2c2"
+    assert set(bench.EXTRAS) == {"tiny-fp32-p2", "gpt2-small-tp4", "gpt3-6.7b-tp8-rowsplit2", "reshard-2x4-mesh"}
+    assert bench.FLUSH_BYTES >= 512 << 20

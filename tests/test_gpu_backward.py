@@ -7,7 +7,7 @@ import torch
 
 import sharded_gemm_amd as tp
 from sharded_gemm_amd import inputs
-from sharded_gemm_amd.workloads import GPT3_6P7B, TINY
+from sharded_gemm_amd.workloads import GPT3_175B, GPT3_6P7B, TINY
 from oracle import layout as L
 from oracle import mlp as O
 from oracle import reduce as R
@@ -294,25 +294,38 @@ def test_backward_chunks_do_not_change_a_bit():
             assert np.array_equal(bits(a), bits(b))
 
 
-def test_backward_gpt3_6p7b_sampled():
-    """Full GPT-3 6.7B per-rank shape (TP = 8, R = 2): rows of dH / dX / dX_out
-    and columns of dA / rows of dB against the oracle.  Each row of dH depends
-    on its own rows of X and dZ; each column f of dA (row f of dB) on column f
-    of A_i and row f of B_i alone, so the samples are exact restrictions."""
-    w = GPT3_6P7B
+def _chunk_rows(M, Rc, per_chunk):
+    """Rows of each row chunk: its first and last row plus evenly spread ones."""
+    Mr = M // Rc
+    rows = []
+    for r in range(Rc):
+        rows += list(np.unique(np.linspace(r * Mr, (r + 1) * Mr - 1, per_chunk).astype(np.int64)))
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("w", [GPT3_6P7B, GPT3_175B], ids=lambda w: w.name)
+def test_backward_tp8_sampled(w):
+    """Full GPT-3 per-rank shapes at TP = 8 (R = 2), as the bench times them:
+    128 rows of dH / dX / dX_out (64 per row chunk, each chunk's first and last
+    among them) and 32 columns of dA / rows of dB against the oracle.  Each row
+    of dH depends on its own rows of X and dZ; each column f of dA (row f of dB)
+    on column f of A_i and row f of B_i alone, so the samples are exact
+    restrictions.  The peers' input gradients are drawn, not computed."""
     announce(f"backward {w.name} sampled")
     M, H, F, P = w.M, w.H, w.F, w.P
-    X = inputs.normal((M, H), inputs.seed_for(3, inputs.SLOT_X), 1.0, "bf16", "cuda")
-    A = inputs.normal((H, F), inputs.seed_for(3, inputs.SLOT_A), 0.02, "bf16", "cuda")
-    B = inputs.normal((F, H), inputs.seed_for(3, inputs.SLOT_B), 0.02, "bf16", "cuda")
-    dZ = inputs.normal((M, H), 3004, 1.0, "bf16", "cuda")
-    peers = [inputs.normal((M, H), 3050 + p, 1.0, "f32", "cuda") for p in range(P - 1)]
+    X = inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_X), 1.0, "bf16", "cuda")
+    A = inputs.normal((H, F), inputs.seed_for(w.cfg, inputs.SLOT_A), 0.02, "bf16", "cuda")
+    B = inputs.normal((F, H), inputs.seed_for(w.cfg, inputs.SLOT_B), 0.02, "bf16", "cuda")
+    dZ = inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_DZ), 1.0, "bf16", "cuda")
+    peers = [inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_PARTIAL + p), 1.0, "f32", "cuda")
+             for p in range(P - 1)]
     Y, Hs = forward(X, A, B)
     dH, dX, dXo, dA, dB = backward(X, A, B, Hs, Y, dZ, R=w.R, peers=peers)
+    del Y, Hs
     Xc, Ac, Bc, dZc = X.cpu(), A.cpu(), B.cpu(), dZ.cpu()
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(M, 48, replace=False))
-    cols = np.sort(rng.choice(F, 24, replace=False))
+    rows = _chunk_rows(M, w.R, 64)
+    cols = np.sort(np.random.default_rng(0).choice(F, 32, replace=False))
+    announce(f"backward {w.name}: oracle on {len(rows)} rows and {len(cols)} columns")
     gr = O.backward_rank(Xc[rows], Ac, Bc, dZc[rows])
     assert rel_err(dH[rows], gr["dH"]) <= TOL_BF16
     assert rel_err(dX[rows], gr["dX_i"]) <= TOL_BF16

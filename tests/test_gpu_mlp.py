@@ -260,11 +260,11 @@ def _large_case(w, per_chunk):
 
 
 def test_gpt3_6p7b_tp8_rowsplit():
-    _large_case(GPT3_6P7B, per_chunk=32)
+    _large_case(GPT3_6P7B, per_chunk=64)
 
 
 def test_gpt3_175b_tp8_2d():
-    _large_case(GPT3_175B, per_chunk=16)
+    _large_case(GPT3_175B, per_chunk=64)
 
 
 def test_error_leaves_outputs_untouched():

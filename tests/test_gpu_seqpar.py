@@ -8,6 +8,7 @@ import torch
 
 import sharded_gemm_amd as tp
 from sharded_gemm_amd import inputs
+from sharded_gemm_amd.workloads import GPT3_175B
 from oracle import mlp as O
 from oracle import reduce as R
 
@@ -138,6 +139,80 @@ def test_forward_gelu_matches_unsplit_path_bitwise():
     assert rel_err(full[torch.from_numpy(rows)], ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,H,F,Rc,Cc,P,S,with_bias", [
+    (256, 96, 64, 1, 1, 3, 4, True),     # one chunk covers 4 blocks: every row to its block (nout 4)
+    (256, 96, 64, 2, 1, 2, 4, False),    # a chunk covers 2 blocks (nout 2)
+    (192, 80, 48, 1, 2, 2, 3, True),     # 3 blocks, 2 column blocks
+    (256, 64, 32, 4, 1, 3, 2, True),     # a chunk lies inside one block
+    (200, 72, 40, 1, 1, 2, 8, False),    # 8 blocks in the chunk: beyond the epilogue's outputs
+    (64, 256, 512, 1, 1, 2, 2, True),    # the tiny workload's shape
+])
+def test_forward_fp32_integer_exact(M, H, F, Rc, Cc, P, S, with_bias):
+    """fp32 path (the tiny workload's kernels) with the reduce-scatter: the
+    epilogue's form on the serial schedule and the separate kernel on two
+    streams give the same bits, each block equal to the oracle's rows."""
+    announce(f"seqpar fp32 integer exact M={M} H={H} F={F} R={Rc} C={Cc} P={P} S={S} bias={with_bias}")
+    Ms = M // S
+    Xb = [inputs.small_ints((Ms, H), seed=900 + j, lo=-4, hi=4) for j in range(S)]
+    A = _one_hot(H, F, 950).float()
+    B = inputs.small_ints((F, H), seed=951, lo=-4, hi=4)
+    peers = [inputs.small_ints((M, H), seed=960 + p, lo=-512, hi=512) for p in range(P - 1)]
+    bias = inputs.small_ints((H,), seed=959, lo=-64, hi=64) if with_bias else None
+    dev = dict(X_blocks=[x.cuda() for x in Xb], A=A.cuda(), B=B.cuda(), peers=[p.cuda() for p in peers])
+    kw = dict(Rc=Rc, Cc=Cc, act=tp.TP_ACT_NONE, bias=bias.cuda() if with_bias else None)
+    fused = sp_forward(**dev, two_streams=False, **kw)
+    apart = sp_forward(**dev, two_streams=False, fusion=tp.TP_REDUCE_FUSION_OFF, **kw)
+    beside = sp_forward(**dev, two_streams=True, **kw)
+    for got in (apart, beside):
+        for a, b in zip(got[:3], fused[:3]):
+            assert np.array_equal(bits(a), bits(b))
+        for j in range(S):
+            assert np.array_equal(bits(got[3][j]), bits(fused[3][j])), j
+    X = torch.cat(Xb)
+    assert np.array_equal(bits(fused[0]), bits(X))
+    z_ref = O.mlp_rank(X, A, B, O.GELU_NONE)
+    assert np.array_equal(_f64(fused[2]), z_ref)
+    ref = R.reduce_split([z_ref] + [_f64(p) for p in peers], S, "sum", _f64(bias) if with_bias else None)
+    for j in range(S):
+        assert np.array_equal(_f64(fused[3][j]), ref[j]), j
+
+
+def _chunk_rows(M, Rc, per_chunk):
+    Mr = M // Rc
+    rows = []
+    for r in range(Rc):
+        rows += list(np.unique(np.linspace(r * Mr, (r + 1) * Mr - 1, per_chunk).astype(np.int64)))
+    return np.array(rows)
+
+
+def test_forward_gpt3_175b_sampled():
+    """The GPT-3 175B per-rank shape as the bench's sequence-parallel step runs
+    it (TP = 8: 8 sequence blocks, R = 2, C = 2, two streams): the gathered
+    input equals the blocks, and 128 rows of the reduce-scattered output (64
+    per row chunk, each chunk's first and last among them) match the oracle's
+    rank-0 rows plus the drawn peers' rows."""
+    w = GPT3_175B
+    announce(f"seqpar forward {w.name} sampled")
+    M, H, F, P, S = w.M, w.H, w.F, w.P, w.P
+    Ms = M // S
+    Xb = [inputs.normal((Ms, H), inputs.seed_for(w.cfg, inputs.SLOT_X) + 100 * j, 1.0, "bf16", "cuda")
+          for j in range(S)]
+    A = inputs.normal((H, F), inputs.seed_for(w.cfg, inputs.SLOT_A), 0.02, "bf16", "cuda")
+    B = inputs.normal((F, H), inputs.seed_for(w.cfg, inputs.SLOT_B), 0.02, "bf16", "cuda")
+    peers = [inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_PARTIAL + p), 1.0, "f32", "cuda")
+             for p in range(P - 1)]
+    Xg, Y, Z, Zs = sp_forward(Xb, A, B, peers, Rc=w.R, Cc=w.C)
+    X = torch.cat([x.cpu() for x in Xb])
+    assert np.array_equal(bits(Xg), bits(X))
+    rows = _chunk_rows(M, w.R, 64)
+    announce(f"seqpar forward {w.name}: oracle on {len(rows)} rows")
+    z0 = O.mlp_rank_rows(X, A.cpu(), B.cpu(), rows)
+    assert rel_err(Z[torch.from_numpy(rows)], z0) <= TOL_BF16
+    ref = z0 + sum(p[torch.from_numpy(rows).cuda()].cpu().double().numpy() for p in peers)
+    full = torch.cat(Zs)
+    assert rel_err(full[torch.from_numpy(rows)], ref) <= TOL_BF16
+
+
 def sp_backward(X, A, B, Y, dZ_blocks, peers, *, Rc=1, act=tp.TP_ACT_NONE, H_i=None, two_streams=True):
     S = len(dZ_blocks)
     Ms, H = dZ_blocks[0].shape
@@ -208,6 +283,43 @@ def test_backward_gelu_tolerance():
     assert rel_err(dA, g["dA_i"]) <= TOL_BF16
     assert rel_err(dB, g["dB_i"]) <= TOL_BF16
     assert rel_err(torch.cat(dXs), g["dX_i"] + _f64(peers[0])) <= TOL_BF16
+
+
+def test_backward_gpt3_175b_sampled():
+    """The bench's sequence-parallel backward at the GPT-3 175B per-rank shape
+    (TP = 8 blocks, R = 2): dZ gathered from its blocks, 128 rows of the
+    reduce-scattered input gradient and 32 columns of dA / rows of dB against
+    the oracle."""
+    w = GPT3_175B
+    announce(f"seqpar backward {w.name} sampled")
+    M, H, F, P, S = w.M, w.H, w.F, w.P, w.P
+    X = inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_X), 1.0, "bf16", "cuda")
+    A = inputs.normal((H, F), inputs.seed_for(w.cfg, inputs.SLOT_A), 0.02, "bf16", "cuda")
+    B = inputs.normal((F, H), inputs.seed_for(w.cfg, inputs.SLOT_B), 0.02, "bf16", "cuda")
+    dZb = [inputs.normal((M // S, H), inputs.seed_for(w.cfg, inputs.SLOT_DZ) + 100 * j, 1.0, "bf16", "cuda")
+           for j in range(S)]
+    peers = [inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_PARTIAL + p), 1.0, "f32", "cuda")
+             for p in range(P - 1)]
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    Hs = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    tp.tp_colrow_mlp(X, A, B, Y, Z, H_out=Hs)
+    del Z
+    dZg, dX, dA, dB, dXs = sp_backward(X, A, B, Y, dZb, peers, Rc=w.R, act=tp.TP_ACT_GELU_ERF, H_i=Hs)
+    dZ = torch.cat([d.cpu() for d in dZb])
+    assert np.array_equal(bits(dZg), bits(dZ))
+    Xc, Ac, Bc = X.cpu(), A.cpu(), B.cpu()
+    rows = _chunk_rows(M, w.R, 64)
+    cols = np.sort(np.random.default_rng(1).choice(F, 32, replace=False))
+    announce(f"seqpar backward {w.name}: oracle on {len(rows)} rows and {len(cols)} columns")
+    gr = O.backward_rank(Xc[rows], Ac, Bc, dZ[rows])
+    assert rel_err(dX[torch.from_numpy(rows)], gr["dX_i"]) <= TOL_BF16
+    ridx = torch.from_numpy(rows)
+    ref = gr["dX_i"] + sum(p[ridx.cuda()].cpu().double().numpy() for p in peers)
+    assert rel_err(torch.cat(dXs)[ridx], ref) <= TOL_BF16
+    gc = O.backward_rank(Xc, Ac[:, cols], Bc[cols, :], dZ)
+    assert rel_err(dA[:, cols], gc["dA_i"]) <= TOL_BF16
+    assert rel_err(dB[cols, :], gc["dB_i"]) <= TOL_BF16
 
 
 def test_error_leaves_outputs_untouched():

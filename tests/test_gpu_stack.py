@@ -7,6 +7,7 @@ import torch
 
 import sharded_gemm_amd as tp
 from sharded_gemm_amd import inputs
+from sharded_gemm_amd.workloads import GPT3_175B, GPT3_6P7B
 from oracle import mlp as O
 
 from gpu_helpers import Guarded, announce, bits, rel_err, require_gpu
@@ -103,6 +104,50 @@ def test_stack_integer_exact(M, H, Fs, R, C, P, two):
     for l, ((z, xn), (zr, xr)) in enumerate(zip(got, ref)):
         assert np.array_equal(z.double().numpy(), zr), l
         assert np.array_equal(bits(xn), bits(torch.from_numpy(xr).to(torch.bfloat16))), l
+
+
+@pytest.mark.parametrize("w", [GPT3_6P7B, GPT3_175B], ids=lambda w: w.name)
+def test_stack_tp8_sampled(w):
+    """Two layers of a GPT-3 per-rank shape at TP = 8, as the bench's 2-layer
+    step runs them (R row chunks, C column blocks, two streams, the inter-layer
+    overlap): 128 rows of each layer's reduced output and of the next layer's
+    bf16 input (64 per row chunk, each chunk's first and last among them)
+    against the oracle's stack on those rows (rows stay independent through
+    the stack).  The peers' partials of each layer are drawn, not computed."""
+    announce(f"stack {w.name} sampled")
+    M, H, F, P = w.M, w.H, w.F, w.P
+    X0 = inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_X), 1.0, "bf16", "cuda")
+    layers = []
+    for l in range(2):
+        s = inputs.seed_for(w.cfg, 0) + 7919 * (l + 1)
+        layers.append({"A_i": inputs.normal((H, F), s + inputs.SLOT_A, 0.02, "bf16", "cuda"),
+                       "B_i": inputs.normal((F, H), s + inputs.SLOT_B, 0.02, "bf16", "cuda"),
+                       "peers": [inputs.normal((M, H), s + inputs.SLOT_PARTIAL + p, 1.0, "f32", "cuda")
+                                 for p in range(P - 1)]})
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Zi = torch.empty((M, H), device="cuda")
+    xs = [Guarded((M, H), torch.bfloat16) for _ in layers]
+    zs = [Guarded((M, H), torch.float32) for _ in layers]
+    args = [dict(X=X0 if l == 0 else xs[l - 1].t, A_i=layer["A_i"], B_i=layer["B_i"], Y_ws=Y, Z_i=Zi,
+                 row_chunks=w.R, col_chunks=w.C, peer_partials=layer["peers"], Z_out=zs[l].t, X_next=xs[l].t)
+            for l, layer in enumerate(layers)]
+    tp.tp_colrow_mlp_stack(args, s_compute=torch.cuda.current_stream(), s_reduce=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    for g in xs + zs:
+        assert g.guards_intact()
+    rows = []
+    Mr = M // w.R
+    for r in range(w.R):
+        rows += list(np.unique(np.linspace(r * Mr, (r + 1) * Mr - 1, 64).astype(np.int64)))
+    ridx = torch.tensor(rows, device="cuda")
+    announce(f"stack {w.name}: oracle on {len(rows)} rows")
+    ref = O.mlp_stack(X0.index_select(0, ridx).cpu(),
+                      [{"A_i": layer["A_i"].cpu(), "B_i": layer["B_i"].cpu(),
+                        "peers": [p.index_select(0, ridx).cpu() for p in layer["peers"]]} for layer in layers],
+                      dtype="bf16")
+    for l, (zr, xr) in enumerate(ref):
+        assert rel_err(zs[l].t.index_select(0, ridx), zr) <= TOL_BF16, l
+        assert rel_err(xs[l].t.index_select(0, ridx).float(), xr) <= TOL_BF16, l
 
 
 def test_stack_equals_layer_by_layer_calls_bitwise():

@@ -371,6 +371,24 @@ enum { TP_REDUCE_FUSION_AUTO = 0, TP_REDUCE_FUSION_OFF = 1 };
 int tp_colrow_mlp(const tp_mlp_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * tp_colrow_mlp with args->Y_ws = NULL, the hidden activations Y kept instead
+ * in a fixed 32 MiB device array of the library, one per GPU (held from module
+ * load until the process ends), which every row chunk reuses in turn.  Y is
+ * therefore not returned; every other argument, output and result bit is as in
+ * tp_colrow_mlp.  The call allocates nothing (no hipMalloc, no hipFree); the
+ * first call on a device looks up that device's array, and the first call that
+ * needs two streams creates the thread's reusable HIP events, as tp_colrow_mlp
+ * does.  All calls on one GPU share its array: calls that overlap on one GPU
+ * (other streams, other threads) race.
+ * Errors: those of tp_colrow_mlp; TP_ERR_ARG for a non-NULL Y_ws;
+ *         TP_ERR_UNSUPPORTED when one row chunk of Y, (M/R) * F elements of the
+ *         dtype, exceeds 32 MiB (then nothing is enqueued).
+ */
+int tp_colrow_mlp_noalloc(const tp_mlp_args *args, tp_stream_t s_compute, tp_stream_t s_reduce);
+
+/*
  * Enqueue num_layers forward layers, layer l+1 reading layer l's output
  * (layers[l].X_next == layers[l+1].X, same dtype, M, H and row_chunks), with
  * Domino's inter-layer overlap ([DOM] "row-wise split of inputs X": no data

@@ -38,7 +38,7 @@ TP_REDUCE_OP_MIN = 2
 
 # Every symbol include/tpshard.h declares.
 EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_binary", "tp_infer_matmul_dims_mapping", "tp_shard_materialize", "tp_shard_materialize_batch", "tp_shard_gather",
-           "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_stack", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
+           "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_noalloc", "tp_colrow_mlp_stack", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
 TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather", "gemm2_reduce",
                    "gemm_dgrad_reduce")
@@ -160,6 +160,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.tp_partial_reduce_ex.restype = C.c_int
     lib.tp_colrow_mlp.restype = C.c_int
     lib.tp_colrow_mlp.argtypes = [C.POINTER(tp_mlp_args), C.c_void_p, C.c_void_p]
+    lib.tp_colrow_mlp_noalloc.restype = C.c_int
+    lib.tp_colrow_mlp_noalloc.argtypes = [C.POINTER(tp_mlp_args), C.c_void_p, C.c_void_p]
     lib.tp_colrow_mlp_stack.restype = C.c_int
     lib.tp_colrow_mlp_stack.argtypes = [C.POINTER(tp_mlp_args), C.c_int64, C.c_void_p, C.c_void_p]
     lib.tp_colrow_mlp_backward.argtypes = [C.POINTER(tp_mlp_bwd_args), C.c_void_p, C.c_void_p]
@@ -495,10 +497,10 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
     M, H = int(X.shape[0]), int(X.shape[1])
     F = int(A_i.shape[1])
     peers = list(peer_partials)
-    if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Y_ws.shape) != (M, F) \
-            or tuple(Z_i.shape) != (M, H):
+    if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Z_i.shape) != (M, H) \
+            or (Y_ws is not None and tuple(Y_ws.shape) != (M, F)):
         raise ValueError("shapes must be X[M,H], A_i[H,F], B_i[F,H], Y_ws[M,F], Z_i[M,H]")
-    if not (X.dtype == A_i.dtype == B_i.dtype == Y_ws.dtype):
+    if not (X.dtype == A_i.dtype == B_i.dtype) or (Y_ws is not None and Y_ws.dtype != X.dtype):
         raise TypeError("X, A_i, B_i and Y_ws must share one dtype")
     for t in (H_out, X_next):
         if t is not None and t.dtype != X.dtype:
@@ -545,6 +547,21 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, prep
         return Prepared(lib.tp_colrow_mlp, (C.byref(args),), keep + [args], [sc, sr],
                         _tensors(X, A_i, B_i, Y_ws, Z_i, *kw.values()))
     _check(lib.tp_colrow_mlp(C.byref(args), sc, sr))
+
+
+def tp_colrow_mlp_noalloc(X, A_i, B_i, Z_i, *, s_compute=None, s_reduce=None, prepare=False, **kw):
+    """tp_colrow_mlp without a Y workspace: the library keeps Y (one row chunk
+    at a time, at most 32 MiB) in its own fixed device array and allocates
+    nothing.  Same keywords and results as tp_colrow_mlp, except that Y is not
+    returned.  Calls that overlap on one GPU race on that array."""
+    lib = load()
+    args, keep = _mlp_args(X, A_i, B_i, None, Z_i, **kw)
+    sc = _stream_ptr(s_compute)
+    sr = _stream_ptr(s_reduce) if s_reduce is not None else sc
+    if prepare:
+        return Prepared(lib.tp_colrow_mlp_noalloc, (C.byref(args),), keep + [args], [sc, sr],
+                        _tensors(X, A_i, B_i, Z_i, *kw.values()))
+    _check(lib.tp_colrow_mlp_noalloc(C.byref(args), sc, sr))
 
 
 def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None, prepare=False):

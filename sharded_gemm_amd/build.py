@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libtpshard.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "checker.cpp", "api.cpp", "timing.cpp", "shard.hip", "reduce.hip", "gemm.hip"]
+SOURCES = ["plan.cpp", "checker.cpp", "api.cpp", "timing.cpp", "shard.hip", "reduce.hip", "gemm.hip", "noalloc.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

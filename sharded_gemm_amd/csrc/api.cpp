@@ -177,17 +177,21 @@ int reduce_rows(const float *const *parts, int64_t P, int64_t r0, int64_t rows, 
 struct MlpPlan {
   int64_t es = 0, M = 0, H = 0, F = 0, R = 1, C = 1, Mr = 0, Hc = 0;
   bool gather = false, reduce = false;
+  // Y_ws holds one row chunk ([M/R, F]) that every chunk reuses in turn.
+  bool y_chunk = false;
   int epi1 = 0, epi2 = 0;
   SeqSplit sq;
 };
 
-int validate_mlp(const tp_mlp_args *a, MlpPlan *pl) {
+int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   if (!a) return fail(TP_ERR_ARG, "args is NULL");
   const int64_t es = dtype_size(a->dtype);
   if (!es) return fail(TP_ERR_ARG, "unknown dtype %d", a->dtype);
   if (a->act != TP_ACT_NONE && a->act != TP_ACT_GELU_ERF) return fail(TP_ERR_ARG, "unknown act %d", a->act);
   if (a->M < 1 || a->H < 1 || a->F < 1) return fail(TP_ERR_ARG, "M, H, F must be >= 1");
-  if (!a->X || !a->A_i || !a->B_i || !a->Y_ws || !a->Z_i) return fail(TP_ERR_ARG, "X, A_i, B_i, Y_ws and Z_i must be non-NULL");
+  if (!a->X || !a->A_i || !a->B_i || !a->Z_i) return fail(TP_ERR_ARG, "X, A_i, B_i and Z_i must be non-NULL");
+  if (y_chunk && a->Y_ws) return fail(TP_ERR_ARG, "Y_ws must be NULL: this entry point keeps Y in its own scratch");
+  if (!y_chunk && !a->Y_ws) return fail(TP_ERR_ARG, "Y_ws must be non-NULL");
   if (a->row_chunks < 1 || a->col_chunks < 1) return fail(TP_ERR_ARG, "row_chunks and col_chunks must be >= 1");
   if (a->M % a->row_chunks) return fail(TP_ERR_INDIVISIBLE, "row_chunks %lld does not divide M = %lld", (long long)a->row_chunks, (long long)a->M);
   if (a->H % a->col_chunks) return fail(TP_ERR_INDIVISIBLE, "col_chunks %lld does not divide H = %lld", (long long)a->col_chunks, (long long)a->H);
@@ -210,7 +214,10 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl) {
   const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
   const bool gather = a->X_shards != nullptr;
   std::vector<Buf> ins = {{a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
-  std::vector<Buf> outs = {{a->Y_ws, by, "Y_ws"}, {a->Z_i, bz, "Z_i"}};
+  // (The library's own scratch, which replaces Y_ws when y_chunk, is disjoint
+  // from every caller buffer.)
+  std::vector<Buf> outs = {{a->Z_i, bz, "Z_i"}};
+  if (!y_chunk) outs.push_back({a->Y_ws, by, "Y_ws"});
   (gather ? outs : ins).push_back({a->X, bx, "X"});
   if (gather) {
     for (int64_t j = 0; j < sq.S; ++j) {
@@ -247,6 +254,7 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl) {
   pl->Hc = H / pl->C;
   pl->gather = gather;
   pl->reduce = reduce;
+  pl->y_chunk = y_chunk;
   pl->sq = sq;
   pl->epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveBf16 : kEpiGeluBf16) : kEpiIdentBf16)
                   : (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveF32 : kEpiGeluF32) : kEpiPlainF32);
@@ -261,8 +269,10 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl) {
 int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0, hipStream_t s1, bool two,
                   hipEvent_t *ev_blocks, bool last) {
   const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
-  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i,
-              static_cast<char *>(a->Y_ws) + r * Mr * F * es, Mr, F, H, H, F, F};
+  // Chunk r's Y: its own rows of Y_ws, or the one chunk-sized Y_ws, which
+  // chunk r+1's GEMM1 may overwrite once chunk r's GEMM2 (earlier on s0) has read it.
+  char *Yr = static_cast<char *>(a->Y_ws) + (pl.y_chunk ? 0 : r * Mr * F * es);
+  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i, Yr, Mr, F, H, H, F, F};
   if (a->H_out) {
     g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
     g1.ldaux = F;
@@ -274,7 +284,7 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
   std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t c = 0; c < pl.C; ++c) {
     const int64_t zoff = r * Mr * H + c * Hc;
-    GemmArgs g2{static_cast<const char *>(a->Y_ws) + r * Mr * F * es, static_cast<const char *>(a->B_i) + c * Hc * es,
+    GemmArgs g2{Yr, static_cast<const char *>(a->B_i) + c * Hc * es,
                 a->Z_i + zoff, Mr, Hc, F, F, H, H};
     // The block's reduction folds into GEMM2's epilogue where it would run
     // with nothing beside it anyway (the serial schedule and the final block):
@@ -536,9 +546,25 @@ int tp_partial_reduce_ex(const float *const *partials, int64_t P, int64_t rows, 
 
 int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_reduce) {
   clear_error();
+  return colrow_mlp_run(a, s_compute, s_reduce, nullptr);
+}
+
+}  // extern "C"
+
+int tpshard::colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_reduce,
+                            int (*y_scratch)(int64_t bytes, void **out)) {
   MlpPlan pl;
-  int rc = validate_mlp(a, &pl);
+  int rc = validate_mlp(a, &pl, y_scratch != nullptr);
   if (rc != TP_OK) return rc;
+  tp_mlp_args own;
+  if (y_scratch) {
+    // Everything is valid: only now ask for one row chunk's worth of Y.
+    void *y = nullptr;
+    if ((rc = y_scratch(pl.Mr * pl.F * pl.es, &y)) != TP_OK) return rc;
+    own = *a;
+    own.Y_ws = y;
+    a = &own;
+  }
   hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
   const int64_t R = pl.R, C = pl.C, Mr = pl.Mr, H = pl.H, es = pl.es;
   const bool gather = pl.gather;
@@ -587,6 +613,8 @@ int tp_colrow_mlp(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_red
   }
   return TP_OK;
 }
+
+extern "C" {
 
 int tp_colrow_mlp_stack(const tp_mlp_args *layers, int64_t num_layers, tp_stream_t s_compute, tp_stream_t s_reduce) {
   clear_error();

@@ -29,4 +29,13 @@ inline int64_t dtype_size(int32_t dtype) {
 
 constexpr int kMaxRank = 8;
 
+// tp_colrow_mlp's validation and enqueue.  With y_scratch, args->Y_ws must be
+// NULL: once every argument has passed validation, y_scratch is asked for a
+// device buffer of `bytes` (one row chunk of Y, [M/R, F]) that every chunk
+// then reuses in turn (GEMM1 and GEMM2 of every chunk run in order on
+// s_compute, so chunk r+1's GEMM1 only starts after chunk r's GEMM2 has read
+// it); a status other than TP_OK from it is returned as is.
+int colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stream_t s_reduce,
+                   int (*y_scratch)(int64_t bytes, void **out));
+
 }  // namespace tpshard

@@ -505,3 +505,19 @@ def test_binding_checks_sequence_blocks_and_bias():
         bwd(dZ_shards=[x.float() for x in xs])
     with pytest.raises(ValueError):
         bwd(dZ_shards=[torch.zeros((M // S + 1, H), dtype=torch.bfloat16) for _ in range(S)])
+
+
+def test_noalloc_validation():
+    """The allocation-free forward refuses a Y workspace and a row chunk of Y
+    beyond its 32 MiB scratch before it touches the device."""
+    lib = _abi.load()
+    a = _mlp_args()
+    a.Y_ws = FAKE + (3 << 20)
+    assert lib.tp_colrow_mlp_noalloc(C.byref(a), None, None) == _abi.TP_ERR_ARG
+    assert "Y_ws" in lib.tp_last_error().decode()
+    a = _mlp_args(M=4096, F=8192, Y_ws=None)          # one chunk of 64 MiB of bf16
+    assert lib.tp_colrow_mlp_noalloc(C.byref(a), None, None) == _abi.TP_ERR_UNSUPPORTED
+    assert "scratch" in lib.tp_last_error().decode()
+    a = _mlp_args(dtype=9, Y_ws=None)
+    assert lib.tp_colrow_mlp_noalloc(C.byref(a), None, None) == _abi.TP_ERR_ARG
+    assert lib.tp_colrow_mlp_noalloc(None, None, None) == _abi.TP_ERR_ARG

@@ -65,6 +65,17 @@ def log(msg):
 
 # --------------------------------------------------------------------------- workloads
 
+# With --profile the peers' partials are drawn (seeded N(0,1)) instead of
+# computed by the same path, so that a kernel trace of the run holds no GEMM
+# launched outside the timed schedule.  The sums then mean nothing; the timing
+# is the same (the kernels do not look at the values).
+DRAWN_PEERS = False
+
+
+def _peer(w, p, dev="cuda"):
+    return inputs.normal((w.M, w.H), inputs.seed_for(w.cfg, inputs.SLOT_PARTIAL + p), 1.0, "f32", dev)
+
+
 def _device_boxes(shape, spec):
     """{device: box} of a layout, from the library's host-only planner."""
     n, boxes, sod = tp.tp_layout_plan(shape, spec, num_dst=16)
@@ -114,6 +125,9 @@ class MlpStep:
         # peers' partials: computed once, untimed, by the same path
         self.peers = []
         for i in range(1, w.P):
+            if DRAWN_PEERS:
+                self.peers.append(_peer(w, i))
+                continue
             z = torch.empty((w.M, w.H), device=dev)
             tp.tp_colrow_mlp(self.X, self.As[i], self.Bs[i], self.Y, z, row_chunks=w.R, col_chunks=w.C)
             self.peers.append(z)
@@ -269,6 +283,9 @@ class BwdStep:
         # peers' input-gradient partials: their forward and backward, once, untimed, by the same path
         self.peers = []
         for i in range(1, w.P):
+            if DRAWN_PEERS:
+                self.peers.append(_peer(w, i))
+                continue
             tp.tp_colrow_mlp(self.X, self.As[i], self.Bs[i], self.Y, z, row_chunks=w.R, H_out=self.Hs)
             dx = torch.empty((w.M, w.H), device=dev)
             tp.tp_colrow_mlp_backward(self.X, self.As[i], self.Bs[i], self.Hs, self.Y, self.dZ, self.dH, dx,
@@ -375,12 +392,20 @@ class StackStep:
             # peers' partials of this layer's input: computed once, untimed, by the same path
             peers = []
             for i in range(1, w.P):
+                if DRAWN_PEERS:
+                    peers.append(_peer(w, i + 100 * l))
+                    continue
                 z = torch.empty((w.M, w.H), device=dev)
                 tp.tp_colrow_mlp(x, As[i], Bs[i], self.Y, z, row_chunks=w.R)
                 peers.append(z)
             xn = torch.empty((w.M, w.H), dtype=torch.bfloat16, device=dev)
             zo = torch.empty((w.M, w.H), device=dev)
-            tp.tp_colrow_mlp(x, As[0], Bs[0], self.Y, self.Z, row_chunks=w.R, peer_partials=peers, Z_out=zo, X_next=xn)
+            if DRAWN_PEERS:
+                xn.copy_(inputs.normal((w.M, w.H), inputs.seed_for(w.cfg, inputs.SLOT_X) + 7919 * (l + 1), 1.0, "bf16",
+                                       dev))
+            else:
+                tp.tp_colrow_mlp(x, As[0], Bs[0], self.Y, self.Z, row_chunks=w.R, peer_partials=peers, Z_out=zo,
+                                 X_next=xn)
             self.layers.append(dict(X=x, A_i=As[0], B_i=Bs[0], Y_ws=self.Y, Z_i=self.Z, row_chunks=w.R, col_chunks=w.C,
                                     peer_partials=peers, Z_out=zo, X_next=xn))
             x = xn
@@ -554,8 +579,11 @@ def kernel_source_hash():
     files = sorted(glob.glob(os.path.join(ROOT, "sharded_gemm_amd", "csrc", "*.hip")))
     for f in files:
         with open(f, encoding="utf-8") as fh:
-            h.update(os.path.basename(f).encode())
-            h.update(_code_only(fh.read()).encode())
+            code = _code_only(fh.read())
+        if "__global__" not in code:      # no kernel in it (device data only)
+            continue
+        h.update(os.path.basename(f).encode())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 
@@ -714,16 +742,23 @@ def capture(wl):
         return None
 
 
-def measure(wl, steps, warmup, flusher, kernel_tables=True):
+def measure(wl, steps, warmup, flusher, kernel_tables=True, profile=False):
     """Time one workload: K consecutive steps (eager and graph replay; the
     faster gives ms_per_step), per-step times warm and cold in that mode, and
-    the library's per-kernel events, warm and cold (eager launches)."""
+    the library's per-kernel events, warm and cold (eager launches).  With
+    profile, only cold steps run (warm-up included), eagerly: the per-kernel
+    events of the cold steps and their per-step times, so that every kernel
+    launch of the process is one the cold table times."""
     if hasattr(wl, "prepare"):
         wl.prepare()
     dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
     for _ in range(warmup):
+        if profile:
+            flusher(wl.s0)
         wl.step()
     torch.cuda.synchronize()
+    if profile:
+        return measure_profile(wl, steps, flusher, dtype)
     graph = capture(wl)
     s0 = wl.s0
 
@@ -789,6 +824,26 @@ def measure(wl, steps, warmup, flusher, kernel_tables=True):
     return out
 
 
+def measure_profile(wl, steps, flusher, dtype):
+    """Cold eager steps with the library's per-kernel events (--profile)."""
+    tp.tp_timing_enable(True)
+    tp.tp_timing_read()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        flusher(wl.s0)
+        e0.record(wl.s0)
+        wl.step()
+        e1.record(wl.s0)
+    torch.cuda.synchronize()
+    tp.tp_timing_enable(False)
+    table = kernel_table(tp.tp_timing_read(), steps, dtype)
+    cold = spread([e0.elapsed_time(e1) for e0, e1 in evs])
+    return {"ms_per_step": cold["median"], "timed_as": "eager launches, cold, with per-kernel events (profile mode)",
+            "ms_per_step_eager": cold["median"], "ms_per_step_graph": None, "step_ms": {"cold": cold},
+            "dtype": dtype, "kernels_cold": table, "kernels_warm": {}}
+
+
 def rate(wl, ms):
     return wl.work / (ms * 1e-3) / (1e12 if wl.unit == "TFLOP/s" else 1e9)
 
@@ -803,21 +858,22 @@ def run_workload(name, steps, warmup, flusher, args, serial_too=True):
         wl.reduce_fusion = tp.TP_REDUCE_FUSION_OFF
     wl.separate_output = args.separate_output
     log(f"[bench] workload {name}: timing")
-    m = measure(wl, steps, warmup, flusher)
+    m = measure(wl, steps, warmup, flusher, profile=args.profile)
     default_schedule = not (args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output)
     summ = {"config": wl.config(), "value": rate(wl, m["ms_per_step"]), "unit": wl.unit,
             "ms_per_step": m["ms_per_step"], "timed_as": m["timed_as"],
             "ms_per_step_eager": m["ms_per_step_eager"], "ms_per_step_graph": m["ms_per_step_graph"],
             "step_ms": m["step_ms"], "value_cold_median": rate(wl, m["step_ms"]["cold"]["median"]),
+            "peers": "drawn N(0,1) (profile mode)" if DRAWN_PEERS else "computed by the same path",
             "roofline": roofline(m["kernels_cold"], m["dtype"], name, default_schedule),
             "kernels": m["kernels_cold"], "kernels_warm": m["kernels_warm"], "dtype": m["dtype"]}
     for k, v in m["kernels_cold"].items():
         log(f"[bench]   {k:18s} {v['launches_per_step']:.0f}/step  avg {v['avg_ms'] * 1e3:9.1f} us  "
             f"{v['achieved']:9.1f} {v['unit']}  ({100 * v['frac']:.1f}% of {v['peak']:.0f}, cold)")
-    log(f"[bench]   step {m['ms_per_step'] * 1e3:.1f} us ({m['timed_as']}); per step warm median "
-        f"{m['step_ms']['warm']['median'] * 1e3:.1f} us, cold median {m['step_ms']['cold']['median'] * 1e3:.1f} us")
+    log(f"[bench]   step {m['ms_per_step'] * 1e3:.1f} us ({m['timed_as']}); per step cold median "
+        f"{m['step_ms']['cold']['median'] * 1e3:.1f} us")
     two_blocks = isinstance(wl, (MlpStep, BwdStep, StackStep)) and wl.w.R * getattr(wl.w, "C", 1) > 1
-    if serial_too and two_blocks and not args.serial:
+    if serial_too and two_blocks and not args.serial and not args.profile:
         log(f"[bench] workload {name}: serial schedule")
         wl.serial = True
         ms = measure(wl, steps, warmup, flusher, kernel_tables=False)
@@ -867,6 +923,9 @@ def main():
                     help="cap on the reduce kernel's workgroups beside the GEMMs (0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB plain copy (for calibrating traffic counters)")
+    ap.add_argument("--profile", action="store_true",
+                    help="for kernel traces and counters: draw the peers' partials instead of computing them, and "
+                         "run only cold eager steps (warm-up included) with per-kernel events; implies --no-extras")
     ap.add_argument("--no-torch-context", action="store_true",
                     help="skip timing torch.matmul (hipBLASLt) and a torch sum on the headline's shapes")
     args = ap.parse_args()
@@ -883,6 +942,11 @@ def main():
         build.build()
     tp.load()
 
+    if args.profile:
+        global DRAWN_PEERS
+        DRAWN_PEERS = True
+        args.no_extras = True
+        args.no_torch_context = True
     if args.copy_calibration:
         log("[bench] 256 MiB copy for counter calibration")
         copy_calibration()

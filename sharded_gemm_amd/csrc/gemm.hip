@@ -36,15 +36,14 @@
 //  * The MFMA gets W as its first operand and A as its second, so each lane
 //    owns one output row and four adjacent columns: 16-byte (fp32) or 8-byte
 //    (bf16) stores.
-// Ping-pong path (bf16_gemm_pp) for the 256-row tiles: the same tile, DMA and
+// Ping-pong paths (bf16_gemm_pps, and bf16_gemm_pp for 256 x 256 tiles and
+// accumulating 256 x 192 ones) for the 256-row tiles: the same tile, DMA and
 // LDS layout, but the two waves sharing a SIMD run in opposite phases.  The
 // waves of tile rows 0..127 (group A) and of rows 128..255 (group B) sit one
 // barrier apart: between two barriers one group runs its MFMAs while the other
 // reads its next stage from LDS, so the MFMA pipe is fed while LDS reads and
-// their waits happen.  Group A issues all of a stage's DMA.  On MI355X this
-// loop is bound by the LDS read rate (128 bytes per clock per CU; the eight
-// 128 x BN/4 wave blocks read 160-192 KiB of fragments per 64-deep stage)
-// together with the DMA issue, not by the MFMA pipe.
+// their waits happen.  In bf16_gemm_pp group A issues all of a stage's DMA
+// ahead of its reads; bf16_gemm_pps spreads it between both groups' MFMAs.
 // Ragged path (bf16_gemm_ragged): the same MFMA on a 128 x 128 tile with
 // register-staged, bounds-checked loads, for shapes the DMA path cannot take
 // (K not a multiple of 32, N not a multiple of 8, misaligned pointers).
@@ -957,6 +956,194 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
     }
 }
 
+// Ping-pong kernel with split rings (bf16_gemm_pps): the tile, waves,
+// fragment reads and MFMA order of bf16_gemm_pp, with the DMA taken out of the
+// read phases.  With one two-slot ring every DMA of stage s must leave in the
+// one phase that follows the barrier after which both groups are done with
+// stage s-2 and precedes the one after which group A reads stage s-1: the
+// phase in which group A reads LDS.  The issue of a stage's 40-64 DMA
+// instructions (about 15 cycles each through the CU's address unit) then holds
+// up group A's reads while group B waits at the barrier (MI355X phase stamps
+// of bf16_gemm_pp on the 175B GEMM1 shape: about 830 of 2950 cycles per stage).
+// Here the A tile has a ring of three slots and W's tile a ring of two, and
+// each group issues its tile between its own MFMAs:
+//   A: a0 a1 | #0 | R_0 #1 M_0+a2 #2 | R_1 #3 M_1+a3 #4 | ...
+//   B: w0    | #0 | w1 #1 R_0 #2 M_0+w2 #3 R_1 #4 M_1+w3 ...
+// (aS, wS: the A / W tile of stage S; R reads, M multiplies).  Group A's
+// A tile of stage t+2 overwrites stage t-1's slot after #2t+1, group B's W
+// tile of stage t+1 stage t-1's slot after #2t; both groups finished reading
+// stage t-1 by #2t.  Before #2t+2, after which group A reads stage t+1, group
+// A waits for its A tile of stage t+1 (stage t+2's stays in flight) and group
+// B for its W tile of stage t+1.  Every MFMA phase carries its DMA, so the
+// loop has one body and one MFMA chain per group (duplicated chains made the
+// compiler spill): where the stage it would fetch does not exist, it fetches
+// the last stage again, into the slot of the nominal stage, which nothing
+// reads any more.  Same accumulation order as every other kernel, so the
+// results are the same bits.  Measured on MI355X against bf16_gemm_pp: 7-15%
+// faster on every 256 x 192 and 256 x 128 shape here, forward and backward.
+template <int BM, int BN, int EPI, bool AT, bool WT, int WGM = 2>
+__global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
+  constexpr int BK = 64;
+  using C = DmaCfg<BM, BN, BK, 2, AT, WT, WGM, 8 / WGM>;
+  using TA = typename C::TA;
+  using TW = typename C::TW;
+  constexpr int KK = C::KK;
+  constexpr int NG = 4;
+  constexpr int A_PW = TA::PIECES / NG, W_PW = TW::PIECES / NG;
+  constexpr int SA = 3, SW = 2;
+  constexpr int W_BASE = SA * TA::BYTES;
+  static_assert(TA::PIECES % NG == 0 && TW::PIECES % NG == 0, "DMA split");
+  static_assert(SA * TA::BYTES + SW * TW::BYTES <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[SA * TA::BYTES + SW * TW::BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const bool grpA = wave < 4;
+  const int tiles_m = static_cast<int>((p.M + BM - 1) / BM);
+  const int tiles_n = static_cast<int>((p.N + BN - 1) / BN);
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TP_LDS char *)smem));
+  const int64_t ldc = p.ldc;
+  asm volatile("" ::"s"(ldc));
+
+  constexpr int PW = A_PW > W_PW ? A_PW : W_PW;
+  uint32_t src[PW];
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    if (grpA)
+      src[q] = q < A_PW ? static_cast<uint32_t>(TA::src((wave & 3) * A_PW + q, lane, m0, p.M, p.lda) * 2) : 0u;
+    else
+      src[q] = q < W_PW ? static_cast<uint32_t>(TW::src((wave & 3) * W_PW + q, lane, n0, p.N, p.ldw) * 2) : 0u;
+  }
+  const uint32_t step = static_cast<uint32_t>((grpA ? TA::step(p.lda) : TW::step(p.ldw)) * 2);
+  // Piece q of the tile of stage `st` (source) into the slot of stage `slot_st`.
+  auto dma_a = [&](int q, int st, int slot_st) {
+    lds_dma16_s(p.a, src[q] + st * step, lds0 + (slot_st % SA) * TA::BYTES + ((wave & 3) * A_PW + q) * 1024);
+  };
+  auto dma_w = [&](int q, int st, int slot_st) {
+    lds_dma16_s(p.w, src[q] + st * step, lds0 + W_BASE + (slot_st % SW) * TW::BYTES + ((wave & 3) * W_PW + q) * 1024);
+  };
+
+  bf16x8_t fa[KK][C::TM], fb[KK][C::TN];
+  auto read_stage = [&](int st) {
+    const TP_LDS char *a_base = (const TP_LDS char *)smem + (st % SA) * TA::BYTES;
+    const TP_LDS char *w_base = (const TP_LDS char *)smem + W_BASE + (st % SW) * TW::BYTES;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) fa[kk][i] = TA::frag(a_base, wm * C::WM + i * 16, kk, lane);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) fb[kk][j] = TW::frag(w_base, wn * C::WN + j * 16, kk, lane);
+    }
+  };
+  auto coords = [&](int i, int j, int64_t *m, int64_t *n) {
+    *m = m0 + wm * C::WM + i * 16 + (lane & 15);
+    *n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
+  };
+  f32x4_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (EPI == kEpiF32Acc) {
+        int64_t m, n;
+        coords(i, j, &m, &n);
+        if (m < p.M && n < p.N) acc[i][j] = acc_start(p, ldc, m, n, true);
+      }
+    }
+  // The stage's MFMAs with ND DMA pieces of stage `dst` spread between them:
+  // piece q after MFMA number q * NF / ND (ND = 0: none).  Everything is
+  // compile-time, so the chain is one basic block; the scheduling barriers
+  // keep each DMA where it is written.
+  constexpr int NF = KK * C::TN * C::TM;
+  auto mma_stage = [&](auto nd, auto is_a, int dst, int dslot) {
+    constexpr int ND = decltype(nd)::value;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+          if constexpr (ND > 0) {
+            const int f = (kk * C::TN + j) * C::TM + i;
+#pragma unroll
+            for (int q = 0; q < ND; ++q)
+              if (f == q * NF / ND) {
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (decltype(is_a)::value) dma_a(q, dst, dslot); else dma_w(q, dst, dslot);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+          }
+        }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using IA = std::integral_constant<int, A_PW>;
+  using IW = std::integral_constant<int, W_PW>;
+  using T = std::true_type;
+  using F = std::false_type;
+
+  // Every MFMA phase carries its DMA, so the loop has one body: in the last
+  // iterations, where the stage it would fetch does not exist, it fetches the
+  // last stage again into a slot that nothing reads any more (A: the slot of
+  // stage t-1, W: that of stage t-1, both finished by #2t), and the waits
+  // stay as in the steady state.
+  const int nst = static_cast<int>(p.K / BK);
+  const int last = nst - 1;
+  if (nst > 0) {
+    if (grpA) {
+#pragma unroll
+      for (int q = 0; q < A_PW; ++q) dma_a(q, 0, 0);
+#pragma unroll
+      for (int q = 0; q < A_PW; ++q) dma_a(q, min(1, last), 1);
+      wait_vmcnt<A_PW>();
+    } else {
+#pragma unroll
+      for (int q = 0; q < W_PW; ++q) dma_w(q, 0, 0);
+      wait_vmcnt<0>();
+    }
+  }
+  barrier_raw();                                     // #0
+  if (grpA) {
+    for (int t = 0; t < nst; ++t) {
+      read_stage(t);
+      barrier_lgkm0();                               // #2t+1
+      mma_stage(IA{}, T{}, min(t + 2, last), t + 2);   // stage t+2's A tile, slot (t+2) % 3
+      barrier_vm_n<A_PW, 1>(1);                      // #2t+2: stage t+1's A tile landed
+    }
+  } else if (nst > 0) {
+#pragma unroll
+    for (int q = 0; q < W_PW; ++q) dma_w(q, min(1, last), 1);
+    barrier_raw();                                   // #1
+    read_stage(0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // #2
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = 1; t < nst; ++t) {
+      mma_stage(IW{}, F{}, min(t + 1, last), t + 1);   // stage t+1's W tile, slot (t+1) % 2
+      barrier_raw();                                 // #2t+1
+      read_stage(t);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // #2t+2
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mma_stage(I0{}, F{}, 0, 0);
+  }
+  wait_vmcnt<0>();                                   // the repeated fetches of the last stage
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      int64_t m, n;
+      coords(i, j, &m, &n);
+      if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);
+    }
+}
+
 // ---- plain fp32 kernel (tiny fp32 workload) ------------------------------
 // 32 x 32 tile, 256 threads of 2 x 2 outputs, K staged 64 at a time through
 // LDS with the next slab's loads in flight (registers) while the current one
@@ -1091,6 +1278,13 @@ hipError_t launch_pp(const GemmArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int EPI, bool AT, bool WT, int WGM = 2>
+hipError_t launch_pps(const GemmArgs& p, hipStream_t s) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((bf16_gemm_pps<BM, BN, EPI, AT, WT, WGM>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_ragged(const GemmArgs& p, bool vec, hipStream_t s) {
   const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
@@ -1135,9 +1329,16 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   if constexpr (big_ok)
     if (c256 == best) return launch_pp<256, 256, EPI, AT, WT>(p, s);
   if (c192 == best) {
-    // A read transposed (weight gradients): 4 x 2 waves, 2-3% faster.
-    if constexpr (AT) return launch_pp<256, 192, EPI, AT, WT, 64, 2, 4>(p, s);
-    else return launch_pp<256, 192, EPI, AT, WT>(p, s);
+    // A read transposed (weight gradients): 4 x 2 waves, 2-3% faster.  The
+    // accumulating epilogue keeps the single-ring kernel, where the split
+    // rings' extra registers would spill.
+    if constexpr (EPI == kEpiF32Acc) {
+      if constexpr (AT) return launch_pp<256, 192, EPI, AT, WT, 64, 2, 4>(p, s);
+      else return launch_pp<256, 192, EPI, AT, WT>(p, s);
+    } else {
+      if constexpr (AT) return launch_pps<256, 192, EPI, AT, WT, 4>(p, s);
+      else return launch_pps<256, 192, EPI, AT, WT>(p, s);
+    }
   }
   // 256 x 128 tiles: the ping-pong kernel where its 32-bit offsets reach
   // (measured 10-12% faster than the single-group kernel on 4096 x 2048 x 4096).
@@ -1146,8 +1347,8 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   // forward keeps 2 x 4.
   if (c128w == best) {
     if (off32) {
-      if constexpr (AT || WT) return launch_pp<256, 128, EPI, AT, WT, 64, 2, 4>(p, s);
-      else return launch_pp<256, 128, EPI, AT, WT>(p, s);
+      if constexpr (AT || WT) return launch_pps<256, 128, EPI, AT, WT, 4>(p, s);
+      else return launch_pps<256, 128, EPI, AT, WT>(p, s);
     }
     return launch_dma<256, 128, 64, 3, EPI, AT, WT>(p, s);
   }

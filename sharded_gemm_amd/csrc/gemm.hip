@@ -1055,7 +1055,8 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
       }
     }
   // The stage's MFMAs with ND DMA pieces of stage `dst` spread between them:
-  // piece q after MFMA number q * NF / ND (ND = 0: none).  Everything is
+  // piece q after MFMA number (q + 1/2) * NF / ND (ND = 0: none; measured
+  // 1.5-3% faster than starting at the first MFMA).  Everything is
   // compile-time, so the chain is one basic block; the scheduling barriers
   // keep each DMA where it is written.
   constexpr int NF = KK * C::TN * C::TM;
@@ -1072,7 +1073,7 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
             const int f = (kk * C::TN + j) * C::TM + i;
 #pragma unroll
             for (int q = 0; q < ND; ++q)
-              if (f == q * NF / ND) {
+              if (f == q * NF / ND + NF / (2 * ND)) {
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (decltype(is_a)::value) dma_a(q, dst, dslot); else dma_w(q, dst, dslot);
                 __builtin_amdgcn_sched_barrier(0);

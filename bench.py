@@ -526,6 +526,58 @@ class ReshardStep:
                           f"{reps} repetitions"}
 
 
+class ShortRunStep:
+    """Short runs: an fp32 [16777216, 8] tensor (512 MiB) cut into 8 shards on
+    axis 0 (2) and axis 1 (4), so every run is 2 elements (8 bytes), then the
+    shards gathered back into the full tensor.  The pages' axis-1 example at
+    memory-bound size: the split and the gather both go through whole-row
+    blocks with 16-byte accesses."""
+
+    SHAPE = (16777216, 8)
+    SPEC = {"device": list(range(8)), "sharded_dim": [{"axis": 0, "num_shards": 2}, {"axis": 1, "num_shards": 4}]}
+
+    def __init__(self):
+        self.w = None
+        self.src = inputs.normal(self.SHAPE, 7001, device="cuda")
+        self.dst = {d: torch.empty((self.SHAPE[0] // 2, 2), device="cuda") for d in range(8)}
+        self.full = torch.empty(self.SHAPE, device="cuda")
+        torch.cuda.synchronize()
+        self.s0 = torch.cuda.Stream()
+
+    def result(self):
+        return self.full
+
+    def step(self):
+        tp.tp_shard_materialize(self.src, self.SPEC, self.dst, stream=self.s0)
+        tp.tp_shard_gather(self.dst, self.SPEC, [self.full], self.SHAPE, stream=self.s0)
+
+    @property
+    def work(self):
+        return float(4 * self.src.numel() * 4)      # split: read + write; gather: read + write
+
+    unit = "GB/s"
+
+    def config(self):
+        return {"workload": "shortrun-split-gather", "shape": list(self.SHAPE), "dtype": "f32",
+                "sharded_dim": [[0, 2], [1, 4]], "run_bytes": 8, "shards": 8,
+                "step": "split into the 8 shards, then gather them back"}
+
+    def cpu_baseline(self, budget_s):
+        from oracle import layout as L
+        rows = 65536
+        src = self.src[:rows].cpu()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            pieces = L.split(src, self.SPEC)
+            L.gather(pieces, (rows, 8), self.SPEC)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": 4 * rows * 8 * 4 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{rows} of {self.SHAPE[0]} rows split and gathered back; {reps} repetitions"}
+
+
 WORKLOADS = {
     GPT2_SMALL.name: lambda: MlpStep(GPT2_SMALL, split_weights=True),
     GPT3_6P7B.name: lambda: MlpStep(GPT3_6P7B, split_weights=False),
@@ -543,6 +595,7 @@ WORKLOADS = {
     GPT3_6P7B.name + "-2layer": lambda: StackStep(GPT3_6P7B),
     GPT3_175B.name + "-2layer": lambda: StackStep(GPT3_175B),
     GPT3_175B.name + "-sp-bwd": lambda: BwdStep(GPT3_175B, seq=True),
+    "shortrun-split-gather": ShortRunStep,
 }
 
 
@@ -699,7 +752,7 @@ def torch_context(wl, reps=20):
 
 FLUSH_BYTES = 512 << 20
 HEADLINE = GPT3_175B.name
-EXTRAS = (TINY.name, GPT2_SMALL.name, GPT3_6P7B.name, RESHARD.name)
+EXTRAS = (TINY.name, GPT2_SMALL.name, GPT3_6P7B.name, RESHARD.name, "shortrun-split-gather")
 
 
 class Flusher:

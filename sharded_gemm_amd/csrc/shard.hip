@@ -123,6 +123,189 @@ __global__ void __launch_bounds__(kThreads) gather_kernel(GatherArgs a) {
   }
 }
 
+// Short runs.  When the innermost cut axis leaves runs of under 16 bytes, a
+// shard's elements lie a few bytes apart through the whole tensor and the
+// per-shard kernels above read one element per lane from a different row:
+// nothing coalesces, and every shard's workgroups pull the same cache lines.
+// Here the tensor is viewed as rows of n runs of L elements (n shards along
+// the innermost cut axis; the row index runs over every axis before it), and a
+// workgroup takes a block of RB consecutive rows that lie in one box of the
+// outer cut axes, so they are RB consecutive rows of each of the n shards it
+// touches.  The split loads the block with 16-byte loads into LDS and writes
+// each shard's RB x L elements with 16-byte stores assembled from LDS; the
+// gather does the reverse.  Every HBM access is a full 16-byte vector, in
+// order across the lanes.  In LDS each row is padded to an odd number of
+// dwords: the lanes assembling consecutive output vectors read rows a fixed
+// number apart, which with unpadded power-of-two rows would put most of them
+// on a few banks.
+constexpr int kRowsMaxShards = 64;
+constexpr int kRowsLdsBytes = 32 * 1024;
+constexpr int kRowsPer = kRowsLdsBytes / 16 / 256;   // 16-byte vectors per lane per block, at most
+
+struct RowsArgs {
+  int32_t nax;                        // axes before the innermost cut axis
+  int64_t shape[kMaxRank];            // their full extents
+  int64_t ext[kMaxRank];              // their box extents
+  int32_t dweight[kMaxRank];          // weight of each axis's shard digit in the digit index (0: not cut)
+  int32_t sweight;                    // weight of the innermost cut axis's digit
+  int32_t n, L, rb;                   // shards along the innermost cut axis, run length, rows per block
+  int32_t pitch;                      // elements per row in LDS (the row, padded)
+  int64_t rows;                       // rows of the full tensor (a multiple of rb)
+  int32_t slot[kRowsMaxShards];       // digit index -> shard slot, or -1 (not in this call)
+  int32_t dst_begin[kRowsMaxShards + 1];
+  char *dst[kMaxDstPerLaunch];        // split: the devices of slot k at dst_begin[k] ..; gather: the outputs
+  const char *src[kRowsMaxShards];    // gather: slot k's buffer
+  const char *full;                   // split: the full tensor
+  int32_t nout;                       // gather: outputs
+};
+
+// Digit index (shard of the outer cut axes) and local row of full-tensor row r0.
+__device__ __forceinline__ void rows_box(const RowsArgs& a, int64_t r0, int32_t *dig, int64_t *lr) {
+  int64_t rem = r0, l = 0, lstride = 1;
+  int32_t d = 0;
+  for (int i = a.nax - 1; i >= 0; --i) {
+    const int64_t c = rem % a.shape[i];
+    rem /= a.shape[i];
+    d += static_cast<int32_t>(c / a.ext[i]) * a.dweight[i];
+    l += (c % a.ext[i]) * lstride;
+    lstride *= a.ext[i];
+  }
+  *dig = d;
+  *lr = l;
+}
+
+template <int ES>
+struct ElemOf;
+template <> struct ElemOf<2> { typedef uint16_t T; };
+template <> struct ElemOf<4> { typedef uint32_t T; };
+
+// Lane-side index walks: one division per 16-byte vector, then the next
+// element's row and column by increment.
+template <int ES, bool NT>
+__global__ void __launch_bounds__(kThreads) rows_split_kernel(RowsArgs a) {
+  typedef typename ElemOf<ES>::T E;
+  constexpr int EPV = 16 / ES;                       // elements per 16-byte vector
+  static_assert(kThreads == 256, "kRowsPer assumes 256 lanes");
+  __shared__ __attribute__((aligned(16))) E lds[kRowsLdsBytes / ES];
+  const int wrow = a.n * a.L;
+  const int blk_vec = a.rb * wrow * ES / 16;         // <= kRowsPer * kThreads (host: rb * pitch * ES <= LDS)
+  const int shard_vec = a.rb * a.L * ES / 16;        // output vectors per shard per block
+  const int64_t nblk = a.rows / a.rb;
+  u32x4_t buf[kRowsPer];
+  // The block's rows, 16-byte loads in order; the next block's are in flight
+  // while this one is written out.
+  auto load = [&](int64_t b) {
+    const u32x4_t *in = reinterpret_cast<const u32x4_t *>(a.full + b * a.rb * wrow * ES);
+#pragma unroll
+    for (int q = 0; q < kRowsPer; ++q) {
+      const int i = threadIdx.x + q * kThreads;
+      if (i < blk_vec) buf[q] = __builtin_nontemporal_load(in + i);
+    }
+  };
+  int64_t b = blockIdx.x;
+  if (b < nblk) load(b);
+  for (; b < nblk; b += gridDim.x) {
+#pragma unroll
+    for (int q = 0; q < kRowsPer; ++q) {
+      const int i = threadIdx.x + q * kThreads;
+      if (i >= blk_vec) break;
+      const E *e = reinterpret_cast<const E *>(&buf[q]);
+      int r = i * EPV / wrow, j = i * EPV - r * wrow;
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) {
+        lds[r * a.pitch + j] = e[t];
+        if (++j == wrow) { j = 0; ++r; }
+      }
+    }
+    int32_t dig;
+    int64_t lr;
+    rows_box(a, b * a.rb, &dig, &lr);
+    __syncthreads();
+    if (b + gridDim.x < nblk) load(b + gridDim.x);
+    for (int u = threadIdx.x; u < a.n * shard_vec; u += kThreads) {
+      const int s = u / shard_vec, v = u - s * shard_vec;
+      const int k = a.slot[dig + s * a.sweight];
+      if (k < 0) continue;
+      E e[EPV];
+      int r = v * EPV / a.L, c = v * EPV - r * a.L;
+      const int base = s * a.L;
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) {
+        e[t] = lds[r * a.pitch + base + c];
+        if (++c == a.L) { c = 0; ++r; }
+      }
+      const u32x4_t vec = __builtin_bit_cast(u32x4_t, e);
+      const int64_t off = lr * a.L * ES + static_cast<int64_t>(v) * 16;
+      for (int d = a.dst_begin[k]; d < a.dst_begin[k + 1]; ++d) store_vec<16, NT>(vec, a.dst[d] + off);
+    }
+    __syncthreads();
+  }
+}
+
+template <int ES, bool NT>
+__global__ void __launch_bounds__(kThreads) rows_gather_kernel(RowsArgs a) {
+  typedef typename ElemOf<ES>::T E;
+  constexpr int EPV = 16 / ES;
+  __shared__ __attribute__((aligned(16))) E lds[kRowsLdsBytes / ES];
+  const int wrow = a.n * a.L;
+  const int blk_vec = a.rb * wrow * ES / 16;
+  const int shard_vec = a.rb * a.L * ES / 16;
+  const int nvec = a.n * shard_vec;                  // = blk_vec
+  const int64_t nblk = a.rows / a.rb;
+  u32x4_t buf[kRowsPer];
+  // Each shard's run of the block, 16-byte loads in order; the next block's
+  // are in flight while this one is written out.
+  auto load = [&](int64_t b) {
+    int32_t dig;
+    int64_t lr;
+    rows_box(a, b * a.rb, &dig, &lr);
+#pragma unroll
+    for (int q = 0; q < kRowsPer; ++q) {
+      const int u = threadIdx.x + q * kThreads;
+      if (u < nvec) {
+        const int s = u / shard_vec, v = u - s * shard_vec;
+        const int k = a.slot[dig + s * a.sweight];
+        buf[q] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t *>(a.src[k] + lr * a.L * ES + static_cast<int64_t>(v) * 16));
+      }
+    }
+  };
+  int64_t b = blockIdx.x;
+  if (b < nblk) load(b);
+  for (; b < nblk; b += gridDim.x) {
+#pragma unroll
+    for (int q = 0; q < kRowsPer; ++q) {
+      const int u = threadIdx.x + q * kThreads;
+      if (u >= nvec) break;
+      const int s = u / shard_vec, v = u - s * shard_vec;
+      const E *e = reinterpret_cast<const E *>(&buf[q]);
+      int r = v * EPV / a.L, c = v * EPV - r * a.L;
+      const int base = s * a.L;
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) {
+        lds[r * a.pitch + base + c] = e[t];
+        if (++c == a.L) { c = 0; ++r; }
+      }
+    }
+    __syncthreads();
+    const int64_t r0 = b * a.rb;
+    if (b + gridDim.x < nblk) load(b + gridDim.x);
+    for (int i = threadIdx.x; i < blk_vec; i += kThreads) {
+      E e[EPV];
+      int r = i * EPV / wrow, j = i * EPV - r * wrow;
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) {
+        e[t] = lds[r * a.pitch + j];
+        if (++j == wrow) { j = 0; ++r; }
+      }
+      const u32x4_t vec = __builtin_bit_cast(u32x4_t, e);
+      for (int d = 0; d < a.nout; ++d)
+        store_vec<16, NT>(vec, a.dst[d] + r0 * wrow * ES + static_cast<int64_t>(i) * 16);
+    }
+    __syncthreads();
+  }
+}
+
 // Run/stride decomposition of a plan's (common) shard box.
 struct Geometry {
   int64_t shard_elems = 1;
@@ -220,6 +403,109 @@ dim3 copy_grid(uint32_t total_v, int nshards) {
   return dim3(static_cast<unsigned>(std::min(want, cap)), static_cast<unsigned>(nshards));
 }
 
+// The row-block geometry of a plan whose innermost cut leaves runs of under
+// 16 bytes, or false when the short-run kernels do not apply (long runs; an
+// element size other than 2 or 4; more than kRowsMaxShards shard positions;
+// no block of at least 8 rows that stays inside one box and fits the LDS).
+bool rows_plan(const ShardPlan& plan, int64_t esize, RowsArgs *a) {
+  if (esize != 2 && esize != 4) return false;
+  const int r = plan.ndim;
+  int jstar = -1;
+  for (int i = 0; i < r; ++i)
+    if (plan.extent[i] < plan.shape[i]) jstar = i;
+  if (jstar < 1) return false;
+  int64_t L = plan.extent[jstar];
+  for (int i = jstar + 1; i < r; ++i) L *= plan.shape[i];
+  if (L * esize >= 16) return false;
+  const int64_t n = plan.shape[jstar] / plan.extent[jstar];
+  // Digit index: the shard digits of the cut axes, row-major, the innermost cut axis last.
+  int64_t combos = n, rows = 1;
+  a->sweight = 1;
+  for (int i = jstar - 1; i >= 0; --i) {
+    const int64_t ni = plan.shape[i] / plan.extent[i];
+    a->dweight[i] = ni > 1 ? static_cast<int32_t>(combos) : 0;
+    if (ni > 1) combos *= ni;
+    rows *= plan.shape[i];
+    if (combos > kRowsMaxShards) return false;
+  }
+  if (combos > kRowsMaxShards || plan.nshards() > kRowsMaxShards) return false;
+  // Consecutive rows that stay in one box: the innermost outer cut axis's box
+  // extent times the axes inside it, or every row when no outer axis is cut.
+  int64_t G = rows;
+  for (int i = jstar - 1; i >= 0; --i)
+    if (plan.extent[i] < plan.shape[i]) {
+      G = plan.extent[i];
+      for (int q = i + 1; q < jstar; ++q) G *= plan.shape[q];
+      break;
+    }
+  // LDS row: the row padded to an odd number of dwords (an even number of
+  // elements for 2-byte ones, so that rows stay dword-aligned).
+  int64_t pitch = n * L;
+  while ((pitch * esize) % 4 != 0 || ((pitch * esize) / 4) % 2 == 0) ++pitch;
+  int64_t rb = 1;
+  while (rb * 2 <= G && G % (rb * 2) == 0 && rb * 2 * pitch * esize <= kRowsLdsBytes) rb *= 2;
+  if (rb < 8) return false;
+  a->nax = jstar;
+  for (int i = 0; i < jstar; ++i) {
+    a->shape[i] = plan.shape[i];
+    a->ext[i] = plan.extent[i];
+  }
+  a->n = static_cast<int32_t>(n);
+  a->L = static_cast<int32_t>(L);
+  a->rb = static_cast<int32_t>(rb);
+  a->pitch = static_cast<int32_t>(pitch);
+  a->rows = rows;
+  for (int q = 0; q < kRowsMaxShards; ++q) a->slot[q] = -1;
+  for (int64_t k = 0; k < plan.nshards(); ++k) {
+    int32_t idx = static_cast<int32_t>(plan.offset[k * r + jstar] / plan.extent[jstar]) * a->sweight;
+    for (int i = 0; i < jstar; ++i) idx += static_cast<int32_t>(plan.offset[k * r + i] / plan.extent[i]) * a->dweight[i];
+    a->slot[idx] = static_cast<int32_t>(k);
+  }
+  return true;
+}
+
+bool aligned16p(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+unsigned rows_grid(const RowsArgs& a) {
+  return static_cast<unsigned>(std::min<int64_t>(a.rows / a.rb, 4096));
+}
+
+// The short-run split of one tensor, or 1 when it does not apply (the caller
+// then uses the per-shard kernel).
+int rows_split(const MatJob& jb, hipStream_t stream) {
+  RowsArgs a{};
+  if (!rows_plan(*jb.plan, jb.esize, &a) || !aligned16p(jb.src)) return 1;
+  int nd = 0;
+  a.dst_begin[0] = 0;
+  int64_t ndev = 0;
+  for (int64_t k = 0; k < jb.plan->nshards(); ++k) {
+    const auto& grp = jb.plan->devices[k];
+    if (nd + static_cast<int>(grp.size()) > kMaxDstPerLaunch) return 1;
+    for (int64_t d : grp) {
+      if (!aligned16p(jb.dst[d])) return 1;
+      a.dst[nd++] = static_cast<char *>(jb.dst[d]);
+    }
+    a.dst_begin[k + 1] = nd;
+    ndev += static_cast<int64_t>(grp.size());
+  }
+  a.full = static_cast<const char *>(jb.src);
+  // Algorithmic bytes: the full tensor read once (every element of it belongs
+  // to some shard), each device's shard written once.
+  const int64_t elems = a.rows * a.n * a.L;
+  int64_t per_shard = 1;
+  for (int i = 0; i < jb.plan->ndim; ++i) per_shard *= jb.plan->extent[i];
+  const double bytes = static_cast<double>(elems) * jb.esize + static_cast<double>(ndev) * per_shard * jb.esize;
+  const bool nt = static_cast<double>(ndev) * per_shard * jb.esize > static_cast<double>(kCachedCopyBytes);
+  hipEvent_t t0 = timing_begin(stream);
+  const dim3 grid(rows_grid(a));
+  if (jb.esize == 4) launch_vb(rows_split_kernel<4, true>, rows_split_kernel<4, false>, nt, grid, stream, a);
+  else launch_vb(rows_split_kernel<2, true>, rows_split_kernel<2, false>, nt, grid, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "materialize launch: %s", hipGetErrorString(e));
+  timing_end(t0, stream, TP_KERNEL_MATERIALIZE, bytes);
+  return TP_OK;
+}
+
 }  // namespace
 
 int shard_materialize_batch_launch(const MatJob *jobs, int njobs, hipStream_t stream) {
@@ -231,6 +517,10 @@ int shard_materialize_batch_launch(const MatJob *jobs, int njobs, hipStream_t st
     const MatJob& jb = jobs[j];
     geo.push_back(geometry(*jb.plan));
     if (geo.back().shard_elems == 0 || jb.plan->nshards() == 0) continue;
+    // Short runs: the row-block kernel, a launch of its own.
+    const int rc = rows_split(jb, stream);
+    if (rc == TP_OK) continue;
+    if (rc < 0) return rc;
     std::vector<const void *> pieces;
     for (const auto& grp : jb.plan->devices)
       for (int64_t d : grp) pieces.push_back(jb.dst[d]);
@@ -314,6 +604,40 @@ int shard_gather_launch(const ShardPlan& plan, const void *const *src, int64_t e
                         hipStream_t stream) {
   const Geometry g = geometry(plan);
   if (g.shard_elems == 0 || plan.nshards() == 0 || nout == 0) return TP_OK;
+  // Short runs: the row-block kernel (every shard position present, every
+  // pointer 16-byte aligned, the outputs in one launch).
+  {
+    RowsArgs a{};
+    bool ok = nout <= kMaxDstPerLaunch && rows_plan(plan, esize, &a);
+    if (ok) {
+      // The gather reads every shard position.
+      int64_t combos = a.n;
+      for (int i = 0; i < a.nax; ++i)
+        if (a.dweight[i]) combos *= plan.shape[i] / plan.extent[i];
+      ok = combos == plan.nshards();
+    }
+    for (int64_t k = 0; ok && k < plan.nshards(); ++k) {
+      a.src[k] = static_cast<const char *>(src[plan.devices[k][0]]);
+      ok = aligned16p(a.src[k]);
+    }
+    for (int64_t j = 0; ok && j < nout; ++j) {
+      a.dst[j] = static_cast<char *>(out[j]);
+      ok = aligned16p(out[j]);
+    }
+    if (ok) {
+      a.nout = static_cast<int32_t>(nout);
+      const double full_bytes = static_cast<double>(a.rows) * a.n * a.L * esize;
+      const bool nt = nout * full_bytes > static_cast<double>(kCachedCopyBytes);
+      hipEvent_t t0 = timing_begin(stream);
+      const dim3 grid(rows_grid(a));
+      if (esize == 4) launch_vb(rows_gather_kernel<4, true>, rows_gather_kernel<4, false>, nt, grid, stream, a);
+      else launch_vb(rows_gather_kernel<2, true>, rows_gather_kernel<2, false>, nt, grid, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return fail(TP_ERR_HIP, "gather launch: %s", hipGetErrorString(e));
+      timing_end(t0, stream, TP_KERNEL_GATHER, (1.0 + nout) * full_bytes);
+      return TP_OK;
+    }
+  }
   std::vector<const void *> pieces;
   for (const auto& grp : plan.devices) pieces.push_back(src[grp[0]]);
   for (int64_t j = 1; j < nout; ++j) pieces.push_back(out[j]);

@@ -76,5 +76,6 @@ def test_spread_reports_median_and_percentiles():
 
 def test_default_workload_is_the_largest_single_gpu_configuration():
     assert bench.HEADLINE == "gpt3-175b-tp8-2d-r2c2"
-    assert set(bench.EXTRAS) == {"tiny-fp32-p2", "gpt2-small-tp4", "gpt3-6.7b-tp8-rowsplit2", "reshard-2x4-mesh"}
+    assert set(bench.EXTRAS) == {"tiny-fp32-p2", "gpt2-small-tp4", "gpt3-6.7b-tp8-rowsplit2", "reshard-2x4-mesh",
+                                 "shortrun-split-gather"}
     assert bench.FLUSH_BYTES >= 512 << 20

@@ -95,6 +95,11 @@ class MlpStep:
     # torch.distributed.all_reduce does; separate_output keeps Z_i and writes
     # the sum to its own buffer instead.
     separate_output = False
+    # With full weights: rank 0 reads its column shard of A in place (a row
+    # stride of P*F) and its row shard of B (contiguous rows), as the
+    # column-parallel layer uses its shard; cut_weights copies both out of the
+    # full weights at every step instead (one batched layout launch).
+    cut_weights = False
 
     def __init__(self, w, split_weights: bool, seq: bool = False):
         self.w = w
@@ -159,13 +164,16 @@ class MlpStep:
         self.cut_layouts = None
         if self.layouts:
             self.cut_layouts = tp.tp_shard_materialize_batch(self.layouts, stream=self.s0, prepare=True)
-        if self.split:
+        A0, B0 = self.As[0], self.Bs[0]
+        if self.split and self.cut_weights:
             # rank 0's column shard of A and row shard of B in one batched call
             # (one launch): each rank materialises its own share
             self.cut = tp.tp_shard_materialize_batch([(self.A, self.sa, {0: self.As[0]}, 0),
                                                       (self.B, self.sb, {0: self.Bs[0]}, 0)],
                                                      stream=self.s0, prepare=True)
-        self.mlp = tp.tp_colrow_mlp(self.X, self.As[0], self.Bs[0], self.Y, self.Z, row_chunks=self.w.R,
+        elif self.split:
+            A0, B0 = self.A[:, :self.w.F], self.B[:self.w.F]
+        self.mlp = tp.tp_colrow_mlp(self.X, A0, B0, self.Y, self.Z, row_chunks=self.w.R,
                                     col_chunks=self.w.C, peer_partials=self.peers,
                                     Z_out=None if self.seq else self._z_out(), s_compute=self.s0,
                                     s_reduce=self.s0 if self.serial else self.s1,
@@ -190,7 +198,9 @@ class MlpStep:
         w = self.w
         cfg = {"workload": w.name + ("-sp" if self.seq else ""), "tokens": w.M, "hidden": w.H, "ffn_per_rank": w.F,
                "tp": w.P, "row_chunks": w.R, "col_chunks": w.C,
-               "weights_cut_each_step": "rank 0's shards of A and B" if self.split else False,
+               "weights": (("rank 0's shards of A and B copied out of the full weights each step" if self.cut_weights
+                            else "rank 0's shards read in place: A's column slice with a row stride of P*F, B's row "
+                                 "slice") if self.split else "per-rank shards drawn as such"),
                "reduce_stream": "compute" if self.serial else "second",
                "reduce_fusion": "auto" if self.reduce_fusion == tp.TP_REDUCE_FUSION_AUTO else "off",
                "reduce_output": ("reduce-scattered blocks" if self.seq else
@@ -225,7 +235,7 @@ class MlpStep:
             if self.layouts:
                 for src, spec, _ in self.layouts:
                     L.split(src.cpu(), spec)
-            if self.split:
+            if self.split and self.cut_weights:
                 L.split(Ac, self.sa)
                 L.split(Bc, self.sb)
             if self.seq:
@@ -243,7 +253,7 @@ class MlpStep:
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
         return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                 "sample": (f"{rows} of {w.M} token rows of the per-rank MLP (fp64, numpy's BLAS), "
-                           f"{'plus cutting the full weights into the shards of every rank (the oracle has no one-device form), ' if self.split else ''}"
+                           f"{'plus cutting the full weights into the shards of every rank (the oracle has no one-device form), ' if self.split and self.cut_weights else ''}"
                            f"{'plus the all-gather of those rows from P blocks, ' if self.seq else ''}"
                            f"plus the {w.P}-way partial sum of those rows; {reps} repetitions, "
                            f"{dt * 1e3:.1f} ms each; host {platform.processor() or platform.machine()}, "
@@ -910,6 +920,7 @@ def run_workload(name, steps, warmup, flusher, args, serial_too=True):
     if args.no_reduce_fusion:
         wl.reduce_fusion = tp.TP_REDUCE_FUSION_OFF
     wl.separate_output = args.separate_output
+    wl.cut_weights = args.cut_weights
     log(f"[bench] workload {name}: timing")
     m = measure(wl, steps, warmup, flusher, profile=args.profile)
     default_schedule = not (args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output)
@@ -970,6 +981,9 @@ def main():
     ap.add_argument("--serial", action="store_true", help="run the reduce on the compute stream")
     ap.add_argument("--separate-output", action="store_true",
                     help="write the reduced output to its own buffer instead of in place over the partial")
+    ap.add_argument("--cut-weights", action="store_true",
+                    help="copy rank 0's weight shards out of the full weights each step (workloads with full weights) "
+                         "instead of reading them in place")
     ap.add_argument("--no-reduce-fusion", action="store_true",
                     help="always run the forward's reduction as its own kernel, never in GEMM2's epilogue")
     ap.add_argument("--reduce-wgs", type=int, default=0,

@@ -343,6 +343,11 @@ typedef struct {
                         of 128 x 128; otherwise,
                         and always with TP_REDUCE_FUSION_OFF (1), a separate
                         reduction kernel runs.  Both give the same bits. */
+  int64_t A_ld;      /* row stride of A_i in elements; 0 = F (contiguous).  With
+                        A_ld = P*F, A_i may point into the full A [H, P*F] at column
+                        i*F: the rank consumes its column shard in place, as the
+                        column-parallel layer uses its weight shard ([CAI] section 5.1),
+                        with no copy.  Must be >= F. */
 } tp_mlp_args;
 
 enum { TP_REDUCE_FUSION_AUTO = 0, TP_REDUCE_FUSION_OFF = 1 };

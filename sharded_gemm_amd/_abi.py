@@ -91,7 +91,7 @@ class tp_mlp_args(C.Structure):
                 ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
                 ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p), ("bias", C.c_void_p),
                 ("seq_splits", C.c_int64), ("X_shards", C.POINTER(C.c_void_p)), ("Z_split", C.POINTER(C.c_void_p)),
-                ("X_next", C.c_void_p), ("reduce_fusion", C.c_int32)]
+                ("X_next", C.c_void_p), ("reduce_fusion", C.c_int32), ("A_ld", C.c_int64)]
 
 
 class tp_mlp_bwd_args(C.Structure):
@@ -497,6 +497,13 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
     M, H = int(X.shape[0]), int(X.shape[1])
     F = int(A_i.shape[1])
     peers = list(peer_partials)
+    # A_i may be a column slice of the full A (rows contiguous, a row stride of
+    # at least F): it is then read in place.
+    A_ld = 0
+    if not A_i.is_contiguous():
+        if A_i.dim() != 2 or A_i.stride(1) != 1 or A_i.stride(0) < F:
+            raise ValueError("A_i must be contiguous or a column slice (unit column stride, row stride >= F)")
+        A_ld = int(A_i.stride(0))
     if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Z_i.shape) != (M, H) \
             or (Y_ws is not None and tuple(Y_ws.shape) != (M, F)):
         raise ValueError("shapes must be X[M,H], A_i[H,F], B_i[F,H], Y_ws[M,F], Z_i[M,H]")
@@ -517,11 +524,11 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
     S, xs, zs = _seq_arrays(X_shards, Z_split, M, H, X.dtype, "X_shards", "Z_split")
     parr = (C.c_void_p * max(1, len(peers)))(*[_ptr(p) for p in peers])
     args = tp_mlp_args(dtype=_dtype_code(X), act=act, M=M, H=H, F=F,
-                       X=_ptr(X), A_i=_ptr(A_i), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
+                       X=_ptr(X), A_i=A_i.data_ptr(), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
                        Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias),
-                       X_next=_ptr(X_next), reduce_fusion=reduce_fusion)
+                       X_next=_ptr(X_next), reduce_fusion=reduce_fusion, A_ld=A_ld)
     args.seq_splits, args.X_shards, args.Z_split = S, xs, zs
     return args, [parr, xs, zs]
 

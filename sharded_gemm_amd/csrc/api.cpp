@@ -211,7 +211,10 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
       (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
     return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
-  const int64_t bx = M * H * es, ba = H * F * es, bb = F * H * es, by = M * F * es, bz = M * H * 4;
+  if (a->A_ld != 0 && a->A_ld < F) return fail(TP_ERR_ARG, "A_ld = %lld < F = %lld", (long long)a->A_ld, (long long)F);
+  const int64_t lda_w = a->A_ld ? a->A_ld : F;
+  if (lda_w >= (int64_t(1) << 31)) return fail(TP_ERR_UNSUPPORTED, "A_ld exceeds the 32-bit index range of the kernels");
+  const int64_t bx = M * H * es, ba = matrix_bytes(H, F, lda_w, es), bb = F * H * es, by = M * F * es, bz = M * H * 4;
   const bool gather = a->X_shards != nullptr;
   std::vector<Buf> ins = {{a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
   // (The library's own scratch, which replaces Y_ws when y_chunk, is disjoint
@@ -272,7 +275,7 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
   // Chunk r's Y: its own rows of Y_ws, or the one chunk-sized Y_ws, which
   // chunk r+1's GEMM1 may overwrite once chunk r's GEMM2 (earlier on s0) has read it.
   char *Yr = static_cast<char *>(a->Y_ws) + (pl.y_chunk ? 0 : r * Mr * F * es);
-  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i, Yr, Mr, F, H, H, F, F};
+  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i, Yr, Mr, F, H, H, a->A_ld ? a->A_ld : F, F};
   if (a->H_out) {
     g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
     g1.ldaux = F;

@@ -521,3 +521,17 @@ def test_noalloc_validation():
     a = _mlp_args(dtype=9, Y_ws=None)
     assert lib.tp_colrow_mlp_noalloc(C.byref(a), None, None) == _abi.TP_ERR_ARG
     assert lib.tp_colrow_mlp_noalloc(None, None, None) == _abi.TP_ERR_ARG
+
+
+def test_column_slice_validation():
+    """A_ld below F is refused; a column slice's strided extent counts in the overlap checks."""
+    lib = _abi.load()
+    a = _mlp_args(A_ld=32)                         # F = 64
+    assert lib.tp_colrow_mlp(C.byref(a), None, None) == _abi.TP_ERR_ARG
+    # A_i rows 256 elements apart: its last row reaches past Y_ws's start
+    a = _mlp_args(A_ld=256 * 64, Y_ws=FAKE + (1 << 20) + 63 * 256 * 64 * 2 + 16)
+    assert lib.tp_colrow_mlp(C.byref(a), None, None) == _abi.TP_ERR_ARG
+    with pytest.raises(ValueError):
+        tp.tp_colrow_mlp(torch.zeros((64, 64), dtype=torch.bfloat16), torch.zeros((64, 128), dtype=torch.bfloat16)[:, ::2],
+                         torch.zeros((64, 64), dtype=torch.bfloat16), torch.zeros((64, 64), dtype=torch.bfloat16),
+                         torch.zeros((64, 64)))

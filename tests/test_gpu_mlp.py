@@ -527,3 +527,30 @@ def test_prepared_call_matches_direct_call():
     Zo.set_(torch.empty_like(Zo))
     with pytest.raises(tp.TpError, match="moved"):
         call()
+
+
+@pytest.mark.parametrize("Rc,Cc,P,fusion", [(1, 1, 4, tp.TP_REDUCE_FUSION_AUTO), (2, 2, 3, tp.TP_REDUCE_FUSION_AUTO),
+                                            (1, 1, 4, tp.TP_REDUCE_FUSION_OFF), (2, 1, 8, tp.TP_REDUCE_FUSION_AUTO)])
+def test_column_shard_read_in_place(Rc, Cc, P, fusion):
+    """A_i as a column slice of the full A (row stride P*F, A_ld) gives the bits
+    of the copied shard, for the GPT-2 shape's small tiles and a ping-pong tile."""
+    for M, H, F, dt in ((4096, 768, 768, "bf16"), (2048, 512, 2048, "bf16"), (64, 256, 512, "f32")):
+        announce(f"mlp column shard in place M={M} H={H} F={F} {dt} R={Rc} C={Cc} P={P} fusion={fusion}")
+        X = inputs.normal((M, H), 4501, 1.0, dt).cuda()
+        A = inputs.normal((H, P * F), 4502, 0.02, dt).cuda()
+        B = inputs.normal((P * F, H), 4503, 0.02, dt).cuda()
+        peers = [inputs.normal((M, H), 4510 + p).cuda() for p in range(P - 1)]
+        i = P - 1                                   # the last rank's shard: offset and stride both matter
+        outs = []
+        for A_i, B_i in ((A[:, i * F:(i + 1) * F].contiguous(), B[i * F:(i + 1) * F].contiguous()),
+                         (A[:, i * F:(i + 1) * F], B[i * F:(i + 1) * F])):
+            Y = Guarded((M, F), X.dtype)
+            Z = Guarded((M, H), torch.float32)
+            Zo = Guarded((M, H), torch.float32)
+            tp.tp_colrow_mlp(X, A_i, B_i, Y.t, Z.t, row_chunks=Rc, col_chunks=Cc, peer_partials=peers, Z_out=Zo.t,
+                             reduce_fusion=fusion, s_reduce=torch.cuda.Stream())
+            torch.cuda.synchronize()
+            assert Y.guards_intact() and Z.guards_intact() and Zo.guards_intact()
+            outs.append([bits(g.t.cpu()) for g in (Y, Z, Zo)])
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b)

@@ -492,10 +492,13 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *args, tp_stream_t s_compute, t
  * reduction folded into its epilogue and the dX GEMM with the input gradient's
  * reduction folded into its epilogue (both memory-bound: their work counts
  * bytes, the operands and the peers' partials read once and each output
- * written once). */
+ * written once).  TP_KERNEL_REDUCE_TAIL is the forward's last-block reduction
+ * on a chunked two-stream schedule, which no GEMM runs beside (a one-shot
+ * grid over the whole chip); every other reduction is TP_KERNEL_REDUCE. */
 enum { TP_KERNEL_MATERIALIZE = 0, TP_KERNEL_GEMM1 = 1, TP_KERNEL_GEMM2 = 2, TP_KERNEL_REDUCE = 3,
        TP_KERNEL_GEMM_DGRAD = 4, TP_KERNEL_GEMM_WGRAD = 5, TP_KERNEL_GATHER = 6,
-       TP_KERNEL_GEMM2_REDUCE = 7, TP_KERNEL_GEMM_DGRAD_REDUCE = 8, TP_KERNEL_KINDS = 9 };
+       TP_KERNEL_GEMM2_REDUCE = 7, TP_KERNEL_GEMM_DGRAD_REDUCE = 8, TP_KERNEL_REDUCE_TAIL = 9,
+       TP_KERNEL_KINDS = 10 };
 
 typedef struct {
   int64_t launches;  /* kernel launches timed since the last read */

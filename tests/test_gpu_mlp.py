@@ -487,6 +487,33 @@ def test_fusion_taken_where_the_rule_says(M, H, F, P, fused):
     assert st["reduce"]["launches"] == (1 if (P > 1 and not fused) else 0)
 
 
+@pytest.mark.parametrize("two_streams", [True, False])
+def test_timing_files_the_tail_reduction_apart(two_streams):
+    """On a chunked two-stream schedule the last block's reduction, which no
+    GEMM runs beside, is timed as reduce_tail and the earlier blocks' as
+    reduce; on one stream every block's reduction is reduce."""
+    announce(f"mlp timing of the tail reduction two_streams={two_streams}")
+    M, H, F, P, Rc = 512, 384, 256, 8, 2
+    X = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((H, F), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((F, H), dtype=torch.bfloat16, device="cuda")
+    peers = [torch.zeros((M, H), device="cuda") for _ in range(P - 1)]
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty((M, H), device="cuda")
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream() if two_streams else s0
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        tp.tp_colrow_mlp(X, A, B, Y, Z, row_chunks=Rc, peer_partials=peers, Z_out=Z, s_compute=s0, s_reduce=s1)
+        st = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    assert st["reduce"]["launches"] == (Rc - 1 if two_streams else Rc)
+    assert st["reduce_tail"]["launches"] == (1 if two_streams else 0)
+    assert st["reduce_tail"]["work"] == (4.0 * (P + 1) * (M // Rc) * H if two_streams else 0.0)
+
+
 def test_max_ranks_integer_exact():
     """P = 64 virtual ranks (63 peers), chunked, on two streams: exact."""
     announce("mlp P=64 integer exact")

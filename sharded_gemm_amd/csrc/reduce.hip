@@ -5,10 +5,19 @@
 // layer's bias acts on the full output, so it is added once after the sum;
 // sections 3 and 5.3: the reduce-scatter form leaves rank j with row block j).
 //
-// Pure HBM streaming: each lane owns UNROLL output vectors, issues the loads
-// of every partial for all of them before it adds anything (P x UNROLL loads
-// in flight per lane), then adds in ascending p and stores.  Inputs are read
-// once and outputs written once, so both bypass cache retention (non-temporal).
+// Pure HBM streaming, inputs read once and outputs written once, both
+// bypassing cache retention (non-temporal), in one of two forms:
+//  * alone on the chip (a one-shot grid) over whole rows: each lane owns four
+//    output vectors, 256 lanes apart, and walks the partials in ascending p
+//    one 16-byte load at a time, each waited for before the next is issued,
+//    so a wave reads one partial's contiguous kilobyte at a time.  On MI355X,
+//    cold, that is 2-12% faster than keeping every partial's load in flight
+//    (78% of HBM on an 8-way sum of 67 MB partials, against 70%);
+//  * beside a GEMM (a capped grid striding over the rows), or over a column
+//    block of wider rows: each lane owns one vector and keeps eight partials'
+//    loads in flight before adding; with the few workgroups the GEMM leaves
+//    room for, one load at a time per wave would not keep the reduce's share
+//    of HBM busy (6.7B step: 553 against 424 us).
 // Rows may be strided (ld), which is how a column block of a wider matrix is
 // reduced.  Besides (or instead of) the fp32 result the kernel can write a
 // copy in the next layer's input precision (bf16, rounded to nearest even, or
@@ -29,7 +38,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxP = 64;
 constexpr int kMaxOut = 64;
-constexpr int kGroup = 8;   // partials loaded together before adding
+constexpr int kGroup = 8;   // partials loaded together before adding (capped grids)
 
 struct RedArgs {
   const float *in[kMaxP];
@@ -95,37 +104,52 @@ __device__ __forceinline__ void store_lo(void *base, int64_t off, V v) {
   }
 }
 
-template <int VW, int UNROLL, int OP, bool BIAS, bool HI, int LO, bool NT = true>
+// SER: the serialised form (UNROLL vectors per lane), else the grouped one.
+template <int VW, int UNROLL, int OP, bool BIAS, bool HI, int LO, bool NT, bool SER>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(RedArgs a) {
   typedef typename FVec<VW>::T V;
-  const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < a.total_v; base += stride * UNROLL) {
+  const uint32_t stride = gridDim.x * kThreads * UNROLL;
+  for (uint32_t base = blockIdx.x * kThreads * UNROLL + threadIdx.x; base < a.total_v; base += stride) {
     int64_t in_off[UNROLL];
     bool ok[UNROLL];
     uint32_t row[UNROLL], col[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const uint32_t idx = base + u * stride;
+      const uint32_t idx = base + u * kThreads;
       ok[u] = idx < a.total_v;
       row[u] = ok[u] ? idx / a.cols_v : 0;
       col[u] = ok[u] ? idx - row[u] * a.cols_v : 0;
       in_off[u] = static_cast<int64_t>(row[u]) * a.ld_in + static_cast<int64_t>(col[u]) * VW;
     }
     V acc[UNROLL];
-    for (int p0 = 0; p0 < a.P; p0 += kGroup) {
-      V v[kGroup][UNROLL];
+    if constexpr (SER) {
+      for (int p = 0; p < a.P; ++p) {
+        const float *src = a.in[p];
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g)
+        for (int u = 0; u < UNROLL; ++u) {
+          if (!ok[u]) continue;
+          const V v = NT ? __builtin_nontemporal_load(reinterpret_cast<const V *>(src + in_off[u]))
+                         : *reinterpret_cast<const V *>(src + in_off[u]);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          acc[u] = p == 0 ? v : combine<OP>(acc[u], v);
+        }
+      }
+    } else {
+      for (int p0 = 0; p0 < a.P; p0 += kGroup) {
+        V v[kGroup][UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-          if (p0 + g < a.P && ok[u])
-            v[g][u] = NT ? __builtin_nontemporal_load(reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]))
-                         : *reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]);
+        for (int g = 0; g < kGroup; ++g)
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g)
+          for (int u = 0; u < UNROLL; ++u)
+            if (p0 + g < a.P && ok[u])
+              v[g][u] = NT ? __builtin_nontemporal_load(reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]))
+                           : *reinterpret_cast<const V *>(a.in[p0 + g] + in_off[u]);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-          if (p0 + g < a.P) acc[u] = (p0 + g == 0) ? v[g][u] : combine<OP>(acc[u], v[g][u]);
+        for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u)
+            if (p0 + g < a.P) acc[u] = (p0 + g == 0) ? v[g][u] : combine<OP>(acc[u], v[g][u]);
+      }
     }
     if constexpr (BIAS) {
 #pragma unroll
@@ -182,10 +206,14 @@ int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int
   a.rows_per_out = static_cast<uint32_t>(rows_per_out);
   a.ld_in = ld_in;
   a.ld_out = ld_out;
-  // One vector per lane in a one-shot grid keeps the most loads in flight
-  // (measured best on MI355X against 2- and 4-deep unrolled grid-stride loops).
-  constexpr int kUnroll = 1;
-  const int64_t want = (total_v + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  // Alone over whole rows: four vectors per lane in a one-shot grid,
+  // serialised loads (measured best on MI355X of 1, 2 and 4 vectors and of 1
+  // to 8 workgroups per CU).  Capped, or a column block of wider rows: one
+  // vector per lane, grouped loads (the GPT-3 175B step's last column-block
+  // reduce ran 8% slower serialised, 81 against 75 us).
+  const bool ser = max_wgs <= 0 && ld_in == cols;
+  const int64_t per_wg = kThreads * (ser ? 4 : 1);
+  const int64_t want = (total_v + per_wg - 1) / per_wg;
   const int64_t cap = max_wgs > 0 ? std::min<int64_t>(max_wgs, 1 << 20) : (1 << 20);
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>(want, cap)));
   // Small reduces (inputs and outputs within kCachedBytes) use cached loads and
@@ -193,14 +221,15 @@ int partial_reduce_launch(const float *const *partials, int P, int64_t rows, int
   constexpr int64_t kCachedBytes = int64_t(128) << 20;
   const bool nt = 4.0 * (P + nout) * static_cast<double>(rows) * cols > static_cast<double>(kCachedBytes);
   auto go = [&](auto vw, auto o, auto b, auto h, auto l) {
-    if (nt)
-      hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value,
-                                        decltype(h)::value, decltype(l)::value, true>),
-                         grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((reduce_kernel<decltype(vw)::value, kUnroll, decltype(o)::value, decltype(b)::value,
-                                        decltype(h)::value, decltype(l)::value, false>),
-                         grid, dim3(kThreads), 0, stream, a);
+    constexpr int VW = decltype(vw)::value, OP = decltype(o)::value, LO = decltype(l)::value;
+    constexpr bool BI = decltype(b)::value, HI = decltype(h)::value;
+    if (ser) {
+      if (nt) hipLaunchKernelGGL((reduce_kernel<VW, 4, OP, BI, HI, LO, true, true>), grid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((reduce_kernel<VW, 4, OP, BI, HI, LO, false, true>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+      if (nt) hipLaunchKernelGGL((reduce_kernel<VW, 1, OP, BI, HI, LO, true, false>), grid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((reduce_kernel<VW, 1, OP, BI, HI, LO, false, false>), grid, dim3(kThreads), 0, stream, a);
+    }
   };
   using std::integral_constant;
   // The second output exists for sums only (a layer's output feeding the next layer).

@@ -36,14 +36,13 @@
 //  * The MFMA gets W as its first operand and A as its second, so each lane
 //    owns one output row and four adjacent columns: 16-byte (fp32) or 8-byte
 //    (bf16) stores.
-// Ping-pong paths (bf16_gemm_pps, and bf16_gemm_pp for accumulating 256 x 192
-// tiles) for the 256-row tiles: the same tile, DMA and
-// LDS layout, but the two waves sharing a SIMD run in opposite phases.  The
-// waves of tile rows 0..127 (group A) and of rows 128..255 (group B) sit one
-// barrier apart: between two barriers one group runs its MFMAs while the other
-// reads its next stage from LDS, so the MFMA pipe is fed while LDS reads and
-// their waits happen.  In bf16_gemm_pp group A issues all of a stage's DMA
-// ahead of its reads; bf16_gemm_pps spreads it between both groups' MFMAs.
+// Ping-pong path (bf16_gemm_pps) for the 256-row tiles: the same tile, DMA
+// and LDS layout, but the two waves sharing a SIMD run in opposite phases.
+// The waves of tile rows 0..127 (group A) and of rows 128..255 (group B) sit
+// one barrier apart: between two barriers one group runs its MFMAs while the
+// other reads its next stage from LDS, so the MFMA pipe is fed while LDS reads
+// and their waits happen; each group issues its operand's DMA between its own
+// MFMAs.
 // Ragged path (bf16_gemm_ragged): the same MFMA on a 128 x 128 tile with
 // register-staged, bounds-checked loads, for shapes the DMA path cannot take
 // (K not a multiple of 32, N not a multiple of 8, misaligned pointers).
@@ -829,144 +828,19 @@ __device__ __forceinline__ void barrier_vm_n(int n) {
   }
 }
 
-// The ping-pong kernel: 8 waves (WGM x 8/WGM), BK = 64 or 32, S slots.  Waves
-// 0-3 form the group that issues the DMA, waves 4-7 the other; wave w runs on
-// SIMD w % 4, so each SIMD holds one wave of each group in either layout.
-template <int BM, int BN, int EPI, bool AT, bool WT, int BK = 64, int S = 2, int WGM = 2>
-__global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
-  using C = DmaCfg<BM, BN, BK, S, AT, WT, WGM, 8 / WGM>;
-  using TA = typename C::TA;
-  using TW = typename C::TW;
-  constexpr int KK = C::KK;
-  constexpr int NG = 4;                              // waves of the issuing group
-  constexpr int A_PW = TA::PIECES / NG, W_PW = TW::PIECES / NG, L = A_PW + W_PW;
-  static_assert(TA::PIECES % NG == 0 && TW::PIECES % NG == 0, "DMA split");
-  static_assert(S >= 2 && (S - 1) * L < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char smem[S * C::STAGE];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const bool grpA = wave < 4;
-  const int tiles_m = static_cast<int>((p.M + BM - 1) / BM);
-  const int tiles_n = static_cast<int>((p.N + BN - 1) / BN);
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TP_LDS char *)smem));
-  const int64_t ldc = p.ldc;
-  asm volatile("" ::"s"(ldc));
-
-  // Group A's DMA pieces as 32-bit byte offsets from the operand bases (the
-  // launcher only picks this kernel when every offset fits).
-  uint32_t a_src[A_PW], w_src[W_PW];
-#pragma unroll
-  for (int q = 0; q < A_PW; ++q)
-    a_src[q] = static_cast<uint32_t>(TA::src((wave & 3) * A_PW + q, lane, m0, p.M, p.lda) * 2);
-#pragma unroll
-  for (int q = 0; q < W_PW; ++q)
-    w_src[q] = static_cast<uint32_t>(TW::src((wave & 3) * W_PW + q, lane, n0, p.N, p.ldw) * 2);
-  const uint32_t a_step = static_cast<uint32_t>(TA::step(p.lda) * 2);
-  const uint32_t w_step = static_cast<uint32_t>(TW::step(p.ldw) * 2);
-  auto issue = [&](int st, int slot) {
-    const uint32_t base = lds0 + slot * C::STAGE;
-#pragma unroll
-    for (int q = 0; q < A_PW; ++q)
-      lds_dma16_s(p.a, a_src[q] + st * a_step, base + ((wave & 3) * A_PW + q) * 1024);
-#pragma unroll
-    for (int q = 0; q < W_PW; ++q)
-      lds_dma16_s(p.w, w_src[q] + st * w_step, base + TA::BYTES + ((wave & 3) * W_PW + q) * 1024);
-  };
-
-  // Every k-step of the stage in slot `slot`.
-  bf16x8_t fa[KK][C::TM], fb[KK][C::TN];
-  auto read_stage = [&](int slot) {
-    const TP_LDS char *base = (const TP_LDS char *)smem + slot * C::STAGE;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) fa[kk][i] = TA::frag(base, wm * C::WM + i * 16, kk, lane);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) fb[kk][j] = TW::frag(base + TA::BYTES, wn * C::WN + j * 16, kk, lane);
-    }
-  };
-  auto coords = [&](int i, int j, int64_t *m, int64_t *n) {
-    *m = m0 + wm * C::WM + i * 16 + (lane & 15);
-    *n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
-  };
-  f32x4_t acc[C::TM][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (EPI == kEpiF32Acc) {
-        int64_t m, n;
-        coords(i, j, &m, &n);
-        if (m < p.M && n < p.N) acc[i][j] = acc_start(p, ldc, m, n, true);
-      }
-    }
-  auto mma_stage = [&]() {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
-  };
-
-  // Schedule (barriers counted from 0; both groups execute 2 * nst + 1):
-  //   A: issue 0..S-1 | wait | #0 | M_0 #1 C_0 #2 | M_1 #3 C_1 #4 | ... | M_{n-1} #2n-1 C_{n-1} #2n
-  //   B:                  | #0 | #1 | M_0 #2 C_0 #3 | ... | M_{n-1} #2n C_{n-1}
-  // Between two barriers one group runs MFMAs while the other reads LDS.
-  // From t = 1 on, A issues stage t+S-1 in M_t into the slot of stage t-1,
-  // which both groups finished reading before #2t; at the end of C_t A waits
-  // until stage t+1 has landed (the stages after it may stay in flight).
-  const int nst = static_cast<int>(p.K / BK);
-  if (grpA) {
-    const int pre = nst < S ? nst : S;
-    for (int st = 0; st < pre; ++st) issue(st, st);
-    if (pre > 0) {
-      if (pre == S) wait_vmcnt<(S - 1) * L>(); else wait_vmcnt<0>();
-    }
-  }
-  barrier_raw();
-  if (!grpA) barrier_raw();
-  for (int t = 0; t < nst; ++t) {
-    if (grpA && t >= 1 && t + S - 1 < nst) issue(t + S - 1, (t + S - 1) % S);
-    read_stage(t % S);
-    barrier_lgkm0();
-    mma_stage();
-    if (grpA) {
-      // stages issued beyond t+1: min(S-2, nst-2-t)
-      const int later = min(S - 2, nst - 2 - t);
-      barrier_vm_n<L, S - 2>(later < 0 ? 0 : later);
-    } else if (t + 1 < nst) {
-      barrier_raw();
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      int64_t m, n;
-      coords(i, j, &m, &n);
-      if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);
-    }
-}
-
-// Ping-pong kernel with split rings (bf16_gemm_pps): the tile, waves,
-// fragment reads and MFMA order of bf16_gemm_pp, with the DMA taken out of the
-// read phases.  With one two-slot ring every DMA of stage s must leave in the
-// one phase that follows the barrier after which both groups are done with
-// stage s-2 and precedes the one after which group A reads stage s-1: the
-// phase in which group A reads LDS.  The issue of a stage's 40-64 DMA
-// instructions (about 15 cycles each through the CU's address unit) then holds
-// up group A's reads while group B waits at the barrier (MI355X phase stamps
-// of bf16_gemm_pp on the 175B GEMM1 shape: about 830 of 2950 cycles per stage).
-// Here the A tile has a ring of three slots and W's tile a ring of two, and
-// each group issues its tile between its own MFMAs:
+// The ping-pong kernel (bf16_gemm_pps): 8 waves (WGM x 8/WGM) on a 256-row
+// tile, K staged 64 at a time.  Waves 0-3 (group A, tile rows 0..127) and
+// 4-7 (group B, rows 128..255) run one barrier apart; wave w sits on SIMD
+// w % 4, so each SIMD holds one wave of each group and feeds its matrix pipe
+// from one while the other reads LDS.  With a single two-slot ring every DMA
+// of stage s would have to leave in the one phase that follows the barrier
+// after which both groups are done with stage s-2 and precedes the one after
+// which group A reads stage s-1, the phase in which group A reads LDS: the
+// issue of a stage's 40-64 DMA instructions (about 15 cycles each through the
+// CU's address unit) then held up group A's reads while group B waited at the
+// barrier (MI355X phase stamps on the 175B GEMM1 shape: about 830 of 2950
+// cycles per stage).  Here the A tile has a ring of three slots and W's tile a
+// ring of two, and each group issues its tile between its own MFMAs:
 //   A: a0 a1 | #0 | R_0 #1 M_0+a2 #2 | R_1 #3 M_1+a3 #4 | ...
 //   B: w0    | #0 | w1 #1 R_0 #2 M_0+w2 #3 R_1 #4 M_1+w3 ...
 // (aS, wS: the A / W tile of stage S; R reads, M multiplies).  Group A's
@@ -979,8 +853,9 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pp(GemmArgs p) {
 // compiler spill): where the stage it would fetch does not exist, it fetches
 // the last stage again, into the slot of the nominal stage, which nothing
 // reads any more.  Same accumulation order as every other kernel, so the
-// results are the same bits.  Measured on MI355X against bf16_gemm_pp: 7-15%
-// faster on every 256 x 192 and 256 x 128 shape here, forward and backward.
+// results are the same bits.  Measured on MI355X against the single-ring
+// form: 7-15% faster on every 256 x 192 and 256 x 128 shape here, forward and
+// backward, 8% on 256 x 256 and 9-14% with the accumulating epilogue.
 template <int BM, int BN, int EPI, bool AT, bool WT, int WGM = 2>
 __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
   constexpr int BK = 64;
@@ -1038,17 +913,21 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
     *n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
   };
   f32x4_t acc[C::TM][C::TN];
+  // Zeros, or C's tile: set right before each group's first MFMA, so that a
+  // loaded tile is not live across the DMA set-up (it spilled there).
+  auto init_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (EPI == kEpiF32Acc) {
-        int64_t m, n;
-        coords(i, j, &m, &n);
-        if (m < p.M && n < p.N) acc[i][j] = acc_start(p, ldc, m, n, true);
+      for (int j = 0; j < C::TN; ++j) {
+        acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (EPI == kEpiF32Acc) {
+          int64_t m, n;
+          coords(i, j, &m, &n);
+          if (m < p.M && n < p.N) acc[i][j] = acc_start(p, ldc, m, n, true);
+        }
       }
-    }
+  };
   // The stage's MFMAs with ND DMA pieces of stage `dst` spread between them:
   // piece q after MFMA number (q + 1/2) * NF / ND (ND = 0: none; measured
   // 1.5-3% faster than starting at the first MFMA).  Everything is
@@ -1104,6 +983,7 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
   }
   barrier_raw();                                     // #0
   if (grpA) {
+    init_acc();
     for (int t = 0; t < nst; ++t) {
       read_stage(t);
       barrier_lgkm0();                               // #2t+1
@@ -1118,6 +998,7 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // #2
     __builtin_amdgcn_sched_barrier(0);
+    init_acc();
     for (int t = 1; t < nst; ++t) {
       mma_stage(IW{}, F{}, min(t + 1, last), t + 1);   // stage t+1's W tile, slot (t+1) % 2
       barrier_raw();                                 // #2t+1
@@ -1127,6 +1008,8 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     mma_stage(I0{}, F{}, 0, 0);
+  } else {
+    init_acc();
   }
   wait_vmcnt<0>();                                   // the repeated fetches of the last stage
 
@@ -1267,13 +1150,6 @@ hipError_t launch_dma_group(const GemmArgs *ps, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int EPI, bool AT, bool WT, int BK = 64, int S = 2, int WGM = 2>
-hipError_t launch_pp(const GemmArgs& p, hipStream_t s) {
-  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((bf16_gemm_pp<BM, BN, EPI, AT, WT, BK, S, WGM>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s, p);
-  return hipGetLastError();
-}
-
 template <int BM, int BN, int EPI, bool AT, bool WT, int WGM = 2>
 hipError_t launch_pps(const GemmArgs& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -1326,16 +1202,9 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
   if constexpr (big_ok)
     if (c256 == best) return launch_pps<256, 256, EPI, AT, WT>(p, s);
   if (c192 == best) {
-    // A read transposed (weight gradients): 4 x 2 waves, 2-3% faster.  The
-    // accumulating epilogue keeps the single-ring kernel, where the split
-    // rings' extra registers would spill.
-    if constexpr (EPI == kEpiF32Acc) {
-      if constexpr (AT) return launch_pp<256, 192, EPI, AT, WT, 64, 2, 4>(p, s);
-      else return launch_pp<256, 192, EPI, AT, WT>(p, s);
-    } else {
-      if constexpr (AT) return launch_pps<256, 192, EPI, AT, WT, 4>(p, s);
-      else return launch_pps<256, 192, EPI, AT, WT>(p, s);
-    }
+    // A read transposed (weight gradients): 4 x 2 waves, 2-3% faster.
+    if constexpr (AT) return launch_pps<256, 192, EPI, AT, WT, 4>(p, s);
+    else return launch_pps<256, 192, EPI, AT, WT>(p, s);
   }
   // 256 x 128 tiles: the ping-pong kernel where its 32-bit offsets reach
   // (measured 10-12% faster than the single-group kernel on 4096 x 2048 x 4096).

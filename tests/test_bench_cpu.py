@@ -68,6 +68,21 @@ def test_fractions_per_kernel_family():
     assert r["kernel"] == "gemm1" and r["avg_ms"] == 0.25 and r["timing"] == "cold"
 
 
+def test_tail_reduce_is_its_own_hbm_kernel():
+    """The last block's reduction (alone on a one-shot grid) is reported apart
+    from the reductions beside the GEMMs, each priced against HBM, and neither
+    is taken as the dominant kernel while GEMMs are present."""
+    st = {name: {"launches": 0, "total_ms": 0.0, "min_ms": 0.0, "max_ms": 0.0, "work": 0.0}
+          for name in ("gemm1", "gemm2", "reduce", "reduce_tail")}
+    st["gemm2"].update(launches=4, total_ms=0.58, work=4 * 154.6e9)
+    st["reduce"].update(launches=3, total_ms=0.45, work=3 * 453e6)
+    st["reduce_tail"].update(launches=1, total_ms=0.075, work=453e6)
+    k = bench.kernel_table(st, 1, "bf16")
+    assert k["reduce_tail"]["unit"] == "GB/s" and k["reduce_tail"]["bound"] == "hbm"
+    assert abs(k["reduce_tail"]["achieved"] - 6040.0) < 1 and abs(k["reduce"]["achieved"] - 3020.0) < 1
+    assert bench.roofline(k, "bf16", "w")["kernel"] == "gemm2"
+
+
 def test_spread_reports_median_and_percentiles():
     s = bench.spread([1.0, 2.0, 3.0, 4.0, 100.0])
     assert s["median"] == 3.0 and s["n"] == 5

@@ -48,6 +48,22 @@ def test_integer_partials_bit_exact():
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("rows,cols", [(0, 16), (16, 0)])
+def test_empty_block_is_a_no_op(rows, cols):
+    """A block with no rows or no columns launches nothing and leaves the
+    output untouched, in both modes."""
+    announce(f"reduce empty block rows={rows} cols={cols}")
+    parts = [torch.zeros((16, 16), device="cuda") for _ in range(3)]
+    full = Guarded((16, 16), torch.float32)
+    tp.tp_partial_reduce(parts, [full.t], tp.TP_REDUCE_FULL, rows=rows, cols=cols, ld_in=16, ld_out=16)
+    outs = [Guarded((8, 16), torch.float32) for _ in range(2)]
+    tp.tp_partial_reduce(parts, [o.t for o in outs], tp.TP_REDUCE_SPLIT, rows=rows, cols=cols, ld_in=16, ld_out=16)
+    torch.cuda.synchronize()
+    for g in [full] + outs:
+        assert g.guards_intact()
+        assert (bits(g.t.cpu()) == np.int32(0x7FC0DEAD)).all()
+
+
 def test_in_place():
     announce("reduce FULL in place")
     parts_cpu = [inputs.normal((96, 200), seed=7000 + p) for p in range(4)]

@@ -338,11 +338,13 @@ typedef struct {
                         block of the two-stream one), GEMM2 adds the peers' partials
                         and the bias in its epilogue and writes Z_out / X_next itself.
                         Taken for P <= 4 and Z_out or a Z_split whose chunk spans at
-                        most 4 sequence blocks; for bf16 also 16-byte aligned rows,
-                        F a multiple of 32 and blocks of fewer than 256 output tiles
-                        of 128 x 128; otherwise,
-                        and always with TP_REDUCE_FUSION_OFF (1), a separate
-                        reduction kernel runs.  Both give the same bits. */
+                        most 4 sequence blocks on blocks of fewer than 256 output
+                        tiles of 128 x 128 (bf16: 16-byte aligned rows, F a multiple
+                        of 32), and for bf16 blocks of at least that many tiles with
+                        P <= 16, Z_out (or a Z_split block holding the whole chunk),
+                        16-byte aligned rows and F a multiple of 64; otherwise, and
+                        always with TP_REDUCE_FUSION_OFF (1), a separate reduction
+                        kernel runs.  Both give the same bits. */
   int64_t A_ld;      /* row stride of A_i in elements; 0 = F (contiguous).  With
                         A_ld = P*F, A_i may point into the full A [H, P*F] at column
                         i*F: the rank consumes its column shard in place, as the

@@ -294,7 +294,7 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     // one launch fewer and no second read of the partial just written.
     const bool final_block = last && c + 1 == pl.C;
     if (pl.reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && (!two || final_block) &&
-        (pl.epi2 == kEpiF32 || pl.epi2 == kEpiPlainF32) && a->P - 1 <= kMaxFusedPeers) {
+        (pl.epi2 == kEpiF32 || pl.epi2 == kEpiPlainF32) && a->P - 1 <= kMaxEpiPeers) {
       const bool f32 = pl.epi2 == kEpiPlainF32;
       GemmArgs gr = g2;
       gr.red.np = static_cast<int32_t>(a->P - 1);

@@ -17,15 +17,21 @@ namespace tpshard {
 // Peers and lo are [M][ldc] like C; bias is indexed by column.  The fp32 sum
 // goes to out[0] ([M][ldc]), or, reduce-scattered, row m to out[m / rows_per_out]
 // at row m % rows_per_out (each [rows_per_out][ldc]).
+// Two forms: on the small-tile path the peers' vectors stream in during the
+// k loop (at most kMaxFusedPeers peers: their vectors sit beside the
+// accumulators); on the 256-row tiles the epilogue stages each half tile
+// through LDS and reads the peers' rows whole (at most kMaxEpiPeers peers,
+// one fp32 output).
 constexpr int kMaxFusedPeers = 3;
+constexpr int kMaxEpiPeers = 15;
 constexpr int kMaxFusedOuts = 4;
 struct EpiReduce {
-  const float *peer[kMaxFusedPeers];
+  const float *peer[kMaxEpiPeers];
   float *out[kMaxFusedOuts];   // fp32 sum, or out[0] null for none; a single out may equal C
                                // (then C receives the sum only)
   const float *bias;           // or null
   void *lo;                    // copy of the sum in bf16 (RNE) or fp32, or null (single out only)
-  int32_t np;                  // peers used, 0..kMaxFusedPeers
+  int32_t np;                  // peers used (see the two forms above)
   int32_t lo_bf16;             // lo holds bf16 (else fp32)
   int32_t nout;                // outputs, 1..kMaxFusedOuts
   int32_t rows_per_out;        // rows of each output when nout > 1
@@ -68,9 +74,12 @@ enum {
 hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s);
 
 // Whether gemm_launch takes p with kEpiF32Red: A not transposed, whole
-// 16-byte vectors along every row of C, the peers, out, bias and lo, on the
-// small-tile path (fewer 128 x 128 tiles than CUs, K % 32 == 0), where the
-// peers' loads fit beside the accumulators without costing occupancy.
+// 16-byte vectors along every row of C, the peers, out, bias and lo; either
+// on the small-tile path (fewer 128 x 128 tiles than CUs, K % 32 == 0, at most
+// kMaxFusedPeers peers), where the peers' loads fit beside the accumulators
+// without costing occupancy, or on the 256-row tiles (W not transposed,
+// K % 64 == 0, operands within 32-bit offsets, at most kMaxEpiPeers peers, one
+// output), where the epilogue stages the tile through LDS.
 bool gemm_red_ok(const GemmArgs& p);
 // The same for kEpiPlainF32Red (the fp32 kernel, any alignment and size).
 bool gemm_red_ok_f32(const GemmArgs& p);

@@ -1013,14 +1013,69 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
   }
   wait_vmcnt<0>();                                   // the repeated fetches of the last stage
 
+  if constexpr (EPI == kEpiF32Red) {
+    // The block's sum over the peers, in the separate reduction's order (the
+    // tile's own partial, every peer in turn, then the bias), with the peers
+    // read as whole rows: the accumulators' layout (16 rows of 64 bytes per
+    // vector load) would read them at half the rate.  Each half tile (128
+    // rows, one wave group's accumulators) is written to LDS, then all 512
+    // lanes walk it row by row: own value from LDS, the peers' vectors from
+    // HBM (up to eight in flight), the sum to out[0] and lo, the partial to C
+    // unless the sum goes in place over it.
+    const EpiReduce& r = p.red;
+    constexpr int PITCH = BN * 4 + 16;                 // LDS bytes per row (16 bytes of padding)
+    constexpr int VPR = BN / 4;                        // 16-byte vectors per row
+    static_assert(128 * PITCH <= SA * TA::BYTES + SW * TW::BYTES, "half tile in LDS");
+    TP_LDS char *half = (TP_LDS char *)smem;
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();                                 // LDS free: fragments read, DMA landed, previous half done
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      int64_t m, n;
-      coords(i, j, &m, &n);
-      if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);
+      for (int i = 0; i < C::TM; ++i) {
+        const int tr = wm * C::WM + i * 16 + (lane & 15);   // row in the tile (uniform half per wave)
+        if (tr / 128 != h) continue;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          *(TP_LDS f32x4_t *)(half + (tr - h * 128) * PITCH + (wn * C::WN + j * 16 + 4 * (lane >> 4)) * 4) = acc[i][j];
+      }
+      __syncthreads();
+      for (int u = threadIdx.x; u < 128 * VPR; u += 512) {
+        const int row = u / VPR, cv = u - row * VPR;
+        const int64_t m = m0 + h * 128 + row, n = n0 + cv * 4;
+        if (m >= p.M || n >= p.N) continue;
+        const int64_t off = m * ldc + n;
+        f32x4_t sum = *(const TP_LDS f32x4_t *)(half + row * PITCH + cv * 16);
+        if (r.out[0] != p.c) *reinterpret_cast<f32x4_t *>(static_cast<float *>(p.c) + off) = sum;
+        for (int q0 = 0; q0 < r.np; q0 += 8) {
+          f32x4_t v[8];
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (q0 + g < r.np) v[g] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(r.peer[q0 + g] + off));
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (q0 + g < r.np) sum = sum + v[g];
+        }
+        if (r.bias) sum = sum + *reinterpret_cast<const f32x4_t *>(r.bias + n);
+        if (r.out[0]) __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out[0] + off));
+        if (r.lo) {
+          if (r.lo_bf16)
+            *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(r.lo) + off) =
+                u32x2_t{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+          else
+            *reinterpret_cast<f32x4_t *>(static_cast<float *>(r.lo) + off) = sum;
+        }
+      }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        int64_t m, n;
+        coords(i, j, &m, &n);
+        if (m < p.M && n < p.N) epi_store<EPI>(p, ldc, m, n, acc[i][j], true);
+      }
+  }
 }
 
 // ---- plain fp32 kernel (tiny fp32 workload) ------------------------------
@@ -1223,6 +1278,23 @@ hipError_t dispatch_bf16(const GemmArgs& p, bool dma_ok, bool vec, hipStream_t s
 
 bool aligned16(const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+// GEMM2 with the block's sum in the epilogue on the 256-row tiles: the tile
+// the cost model takes among the split-ring ones (the only kernels with that
+// epilogue).
+hipError_t dispatch_red_tiles(const GemmArgs& p, hipStream_t s) {
+  auto cost = [&](int bm, int bn, double eff) {
+    const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    return static_cast<double>((tiles + kCUs - 1) / kCUs) * bm * bn / eff;
+  };
+  const double c256 = cost(256, 256, 1.0), c192 = cost(256, 192, 0.95), c128w = cost(256, 128, 0.85);
+  if (c256 <= c192 && c256 <= c128w) return launch_pps<256, 256, kEpiF32Red, false, false>(p, s);
+  if (c192 <= c128w) return launch_pps<256, 192, kEpiF32Red, false, false>(p, s);
+  return launch_pps<256, 128, kEpiF32Red, false, false>(p, s);
+}
+
+// Fewer 128 x 128 tiles than CUs: the small-tile path.
+bool small_problem(const GemmArgs& p) { return ((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs; }
+
 }  // namespace
 
 // Conditions for 16-byte access along every operand's contiguous dimension
@@ -1268,6 +1340,7 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
       case kEpiGeluSaveBf16: return dispatch_bf16<kEpiGeluSaveBf16, false, false>(p, dma_ok, vec, s);
       case kEpiF32Red:
         if (!gemm_red_ok(p)) return hipErrorInvalidValue;
+        if (!small_problem(p)) return dispatch_red_tiles(p, s);
         if (p.red.nout > 1) {
           if (p.K % 64 == 0) return launch_dma<64, 64, 64, 2, kEpiF32RedSplit, false, false, 2, 2>(p, s);
           return launch_dma<64, 64, 32, 4, kEpiF32RedSplit, false, false, 2, 2>(p, s);
@@ -1300,10 +1373,15 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
 
 bool gemm_red_ok(const GemmArgs& p) {
   const EpiReduce& r = p.red;
-  const bool small = ((p.M + 127) / 128) * ((p.N + 127) / 128) < kCUs;
-  if (p.a_t || p.acc_init || r.np < 0 || r.np > kMaxFusedPeers || !small || p.K <= 0 || p.K % 32 != 0 ||
-      !gemm_vec_ok(p, 4, false))
+  if (p.a_t || p.acc_init || r.np < 0 || p.K <= 0 || p.K % 32 != 0 || !gemm_vec_ok(p, 4, false)) return false;
+  if (!small_problem(p)) {
+    // The split-ring tiles: forward layout, 64-deep stages, 32-bit operand
+    // offsets, one output.
+    const bool off32 = p.M * p.lda * 2 < (int64_t{1} << 31) && p.K * p.ldw * 2 < (int64_t{1} << 31);
+    if (p.w_t || r.np > kMaxEpiPeers || p.K % 64 != 0 || !off32 || r.nout != 1) return false;
+  } else if (r.np > kMaxFusedPeers) {
     return false;
+  }
   bool ok = !r.bias || aligned16(r.bias);
   for (int q = 0; q < r.np; ++q) ok = ok && r.peer[q] && aligned16(r.peer[q]);
   if (r.nout < 1 || r.nout > kMaxFusedOuts || (p.w_t && r.nout > 1)) return false;

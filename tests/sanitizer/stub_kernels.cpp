@@ -81,8 +81,11 @@ hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t) {
 // what the kernels' own conditions would, minus alignment, so both the fused
 // and the separate reduction paths get exercised.
 bool gemm_red_ok(const GemmArgs& p) {
-  return !p.a_t && !p.acc_init && p.red.np >= 0 && p.red.np <= kMaxFusedPeers && p.red.nout >= 1 &&
-         p.red.nout <= kMaxFusedOuts && p.K % 32 == 0 && ((p.M + 127) / 128) * ((p.N + 127) / 128) < 256 &&
+  if (p.a_t || p.acc_init || p.red.np < 0 || p.K % 32 != 0 || p.K <= 0) return false;
+  if (((p.M + 127) / 128) * ((p.N + 127) / 128) >= 256)   // the 256-row tiles: the epilogue stages the tile
+    return !p.w_t && p.red.np <= kMaxEpiPeers && p.K % 64 == 0 && p.red.nout == 1 &&
+           p.M * p.lda * 2 < (int64_t{1} << 31) && p.K * p.ldw * 2 < (int64_t{1} << 31);
+  return p.red.np <= kMaxFusedPeers && p.red.nout >= 1 && p.red.nout <= kMaxFusedOuts &&
          !(p.w_t && p.red.nout > 1) && (p.red.nout == 1 || (!p.red.lo && p.red.rows_per_out * p.red.nout == p.M));
 }
 bool gemm_red_ok_f32(const GemmArgs& p) {

@@ -372,6 +372,15 @@ def _run_fusion(X, A, B, peers, *, fusion, R=1, C=1, bias=None, z_out=True, in_p
     (300, 264, 192, 4, 3, 3, {"x_next": True, "in_place": True}),  # serial, ragged rows, 3 x 3 blocks, in place
     (512, 384, 256, 5, 1, 1, {}),                                  # 4 peers: separate reduction
     (520, 392, 200, 3, 1, 1, {}),                                  # K % 32 != 0: separate reduction
+    # the 256-row tiles, the tile staged through LDS in the epilogue: 256 x 128, 256 x 256 (in place),
+    # 256 x 192 (bias and the bf16 next input), 15 peers with ragged rows, only the final block of a
+    # two-stream schedule, and 16 peers (past the limit: separate reduction)
+    (2048, 2048, 512, 8, 1, 1, {}),
+    (4096, 4096, 256, 8, 1, 1, {"in_place": True}),
+    (2048, 6144, 512, 8, 1, 1, {"bias": True, "x_next": True}),
+    (2000, 4096, 256, 16, 1, 1, {"bias": True}),
+    (4096, 4096, 256, 8, 2, 1, {"bias": True, "two": True}),
+    (2048, 2048, 256, 17, 1, 1, {}),
 ])
 def test_reduce_fusion_same_bits(M, H, F, P, Rc, Cc, opts):
     """GEMM2 with the block's reduction folded into its epilogue writes the
@@ -464,10 +473,13 @@ def test_timing_reports_the_fused_kernel():
 
 
 @pytest.mark.parametrize("M,H,F,P,fused", [(512, 384, 256, 4, True), (512, 384, 256, 5, False),
-                                            (520, 392, 200, 3, False), (512, 384, 256, 1, False)])
+                                            (520, 392, 200, 3, False), (512, 384, 256, 1, False),
+                                            (2048, 2048, 512, 8, True), (2048, 2048, 512, 16, True),
+                                            (2048, 2048, 512, 17, False), (2048, 2048, 480, 8, False)])
 def test_fusion_taken_where_the_rule_says(M, H, F, P, fused):
     """The reduction runs in GEMM2's epilogue for P <= 4 with F % 32 == 0 on a
-    small block, and as its own kernel otherwise (P = 1 has nothing to sum)."""
+    small block, and for P <= 16 with F % 64 == 0 on a block of the 256-row
+    tiles; as its own kernel otherwise (P = 1 has nothing to sum)."""
     announce(f"mlp fusion rule M={M} H={H} F={F} P={P}")
     X = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
     A = torch.zeros((H, F), dtype=torch.bfloat16, device="cuda")

@@ -341,8 +341,8 @@ typedef struct {
                         most 4 sequence blocks on blocks of fewer than 256 output
                         tiles of 128 x 128 (bf16: 16-byte aligned rows, F a multiple
                         of 32), and for bf16 blocks of at least that many tiles with
-                        P <= 16, Z_out (or a Z_split block holding the whole chunk),
-                        16-byte aligned rows and F a multiple of 64; otherwise, and
+                        P <= 16, the same outputs, 16-byte aligned rows and F a
+                        multiple of 64; otherwise, and
                         always with TP_REDUCE_FUSION_OFF (1), a separate reduction
                         kernel runs.  Both give the same bits. */
   int64_t A_ld;      /* row stride of A_i in elements; 0 = F (contiguous).  With

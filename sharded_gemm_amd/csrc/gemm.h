@@ -20,8 +20,7 @@ namespace tpshard {
 // Two forms: on the small-tile path the peers' vectors stream in during the
 // k loop (at most kMaxFusedPeers peers: their vectors sit beside the
 // accumulators); on the 256-row tiles the epilogue stages each half tile
-// through LDS and reads the peers' rows whole (at most kMaxEpiPeers peers,
-// one fp32 output).
+// through LDS and reads the peers' rows whole (at most kMaxEpiPeers peers).
 constexpr int kMaxFusedPeers = 3;
 constexpr int kMaxEpiPeers = 15;
 constexpr int kMaxFusedOuts = 4;
@@ -78,8 +77,8 @@ hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s);
 // on the small-tile path (fewer 128 x 128 tiles than CUs, K % 32 == 0, at most
 // kMaxFusedPeers peers), where the peers' loads fit beside the accumulators
 // without costing occupancy, or on the 256-row tiles (W not transposed,
-// K % 64 == 0, operands within 32-bit offsets, at most kMaxEpiPeers peers, one
-// output), where the epilogue stages the tile through LDS.
+// K % 64 == 0, operands within 32-bit offsets, at most kMaxEpiPeers peers),
+// where the epilogue stages the tile through LDS.
 bool gemm_red_ok(const GemmArgs& p);
 // The same for kEpiPlainF32Red (the fp32 kernel, any alignment and size).
 bool gemm_red_ok_f32(const GemmArgs& p);

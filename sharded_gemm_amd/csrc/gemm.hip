@@ -1021,7 +1021,8 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
     // rows, one wave group's accumulators) is written to LDS, then all 512
     // lanes walk it row by row: own value from LDS, the peers' vectors from
     // HBM (up to eight in flight), the sum to out[0] and lo, the partial to C
-    // unless the sum goes in place over it.
+    // unless the sum goes in place over it (or, reduce-scattered, each row to
+    // its sequence block).
     const EpiReduce& r = p.red;
     constexpr int PITCH = BN * 4 + 16;                 // LDS bytes per row (16 bytes of padding)
     constexpr int VPR = BN / 4;                        // 16-byte vectors per row
@@ -1056,7 +1057,13 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
             if (q0 + g < r.np) sum = sum + v[g];
         }
         if (r.bias) sum = sum + *reinterpret_cast<const f32x4_t *>(r.bias + n);
-        if (r.out[0]) __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out[0] + off));
+        if (r.nout > 1) {
+          // reduce-scattered: row m to out[m / rows_per_out]
+          const int64_t jo = m / r.rows_per_out;
+          __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out[jo] + (m - jo * r.rows_per_out) * ldc + n));
+        } else if (r.out[0]) {
+          __builtin_nontemporal_store(sum, reinterpret_cast<f32x4_t *>(r.out[0] + off));
+        }
         if (r.lo) {
           if (r.lo_bf16)
             *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(r.lo) + off) =
@@ -1376,9 +1383,9 @@ bool gemm_red_ok(const GemmArgs& p) {
   if (p.a_t || p.acc_init || r.np < 0 || p.K <= 0 || p.K % 32 != 0 || !gemm_vec_ok(p, 4, false)) return false;
   if (!small_problem(p)) {
     // The split-ring tiles: forward layout, 64-deep stages, 32-bit operand
-    // offsets, one output.
+    // offsets.
     const bool off32 = p.M * p.lda * 2 < (int64_t{1} << 31) && p.K * p.ldw * 2 < (int64_t{1} << 31);
-    if (p.w_t || r.np > kMaxEpiPeers || p.K % 64 != 0 || !off32 || r.nout != 1) return false;
+    if (p.w_t || r.np > kMaxEpiPeers || p.K % 64 != 0 || !off32) return false;
   } else if (r.np > kMaxFusedPeers) {
     return false;
   }

@@ -92,6 +92,11 @@ def test_forward_integer_exact(M, H, F, Rc, Cc, P, S):
     (1024, 384, 256, 2, 2, 4, 4),     # a chunk covers 2 blocks, 2 column blocks
     (1024, 384, 256, 4, 1, 3, 2),     # a chunk lies inside one block
     (1200, 264, 160, 1, 1, 2, 8),     # 8 blocks in the chunk: separate reduce-scatter
+    # the 256-row tiles, the tile staged through LDS: a chunk over 4 blocks (8 ranks), a chunk inside a block,
+    # ragged rows over 2 blocks
+    (4096, 4096, 512, 1, 1, 8, 4),
+    (4096, 2048, 512, 2, 1, 8, 2),
+    (3000, 4096, 256, 1, 1, 4, 2),
 ])
 def test_forward_reduce_fusion_same_bits(M, H, F, Rc, Cc, P, S):
     """The reduce-scatter folded into GEMM2's epilogue (serial schedule: every

@@ -815,14 +815,23 @@ def measure(wl, steps, warmup, flusher, kernel_tables=True, profile=False):
     if hasattr(wl, "prepare"):
         wl.prepare()
     dtype = "bf16" if getattr(getattr(wl, "w", None), "dtype", "f32") == "bf16" else "f32"
-    for _ in range(warmup):
-        if profile:
+    if profile:
+        for _ in range(warmup):
             flusher(wl.s0)
+            wl.step()
+        torch.cuda.synchronize()
+        return measure_profile(wl, steps, flusher, dtype)
+    # One eager step gives the result a graph replay must reproduce; the W
+    # warm-up steps come after the capture, right before the timed ones: the
+    # capture leaves the GPU idle for a while, and the first 5-10 ms of work
+    # after an idle spell run up to 10% slower (MI355X: 175B step 1,343 against
+    # 1,145 us over the first ten steps after 2 s idle).
+    wl.step()
+    torch.cuda.synchronize()
+    graph = capture(wl)
+    for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
-    if profile:
-        return measure_profile(wl, steps, flusher, dtype)
-    graph = capture(wl)
     s0 = wl.s0
 
     def one(use_graph):
@@ -972,7 +981,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-extras", action="store_true",
                     help="time only --workload (the default run also times the other four configurations)")

@@ -335,7 +335,10 @@ typedef struct {
                         layer's input; Z_out may then be NULL.  Not with Z_split. */
   int32_t reduce_fusion; /* TP_REDUCE_FUSION_AUTO (0): where a block's reduction would
                         run with nothing beside it (the serial schedule, or the final
-                        block of the two-stream one), GEMM2 adds the peers' partials
+                        block of the two-stream one), or beside GEMMs too short to
+                        cover it (bf16: its bytes at 6 TB/s take more than 3/4 of the
+                        next block's GEMM2, or of the next chunk's GEMM1 and first
+                        GEMM2, at 1.2 PFLOP/s), GEMM2 adds the peers' partials
                         and the bias in its epilogue and writes Z_out / X_next itself.
                         Taken for P <= 4 and Z_out or a Z_split whose chunk spans at
                         most 4 sequence blocks on blocks of fewer than 256 output
@@ -363,7 +366,10 @@ enum { TP_REDUCE_FUSION_AUTO = 0, TP_REDUCE_FUSION_OFF = 1 };
  * s_compute is made to wait for s_reduce, so completion of s_compute means the
  * whole call is done.  s_reduce may equal s_compute (serial schedule); with a
  * single block (R = C = 1) the reduce runs on s_compute, as nothing could
- * overlap it.  The calls are capturable into a HIP graph (no memsets, no
+ * overlap it, and so it does (in GEMM2's epilogue, reduce_fusion AUTO) for a
+ * block whose reduction the next GEMMs are too short to cover; where that
+ * leaves s_reduce nothing to do the call keeps to s_compute.  The calls are
+ * capturable into a HIP graph (no memsets, no
  * allocation, no host synchronisation).
  * Chunking never changes a result bit: each output element is accumulated in
  * the same order whatever R and C are.  With sequence parallelism (S > 1) the

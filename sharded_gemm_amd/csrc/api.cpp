@@ -42,6 +42,11 @@ constexpr int64_t kMaxLayers = 1024;
 // workgroups; one workgroup per CU back-fills those gaps without crowding out
 // the next GEMM (measured on MI355X against 32 ... 16384).
 constexpr int64_t kReduceBesideGemm = 256;
+// Rates for weighing a block's reduction against the GEMMs it would run
+// beside (MI355X, measured in the step: bf16 GEMMs at about 1.2 PFLOP/s, a
+// reduction alone at about 6 TB/s), and the share of those GEMMs' time the
+// reduction may take and still run beside them.
+constexpr double kGemmFlopRate = 1.2e15, kReduceByteRate = 6.0e12, kBesideShare = 0.75;
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -265,17 +270,93 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   return TP_OK;
 }
 
+// Chunk r's Y: its own rows of Y_ws, or the one chunk-sized Y_ws, which
+// chunk r+1's GEMM1 may overwrite once chunk r's GEMM2 (earlier on s0) has read it.
+char *chunk_y(const tp_mlp_args *a, const MlpPlan& pl, int64_t r) {
+  return static_cast<char *>(a->Y_ws) + (pl.y_chunk ? 0 : r * pl.Mr * pl.F * pl.es);
+}
+
+// GEMM2 of block (r, c): Z_i[r, c] = Y[r] B_i[:, c].
+GemmArgs block_gemm2(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c) {
+  const int64_t zoff = r * pl.Mr * pl.H + c * pl.Hc;
+  return GemmArgs{chunk_y(a, pl, r), static_cast<const char *>(a->B_i) + c * pl.Hc * pl.es, a->Z_i + zoff,
+                  pl.Mr, pl.Hc, pl.F, pl.F, pl.H, pl.H};
+}
+
+// Whether block (r, c)'s reduction folds into its GEMM2's epilogue, and if so
+// that GEMM2 (*gr).  It does where the reduction would run with nothing beside
+// it anyway (one stream, or the final block: `last` says nothing follows chunk
+// r on s0): one launch fewer and no second read of the partial just written.
+// It does so too on two streams where the GEMMs that s0 issues next (the next
+// block's GEMM2, or the next chunk's GEMM1 and first GEMM2) are too short to
+// cover it: beside them it would slow them by about its own length and still
+// run past them (GPT-3 6.7B at TP = 8, R = 2: 604 MB of reduction beside
+// 137 GFLOP; that step took 417 us on two streams against 388 us with each
+// chunk's sum in GEMM2's epilogue).  The kernel must take the block as well
+// (gemm_red_ok).
+bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, bool two, bool last,
+                 GemmArgs *gr) {
+  const int64_t H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
+  const bool f32 = pl.epi2 == kEpiPlainF32;
+  if (!pl.reduce || a->reduce_fusion != TP_REDUCE_FUSION_AUTO || !(pl.epi2 == kEpiF32 || f32) ||
+      a->P - 1 > kMaxEpiPeers)
+    return false;
+  const bool final_block = last && c + 1 == pl.C;
+  if (two && !final_block) {
+    if (f32) return false;
+    const double next_flops = 2.0 * Mr * F * (c + 1 < pl.C ? Hc : H + Hc);
+    const double red_bytes = 4.0 * (a->P + 1) * Mr * Hc;
+    if (red_bytes / kReduceByteRate <= kBesideShare * next_flops / kGemmFlopRate) return false;
+  }
+  const int64_t zoff = r * Mr * H + c * Hc;
+  *gr = block_gemm2(a, pl, r, c);
+  gr->red.np = static_cast<int32_t>(a->P - 1);
+  for (int64_t p = 1; p < a->P; ++p) gr->red.peer[p - 1] = a->peer_partials[p - 1] + zoff;
+  gr->red.nout = 1;
+  gr->red.rows_per_out = static_cast<int32_t>(Mr);
+  if (a->Z_split) {
+    // Reduce-scattered: the chunk lies in one sequence block, or covers
+    // whole ones (the two nest).
+    const int64_t Ms = pl.sq.Ms, g0 = r * Mr, j0 = g0 / Ms;
+    if (Mr <= Ms) {
+      gr->red.out[0] = a->Z_split[j0] + (g0 - j0 * Ms) * H + c * Hc;
+    } else if (Mr / Ms <= kMaxFusedOuts) {
+      gr->red.nout = static_cast<int32_t>(Mr / Ms);
+      gr->red.rows_per_out = static_cast<int32_t>(Ms);
+      for (int64_t k = 0; k < Mr / Ms; ++k) gr->red.out[k] = a->Z_split[j0 + k] + c * Hc;
+    } else {
+      return false;
+    }
+  } else {
+    gr->red.out[0] = a->Z_out ? a->Z_out + zoff : nullptr;
+  }
+  gr->red.bias = a->bias ? a->bias + c * Hc : nullptr;
+  gr->red.lo = a->X_next ? static_cast<char *>(a->X_next) + zoff * pl.es : nullptr;
+  gr->red.lo_bf16 = a->dtype == TP_BF16;
+  return f32 ? gemm_red_ok_f32(*gr) : gemm_red_ok(*gr);
+}
+
+// Whether any block of the layer hands its reduction to s1 on a two-stream
+// schedule; `last_chunk_last`: nothing follows the layer's last chunk on s0.
+bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_last) {
+  if (!pl.reduce) return false;
+  GemmArgs gr{};
+  for (int64_t r = 0; r < pl.R; ++r)
+    for (int64_t c = 0; c < pl.C; ++c)
+      if (!fused_block(a, pl, r, c, true, last_chunk_last && r + 1 == pl.R, &gr)) return true;
+  return false;
+}
+
 // Row chunk r of one forward layer: GEMM1 and, per column block, GEMM2 and its
-// reduction (handed to s1 through ev_blocks[c] when `two`).  `last`: nothing
-// follows this chunk on s0, so its final block's reduction runs alone and takes
-// the whole chip (a one-shot grid) instead of the share sized to run beside a GEMM.
+// reduction (in GEMM2's epilogue, or handed to s1 through ev_blocks[c] when
+// `two`).  `last`: nothing follows this chunk on s0, so its final block's
+// reduction runs alone and takes the whole chip (a one-shot grid) instead of
+// the share sized to run beside a GEMM.
 int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0, hipStream_t s1, bool two,
                   hipEvent_t *ev_blocks, bool last) {
   const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
-  // Chunk r's Y: its own rows of Y_ws, or the one chunk-sized Y_ws, which
-  // chunk r+1's GEMM1 may overwrite once chunk r's GEMM2 (earlier on s0) has read it.
-  char *Yr = static_cast<char *>(a->Y_ws) + (pl.y_chunk ? 0 : r * Mr * F * es);
-  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i, Yr, Mr, F, H, H, a->A_ld ? a->A_ld : F, F};
+  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i, chunk_y(a, pl, r), Mr, F, H, H,
+              a->A_ld ? a->A_ld : F, F};
   if (a->H_out) {
     g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
     g1.ldaux = F;
@@ -287,55 +368,24 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
   std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t c = 0; c < pl.C; ++c) {
     const int64_t zoff = r * Mr * H + c * Hc;
-    GemmArgs g2{Yr, static_cast<const char *>(a->B_i) + c * Hc * es,
-                a->Z_i + zoff, Mr, Hc, F, F, H, H};
-    // The block's reduction folds into GEMM2's epilogue where it would run
-    // with nothing beside it anyway (the serial schedule and the final block):
-    // one launch fewer and no second read of the partial just written.
     const bool final_block = last && c + 1 == pl.C;
-    if (pl.reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && (!two || final_block) &&
-        (pl.epi2 == kEpiF32 || pl.epi2 == kEpiPlainF32) && a->P - 1 <= kMaxEpiPeers) {
+    GemmArgs gr{};
+    if (fused_block(a, pl, r, c, two, last, &gr)) {
       const bool f32 = pl.epi2 == kEpiPlainF32;
-      GemmArgs gr = g2;
-      gr.red.np = static_cast<int32_t>(a->P - 1);
-      for (int64_t p = 1; p < a->P; ++p) gr.red.peer[p - 1] = a->peer_partials[p - 1] + zoff;
-      gr.red.nout = 1;
-      gr.red.rows_per_out = static_cast<int32_t>(Mr);
-      bool fits = true;
-      if (a->Z_split) {
-        // Reduce-scattered: the chunk lies in one sequence block, or covers
-        // whole ones (the two nest).
-        const int64_t Ms = pl.sq.Ms, g0 = r * Mr, j0 = g0 / Ms;
-        if (Mr <= Ms) {
-          gr.red.out[0] = a->Z_split[j0] + (g0 - j0 * Ms) * H + c * Hc;
-        } else if (Mr / Ms <= kMaxFusedOuts) {
-          gr.red.nout = static_cast<int32_t>(Mr / Ms);
-          gr.red.rows_per_out = static_cast<int32_t>(Ms);
-          for (int64_t k = 0; k < Mr / Ms; ++k) gr.red.out[k] = a->Z_split[j0 + k] + c * Hc;
-        } else {
-          fits = false;
-        }
-      } else {
-        gr.red.out[0] = a->Z_out ? a->Z_out + zoff : nullptr;
-      }
-      gr.red.bias = a->bias ? a->bias + c * Hc : nullptr;
-      gr.red.lo = a->X_next ? static_cast<char *>(a->X_next) + zoff * es : nullptr;
-      gr.red.lo_bf16 = a->dtype == TP_BF16;
-      if (fits && (f32 ? gemm_red_ok_f32(gr) : gemm_red_ok(gr))) {
-        t0 = timing_begin(s0);
-        e = gemm_launch(gr, f32 ? kEpiPlainF32Red : kEpiF32Red, s0);
-        if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
-        // Memory-bound: its work is bytes (Y rows and B columns, the peers'
-        // blocks and the bias read once, every output written once).
-        const double cells = static_cast<double>(Mr) * Hc;
-        const double bytes = es * (static_cast<double>(Mr) * F + static_cast<double>(F) * Hc) +
-                             4.0 * gr.red.np * cells + (gr.red.out[0] != gr.c ? 4.0 * cells : 0.0) +
-                             (gr.red.out[0] ? 4.0 * cells : 0.0) + (gr.red.lo ? es * cells : 0.0) +
-                             (gr.red.bias ? 4.0 * Hc : 0.0);
-        timing_end(t0, s0, TP_KERNEL_GEMM2_REDUCE, bytes);
-        continue;
-      }
+      t0 = timing_begin(s0);
+      e = gemm_launch(gr, f32 ? kEpiPlainF32Red : kEpiF32Red, s0);
+      if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+      // Memory-bound: its work is bytes (Y rows and B columns, the peers'
+      // blocks and the bias read once, every output written once).
+      const double cells = static_cast<double>(Mr) * Hc;
+      const double bytes = es * (static_cast<double>(Mr) * F + static_cast<double>(F) * Hc) +
+                           4.0 * gr.red.np * cells + (gr.red.out[0] != gr.c ? 4.0 * cells : 0.0) +
+                           (gr.red.out[0] ? 4.0 * cells : 0.0) + (gr.red.lo ? es * cells : 0.0) +
+                           (gr.red.bias ? 4.0 * Hc : 0.0);
+      timing_end(t0, s0, TP_KERNEL_GEMM2_REDUCE, bytes);
+      continue;
     }
+    const GemmArgs g2 = block_gemm2(a, pl, r, c);
     t0 = timing_begin(s0);
     e = gemm_launch(g2, pl.epi2, s0);
     if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
@@ -573,10 +623,11 @@ int tpshard::colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stre
   const int64_t R = pl.R, C = pl.C, Mr = pl.Mr, H = pl.H, es = pl.es;
   const bool gather = pl.gather;
   // The reduce stream only pays when a later block's GEMMs can run beside an
-  // earlier block's reduce or gather; with a single block the hand-off (an
-  // event record and a cross-queue wait, about 10 us each way on MI355X) is
-  // pure latency.
-  const bool two = (s0 != s1) && (pl.reduce || gather) && R * C > 1;
+  // earlier block's reduce or gather; with a single block, or where every
+  // block's reduction goes into GEMM2's epilogue and nothing is gathered
+  // beside, the hand-off (an event record and a cross-queue wait, about 10 us
+  // each way on MI355X) is pure latency.
+  const bool two = (s0 != s1) && R * C > 1 && ((gather && R > 1) || any_block_beside(a, pl, true));
   hipEvent_t *ev = nullptr;
   if (two) {
     if ((rc = get_events(static_cast<size_t>(R * C + R + 2), &ev)) != TP_OK) return rc;
@@ -652,8 +703,11 @@ int tp_colrow_mlp_stack(const tp_mlp_args *layers, int64_t num_layers, tp_stream
   }
   // [DOM] inter-layer overlap: chunk r of layer l+1 needs only chunk r of
   // layer l's reduced output, so the reduction of layer l's later chunks runs
-  // on s_reduce beside layer l+1's GEMMs of the earlier ones.
-  const bool two = (s0 != s1) && any_reduce && any_split;
+  // on s_reduce beside layer l+1's GEMMs of the earlier ones (unless every
+  // block's reduction goes into its GEMM2's epilogue).
+  bool beside = false;
+  for (int64_t l = 0; l < num_layers; ++l) beside = beside || any_block_beside(&layers[l], pl[l], l + 1 == num_layers);
+  const bool two = (s0 != s1) && any_reduce && any_split && beside;
   hipEvent_t *ev = nullptr;
   if (two && (rc = get_events(static_cast<size_t>(nev), &ev)) != TP_OK) return rc;
   hipError_t e;

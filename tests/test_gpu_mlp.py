@@ -526,6 +526,42 @@ def test_timing_files_the_tail_reduction_apart(two_streams):
     assert st["reduce_tail"]["work"] == (4.0 * (P + 1) * (M // Rc) * H if two_streams else 0.0)
 
 
+
+@pytest.mark.parametrize("M,H,F,Rc,Cc,P,beside", [(4096, 2048, 512, 2, 1, 8, 0), (4096, 4096, 6144, 2, 2, 8, 3)])
+def test_two_streams_fold_uncovered_reductions(M, H, F, Rc, Cc, P, beside):
+    """On two streams a block's reduction runs beside the next GEMMs only where
+    they are long enough to cover it; otherwise it goes into its GEMM2's
+    epilogue, and where that leaves nothing for the second stream the schedule
+    keeps to one.  First case: chunk 0's sum of 8 partials (151 MB) against
+    the next chunk's 8.6 GFLOP, so both chunks fold; second: the GPT-3 175B
+    block ratio (F = 6144), three reductions beside and the final one folded.
+    The sums are the same bits as with the separate reduction."""
+    announce(f"mlp uncovered reductions M={M} H={H} F={F} R={Rc} C={Cc} P={P}")
+    X = inputs.normal((M, H), 381, 1.0, "bf16").cuda()
+    A = inputs.normal((H, F), 382, 1.0 / np.sqrt(H), "bf16").cuda()
+    B = inputs.normal((F, H), 383, 1.0 / np.sqrt(F), "bf16").cuda()
+    peers = [inputs.normal((M, H), 390 + p).cuda() for p in range(P - 1)]
+    Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Z, Zo = torch.empty((M, H), device="cuda"), torch.empty((M, H), device="cuda")
+    Z2, Zo2 = torch.empty((M, H), device="cuda"), torch.empty((M, H), device="cuda")
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        tp.tp_colrow_mlp(X, A, B, Y, Z, row_chunks=Rc, col_chunks=Cc, peer_partials=peers, Z_out=Zo,
+                         s_compute=s0, s_reduce=s1)
+        st = tp.tp_timing_read()
+        tp.tp_colrow_mlp(X, A, B, Y, Z2, row_chunks=Rc, col_chunks=Cc, peer_partials=peers, Z_out=Zo2,
+                         s_compute=s0, s_reduce=s1, reduce_fusion=tp.TP_REDUCE_FUSION_OFF)
+        torch.cuda.synchronize()
+    finally:
+        tp.tp_timing_enable(False)
+    assert st["reduce"]["launches"] == beside and st["reduce_tail"]["launches"] == 0
+    assert st["gemm2_reduce"]["launches"] == Rc * Cc - beside
+    assert st["gemm2"]["launches"] == beside
+    assert torch.equal(Zo, Zo2) and torch.equal(Z, Z2)
+
 def test_max_ranks_integer_exact():
     """P = 64 virtual ranks (63 peers), chunked, on two streams: exact."""
     announce("mlp P=64 integer exact")

@@ -336,10 +336,11 @@ typedef struct {
   int32_t reduce_fusion; /* TP_REDUCE_FUSION_AUTO (0): where a block's reduction would
                         run with nothing beside it (the serial schedule, or the final
                         block of the two-stream one), or beside GEMMs too short to
-                        cover it (bf16: its bytes at 6 TB/s take more than 3/4 of the
-                        next block's GEMM2, or of the next chunk's GEMM1 and first
-                        GEMM2, at 1.2 PFLOP/s), GEMM2 adds the peers' partials
-                        and the bias in its epilogue and writes Z_out / X_next itself.
+                        cover it (bf16, tp_colrow_mlp only: its bytes at 6 TB/s take
+                        more than 3/4 of the next block's GEMM2, or of the next
+                        chunk's GEMM1 and first GEMM2, at 1.2 PFLOP/s), GEMM2 adds
+                        the peers' partials and the bias in its epilogue and writes
+                        Z_out / X_next itself.
                         Taken for P <= 4 and Z_out or a Z_split whose chunk spans at
                         most 4 sequence blocks on blocks of fewer than 256 output
                         tiles of 128 x 128 (bf16: 16-byte aligned rows, F a multiple

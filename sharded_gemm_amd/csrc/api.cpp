@@ -292,9 +292,12 @@ GemmArgs block_gemm2(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t
 // cover it: beside them it would slow them by about its own length and still
 // run past them (GPT-3 6.7B at TP = 8, R = 2: 604 MB of reduction beside
 // 137 GFLOP; that step took 417 us on two streams against 388 us with each
-// chunk's sum in GEMM2's epilogue).  The kernel must take the block as well
+// chunk's sum in GEMM2's epilogue).  Only where `weigh`: a stack of layers
+// keeps every reduction it can beside the GEMMs (GPT-3 6.7B, two layers:
+// 866 us so against 884-897 us with each chunk folded, whose epilogue then
+// also writes the next layer's input).  The kernel must take the block as well
 // (gemm_red_ok).
-bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, bool two, bool last,
+bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, bool two, bool last, bool weigh,
                  GemmArgs *gr) {
   const int64_t H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
   const bool f32 = pl.epi2 == kEpiPlainF32;
@@ -303,7 +306,7 @@ bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, 
     return false;
   const bool final_block = last && c + 1 == pl.C;
   if (two && !final_block) {
-    if (f32) return false;
+    if (f32 || !weigh) return false;
     const double next_flops = 2.0 * Mr * F * (c + 1 < pl.C ? Hc : H + Hc);
     const double red_bytes = 4.0 * (a->P + 1) * Mr * Hc;
     if (red_bytes / kReduceByteRate <= kBesideShare * next_flops / kGemmFlopRate) return false;
@@ -338,12 +341,12 @@ bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, 
 
 // Whether any block of the layer hands its reduction to s1 on a two-stream
 // schedule; `last_chunk_last`: nothing follows the layer's last chunk on s0.
-bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_last) {
+bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_last, bool weigh) {
   if (!pl.reduce) return false;
   GemmArgs gr{};
   for (int64_t r = 0; r < pl.R; ++r)
     for (int64_t c = 0; c < pl.C; ++c)
-      if (!fused_block(a, pl, r, c, true, last_chunk_last && r + 1 == pl.R, &gr)) return true;
+      if (!fused_block(a, pl, r, c, true, last_chunk_last && r + 1 == pl.R, weigh, &gr)) return true;
   return false;
 }
 
@@ -351,9 +354,9 @@ bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_l
 // reduction (in GEMM2's epilogue, or handed to s1 through ev_blocks[c] when
 // `two`).  `last`: nothing follows this chunk on s0, so its final block's
 // reduction runs alone and takes the whole chip (a one-shot grid) instead of
-// the share sized to run beside a GEMM.
+// the share sized to run beside a GEMM.  `weigh`: as in fused_block.
 int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0, hipStream_t s1, bool two,
-                  hipEvent_t *ev_blocks, bool last) {
+                  hipEvent_t *ev_blocks, bool last, bool weigh) {
   const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
   GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i, chunk_y(a, pl, r), Mr, F, H, H,
               a->A_ld ? a->A_ld : F, F};
@@ -370,7 +373,7 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     const int64_t zoff = r * Mr * H + c * Hc;
     const bool final_block = last && c + 1 == pl.C;
     GemmArgs gr{};
-    if (fused_block(a, pl, r, c, two, last, &gr)) {
+    if (fused_block(a, pl, r, c, two, last, weigh, &gr)) {
       const bool f32 = pl.epi2 == kEpiPlainF32;
       t0 = timing_begin(s0);
       e = gemm_launch(gr, f32 ? kEpiPlainF32Red : kEpiF32Red, s0);
@@ -627,7 +630,7 @@ int tpshard::colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stre
   // block's reduction goes into GEMM2's epilogue and nothing is gathered
   // beside, the hand-off (an event record and a cross-queue wait, about 10 us
   // each way on MI355X) is pure latency.
-  const bool two = (s0 != s1) && R * C > 1 && ((gather && R > 1) || any_block_beside(a, pl, true));
+  const bool two = (s0 != s1) && R * C > 1 && ((gather && R > 1) || any_block_beside(a, pl, true, true));
   hipEvent_t *ev = nullptr;
   if (two) {
     if ((rc = get_events(static_cast<size_t>(R * C + R + 2), &ev)) != TP_OK) return rc;
@@ -660,7 +663,8 @@ int tpshard::colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stre
     if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
     if (gather && two && r > 0 && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess)
       return hip_fail(e, "hipStreamWaitEvent");
-    if ((rc = enqueue_chunk(a, pl, r, s0, s1, two, two ? ev_red + r * C : nullptr, r + 1 == R)) != TP_OK) return rc;
+    if ((rc = enqueue_chunk(a, pl, r, s0, s1, two, two ? ev_red + r * C : nullptr, r + 1 == R, true)) != TP_OK)
+      return rc;
   }
   if (two) {
     if ((e = hipEventRecord(ev_join, s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -706,7 +710,8 @@ int tp_colrow_mlp_stack(const tp_mlp_args *layers, int64_t num_layers, tp_stream
   // on s_reduce beside layer l+1's GEMMs of the earlier ones (unless every
   // block's reduction goes into its GEMM2's epilogue).
   bool beside = false;
-  for (int64_t l = 0; l < num_layers; ++l) beside = beside || any_block_beside(&layers[l], pl[l], l + 1 == num_layers);
+  for (int64_t l = 0; l < num_layers; ++l)
+    beside = beside || any_block_beside(&layers[l], pl[l], l + 1 == num_layers, false);
   const bool two = (s0 != s1) && any_reduce && any_split && beside;
   hipEvent_t *ev = nullptr;
   if (two && (rc = get_events(static_cast<size_t>(nev), &ev)) != TP_OK) return rc;
@@ -721,7 +726,8 @@ int tp_colrow_mlp_stack(const tp_mlp_args *layers, int64_t num_layers, tp_stream
       if (two && prev_done && (e = hipStreamWaitEvent(s0, prev_done[r], 0)) != hipSuccess)
         return hip_fail(e, "hipStreamWaitEvent");
       const bool last = l + 1 == num_layers && r + 1 == R;
-      if ((rc = enqueue_chunk(&layers[l], pl[l], r, s0, s1, two, two ? blocks + r * pl[l].C : nullptr, last)) != TP_OK)
+      if ((rc = enqueue_chunk(&layers[l], pl[l], r, s0, s1, two, two ? blocks + r * pl[l].C : nullptr, last,
+                              false)) != TP_OK)
         return rc;
       if (two && pl[l].reduce && (e = hipEventRecord(done[r], s1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }

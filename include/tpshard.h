@@ -467,20 +467,20 @@ typedef struct {
                         128 x 128 per chunk (small layers, whose GEMMs are too short
                         for the hand-off to s_reduce to pay); otherwise, and always
                         with TP_REDUCE_FUSION_OFF (1), the reduction runs on
-                        s_reduce beside the weight-gradient GEMMs.  Same bits. */
+                        s_reduce beside the later GEMMs.  Same bits. */
 } tp_mlp_bwd_args;
 
 /*
  * Enqueue the backward of one rank's MLP share ([CAI] section 2.2; [DOM]
  * "backward": each gradient GEMM splits into an input-gradient GEMM and an
- * independent weight-gradient GEMM, so the reduction of one micro-batch's input
- * gradient hides behind that micro-batch's weight-gradient GEMMs).  For each row
- * chunk r, on s_compute: dH[r] = (dZ[r] B_i^T) * act'(H_i[r]) (one GEMM, the
- * derivative applied to its fp32 accumulator), dX_i[r] = dH[r] A_i^T; then, when
- * P > 1, s_reduce waits for chunk r and reduces dX[r] into dX_out while
- * s_compute runs dA_i += X[r]^T dH[r] and dB_i += Y_i[r]^T dZ[r].  The weight
- * gradients continue one fp32 accumulation across chunks (each GEMM starts
- * from the previous chunk's result), so the result does not depend on R.
+ * independent weight-gradient GEMM, so the reduction of an input gradient hides
+ * behind GEMMs that do not depend on it).  For each row chunk r, on s_compute:
+ * dH[r] = (dZ[r] B_i^T) * act'(H_i[r]) (one GEMM, the derivative applied to its
+ * fp32 accumulator), dX_i[r] = dH[r] A_i^T; then, when P > 1, s_reduce waits
+ * for chunk r and reduces dX[r] into dX_out while s_compute moves on to chunk
+ * r+1, and after the last chunk to dA_i (+)= X^T dH and dB_i (+)= Y_i^T dZ over
+ * all M rows, one pass each.  Each weight-gradient element is accumulated over
+ * the rows in the same order whatever R is, so the result does not depend on R.
  * Small layers instead sum dX over the ranks in the dX GEMM's epilogue on
  * s_compute (reduce_fusion), with the same bits.
  * Before returning, s_compute waits for s_reduce.  Capturable into a HIP graph.

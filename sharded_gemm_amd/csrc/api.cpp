@@ -890,31 +890,38 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
                        two ? (a->reduce_workgroups ? a->reduce_workgroups : kReduceBesideGemm) : 0, nullptr);
       if (rc != TP_OK) return rc;
     }
-    // Weight gradients, contracting over this chunk's rows and continuing the
-    // previous chunk's accumulation: dA_i += X[r]^T dH[r], dB_i += Y_i[r]^T dZ[r].
-    const int cont = (r > 0 || a->accumulate) ? 1 : 0;
-    GemmArgs ga{X + r * Mr * H * es, dH + r * Mr * F * es, a->dA_i, H, F, Mr, H, F, F};
+  }
+  // Weight gradients over all rows in one pass each, once every chunk's dH is
+  // there: dA_i (+)= X^T dH, dB_i (+)= Y_i^T dZ.  The same bits as one pass per
+  // chunk continuing the previous chunk's sum (each element is accumulated over
+  // the rows in the same order), without reading and rewriting the fp32
+  // gradients once per further chunk (the 175B shapes: 302 MB each way per
+  // weight and chunk).  The last chunk's dX reduction runs beside them.
+  {
+    const int cont = a->accumulate ? 1 : 0;
+    GemmArgs ga{X, dH, a->dA_i, H, F, M, H, F, F};
     ga.a_t = 1;
     ga.acc_init = cont;
-    GemmArgs gb{Yi + r * Mr * F * es, dZ + r * Mr * H * es, a->dB_i, F, H, Mr, F, H, H};
+    GemmArgs gb{Yi, dZ, a->dB_i, F, H, M, F, H, H};
     gb.a_t = 1;
     gb.acc_init = cont;
     const GemmArgs pair[2] = {ga, gb};
+    hipEvent_t t0;
     if (gemm_group_ok(pair, 2, epi_f32)) {
       // Both too small to fill the chip alone: one grouped launch.
       t0 = timing_begin(s0);
       e = gemm_launch_group(pair, 2, epi_f32, s0);
       if (e != hipSuccess) return hip_fail(e, "dA/dB GEMM launch");
-      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * Mr * 2);
+      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * M * 2);
     } else {
       t0 = timing_begin(s0);
       e = gemm_launch(ga, epi_f32, s0);
       if (e != hipSuccess) return hip_fail(e, "dA GEMM launch");
-      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * Mr);
+      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * H * F * M);
       t0 = timing_begin(s0);
       e = gemm_launch(gb, epi_f32, s0);
       if (e != hipSuccess) return hip_fail(e, "dB GEMM launch");
-      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * F * H * Mr);
+      timing_end(t0, s0, TP_KERNEL_GEMM_WGRAD, 2.0 * F * H * M);
     }
   }
   if (two) {

@@ -84,14 +84,14 @@ def _f64(t):
     (256, 2048, 6144, 1, 2),
     # dH GEMM on the ping-pong kernel with W given transposed (256 x 192)
     (4096, 256, 6144, 2, 2),
-    # every GEMM on the ping-pong kernel's 256 x 128 tiles (dA, dB with A transposed; accumulating for R = 2)
+    # every GEMM on the ping-pong kernel's 256 x 128 tiles (dA, dB with A transposed)
     (4000, 2000, 2000, 1, 2), (4000, 2000, 2000, 2, 2),
-    # dA on 256 x 192 tiles with A transposed, accumulating over two chunks
+    # dA on 256 x 192 tiles with A transposed
     (512, 2048, 6144, 2, 2),
     # dA and dB in one grouped launch, 45 tiles each (the second problem's tiles start off the XCD stride)
     (256, 576, 320, 1, 2),
-    # the same, 32-deep stages (96 tokens per chunk), accumulating over two chunks
-    (192, 576, 320, 2, 2),
+    # the same, 32-deep stages (160 tokens)
+    (160, 576, 320, 2, 2),
 ])
 def test_backward_integer_exact(M, H, F, Rc, P):
     """One-hot A_i (columns) and B_i (rows) keep every value a small integer:
@@ -116,14 +116,22 @@ def test_backward_integer_exact(M, H, F, Rc, P):
         assert np.array_equal(_f64(dXo), R.reduce_full([g["dX_i"]] + [p.double().numpy() for p in peers]))
 
 
-def test_backward_accumulates_weight_gradients():
+@pytest.mark.parametrize("M,H,F,dt", [
+    (512, 384, 256, "bf16"),
+    # the accumulating weight-gradient GEMMs (A transposed) on larger tiles, and
+    # in the grouped launch with 64- and 32-deep stages
+    (4000, 2000, 2000, "bf16"), (512, 2048, 6144, "bf16"), (256, 576, 320, "bf16"), (160, 576, 320, "bf16"),
+    # the fp32 GEMM continuing from C, off its tile sizes
+    (130, 129, 65, "f32"),
+])
+def test_backward_accumulates_weight_gradients(M, H, F, dt):
     """accumulate = 1 continues from the given dA_i, dB_i: exact integers twice over."""
-    announce("backward accumulate")
-    M, H, F = 512, 384, 256
-    X = inputs.small_ints((M, H), seed=421, lo=-4, hi=4, dtype="bf16").cuda()
-    A = _one_hot(H, F, 422).cuda()
-    B = _one_hot(H, F, 423).t().contiguous().cuda()
-    dZ = inputs.small_ints((M, H), seed=424, lo=-4, hi=4, dtype="bf16").cuda()
+    announce(f"backward accumulate M={M} H={H} F={F} {dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    X = inputs.small_ints((M, H), seed=421, lo=-4, hi=4, dtype=dt).cuda()
+    A = _one_hot(H, F, 422).to(tdt).cuda()
+    B = _one_hot(H, F, 423).t().contiguous().to(tdt).cuda()
+    dZ = inputs.small_ints((M, H), seed=424, lo=-4, hi=4, dtype=dt).cuda()
     Y, _ = forward(X, A, B, act=tp.TP_ACT_NONE)
     _, _, _, dA1, dB1 = backward(X, A, B, None, Y, dZ, R=2, act=tp.TP_ACT_NONE)
     _, _, _, dA2, dB2 = backward(X, A, B, None, Y, dZ, R=2, act=tp.TP_ACT_NONE, dA0=dA1.cuda(), dB0=dB1.cuda())
@@ -157,8 +165,8 @@ def test_backward_gelu(M, H, F, Rc, P):
                                         (1, 1, 1, 1, 2)])
 def test_backward_gelu_fp32_ragged(M, H, F, Rc, P):
     """fp32 throughout, sizes off the 32 x 32 tile and the 64-deep k slab: the
-    fused GeLU derivative, transposed operands of the weight gradients and
-    their accumulation over row chunks."""
+    fused GeLU derivative, and the transposed operands of the weight
+    gradients, taken over all rows at once."""
     announce(f"backward gelu fp32 M={M} H={H} F={F} R={Rc} P={P}")
     X = inputs.normal((M, H), 521, 1.0)
     A = inputs.normal((H, F), 522, 1.0 / np.sqrt(H))

@@ -85,7 +85,8 @@ def _device_boxes(shape, spec):
 class MlpStep:
     """Per-rank MLP step, optionally preceded by cutting the weights.  With
     ``seq`` the step is the sequence-parallel form: the input arrives as P
-    sequence blocks that the call all-gathers, and the output is
+    sequence blocks that GEMM1 reads where they lie (or, with gather_input,
+    that the call first all-gathers into X), and the output is
     reduce-scattered into P blocks."""
 
     serial = False
@@ -95,6 +96,9 @@ class MlpStep:
     # torch.distributed.all_reduce does; separate_output keeps Z_i and writes
     # the sum to its own buffer instead.
     separate_output = False
+    # Sequence parallel: all-gather the blocks into X before GEMM1 instead of
+    # letting GEMM1 read them where they lie.
+    gather_input = False
     # With full weights: rank 0 reads its column shard of A in place (a row
     # stride of P*F) and its row shard of B (contiguous rows), as the
     # column-parallel layer uses its shard; cut_weights copies both out of the
@@ -173,7 +177,8 @@ class MlpStep:
                                                      stream=self.s0, prepare=True)
         elif self.split:
             A0, B0 = self.A[:, :self.w.F], self.B[:self.w.F]
-        self.mlp = tp.tp_colrow_mlp(self.X, A0, B0, self.Y, self.Z, row_chunks=self.w.R,
+        X = None if (self.seq and not self.gather_input) else self.X
+        self.mlp = tp.tp_colrow_mlp(X, A0, B0, self.Y, self.Z, row_chunks=self.w.R,
                                     col_chunks=self.w.C, peer_partials=self.peers,
                                     Z_out=None if self.seq else self._z_out(), s_compute=self.s0,
                                     s_reduce=self.s0 if self.serial else self.s1,
@@ -207,7 +212,9 @@ class MlpStep:
                                  "separate buffer" if self.separate_output else "in place over the partial (all-reduce)"),
                "peers": "virtual ranks 1..P-1, partials precomputed by the same path"}
         if self.seq:
-            cfg["sequence_parallel"] = {"blocks": w.P, "input": "all-gathered from P sequence blocks",
+            cfg["sequence_parallel"] = {"blocks": w.P,
+                                        "input": "all-gathered from P sequence blocks" if self.gather_input else
+                                                 "read by GEMM1 from the P sequence blocks where they lie",
                                         "output": "reduce-scattered into P sequence blocks"}
         if self.layouts:
             cfg["layouts_cut_each_step"] = "the 2 x 2 tensor under the " + ", ".join(TINY_LAYOUT_SPECS) + " specs"
@@ -930,9 +937,11 @@ def run_workload(name, steps, warmup, flusher, args, serial_too=True):
         wl.reduce_fusion = tp.TP_REDUCE_FUSION_OFF
     wl.separate_output = args.separate_output
     wl.cut_weights = args.cut_weights
+    wl.gather_input = args.gather_input
     log(f"[bench] workload {name}: timing")
     m = measure(wl, steps, warmup, flusher, profile=args.profile)
-    default_schedule = not (args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output)
+    default_schedule = not (args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output or
+                            args.gather_input)
     summ = {"config": wl.config(), "value": rate(wl, m["ms_per_step"]), "unit": wl.unit,
             "ms_per_step": m["ms_per_step"], "timed_as": m["timed_as"],
             "ms_per_step_eager": m["ms_per_step_eager"], "ms_per_step_graph": m["ms_per_step_graph"],
@@ -990,6 +999,9 @@ def main():
     ap.add_argument("--serial", action="store_true", help="run the reduce on the compute stream")
     ap.add_argument("--separate-output", action="store_true",
                     help="write the reduced output to its own buffer instead of in place over the partial")
+    ap.add_argument("--gather-input", action="store_true",
+                    help="sequence-parallel workloads: all-gather the input blocks into X before GEMM1 instead of "
+                         "reading them in place")
     ap.add_argument("--cut-weights", action="store_true",
                     help="copy rank 0's weight shards out of the full weights each step (workloads with full weights) "
                          "instead of reading them in place")

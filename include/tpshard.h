@@ -289,7 +289,8 @@ typedef struct {
                         the fp32 accumulator of X A_i (the pages never define GeLU;
                         the exact erf form is the reading taken); TP_ACT_NONE */
   int64_t M, H, F;   /* X[M,H], A_i[H,F], B_i[F,H]; all >= 1 */
-  const void *X;     /* [M, H] row-major, replicated input of every rank */
+  const void *X;     /* [M, H] row-major, replicated input of every rank (NULL only
+                        with X_shards, below) */
   const void *A_i;   /* [H, F] row-major: this rank's column slice of A ([CAI] section 2) */
   const void *B_i;   /* [F, H] row-major: this rank's row slice of B ([CAI] section 2.1) */
   void *Y_ws;        /* [M, F] caller-owned workspace; on completion holds
@@ -326,7 +327,13 @@ typedef struct {
                         (dtype): sequence block j of the input.  When set the call
                         all-gathers them into X, which is then a caller-owned
                         [M, H] workspace the call writes, chunk r on s_reduce before
-                        chunk r's first GEMM on s_compute reads it */
+                        chunk r's first GEMM on s_compute reads it; or X is NULL and
+                        GEMM1 reads the blocks where they lie (the all-gather folded
+                        into its operand loads; nothing is gathered).  That needs
+                        each row chunk inside one block, or, where a chunk spans
+                        blocks, bf16, 16-byte aligned blocks of a multiple of 256
+                        rows, at most 8 per chunk, H a multiple of 32 (else
+                        TP_ERR_UNSUPPORTED) */
   float *const *Z_split; /* optional host array of S device pointers, each [M/S, H] fp32:
                         the reduce-scattered output, block j = rows [j*M/S, (j+1)*M/S)
                         of Z_i + peers (+ bias).  Replaces Z_out, which must be NULL. */

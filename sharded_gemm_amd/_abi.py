@@ -493,8 +493,18 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
 def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
               act=TP_ACT_GELU_ERF, reduce_workgroups=0, H_out=None, bias=None, X_shards=None, Z_split=None,
               X_next=None, reduce_fusion=TP_REDUCE_FUSION_AUTO):
-    """(tp_mlp_args, keep-alive list) for one forward layer, shapes checked."""
-    M, H = int(X.shape[0]), int(X.shape[1])
+    """(tp_mlp_args, keep-alive list) for one forward layer, shapes checked.
+    X may be None with X_shards: GEMM1 then reads the blocks where they lie."""
+    if X is None:
+        if not X_shards:
+            raise ValueError("X may be None only with X_shards")
+        X_shards = list(X_shards)
+        x0 = X_shards[0]
+        if not hasattr(x0, "data_ptr") or x0.dim() != 2:
+            raise TypeError("every X_shards block must be a 2-D tensor")
+        M, H, xref = int(x0.shape[0]) * len(X_shards), int(x0.shape[1]), x0
+    else:
+        M, H, xref = int(X.shape[0]), int(X.shape[1]), X
     F = int(A_i.shape[1])
     peers = list(peer_partials)
     # A_i may be a column slice of the full A (rows contiguous, a row stride of
@@ -507,10 +517,10 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
     if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Z_i.shape) != (M, H) \
             or (Y_ws is not None and tuple(Y_ws.shape) != (M, F)):
         raise ValueError("shapes must be X[M,H], A_i[H,F], B_i[F,H], Y_ws[M,F], Z_i[M,H]")
-    if not (X.dtype == A_i.dtype == B_i.dtype) or (Y_ws is not None and Y_ws.dtype != X.dtype):
+    if not (xref.dtype == A_i.dtype == B_i.dtype) or (Y_ws is not None and Y_ws.dtype != xref.dtype):
         raise TypeError("X, A_i, B_i and Y_ws must share one dtype")
     for t in (H_out, X_next):
-        if t is not None and t.dtype != X.dtype:
+        if t is not None and t.dtype != xref.dtype:
             raise TypeError("H_out and X_next are in the input dtype")
     if H_out is not None and tuple(H_out.shape) != (M, F):
         raise ValueError("H_out must be [M, F]")
@@ -521,9 +531,9 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
         if t.dtype != torch.float32 or tuple(t.shape) != (M, H):
             raise TypeError("Z_i, peer partials and Z_out must be fp32 [M, H]")
     _check_bias(bias, H)
-    S, xs, zs = _seq_arrays(X_shards, Z_split, M, H, X.dtype, "X_shards", "Z_split")
+    S, xs, zs = _seq_arrays(X_shards, Z_split, M, H, xref.dtype, "X_shards", "Z_split")
     parr = (C.c_void_p * max(1, len(peers)))(*[_ptr(p) for p in peers])
-    args = tp_mlp_args(dtype=_dtype_code(X), act=act, M=M, H=H, F=F,
+    args = tp_mlp_args(dtype=_dtype_code(xref), act=act, M=M, H=H, F=F,
                        X=_ptr(X), A_i=A_i.data_ptr(), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
@@ -542,7 +552,8 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, prep
     bias, X_shards, Z_split, X_next, reduce_fusion (TP_REDUCE_FUSION_AUTO lets GEMM2's
     epilogue take the reduction where nothing would run beside it; TP_REDUCE_FUSION_OFF
     keeps the separate reduction kernel; same bits either way).  Sequence parallelism: with ``X_shards`` (S tensors
-    [M/S, H]) X is a workspace the call fills by all-gathering them; with ``Z_split``
+    [M/S, H]) X is a workspace the call fills by all-gathering them, or None: GEMM1 then reads the blocks where
+    they lie (the all-gather folded into its operand loads; X is not written); with ``Z_split``
     (S tensors [M/S, H] fp32) the sum is reduce-scattered into the blocks instead of
     written to Z_out.  With ``prepare=True`` nothing runs; a ``Prepared`` call taking
     (s_compute, s_reduce) is returned."""

@@ -182,11 +182,43 @@ int reduce_rows(const float *const *parts, int64_t P, int64_t r0, int64_t rows, 
 struct MlpPlan {
   int64_t es = 0, M = 0, H = 0, F = 0, R = 1, C = 1, Mr = 0, Hc = 0;
   bool gather = false, reduce = false;
+  // X is NULL and GEMM1 reads the sequence blocks X_shards where they lie.
+  bool x_in_place = false;
   // Y_ws holds one row chunk ([M/R, F]) that every chunk reuses in turn.
   bool y_chunk = false;
   int epi1 = 0, epi2 = 0;
   SeqSplit sq;
 };
+
+// Chunk r's Y: its own rows of Y_ws, or the one chunk-sized Y_ws, which
+// chunk r+1's GEMM1 may overwrite once chunk r's GEMM2 (earlier on s0) has read it.
+char *chunk_y(const tp_mlp_args *a, const MlpPlan& pl, int64_t r) {
+  return static_cast<char *>(a->Y_ws) + (pl.y_chunk ? 0 : r * pl.Mr * pl.F * pl.es);
+}
+
+// GEMM1 of row chunk r: Y[r] = act(X[r] A_i).  X[r] is rows of X, or, with X
+// NULL, the sequence blocks where they lie: at an offset into the one block
+// that holds the chunk, or the chunk's blocks as A's row blocks.
+GemmArgs chunk_gemm1(const tp_mlp_args *a, const MlpPlan& pl, int64_t r) {
+  const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr;
+  GemmArgs g1{nullptr, a->A_i, chunk_y(a, pl, r), Mr, F, H, H, a->A_ld ? a->A_ld : F, F};
+  if (!pl.x_in_place) {
+    g1.a = static_cast<const char *>(a->X) + r * Mr * H * es;
+  } else {
+    const int64_t Ms = pl.sq.Ms, g0 = r * Mr, j0 = g0 / Ms;
+    if (Mr <= Ms) {
+      g1.a = static_cast<const char *>(a->X_shards[j0]) + (g0 - j0 * Ms) * H * es;
+    } else {
+      g1.a_blk_rows = Ms;
+      for (int64_t k = 0; k < Mr / Ms && k < kMaxABlocks; ++k) g1.a_blk[k] = a->X_shards[j0 + k];
+    }
+  }
+  if (a->H_out) {
+    g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
+    g1.ldaux = F;
+  }
+  return g1;
+}
 
 int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   if (!a) return fail(TP_ERR_ARG, "args is NULL");
@@ -194,7 +226,9 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   if (!es) return fail(TP_ERR_ARG, "unknown dtype %d", a->dtype);
   if (a->act != TP_ACT_NONE && a->act != TP_ACT_GELU_ERF) return fail(TP_ERR_ARG, "unknown act %d", a->act);
   if (a->M < 1 || a->H < 1 || a->F < 1) return fail(TP_ERR_ARG, "M, H, F must be >= 1");
-  if (!a->X || !a->A_i || !a->B_i || !a->Z_i) return fail(TP_ERR_ARG, "X, A_i, B_i and Z_i must be non-NULL");
+  if (!a->A_i || !a->B_i || !a->Z_i) return fail(TP_ERR_ARG, "A_i, B_i and Z_i must be non-NULL");
+  if (!a->X && !a->X_shards)
+    return fail(TP_ERR_ARG, "X must be non-NULL (or NULL with X_shards: GEMM1 then reads the blocks where they lie)");
   if (y_chunk && a->Y_ws) return fail(TP_ERR_ARG, "Y_ws must be NULL: this entry point keeps Y in its own scratch");
   if (!y_chunk && !a->Y_ws) return fail(TP_ERR_ARG, "Y_ws must be non-NULL");
   if (a->row_chunks < 1 || a->col_chunks < 1) return fail(TP_ERR_ARG, "row_chunks and col_chunks must be >= 1");
@@ -220,14 +254,14 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   const int64_t lda_w = a->A_ld ? a->A_ld : F;
   if (lda_w >= (int64_t(1) << 31)) return fail(TP_ERR_UNSUPPORTED, "A_ld exceeds the 32-bit index range of the kernels");
   const int64_t bx = M * H * es, ba = matrix_bytes(H, F, lda_w, es), bb = F * H * es, by = M * F * es, bz = M * H * 4;
-  const bool gather = a->X_shards != nullptr;
+  const bool gather = a->X_shards != nullptr && a->X;
   std::vector<Buf> ins = {{a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
   // (The library's own scratch, which replaces Y_ws when y_chunk, is disjoint
   // from every caller buffer.)
   std::vector<Buf> outs = {{a->Z_i, bz, "Z_i"}};
   if (!y_chunk) outs.push_back({a->Y_ws, by, "Y_ws"});
-  (gather ? outs : ins).push_back({a->X, bx, "X"});
-  if (gather) {
+  if (a->X) (gather ? outs : ins).push_back({a->X, bx, "X"});
+  if (a->X_shards) {
     for (int64_t j = 0; j < sq.S; ++j) {
       if (!a->X_shards[j]) return fail(TP_ERR_ARG, "X_shards[%lld] is NULL", (long long)j);
       ins.push_back({a->X_shards[j], sq.Ms * H * es, "X shard"});
@@ -267,13 +301,22 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   pl->epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveBf16 : kEpiGeluBf16) : kEpiIdentBf16)
                   : (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveF32 : kEpiGeluF32) : kEpiPlainF32);
   pl->epi2 = bf16 ? kEpiF32 : kEpiPlainF32;
+  pl->x_in_place = !a->X;
+  if (pl->x_in_place) {
+    // A row chunk inside one block is read at an offset; one that spans
+    // blocks needs them as whole tiles' worth of rows on the DMA paths.
+    for (int64_t r = 0; r < pl->R; ++r) {
+      const GemmArgs g1 = chunk_gemm1(a, *pl, r);
+      if (g1.a_blk_rows == 0) continue;
+      if (pl->Mr / sq.Ms > kMaxABlocks || !gemm_blocks_ok(g1, pl->epi1))
+        return fail(TP_ERR_UNSUPPORTED,
+                    "X = NULL: row chunks of %lld rows span sequence blocks of %lld rows, which GEMM1 reads in place "
+                    "only for bf16, 16-byte aligned blocks of a multiple of 256 rows, at most %d per chunk, and "
+                    "H a multiple of 32",
+                    (long long)pl->Mr, (long long)sq.Ms, kMaxABlocks);
+    }
+  }
   return TP_OK;
-}
-
-// Chunk r's Y: its own rows of Y_ws, or the one chunk-sized Y_ws, which
-// chunk r+1's GEMM1 may overwrite once chunk r's GEMM2 (earlier on s0) has read it.
-char *chunk_y(const tp_mlp_args *a, const MlpPlan& pl, int64_t r) {
-  return static_cast<char *>(a->Y_ws) + (pl.y_chunk ? 0 : r * pl.Mr * pl.F * pl.es);
 }
 
 // GEMM2 of block (r, c): Z_i[r, c] = Y[r] B_i[:, c].
@@ -358,12 +401,7 @@ bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_l
 int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0, hipStream_t s1, bool two,
                   hipEvent_t *ev_blocks, bool last, bool weigh) {
   const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
-  GemmArgs g1{static_cast<const char *>(a->X) + r * Mr * H * es, a->A_i, chunk_y(a, pl, r), Mr, F, H, H,
-              a->A_ld ? a->A_ld : F, F};
-  if (a->H_out) {
-    g1.aux = static_cast<char *>(a->H_out) + r * Mr * F * es;
-    g1.ldaux = F;
-  }
+  const GemmArgs g1 = chunk_gemm1(a, pl, r);
   hipEvent_t t0 = timing_begin(s0);
   hipError_t e = gemm_launch(g1, pl.epi1, s0);
   if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");

@@ -36,6 +36,10 @@ struct EpiReduce {
   int32_t rows_per_out;        // rows of each output when nout > 1
 };
 
+// A (not transposed) may come as row blocks held apart, e.g. the sequence
+// blocks of an all-gathered input read where they lie.
+constexpr int kMaxABlocks = 8;
+
 struct GemmArgs {
   const void *a;
   const void *w;
@@ -52,6 +56,12 @@ struct GemmArgs {
   int acc_init = 0;
   // kEpiF32Red only.
   EpiReduce red{};
+  // a_blk_rows > 0: A's rows [j * a_blk_rows, (j + 1) * a_blk_rows) are the
+  // rows of a_blk[j] ([a_blk_rows][lda] each) and `a` is unused.  DMA paths
+  // only, A not transposed, a_blk_rows a multiple of 256 so that no tile
+  // straddles two blocks (gemm_blocks_ok).
+  const void *a_blk[kMaxABlocks] = {};
+  int64_t a_blk_rows = 0;
 };
 
 enum {
@@ -88,6 +98,11 @@ bool gemm_red_ok_f32(const GemmArgs& p);
 // that would each leave CUs idle.  gemm_launch_group returns
 // hipErrorInvalidValue otherwise.
 bool gemm_group_ok(const GemmArgs *ps, int n, int epi);
+// Whether gemm_launch takes p's A as row blocks (a_blk_rows > 0) with epilogue
+// epi: bf16 operands on the DMA paths (16-byte aligned blocks and rows, K a
+// multiple of 32), A not transposed, a_blk_rows a multiple of 256, at most
+// kMaxABlocks blocks.
+bool gemm_blocks_ok(const GemmArgs& p, int epi);
 hipError_t gemm_launch_group(const GemmArgs *ps, int n, int epi, hipStream_t s);
 
 }  // namespace tpshard

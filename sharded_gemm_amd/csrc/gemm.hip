@@ -267,6 +267,23 @@ __device__ __forceinline__ void tile_coords(int bid, int ntiles, int tiles_m, in
   *tn = local / gm;
 }
 
+// The part of A that holds the tile whose first row is m0: its base, the
+// tile's first row within it and the rows it has (A itself, unless A comes as
+// row blocks, none of which a tile straddles).  Wave-uniform.
+struct APart {
+  const void *base;
+  int64_t row0, rows;
+};
+__device__ __forceinline__ APart a_part(const GemmArgs& p, int64_t m0) {
+  if (p.a_blk_rows == 0) return {p.a, m0, p.M};
+  const int64_t j = m0 / p.a_blk_rows, first = j * p.a_blk_rows;
+  const void *base = p.a_blk[0];
+#pragma unroll
+  for (int q = 1; q < kMaxABlocks; ++q)
+    if (j == q) base = p.a_blk[q];
+  return {base, m0 - first, p.M - first < p.a_blk_rows ? p.M - first : p.a_blk_rows};
+}
+
 // ---- ragged path: register-staged, bounds-checked ------------------------
 // LDS holds, per stage, X rows [m][k] and W columns [n][k] (k contiguous, 64
 // bf16 per row, chunk c of row r at chunk position c ^ swz(r)).
@@ -600,7 +617,8 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, int bid) {
   tile_coords(bid, tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TP_LDS char *)smem));
-  const uint16_t *A = static_cast<const uint16_t *>(p.a);
+  const APart ap = a_part(p, m0);
+  const uint16_t *A = static_cast<const uint16_t *>(ap.base);
   const uint16_t *W = static_cast<const uint16_t *>(p.w);
   // The output stride is only used after the main loop; left to the compiler
   // its scalar load would still be in flight when the loop starts, and since
@@ -615,7 +633,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, int bid) {
   // slot) is never issued.
   int64_t a_src[C::A_PW], w_src[C::W_PW];
 #pragma unroll
-  for (int q = 0; q < C::A_PW; ++q) a_src[q] = TA::src(wave * C::A_PW + q, lane, m0, p.M, p.lda);
+  for (int q = 0; q < C::A_PW; ++q) a_src[q] = TA::src(wave * C::A_PW + q, lane, ap.row0, ap.rows, p.lda);
 #pragma unroll
   for (int q = 0; q < C::W_PW; ++q)
     w_src[q] = TW::src(min(wave + q * C::NW, TW::PIECES - 1), lane, n0, p.N, p.ldw);
@@ -887,9 +905,10 @@ __global__ void __launch_bounds__(512, 1) bf16_gemm_pps(GemmArgs p) {
   // spill the 256 x 256 tile's accumulators.
   const uint32_t step = static_cast<uint32_t>((grpA ? TA::step(p.lda) : TW::step(p.ldw)) * 2);
   // Piece q of the tile of stage `st` (source) into the slot of stage `slot_st`.
+  const APart ap = a_part(p, m0);
   auto dma_a = [&](int q, int st, int slot_st) {
-    const uint32_t src = static_cast<uint32_t>(TA::src((wave & 3) * A_PW + q, lane, m0, p.M, p.lda) * 2);
-    lds_dma16_s(p.a, src + st * step, lds0 + (slot_st % SA) * TA::BYTES + ((wave & 3) * A_PW + q) * 1024);
+    const uint32_t src = static_cast<uint32_t>(TA::src((wave & 3) * A_PW + q, lane, ap.row0, ap.rows, p.lda) * 2);
+    lds_dma16_s(ap.base, src + st * step, lds0 + (slot_st % SA) * TA::BYTES + ((wave & 3) * A_PW + q) * 1024);
   };
   auto dma_w = [&](int q, int st, int slot_st) {
     const uint32_t src = static_cast<uint32_t>(TW::src((wave & 3) * W_PW + q, lane, n0, p.N, p.ldw) * 2);
@@ -1316,6 +1335,7 @@ bool gemm_vec_ok(const GemmArgs& p, int64_t out_esize, bool uses_aux) {
 
 hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (p.a_blk_rows && !gemm_blocks_ok(p, epi_in)) return hipErrorInvalidValue;
   int epi = epi_in;
   const bool fp32 = epi == kEpiGeluF32 || epi == kEpiPlainF32 || epi == kEpiGeluSaveF32 || epi == kEpiDGeluF32 ||
                     epi == kEpiPlainF32Red;
@@ -1401,6 +1421,18 @@ bool gemm_red_ok(const GemmArgs& p) {
   }
   if (r.lo) ok = ok && (reinterpret_cast<uintptr_t>(r.lo) & (r.lo_bf16 ? 7u : 15u)) == 0;
   return ok;
+}
+
+bool gemm_blocks_ok(const GemmArgs& p, int epi) {
+  if (p.a_blk_rows <= 0 || p.a_blk_rows % 256 != 0 || p.a_t || p.M <= 0 || p.K <= 0 || p.K % 32 != 0) return false;
+  if (epi != kEpiGeluBf16 && epi != kEpiIdentBf16 && epi != kEpiF32 && epi != kEpiGeluSaveBf16 && epi != kEpiF32Red)
+    return false;
+  const int64_t nblk = (p.M + p.a_blk_rows - 1) / p.a_blk_rows;
+  if (nblk > kMaxABlocks) return false;
+  for (int64_t j = 0; j < nblk; ++j)
+    if (!p.a_blk[j] || !aligned16(p.a_blk[j])) return false;
+  const int64_t out_esize = epi == kEpiF32 || epi == kEpiF32Red ? 4 : 2;
+  return gemm_vec_ok(p, out_esize, epi == kEpiGeluSaveBf16);
 }
 
 bool gemm_red_ok_f32(const GemmArgs& p) {

@@ -5,6 +5,7 @@
 // inside one allocation the test registered, and aborts otherwise, so the
 // scheduler's pointer arithmetic is verified for every call it makes.
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -58,7 +59,15 @@ hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const int64_t in_es = f32_epi(epi) ? 4 : 2;
   const bool out_f32 = f32_epi(epi) || epi == kEpiF32 || epi == kEpiF32Red;
-  if (p.a_t) need(p.a, p.K, p.M, p.lda, in_es, "GEMM A^T"); else need(p.a, p.M, p.K, p.lda, in_es, "GEMM A");
+  if (p.a_blk_rows > 0) {
+    if (!gemm_blocks_ok(p, epi)) return hipErrorInvalidValue;
+    for (int64_t j = 0; j * p.a_blk_rows < p.M; ++j)
+      need(p.a_blk[j], std::min(p.a_blk_rows, p.M - j * p.a_blk_rows), p.K, p.lda, in_es, "GEMM A block");
+  } else if (p.a_t) {
+    need(p.a, p.K, p.M, p.lda, in_es, "GEMM A^T");
+  } else {
+    need(p.a, p.M, p.K, p.lda, in_es, "GEMM A");
+  }
   if (p.w_t) need(p.w, p.N, p.K, p.ldw, in_es, "GEMM W^T"); else need(p.w, p.K, p.N, p.ldw, in_es, "GEMM W");
   need(p.c, p.M, p.N, p.ldc, out_f32 ? 4 : 2, "GEMM C");
   if (epi == kEpiGeluSaveBf16 || epi == kEpiDGeluBf16) need(p.aux, p.M, p.N, p.ldaux, 2, "GEMM aux");
@@ -92,6 +101,16 @@ bool gemm_red_ok(const GemmArgs& p) {
 bool gemm_red_ok_f32(const GemmArgs& p) {
   return !p.a_t && !p.w_t && !p.acc_init && p.red.np >= 0 && p.red.np <= kMaxFusedPeers && p.red.nout >= 1 &&
          p.red.nout <= kMaxFusedOuts && (p.red.nout == 1 || (!p.red.lo && p.red.rows_per_out * p.red.nout == p.M));
+}
+bool gemm_blocks_ok(const GemmArgs& p, int epi) {
+  if (p.a_blk_rows <= 0 || p.a_blk_rows % 256 != 0 || p.a_t || p.K % 32 != 0 || p.K <= 0) return false;
+  if (epi != kEpiGeluBf16 && epi != kEpiIdentBf16 && epi != kEpiF32 && epi != kEpiGeluSaveBf16 && epi != kEpiF32Red)
+    return false;
+  const int64_t nblk = (p.M + p.a_blk_rows - 1) / p.a_blk_rows;
+  if (nblk > kMaxABlocks) return false;
+  for (int64_t j = 0; j < nblk; ++j)
+    if (!p.a_blk[j]) return false;
+  return true;
 }
 bool gemm_group_ok(const GemmArgs *ps, int n, int epi) {
   if (n < 1 || n > 4 || epi != kEpiF32) return false;

@@ -386,6 +386,10 @@ def test_sequence_parallel_validation():
     assert fwd(seq_splits=4, Z_split=_ptrs([zs[0], zs[0] + 64, zs[2], zs[3]])) == _abi.TP_ERR_ARG   # blocks overlap
     # 24 rows: chunks of 8 (R = 3) and sequence blocks of 6 (S = 4) do not nest
     assert fwd(M=24, seq_splits=4, row_chunks=3, X_shards=_ptrs(xs)) == _abi.TP_ERR_UNSUPPORTED
+    # X = NULL: GEMM1 would read the blocks in place, but a 64-row chunk over
+    # blocks of 16 rows would put one tile across several blocks
+    assert fwd(X=None, seq_splits=4, X_shards=_ptrs(xs)) == _abi.TP_ERR_UNSUPPORTED
+    assert fwd(X=None, seq_splits=4, X_shards=_ptrs([xs[0], None, xs[2], xs[3]])) == _abi.TP_ERR_ARG
 
     def bwd(**kw):
         return lib.tp_colrow_mlp_backward(C.byref(_bwd_args(**kw)), None, None)
@@ -477,6 +481,11 @@ def test_binding_checks_sequence_blocks_and_bias():
         fwd(X_shards=[x.float() for x in xs])                            # not X's dtype
     with pytest.raises(ValueError):
         fwd(X_shards=xs, Z_split=zs[:2])                                 # counts differ
+    with pytest.raises(ValueError):
+        tp.tp_colrow_mlp(None, A, B, Y, Z)                               # X = None needs X_shards
+    with pytest.raises(tp.TpError) as e:                                 # read in place: blocks of 16 rows
+        tp.tp_colrow_mlp(None, A, B, Y, Z, X_shards=xs, s_compute=0, s_reduce=0)
+    assert e.value.kind == "unsupported"
     with pytest.raises(TypeError):
         fwd(Z_out=torch.zeros((M, H)), bias=torch.zeros(H, dtype=torch.bfloat16))
     with pytest.raises(ValueError):

@@ -37,9 +37,10 @@ def _f64(t):
 
 
 def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bias=None, two_streams=True,
-               fusion=tp.TP_REDUCE_FUSION_AUTO):
+               fusion=tp.TP_REDUCE_FUSION_AUTO, in_place=False):
     """tp_colrow_mlp with X_shards and Z_split into guarded buffers; returns CPU
-    copies (X gathered, Y, Z_i, [Z blocks])."""
+    copies (X gathered, Y, Z_i, [Z blocks]).  in_place: X = None, GEMM1 reads
+    the blocks where they lie (the returned X is then the untouched workspace)."""
     S = len(X_blocks)
     Ms, H = X_blocks[0].shape
     M, F = Ms * S, A.shape[1]
@@ -49,12 +50,15 @@ def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bia
     Zs = [Guarded((Ms, H), torch.float32) for _ in range(S)]
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream() if two_streams else s0
-    tp.tp_colrow_mlp(Xw.t, A, B, Y.t, Z.t, row_chunks=Rc, col_chunks=Cc, peer_partials=list(peers), act=act,
+    tp.tp_colrow_mlp(None if in_place else Xw.t, A, B, Y.t, Z.t, row_chunks=Rc, col_chunks=Cc,
+                     peer_partials=list(peers), act=act,
                      s_compute=s0, s_reduce=s1, bias=bias, X_shards=list(X_blocks), Z_split=[g.t for g in Zs],
                      reduce_fusion=fusion)
     torch.cuda.synchronize()
     for g in [Xw, Y, Z] + Zs:
         assert g.guards_intact(), "write outside an output buffer"
+    if in_place:
+        assert Xw.body_untouched(), "X = None: nothing is gathered"
     return Xw.t.cpu(), Y.t.cpu(), Z.t.cpu(), [g.t.cpu() for g in Zs]
 
 
@@ -116,6 +120,52 @@ def test_forward_reduce_fusion_same_bits(M, H, F, Rc, Cc, P, S):
     for j in range(S):
         assert np.array_equal(bits(got[3][j]), bits(ref[3][j])), j
 
+
+
+@pytest.mark.parametrize("M,H,F,Rc,Cc,P,S,dt", [
+    (1024, 384, 256, 2, 1, 4, 2, "bf16"),     # each row chunk inside one block: read at an offset
+    (2048, 512, 256, 1, 1, 4, 4, "bf16"),     # a chunk over 4 blocks of 512 rows, small tiles
+    (4096, 768, 768, 1, 1, 4, 4, "bf16"),     # GPT-2-small shape
+    (4096, 1024, 2048, 2, 1, 8, 8, "bf16"),   # chunks over 4 blocks each, the 256-row tiles
+    (3072, 512, 1536, 1, 2, 2, 4, "bf16"),    # 768-row blocks, the 256-row tiles, two column blocks
+    (1030, 640, 320, 2, 1, 3, 2, "bf16"),     # ragged rows inside one block each
+    (256, 96, 64, 4, 1, 2, 2, "f32"),         # fp32, chunks inside blocks
+])
+def test_forward_blocks_read_in_place_same_bits(M, H, F, Rc, Cc, P, S, dt):
+    """With X = None GEMM1 reads the sequence blocks where they lie instead of
+    gathering them first: the same Y, Z_i and reduce-scattered sum, bit for bit."""
+    announce(f"seqpar blocks in place M={M} H={H} F={F} R={Rc} C={Cc} P={P} S={S} {dt}")
+    Ms = M // S
+    Xb = [inputs.normal((Ms, H), seed=880 + j, dtype=dt).cuda() for j in range(S)]
+    A = inputs.normal((H, F), seed=890, std=0.05, dtype=dt).cuda()
+    B = inputs.normal((F, H), seed=891, std=0.05, dtype=dt).cuda()
+    peers = [inputs.normal((M, H), seed=895 + p).cuda() for p in range(P - 1)]
+    kw = dict(Rc=Rc, Cc=Cc)
+    got = sp_forward(Xb, A, B, peers, in_place=True, **kw)
+    ref = sp_forward(Xb, A, B, peers, **kw)
+    for a, b in zip(got[1:3], ref[1:3]):
+        assert np.array_equal(bits(a), bits(b))
+    for j in range(S):
+        assert np.array_equal(bits(got[3][j]), bits(ref[3][j])), j
+
+
+def test_forward_blocks_in_place_rejects_blocks_off_the_tile():
+    """A row chunk over blocks of 128 rows cannot be read in place (a 256-row
+    tile would straddle two blocks): rejected before any launch."""
+    announce("seqpar blocks in place, rejected")
+    M, H, F, S = 1024, 256, 128, 8
+    Xb = [torch.zeros((M // S, H), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    A = torch.zeros((H, F), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((F, H), dtype=torch.bfloat16, device="cuda")
+    Y = Guarded((M, F), torch.bfloat16)
+    Z = Guarded((M, H), torch.float32)
+    Zs = [Guarded((M // S, H), torch.float32) for _ in range(S)]
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_colrow_mlp(None, A, B, Y.t, Z.t, X_shards=Xb, Z_split=[g.t for g in Zs])
+    assert e.value.kind == "unsupported"
+    torch.cuda.synchronize()
+    for g in [Y, Z] + Zs:
+        assert g.body_untouched() and g.guards_intact()
 
 def test_forward_gelu_matches_unsplit_path_bitwise():
     """GeLU on random bf16 inputs: the sequence-parallel call gives the same bits

@@ -832,13 +832,20 @@ def measure(wl, steps, warmup, flusher, kernel_tables=True, profile=False):
     # warm-up steps come after the capture, right before the timed ones: the
     # capture leaves the GPU idle for a while, and the first 5-10 ms of work
     # after an idle spell run up to 10% slower (MI355X: 175B step 1,343 against
-    # 1,145 us over the first ten steps after 2 s idle).
+    # 1,145 us over the first ten steps after 2 s idle; once GPT-2's 20 timed
+    # steps came out at 84 us each against 28).
     wl.step()
     torch.cuda.synchronize()
     graph = capture(wl)
-    for _ in range(warmup):
-        wl.step()
-    torch.cuda.synchronize()
+    # W steps, repeated until they have kept the GPU busy for 20 ms: a short
+    # step (GPT-2's 28 us) would otherwise be timed inside that ramp.
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(warmup):
+            wl.step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= 0.02 or warmup == 0:
+            break
     s0 = wl.s0
 
     def one(use_graph):

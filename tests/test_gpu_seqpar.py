@@ -240,14 +240,16 @@ def _chunk_rows(M, Rc, per_chunk):
     return np.array(rows)
 
 
-def test_forward_gpt3_175b_sampled():
+@pytest.mark.parametrize("in_place", [True, False])
+def test_forward_gpt3_175b_sampled(in_place):
     """The GPT-3 175B per-rank shape as the bench's sequence-parallel step runs
-    it (TP = 8: 8 sequence blocks, R = 2, C = 2, two streams): the gathered
-    input equals the blocks, and 128 rows of the reduce-scattered output (64
+    it (TP = 8: 8 sequence blocks, R = 2, C = 2, two streams; GEMM1 reading the
+    blocks where they lie, or after gathering them, when the gathered input
+    must equal the blocks), and 128 rows of the reduce-scattered output (64
     per row chunk, each chunk's first and last among them) match the oracle's
     rank-0 rows plus the drawn peers' rows."""
     w = GPT3_175B
-    announce(f"seqpar forward {w.name} sampled")
+    announce(f"seqpar forward {w.name} sampled in_place={in_place}")
     M, H, F, P, S = w.M, w.H, w.F, w.P, w.P
     Ms = M // S
     Xb = [inputs.normal((Ms, H), inputs.seed_for(w.cfg, inputs.SLOT_X) + 100 * j, 1.0, "bf16", "cuda")
@@ -256,9 +258,10 @@ def test_forward_gpt3_175b_sampled():
     B = inputs.normal((F, H), inputs.seed_for(w.cfg, inputs.SLOT_B), 0.02, "bf16", "cuda")
     peers = [inputs.normal((M, H), inputs.seed_for(w.cfg, inputs.SLOT_PARTIAL + p), 1.0, "f32", "cuda")
              for p in range(P - 1)]
-    Xg, Y, Z, Zs = sp_forward(Xb, A, B, peers, Rc=w.R, Cc=w.C)
+    Xg, Y, Z, Zs = sp_forward(Xb, A, B, peers, Rc=w.R, Cc=w.C, in_place=in_place)
     X = torch.cat([x.cpu() for x in Xb])
-    assert np.array_equal(bits(Xg), bits(X))
+    if not in_place:
+        assert np.array_equal(bits(Xg), bits(X))
     rows = _chunk_rows(M, w.R, 64)
     announce(f"seqpar forward {w.name}: oracle on {len(rows)} rows")
     z0 = O.mlp_rank_rows(X, A.cpu(), B.cpu(), rows)

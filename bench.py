@@ -104,6 +104,10 @@ class MlpStep:
     # column-parallel layer uses its shard; cut_weights copies both out of the
     # full weights at every step instead (one batched layout launch).
     cut_weights = False
+    # Rank 0's weights in a linear layer's [out, in] layout (the same values,
+    # transposed once at set-up): A_i^T [F, H] and B_i^T [H, F], with full
+    # weights their row / column slices read in place.
+    weights_linear = False
 
     def __init__(self, w, split_weights: bool, seq: bool = False):
         self.w = w
@@ -177,6 +181,17 @@ class MlpStep:
                                                      stream=self.s0, prepare=True)
         elif self.split:
             A0, B0 = self.A[:, :self.w.F], self.B[:self.w.F]
+        layout = tp.TP_WEIGHTS_MATH
+        if self.weights_linear:
+            if self.cut_weights:
+                raise ValueError("--weights linear reads the shards in place; it does not combine with --cut-weights")
+            layout = tp.TP_WEIGHTS_LINEAR
+            if self.split:
+                self.W1, self.W2 = self.A.t().contiguous(), self.B.t().contiguous()   # [P*F, H], [H, P*F]
+                A0, B0 = self.W1[:self.w.F], self.W2[:, :self.w.F]
+            else:
+                A0, B0 = A0.t().contiguous(), B0.t().contiguous()
+            torch.cuda.synchronize()
         X = None if (self.seq and not self.gather_input) else self.X
         self.mlp = tp.tp_colrow_mlp(X, A0, B0, self.Y, self.Z, row_chunks=self.w.R,
                                     col_chunks=self.w.C, peer_partials=self.peers,
@@ -184,7 +199,7 @@ class MlpStep:
                                     s_reduce=self.s0 if self.serial else self.s1,
                                     reduce_workgroups=self.reduce_wgs, X_shards=self.Xb if self.seq else None,
                                     Z_split=self.Zs if self.seq else None, reduce_fusion=self.reduce_fusion,
-                                    prepare=True)
+                                    weight_layout=layout, prepare=True)
 
     def step(self):
         if self.cut_layouts is not None:
@@ -205,7 +220,9 @@ class MlpStep:
                "tp": w.P, "row_chunks": w.R, "col_chunks": w.C,
                "weights": (("rank 0's shards of A and B copied out of the full weights each step" if self.cut_weights
                             else "rank 0's shards read in place: A's column slice with a row stride of P*F, B's row "
-                                 "slice") if self.split else "per-rank shards drawn as such"),
+                                 "slice") if self.split else "per-rank shards drawn as such")
+                          + (", stored [out, in] as a linear layer's (A_i^T [F, H], B_i^T [H, F])"
+                             if self.weights_linear else ""),
                "reduce_stream": "compute" if self.serial else "second",
                "reduce_fusion": "auto" if self.reduce_fusion == tp.TP_REDUCE_FUSION_AUTO else "off",
                "reduce_output": ("reduce-scattered blocks" if self.seq else
@@ -945,10 +962,11 @@ def run_workload(name, steps, warmup, flusher, args, serial_too=True):
     wl.separate_output = args.separate_output
     wl.cut_weights = args.cut_weights
     wl.gather_input = args.gather_input
+    wl.weights_linear = args.weights == "linear"
     log(f"[bench] workload {name}: timing")
     m = measure(wl, steps, warmup, flusher, profile=args.profile)
     default_schedule = not (args.serial or args.reduce_wgs or args.no_reduce_fusion or args.separate_output or
-                            args.gather_input)
+                            args.gather_input or args.weights != "math")
     summ = {"config": wl.config(), "value": rate(wl, m["ms_per_step"]), "unit": wl.unit,
             "ms_per_step": m["ms_per_step"], "timed_as": m["timed_as"],
             "ms_per_step_eager": m["ms_per_step_eager"], "ms_per_step_graph": m["ms_per_step_graph"],
@@ -1006,6 +1024,9 @@ def main():
     ap.add_argument("--serial", action="store_true", help="run the reduce on the compute stream")
     ap.add_argument("--separate-output", action="store_true",
                     help="write the reduced output to its own buffer instead of in place over the partial")
+    ap.add_argument("--weights", choices=("math", "linear"), default="math",
+                    help="forward MLP workloads: rank 0's weight shards in the math layout (A_i [H, F], B_i [F, H]) "
+                         "or a linear layer's [out, in] (A_i^T, B_i^T)")
     ap.add_argument("--gather-input", action="store_true",
                     help="sequence-parallel workloads: all-gather the input blocks into X before GEMM1 instead of "
                          "reading them in place")

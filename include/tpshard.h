@@ -356,12 +356,24 @@ typedef struct {
                         multiple of 64; otherwise, and
                         always with TP_REDUCE_FUSION_OFF (1), a separate reduction
                         kernel runs.  Both give the same bits. */
-  int64_t A_ld;      /* row stride of A_i in elements; 0 = F (contiguous).  With
-                        A_ld = P*F, A_i may point into the full A [H, P*F] at column
-                        i*F: the rank consumes its column shard in place, as the
-                        column-parallel layer uses its weight shard ([CAI] section 5.1),
-                        with no copy.  Must be >= F. */
+  int64_t A_ld;      /* row stride of A_i in elements; 0 = contiguous.  TP_WEIGHTS_MATH:
+                        with A_ld = P*F, A_i may point into the full A [H, P*F] at
+                        column i*F: the rank consumes its column shard in place, as
+                        the column-parallel layer uses its weight shard ([CAI]
+                        section 5.1), with no copy.  Must be >= F (MATH) or >= H
+                        (LINEAR). */
+  int32_t weight_layout; /* TP_WEIGHTS_MATH (0): A_i is [H, F] and B_i [F, H] (Y = X A_i,
+                        Z_i = Y B_i).  TP_WEIGHTS_LINEAR (1): both as a linear layer
+                        stores its weight, [out, in]: A_i is [F, H] (A_i^T) and B_i
+                        [H, F] (B_i^T); the GEMMs read them k-contiguous, with no
+                        transpose pass.  Same results, bit for bit. */
+  int64_t B_ld;      /* row stride of B_i in elements; 0 = contiguous.  TP_WEIGHTS_LINEAR:
+                        with B_ld = P*F, B_i may point into the full [H, P*F] weight
+                        at column i*F (the row-parallel layer's shard, in place).
+                        Must be >= H (MATH) or >= F (LINEAR). */
 } tp_mlp_args;
+
+enum { TP_WEIGHTS_MATH = 0, TP_WEIGHTS_LINEAR = 1 };
 
 enum { TP_REDUCE_FUSION_AUTO = 0, TP_REDUCE_FUSION_OFF = 1 };
 
@@ -475,6 +487,10 @@ typedef struct {
                         for the hand-off to s_reduce to pay); otherwise, and always
                         with TP_REDUCE_FUSION_OFF (1), the reduction runs on
                         s_reduce beside the later GEMMs.  Same bits. */
+  int32_t weight_layout; /* TP_WEIGHTS_MATH (0): A_i [H, F], B_i [F, H], and dA_i, dB_i
+                        written in that layout.  TP_WEIGHTS_LINEAR (1): A_i [F, H],
+                        B_i [H, F] (a linear layer's [out, in]), and dA_i [F, H],
+                        dB_i [H, F] likewise.  All contiguous. */
 } tp_mlp_bwd_args;
 
 /*

@@ -46,6 +46,9 @@ TP_KERNEL_NAMES = ("materialize", "gemm1", "gemm2", "reduce", "gemm_dgrad", "gem
 TP_REDUCE_FUSION_AUTO = 0
 TP_REDUCE_FUSION_OFF = 1
 
+TP_WEIGHTS_MATH = 0
+TP_WEIGHTS_LINEAR = 1
+
 
 class TpError(RuntimeError):
     def __init__(self, code: int, msg: str):
@@ -91,7 +94,8 @@ class tp_mlp_args(C.Structure):
                 ("peer_partials", C.POINTER(C.c_void_p)), ("Z_out", C.c_void_p),
                 ("reduce_workgroups", C.c_int64), ("H_out", C.c_void_p), ("bias", C.c_void_p),
                 ("seq_splits", C.c_int64), ("X_shards", C.POINTER(C.c_void_p)), ("Z_split", C.POINTER(C.c_void_p)),
-                ("X_next", C.c_void_p), ("reduce_fusion", C.c_int32), ("A_ld", C.c_int64)]
+                ("X_next", C.c_void_p), ("reduce_fusion", C.c_int32), ("A_ld", C.c_int64),
+                ("weight_layout", C.c_int32), ("B_ld", C.c_int64)]
 
 
 class tp_mlp_bwd_args(C.Structure):
@@ -104,7 +108,7 @@ class tp_mlp_bwd_args(C.Structure):
                 ("peer_dX", C.POINTER(C.c_void_p)), ("dX_out", C.c_void_p),
                 ("reduce_workgroups", C.c_int64),
                 ("seq_splits", C.c_int64), ("dZ_shards", C.POINTER(C.c_void_p)), ("dX_split", C.POINTER(C.c_void_p)),
-                ("reduce_fusion", C.c_int32)]
+                ("reduce_fusion", C.c_int32), ("weight_layout", C.c_int32)]
 
 
 class tp_materialize_item(C.Structure):
@@ -492,7 +496,7 @@ def tp_partial_reduce(partials, out, mode=TP_REDUCE_FULL, rows=None, cols=None, 
 
 def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partials=(), Z_out=None,
               act=TP_ACT_GELU_ERF, reduce_workgroups=0, H_out=None, bias=None, X_shards=None, Z_split=None,
-              X_next=None, reduce_fusion=TP_REDUCE_FUSION_AUTO):
+              X_next=None, reduce_fusion=TP_REDUCE_FUSION_AUTO, weight_layout=TP_WEIGHTS_MATH):
     """(tp_mlp_args, keep-alive list) for one forward layer, shapes checked.
     X may be None with X_shards: GEMM1 then reads the blocks where they lie."""
     if X is None:
@@ -505,18 +509,24 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
         M, H, xref = int(x0.shape[0]) * len(X_shards), int(x0.shape[1]), x0
     else:
         M, H, xref = int(X.shape[0]), int(X.shape[1]), X
-    F = int(A_i.shape[1])
+    linear = weight_layout == TP_WEIGHTS_LINEAR
+    F = int(A_i.shape[0] if linear else A_i.shape[1])
     peers = list(peer_partials)
-    # A_i may be a column slice of the full A (rows contiguous, a row stride of
-    # at least F): it is then read in place.
-    A_ld = 0
-    if not A_i.is_contiguous():
-        if A_i.dim() != 2 or A_i.stride(1) != 1 or A_i.stride(0) < F:
-            raise ValueError("A_i must be contiguous or a column slice (unit column stride, row stride >= F)")
-        A_ld = int(A_i.stride(0))
-    if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Z_i.shape) != (M, H) \
+    wa, wb = ((F, H), (H, F)) if linear else ((H, F), (F, H))
+    if tuple(A_i.shape) != wa or tuple(B_i.shape) != wb or tuple(Z_i.shape) != (M, H) \
             or (Y_ws is not None and tuple(Y_ws.shape) != (M, F)):
-        raise ValueError("shapes must be X[M,H], A_i[H,F], B_i[F,H], Y_ws[M,F], Z_i[M,H]")
+        raise ValueError(f"shapes must be X[M,H], A_i{list(wa)}, B_i{list(wb)}, Y_ws[M,F], Z_i[M,H]")
+
+    # A weight may be a column slice of the full weight (unit column stride, a
+    # row stride of at least its row length): it is then read in place.
+    def ld_of(t, name):
+        if t.is_contiguous():
+            return 0
+        if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+            raise ValueError(f"{name} must be contiguous or a column slice (unit column stride, row stride >= "
+                             f"its row length)")
+        return int(t.stride(0))
+    A_ld, B_ld = ld_of(A_i, "A_i"), ld_of(B_i, "B_i")
     if not (xref.dtype == A_i.dtype == B_i.dtype) or (Y_ws is not None and Y_ws.dtype != xref.dtype):
         raise TypeError("X, A_i, B_i and Y_ws must share one dtype")
     for t in (H_out, X_next):
@@ -534,11 +544,12 @@ def _mlp_args(X, A_i, B_i, Y_ws, Z_i, *, row_chunks=1, col_chunks=1, peer_partia
     S, xs, zs = _seq_arrays(X_shards, Z_split, M, H, xref.dtype, "X_shards", "Z_split")
     parr = (C.c_void_p * max(1, len(peers)))(*[_ptr(p) for p in peers])
     args = tp_mlp_args(dtype=_dtype_code(xref), act=act, M=M, H=H, F=F,
-                       X=_ptr(X), A_i=A_i.data_ptr(), B_i=_ptr(B_i), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
+                       X=_ptr(X), A_i=A_i.data_ptr(), B_i=B_i.data_ptr(), Y_ws=_ptr(Y_ws), Z_i=_ptr(Z_i),
                        row_chunks=row_chunks, col_chunks=col_chunks, P=1 + len(peers),
                        peer_partials=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
                        Z_out=_ptr(Z_out), reduce_workgroups=reduce_workgroups, H_out=_ptr(H_out), bias=_ptr(bias),
-                       X_next=_ptr(X_next), reduce_fusion=reduce_fusion, A_ld=A_ld)
+                       X_next=_ptr(X_next), reduce_fusion=reduce_fusion, A_ld=A_ld,
+                       weight_layout=weight_layout, B_ld=B_ld)
     args.seq_splits, args.X_shards, args.Z_split = S, xs, zs
     return args, [parr, xs, zs]
 
@@ -549,7 +560,9 @@ def tp_colrow_mlp(X, A_i, B_i, Y_ws, Z_i, *, s_compute=None, s_reduce=None, prep
     sum rounded to the input dtype (the next layer's input).
 
     Keywords: row_chunks, col_chunks, peer_partials, Z_out, act, reduce_workgroups, H_out,
-    bias, X_shards, Z_split, X_next, reduce_fusion (TP_REDUCE_FUSION_AUTO lets GEMM2's
+    bias, X_shards, Z_split, X_next, weight_layout (TP_WEIGHTS_LINEAR: A_i is [F, H] and
+    B_i [H, F], as a linear layer stores its weight; either may be a column slice of the
+    full weight, read in place), reduce_fusion (TP_REDUCE_FUSION_AUTO lets GEMM2's
     epilogue take the reduction where nothing would run beside it; TP_REDUCE_FUSION_OFF
     keeps the separate reduction kernel; same bits either way).  Sequence parallelism: with ``X_shards`` (S tensors
     [M/S, H]) X is a workspace the call fills by all-gathering them, or None: GEMM1 then reads the blocks where
@@ -600,22 +613,27 @@ def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None, prepare=False):
 def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *, row_chunks=1, peer_dX=(),
                            dX_out=None, act=TP_ACT_GELU_ERF, accumulate=False, s_compute=None, s_reduce=None,
                            reduce_workgroups=0, dZ_shards=None, dX_split=None,
-                           reduce_fusion=TP_REDUCE_FUSION_AUTO, prepare=False):
+                           reduce_fusion=TP_REDUCE_FUSION_AUTO, weight_layout=TP_WEIGHTS_MATH, prepare=False):
     """Backward of one rank's MLP share: dH_ws = (dZ B_i^T) * act'(H_i); dX_i = dH_ws A_i^T;
     dX_out = dX_i + sum(peers); dA_i (+)= X^T dH_ws; dB_i (+)= Y_i^T dZ.
-    reduce_fusion as in tp_colrow_mlp (for the sum of dX).
+    reduce_fusion as in tp_colrow_mlp (for the sum of dX).  weight_layout
+    TP_WEIGHTS_LINEAR: A_i, dA_i are [F, H] and B_i, dB_i [H, F] (a linear layer's
+    [out, in]).
 
     Sequence parallelism: with ``dZ_shards`` dZ is a workspace the call fills by
     all-gathering them; with ``dX_split`` the input gradient is reduce-scattered."""
     lib = load()
+    linear = weight_layout == TP_WEIGHTS_LINEAR
     M, H = int(X.shape[0]), int(X.shape[1])
-    F = int(A_i.shape[1])
+    F = int(A_i.shape[0] if linear else A_i.shape[1])
     peers = list(peer_dX)
-    if tuple(A_i.shape) != (H, F) or tuple(B_i.shape) != (F, H) or tuple(Y_i.shape) != (M, F) \
+    wa, wb = ((F, H), (H, F)) if linear else ((H, F), (F, H))
+    if tuple(A_i.shape) != wa or tuple(B_i.shape) != wb or tuple(Y_i.shape) != (M, F) \
             or tuple(dZ.shape) != (M, H) or tuple(dH_ws.shape) != (M, F) or tuple(dX_i.shape) != (M, H) \
-            or tuple(dA_i.shape) != (H, F) or tuple(dB_i.shape) != (F, H) \
+            or tuple(dA_i.shape) != wa or tuple(dB_i.shape) != wb \
             or (H_i is not None and tuple(H_i.shape) != (M, F)):
-        raise ValueError("shapes must be X, dZ, dX_i [M,H]; A_i, dA_i [H,F]; B_i, dB_i [F,H]; H_i, Y_i, dH_ws [M,F]")
+        raise ValueError(f"shapes must be X, dZ, dX_i [M,H]; A_i, dA_i {list(wa)}; B_i, dB_i {list(wb)}; "
+                         "H_i, Y_i, dH_ws [M,F]")
     ins = [X, A_i, B_i, Y_i, dZ, dH_ws] + ([H_i] if H_i is not None else [])
     if any(t.dtype != X.dtype for t in ins):
         raise TypeError("X, A_i, B_i, H_i, Y_i, dZ and dH_ws must share one dtype")
@@ -632,7 +650,8 @@ def tp_colrow_mlp_backward(X, A_i, B_i, H_i, Y_i, dZ, dH_ws, dX_i, dA_i, dB_i, *
                            dH_ws=_ptr(dH_ws), dX_i=_ptr(dX_i), dA_i=_ptr(dA_i), dB_i=_ptr(dB_i),
                            accumulate=1 if accumulate else 0, row_chunks=row_chunks, P=1 + len(peers),
                            peer_dX=C.cast(parr, C.POINTER(C.c_void_p)) if peers else None,
-                           dX_out=_ptr(dX_out), reduce_workgroups=reduce_workgroups, reduce_fusion=reduce_fusion)
+                           dX_out=_ptr(dX_out), reduce_workgroups=reduce_workgroups, reduce_fusion=reduce_fusion,
+                           weight_layout=weight_layout)
     S, gs, xs = _seq_arrays(dZ_shards, dX_split, M, H, X.dtype, "dZ_shards", "dX_split")
     args.seq_splits, args.dZ_shards, args.dX_split = S, gs, xs
     sc = _stream_ptr(s_compute)

@@ -42,6 +42,8 @@ constexpr int64_t kMaxLayers = 1024;
 // workgroups; one workgroup per CU back-fills those gaps without crowding out
 // the next GEMM (measured on MI355X against 32 ... 16384).
 constexpr int64_t kReduceBesideGemm = 256;
+// GEMMs of fewer 128 x 128 output tiles than this (the CU count) are "small".
+constexpr int64_t kSmallTiles = 256;
 // Rates for weighing a block's reduction against the GEMMs it would run
 // beside (MI355X, measured in the step: bf16 GEMMs at about 1.2 PFLOP/s, a
 // reduction alone at about 6 TB/s), and the share of those GEMMs' time the
@@ -184,6 +186,10 @@ struct MlpPlan {
   bool gather = false, reduce = false;
   // X is NULL and GEMM1 reads the sequence blocks X_shards where they lie.
   bool x_in_place = false;
+  // TP_WEIGHTS_LINEAR: A_i, B_i stored [out, in] (k-contiguous for the GEMMs);
+  // their row strides.
+  bool w_linear = false;
+  int64_t lda = 0, ldb = 0;
   // Y_ws holds one row chunk ([M/R, F]) that every chunk reuses in turn.
   bool y_chunk = false;
   int epi1 = 0, epi2 = 0;
@@ -201,7 +207,8 @@ char *chunk_y(const tp_mlp_args *a, const MlpPlan& pl, int64_t r) {
 // that holds the chunk, or the chunk's blocks as A's row blocks.
 GemmArgs chunk_gemm1(const tp_mlp_args *a, const MlpPlan& pl, int64_t r) {
   const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr;
-  GemmArgs g1{nullptr, a->A_i, chunk_y(a, pl, r), Mr, F, H, H, a->A_ld ? a->A_ld : F, F};
+  GemmArgs g1{nullptr, a->A_i, chunk_y(a, pl, r), Mr, F, H, H, pl.lda, F};
+  g1.w_t = pl.w_linear ? 1 : 0;
   if (!pl.x_in_place) {
     g1.a = static_cast<const char *>(a->X) + r * Mr * H * es;
   } else {
@@ -250,10 +257,20 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) ||
       (M / a->row_chunks) * (H / a->col_chunks) >= (int64_t(1) << 31))
     return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
-  if (a->A_ld != 0 && a->A_ld < F) return fail(TP_ERR_ARG, "A_ld = %lld < F = %lld", (long long)a->A_ld, (long long)F);
-  const int64_t lda_w = a->A_ld ? a->A_ld : F;
-  if (lda_w >= (int64_t(1) << 31)) return fail(TP_ERR_UNSUPPORTED, "A_ld exceeds the 32-bit index range of the kernels");
-  const int64_t bx = M * H * es, ba = matrix_bytes(H, F, lda_w, es), bb = F * H * es, by = M * F * es, bz = M * H * 4;
+  if (a->weight_layout != TP_WEIGHTS_MATH && a->weight_layout != TP_WEIGHTS_LINEAR)
+    return fail(TP_ERR_ARG, "unknown weight_layout %d", a->weight_layout);
+  const bool linear = a->weight_layout == TP_WEIGHTS_LINEAR;
+  // A_i: [H][lda >= F] or, linear, [F][lda >= H]; B_i: [F][ldb >= H] or [H][ldb >= F].
+  const int64_t a_rows = linear ? F : H, a_cols = linear ? H : F, b_rows = linear ? H : F, b_cols = linear ? F : H;
+  if (a->A_ld != 0 && a->A_ld < a_cols)
+    return fail(TP_ERR_ARG, "A_ld = %lld < %lld (the row length of A_i)", (long long)a->A_ld, (long long)a_cols);
+  if (a->B_ld != 0 && a->B_ld < b_cols)
+    return fail(TP_ERR_ARG, "B_ld = %lld < %lld (the row length of B_i)", (long long)a->B_ld, (long long)b_cols);
+  const int64_t lda_w = a->A_ld ? a->A_ld : a_cols, ldb_w = a->B_ld ? a->B_ld : b_cols;
+  if (lda_w >= (int64_t(1) << 31) || ldb_w >= (int64_t(1) << 31))
+    return fail(TP_ERR_UNSUPPORTED, "A_ld or B_ld exceeds the 32-bit index range of the kernels");
+  const int64_t bx = M * H * es, ba = matrix_bytes(a_rows, a_cols, lda_w, es), bb = matrix_bytes(b_rows, b_cols, ldb_w, es),
+                by = M * F * es, bz = M * H * 4;
   const bool gather = a->X_shards != nullptr && a->X;
   std::vector<Buf> ins = {{a->A_i, ba, "A_i"}, {a->B_i, bb, "B_i"}};
   // (The library's own scratch, which replaces Y_ws when y_chunk, is disjoint
@@ -301,6 +318,9 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   pl->epi1 = bf16 ? (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveBf16 : kEpiGeluBf16) : kEpiIdentBf16)
                   : (a->act == TP_ACT_GELU_ERF ? (save ? kEpiGeluSaveF32 : kEpiGeluF32) : kEpiPlainF32);
   pl->epi2 = bf16 ? kEpiF32 : kEpiPlainF32;
+  pl->w_linear = linear;
+  pl->lda = lda_w;
+  pl->ldb = ldb_w;
   pl->x_in_place = !a->X;
   if (pl->x_in_place) {
     // A row chunk inside one block is read at an offset; one that spans
@@ -319,11 +339,15 @@ int validate_mlp(const tp_mlp_args *a, MlpPlan *pl, bool y_chunk = false) {
   return TP_OK;
 }
 
-// GEMM2 of block (r, c): Z_i[r, c] = Y[r] B_i[:, c].
+// GEMM2 of block (r, c): Z_i[r, c] = Y[r] B_i[:, c] (columns c of B_i; with
+// linear weights the same block is rows c of B_i^T).
 GemmArgs block_gemm2(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c) {
   const int64_t zoff = r * pl.Mr * pl.H + c * pl.Hc;
-  return GemmArgs{chunk_y(a, pl, r), static_cast<const char *>(a->B_i) + c * pl.Hc * pl.es, a->Z_i + zoff,
-                  pl.Mr, pl.Hc, pl.F, pl.F, pl.H, pl.H};
+  const int64_t woff = pl.w_linear ? c * pl.Hc * pl.ldb : c * pl.Hc;
+  GemmArgs g{chunk_y(a, pl, r), static_cast<const char *>(a->B_i) + woff * pl.es, a->Z_i + zoff,
+             pl.Mr, pl.Hc, pl.F, pl.F, pl.ldb, pl.H};
+  g.w_t = pl.w_linear ? 1 : 0;
+  return g;
 }
 
 // Whether block (r, c)'s reduction folds into its GEMM2's epilogue, and if so
@@ -801,6 +825,9 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   if (a->reduce_workgroups < 0) return fail(TP_ERR_ARG, "reduce_workgroups < 0");
   if (a->reduce_fusion != TP_REDUCE_FUSION_AUTO && a->reduce_fusion != TP_REDUCE_FUSION_OFF)
     return fail(TP_ERR_ARG, "unknown reduce_fusion %d", a->reduce_fusion);
+  if (a->weight_layout != TP_WEIGHTS_MATH && a->weight_layout != TP_WEIGHTS_LINEAR)
+    return fail(TP_ERR_ARG, "unknown weight_layout %d", a->weight_layout);
+  const bool linear = a->weight_layout == TP_WEIGHTS_LINEAR;
   const int64_t M = a->M, H = a->H, F = a->F;
   if (M >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) || F >= (int64_t(1) << 31) || (M / a->row_chunks) * H >= (int64_t(1) << 31))
     return fail(TP_ERR_UNSUPPORTED, "sizes exceed the 32-bit index range of the kernels");
@@ -837,8 +864,10 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   // dX_i[r] = dH[r] A_i^T: A_i is [H][F], i.e. W^T for W = A_i^T.  With the
   // reduction folded in, the epilogue also sums the peers' dX[r] into dX_out.
   auto dx_gemm = [&](int64_t r, bool fused) {
-    GemmArgs gx{static_cast<const char *>(a->dH_ws) + r * Mr * F * es, a->A_i, a->dX_i + r * Mr * H, Mr, H, F, F, F, H};
-    gx.w_t = 1;
+    // A_i^T: A_i [H][F] read transposed, or the linear layout's [F][H] as is.
+    GemmArgs gx{static_cast<const char *>(a->dH_ws) + r * Mr * F * es, a->A_i, a->dX_i + r * Mr * H, Mr, H, F, F,
+                linear ? H : F, H};
+    gx.w_t = linear ? 0 : 1;
     if (fused) {
       gx.red.np = static_cast<int32_t>(a->P - 1);
       for (int64_t p = 1; p < a->P; ++p) gx.red.peer[p - 1] = a->peer_dX[p - 1] + r * Mr * H;
@@ -850,7 +879,7 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   // Small layers sum dX in the dX GEMM's epilogue: their GEMMs are too short
   // for the hand-off to s_reduce and back to pay for the overlap it buys.
   bool fuse = reduce && a->reduce_fusion == TP_REDUCE_FUSION_AUTO && bf16 && !a->dX_split && a->dX_out &&
-              a->P - 1 <= kMaxFusedPeers;
+              a->P - 1 <= kMaxFusedPeers && ((Mr + 127) / 128) * ((H + 127) / 128) < kSmallTiles;
   for (int64_t r = 0; fuse && r < R; ++r) fuse = gemm_red_ok(dx_gemm(r, true));
   // As in the forward: a second stream only pays when its work can run beside
   // GEMMs: a chunk's reduce beside that chunk's weight-gradient GEMMs, the
@@ -890,8 +919,9 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
     if (gather && two && r > 0 && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess)
       return hip_fail(e, "hipStreamWaitEvent");
     // dH[r] = (dZ[r] B_i^T) * act'(H_i[r]): B_i is [F][H], i.e. W^T for W = B_i^T.
-    GemmArgs gd{dZ + r * Mr * H * es, a->B_i, dH + r * Mr * F * es, Mr, F, H, H, H, F};
-    gd.w_t = 1;
+    // (With linear weights B_i is stored [H][F], B_i^T as is.)
+    GemmArgs gd{dZ + r * Mr * H * es, a->B_i, dH + r * Mr * F * es, Mr, F, H, H, linear ? F : H, F};
+    gd.w_t = linear ? 0 : 1;
     if (gelu) {
       gd.aux = const_cast<char *>(static_cast<const char *>(a->H_i)) + r * Mr * F * es;
       gd.ldaux = F;
@@ -936,11 +966,14 @@ int tp_colrow_mlp_backward(const tp_mlp_bwd_args *a, tp_stream_t s_compute, tp_s
   // gradients once per further chunk (the 175B shapes: 302 MB each way per
   // weight and chunk).  The last chunk's dX reduction runs beside them.
   {
+    // Linear weights take their gradients in the same layout: dA_i^T = dH^T X
+    // ([F][H]) and dB_i^T = dZ^T Y_i ([H][F]), each element the same sum over
+    // the rows.
     const int cont = a->accumulate ? 1 : 0;
-    GemmArgs ga{X, dH, a->dA_i, H, F, M, H, F, F};
+    GemmArgs ga = linear ? GemmArgs{dH, X, a->dA_i, F, H, M, F, H, H} : GemmArgs{X, dH, a->dA_i, H, F, M, H, F, F};
     ga.a_t = 1;
     ga.acc_init = cont;
-    GemmArgs gb{Yi, dZ, a->dB_i, F, H, M, F, H, H};
+    GemmArgs gb = linear ? GemmArgs{dZ, Yi, a->dB_i, H, F, M, H, F, F} : GemmArgs{Yi, dZ, a->dB_i, F, H, M, F, H, H};
     gb.a_t = 1;
     gb.acc_init = cont;
     const GemmArgs pair[2] = {ga, gb};

@@ -85,10 +85,10 @@ hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t s);
 // Whether gemm_launch takes p with kEpiF32Red: A not transposed, whole
 // 16-byte vectors along every row of C, the peers, out, bias and lo; either
 // on the small-tile path (fewer 128 x 128 tiles than CUs, K % 32 == 0, at most
-// kMaxFusedPeers peers), where the peers' loads fit beside the accumulators
-// without costing occupancy, or on the 256-row tiles (W not transposed,
-// K % 64 == 0, operands within 32-bit offsets, at most kMaxEpiPeers peers),
-// where the epilogue stages the tile through LDS.
+// kMaxFusedPeers peers, a single output when W is transposed), where the
+// peers' loads fit beside the accumulators without costing occupancy, or on
+// the 256-row tiles (K % 64 == 0, operands within 32-bit offsets, at most
+// kMaxEpiPeers peers), where the epilogue stages the tile through LDS.
 bool gemm_red_ok(const GemmArgs& p);
 // The same for kEpiPlainF32Red (the fp32 kernel, any alignment and size).
 bool gemm_red_ok_f32(const GemmArgs& p);

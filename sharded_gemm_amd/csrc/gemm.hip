@@ -1307,15 +1307,16 @@ bool aligned16(const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) ==
 // GEMM2 with the block's sum in the epilogue on the 256-row tiles: the tile
 // the cost model takes among the split-ring ones (the only kernels with that
 // epilogue).
+template <bool WT>
 hipError_t dispatch_red_tiles(const GemmArgs& p, hipStream_t s) {
   auto cost = [&](int bm, int bn, double eff) {
     const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
     return static_cast<double>((tiles + kCUs - 1) / kCUs) * bm * bn / eff;
   };
   const double c256 = cost(256, 256, 1.0), c192 = cost(256, 192, 0.95), c128w = cost(256, 128, 0.85);
-  if (c256 <= c192 && c256 <= c128w) return launch_pps<256, 256, kEpiF32Red, false, false>(p, s);
-  if (c192 <= c128w) return launch_pps<256, 192, kEpiF32Red, false, false>(p, s);
-  return launch_pps<256, 128, kEpiF32Red, false, false>(p, s);
+  if (c256 <= c192 && c256 <= c128w) return launch_pps<256, 256, kEpiF32Red, false, WT>(p, s);
+  if (c192 <= c128w) return launch_pps<256, 192, kEpiF32Red, false, WT>(p, s);
+  return launch_pps<256, 128, kEpiF32Red, false, WT>(p, s);
 }
 
 // Fewer 128 x 128 tiles than CUs: the small-tile path.
@@ -1365,9 +1366,10 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
       case kEpiF32: return dispatch_bf16<kEpiF32, false, false>(p, dma_ok, vec, s);
       case kEpiF32Acc: return dispatch_bf16<kEpiF32Acc, false, false>(p, dma_ok, vec, s);
       case kEpiGeluSaveBf16: return dispatch_bf16<kEpiGeluSaveBf16, false, false>(p, dma_ok, vec, s);
+      case kEpiDGeluBf16: return dispatch_bf16<kEpiDGeluBf16, false, false>(p, dma_ok, vec, s);
       case kEpiF32Red:
         if (!gemm_red_ok(p)) return hipErrorInvalidValue;
-        if (!small_problem(p)) return dispatch_red_tiles(p, s);
+        if (!small_problem(p)) return dispatch_red_tiles<false>(p, s);
         if (p.red.nout > 1) {
           if (p.K % 64 == 0) return launch_dma<64, 64, 64, 2, kEpiF32RedSplit, false, false, 2, 2>(p, s);
           return launch_dma<64, 64, 32, 4, kEpiF32RedSplit, false, false, 2, 2>(p, s);
@@ -1383,8 +1385,11 @@ hipError_t gemm_launch(const GemmArgs& p, int epi_in, hipStream_t s) {
     switch (epi) {
       case kEpiF32Red:
         if (!gemm_red_ok(p)) return hipErrorInvalidValue;
+        if (!small_problem(p)) return dispatch_red_tiles<true>(p, s);
         if (p.K % 64 == 0) return launch_dma<64, 64, 64, 2, kEpiF32Red, false, true, 2, 2>(p, s);
         return launch_dma<64, 64, 32, 4, kEpiF32Red, false, true, 2, 2>(p, s);
+      case kEpiGeluBf16: return dispatch_bf16<kEpiGeluBf16, false, true>(p, dma_ok, false, s);
+      case kEpiGeluSaveBf16: return dispatch_bf16<kEpiGeluSaveBf16, false, true>(p, dma_ok, false, s);
       case kEpiDGeluBf16: return dispatch_bf16<kEpiDGeluBf16, false, true>(p, dma_ok, false, s);
       case kEpiIdentBf16: return dispatch_bf16<kEpiIdentBf16, false, true>(p, dma_ok, false, s);
       case kEpiF32: return dispatch_bf16<kEpiF32, false, true>(p, dma_ok, false, s);
@@ -1402,16 +1407,15 @@ bool gemm_red_ok(const GemmArgs& p) {
   const EpiReduce& r = p.red;
   if (p.a_t || p.acc_init || r.np < 0 || p.K <= 0 || p.K % 32 != 0 || !gemm_vec_ok(p, 4, false)) return false;
   if (!small_problem(p)) {
-    // The split-ring tiles: forward layout, 64-deep stages, 32-bit operand
-    // offsets.
-    const bool off32 = p.M * p.lda * 2 < (int64_t{1} << 31) && p.K * p.ldw * 2 < (int64_t{1} << 31);
-    if (p.w_t || r.np > kMaxEpiPeers || p.K % 64 != 0 || !off32) return false;
-  } else if (r.np > kMaxFusedPeers) {
+    // The split-ring tiles: 64-deep stages, 32-bit operand offsets.
+    const bool off32 = p.M * p.lda * 2 < (int64_t{1} << 31) && (p.w_t ? p.N : p.K) * p.ldw * 2 < (int64_t{1} << 31);
+    if (r.np > kMaxEpiPeers || p.K % 64 != 0 || !off32) return false;
+  } else if (r.np > kMaxFusedPeers || (p.w_t && r.nout > 1)) {
     return false;
   }
   bool ok = !r.bias || aligned16(r.bias);
   for (int q = 0; q < r.np; ++q) ok = ok && r.peer[q] && aligned16(r.peer[q]);
-  if (r.nout < 1 || r.nout > kMaxFusedOuts || (p.w_t && r.nout > 1)) return false;
+  if (r.nout < 1 || r.nout > kMaxFusedOuts) return false;
   if (r.nout > 1) {
     // Reduce-scattered: whole blocks of rows per output, no second copy.
     if (r.lo || r.rows_per_out < 1 || static_cast<int64_t>(r.rows_per_out) * r.nout != p.M) return false;

@@ -92,9 +92,9 @@ hipError_t gemm_launch(const GemmArgs& p, int epi, hipStream_t) {
 bool gemm_red_ok(const GemmArgs& p) {
   if (p.a_t || p.acc_init || p.red.np < 0 || p.K % 32 != 0 || p.K <= 0) return false;
   if (((p.M + 127) / 128) * ((p.N + 127) / 128) >= 256)   // the 256-row tiles: the epilogue stages the tile
-    return !p.w_t && p.red.np <= kMaxEpiPeers && p.K % 64 == 0 && p.red.nout >= 1 && p.red.nout <= kMaxFusedOuts &&
+    return p.red.np <= kMaxEpiPeers && p.K % 64 == 0 && p.red.nout >= 1 && p.red.nout <= kMaxFusedOuts &&
            (p.red.nout == 1 || (!p.red.lo && p.red.rows_per_out * p.red.nout == p.M)) &&
-           p.M * p.lda * 2 < (int64_t{1} << 31) && p.K * p.ldw * 2 < (int64_t{1} << 31);
+           p.M * p.lda * 2 < (int64_t{1} << 31) && (p.w_t ? p.N : p.K) * p.ldw * 2 < (int64_t{1} << 31);
   return p.red.np <= kMaxFusedPeers && p.red.nout >= 1 && p.red.nout <= kMaxFusedOuts &&
          !(p.w_t && p.red.nout > 1) && (p.red.nout == 1 || (!p.red.lo && p.red.rows_per_out * p.red.nout == p.M));
 }

@@ -64,6 +64,9 @@ def test_reduce_fusion_constants_match_header():
     vals = dict(re.findall(r"\b(TP_REDUCE_FUSION_[A-Z]+)\s*=\s*(\d+)", src))
     assert {k: int(v) for k, v in vals.items()} == {"TP_REDUCE_FUSION_AUTO": tp.TP_REDUCE_FUSION_AUTO,
                                                      "TP_REDUCE_FUSION_OFF": tp.TP_REDUCE_FUSION_OFF}
+    vals = dict(re.findall(r"\b(TP_WEIGHTS_[A-Z]+)\s*=\s*(\d+)", src))
+    assert {k: int(v) for k, v in vals.items()} == {"TP_WEIGHTS_MATH": tp.TP_WEIGHTS_MATH,
+                                                     "TP_WEIGHTS_LINEAR": tp.TP_WEIGHTS_LINEAR}
 
 
 def _oracle_plan(shape, spec):
@@ -172,6 +175,11 @@ def _mlp_args(**kw):
     (dict(reduce_workgroups=-1), _abi.TP_ERR_ARG),
     (dict(reduce_fusion=2), _abi.TP_ERR_ARG),
     (dict(reduce_fusion=-1), _abi.TP_ERR_ARG),
+    (dict(weight_layout=2), _abi.TP_ERR_ARG),
+    (dict(B_ld=63), _abi.TP_ERR_ARG),                   # B_i rows are H = 64 long
+    (dict(A_ld=63), _abi.TP_ERR_ARG),                   # A_i rows are F = 64 long
+    (dict(weight_layout=1, M=64, H=64, F=32, A_ld=32), _abi.TP_ERR_ARG),   # linear A_i rows are H = 64 long
+    (dict(weight_layout=1, M=64, H=64, F=32, B_ld=31), _abi.TP_ERR_ARG),   # linear B_i rows are F = 32 long
 ])
 def test_mlp_validation(kw, code):
     lib = _abi.load()
@@ -302,6 +310,7 @@ def _bwd_args(**kw):
     (dict(dA_i=FAKE + (9 << 20) + 64), _abi.TP_ERR_ARG),  # overlaps dB_i
     (dict(dX_i=FAKE + (5 << 20)), _abi.TP_ERR_ARG),       # overlaps dZ
     (dict(reduce_workgroups=-1), _abi.TP_ERR_ARG),
+    (dict(weight_layout=3), _abi.TP_ERR_ARG),
 ])
 def test_backward_validation(kw, code):
     lib = _abi.load()
@@ -483,6 +492,10 @@ def test_binding_checks_sequence_blocks_and_bias():
         fwd(X_shards=xs, Z_split=zs[:2])                                 # counts differ
     with pytest.raises(ValueError):
         tp.tp_colrow_mlp(None, A, B, Y, Z)                               # X = None needs X_shards
+    with pytest.raises(ValueError):                                      # linear layout: A_i [F, H], B_i [H, F]
+        fwd(weight_layout=tp.TP_WEIGHTS_LINEAR)
+    with pytest.raises(ValueError):                                      # a weight with a column stride
+        tp.tp_colrow_mlp(X, A, torch.zeros((H, F), dtype=torch.bfloat16).t(), Y, Z, s_compute=0, s_reduce=0)
     with pytest.raises(tp.TpError) as e:                                 # read in place: blocks of 16 rows
         tp.tp_colrow_mlp(None, A, B, Y, Z, X_shards=xs, s_compute=0, s_reduce=0)
     assert e.value.kind == "unsupported"

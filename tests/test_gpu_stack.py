@@ -45,10 +45,11 @@ def _layers_integer(M, H, Fs, P, seed):
 
 
 def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, keep_z=True, prepared=False,
-              fusion=tp.TP_REDUCE_FUSION_AUTO):
+              fusion=tp.TP_REDUCE_FUSION_AUTO, linear=False):
     """The stack on the GPU into guarded buffers; returns per layer (Z_out, X_next)
     CPU copies.  prepared: marshal the call once and replay it twice, the
-    outputs overwritten with NaN in between."""
+    outputs overwritten with NaN in between.  linear: the weights passed in a
+    linear layer's [out, in] layout (A_i^T, B_i^T)."""
     M, H = X0.shape
     dt = X0.dtype
     xs = [X0.cuda()] + [Guarded((M, H), dt) for _ in layers]
@@ -58,7 +59,11 @@ def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, kee
     args = []
     for l, layer in enumerate(layers):
         F = layer["A_i"].shape[1]
-        args.append(dict(X=xs[l] if l == 0 else xs[l].t, A_i=layer["A_i"].cuda(), B_i=layer["B_i"].cuda(),
+        A_i, B_i = layer["A_i"].cuda(), layer["B_i"].cuda()
+        if linear:
+            A_i, B_i = A_i.t().contiguous(), B_i.t().contiguous()
+        args.append(dict(X=xs[l] if l == 0 else xs[l].t, A_i=A_i, B_i=B_i,
+                         weight_layout=tp.TP_WEIGHTS_LINEAR if linear else tp.TP_WEIGHTS_MATH,
                          Y_ws=Y[:, :F] if F == Y.shape[1] else torch.empty((M, F), dtype=dt, device="cuda"),
                          Z_i=Zi, row_chunks=R, col_chunks=C, peer_partials=[p.cuda() for p in layer["peers"]],
                          Z_out=zs[l].t if keep_z else None, act=act,
@@ -104,6 +109,24 @@ def test_stack_integer_exact(M, H, Fs, R, C, P, two):
     for l, ((z, xn), (zr, xr)) in enumerate(zip(got, ref)):
         assert np.array_equal(z.double().numpy(), zr), l
         assert np.array_equal(bits(xn), bits(torch.from_numpy(xr).to(torch.bfloat16))), l
+
+
+@pytest.mark.parametrize("M,H,Fs,R,C,P", [(512, 256, [128, 96], 2, 1, 4), (4096, 768, [768, 768], 2, 1, 4),
+                                           (2048, 2048, [512, 512], 2, 2, 8)])
+def test_stack_linear_weights_same_bits(M, H, Fs, R, C, P):
+    """The stack with every layer's weights in the [out, in] layout gives the
+    math layout's bits in every Z_out and next-layer input."""
+    announce(f"stack linear weights M={M} H={H} F={Fs} R={R} C={C} P={P}")
+    X0 = inputs.normal((M, H), 1211, 1.0, "bf16")
+    layers = [{"A_i": inputs.normal((H, F), 1220 + l, 1.0 / np.sqrt(H), "bf16"),
+               "B_i": inputs.normal((F, H), 1230 + l, 1.0 / np.sqrt(F), "bf16"),
+               "peers": [inputs.normal((M, H), 1240 + 10 * l + p) for p in range(P - 1)],
+               "bias": inputs.normal((H,), 1290 + l)} for l, F in enumerate(Fs)]
+    ref = run_stack(X0, layers, R=R, C=C, act=tp.TP_ACT_GELU_ERF)
+    got = run_stack(X0, layers, R=R, C=C, act=tp.TP_ACT_GELU_ERF, linear=True)
+    for l, ((z, xn), (zr, xr)) in enumerate(zip(got, ref)):
+        assert np.array_equal(bits(z), bits(zr)), l
+        assert np.array_equal(bits(xn), bits(xr)), l
 
 
 @pytest.mark.parametrize("w", [GPT3_6P7B, GPT3_175B], ids=lambda w: w.name)

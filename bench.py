@@ -292,6 +292,7 @@ class BwdStep:
     reduce_wgs = 0
     reduce_fusion = tp.TP_REDUCE_FUSION_AUTO
     separate_output = False   # as in MlpStep: the input gradient's sum goes in place by default
+    weights_linear = False    # as in MlpStep: rank 0's weights (and their gradients) stored [out, in]
 
     def __init__(self, w, seq: bool = False):
         self.w = w
@@ -339,9 +340,15 @@ class BwdStep:
 
     def prepare(self):
         """Marshal the step's library call once (the buffers never move)."""
+        A0, B0, layout = self.As[0], self.Bs[0], tp.TP_WEIGHTS_MATH
+        if self.weights_linear:
+            A0, B0, layout = A0.t().contiguous(), B0.t().contiguous(), tp.TP_WEIGHTS_LINEAR
+            self.dA = torch.empty((self.w.F, self.w.H), device="cuda")
+            self.dB = torch.empty((self.w.H, self.w.F), device="cuda")
+            torch.cuda.synchronize()
         self.call = tp.tp_colrow_mlp_backward(
-            self.X, self.As[0], self.Bs[0], self.Hs, self.Y, self.dZ, self.dH, self.dX, self.dA, self.dB,
-            row_chunks=self.w.R, peer_dX=self.peers,
+            self.X, A0, B0, self.Hs, self.Y, self.dZ, self.dH, self.dX, self.dA, self.dB,
+            row_chunks=self.w.R, peer_dX=self.peers, weight_layout=layout,
             dX_out=None if self.seq else (self.dXo if self.separate_output else self.dX), s_compute=self.s0,
             s_reduce=self.s0 if self.serial else self.s1, reduce_workgroups=self.reduce_wgs,
             dZ_shards=self.dZb if self.seq else None, dX_split=self.dXs if self.seq else None,
@@ -365,6 +372,8 @@ class BwdStep:
                "reduce_output": ("reduce-scattered blocks" if self.seq else
                                  "separate buffer" if self.separate_output else "in place over the partial (all-reduce)"),
                "peers": "virtual ranks 1..P-1, input-gradient partials precomputed by the same path"}
+        if self.weights_linear:
+            cfg["weights"] = "stored [out, in] as a linear layer's (A_i^T [F, H], B_i^T [H, F]), gradients likewise"
         if self.seq:
             cfg["sequence_parallel"] = {"blocks": w.P, "output_gradient": "all-gathered from P sequence blocks",
                                         "input_gradient": "reduce-scattered into P sequence blocks"}

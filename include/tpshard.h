@@ -388,9 +388,12 @@ enum { TP_REDUCE_FUSION_AUTO = 0, TP_REDUCE_FUSION_OFF = 1 };
  * single block (R = C = 1) the reduce runs on s_compute, as nothing could
  * overlap it, and so it does (in GEMM2's epilogue, reduce_fusion AUTO) for a
  * block whose reduction the next GEMMs are too short to cover; where that
- * leaves s_reduce nothing to do the call keeps to s_compute.  The calls are
- * capturable into a HIP graph (no memsets, no
- * allocation, no host synchronisation).
+ * leaves s_reduce nothing to do the call keeps to s_compute.  On s_compute
+ * alone the chunks overlap nothing, so GEMM1 then runs once over all M rows
+ * (larger tiles); each chunk keeps its GEMM2 where its sum folds into that
+ * GEMM2, and otherwise the layer runs as the single block (R = C = 1).  The
+ * calls are capturable into a HIP graph (no memsets, no allocation, no host
+ * synchronisation).
  * Chunking never changes a result bit: each output element is accumulated in
  * the same order whatever R and C are.  With sequence parallelism (S > 1) the
  * gather of chunk r+1's input rows runs on s_reduce beside chunk r's GEMMs,

@@ -417,19 +417,47 @@ bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_l
   return false;
 }
 
+// The layer as a single block (R = C = 1).
+MlpPlan one_block(const MlpPlan& pl) {
+  MlpPlan w = pl;
+  w.R = w.C = 1;
+  w.Mr = pl.M;
+  w.Hc = pl.H;
+  return w;
+}
+
+// Whether GEMM1 can run over every row of the layer in one launch: the
+// kernels' 32-bit index range, and X read in place as at most kMaxABlocks
+// blocks of whole tiles.
+bool gemm1_spans_layer(const tp_mlp_args *a, const MlpPlan& w) {
+  if (w.M * w.F >= (int64_t(1) << 31) || w.M * w.H >= (int64_t(1) << 31)) return false;
+  if (!w.x_in_place) return true;
+  const GemmArgs g1 = chunk_gemm1(a, w, 0);
+  return g1.a_blk_rows == 0 || (w.M / w.sq.Ms <= kMaxABlocks && gemm_blocks_ok(g1, w.epi1));
+}
+
+int launch_gemm1(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0) {
+  const GemmArgs g1 = chunk_gemm1(a, pl, r);
+  hipEvent_t t0 = timing_begin(s0);
+  const hipError_t e = gemm_launch(g1, pl.epi1, s0);
+  if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
+  timing_end(t0, s0, TP_KERNEL_GEMM1, 2.0 * pl.Mr * pl.F * pl.H);
+  return TP_OK;
+}
+
 // Row chunk r of one forward layer: GEMM1 and, per column block, GEMM2 and its
 // reduction (in GEMM2's epilogue, or handed to s1 through ev_blocks[c] when
 // `two`).  `last`: nothing follows this chunk on s0, so its final block's
 // reduction runs alone and takes the whole chip (a one-shot grid) instead of
 // the share sized to run beside a GEMM.  `weigh`: as in fused_block.
+// `gemm1`: false where one earlier GEMM1 launch already covered every row.
 int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_t s0, hipStream_t s1, bool two,
-                  hipEvent_t *ev_blocks, bool last, bool weigh) {
+                  hipEvent_t *ev_blocks, bool last, bool weigh, bool gemm1 = true) {
   const int64_t es = pl.es, H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
-  const GemmArgs g1 = chunk_gemm1(a, pl, r);
-  hipEvent_t t0 = timing_begin(s0);
-  hipError_t e = gemm_launch(g1, pl.epi1, s0);
-  if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
-  timing_end(t0, s0, TP_KERNEL_GEMM1, 2.0 * Mr * F * H);
+  int rc0 = gemm1 ? launch_gemm1(a, pl, r, s0) : TP_OK;
+  if (rc0 != TP_OK) return rc0;
+  hipEvent_t t0 = nullptr;
+  hipError_t e;
   std::vector<const float *> parts(static_cast<size_t>(a->P));
   for (int64_t c = 0; c < pl.C; ++c) {
     const int64_t zoff = r * Mr * H + c * Hc;
@@ -685,14 +713,34 @@ int tpshard::colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stre
     a = &own;
   }
   hipStream_t s0 = static_cast<hipStream_t>(s_compute), s1 = static_cast<hipStream_t>(s_reduce);
-  const int64_t R = pl.R, C = pl.C, Mr = pl.Mr, H = pl.H, es = pl.es;
   const bool gather = pl.gather;
   // The reduce stream only pays when a later block's GEMMs can run beside an
   // earlier block's reduce or gather; with a single block, or where every
   // block's reduction goes into GEMM2's epilogue and nothing is gathered
   // beside, the hand-off (an event record and a cross-queue wait, about 10 us
   // each way on MI355X) is pure latency.
-  const bool two = (s0 != s1) && R * C > 1 && ((gather && R > 1) || any_block_beside(a, pl, true, true));
+  const bool two = (s0 != s1) && pl.R * pl.C > 1 && ((gather && pl.R > 1) || any_block_beside(a, pl, true, true));
+  // On one stream the row chunks overlap nothing: they only cut GEMM1 into
+  // smaller launches with smaller tiles.  Where every chunk's sum goes into
+  // its GEMM2's epilogue, GEMM1 therefore runs once over all rows and each
+  // chunk keeps its GEMM2 (GPT-3 6.7B at TP = 8, R = 2: GEMM1 over 8192 rows
+  // in 103 us against two 4096-row launches of 67 us, step 371-372 against
+  // 389 us; as one block, 385-387 us, its 8192-row GEMM2 with the sum taking
+  // 295 us against 2 x 137).  Where no chunk's sum folds (too many peers for
+  // a small block's epilogue, or fusion off) or there is nothing to sum, the
+  // layer runs as one block, whose sum may still fold.  A row's result is
+  // the same bits however the rows and columns are cut.
+  const MlpPlan whole = one_block(pl);
+  const MlpPlan *run = &pl;
+  bool gemm1_whole = false;
+  if (!two && pl.R * pl.C > 1 && !pl.y_chunk && gemm1_spans_layer(a, whole)) {
+    GemmArgs gr{};
+    if (pl.reduce && fused_block(a, pl, pl.R - 1, pl.C - 1, false, true, true, &gr))
+      gemm1_whole = pl.R > 1;
+    else
+      run = &whole;
+  }
+  const int64_t R = run->R, C = run->C, Mr = run->Mr, H = pl.H, es = pl.es;
   hipEvent_t *ev = nullptr;
   if (two) {
     if ((rc = get_events(static_cast<size_t>(R * C + R + 2), &ev)) != TP_OK) return rc;
@@ -715,17 +763,23 @@ int tpshard::colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stre
     }
     return TP_OK;
   };
-  if (gather && (rc = gather_chunk(0)) != TP_OK) return rc;
+  if (gather && gemm1_whole) {
+    if ((rc = gather_rows(a->X_shards, pl.sq.Ms, 0, pl.M, H, es, const_cast<void *>(a->X), s0)) != TP_OK) return rc;
+  } else if (gather && (rc = gather_chunk(0)) != TP_OK) {
+    return rc;
+  }
   if (two && gather && R > 1) {
     if ((e = hipEventRecord(ev_fork, s0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(s1, ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
+  if (gemm1_whole && (rc = launch_gemm1(a, whole, 0, s0)) != TP_OK) return rc;
   for (int64_t r = 0; r < R; ++r) {
     // The next chunk's input rows travel on s_reduce while this chunk computes.
-    if (gather && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
+    if (gather && !gemm1_whole && r + 1 < R && (rc = gather_chunk(r + 1)) != TP_OK) return rc;
     if (gather && two && r > 0 && (e = hipStreamWaitEvent(s0, ev_gat[r], 0)) != hipSuccess)
       return hip_fail(e, "hipStreamWaitEvent");
-    if ((rc = enqueue_chunk(a, pl, r, s0, s1, two, two ? ev_red + r * C : nullptr, r + 1 == R, true)) != TP_OK)
+    if ((rc = enqueue_chunk(a, *run, r, s0, s1, two, two ? ev_red + r * C : nullptr, r + 1 == R, true,
+                            !gemm1_whole)) != TP_OK)
       return rc;
   }
   if (two) {

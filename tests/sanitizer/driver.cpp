@@ -403,6 +403,30 @@ void mlp_calls() {
                        "valid forward");
                 ok += rc == TP_OK;
               }
+        // X read where its sequence blocks lie (X = NULL); with 256-row blocks
+        // GEMM1 may cover several, or (one stream, the chunks' sums folded
+        // but not the whole layer's) every block in one launch.
+        if (S > 1 && dtype == TP_BF16) {
+          const int64_t Mb = 256 * S;
+          MlpBufs bb = mlp_bufs(Mb, H, F, P, S, dtype);
+          for (int64_t R : {1, 2, 4, 8})
+            for (int64_t C : {1, 2})
+              for (int32_t layout : {TP_WEIGHTS_MATH, TP_WEIGHTS_LINEAR})
+                for (int32_t fusion : {TP_REDUCE_FUSION_AUTO, TP_REDUCE_FUSION_OFF}) {
+                  if (Mb % R) continue;
+                  tp_mlp_args a = mlp_args(bb, dtype, R, C, P);
+                  a.X = nullptr;
+                  a.seq_splits = S;
+                  a.X_shards = bb.xs.data();
+                  a.Z_split = bb.zs.data();
+                  a.Z_out = nullptr;
+                  a.weight_layout = layout;
+                  a.reduce_fusion = fusion;
+                  const int rc = note(tp_colrow_mlp(&a, nullptr, nullptr));
+                  expect(rc == TP_OK || rc == TP_ERR_UNSUPPORTED, "valid forward, X in place");
+                  ok += rc == TP_OK;
+                }
+        }
         // each rejection
         tp_mlp_args a = mlp_args(b, dtype, 1, 1, P);
         a.row_chunks = 3;

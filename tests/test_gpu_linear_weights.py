@@ -24,12 +24,14 @@ def setup_module(_):
     require_gpu()
 
 
-def _forward(X, A, B, peers, *, layout, R=1, C=1, h_out=False, seq=0, bias=None):
+def _forward(X, A, B, peers, *, layout, R=1, C=1, h_out=False, seq=0, bias=None, noalloc=False):
     """One forward call into guarded buffers (two streams); returns CPU copies
-    of Y, Z_i, the sum (Z_out, or the concatenated Z_split blocks) and H_out."""
+    of Y, Z_i, the sum (Z_out, or the concatenated Z_split blocks) and H_out.
+    noalloc: through the allocation-free entry point, which keeps the row
+    chunks (Y is then not returned)."""
     M, H = X.shape
     F = A.shape[0] if layout == tp.TP_WEIGHTS_LINEAR else A.shape[1]
-    Y = Guarded((M, F), X.dtype)
+    Y = None if noalloc else Guarded((M, F), X.dtype)
     Z = Guarded((M, H), torch.float32)
     Zo = Guarded((M, H), torch.float32) if (peers and not seq) else None
     Hs = Guarded((M, F), X.dtype) if h_out else None
@@ -40,14 +42,18 @@ def _forward(X, A, B, peers, *, layout, R=1, C=1, h_out=False, seq=0, bias=None)
         kw["X_shards"] = [b.clone() for b in torch.chunk(X, seq)]
         kw["Z_split"] = [g.t for g in Zs]
         X = None
-    tp.tp_colrow_mlp(X, A, B, Y.t, Z.t, Z_out=Zo.t if Zo is not None else None,
-                     H_out=Hs.t if Hs is not None else None, **kw)
+    kw.update(Z_out=Zo.t if Zo is not None else None, H_out=Hs.t if Hs is not None else None)
+    if noalloc:
+        tp.tp_colrow_mlp_noalloc(X, A, B, Z.t, **kw)
+    else:
+        tp.tp_colrow_mlp(X, A, B, Y.t, Z.t, **kw)
     torch.cuda.synchronize()
-    outs = [Y, Z] + ([Zo] if Zo is not None else []) + ([Hs] if Hs is not None else []) + (Zs or [])
+    outs = [Z] + ([Y] if Y is not None else []) + ([Zo] if Zo is not None else []) + \
+        ([Hs] if Hs is not None else []) + (Zs or [])
     for g in outs:
         assert g.guards_intact(), "write outside an output buffer"
     total = Zo.t.cpu() if Zo is not None else (torch.cat([g.t.cpu() for g in Zs]) if seq else None)
-    return Y.t.cpu(), Z.t.cpu(), total, (Hs.t.cpu() if Hs is not None else None)
+    return (Y.t.cpu() if Y is not None else None), Z.t.cpu(), total, (Hs.t.cpu() if Hs is not None else None)
 
 
 @pytest.mark.parametrize("M,H,F,R,C,P,opts", [
@@ -76,6 +82,14 @@ def test_forward_linear_layout_same_bits(M, H, F, R, C, P, opts):
     for a, b in zip(got, ref):
         if b is not None:
             assert np.array_equal(bits(a), bits(b))
+    if R * C > 1:
+        # Every row chunk kept (one stream may merge their GEMM1s, or run the layer as one block):
+        # each block's GEMM2 reads its rows of B_i^T at its offset.
+        kept = _forward(X, A.t().contiguous(), B.t().contiguous(), peers, layout=tp.TP_WEIGHTS_LINEAR, noalloc=True,
+                        **kw)
+        for a, b in zip(kept[1:], ref[1:]):
+            if b is not None:
+                assert np.array_equal(bits(a), bits(b))
 
 
 def test_forward_linear_shards_read_in_place():

@@ -23,21 +23,43 @@ def setup_module(_):
     require_gpu()
 
 
-def run_rank(X, A_i, B_i, *, R=1, C=1, peers=(), act=tp.TP_ACT_GELU_ERF, two_streams=False):
-    """One tp_colrow_mlp call into canary-guarded outputs; returns CPU copies."""
+def _call_rank(X, A_i, B_i, *, R, C, peers, act, two_streams, fusion=tp.TP_REDUCE_FUSION_AUTO, noalloc=False):
     M, H = X.shape
     F = A_i.shape[1]
-    Y = Guarded((M, F), X.dtype)
+    Y = None if noalloc else Guarded((M, F), X.dtype)
     Z = Guarded((M, H), torch.float32)
     Zo = Guarded((M, H), torch.float32) if peers else None
     s0 = torch.cuda.current_stream()
-    s1 = torch.cuda.Stream() if two_streams else s0
-    tp.tp_colrow_mlp(X, A_i, B_i, Y.t, Z.t, row_chunks=R, col_chunks=C, peer_partials=list(peers),
-                     Z_out=Zo.t if Zo is not None else None, act=act, s_compute=s0, s_reduce=s1)
+    kw = dict(row_chunks=R, col_chunks=C, peer_partials=list(peers), Z_out=Zo.t if Zo is not None else None,
+              act=act, reduce_fusion=fusion, s_compute=s0, s_reduce=torch.cuda.Stream() if two_streams else s0)
+    if noalloc:
+        tp.tp_colrow_mlp_noalloc(X, A_i, B_i, Z.t, **kw)
+    else:
+        tp.tp_colrow_mlp(X, A_i, B_i, Y.t, Z.t, **kw)
     torch.cuda.synchronize()
-    for g in (Y, Z) + ((Zo,) if Zo is not None else ()):
-        assert g.guards_intact(), "write outside an output buffer"
-    return Y.t.cpu(), Z.t.cpu(), (Zo.t.cpu() if Zo is not None else None)
+    for g in (Y, Z, Zo):
+        assert g is None or g.guards_intact(), "write outside an output buffer"
+    return [g.t.cpu() if g is not None else None for g in (Y, Z, Zo)]
+
+
+def run_rank(X, A_i, B_i, *, R=1, C=1, peers=(), act=tp.TP_ACT_GELU_ERF, two_streams=False):
+    """One tp_colrow_mlp call into canary-guarded outputs; returns CPU copies
+    of Y, Z_i and Z_out.  Where a schedule on one stream may merge the row
+    chunks (one GEMM1 over all rows, or the layer as one block), the two
+    schedules that keep every chunk run too and must give the same bits: the
+    allocation-free entry point (Y kept one chunk at a time) and two streams
+    with the separate reduction beside the GEMMs."""
+    kw = dict(R=R, C=C, peers=peers, act=act)
+    out = _call_rank(X, A_i, B_i, two_streams=two_streams, **kw)
+    if R * C > 1:
+        kept = _call_rank(X, A_i, B_i, two_streams=two_streams, noalloc=True, **kw)
+        for a, b in zip(out[1:], kept[1:]):
+            assert (a is None and b is None) or np.array_equal(bits(a), bits(b))
+        if peers:
+            kept = _call_rank(X, A_i, B_i, two_streams=True, fusion=tp.TP_REDUCE_FUSION_OFF, **kw)
+            for a, b in zip(out, kept):
+                assert np.array_equal(bits(a), bits(b))
+    return tuple(out)
 
 
 def _bf16_exact(x64):
@@ -342,19 +364,24 @@ def test_row_parallel_bias_integer_exact(M, H, F, Rc, Cc, P):
 
 
 def _run_fusion(X, A, B, peers, *, fusion, R=1, C=1, bias=None, z_out=True, in_place=False, x_next=False,
-                two=False):
-    """One call into guarded outputs; returns the CPU copies of Z, Z_out and X_next."""
+                two=False, noalloc=False):
+    """One call into guarded outputs; returns the CPU copies of Y (None through
+    the allocation-free entry point, which keeps Y to itself), Z, Z_out and X_next."""
     M, H = X.shape
     F = A.shape[1]
-    Y = Guarded((M, F), X.dtype)
+    Y = None if noalloc else Guarded((M, F), X.dtype)
     Z = Guarded((M, H), torch.float32)
     Zo = Guarded((M, H), torch.float32) if (z_out and not in_place) else None
     Xn = Guarded((M, H), X.dtype) if x_next else None
     s0 = torch.cuda.current_stream()
-    tp.tp_colrow_mlp(X, A, B, Y.t, Z.t, row_chunks=R, col_chunks=C, peer_partials=list(peers),
-                     Z_out=Z.t if in_place else (Zo.t if Zo is not None else None), bias=bias,
-                     X_next=Xn.t if Xn is not None else None, reduce_fusion=fusion,
-                     s_compute=s0, s_reduce=torch.cuda.Stream() if two else s0)
+    kw = dict(row_chunks=R, col_chunks=C, peer_partials=list(peers),
+              Z_out=Z.t if in_place else (Zo.t if Zo is not None else None), bias=bias,
+              X_next=Xn.t if Xn is not None else None, reduce_fusion=fusion,
+              s_compute=s0, s_reduce=torch.cuda.Stream() if two else s0)
+    if noalloc:
+        tp.tp_colrow_mlp_noalloc(X, A, B, Z.t, **kw)
+    else:
+        tp.tp_colrow_mlp(X, A, B, Y.t, Z.t, **kw)
     torch.cuda.synchronize()
     outs = [g for g in (Y, Z, Zo, Xn) if g is not None]
     assert all(g.guards_intact() for g in outs), "write outside an output buffer"
@@ -368,8 +395,11 @@ def _run_fusion(X, A, B, peers, *, fusion, R=1, C=1, bias=None, z_out=True, in_p
     (512, 384, 256, 2, 1, 1, {"z_out": False, "x_next": True}),    # only the next layer's input
     (515, 256, 96, 1, 1, 1, {"bias": True}),                       # no peers: the bias alone
     (1000, 512, 256, 4, 2, 2, {"bias": True, "two": True}),        # only the final block folds
-    (1000, 512, 256, 3, 2, 2, {"bias": True, "x_next": True}),     # serial: every block folds at its column offset
-    (300, 264, 192, 4, 3, 3, {"x_next": True, "in_place": True}),  # serial, ragged rows, 3 x 3 blocks, in place
+    (1000, 512, 256, 3, 2, 2, {"bias": True, "x_next": True}),     # one stream: one GEMM1, each block folds at its offsets
+    (300, 264, 192, 4, 3, 3, {"x_next": True, "in_place": True}),  # the same, ragged rows, 3 x 3 blocks, in place
+    # without a Y workspace every chunk keeps its GEMM1 as well
+    (1000, 512, 256, 3, 2, 2, {"bias": True, "x_next": True, "noalloc": True}),
+    (300, 264, 192, 4, 3, 3, {"x_next": True, "in_place": True, "noalloc": True}),
     (512, 384, 256, 5, 1, 1, {}),                                  # 4 peers: separate reduction
     (520, 392, 200, 3, 1, 1, {}),                                  # K % 32 != 0: separate reduction
     # the 256-row tiles, the tile staged through LDS in the epilogue: 256 x 128, 256 x 256 (in place),
@@ -381,6 +411,7 @@ def _run_fusion(X, A, B, peers, *, fusion, R=1, C=1, bias=None, z_out=True, in_p
     (2000, 4096, 256, 16, 1, 1, {"bias": True}),
     (4096, 4096, 256, 8, 2, 1, {"bias": True, "two": True}),
     (2048, 2048, 256, 17, 1, 1, {}),
+    (2048, 2048, 512, 8, 2, 2, {"bias": True, "noalloc": True}),   # 256-row tiles, each block at its offsets
 ])
 def test_reduce_fusion_same_bits(M, H, F, P, Rc, Cc, opts):
     """GEMM2 with the block's reduction folded into its epilogue writes the
@@ -415,7 +446,8 @@ def test_reduce_fusion_same_bits(M, H, F, P, Rc, Cc, opts):
     (64, 256, 512, 2, 1, 1, {}),                                   # the tiny fp32 workload's rank
     (77, 45, 51, 3, 1, 1, {"bias": True, "x_next": True}),         # ragged everything, fp32 next input
     (130, 129, 65, 4, 1, 1, {"in_place": True}),                   # Z_out = Z_i
-    (130, 128, 65, 3, 2, 2, {"bias": True}),                       # serial: every block folds
+    (130, 128, 65, 3, 2, 2, {"bias": True}),                       # one stream: one GEMM1, every block folds
+    (130, 128, 65, 3, 2, 2, {"bias": True, "noalloc": True}),      # every chunk's GEMM1 kept too
     (130, 128, 65, 3, 2, 2, {"bias": True, "two": True}),          # only the final block folds
 ])
 def test_reduce_fusion_same_bits_fp32(M, H, F, P, Rc, Cc, opts):
@@ -503,7 +535,9 @@ def test_fusion_taken_where_the_rule_says(M, H, F, P, fused):
 def test_timing_files_the_tail_reduction_apart(two_streams):
     """On a chunked two-stream schedule the last block's reduction, which no
     GEMM runs beside, is timed as reduce_tail and the earlier blocks' as
-    reduce; on one stream every block's reduction is reduce."""
+    reduce; on one stream, where no chunk's sum fits GEMM2's epilogue (7
+    peers on small blocks), the chunks run as one block: one GEMM1, one
+    reduce."""
     announce(f"mlp timing of the tail reduction two_streams={two_streams}")
     M, H, F, P, Rc = 512, 384, 256, 8, 2
     X = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
@@ -521,7 +555,8 @@ def test_timing_files_the_tail_reduction_apart(two_streams):
         st = tp.tp_timing_read()
     finally:
         tp.tp_timing_enable(False)
-    assert st["reduce"]["launches"] == (Rc - 1 if two_streams else Rc)
+    assert st["reduce"]["launches"] == (Rc - 1 if two_streams else 1)
+    assert st["gemm1"]["launches"] == (Rc if two_streams else 1)
     assert st["reduce_tail"]["launches"] == (1 if two_streams else 0)
     assert st["reduce_tail"]["work"] == (4.0 * (P + 1) * (M // Rc) * H if two_streams else 0.0)
 
@@ -532,10 +567,11 @@ def test_two_streams_fold_uncovered_reductions(M, H, F, Rc, Cc, P, beside):
     """On two streams a block's reduction runs beside the next GEMMs only where
     they are long enough to cover it; otherwise it goes into its GEMM2's
     epilogue, and where that leaves nothing for the second stream the schedule
-    keeps to one.  First case: chunk 0's sum of 8 partials (151 MB) against
-    the next chunk's 8.6 GFLOP, so both chunks fold; second: the GPT-3 175B
-    block ratio (F = 6144), three reductions beside and the final one folded.
-    The sums are the same bits as with the separate reduction."""
+    keeps to one, with one GEMM1 over all rows.  First case: chunk 0's sum of
+    8 partials (151 MB) against the next chunk's 8.6 GFLOP, so both chunks
+    fold; second: the GPT-3 175B block ratio (F = 6144), three reductions
+    beside and the final one folded.  The sums are the same bits as with the
+    separate reduction."""
     announce(f"mlp uncovered reductions M={M} H={H} F={F} R={Rc} C={Cc} P={P}")
     X = inputs.normal((M, H), 381, 1.0, "bf16").cuda()
     A = inputs.normal((H, F), 382, 1.0 / np.sqrt(H), "bf16").cuda()
@@ -560,7 +596,71 @@ def test_two_streams_fold_uncovered_reductions(M, H, F, Rc, Cc, P, beside):
     assert st["reduce"]["launches"] == beside and st["reduce_tail"]["launches"] == 0
     assert st["gemm2_reduce"]["launches"] == Rc * Cc - beside
     assert st["gemm2"]["launches"] == beside
+    assert st["gemm1"]["launches"] == (Rc if beside else 1)
     assert torch.equal(Zo, Zo2) and torch.equal(Z, Z2)
+
+@pytest.mark.parametrize("Rc,Cc,act,h_out,folds", [(2, 1, tp.TP_ACT_GELU_ERF, True, 2), (2, 2, tp.TP_ACT_NONE, False, 1),
+                                               (4, 1, tp.TP_ACT_GELU_ERF, False, 1)])
+def test_one_stream_merges_the_chunks(Rc, Cc, act, h_out, folds):
+    """Row chunks on one stream overlap nothing, so GEMM1 runs once over all
+    rows; where each chunk's block folds its sum into GEMM2 (2048 x 2048, the
+    256-row tiles) the blocks keep their GEMM2s, and where none does (7 peers
+    on the small tiles) the layer runs as one block whose sum folds.  Y,
+    H_out, Z_i and the sum are the same bits as the chunked two-stream schedule
+    (the separate reduction beside the GEMMs) and as the allocation-free entry
+    point, which keeps every chunk (Y holds one chunk), and match the oracle on
+    sampled rows."""
+    announce(f"mlp one stream, chunks merged R={Rc} C={Cc} act={act} h_out={h_out}")
+    M, H, F, P = 4096, 2048, 512, 8
+    X = inputs.normal((M, H), 461, 1.0, "bf16")
+    A = inputs.normal((H, F), 462, 1.0 / np.sqrt(H), "bf16")
+    B = inputs.normal((F, H), 463, 1.0 / np.sqrt(F), "bf16")
+    peers_cpu = [inputs.normal((M, H), 470 + p) for p in range(P - 1)]
+    Xd, Ad, Bd, peers = X.cuda(), A.cuda(), B.cuda(), [p.cuda() for p in peers_cpu]
+
+    def run(two, fusion, noalloc=False):
+        Y = Guarded((M, F), torch.bfloat16)
+        Hs = Guarded((M, F), torch.bfloat16) if h_out else None
+        Z, Zo = Guarded((M, H), torch.float32), Guarded((M, H), torch.float32)
+        s0 = torch.cuda.current_stream()
+        kw = dict(row_chunks=Rc, col_chunks=Cc, peer_partials=peers, Z_out=Zo.t, act=act, reduce_fusion=fusion,
+                  H_out=Hs.t if h_out else None, s_compute=s0, s_reduce=torch.cuda.Stream() if two else s0)
+        if noalloc:
+            tp.tp_colrow_mlp_noalloc(Xd, Ad, Bd, Z.t, **kw)
+        else:
+            tp.tp_colrow_mlp(Xd, Ad, Bd, Y.t, Z.t, **kw)
+        torch.cuda.synchronize()
+        outs = [Y, Z, Zo] + ([Hs] if h_out else [])
+        assert all(g.guards_intact() for g in outs), "write outside an output buffer"
+        return [None if (noalloc and g is Y) else g.t.cpu() for g in outs]
+
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        got = run(False, tp.TP_REDUCE_FUSION_AUTO)
+        st = tp.tp_timing_read()
+        chunked = run(True, tp.TP_REDUCE_FUSION_OFF)
+        st_chunked = tp.tp_timing_read()
+        kept = run(False, tp.TP_REDUCE_FUSION_AUTO, noalloc=True)
+        st_kept = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    assert st["gemm1"]["launches"] == 1 and st["gemm2_reduce"]["launches"] == folds
+    assert st["gemm2"]["launches"] == 0 and st["reduce"]["launches"] == 0
+    assert st_chunked["gemm1"]["launches"] == Rc and st_chunked["gemm2"]["launches"] == Rc * Cc
+    # (at R = C = 2 each kept block takes the small tiles, whose epilogue sums at most 3 peers: separate reductions)
+    assert st_kept["gemm1"]["launches"] == Rc
+    assert st_kept["gemm2_reduce"]["launches"] + st_kept["gemm2"]["launches"] == Rc * Cc
+    for a, b, c in zip(got, chunked, kept):
+        assert np.array_equal(bits(a), bits(b))
+        if c is not None:
+            assert np.array_equal(bits(a), bits(c))
+    rows = np.linspace(0, M - 1, 128).astype(np.int64)
+    z0 = O.mlp_rank_rows(X, A, B, rows, act=O.GELU_ERF if act == tp.TP_ACT_GELU_ERF else O.GELU_NONE)
+    assert rel_err(got[1][torch.from_numpy(rows)], z0) <= TOL_BF16
+    total = z0 + sum(p[torch.from_numpy(rows)].double().numpy() for p in peers_cpu)
+    assert rel_err(got[2][torch.from_numpy(rows)], total) <= TOL_BF16
+
 
 def test_max_ranks_integer_exact():
     """P = 64 virtual ranks (63 peers), chunked, on two streams: exact."""

@@ -37,10 +37,12 @@ def _f64(t):
 
 
 def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bias=None, two_streams=True,
-               fusion=tp.TP_REDUCE_FUSION_AUTO, in_place=False):
+               fusion=tp.TP_REDUCE_FUSION_AUTO, in_place=False, noalloc=False):
     """tp_colrow_mlp with X_shards and Z_split into guarded buffers; returns CPU
     copies (X gathered, Y, Z_i, [Z blocks]).  in_place: X = None, GEMM1 reads
-    the blocks where they lie (the returned X is then the untouched workspace)."""
+    the blocks where they lie (the returned X is then the untouched workspace).
+    noalloc: through the allocation-free entry point, which keeps the row
+    chunks (the returned Y is then the untouched workspace)."""
     S = len(X_blocks)
     Ms, H = X_blocks[0].shape
     M, F = Ms * S, A.shape[1]
@@ -50,10 +52,12 @@ def sp_forward(X_blocks, A, B, peers, *, Rc=1, Cc=1, act=tp.TP_ACT_GELU_ERF, bia
     Zs = [Guarded((Ms, H), torch.float32) for _ in range(S)]
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream() if two_streams else s0
-    tp.tp_colrow_mlp(None if in_place else Xw.t, A, B, Y.t, Z.t, row_chunks=Rc, col_chunks=Cc,
-                     peer_partials=list(peers), act=act,
-                     s_compute=s0, s_reduce=s1, bias=bias, X_shards=list(X_blocks), Z_split=[g.t for g in Zs],
-                     reduce_fusion=fusion)
+    kw = dict(row_chunks=Rc, col_chunks=Cc, peer_partials=list(peers), act=act, s_compute=s0, s_reduce=s1, bias=bias,
+              X_shards=list(X_blocks), Z_split=[g.t for g in Zs], reduce_fusion=fusion)
+    if noalloc:
+        tp.tp_colrow_mlp_noalloc(None if in_place else Xw.t, A, B, Z.t, **kw)
+    else:
+        tp.tp_colrow_mlp(None if in_place else Xw.t, A, B, Y.t, Z.t, **kw)
     torch.cuda.synchronize()
     for g in [Xw, Y, Z] + Zs:
         assert g.guards_intact(), "write outside an output buffer"
@@ -103,8 +107,9 @@ def test_forward_integer_exact(M, H, F, Rc, Cc, P, S):
     (3000, 4096, 256, 1, 1, 4, 2),
 ])
 def test_forward_reduce_fusion_same_bits(M, H, F, Rc, Cc, P, S):
-    """The reduce-scatter folded into GEMM2's epilogue (serial schedule: every
-    block folds) gives the separate kernel's bits in every sequence block."""
+    """The reduce-scatter folded into GEMM2's epilogue (one stream: one GEMM1
+    over all rows, every block folds) gives the separate kernel's bits in
+    every sequence block."""
     announce(f"seqpar reduce fusion M={M} H={H} F={F} R={Rc} C={Cc} P={P} S={S}")
     Ms = M // S
     Xb = [inputs.normal((Ms, H), seed=780 + j, dtype="bf16").cuda() for j in range(S)]
@@ -143,6 +148,44 @@ def test_forward_blocks_read_in_place_same_bits(M, H, F, Rc, Cc, P, S, dt):
     kw = dict(Rc=Rc, Cc=Cc)
     got = sp_forward(Xb, A, B, peers, in_place=True, **kw)
     ref = sp_forward(Xb, A, B, peers, **kw)
+    for a, b in zip(got[1:3], ref[1:3]):
+        assert np.array_equal(bits(a), bits(b))
+    for j in range(S):
+        assert np.array_equal(bits(got[3][j]), bits(ref[3][j])), j
+    if Rc > 1:
+        # The chunks kept (a one-stream schedule may read every block in one GEMM1): each chunk's rows
+        # at an offset into its block, or its blocks in turn.
+        kept = sp_forward(Xb, A, B, peers, in_place=True, noalloc=True, **kw)
+        assert np.array_equal(bits(kept[2]), bits(ref[2]))
+        for j in range(S):
+            assert np.array_equal(bits(kept[3][j]), bits(ref[3][j])), j
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_one_stream_gemm1_over_all_rows(in_place):
+    """One stream, 8 sequence blocks, R = 2: each chunk's sum folds into its
+    GEMM2 (4 blocks apiece), so GEMM1 runs once over all rows, read in place
+    from the 8 blocks or from X gathered whole first, and each chunk keeps its
+    GEMM2.  The same bits as the chunked two-stream schedule with the separate
+    reduce-scatter."""
+    announce(f"seqpar one stream, GEMM1 over all rows, in_place={in_place}")
+    M, H, F, P, S, Rc = 4096, 2048, 512, 8, 8, 2
+    Ms = M // S
+    Xb = [inputs.normal((Ms, H), seed=980 + j, dtype="bf16").cuda() for j in range(S)]
+    A = inputs.normal((H, F), seed=990, std=0.05, dtype="bf16").cuda()
+    B = inputs.normal((F, H), seed=991, std=0.05, dtype="bf16").cuda()
+    peers = [inputs.normal((M, H), seed=995 + p).cuda() for p in range(P - 1)]
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        got = sp_forward(Xb, A, B, peers, Rc=Rc, two_streams=False, in_place=in_place)
+        st = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    assert st["gemm1"]["launches"] == 1
+    assert st["gemm1"]["work"] == 2.0 * M * F * H
+    assert st["gemm2_reduce"]["launches"] == Rc and st["gemm2"]["launches"] == 0
+    ref = sp_forward(Xb, A, B, peers, Rc=Rc, fusion=tp.TP_REDUCE_FUSION_OFF, in_place=in_place)
     for a, b in zip(got[1:3], ref[1:3]):
         assert np.array_equal(bits(a), bits(b))
     for j in range(S):

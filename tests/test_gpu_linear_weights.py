@@ -24,11 +24,11 @@ def setup_module(_):
     require_gpu()
 
 
-def _forward(X, A, B, peers, *, layout, R=1, C=1, h_out=False, seq=0, bias=None, noalloc=False):
+def _forward(X, A, B, peers, *, layout, R=1, C=1, h_out=False, seq=0, bias=None, noalloc=False, one=False):
     """One forward call into guarded buffers (two streams); returns CPU copies
     of Y, Z_i, the sum (Z_out, or the concatenated Z_split blocks) and H_out.
     noalloc: through the allocation-free entry point, which keeps the row
-    chunks (Y is then not returned)."""
+    chunks (Y is then not returned).  one: s_reduce = s_compute."""
     M, H = X.shape
     F = A.shape[0] if layout == tp.TP_WEIGHTS_LINEAR else A.shape[1]
     Y = None if noalloc else Guarded((M, F), X.dtype)
@@ -37,7 +37,8 @@ def _forward(X, A, B, peers, *, layout, R=1, C=1, h_out=False, seq=0, bias=None,
     Hs = Guarded((M, F), X.dtype) if h_out else None
     Zs = [Guarded((M // seq, H), torch.float32) for _ in range(seq)] if seq else None
     kw = dict(row_chunks=R, col_chunks=C, peer_partials=list(peers), weight_layout=layout, bias=bias,
-              s_compute=torch.cuda.current_stream(), s_reduce=torch.cuda.Stream())
+              s_compute=torch.cuda.current_stream(),
+              s_reduce=torch.cuda.current_stream() if one else torch.cuda.Stream())
     if seq:
         kw["X_shards"] = [b.clone() for b in torch.chunk(X, seq)]
         kw["Z_split"] = [g.t for g in Zs]
@@ -65,6 +66,7 @@ def _forward(X, A, B, peers, *, layout, R=1, C=1, h_out=False, seq=0, bias=None,
     (2048, 2048, 512, 2, 1, 8, {"seq": 8}),            # sequence parallel: reduce-scattered, blocks in place
     (1024, 512, 256, 2, 1, 4, {"seq": 4}),             # the same on the small tiles (separate reduce-scatter)
     (256, 96, 64, 2, 1, 2, {"f32": True}),             # fp32 throughout
+    (4096, 2048, 512, 2, 1, 8, {"h_out": True, "one": True}),  # one stream: GEMM1 over all rows, each chunk's GEMM2 folds
 ])
 def test_forward_linear_layout_same_bits(M, H, F, R, C, P, opts):
     """A_i^T and B_i^T given as [F, H] and [H, F]: Y, Z_i, the sum and H_out
@@ -76,7 +78,7 @@ def test_forward_linear_layout_same_bits(M, H, F, R, C, P, opts):
     B = inputs.normal((F, H), 1103, 1.0 / np.sqrt(F), dt).cuda()
     peers = [inputs.normal((M, H), 1110 + p).cuda() for p in range(P - 1)]
     bias = inputs.normal((H,), 1109).cuda() if opts.get("bias") else None
-    kw = dict(R=R, C=C, h_out=opts.get("h_out", False), seq=opts.get("seq", 0), bias=bias)
+    kw = dict(R=R, C=C, h_out=opts.get("h_out", False), seq=opts.get("seq", 0), bias=bias, one=opts.get("one", False))
     ref = _forward(X, A, B, peers, layout=tp.TP_WEIGHTS_MATH, **kw)
     got = _forward(X, A.t().contiguous(), B.t().contiguous(), peers, layout=tp.TP_WEIGHTS_LINEAR, **kw)
     for a, b in zip(got, ref):

@@ -431,7 +431,10 @@ int tp_colrow_mlp_noalloc(const tp_mlp_args *args, tp_stream_t s_compute, tp_str
  * dependency across row chunks, so the reduction of layer l's chunk r runs on
  * s_reduce beside the GEMMs of layer l+1's earlier chunks; DominoTransformer's
  * inter_layer_overlap_forward).  Chunk r of layer l+1 waits only for chunk r
- * of layer l.  Each layer is validated as by tp_colrow_mlp (sequence
+ * of layer l.  Layers that would each keep to s_compute alone (every block's
+ * sum folded into its GEMM2's epilogue, as tp_colrow_mlp decides) have nothing
+ * to overlap and run one after another, each as tp_colrow_mlp runs it on one
+ * stream.  Each layer is validated as by tp_colrow_mlp (sequence
  * parallelism is not supported inside a stack); buffers other than a layer's
  * own inputs and outputs may be shared between layers (one Y_ws for all, X
  * buffers used in turn), since each chunk's reuse is ordered by the schedule.

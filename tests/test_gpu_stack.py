@@ -1,6 +1,6 @@
 """GPU parity of tp_colrow_mlp_stack (layers chained through the reduce's
-fused next-layer input, with the inter-layer overlap) and of the X_next
-output, against the oracle's layer stack."""
+fused next-layer input, with the inter-layer overlap or one after another)
+and of the X_next output, against the oracle's layer stack."""
 import numpy as np
 import pytest
 import torch
@@ -90,12 +90,17 @@ def run_stack(X0, layers, *, R=1, C=1, act=tp.TP_ACT_NONE, two_streams=True, kee
 
 
 @pytest.mark.parametrize("M,H,Fs,R,C,P,two", [
-    (512, 256, [128, 96], 2, 1, 4, True),      # inter-layer overlap over two row chunks
+    # every block's sum folds (at most 3 peers on the small tiles): the layers one after another
+    (512, 256, [128, 96], 2, 1, 4, True),
     (768, 384, [64, 64, 32], 3, 2, 3, True),
     (300, 264, [136, 64], 3, 2, 2, True),      # ragged tiles
     (256, 128, [64, 64], 1, 1, 2, True),       # one block: serial schedule
     (512, 256, [128, 128], 2, 2, 4, False),    # one stream
     (4096, 768, [768, 768], 2, 1, 4, True),    # GPT-2-small shape
+    # 7 peers: the sums run beside the GEMMs, the inter-layer overlap over the row chunks
+    (512, 256, [128, 96], 2, 1, 8, True),
+    (768, 384, [64, 64, 32], 3, 2, 8, True),
+    (300, 264, [136, 64], 3, 2, 8, True),      # ragged tiles
 ])
 def test_stack_integer_exact(M, H, Fs, R, C, P, two):
     """Exact integers through every layer: each Z_out and each next-layer input
@@ -129,11 +134,42 @@ def test_stack_linear_weights_same_bits(M, H, Fs, R, C, P):
         assert np.array_equal(bits(xn), bits(xr)), l
 
 
+def test_stack_layers_one_after_another():
+    """Layers whose every block's sum folds into its GEMM2 (chunks of 2048 x 2048
+    on the 256-row tiles, 7 peers, too much to sum beside the next GEMMs) run
+    one after another, each with one GEMM1 over all rows: the same bits in
+    every Z_out and next-layer input as the inter-layer overlap with the
+    separate reductions."""
+    announce("stack layer by layer")
+    M, H, Fs, P, R = 4096, 2048, [512, 512], 8, 2
+    X0 = inputs.normal((M, H), 1251, 1.0, "bf16")
+    layers = [{"A_i": inputs.normal((H, F), 1260 + l, 1.0 / np.sqrt(H), "bf16"),
+               "B_i": inputs.normal((F, H), 1270 + l, 1.0 / np.sqrt(F), "bf16"),
+               "peers": [inputs.normal((M, H), 1280 + 10 * l + p) for p in range(P - 1)],
+               "bias": inputs.normal((H,), 1295 + l)} for l, F in enumerate(Fs)]
+    tp.tp_timing_enable(True)
+    try:
+        tp.tp_timing_read()
+        got = run_stack(X0, layers, R=R, act=tp.TP_ACT_GELU_ERF)
+        st = tp.tp_timing_read()
+        ref = run_stack(X0, layers, R=R, act=tp.TP_ACT_GELU_ERF, fusion=tp.TP_REDUCE_FUSION_OFF)
+        st_ref = tp.tp_timing_read()
+    finally:
+        tp.tp_timing_enable(False)
+    assert st["gemm1"]["launches"] == len(Fs) and st["gemm2_reduce"]["launches"] == R * len(Fs)
+    assert st["reduce"]["launches"] == 0 and st["gemm2"]["launches"] == 0
+    assert st_ref["gemm1"]["launches"] == R * len(Fs) and st_ref["gemm2"]["launches"] == R * len(Fs)
+    for l, ((z, xn), (zr, xr)) in enumerate(zip(got, ref)):
+        assert np.array_equal(bits(z), bits(zr)), l
+        assert np.array_equal(bits(xn), bits(xr)), l
+
+
 @pytest.mark.parametrize("w", [GPT3_6P7B, GPT3_175B], ids=lambda w: w.name)
 def test_stack_tp8_sampled(w):
     """Two layers of a GPT-3 per-rank shape at TP = 8, as the bench's 2-layer
-    step runs them (R row chunks, C column blocks, two streams, the inter-layer
-    overlap): 128 rows of each layer's reduced output and of the next layer's
+    step runs them (R row chunks, C column blocks, two streams; the 175B layers
+    with the inter-layer overlap, the 6.7B ones one after another, every
+    chunk's sum folded): 128 rows of each layer's reduced output and of the next layer's
     bf16 input (64 per row chunk, each chunk's first and last among them)
     against the oracle's stack on those rows (rows stay independent through
     the stack).  The peers' partials of each layer are drawn, not computed."""

@@ -304,15 +304,19 @@ def test_error_leaves_outputs_untouched():
     assert Y.body_untouched() and Z.body_untouched()
 
 
-def test_graph_replay_matches_eager():
-    """The two-stream chunked call captured into a HIP graph: every replay,
-    with eager work and host synchronisation in between, equals the eager call."""
-    announce("mlp graph capture and replay")
+@pytest.mark.parametrize("P", [4, 8])
+def test_graph_replay_matches_eager(P):
+    """The chunked call offered two streams, captured into a HIP graph: with 3
+    peers every block's sum folds into its GEMM2 and the call keeps to one
+    stream (one GEMM1 over all rows); with 7 the small blocks' sums run on the
+    second stream beside the GEMMs.  Every replay, with eager work and host
+    synchronisation in between, equals the eager call."""
+    announce(f"mlp graph capture and replay P={P}")
     M, H, F, Rc, Cc = 1024, 512, 384, 2, 2
     X = inputs.normal((M, H), 401, 1.0, "bf16").cuda()
     A = inputs.normal((H, F), 402, 0.05, "bf16").cuda()
     B = inputs.normal((F, H), 403, 0.05, "bf16").cuda()
-    peers = [inputs.normal((M, H), 410 + p).cuda() for p in range(3)]
+    peers = [inputs.normal((M, H), 410 + p).cuda() for p in range(P - 1)]
     Y = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
     Z = torch.empty((M, H), device="cuda")
     Zo = torch.empty((M, H), device="cuda")

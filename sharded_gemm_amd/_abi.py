@@ -596,9 +596,10 @@ def tp_colrow_mlp_noalloc(X, A_i, B_i, Z_i, *, s_compute=None, s_reduce=None, pr
 
 
 def tp_colrow_mlp_stack(layers, s_compute=None, s_reduce=None, prepare=False):
-    """Forward layers in sequence with the inter-layer overlap; ``layers`` is a list
-    of dicts of tp_colrow_mlp's arguments (X, A_i, B_i, Y_ws, Z_i and keywords), each
-    layer but the last writing the next one's X through X_next."""
+    """Forward layers in sequence with the inter-layer overlap (or one after another
+    where each layer alone would keep to s_compute); ``layers`` is a list of dicts of
+    tp_colrow_mlp's arguments (X, A_i, B_i, Y_ws, Z_i and keywords), each layer but
+    the last writing the next one's X through X_next."""
     lib = load()
     built = [_mlp_args(**dict(layer)) for layer in layers]
     arr = (tp_mlp_args * max(1, len(built)))(*[b[0] for b in built])

@@ -8,7 +8,7 @@ import torch
 
 import sharded_gemm_amd as tp
 from sharded_gemm_amd import inputs
-from sharded_gemm_amd.workloads import GPT3_175B
+from sharded_gemm_amd.workloads import GPT3_175B, GPT3_6P7B
 from oracle import mlp as O
 from oracle import reduce as R
 
@@ -283,15 +283,17 @@ def _chunk_rows(M, Rc, per_chunk):
     return np.array(rows)
 
 
+@pytest.mark.parametrize("w", [GPT3_175B, GPT3_6P7B], ids=lambda w: w.name)
 @pytest.mark.parametrize("in_place", [True, False])
-def test_forward_gpt3_175b_sampled(in_place):
-    """The GPT-3 175B per-rank shape as the bench's sequence-parallel step runs
-    it (TP = 8: 8 sequence blocks, R = 2, C = 2, two streams; GEMM1 reading the
-    blocks where they lie, or after gathering them, when the gathered input
-    must equal the blocks), and 128 rows of the reduce-scattered output (64
-    per row chunk, each chunk's first and last among them) match the oracle's
-    rank-0 rows plus the drawn peers' rows."""
-    w = GPT3_175B
+def test_forward_gpt3_sampled(w, in_place):
+    """A GPT-3 per-rank shape as the bench's sequence-parallel step runs it
+    (TP = 8: 8 sequence blocks, R row chunks, C column blocks, two streams
+    offered; GEMM1 reading the blocks where they lie, or after gathering them,
+    when the gathered input must equal the blocks; for 6.7B with the blocks in
+    place the call keeps to one stream and one GEMM1 reads all 8 blocks), and
+    128 rows of the reduce-scattered output (64 per row chunk, each chunk's
+    first and last among them) match the oracle's rank-0 rows plus the drawn
+    peers' rows."""
     announce(f"seqpar forward {w.name} sampled in_place={in_place}")
     M, H, F, P, S = w.M, w.H, w.F, w.P, w.P
     Ms = M // S

@@ -388,10 +388,12 @@ enum { TP_REDUCE_FUSION_AUTO = 0, TP_REDUCE_FUSION_OFF = 1 };
  * single block (R = C = 1) the reduce runs on s_compute, as nothing could
  * overlap it, and so it does (in GEMM2's epilogue, reduce_fusion AUTO) for a
  * block whose reduction the next GEMMs are too short to cover; where that
- * leaves s_reduce nothing to do the call keeps to s_compute.  On s_compute
- * alone the chunks overlap nothing, so GEMM1 then runs once over all M rows
- * (larger tiles); each chunk keeps its GEMM2 where its sum folds into that
- * GEMM2, and otherwise the layer runs as the single block (R = C = 1).  The
+ * leaves s_reduce nothing to do the call keeps to s_compute.  GEMM1 runs
+ * once over all M rows (larger tiles, and no sum beside it) ahead of the
+ * blocks' GEMM2s wherever that leaves every block's sum where it would be
+ * with a GEMM1 per chunk; on s_compute alone the chunks overlap nothing, so
+ * each keeps its GEMM2 where its sum folds into that GEMM2, and otherwise the
+ * layer runs as the single block (R = C = 1).  The
  * calls are capturable into a HIP graph (no memsets, no allocation, no host
  * synchronisation).
  * Chunking never changes a result bit: each output element is accumulated in

@@ -365,7 +365,7 @@ GemmArgs block_gemm2(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t
 // also writes the next layer's input).  The kernel must take the block as well
 // (gemm_red_ok).
 bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, bool two, bool last, bool weigh,
-                 GemmArgs *gr) {
+                 GemmArgs *gr, bool g1_done = false) {
   const int64_t H = pl.H, F = pl.F, Mr = pl.Mr, Hc = pl.Hc;
   const bool f32 = pl.epi2 == kEpiPlainF32;
   if (!pl.reduce || a->reduce_fusion != TP_REDUCE_FUSION_AUTO || !(pl.epi2 == kEpiF32 || f32) ||
@@ -374,7 +374,8 @@ bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, 
   const bool final_block = last && c + 1 == pl.C;
   if (two && !final_block) {
     if (f32 || !weigh) return false;
-    const double next_flops = 2.0 * Mr * F * (c + 1 < pl.C ? Hc : H + Hc);
+    // (with every GEMM1 already done, the next block's GEMM2 alone)
+    const double next_flops = 2.0 * Mr * F * (c + 1 < pl.C || g1_done ? Hc : H + Hc);
     const double red_bytes = 4.0 * (a->P + 1) * Mr * Hc;
     if (red_bytes / kReduceByteRate <= kBesideShare * next_flops / kGemmFlopRate) return false;
   }
@@ -408,13 +409,28 @@ bool fused_block(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, int64_t c, 
 
 // Whether any block of the layer hands its reduction to s1 on a two-stream
 // schedule; `last_chunk_last`: nothing follows the layer's last chunk on s0.
-bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_last, bool weigh) {
+bool any_block_beside(const tp_mlp_args *a, const MlpPlan& pl, bool last_chunk_last, bool weigh,
+                      bool g1_done = false) {
   if (!pl.reduce) return false;
   GemmArgs gr{};
   for (int64_t r = 0; r < pl.R; ++r)
     for (int64_t c = 0; c < pl.C; ++c)
-      if (!fused_block(a, pl, r, c, true, last_chunk_last && r + 1 == pl.R, weigh, &gr)) return true;
+      if (!fused_block(a, pl, r, c, true, last_chunk_last && r + 1 == pl.R, weigh, &gr, g1_done)) return true;
   return false;
+}
+
+// Whether every block of the layer takes the same place on two streams
+// (beside the next GEMMs, or folded) when every GEMM1 runs first as when each
+// chunk's GEMM1 runs ahead of its GEMM2s.
+bool same_places_with_gemm1_first(const tp_mlp_args *a, const MlpPlan& pl) {
+  GemmArgs gr{};
+  for (int64_t r = 0; r < pl.R; ++r)
+    for (int64_t c = 0; c < pl.C; ++c) {
+      const bool last = r + 1 == pl.R;
+      if (fused_block(a, pl, r, c, true, last, true, &gr, false) != fused_block(a, pl, r, c, true, last, true, &gr, true))
+        return false;
+    }
+  return true;
 }
 
 // The layer as a single block (R = C = 1).
@@ -463,7 +479,7 @@ int enqueue_chunk(const tp_mlp_args *a, const MlpPlan& pl, int64_t r, hipStream_
     const int64_t zoff = r * Mr * H + c * Hc;
     const bool final_block = last && c + 1 == pl.C;
     GemmArgs gr{};
-    if (fused_block(a, pl, r, c, two, last, weigh, &gr)) {
+    if (fused_block(a, pl, r, c, two, last, weigh, &gr, !gemm1)) {
       const bool f32 = pl.epi2 == kEpiPlainF32;
       t0 = timing_begin(s0);
       e = gemm_launch(gr, f32 ? kEpiPlainF32Red : kEpiF32Red, s0);
@@ -733,6 +749,14 @@ int tpshard::colrow_mlp_run(const tp_mlp_args *a, tp_stream_t s_compute, tp_stre
   const MlpPlan whole = one_block(pl);
   const MlpPlan *run = &pl;
   bool gemm1_whole = false;
+  // On two streams, too, GEMM1 runs first over all rows where that moves no
+  // block's sum off the second stream: each sum then runs beside the next
+  // block's GEMM2 and none beside a GEMM1 (GPT-3 175B, R = 2, C = 2: the
+  // second chunk's GEMM1 ran 15-22 us slower beside the first chunk's last
+  // sum).
+  if (two && pl.R > 1 && !gather && !pl.y_chunk && gemm1_spans_layer(a, whole) &&
+      same_places_with_gemm1_first(a, pl))
+    gemm1_whole = true;
   if (!two && pl.R * pl.C > 1 && !pl.y_chunk && gemm1_spans_layer(a, whole)) {
     GemmArgs gr{};
     if (pl.reduce && fused_block(a, pl, pl.R - 1, pl.C - 1, false, true, true, &gr))

@@ -44,11 +44,12 @@ def _call_rank(X, A_i, B_i, *, R, C, peers, act, two_streams, fusion=tp.TP_REDUC
 
 def run_rank(X, A_i, B_i, *, R=1, C=1, peers=(), act=tp.TP_ACT_GELU_ERF, two_streams=False):
     """One tp_colrow_mlp call into canary-guarded outputs; returns CPU copies
-    of Y, Z_i and Z_out.  Where a schedule on one stream may merge the row
-    chunks (one GEMM1 over all rows, or the layer as one block), the two
-    schedules that keep every chunk run too and must give the same bits: the
-    allocation-free entry point (Y kept one chunk at a time) and two streams
-    with the separate reduction beside the GEMMs."""
+    of Y, Z_i and Z_out.  Where the schedule may merge the row chunks (one
+    GEMM1 over all rows, or on one stream the layer as one block), two
+    schedules that keep them apart run too and must give the same bits: the
+    allocation-free entry point (every chunk's GEMM1 apart, Y kept one chunk at
+    a time) and two streams with each block's separate reduction beside the
+    next block's GEMM2."""
     kw = dict(R=R, C=C, peers=peers, act=act)
     out = _call_rank(X, A_i, B_i, two_streams=two_streams, **kw)
     if R * C > 1:
@@ -537,11 +538,11 @@ def test_fusion_taken_where_the_rule_says(M, H, F, P, fused):
 
 @pytest.mark.parametrize("two_streams", [True, False])
 def test_timing_files_the_tail_reduction_apart(two_streams):
-    """On a chunked two-stream schedule the last block's reduction, which no
-    GEMM runs beside, is timed as reduce_tail and the earlier blocks' as
-    reduce; on one stream, where no chunk's sum fits GEMM2's epilogue (7
-    peers on small blocks), the chunks run as one block: one GEMM1, one
-    reduce."""
+    """On the two-stream schedule (GEMM1 first over all rows, then each block's
+    GEMM2 with its reduction beside the next) the last block's reduction, which
+    no GEMM runs beside, is timed as reduce_tail and the earlier blocks' as
+    reduce; on one stream, where no chunk's sum fits GEMM2's epilogue (7 peers
+    on small blocks), the chunks run as one block: one GEMM1, one reduce."""
     announce(f"mlp timing of the tail reduction two_streams={two_streams}")
     M, H, F, P, Rc = 512, 384, 256, 8, 2
     X = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
@@ -560,7 +561,7 @@ def test_timing_files_the_tail_reduction_apart(two_streams):
     finally:
         tp.tp_timing_enable(False)
     assert st["reduce"]["launches"] == (Rc - 1 if two_streams else 1)
-    assert st["gemm1"]["launches"] == (Rc if two_streams else 1)
+    assert st["gemm1"]["launches"] == 1          # every chunk's rows in one GEMM1, on either schedule
     assert st["reduce_tail"]["launches"] == (1 if two_streams else 0)
     assert st["reduce_tail"]["work"] == (4.0 * (P + 1) * (M // Rc) * H if two_streams else 0.0)
 
@@ -600,7 +601,7 @@ def test_two_streams_fold_uncovered_reductions(M, H, F, Rc, Cc, P, beside):
     assert st["reduce"]["launches"] == beside and st["reduce_tail"]["launches"] == 0
     assert st["gemm2_reduce"]["launches"] == Rc * Cc - beside
     assert st["gemm2"]["launches"] == beside
-    assert st["gemm1"]["launches"] == (Rc if beside else 1)
+    assert st["gemm1"]["launches"] == 1          # GEMM1 first over all rows, on either schedule
     assert torch.equal(Zo, Zo2) and torch.equal(Z, Z2)
 
 @pytest.mark.parametrize("Rc,Cc,act,h_out,folds", [(2, 1, tp.TP_ACT_GELU_ERF, True, 2), (2, 2, tp.TP_ACT_NONE, False, 1),
@@ -610,8 +611,8 @@ def test_one_stream_merges_the_chunks(Rc, Cc, act, h_out, folds):
     rows; where each chunk's block folds its sum into GEMM2 (2048 x 2048, the
     256-row tiles) the blocks keep their GEMM2s, and where none does (7 peers
     on the small tiles) the layer runs as one block whose sum folds.  Y,
-    H_out, Z_i and the sum are the same bits as the chunked two-stream schedule
-    (the separate reduction beside the GEMMs) and as the allocation-free entry
+    H_out, Z_i and the sum are the same bits as the two-stream schedule (each
+    block's separate reduction beside the next GEMM2) and as the allocation-free entry
     point, which keeps every chunk (Y holds one chunk), and match the oracle on
     sampled rows."""
     announce(f"mlp one stream, chunks merged R={Rc} C={Cc} act={act} h_out={h_out}")
@@ -651,7 +652,7 @@ def test_one_stream_merges_the_chunks(Rc, Cc, act, h_out, folds):
         tp.tp_timing_enable(False)
     assert st["gemm1"]["launches"] == 1 and st["gemm2_reduce"]["launches"] == folds
     assert st["gemm2"]["launches"] == 0 and st["reduce"]["launches"] == 0
-    assert st_chunked["gemm1"]["launches"] == Rc and st_chunked["gemm2"]["launches"] == Rc * Cc
+    assert st_chunked["gemm1"]["launches"] == 1 and st_chunked["gemm2"]["launches"] == Rc * Cc
     # (at R = C = 2 each kept block takes the small tiles, whose epilogue sums at most 3 peers: separate reductions)
     assert st_kept["gemm1"]["launches"] == Rc
     assert st_kept["gemm2_reduce"]["launches"] + st_kept["gemm2"]["launches"] == Rc * Cc

@@ -1004,11 +1004,18 @@ def run_workload(name, steps, warmup, flusher, args, serial_too=True):
     g1 = m["kernels_cold"].get("gemm1", {}).get("launches_per_step")
     if isinstance(wl, MlpStep) and g1 is not None and g1 < wl.w.R:
         # What the library made of the row chunks (seen in its launch counts).
-        one = "one stream" + ("" if wl.serial else " (the second offered, unused)")
-        summ["config"]["schedule"] = (one + ": every row chunk's sum folds into its GEMM2's epilogue, so GEMM1 runs "
-                                      "once over all rows and each chunk keeps its GEMM2"
-                                      if "gemm2_reduce" in m["kernels_cold"] and "reduce" not in m["kernels_cold"]
-                                      else one + ": the row chunks run as one block")
+        kc = m["kernels_cold"]
+        if "reduce" in kc and not wl.serial:
+            summ["config"]["schedule"] = (
+                "two streams: GEMM1 once over all rows, then each block's GEMM2 with the previous block's sum "
+                "beside it on the second stream" +
+                ("; the last block's sum in its GEMM2's epilogue" if "gemm2_reduce" in kc else ""))
+        else:
+            one = "one stream" + ("" if wl.serial else " (the second offered, unused)")
+            summ["config"]["schedule"] = (one + ": every row chunk's sum folds into its GEMM2's epilogue, so GEMM1 "
+                                          "runs once over all rows and each chunk keeps its GEMM2"
+                                          if "gemm2_reduce" in kc and "reduce" not in kc
+                                          else one + ": the row chunks run as one block")
     for k, v in m["kernels_cold"].items():
         log(f"[bench]   {k:18s} {v['launches_per_step']:.0f}/step  avg {v['avg_ms'] * 1e3:9.1f} us  "
             f"{v['achieved']:9.1f} {v['unit']}  ({100 * v['frac']:.1f}% of {v['peak']:.0f}, cold)")

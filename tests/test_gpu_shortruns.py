@@ -34,8 +34,16 @@ CASES = [
     ((2048, 12), {"device": [3, 1, 0, 2], "sharded_dim": [{"axis": 1, "num_shards": 4}]}, "bf16"),          # 6-byte runs
     ((16, 64, 8), {"device": list(range(16)),
                    "sharded_dim": [{"axis": 2, "num_shards": 8}, {"axis": 0, "num_shards": 2}]}, "bf16"),
+    # 8-byte runs: odd n with replicas, n = 8 and 16, an outer cut with an axis inside it
+    ((2048, 12), {"device": [-1, -2, -3], "device_map": {-1: [0, 3], -2: [1, 4], -3: [2, 5]},
+                  "sharded_dim": [{"axis": 1, "num_shards": 3}]}, "bf16"),
+    ((1024, 16), {"device": list(range(8)), "sharded_dim": [{"axis": 1, "num_shards": 8}]}, "f32"),
+    ((512, 2, 32), {"device": list(range(16)),
+                    "sharded_dim": [{"axis": 0, "num_shards": 2}, {"axis": 2, "num_shards": 8}]}, "bf16"),
+    ((1024, 32), {"device": list(range(16)), "sharded_dim": [{"axis": 1, "num_shards": 16}]}, "f32"),
     # nine 512-row blocks: the gather's workgroups take two blocks each, one of them three
     ((4608, 8), {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 1, "num_shards": 4}]}, "f32"),
+    ((4608, 12), {"device": [0, 1, 2, 3], "sharded_dim": [{"axis": 1, "num_shards": 4}]}, "bf16"),
     # not taken by the row-block kernels: blocks of fewer than 8 rows, 16-byte runs
     ((100, 8), {"device": list(range(8)), "sharded_dim": [{"axis": 1, "num_shards": 8}]}, "bf16"),
     ((8, 256, 12), {"device": list(range(6)),

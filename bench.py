@@ -7,9 +7,11 @@ on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input.
 The headline workload is the GPT-3 175B per-rank MLP at TP = 8 with the
-Domino 2D split (X in 2 row chunks, B_i in 2 column blocks): GEMM1 + GeLU per
-row chunk, GEMM2 per block into the fp32 partial, and each block's 8-way
-partial sum on a second stream beside the next block's GEMMs.  The value is
+Domino 2D split (X in 2 row chunks, B_i in 2 column blocks): GEMM1 + GeLU
+(over both row chunks in one launch where the library so schedules it), GEMM2
+per block into the fp32 partial, and each block's 8-way partial sum on a
+second stream beside the next block's GEMM2, the last block's in its GEMM2's
+epilogue.  The value is
 per-rank MLP TFLOP/s (2 GEMMs of 2*M*H*F flops) over K consecutive steps,
 timed as eager launches, as K replays of a one-step HIP graph and as one
 replay of a graph holding the K steps (the fastest counts, named in
@@ -724,11 +726,13 @@ def kernel_table(stats, steps, dtype):
     return out
 
 
-def roofline(kernels, dtype, workload, default_schedule=True, timing="cold"):
+def roofline(kernels, dtype, workload, default_schedule=True, timing="cold", kernels_warm=None):
     """Roofline entry of the dominant kernel: the kernel with the most time per
     step among the GEMMs (together most of an MLP step), GEMM2 counting with
     the reduction when that runs in its epilogue; elsewhere the kernel with the
-    most time."""
+    most time.  `frac` is the cold figure; the same kernel's rate with the
+    steps back to back (as the value's timed steps run) rides along as
+    `warm`."""
     if not kernels:
         return None
     pool = [k for k in kernels if k.startswith("gemm")] or list(kernels)
@@ -737,9 +741,13 @@ def roofline(kernels, dtype, workload, default_schedule=True, timing="cold"):
     # The counters were taken with the default schedule and outputs; another
     # schedule moves other bytes.
     traffic = measured_traffic(workload, name) if default_schedule else None
-    return {"kernel": name, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"], "unit": k["unit"],
-            "frac": k["frac"], "traffic": traffic, "avg_ms": k["avg_ms"],
-            "work_per_launch": k["work_per_launch"], "timing": timing}
+    out = {"kernel": name, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"], "unit": k["unit"],
+           "frac": k["frac"], "traffic": traffic, "avg_ms": k["avg_ms"],
+           "work_per_launch": k["work_per_launch"], "timing": timing}
+    kw = (kernels_warm or {}).get(name)
+    if kw:
+        out["warm"] = {"achieved": kw["achieved"], "frac": kw["frac"], "avg_ms": kw["avg_ms"]}
+    return out
 
 
 # --------------------------------------------------------------------------- torch context
@@ -1006,7 +1014,8 @@ def run_workload(name, steps, warmup, flusher, args, serial_too=True):
             "ms_per_step_graph_k": m.get("ms_per_step_graph_k"),
             "step_ms": m["step_ms"], "value_cold_median": rate(wl, m["step_ms"]["cold"]["median"]),
             "peers": "drawn N(0,1) (profile mode)" if DRAWN_PEERS else "computed by the same path",
-            "roofline": roofline(m["kernels_cold"], m["dtype"], name, default_schedule),
+            "roofline": roofline(m["kernels_cold"], m["dtype"], name, default_schedule,
+                                 kernels_warm=m["kernels_warm"]),
             "kernels": m["kernels_cold"], "kernels_warm": m["kernels_warm"], "dtype": m["dtype"]}
     g1 = m["kernels_cold"].get("gemm1", {}).get("launches_per_step")
     if isinstance(wl, MlpStep) and g1 is not None and g1 < wl.w.R:

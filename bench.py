@@ -726,6 +726,23 @@ def kernel_table(stats, steps, dtype):
     return out
 
 
+def schedule_label(kernels, row_chunks, serial):
+    """What the library made of the row chunks, read off its launch counts:
+    None while every chunk keeps its own GEMM1 (the schedule as configured)."""
+    g1 = kernels.get("gemm1", {}).get("launches_per_step")
+    if g1 is None or g1 >= row_chunks:
+        return None
+    if "reduce" in kernels and not serial:
+        return ("two streams: GEMM1 once over all rows, then each block's GEMM2 with the previous block's sum "
+                "beside it on the second stream" +
+                ("; the last block's sum in its GEMM2's epilogue" if "gemm2_reduce" in kernels else ""))
+    one = "one stream" + ("" if serial else " (the second offered, unused)")
+    if "gemm2_reduce" in kernels and "reduce" not in kernels:
+        return one + (": every row chunk's sum folds into its GEMM2's epilogue, so GEMM1 runs once over all rows "
+                      "and each chunk keeps its GEMM2")
+    return one + ": the row chunks run as one block"
+
+
 def roofline(kernels, dtype, workload, default_schedule=True, timing="cold", kernels_warm=None):
     """Roofline entry of the dominant kernel: the kernel with the most time per
     step among the GEMMs (together most of an MLP step), GEMM2 counting with
@@ -1017,21 +1034,9 @@ def run_workload(name, steps, warmup, flusher, args, serial_too=True):
             "roofline": roofline(m["kernels_cold"], m["dtype"], name, default_schedule,
                                  kernels_warm=m["kernels_warm"]),
             "kernels": m["kernels_cold"], "kernels_warm": m["kernels_warm"], "dtype": m["dtype"]}
-    g1 = m["kernels_cold"].get("gemm1", {}).get("launches_per_step")
-    if isinstance(wl, MlpStep) and g1 is not None and g1 < wl.w.R:
-        # What the library made of the row chunks (seen in its launch counts).
-        kc = m["kernels_cold"]
-        if "reduce" in kc and not wl.serial:
-            summ["config"]["schedule"] = (
-                "two streams: GEMM1 once over all rows, then each block's GEMM2 with the previous block's sum "
-                "beside it on the second stream" +
-                ("; the last block's sum in its GEMM2's epilogue" if "gemm2_reduce" in kc else ""))
-        else:
-            one = "one stream" + ("" if wl.serial else " (the second offered, unused)")
-            summ["config"]["schedule"] = (one + ": every row chunk's sum folds into its GEMM2's epilogue, so GEMM1 "
-                                          "runs once over all rows and each chunk keeps its GEMM2"
-                                          if "gemm2_reduce" in kc and "reduce" not in kc
-                                          else one + ": the row chunks run as one block")
+    label = schedule_label(m["kernels_cold"], wl.w.R, wl.serial) if isinstance(wl, MlpStep) else None
+    if label:
+        summ["config"]["schedule"] = label
     for k, v in m["kernels_cold"].items():
         log(f"[bench]   {k:18s} {v['launches_per_step']:.0f}/step  avg {v['avg_ms'] * 1e3:9.1f} us  "
             f"{v['achieved']:9.1f} {v['unit']}  ({100 * v['frac']:.1f}% of {v['peak']:.0f}, cold)")

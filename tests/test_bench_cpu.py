@@ -94,3 +94,16 @@ def test_default_workload_is_the_largest_single_gpu_configuration():
     assert set(bench.EXTRAS) == {"tiny-fp32-p2", "gpt2-small-tp4", "gpt3-6.7b-tp8-rowsplit2", "reshard-2x4-mesh",
                                  "shortrun-split-gather"}
     assert bench.FLUSH_BYTES >= 512 << 20
+
+
+def test_schedule_label_from_launch_counts():
+    """The record names the schedule the library chose, from its launch counts."""
+    k = lambda **n: {name: {"launches_per_step": c} for name, c in n.items()}
+    # a GEMM1 per chunk: the schedule as configured, no label
+    assert bench.schedule_label(k(gemm1=2, gemm2=4, reduce=3, gemm2_reduce=1), 2, False) is None
+    two = bench.schedule_label(k(gemm1=1, gemm2=3, reduce=3, gemm2_reduce=1), 2, False)
+    assert two.startswith("two streams") and "epilogue" in two
+    fold = bench.schedule_label(k(gemm1=1, gemm2_reduce=2), 2, False)
+    assert fold.startswith("one stream (the second offered, unused)") and "folds" in fold
+    assert bench.schedule_label(k(gemm1=1, gemm2_reduce=2), 2, True).startswith("one stream:")
+    assert bench.schedule_label(k(gemm1=1, gemm2=1, reduce=1), 2, True).endswith("as one block")

@@ -734,3 +734,47 @@ def test_column_shard_read_in_place(Rc, Cc, P, fusion):
             outs.append([bits(g.t.cpu()) for g in (Y, Z, Zo)])
         for a, b in zip(*outs):
             assert np.array_equal(a, b)
+
+
+def test_two_stream_gemm1_first_equals_one_block():
+    """The headline's schedule shape (GEMM1 once over all rows, R = C = 2, three
+    sums beside the next GEMM2 and the last in its epilogue: F = 6144 as in
+    the 175B layer, so each block's sum is short enough to run beside the
+    next block's GEMM2, and blocks of 2048 x 2048 take the 256-row tiles
+    whose epilogue sums 7 peers) with every output the fused epilogue writes (the sum
+    with the bias, the next layer's bf16 input, the pre-activation and Y)
+    equals the same layer run as one block on one stream, bit for bit: chunking
+    and the schedule change no result bit.  Guarded outputs catch stray
+    writes."""
+    M, H, F, P, Rc, Cc = 4096, 4096, 6144, 8, 2, 2
+    announce(f"mlp two-stream GEMM1-first against one block M={M} H={H} F={F} P={P} R={Rc} C={Cc}")
+    X = inputs.normal((M, H), 401, 1.0, "bf16").cuda()
+    A = inputs.normal((H, F), 402, 1.0 / np.sqrt(H), "bf16").cuda()
+    B = inputs.normal((F, H), 403, 1.0 / np.sqrt(F), "bf16").cuda()
+    bias = inputs.normal((H,), 404, 0.1).cuda()
+    peers = [inputs.normal((M, H), 410 + p).cuda() for p in range(P - 1)]
+    outs = []
+    for two in (True, False):
+        Y, Hh = Guarded((M, F), torch.bfloat16), Guarded((M, F), torch.bfloat16)
+        Z, Zo, Xn = Guarded((M, H), torch.float32), Guarded((M, H), torch.float32), Guarded((M, H), torch.bfloat16)
+        s0 = torch.cuda.current_stream()
+        s1 = torch.cuda.Stream() if two else s0
+        tp.tp_timing_enable(True)
+        try:
+            tp.tp_timing_read()
+            tp.tp_colrow_mlp(X, A, B, Y.t, Z.t, row_chunks=Rc if two else 1, col_chunks=Cc if two else 1,
+                             peer_partials=peers, Z_out=Zo.t, bias=bias, X_next=Xn.t, H_out=Hh.t,
+                             s_compute=s0, s_reduce=s1)
+            st = tp.tp_timing_read()
+        finally:
+            tp.tp_timing_enable(False)
+        torch.cuda.synchronize()
+        for g in (Y, Hh, Z, Zo, Xn):
+            assert g.guards_intact()
+        if two:
+            assert st["gemm1"]["launches"] == 1 and st["gemm2"]["launches"] == Rc * Cc - 1
+            assert st["reduce"]["launches"] == Rc * Cc - 1 and st["gemm2_reduce"]["launches"] == 1
+        outs.append([g.t.clone() for g in (Y, Hh, Zo, Xn)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
